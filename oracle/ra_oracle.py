@@ -1,0 +1,275 @@
+"""Plain, slow, obviously correct fp64 definition of one RetrievalAttention
+decode step with an exact top-k retrieval. TEST INFRASTRUCTURE ONLY: the
+product path never imports this module.
+
+Source pages (cited by title and slide/equation, never by line):
+
+* RetrievalAttention slides (arXiv:2409.10516v3 discussion deck)
+  - frame "Sparse attention renormalizes selected tokens": Eq. (1) scores and
+    softmax, Eq. (2) renormalised attention over a selected set, and the
+    fixed retrieval budget (top-k) used instead of a threshold.
+  - frame "The GPU keeps 640 fixed positions": static set W = first 128 +
+    last 512 tokens, W and the retrieved set are disjoint, GQA query heads get
+    their own indices over shared KV storage.
+  - frame "Two local softmax outputs need global weights": the stable partial
+    form (m_S, Z_S, o_S) and the merge weights gamma_S, Eqs. (3)-(5).
+  - backup frame "the normalization identity": N_S, Z_S, and that merging
+    disjoint partials gives the exact softmax on their union.
+  - frame "The bottleneck is both storage and KV access": Table 1, KV capacity.
+
+Readings of points the pages leave open (listed in the design notes too):
+
+* d in 1/sqrt(d) is the head dimension (128).
+* The retrieved set is searched over M = [0, N) minus W, so it never holds a
+  W position; k_eff = min(k, |M|).
+* Ties at the k-th score go to the lower position; the retrieved indices are
+  returned in ascending position order.
+* GQA groups are contiguous: query head h reads KV head floor(h / G),
+  G = H_q / H_kv. Selection is per query head.
+* An empty attended set gives out = 0 and lse = -inf.
+
+Every quantity is float64 after exact widening of the bf16 inputs.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+HEAD_DIM = 128
+
+# Token tile for score computation: bounds the fp64 working set (a 1M-token
+# layer is 8 GiB as fp64, so K is widened one tile at a time).
+_SCORE_TILE = 65536
+
+
+def as_f64(x) -> np.ndarray:
+    """Widen an input array to float64 exactly.
+
+    ``uint16`` arrays are taken as raw bfloat16 bit patterns (the top 16 bits
+    of an IEEE binary32), so the widening is exact. Any float array is cast.
+    """
+    a = np.asarray(x)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Sets: RetrievalAttention slides, frame "The GPU keeps 640 fixed positions".
+# --------------------------------------------------------------------------
+
+def static_set(N: int, n_sink: int, window: int) -> np.ndarray:
+    """W: the first ``n_sink`` and the last ``window`` positions of [0, N).
+
+    The slides fix W as the first 128 plus the last 512 tokens; the two counts
+    are parameters here. Returned sorted, without duplicates.
+    """
+    if N < 0 or n_sink < 0 or window < 0:
+        raise ValueError("N, n_sink and window must be non-negative")
+    first = np.arange(0, min(n_sink, N), dtype=np.int64)
+    last = np.arange(max(N - window, 0), N, dtype=np.int64)
+    return np.union1d(first, last)
+
+
+def selection_domain(N: int, n_sink: int, window: int) -> np.ndarray:
+    """M = [0, N) minus W: the positions retrieval may choose from.
+
+    W and the retrieved set are disjoint on the slides, and only retrieved
+    KV outside W enters the second partial.
+    """
+    return np.setdiff1d(np.arange(N, dtype=np.int64), static_set(N, n_sink, window))
+
+
+# --------------------------------------------------------------------------
+# Scores: RetrievalAttention slides, "Sparse attention renormalizes selected
+# tokens", Eq. (1): z_i = q_t k_i^T / sqrt(d).
+# --------------------------------------------------------------------------
+
+def scores(q, K) -> np.ndarray:
+    """z[h, n] = (q[h] . K[n, g(h)]) / sqrt(d) for every cached position n.
+
+    q: [H_q, d]; K: [N, H_kv, d] (logical token order). g(h) = h // G with
+    G = H_q / H_kv: GQA query heads share their group's KV storage.
+    Returns float64 [H_q, N].
+    """
+    qf = as_f64(q)
+    H_q, d = qf.shape
+    Kn = np.asarray(K)
+    N, H_kv, d2 = Kn.shape
+    if d2 != d:
+        raise ValueError("head_dim mismatch between q and K")
+    if H_q % H_kv != 0:
+        raise ValueError("H_q must be a multiple of H_kv")
+    G = H_q // H_kv
+    inv_sqrt_d = 1.0 / math.sqrt(d)
+    z = np.empty((H_q, N), dtype=np.float64)
+    for t0 in range(0, N, _SCORE_TILE):
+        t1 = min(N, t0 + _SCORE_TILE)
+        Kt = as_f64(Kn[t0:t1])  # [T, H_kv, d]
+        for g in range(H_kv):
+            qg = qf[g * G:(g + 1) * G]          # the G query heads of group g
+            z[g * G:(g + 1) * G, t0:t1] = (qg @ Kt[:, g, :].T) * inv_sqrt_d
+    return z
+
+
+# --------------------------------------------------------------------------
+# Exact top-k: the fixed retrieval budget ("usually top-100") of the slides'
+# Eq. (2) frame, searched over M ("The GPU keeps 640 fixed positions").
+# --------------------------------------------------------------------------
+
+def topk(z_h: np.ndarray, M: np.ndarray, k: int) -> np.ndarray:
+    """Omega: the k_eff = min(k, |M|) positions of M with the largest score.
+
+    Ties at the k-th score go to the lower position. Returned ascending.
+    """
+    if k < 0:
+        raise ValueError("k must be non-negative")
+    M = np.asarray(M, dtype=np.int64)
+    k_eff = min(k, M.size)
+    if k_eff == 0:
+        return np.zeros(0, dtype=np.int64)
+    zM = z_h[M]
+    # the k_eff-th largest score over M
+    t = np.partition(zM, M.size - k_eff)[M.size - k_eff]
+    above = M[zM > t]
+    equal = M[zM == t]                    # ascending, because M is
+    take = k_eff - above.size
+    return np.sort(np.concatenate([above, equal[:take]]))
+
+
+# --------------------------------------------------------------------------
+# Partials and merge: "Two local softmax outputs need global weights",
+# Eqs. (3)-(5), and the backup frame "the normalization identity".
+# --------------------------------------------------------------------------
+
+def partial(z_h: np.ndarray, V_g, S) -> tuple[float, float, np.ndarray]:
+    """(m_S, Z_S, N_S) for one head over the index set S.
+
+    m_S = max_{i in S} z_i; Z_S = sum e^{z_i - m_S};
+    N_S = sum e^{z_i - m_S} v_i (so o_S = N_S / Z_S).
+    V_g: [N, d] values of the head's KV group. Empty S gives (-inf, 0, 0).
+    """
+    S = np.asarray(S, dtype=np.int64)
+    Vf = as_f64(V_g[S]) if S.size else np.zeros((0, np.asarray(V_g).shape[-1]))
+    if S.size == 0:
+        return -math.inf, 0.0, np.zeros(Vf.shape[-1], dtype=np.float64)
+    zs = z_h[S]
+    m = float(zs.max())
+    e = np.exp(zs - m)
+    return m, float(e.sum()), e @ Vf
+
+
+def merge(parts) -> tuple[np.ndarray, float]:
+    """Combine disjoint partials: m = max_S m_S, weights e^{m_S - m}.
+
+    o = sum_S e^{m_S-m} N_S / sum_S e^{m_S-m} Z_S, which equals
+    sum_S gamma_S o_S with gamma_S = e^{m_S-m} Z_S / sum_T e^{m_T-m} Z_T.
+    Returns (o, lse) with lse = m + ln sum_S e^{m_S-m} Z_S. No non-empty
+    partial gives (0, -inf).
+    """
+    parts = list(parts)
+    d = parts[0][2].shape[-1] if parts else HEAD_DIM
+    parts = [p for p in parts if p[1] > 0.0]
+    if not parts:
+        return np.zeros(d, dtype=np.float64), -math.inf
+    m = max(p[0] for p in parts)
+    num = sum(math.exp(p[0] - m) * p[2] for p in parts)
+    den = sum(math.exp(p[0] - m) * p[1] for p in parts)
+    return num / den, m + math.log(den)
+
+
+def attend(z_h: np.ndarray, V_g, S) -> tuple[np.ndarray, float]:
+    """Eq. (2): softmax over the selected set S, renormalised on S, times V.
+
+    o = sum_{i in S} e^{z_i} / sum_{j in S} e^{z_j} * v_i, computed with the
+    max subtracted. Returns (o [d], lse). Empty S gives (zeros, -inf).
+    """
+    d = np.asarray(V_g).shape[-1]
+    S = np.asarray(S, dtype=np.int64)
+    if S.size == 0:
+        return np.zeros(d, dtype=np.float64), -math.inf
+    zs = z_h[S]
+    m = float(zs.max())
+    e = np.exp(zs - m)
+    den = float(e.sum())
+    p = e / den
+    return p @ as_f64(V_g[S]), m + math.log(den)
+
+
+def dense(z_h: np.ndarray, V_g) -> tuple[np.ndarray, float]:
+    """Eq. (1): full softmax attention over every cached position."""
+    return attend(z_h, V_g, np.arange(z_h.shape[0], dtype=np.int64))
+
+
+# --------------------------------------------------------------------------
+# One decode step.
+# --------------------------------------------------------------------------
+
+def decode_head(z_h: np.ndarray, V_g, W: np.ndarray, M: np.ndarray, k: int):
+    """One query head: Omega = top-k over M, then attention over W u Omega.
+
+    Also returns the two-partial merge (W, Omega) of Eqs. (3)-(5), which must
+    equal the direct softmax over the union.
+    """
+    omega = topk(z_h, M, k)
+    S = np.union1d(W, omega)
+    o, lse = attend(z_h, V_g, S)
+    o_m, lse_m = merge([partial(z_h, V_g, W), partial(z_h, V_g, omega)])
+    return omega, o, lse, o_m, lse_m
+
+
+def decode(q, K, V, k: int, n_sink: int, window: int, with_dense: bool = False):
+    """One decode step for one sequence (all query heads).
+
+    q: [H_q, d]; K, V: [N, H_kv, d] in logical order (N = length after the
+    new token was appended, so the recent window includes it).
+    Returns a dict with float64 ``z`` [H_q, N], ``out`` [H_q, d], ``lse``
+    [H_q], the merged-partials ``out_merge``/``lse_merge``, and ``idx``: a
+    list of ascending int64 arrays (one per head, length k_eff). With
+    ``with_dense`` also the dense output and the attention mass recovered
+    (sum of full-softmax weights over W u Omega, the Fig. 2 metric).
+    """
+    Kn = np.asarray(K)
+    Vn = np.asarray(V)
+    N, H_kv, d = Kn.shape
+    qf = as_f64(q)
+    H_q = qf.shape[0]
+    G = H_q // H_kv
+    z = scores(qf, Kn)
+    W = static_set(N, n_sink, window)
+    M = selection_domain(N, n_sink, window)
+    out = np.zeros((H_q, d))
+    out_m = np.zeros((H_q, d))
+    lse = np.zeros(H_q)
+    lse_m = np.zeros(H_q)
+    idx = []
+    dense_out = np.zeros((H_q, d)) if with_dense else None
+    mass = np.zeros(H_q) if with_dense else None
+    for h in range(H_q):
+        Vg = Vn[:, h // G, :]
+        om, o, l, o2, l2 = decode_head(z[h], Vg, W, M, k)
+        idx.append(om)
+        out[h], lse[h] = o, l
+        out_m[h] = o2
+        lse_m[h] = l2
+        if with_dense:
+            dense_out[h], l_all = dense(z[h], Vg)
+            S = np.union1d(W, om)
+            mass[h] = float(np.exp(z[h][S] - l_all).sum()) if S.size else 0.0
+    res = dict(z=z, out=out, lse=lse, out_merge=out_m, lse_merge=lse_m, idx=idx,
+               W=W, M=M)
+    if with_dense:
+        res["dense_out"] = dense_out
+        res["mass_recovered"] = mass
+    return res
+
+
+# --------------------------------------------------------------------------
+# KV sizing: "The bottleneck is both storage and KV access", Table 1.
+# --------------------------------------------------------------------------
+
+def kv_bytes_per_token(n_layers: int, H_kv: int, head_dim: int, elem_bytes: int) -> int:
+    """Bytes of K plus V per cached token across all layers: 2*L*H_kv*d*b."""
+    return 2 * n_layers * H_kv * head_dim * elem_bytes

@@ -1,0 +1,124 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check that at least
+one pin in test_oracle_pins.py fails for each: the pins are strong enough
+to catch a dropped term, a wrong sign or index, or a transposed operand."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import ra_oracle as ro
+import tests.test_oracle_pins as pins
+
+
+_REAL_SCORES = ro.scores
+_REAL_TOPK = ro.topk
+
+
+def _scores_no_scale(q, K):
+    return _REAL_SCORES(q, K) * math.sqrt(ro.HEAD_DIM)
+
+
+def _scores_wrong_group(q, K):
+    qf = ro.as_f64(q)
+    Kf = ro.as_f64(K)
+    H_q = qf.shape[0]
+    H_kv = Kf.shape[1]
+    z = np.empty((H_q, Kf.shape[0]))
+    for h in range(H_q):
+        z[h] = Kf[:, h % H_kv, :] @ qf[h] / math.sqrt(ro.HEAD_DIM)
+    return z
+
+
+def _topk_smallest(z_h, M, k):
+    return _REAL_TOPK(-z_h, M, k)
+
+
+def _topk_ties_high(z_h, M, k):
+    M = np.asarray(M, dtype=np.int64)
+    k_eff = min(k, M.size)
+    if k_eff == 0:
+        return np.zeros(0, dtype=np.int64)
+    zM = z_h[M]
+    t = np.partition(zM, M.size - k_eff)[M.size - k_eff]
+    above = M[zM > t]
+    equal = M[zM == t][::-1]
+    return np.sort(np.concatenate([above, equal[:k_eff - above.size]]))
+
+
+def _static_off_by_one(N, n_sink, window):
+    first = np.arange(0, min(n_sink, N))
+    last = np.arange(max(N - window - 1, 0), N)
+    return np.union1d(first, last).astype(np.int64)
+
+
+def _merge_no_rescale(parts):
+    parts = [p for p in parts if p[1] > 0.0]
+    if not parts:
+        return np.zeros(ro.HEAD_DIM), -math.inf
+    num = sum(p[2] for p in parts)
+    den = sum(p[1] for p in parts)
+    m = max(p[0] for p in parts)
+    return num / den, m + math.log(den)
+
+
+def _attend_no_renorm(z_h, V_g, S):
+    S = np.asarray(S, dtype=np.int64)
+    if S.size == 0:
+        return np.zeros(np.asarray(V_g).shape[-1]), -math.inf
+    e = np.exp(z_h[S])
+    return e @ ro.as_f64(V_g[S]), float(np.log(e.sum()))
+
+
+_REAL_ATTEND = ro.attend
+
+
+def _attend_transposed_v(z_h, V_g, S):
+    o, l = _REAL_ATTEND(z_h, V_g, S)
+    return o[::-1].copy(), l
+
+
+MUTANTS = {
+    "scores_no_scale": ("scores", _scores_no_scale),
+    "scores_wrong_group": ("scores", _scores_wrong_group),
+    "topk_smallest": ("topk", _topk_smallest),
+    "topk_ties_high": ("topk", _topk_ties_high),
+    "static_off_by_one": ("static_set", _static_off_by_one),
+    "merge_no_rescale": ("merge", _merge_no_rescale),
+    "attend_no_renorm": ("attend", _attend_no_renorm),
+    "attend_transposed_v": ("attend", _attend_transposed_v),
+}
+
+PIN_FUNCS = [getattr(pins, n) for n in dir(pins) if n.startswith("test_")]
+
+
+def _run_pins():
+    """Run every parameter-free pin; return the number that fail."""
+    failed = 0
+    for f in PIN_FUNCS:
+        params = getattr(f, "pytestmark", [])
+        cases = [()]
+        for m in params:
+            if m.name == "parametrize":
+                names = m.args[0]
+                cases = [c if isinstance(c, tuple) else (c,) for c in m.args[1]]
+        for c in cases:
+            try:
+                f(*c)
+            except (AssertionError, ValueError, IndexError, FloatingPointError):
+                failed += 1
+    return failed
+
+
+def test_pins_pass_on_the_real_oracle():
+    assert _run_pins() == 0
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_every_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(ro, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn)
+    with np.errstate(all="ignore"):
+        assert _run_pins() > 0, f"mutant {name} survived every pin"

@@ -1,0 +1,316 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: closed
+forms, brute force over all subsets, special cases that reduce to a library
+routine (scipy), algebraic invariants, and Table 1's printed KV capacities.
+"""
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp, softmax
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+D = 128
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest even) and return the raw bits."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return r
+
+
+# ---------------------------------------------------------------- widening
+
+def test_bf16_widening_known_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x0001, 0x7F7F, 0x0000, 0x8000, 0x3E00], dtype=np.uint16)
+    v = oracle.as_f64(bits)
+    assert v[0] == 1.0 and v[1] == -2.0
+    assert v[2] == 2.0 ** -133                      # smallest bf16 subnormal
+    assert v[3] == (2 - 2 ** -7) * 2.0 ** 127       # largest finite bf16
+    assert v[4] == 0.0 and math.copysign(1, v[5]) == -1
+    assert v[6] == 0.125
+
+
+# ---------------------------------------------------------------- sets
+
+@pytest.mark.parametrize("N,ns,win,W", [
+    (10, 2, 3, [0, 1, 7, 8, 9]),
+    (4, 3, 3, [0, 1, 2, 3]),
+    (6, 0, 0, []),
+    (6, 0, 2, [4, 5]),
+    (6, 2, 0, [0, 1]),
+    (1, 128, 512, [0]),
+    (0, 1, 1, []),
+    (700, 128, 512, list(range(0, 128)) + list(range(188, 700))),
+])
+def test_static_set_and_domain_by_hand(N, ns, win, W):
+    assert oracle.static_set(N, ns, win).tolist() == W
+    assert oracle.selection_domain(N, ns, win).tolist() == [n for n in range(N) if n not in W]
+
+
+# ---------------------------------------------------------------- scores
+
+def test_scores_unit_query_reads_one_coordinate():
+    r = rng(1)
+    K = to_bf16_bits(r.standard_normal((50, 2, D)))
+    q = np.zeros((4, D))
+    for h in range(4):
+        q[h, 7 * h + 3] = 1.0
+    z = oracle.scores(q, K)
+    Kf = oracle.as_f64(K)
+    for h in range(4):
+        np.testing.assert_allclose(z[h], Kf[:, h // 2, 7 * h + 3] / math.sqrt(D), rtol=4e-16, atol=0)
+
+
+def test_scores_all_ones_gives_sqrt_d():
+    z = oracle.scores(np.ones((1, D)), np.ones((3, 1, D), dtype=np.float64))
+    np.testing.assert_allclose(z, math.sqrt(D), rtol=1e-15)
+
+
+def test_scores_gqa_contiguous_groups():
+    # KV head 0 holds +1 keys, KV head 1 holds -1 keys; with G = 4 query
+    # heads 0..3 must read head 0 and 4..7 head 1.
+    K = np.zeros((5, 2, D))
+    K[:, 0] = 1.0
+    K[:, 1] = -1.0
+    z = oracle.scores(np.ones((8, D)), K)
+    s = math.sqrt(D)
+    np.testing.assert_allclose(z[:4], s)
+    np.testing.assert_allclose(z[4:], -s)
+
+
+def test_scores_exact_rational_dot():
+    r = rng(2)
+    q = to_bf16_bits(r.standard_normal((2, D)))
+    K = to_bf16_bits(r.standard_normal((6, 1, D)))
+    z = oracle.scores(q, K)
+    qf, Kf = oracle.as_f64(q), oracle.as_f64(K)
+    for h in range(2):
+        for n in range(6):
+            exact = sum(Fraction(a) * Fraction(b) for a, b in zip(qf[h], Kf[n, 0]))
+            assert abs(z[h, n] * math.sqrt(D) - float(exact)) <= 1e-13 * (1 + abs(float(exact)))
+
+
+def test_scores_tiles_agree_across_tile_boundary():
+    r = rng(3)
+    N = 65536 + 300
+    K = r.standard_normal((N, 1, D)).astype(np.float32)
+    q = r.standard_normal((2, D))
+    z = oracle.scores(q, K)
+    for n in (0, 65535, 65536, N - 1):
+        np.testing.assert_allclose(z[:, n], q @ K[n, 0].astype(np.float64) / math.sqrt(D), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- top-k
+
+def brute_topk(z, M, k):
+    """The unique subset of M of size min(k,|M|) whose every member beats
+    every non-member under (higher score first, then lower position)."""
+    M = list(M)
+    k_eff = min(k, len(M))
+    hits = []
+    for S in itertools.combinations(M, k_eff):
+        rest = [n for n in M if n not in S]
+        ok = all((z[a] > z[b]) or (z[a] == z[b] and a < b) for a in S for b in rest)
+        if ok:
+            hits.append(list(S))
+    assert len(hits) == 1
+    return hits[0]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_brute_force_small(seed):
+    r = rng(100 + seed)
+    N = int(r.integers(1, 15))
+    # few distinct values, so ties are common
+    z = r.integers(-3, 4, size=N).astype(np.float64) * 0.5
+    ns, win = int(r.integers(0, 4)), int(r.integers(0, 4))
+    M = oracle.selection_domain(N, ns, win)
+    for k in range(0, len(M) + 2):
+        got = oracle.topk(z, M, k).tolist()
+        assert got == sorted(got)
+        assert got == brute_topk(z, M, k)
+
+
+def test_topk_constant_scores_take_lowest_positions():
+    z = np.full(100, 0.25)
+    M = oracle.selection_domain(100, 10, 20)
+    assert oracle.topk(z, M, 7).tolist() == list(range(10, 17))
+
+
+def test_topk_full_sort_crosscheck():
+    r = rng(4)
+    N = 5000
+    z = np.round(r.standard_normal(N), 2)       # many ties
+    M = oracle.selection_domain(N, 16, 64)
+    order = np.lexsort((M, -z[M]))              # by score desc, then position asc
+    for k in (1, 10, 64, 777, len(M)):
+        assert oracle.topk(z, M, k).tolist() == sorted(M[order[:k]].tolist())
+
+
+def test_topk_never_returns_static_positions():
+    z = np.zeros(300)
+    z[:16] = 100.0       # sinks score highest
+    z[-64:] = 90.0       # the recent window next
+    M = oracle.selection_domain(300, 16, 64)
+    om = oracle.topk(z, M, 10)
+    assert set(om.tolist()).isdisjoint(oracle.static_set(300, 16, 64).tolist())
+
+
+def test_topk_picks_largest_not_smallest():
+    z = np.arange(50, dtype=np.float64)
+    assert oracle.topk(z, np.arange(50), 3).tolist() == [47, 48, 49]
+
+
+# ---------------------------------------------------------------- attention
+
+def random_case(seed, N=300, H_kv=2, G=2, scale=1.0):
+    r = rng(seed)
+    q = to_bf16_bits(r.standard_normal((H_kv * G, D)) * scale)
+    K = to_bf16_bits(r.standard_normal((N, H_kv, D)))
+    V = to_bf16_bits(r.standard_normal((N, H_kv, D)))
+    return q, K, V
+
+
+def test_k_at_least_M_equals_dense():
+    q, K, V = random_case(5)
+    res = oracle.decode(q, K, V, k=10 ** 6, n_sink=8, window=16, with_dense=True)
+    np.testing.assert_allclose(res["out"], res["dense_out"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(res["mass_recovered"], 1.0, rtol=1e-12)
+
+
+def test_weights_sum_to_one_via_constant_values():
+    q, K, _ = random_case(6)
+    V = np.ones((300, 2, D))
+    res = oracle.decode(q, K, V, k=20, n_sink=4, window=8)
+    np.testing.assert_allclose(res["out"], 1.0, rtol=1e-14)
+
+
+def test_merge_of_any_disjoint_partition_equals_union():
+    r = rng(7)
+    z = r.standard_normal(400) * 3
+    V = r.standard_normal((400, D))
+    S = r.choice(400, 150, replace=False)
+    for parts in (1, 2, 3, 5):
+        cuts = np.sort(r.choice(np.arange(1, 150), parts - 1, replace=False))
+        pieces = np.split(r.permutation(S), cuts)
+        o, l = oracle.merge([oracle.partial(z, V, p) for p in pieces])
+        o_ref, l_ref = oracle.attend(z, V, S)
+        np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-14)
+        assert abs(l - l_ref) < 1e-12
+
+
+def test_merge_ignores_empty_partials():
+    r = rng(8)
+    z = r.standard_normal(20)
+    V = r.standard_normal((20, D))
+    o, l = oracle.merge([oracle.partial(z, V, []), oracle.partial(z, V, [3, 4])])
+    o_ref, l_ref = oracle.attend(z, V, [3, 4])
+    np.testing.assert_allclose(o, o_ref, rtol=1e-14)
+    o, l = oracle.merge([oracle.partial(z, V, [])])
+    assert np.all(o == 0) and l == -math.inf
+
+
+def test_one_hot_values_read_the_softmax_weights():
+    r = rng(9)
+    N = 120
+    z = r.standard_normal(N) * 2
+    V = np.eye(N, D)          # row i is e_i
+    S = np.sort(r.choice(N, 40, replace=False))
+    o, l = oracle.attend(z, V, S)
+    w = softmax(z[S])
+    np.testing.assert_allclose(o[S], w, rtol=1e-13)
+    assert np.all(o[np.setdiff1d(np.arange(D), S)] == 0)
+    assert abs(l - logsumexp(z[S])) < 1e-12
+
+
+def test_constant_keys_give_mean_of_values():
+    r = rng(10)
+    N = 200
+    K = np.tile(r.standard_normal((1, 1, D)), (N, 1, 1))
+    V = r.standard_normal((N, 1, D))
+    q = r.standard_normal((1, D))
+    res = oracle.decode(q, K, V, k=30, n_sink=5, window=7)
+    S = np.union1d(res["W"], res["idx"][0])
+    np.testing.assert_allclose(res["out"][0], V[S, 0].mean(0), rtol=1e-12, atol=1e-14)
+    # all scores tie, so the lowest positions of M are retrieved
+    assert res["idx"][0].tolist() == list(range(5, 35))
+
+
+def test_single_element_set_returns_that_value_row():
+    r = rng(11)
+    z = r.standard_normal(10)
+    V = r.standard_normal((10, D))
+    o, l = oracle.attend(z, V, [6])
+    np.testing.assert_array_equal(o, V[6])
+    assert l == z[6]
+
+
+def test_k_zero_is_static_set_attention():
+    q, K, V = random_case(12)
+    res = oracle.decode(q, K, V, k=0, n_sink=4, window=32)
+    W = oracle.static_set(300, 4, 32)
+    z = res["z"]
+    Vf = oracle.as_f64(V)
+    for h in range(4):
+        assert res["idx"][h].size == 0
+        np.testing.assert_allclose(res["out"][h], softmax(z[h, W]) @ Vf[W, h // 2], rtol=1e-12, atol=1e-14)
+
+
+def test_no_static_set_is_pure_topk_attention():
+    q, K, V = random_case(13)
+    res = oracle.decode(q, K, V, k=17, n_sink=0, window=0)
+    z = res["z"]
+    Vf = oracle.as_f64(V)
+    for h in range(4):
+        om = res["idx"][h]
+        assert om.size == 17
+        np.testing.assert_allclose(res["out"][h], softmax(z[h, om]) @ Vf[om, h // 2], rtol=1e-12, atol=1e-14)
+        assert abs(res["lse"][h] - logsumexp(z[h, om])) < 1e-12
+
+
+def test_decode_merge_path_equals_direct_softmax():
+    q, K, V = random_case(14, scale=3.0)
+    res = oracle.decode(q, K, V, k=40, n_sink=8, window=24)
+    np.testing.assert_allclose(res["out_merge"], res["out"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(res["lse_merge"], res["lse"], rtol=1e-13)
+
+
+def test_empty_attended_set():
+    q, K, V = random_case(15, N=10)
+    res = oracle.decode(q, K, V, k=0, n_sink=0, window=0)
+    assert np.all(res["out"] == 0) and np.all(res["lse"] == -np.inf)
+
+
+def test_large_score_range_is_stable():
+    # sink-like keys with very large scores must not overflow the softmax
+    z = np.array([700.0, -700.0, 699.0, 0.0])
+    V = np.eye(4, D)
+    o, l = oracle.attend(z, V, [0, 1, 2, 3])
+    np.testing.assert_allclose(o[:4], softmax(z), rtol=1e-13, atol=1e-300)
+    assert abs(l - logsumexp(z)) < 1e-10
+
+
+# ---------------------------------------------------------------- KV sizing
+
+def test_table1_kv_capacity_row():
+    g = json.load(open(os.path.join(GOLDEN, "table1_kv_capacity.json")))
+    m = g["model"]
+    per_tok = oracle.kv_bytes_per_token(m["n_layers"], m["H_kv"], m["head_dim"], m["elem_bytes"])
+    assert per_tok == 128 * 1024
+    for toks, printed in zip(g["prompt_tokens"], g["printed_capacity_gb"]):
+        gib = toks * per_tok / 2 ** 30
+        assert float(f"{gib:.3g}") == printed or round(gib, 1) == printed
