@@ -1,0 +1,176 @@
+/*
+ * ra.h - C ABI of the exact top-k sparse GQA decode step (MI355X / gfx950).
+ *
+ * One call computes, for every sequence b and query head h, the decode step
+ * of RetrievalAttention with an exact retrieval:
+ *
+ *   z[n]   = q_h . k_n / sqrt(128) for every cached position n
+ *            (RetrievalAttention slides, "Sparse attention renormalizes
+ *            selected tokens", Eq. (1));
+ *   W      = the first n_sink and the last `window` positions (frame "The GPU
+ *            keeps 640 fixed positions": first 128 + last 512 tokens);
+ *   Omega  = the k_eff = min(k[b], |M|) positions of M = [0, N) \ W with the
+ *            largest z, ties to the lower position (the fixed retrieval
+ *            budget of the Eq. (2) frame; W and Omega disjoint);
+ *   out    = softmax(z) . V over W u Omega, renormalised on that set (Eq. (2)),
+ *            computed as partials merged by log-sum-exp (frame "Two local
+ *            softmax outputs need global weights", Eqs. (3)-(5)).
+ *
+ * GQA: query head h reads KV head h / G, G = H_q / H_kv (contiguous groups);
+ * each query head gets its own retrieved indices over the shared KV storage
+ * (frame "The GPU keeps 640 fixed positions").
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are HIP device memory owned by the caller; the
+ *    library never allocates, frees, synchronises or reads device memory on
+ *    the host. Work is enqueued on `stream` in order; buffers must stay live
+ *    until the stream has executed it.
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - Host arguments are validated before anything is enqueued; on an error
+ *    nothing is enqueued and the status says why. Device contents (lengths,
+ *    budgets, block-table entries) are trusted, but clamped so that no access
+ *    leaves its buffer: a length is clamped to [0, min(max_seq_len,
+ *    64 * max_pages)], a budget to [0, k_max], and a page id outside
+ *    [0, num_pages) reads page 0.
+ *  - The library is stateless and reentrant; no C++ exception crosses it.
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RA_ABI_VERSION 1
+#define RA_HEAD_DIM 128
+#define RA_PAGE_SIZE 64
+#define RA_MAX_SEQ_LEN (1 << 27)
+#define RA_MAX_BATCH 65535
+
+typedef enum ra_status {
+  RA_OK = 0,
+  RA_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, H_q % H_kv != 0, ... */
+  RA_ERR_WORKSPACE = 2,        /* ws_bytes below ra_decode_workspace_bytes(...) */
+  RA_ERR_UNSUPPORTED = 3,      /* head_dim != 128, page_size != 64, G not in {1,2,4,8} */
+  RA_ERR_HIP = 4               /* a kernel launch reported an error */
+} ra_status;
+
+/*
+ * One layer's paged KV cache.
+ *  k_pool, v_pool: device bf16 [num_pages][H_kv][64][128]; the 64 x 128 block
+ *                  of one (page, KV head) is contiguous (16 KiB).
+ *  block_table:    device int32 [B][max_pages]; entry [b][j] is the physical
+ *                  page holding positions 64 j .. 64 j + 63 of sequence b.
+ * Page allocation is the caller's job.
+ */
+typedef struct ra_kv_layer {
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  const int32_t* block_table;
+  int32_t num_pages;
+  int32_t max_pages;
+  int32_t H_kv;
+  int32_t head_dim;  /* must be 128 */
+  int32_t page_size; /* must be 64 */
+} ra_kv_layer;
+
+/* RA_ABI_VERSION of the built library. */
+int ra_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* ra_status_str(ra_status s);
+
+/*
+ * Bytes of scratch workspace ra_decode_step needs for these capacities
+ * (score rows, histograms, selection bitmaps, candidate lists and split-K
+ * partials). Returns 0 if the arguments are invalid.
+ */
+size_t ra_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv,
+                                 int32_t max_seq_len, int32_t k_max);
+
+/*
+ * Append one token's key and value per (sequence, KV head): write k_new[b][g]
+ * and v_new[b][g] to slot pos[b] % 64 of page block_table[b][pos[b] / 64].
+ * This is the "decode one new token at a time" step of the slides' setting
+ * frame ("One question: how can decoding read less KV?").
+ *  k_new, v_new: device bf16 [B][H_kv][128].
+ *  pos:          device int32 [B], the new token's position (its sequence's
+ *                length before the append). Positions outside
+ *                [0, 64 * max_pages) are skipped.
+ */
+ra_status ra_kv_append(const ra_kv_layer* kv, const uint16_t* k_new,
+                       const uint16_t* v_new, const int32_t* pos, int32_t B,
+                       hipStream_t stream);
+
+/*
+ * One decode step (see the top of this file for what it computes).
+ *  q:           device bf16 [B][H_q][128], the new token's queries.
+ *  seq_lens:    device int32 [B], lengths N_b after the append, so the recent
+ *               window includes the new token.
+ *  max_seq_len: host capacity >= every N_b; sizes the grids and workspace.
+ *  k:           device int32 [B], per-sequence budget k_b (0 <= k_b <= k_max).
+ *  n_sink, window: sizes of the static set (>= 0).
+ *  out:         device fp32 [B][H_q][128].
+ *  out_lse:     device fp32 [B][H_q] (may be NULL): log-sum-exp of z over
+ *               W u Omega, -inf when that set is empty.
+ *  out_idx:     device int32 [B][H_q][k_max]: Omega in ascending position
+ *               order, then -1 up to k_max (may be NULL only if k_max == 0).
+ *  ws, ws_bytes: device workspace of at least ra_decode_workspace_bytes(B,
+ *               H_q, kv->H_kv, max_seq_len, k_max) bytes, 256-byte aligned;
+ *               no initial contents are required. Calls that share a
+ *               workspace must be ordered on one stream.
+ * An empty W u Omega gives out = 0. Launch count and grid sizes depend only on
+ * the host arguments, so the call can be captured into a HIP graph.
+ */
+ra_status ra_decode_step(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
+                         const int32_t* seq_lens, int32_t B,
+                         int32_t max_seq_len, const int32_t* k, int32_t k_max,
+                         int32_t n_sink, int32_t window, float* out,
+                         float* out_lse, int32_t* out_idx, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The kernels of one decode step, in launch order. ra_decode_step runs
+ * stages RA_STAGE_PREP .. RA_STAGE_MERGE; ra_decode_stages runs a contiguous
+ * sub-range of them with the same arguments, so each kernel can be timed or
+ * inspected on its own. State passes between stages through `ws`, so a range
+ * must start where the previous range on the same workspace ended.
+ */
+typedef enum ra_stage {
+  RA_STAGE_PREP = 0,    /* clear histograms and counters, sequence offsets */
+  RA_STAGE_SCAN = 1,    /* all scores + per-head radix histogram of M */
+  RA_STAGE_FILTER = 2,  /* threshold bucket, sure-set bitmap, candidates */
+  RA_STAGE_RESOLVE = 3, /* exact selection inside the threshold bucket */
+  RA_STAGE_GATHER = 4,  /* out_idx + split-K softmax-V partials */
+  RA_STAGE_MERGE = 5,   /* log-sum-exp merge into out / out_lse, -1 padding */
+  RA_STAGE_COUNT = 6
+} ra_stage;
+
+ra_status ra_decode_stages(const uint16_t* q, int32_t H_q,
+                           const ra_kv_layer* kv, const int32_t* seq_lens,
+                           int32_t B, int32_t max_seq_len, const int32_t* k,
+                           int32_t k_max, int32_t n_sink, int32_t window,
+                           float* out, float* out_lse, int32_t* out_idx,
+                           void* ws, size_t ws_bytes, int32_t first_stage,
+                           int32_t last_stage, hipStream_t stream);
+
+/*
+ * Where the fp32 scores live inside a workspace sized for these capacities:
+ * after RA_STAGE_SCAN, z for (b, h, n) is the float at byte offset
+ * returned + 4 * ((b * H_q + h) * (*row_stride) + n). Returns (size_t)-1 if
+ * the arguments are invalid.
+ */
+size_t ra_workspace_scores_offset(int32_t B, int32_t H_q, int32_t H_kv,
+                                  int32_t max_seq_len, int32_t k_max,
+                                  int64_t* row_stride);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

@@ -1,0 +1,202 @@
+"""ctypes binding of libra.so (include/ra.h): argument marshalling only.
+
+Every step of the decode path runs in the library's HIP kernels. If the
+library has not been built this module raises on import: there is no
+fallback. Tensors are torch tensors on the GPU; they are passed as raw
+pointers, with their dtype, shape, contiguity and alignment checked first.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_int, c_int32, c_int64, c_size_t, c_void_p, c_char_p
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libra.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m top_sparse_attention_gqa_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+RA_OK = 0
+RA_ERR_INVALID_ARGUMENT = 1
+RA_ERR_WORKSPACE = 2
+RA_ERR_UNSUPPORTED = 3
+RA_ERR_HIP = 4
+
+STAGE_PREP, STAGE_SCAN, STAGE_FILTER, STAGE_RESOLVE, STAGE_GATHER, STAGE_MERGE = range(6)
+STAGE_COUNT = 6
+
+HEAD_DIM = 128
+PAGE_SIZE = 64
+
+EXPORTS = ["ra_abi_version", "ra_status_str", "ra_decode_workspace_bytes",
+           "ra_kv_append", "ra_decode_step", "ra_decode_stages",
+           "ra_workspace_scores_offset"]
+
+
+class KVLayerStruct(ctypes.Structure):
+    _fields_ = [("k_pool", c_void_p), ("v_pool", c_void_p), ("block_table", c_void_p),
+                ("num_pages", c_int32), ("max_pages", c_int32), ("H_kv", c_int32),
+                ("head_dim", c_int32), ("page_size", c_int32)]
+
+
+_lib.ra_abi_version.restype = c_int
+_lib.ra_abi_version.argtypes = []
+_lib.ra_status_str.restype = c_char_p
+_lib.ra_status_str.argtypes = [c_int]
+_lib.ra_decode_workspace_bytes.restype = c_size_t
+_lib.ra_decode_workspace_bytes.argtypes = [c_int32] * 5
+_lib.ra_workspace_scores_offset.restype = c_size_t
+_lib.ra_workspace_scores_offset.argtypes = [c_int32] * 5 + [POINTER(c_int64)]
+_lib.ra_kv_append.restype = c_int
+_lib.ra_kv_append.argtypes = [POINTER(KVLayerStruct), c_void_p, c_void_p, c_void_p, c_int32, c_void_p]
+_DECODE_ARGS = [c_void_p, c_int32, POINTER(KVLayerStruct), c_void_p, c_int32, c_int32,
+                c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                c_void_p, c_size_t]
+_lib.ra_decode_step.restype = c_int
+_lib.ra_decode_step.argtypes = _DECODE_ARGS + [c_void_p]
+_lib.ra_decode_stages.restype = c_int
+_lib.ra_decode_stages.argtypes = _DECODE_ARGS + [c_int32, c_int32, c_void_p]
+
+
+class RAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)}")
+
+
+def abi_version() -> int:
+    return _lib.ra_abi_version()
+
+
+def status_str(status: int) -> str:
+    return _lib.ra_status_str(status).decode()
+
+
+def decode_workspace_bytes(B: int, H_q: int, H_kv: int, max_seq_len: int, k_max: int) -> int:
+    return int(_lib.ra_decode_workspace_bytes(B, H_q, H_kv, max_seq_len, k_max))
+
+
+def workspace_scores_offset(B, H_q, H_kv, max_seq_len, k_max):
+    """(byte offset, row stride in floats) of the score rows inside a workspace."""
+    stride = c_int64(0)
+    off = _lib.ra_workspace_scores_offset(B, H_q, H_kv, max_seq_len, k_max, ctypes.byref(stride))
+    if off == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid capacities")
+    return int(off), int(stride.value)
+
+
+def _ptr(t, dtype, name, nullable=False):
+    if t is None:
+        if nullable:
+            return None
+        raise ValueError(f"{name} is required")
+    if isinstance(t, int):  # raw device address
+        return t
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name} must be 16-byte aligned")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class KVLayer:
+    """One layer's paged KV cache: bf16 pools [num_pages][H_kv][64][128] and
+    an int32 block table [B][max_pages]."""
+
+    def __init__(self, k_pool, v_pool, block_table):
+        for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+            if t.dim() != 4 or t.shape[2] != PAGE_SIZE or t.shape[3] != HEAD_DIM:
+                raise ValueError(f"{n} must be [num_pages][H_kv][64][128]")
+        if k_pool.shape != v_pool.shape:
+            raise ValueError("k_pool and v_pool shapes differ")
+        if block_table.dim() != 2:
+            raise ValueError("block_table must be [B][max_pages]")
+        self.k_pool, self.v_pool, self.block_table = k_pool, v_pool, block_table
+        self.struct = KVLayerStruct(
+            _ptr(k_pool, torch.bfloat16, "k_pool"), _ptr(v_pool, torch.bfloat16, "v_pool"),
+            _ptr(block_table, torch.int32, "block_table"), k_pool.shape[0],
+            block_table.shape[1], k_pool.shape[1], HEAD_DIM, PAGE_SIZE)
+
+    @property
+    def H_kv(self) -> int:
+        return self.k_pool.shape[1]
+
+
+def alloc_workspace(B, H_q, H_kv, max_seq_len, k_max, device="cuda") -> torch.Tensor:
+    n = decode_workspace_bytes(B, H_q, H_kv, max_seq_len, k_max)
+    if n == 0:
+        raise ValueError("invalid capacities")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def kv_append(kv: KVLayer, k_new, v_new, pos, stream=None) -> None:
+    """ra_kv_append: write one token's K/V rows ([B][H_kv][128] bf16) at
+    positions pos ([B] int32)."""
+    B = pos.shape[0]
+    st = _lib.ra_kv_append(ctypes.byref(kv.struct), _ptr(k_new, torch.bfloat16, "k_new"),
+                           _ptr(v_new, torch.bfloat16, "v_new"), _ptr(pos, torch.int32, "pos"),
+                           B, _stream(stream))
+    if st != RA_OK:
+        raise RAError(st, "ra_kv_append")
+
+
+def decode_stages(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, window,
+                  out, out_lse, out_idx, ws, first=STAGE_PREP, last=STAGE_MERGE,
+                  stream=None) -> None:
+    """ra_decode_stages (ra_decode_step when first..last covers every stage)."""
+    B, H_q = q.shape[0], q.shape[1]
+    st = _lib.ra_decode_stages(
+        _ptr(q, torch.bfloat16, "q"), H_q, ctypes.byref(kv.struct),
+        _ptr(seq_lens, torch.int32, "seq_lens"), B, max_seq_len, _ptr(k, torch.int32, "k"),
+        k_max, n_sink, window, _ptr(out, torch.float32, "out"),
+        _ptr(out_lse, torch.float32, "out_lse", nullable=True),
+        _ptr(out_idx, torch.int32, "out_idx", nullable=(k_max == 0)),
+        _ptr(ws, torch.uint8, "ws"), ws.numel() if not isinstance(ws, int) else 0,
+        first, last, _stream(stream))
+    if st != RA_OK:
+        raise RAError(st, "ra_decode_stages")
+
+
+def decode_step(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, window,
+                out, out_lse, out_idx, ws, stream=None) -> None:
+    """ra_decode_step: one exact top-k sparse GQA decode step."""
+    B, H_q = q.shape[0], q.shape[1]
+    st = _lib.ra_decode_step(
+        _ptr(q, torch.bfloat16, "q"), H_q, ctypes.byref(kv.struct),
+        _ptr(seq_lens, torch.int32, "seq_lens"), B, max_seq_len, _ptr(k, torch.int32, "k"),
+        k_max, n_sink, window, _ptr(out, torch.float32, "out"),
+        _ptr(out_lse, torch.float32, "out_lse", nullable=True),
+        _ptr(out_idx, torch.int32, "out_idx", nullable=(k_max == 0)),
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream))
+    if st != RA_OK:
+        raise RAError(st, "ra_decode_step")
+
+
+def scores_view(ws: torch.Tensor, B, H_q, H_kv, max_seq_len, k_max) -> torch.Tensor:
+    """The fp32 score rows [B][H_q][row_stride] inside a workspace (valid
+    after the scan stage)."""
+    off, stride = workspace_scores_offset(B, H_q, H_kv, max_seq_len, k_max)
+    n = B * H_q * stride
+    return ws[off:off + 4 * n].view(torch.float32).view(B, H_q, stride)
+
+
+raw = _lib  # the C entry points, for tests that pass raw pointers

@@ -1,0 +1,227 @@
+// Host side of the C ABI: argument validation (pure host code, no HIP call
+// before it passes), workspace carving and the launch sequence of one decode
+// step. Every kernel is enqueued on the caller's stream; nothing here
+// allocates, synchronises or reads device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "ra.h"
+#include "ra_internal.h"
+
+namespace ra {
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool ws_layout(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seq_len,
+               int32_t k_max, WsLayout* L) {
+  if (B <= 0 || B > RA_MAX_BATCH || H_q <= 0 || H_kv <= 0 || H_q % H_kv != 0)
+    return false;
+  if (max_seq_len <= 0 || max_seq_len > RA_MAX_SEQ_LEN || k_max < 0)
+    return false;
+  const int64_t heads = int64_t(B) * H_q;
+  if (heads > 65535) return false;  // grid y limit of the per-head kernels
+  L->n_cap = (int64_t(max_seq_len) + kTile - 1) / kTile * kTile;
+  L->n_tiles = int32_t(L->n_cap / kTile);
+  L->cap = int32_t(std::min<int64_t>(kCandCapMax, L->n_cap));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L->off_scores = take(size_t(heads) * L->n_cap * sizeof(float));
+  L->off_hist = take(size_t(heads) * kHistStride * sizeof(uint32_t));
+  L->off_state = take(size_t(heads) * sizeof(HeadState));
+  L->off_seqoff = take(size_t(B + 1) * sizeof(int64_t));
+  L->off_tilecnt = take(size_t(heads) * L->n_tiles * sizeof(uint32_t));
+  L->off_bitmap = take(size_t(heads) * (L->n_cap / 64) * sizeof(uint64_t));
+  L->off_cand = take(size_t(heads) * L->cap * sizeof(uint64_t));
+  L->off_part_mz = take(size_t(heads) * L->n_tiles * 2 * sizeof(float));
+  L->off_part_n = take(size_t(heads) * L->n_tiles * kHeadDim * sizeof(float));
+  L->total = off;
+  return true;
+}
+
+static int cu_count() {
+  // CU count per device, read once.
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> g(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+static ra_status check_kv(const ra_kv_layer* kv) {
+  if (!kv || !kv->k_pool || !kv->v_pool || !kv->block_table)
+    return RA_ERR_INVALID_ARGUMENT;
+  if (kv->num_pages <= 0 || kv->max_pages <= 0 || kv->H_kv <= 0)
+    return RA_ERR_INVALID_ARGUMENT;
+  if (kv->head_dim != RA_HEAD_DIM || kv->page_size != RA_PAGE_SIZE)
+    return RA_ERR_UNSUPPORTED;
+  return RA_OK;
+}
+
+static ra_status validate_decode(const uint16_t* q, int32_t H_q,
+                                 const ra_kv_layer* kv, const int32_t* seq_lens,
+                                 int32_t B, int32_t max_seq_len,
+                                 const int32_t* k, int32_t k_max,
+                                 int32_t n_sink, int32_t window, float* out,
+                                 int32_t* out_idx, void* ws, size_t ws_bytes,
+                                 WsLayout* L) {
+  ra_status st = check_kv(kv);
+  if (st != RA_OK) return st;
+  if (!q || !seq_lens || !k || !out || !ws) return RA_ERR_INVALID_ARGUMENT;
+  if (k_max > 0 && !out_idx) return RA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || B > RA_MAX_BATCH || H_q <= 0 || max_seq_len <= 0 ||
+      max_seq_len > RA_MAX_SEQ_LEN || k_max < 0 || n_sink < 0 || window < 0)
+    return RA_ERR_INVALID_ARGUMENT;
+  if (H_q % kv->H_kv != 0) return RA_ERR_INVALID_ARGUMENT;
+  const int G = H_q / kv->H_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return RA_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return RA_ERR_INVALID_ARGUMENT;
+  if (!ws_layout(B, H_q, kv->H_kv, max_seq_len, k_max, L))
+    return RA_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < L->total) return RA_ERR_WORKSPACE;
+  return RA_OK;
+}
+
+static Params make_params(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
+                          const int32_t* seq_lens, int32_t B,
+                          int32_t max_seq_len, const int32_t* k, int32_t k_max,
+                          int32_t n_sink, int32_t window, float* out,
+                          float* out_lse, int32_t* out_idx, void* ws,
+                          const WsLayout& L) {
+  Params p{};
+  char* base = static_cast<char*>(ws);
+  p.q = q;
+  p.k_pool = kv->k_pool;
+  p.v_pool = kv->v_pool;
+  p.block_table = kv->block_table;
+  p.seq_lens = seq_lens;
+  p.kk = k;
+  p.out = out;
+  p.lse = out_lse;
+  p.out_idx = out_idx;
+  p.B = B;
+  p.H_q = H_q;
+  p.H_kv = kv->H_kv;
+  p.G = H_q / kv->H_kv;
+  p.max_pages = kv->max_pages;
+  p.num_pages = kv->num_pages;
+  p.max_seq_len = max_seq_len;
+  p.k_max = k_max;
+  p.n_sink = n_sink;
+  p.window = window;
+  p.scores = reinterpret_cast<float*>(base + L.off_scores);
+  p.hist = reinterpret_cast<uint32_t*>(base + L.off_hist);
+  p.state = reinterpret_cast<HeadState*>(base + L.off_state);
+  p.seq_off = reinterpret_cast<int64_t*>(base + L.off_seqoff);
+  p.tile_cnt = reinterpret_cast<uint32_t*>(base + L.off_tilecnt);
+  p.bitmap = reinterpret_cast<uint64_t*>(base + L.off_bitmap);
+  p.cand = reinterpret_cast<uint64_t*>(base + L.off_cand);
+  p.part_mz = reinterpret_cast<float*>(base + L.off_part_mz);
+  p.part_n = reinterpret_cast<float*>(base + L.off_part_n);
+  p.n_cap = L.n_cap;
+  p.n_tiles = L.n_tiles;
+  p.cap = L.cap;
+  return p;
+}
+
+}  // namespace ra
+
+using namespace ra;
+
+extern "C" {
+
+int ra_abi_version(void) { return RA_ABI_VERSION; }
+
+const char* ra_status_str(ra_status s) {
+  switch (s) {
+    case RA_OK: return "RA_OK";
+    case RA_ERR_INVALID_ARGUMENT: return "RA_ERR_INVALID_ARGUMENT";
+    case RA_ERR_WORKSPACE: return "RA_ERR_WORKSPACE";
+    case RA_ERR_UNSUPPORTED: return "RA_ERR_UNSUPPORTED";
+    case RA_ERR_HIP: return "RA_ERR_HIP";
+  }
+  return "RA_ERR_UNKNOWN";
+}
+
+size_t ra_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv,
+                                 int32_t max_seq_len, int32_t k_max) {
+  WsLayout L;
+  if (!ws_layout(B, H_q, H_kv, max_seq_len, k_max, &L)) return 0;
+  return L.total;
+}
+
+size_t ra_workspace_scores_offset(int32_t B, int32_t H_q, int32_t H_kv,
+                                  int32_t max_seq_len, int32_t k_max,
+                                  int64_t* row_stride) {
+  WsLayout L;
+  if (!ws_layout(B, H_q, H_kv, max_seq_len, k_max, &L)) return size_t(-1);
+  if (row_stride) *row_stride = L.n_cap;
+  return L.off_scores;
+}
+
+ra_status ra_kv_append(const ra_kv_layer* kv, const uint16_t* k_new,
+                       const uint16_t* v_new, const int32_t* pos, int32_t B,
+                       hipStream_t stream) {
+  ra_status st = check_kv(kv);
+  if (st != RA_OK) return st;
+  if (!k_new || !v_new || !pos || B <= 0 || B > RA_MAX_BATCH)
+    return RA_ERR_INVALID_ARGUMENT;
+  if (launch_kv_append(*kv, k_new, v_new, pos, B, stream) != hipSuccess)
+    return RA_ERR_HIP;
+  return RA_OK;
+}
+
+ra_status ra_decode_stages(const uint16_t* q, int32_t H_q,
+                           const ra_kv_layer* kv, const int32_t* seq_lens,
+                           int32_t B, int32_t max_seq_len, const int32_t* k,
+                           int32_t k_max, int32_t n_sink, int32_t window,
+                           float* out, float* out_lse, int32_t* out_idx,
+                           void* ws, size_t ws_bytes, int32_t first_stage,
+                           int32_t last_stage, hipStream_t stream) {
+  WsLayout L;
+  ra_status st = validate_decode(q, H_q, kv, seq_lens, B, max_seq_len, k,
+                                 k_max, n_sink, window, out, out_idx, ws,
+                                 ws_bytes, &L);
+  if (st != RA_OK) return st;
+  if (first_stage < 0 || last_stage >= RA_STAGE_COUNT ||
+      first_stage > last_stage)
+    return RA_ERR_INVALID_ARGUMENT;
+  Params p = make_params(q, H_q, kv, seq_lens, B, max_seq_len, k, k_max,
+                         n_sink, window, out, out_lse, out_idx, ws, L);
+  p.num_cus = cu_count();
+  using Launcher = hipError_t (*)(const Params&, hipStream_t);
+  static const Launcher stages[RA_STAGE_COUNT] = {
+      launch_prep,    launch_scan,   launch_filter,
+      launch_resolve, launch_gather, launch_merge};
+  for (int s = first_stage; s <= last_stage; ++s) {
+    if (stages[s](p, stream) != hipSuccess) return RA_ERR_HIP;
+  }
+  return RA_OK;
+}
+
+ra_status ra_decode_step(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
+                         const int32_t* seq_lens, int32_t B,
+                         int32_t max_seq_len, const int32_t* k, int32_t k_max,
+                         int32_t n_sink, int32_t window, float* out,
+                         float* out_lse, int32_t* out_idx, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  return ra_decode_stages(q, H_q, kv, seq_lens, B, max_seq_len, k, k_max,
+                          n_sink, window, out, out_lse, out_idx, ws, ws_bytes,
+                          RA_STAGE_PREP, RA_STAGE_MERGE, stream);
+}
+
+}  // extern "C"
