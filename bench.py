@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of one exact top-k sparse GQA decode step on one MI355X.
+
+Default workload: one Llama-3-8B layer (H_q=32, H_kv=8, d=128, bf16 KV) at
+N = 1,048,576 cached tokens with k = 1 % of N (10,485) retrieved keys per
+query head and the static set n_sink=128 + window=512; seeded synthetic
+inputs (OOD queries vs keys, 64 planted needles per query head, x4 sink
+keys). Inputs are resident in HBM before timing starts.
+
+One step = every kernel of ra_decode_step (prep, scan, filter, resolve,
+gather, merge), launched stage by stage through ra_decode_stages with HIP
+events between the stages, so the scan kernel's own duration is measured
+in the timed region. Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload C3_1] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-step latency (ms) + KV GB/s vs HBM peak, Llama-3-8B layer @128K/1M"
+HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E peak
+SCAN_SRC = os.path.join(ROOT, "top_sparse_attention_gqa_amd", "csrc", "score_scan.hip")
+
+WORKLOAD_TEXT = {
+    "C1": "tiny decode step: H_q=4, H_kv=1, N=4096, k=64, n_sink=16, window=64",
+    "C2": "Llama-3-8B layer: H_q=32, H_kv=8, d=128, N=131072, k=2048, n_sink=128, window=512",
+    "C3_1": "Llama-3-8B layer: H_q=32, H_kv=8, d=128, N=1048576, k=1% (10485), n_sink=128, window=512",
+    "C3_2": "Llama-3-8B layer: H_q=32, H_kv=8, d=128, N=1048576, k=2% (20971), n_sink=128, window=512",
+    "C3_3": "Llama-3-8B layer: H_q=32, H_kv=8, d=128, N=1048576, k=3% (31457), n_sink=128, window=512",
+    "C4": "16 ragged sequences (N uniform in [32768, 131072]) of a Llama-3-8B layer, 64-token pages in shuffled order, k=2% of each length",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="C3_1", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def make_inputs(name: str, device: str):
+    import synth
+
+    c = synth.config(name)
+    lens = list(c.seq_lens) if c.seq_lens else synth.draw_lengths(c.B, *c.len_range, c.seed)
+    ks = [c.k_for(n) for n in lens]
+    kbytes = sum(lens) * c.H_kv * 256
+    # below 1 GiB of keys, rotate independent copies so the 256 MB last-level
+    # cache cannot serve K from one step to the next
+    copies = 1 if kbytes >= (1 << 30) else min(4, -(-(1 << 30) // kbytes))
+    layers = [synth.make_layer(c.H_q, c.H_kv, lens, ks, c.n_sink, c.window,
+                               c.needles_per_head, c.seed + 1000 * i, device,
+                               shuffle_pages=c.shuffle_pages) for i in range(copies)]
+    return c, lens, ks, layers
+
+
+def algorithmic_bytes(c, lens, ks, idx_np, n_sink, window):
+    """K for every cached token, V rows over the per-group union of the
+    retrieved and static sets, plus q, out, lse and out_idx."""
+    import numpy as np
+
+    G = c.H_q // c.H_kv
+    kb = sum(lens) * c.H_kv * 256
+    vrows = 0
+    for b, n in enumerate(lens):
+        W = np.union1d(np.arange(min(n_sink, n)), np.arange(max(n - window, 0), n))
+        for g in range(c.H_kv):
+            sel = idx_np[b, g * G:(g + 1) * G].ravel()
+            vrows += np.union1d(sel[sel >= 0], W).size
+    B = len(lens)
+    small = B * c.H_q * (256 + 512 + 4) + B * c.H_q * max(ks) * 4
+    return kb, vrows * 256, small
+
+
+def traffic_from_profile(scan_bytes_per_launch):
+    """HBM bytes per scan launch from the committed rocprofv3 counter summary,
+    scaled by the copy-kernel calibration; None if absent or if the scan
+    kernel's source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "score_scan_C3_1_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        sha = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
+        if d.get("source_sha256") != sha:
+            return None
+        cal = d["copy_calibration"]
+        f_scale = cal["bytes_read"] / (cal["fetch_kib"] * 1024.0)
+        w_scale = cal["bytes_written"] / (cal["write_kib"] * 1024.0)
+        return d["fetch_kib_per_dispatch"] * 1024.0 * f_scale + \
+            d["write_kib_per_dispatch"] * 1024.0 * w_scale
+    except (KeyError, ValueError, ZeroDivisionError, OSError):
+        return None
+
+
+def cpu_baseline(c, L, lens, ks, budget_s=12.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same
+    workload and scale it to ms per full decode step."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = len(os.sched_getaffinity(0))
+    G = c.H_q // c.H_kv
+    b = 0
+    n = lens[b]
+    q_all = synth.bf16_bits(L.q[b])
+    spent = 0.0
+    groups = 0
+    for g in range(c.H_kv):
+        K = synth.depage(L.k_pool, L.block_table, b, n, heads=[g])
+        V = synth.depage(L.v_pool, L.block_table, b, n, heads=[g])
+        t = time.perf_counter()
+        oracle.decode(q_all[g * G:(g + 1) * G], K, V, ks[b], c.n_sink, c.window)
+        spent += time.perf_counter() - t
+        groups += 1
+        del K, V
+        if spent >= budget_s:
+            break
+    per_seq_groups = c.H_kv * len(lens)
+    scale = per_seq_groups / groups * (np.mean(lens) / n)
+    return {
+        "value": round(spent / groups * per_seq_groups * (np.mean(lens) / n) * 1e3, 3),
+        "unit": "ms",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle (scores, exact top-k, sparse attention) on {groups} of "
+                   f"{c.H_kv} KV groups ({groups * G} query heads) of sequence 0 "
+                   f"(N={n}), {spent:.1f} s of CPU time, scaled x{scale:.2f} to one "
+                   f"full decode step"),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import top_sparse_attention_gqa_amd as ra
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = "cuda"
+    c, lens, ks, layers = make_inputs(args.workload, dev)
+    B, H_q, H_kv = len(lens), c.H_q, c.H_kv
+    max_seq_len = max(lens)
+    k_max = max(ks)
+    seq = torch.tensor(lens, dtype=torch.int32, device=dev)
+    kt = torch.tensor(ks, dtype=torch.int32, device=dev)
+    out = torch.empty(B, H_q, 128, device=dev)
+    lse = torch.empty(B, H_q, device=dev)
+    idx = torch.empty(B, H_q, k_max, dtype=torch.int32, device=dev)
+    ws = ra.alloc_workspace(B, H_q, H_kv, max_seq_len, k_max, device=dev)
+    kvs = [ra.KVLayer(L.k_pool, L.v_pool, L.block_table) for L in layers]
+    n_stage = ra._lib.STAGE_COUNT
+
+    def step(i, ev=None):
+        L = layers[i % len(layers)]
+        kv = kvs[i % len(layers)]
+        if ev is None:
+            ra.decode_step(L.q, kv, seq, max_seq_len, kt, k_max, c.n_sink, c.window,
+                           out, lse, idx, ws)
+            return
+        ev[0].record()
+        for s in range(n_stage):
+            ra.decode_stages(L.q, kv, seq, max_seq_len, kt, k_max, c.n_sink, c.window,
+                             out, lse, idx, ws, s, s)
+            ev[s + 1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_stage + 1)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = list(ra.STAGE_NAMES)
+    stage_ms = np.array([[e[s].elapsed_time(e[s + 1]) for s in range(n_stage)] for e in events])
+    step_gpu_ms = np.array([e[0].elapsed_time(e[n_stage]) for e in events])
+    ms_per_step = wall * 1e3 / args.steps
+
+    # algorithmic bytes from the retrieved sets of copy 0
+    step(0)
+    torch.cuda.synchronize()
+    kb, vb, small = algorithmic_bytes(c, lens, ks, idx.cpu().numpy(), c.n_sink, c.window)
+    step_bytes = kb + vb + small
+    scan_bytes = kb + B * H_q * 256
+    scan_s = float(stage_ms[:, ra.STAGE_SCAN].mean()) * 1e-3
+    achieved = scan_bytes / scan_s / 1e9
+    traffic = traffic_from_profile(scan_bytes)
+
+    if args.copy_calib_mib:
+        a = torch.empty(args.copy_calib_mib << 20, dtype=torch.uint8, device=dev)
+        bcopy = torch.empty_like(a)
+        for _ in range(3):
+            bcopy.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(c, layers[0], lens, ks)
+
+    line = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: OOD q vs K, 64 planted needles per query head, x4 sink keys)",
+        "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
+                   "B": B, "H_q": H_q, "H_kv": H_kv, "head_dim": 128,
+                   "seq_len": max_seq_len, "k": k_max, "n_sink": c.n_sink,
+                   "window": c.window, "kv_copies_rotated": len(layers),
+                   "accumulate": "fp32"},
+        "kv_tokens_per_s": round(sum(lens) / (ms_per_step * 1e-3), 1),
+        "step_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_gpu_ms_median": round(float(np.median(step_gpu_ms)), 4),
+        "algorithmic_bytes": {"K": kb, "V": vb, "q_out_idx": small, "step": step_bytes},
+        "kernels_us": {n: round(float(stage_ms[:, i].mean()) * 1e3, 2) for i, n in enumerate(names)},
+        "roofline": {"kernel": "scan_kernel (score scan + candidate staging)",
+                     "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None if traffic is None else int(round(traffic)),
+                     "algorithmic_bytes_per_launch": scan_bytes,
+                     "avg_launch_us": round(scan_s * 1e6, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -142,13 +142,15 @@ ra_status ra_decode_step(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
  * must start where the previous range on the same workspace ended.
  */
 typedef enum ra_stage {
-  RA_STAGE_PREP = 0,    /* clear histograms and counters, sequence offsets */
-  RA_STAGE_SCAN = 1,    /* all scores + per-head radix histogram of M */
-  RA_STAGE_FILTER = 2,  /* threshold bucket, sure-set bitmap, candidates */
-  RA_STAGE_RESOLVE = 3, /* exact selection inside the threshold bucket */
-  RA_STAGE_GATHER = 4,  /* out_idx + split-K softmax-V partials */
-  RA_STAGE_MERGE = 5,   /* log-sum-exp merge into out / out_lse, -1 padding */
-  RA_STAGE_COUNT = 6
+  RA_STAGE_PREP = 0,   /* clear histograms and counters, sequence offsets */
+  RA_STAGE_SAMPLE = 1, /* score a sample of pages: per-head candidate threshold */
+  RA_STAGE_SCAN = 2,   /* all scores; keep W and the candidates above it */
+  RA_STAGE_SELECT = 3, /* exact top-k among the candidates, ties to lower n */
+  RA_STAGE_DENSE = 4,  /* exact top-k over every score, only for heads the
+                          sample could not decide (no work otherwise) */
+  RA_STAGE_GATHER = 5, /* out_idx + split-K softmax-V partials */
+  RA_STAGE_MERGE = 6,  /* log-sum-exp merge into out / out_lse, -1 padding */
+  RA_STAGE_COUNT = 7
 } ra_stage;
 
 ra_status ra_decode_stages(const uint16_t* q, int32_t H_q,
@@ -160,9 +162,11 @@ ra_status ra_decode_stages(const uint16_t* q, int32_t H_q,
                            int32_t last_stage, hipStream_t stream);
 
 /*
- * Where the fp32 scores live inside a workspace sized for these capacities:
- * after RA_STAGE_SCAN, z for (b, h, n) is the float at byte offset
- * returned + 4 * ((b * H_q + h) * (*row_stride) + n). Returns (size_t)-1 if
+ * Where the fp32 score rows live inside a workspace sized for these
+ * capacities: z for (b, h, n) is the float at byte offset
+ * returned + 4 * ((b * H_q + h) * (*row_stride) + n). After RA_STAGE_SELECT
+ * it holds the positions of W and of the retrieved set (after RA_STAGE_DENSE,
+ * every position of a head that took the dense path). Returns (size_t)-1 if
  * the arguments are invalid.
  */
 size_t ra_workspace_scores_offset(int32_t B, int32_t H_q, int32_t H_kv,

@@ -11,10 +11,12 @@ Distribution (the workloads' description, read plainly):
 * values V ~ N(0, 1).
 * Needles: positions drawn uniformly without replacement from the
   selection domain (outside the sink prefix and the recent window), each
-  owned by one query head h. The needle's key gets (6 / |q_h|) q_h added.
-  Over keys drawn as above, q_h . k / sqrt(d) has standard deviation
-  sigma_h = |q_h| / sqrt(d), so the addition lifts that key's score by exactly
-  6 sigma_h; no score is computed here, only the norm |q_h|.
+  owned by one query head h. A needle key is aligned to its query:
+  0.5 u + 0.1 x + (6 / |q_h|) q_h, where x is the N(0, 1) draw the key had.
+  Over keys drawn as above, q_h . k / sqrt(d) has mean mu_h = 0.5 q_h . u /
+  sqrt(d) and standard deviation sigma_h = |q_h| / sqrt(d), so the needle
+  scores mu_h + 6 sigma_h up to a tenth of sigma_h of noise. No score is
+  computed here, only the norm |q_h|.
 * Sinks: the keys at positions 0..3 are multiplied by 4, after the offset
   and the needles.
 * Everything is drawn in fp32 and rounded to bf16 (round to nearest even)
@@ -135,7 +137,8 @@ def make_layer(H_q: int, H_kv: int, seq_lens, ks, n_sink: int, window: int,
                 if bool(sel.any()):
                     npos = nd[sel, 0] - t0
                     nh = nd[sel, 1]
-                    kc[npos, nh // G] += coef[nh, None] * q32[b, nh]
+                    noise = kc[npos, nh // G] - 0.5 * u
+                    kc[npos, nh // G] = 0.5 * u + 0.1 * noise + coef[nh, None] * q32[b, nh]
             if t0 == 0 and sink_tokens > 0:
                 kc[:min(sink_tokens, t1)] *= sink_scale
             _store(k_pool, table_dev[b], t0, kc, tail_fill)
@@ -186,13 +189,17 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def depage(pool: torch.Tensor, block_table: torch.Tensor, b: int, N: int,
-           t0: int = 0, t1: int | None = None) -> np.ndarray:
+           t0: int = 0, t1: int | None = None, heads=None) -> np.ndarray:
     """Logical rows [t0, t1) of sequence b from a paged pool, as raw bf16
-    bits: host uint16 [t1 - t0][H_kv][128]. Pure data movement."""
+    bits: host uint16 [t1 - t0][H_kv][128] (or only the KV heads listed in
+    ``heads``). Pure data movement."""
     t1 = N if t1 is None else t1
     p0, p1 = t0 // PAGE, -(-t1 // PAGE)
     ids = block_table[b, p0:p1].long().to(pool.device)
-    x = pool[ids].permute(0, 2, 1, 3).reshape((p1 - p0) * PAGE, pool.shape[1], pool.shape[3])
+    x = pool[ids]
+    if heads is not None:
+        x = x[:, list(heads)]
+    x = x.permute(0, 2, 1, 3).reshape((p1 - p0) * PAGE, x.shape[1], pool.shape[3])
     x = x[t0 - p0 * PAGE: t1 - p0 * PAGE]
     return bf16_bits(x)
 

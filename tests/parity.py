@@ -62,16 +62,10 @@ def gpu_decode(L: synth.LayerInputs, max_seq_len: int | None = None, k_max: int 
     idx = torch.full((B, H_q, max(k_max, 1)), -7, dtype=torch.int32, device=dev)
     ws = ra.alloc_workspace(B, H_q, L.H_kv, max_seq_len, k_max, device=dev)
     ws.fill_(0xA5)  # no initial contents are required
-    if with_scores:
-        ra.decode_stages(L.q, kv, seq, max_seq_len, kt, k_max, n_sink, window, out, lse,
-                         idx if k_max else None, ws, ra.STAGE_PREP, ra.STAGE_SCAN)
-        sc = ra.scores_view(ws, B, H_q, L.H_kv, max_seq_len, k_max).clone()
-        ra.decode_stages(L.q, kv, seq, max_seq_len, kt, k_max, n_sink, window, out, lse,
-                         idx if k_max else None, ws, ra.STAGE_FILTER, ra.STAGE_MERGE)
-    else:
-        ra.decode_step(L.q, kv, seq, max_seq_len, kt, k_max, n_sink, window, out, lse,
-                       idx if k_max else None, ws)
-        sc = None
+    ra.decode_step(L.q, kv, seq, max_seq_len, kt, k_max, n_sink, window, out, lse,
+                   idx if k_max else None, ws)
+    # the score rows hold W and the retrieved positions after the step
+    sc = ra.scores_view(ws, B, H_q, L.H_kv, max_seq_len, k_max).clone() if with_scores else None
     torch.cuda.synchronize()
     return Run(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
                idx.cpu().numpy()[:, :, :k_max],
@@ -98,10 +92,13 @@ def score_bound(q_bits, K_bits) -> np.ndarray:
     return s
 
 
-def check_scores(z_gpu_row, z64, bound) -> None:
-    n = z64.shape[-1]
-    err = np.abs(z_gpu_row[..., :n].astype(np.float64) - z64)
-    lim = gamma(130) * bound + 2.0 ** -23 * np.abs(z64)
+def check_scores(z_gpu_row, z64, bound, positions) -> None:
+    """Scores the GPU kept (W and the retrieved set) within the fp32 bound."""
+    pos = np.asarray(positions, dtype=np.int64)
+    if pos.size == 0:
+        return
+    err = np.abs(z_gpu_row[pos].astype(np.float64) - z64[pos])
+    lim = gamma(130) * bound[pos] + 2.0 ** -23 * np.abs(z64[pos])
     bad = err > lim
     assert not bad.any(), f"{bad.sum()} scores outside the fp32 bound, worst {err.max():.3e}"
 
@@ -160,9 +157,11 @@ def compare_sequence(L: synth.LayerInputs, run: Run, b: int, heads=None, ks=None
     eps = gamma(130) * bound.max(axis=1)
     band_diffs = 0
     for i, h in enumerate(heads):
-        if run.scores is not None and check_score_rows:
-            check_scores(run.scores[b, h], res["z"][i], bound[i])
         band_diffs += check_indices(run.idx[b, h], res, i, k, eps[i])
+        if run.scores is not None and check_score_rows:
+            sel = run.idx[b, h]
+            check_scores(run.scores[b, h], res["z"][i], bound[i],
+                         np.union1d(res["W"], sel[sel >= 0]))
         check_out(run.out[b, h], res["out"][i], f"out[b={b},h={h}]")
         check_out(np.array([run.lse[b, h]]), np.array([res["lse"][i]]), f"lse[b={b},h={h}]")
     return {"band_diffs": band_diffs, "res": res}

@@ -125,7 +125,7 @@ def test_stage_range_validation():
     args = [FAKE, 4, ctypes.byref(kv), FAKE, 1, 640, FAKE, 8, 4, 8, FAKE, None, FAKE, FAKE, 1 << 40]
     assert _lib.raw.ra_decode_stages(*args, 3, 2, None) == ra.RA_ERR_INVALID_ARGUMENT
     assert _lib.raw.ra_decode_stages(*args, -1, 2, None) == ra.RA_ERR_INVALID_ARGUMENT
-    assert _lib.raw.ra_decode_stages(*args, 0, 6, None) == ra.RA_ERR_INVALID_ARGUMENT
+    assert _lib.raw.ra_decode_stages(*args, 0, 7, None) == ra.RA_ERR_INVALID_ARGUMENT
 
 
 def test_kv_append_validation():

@@ -135,6 +135,21 @@ def test_constant_keys_rescan_path():
         assert run.idx[0, h].tolist() == list(range(16, 16 + 5000))
 
 
+def test_misleading_sample_takes_the_dense_path():
+    # keys aligned with every query only on the sampled pages (one page in 4
+    # at N = 32768): the sample sees mostly high scores, so its threshold
+    # leaves fewer than k candidates and the head is decided on the dense path
+    say("case sample_misled: N=32768, high keys on sampled pages only, k=9000")
+    L = layer(4, 1, [32768], [9000], 16, 64)
+    qdir = L.q[0].float().sum(0)
+    qdir = qdir / qdir.norm()
+    for j in range(2, 512, 4):
+        pg = int(L.block_table[0, j])
+        L.k_pool[pg, 0] = (L.k_pool[pg, 0].float() + 3.0 * qdir).to(torch.bfloat16)
+    run = gpu_decode(L, with_scores=True)
+    compare_sequence(L, run, 0)
+
+
 def test_integer_scores_with_many_ties():
     say("case ternary: integer-valued dot products, N=12000")
     L = layer(8, 2, [12000], [700], 16, 64)

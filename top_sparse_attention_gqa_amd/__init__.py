@@ -16,12 +16,15 @@ from ._lib import (  # noqa: F401
     RA_ERR_UNSUPPORTED,
     RA_ERR_WORKSPACE,
     RA_OK,
-    STAGE_FILTER,
+    STAGE_COUNT,
+    STAGE_DENSE,
     STAGE_GATHER,
     STAGE_MERGE,
+    STAGE_NAMES,
     STAGE_PREP,
-    STAGE_RESOLVE,
+    STAGE_SAMPLE,
     STAGE_SCAN,
+    STAGE_SELECT,
     KVLayer,
     KVLayerStruct,
     RAError,

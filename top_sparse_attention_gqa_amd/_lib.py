@@ -29,8 +29,10 @@ RA_ERR_WORKSPACE = 2
 RA_ERR_UNSUPPORTED = 3
 RA_ERR_HIP = 4
 
-STAGE_PREP, STAGE_SCAN, STAGE_FILTER, STAGE_RESOLVE, STAGE_GATHER, STAGE_MERGE = range(6)
-STAGE_COUNT = 6
+(STAGE_PREP, STAGE_SAMPLE, STAGE_SCAN, STAGE_SELECT, STAGE_DENSE, STAGE_GATHER,
+ STAGE_MERGE) = range(7)
+STAGE_COUNT = 7
+STAGE_NAMES = ["prep", "sample", "scan", "select", "dense", "gather", "merge"]
 
 HEAD_DIM = 128
 PAGE_SIZE = 64
@@ -192,8 +194,9 @@ def decode_step(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, window,
 
 
 def scores_view(ws: torch.Tensor, B, H_q, H_kv, max_seq_len, k_max) -> torch.Tensor:
-    """The fp32 score rows [B][H_q][row_stride] inside a workspace (valid
-    after the scan stage)."""
+    """The fp32 score rows [B][H_q][row_stride] inside a workspace: W and
+    the retrieved positions after the select stage (every position of a head
+    that took the dense path)."""
     off, stride = workspace_scores_offset(B, H_q, H_kv, max_seq_len, k_max)
     n = B * H_q * stride
     return ws[off:off + 4 * n].view(torch.float32).view(B, H_q, stride)

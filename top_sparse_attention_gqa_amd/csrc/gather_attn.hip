@@ -33,6 +33,14 @@ __device__ __forceinline__ uint64_t range_mask(int nw, int a, int c) {
 __device__ __forceinline__ float bf16lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
 
+// Exclusive prefix over the block of per-head popcounts packed four heads
+// per 64-bit word (16-bit fields: a tile holds at most 8192 positions).
+template <int G>
+struct PackedCounts {
+  static constexpr int kWords = (G + 3) / 4;
+  int64_t v[kWords];
+};
+
 template <int G>
 __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
   const int tile = blockIdx.x;
@@ -53,12 +61,11 @@ __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
   const int wstart = max(sg.N - p.window, 0);  // W = [0, lo) u [wstart, N)
 
   __shared__ uint64_t bm[G][kWordsPerTile];
-  __shared__ uint32_t wpre[kWordsPerTile];
+  __shared__ int32_t s_pg[kWordsPerTile];
   __shared__ int32_t upos[kTile];
   __shared__ uint8_t umem[kTile];
   __shared__ uint32_t s_off[G];
-  __shared__ float s_m[G];
-  __shared__ float s_part[kGathWaves][G];
+  __shared__ float s_zs[kGathWaves][G];
   __shared__ float s_acc[kGathWaves][G][kHeadDim];
   __shared__ int64_t s_tmp[16];
 
@@ -67,25 +74,41 @@ __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
     const int w = i - hh * kWordsPerTile;
     bm[hh][w] = p.bitmap[(bh0 + hh) * words_row + size_t(tile) * kWordsPerTile + w];
   }
+  // a 64-bit word covers exactly one 64-token page
+  if (tid < kWordsPerTile)
+    s_pg[tid] = (t0 + tid * 64 < sg.N) ? page_of(p, b, (t0 >> 6) + tid) : 0;
   for (int hh = wave; hh < G; hh += kGathWaves) {
     uint32_t s = 0;
     for (int t = lane; t < tile; t += 64) s += p.tile_cnt[(bh0 + hh) * p.n_tiles + t];
     s = wave_sum(s);
     if (lane == 0) s_off[hh] = s;
   }
+  float mref[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) mref[hh] = softmax_ref(p.state[bh0 + hh], sg.k_eff);
   __syncthreads();
 
-  // union of the group's selections and W, as an ordered position list
+  // union of the group's selections and W, as an ordered position list, and
+  // each head's rank offsets for its out_idx slice
   uint64_t uw = 0, wm = 0;
   const int nw = t0 + tid * 64;
+  PackedCounts<G> pc;
+#pragma unroll
+  for (int j = 0; j < PackedCounts<G>::kWords; ++j) pc.v[j] = 0;
   if (tid < kWordsPerTile) {
     wm = range_mask(nw, 0, sg.lo) | range_mask(nw, wstart, sg.N);
     uw = wm;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) uw |= bm[hh][tid];
+    for (int hh = 0; hh < G; ++hh) {
+      uw |= bm[hh][tid];
+      pc.v[hh >> 2] |= int64_t(__popcll(bm[hh][tid])) << (16 * (hh & 3));
+    }
   }
-  int64_t utotal;
-  const int64_t ex = block_excl_scan(tid < kWordsPerTile ? __popcll(uw) : 0, s_tmp, &utotal);
+  int64_t utotal, unused;
+  const int64_t ex = block_excl_scan(__popcll(uw), s_tmp, &utotal);
+  PackedCounts<G> px;
+#pragma unroll
+  for (int j = 0; j < PackedCounts<G>::kWords; ++j) px.v[j] = block_excl_scan(pc.v[j], s_tmp, &unused);
   if (tid < kWordsPerTile) {
     int pos = int(ex);
     uint64_t x = uw;
@@ -103,57 +126,27 @@ __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
       umem[pos] = uint8_t(mem);
       ++pos;
     }
-  }
-
-  // this tile's slice of out_idx, per head, ascending
-  if (p.k_max > 0) {
-#pragma unroll 1
-    for (int hh = 0; hh < G; ++hh) {
-      const uint64_t x0 = tid < kWordsPerTile ? bm[hh][tid] : 0ull;
-      int64_t tot;
-      const int64_t hx = block_excl_scan(__popcll(x0), s_tmp, &tot);
-      uint32_t rank = s_off[hh] + uint32_t(hx);
-      int32_t* dst = p.out_idx + (bh0 + hh) * p.k_max;
-      uint64_t x = x0;
-      while (x) {
-        const int bit = __ffsll((unsigned long long)x) - 1;
-        x &= x - 1ull;
-        if (rank < uint32_t(p.k_max)) dst[rank] = nw + bit;
-        ++rank;
+    if (p.k_max > 0) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        uint32_t rank = s_off[hh] + uint32_t((px.v[hh >> 2] >> (16 * (hh & 3))) & 0xFFFF);
+        int32_t* dst = p.out_idx + (bh0 + hh) * p.k_max;
+        uint64_t y = bm[hh][tid];
+        while (y) {
+          const int bit = __ffsll((unsigned long long)y) - 1;
+          y &= y - 1ull;
+          if (rank < uint32_t(p.k_max)) dst[rank] = nw + bit;
+          ++rank;
+        }
       }
     }
   }
   __syncthreads();
   const int U = int(utotal);
 
-  // per-head maximum over the attended positions of this tile
-  float lm[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) lm[hh] = -INFINITY;
-  for (int i = tid; i < U; i += kGathThreads) {
-    const int n = upos[i];
-    const uint32_t mem = umem[i];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-      if ((mem >> hh) & 1u) lm[hh] = fmaxf(lm[hh], p.scores[(bh0 + hh) * p.n_cap + n]);
-  }
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const float v = wave_max(lm[hh]);
-    if (lane == 0) s_part[wave][hh] = v;
-  }
-  __syncthreads();
-  if (tid < G) {
-    float v = s_part[0][tid];
-    for (int w = 1; w < kGathWaves; ++w) v = fmaxf(v, s_part[w][tid]);
-    s_m[tid] = v;
-  }
-  __syncthreads();
-  float mh[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) mh[hh] = s_m[hh];
-
-  // accumulate: 4 positions per wave step, 16 lanes x 8 dims per V row
+  // accumulate e^{z - m} v: 4 rows per wave step, 16 lanes x 8 dims per V
+  // row, kUnroll rows per lane in flight
+  constexpr int kUnroll = 4;
   float acc[G][8];
   float zs[G];
 #pragma unroll
@@ -162,23 +155,35 @@ __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
   }
-  const size_t vstride_page = size_t(p.H_kv) * kPage * kHeadDim;
-  for (int i = wave * 4 + row; i < U; i += kGathWaves * 4) {
-    const int n = upos[i];
-    const uint32_t mem = umem[i];
-    const int pg = page_of(p, b, n >> 6);
-    const uint4 v = *reinterpret_cast<const uint4*>(
-        p.v_pool + size_t(pg) * vstride_page + (size_t(g) * kPage + (n & 63)) * kHeadDim + r * 8);
-    const float vf[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
-                         bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+  const size_t vpage = size_t(p.H_kv) * kPage * kHeadDim;
+  const uint16_t* vbase = p.v_pool + size_t(g) * kPage * kHeadDim + r * 8;
+  for (int i0 = wave * 4 + row; i0 < U; i0 += kGathWaves * 4 * kUnroll) {
+    uint4 v[kUnroll];
+    float z[kUnroll][G];
+    uint32_t mem[kUnroll];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const bool on = (mem >> hh) & 1u;
-      const float z = on ? p.scores[(bh0 + hh) * p.n_cap + n] : 0.0f;
-      const float w = on ? expf(z - mh[hh]) : 0.0f;
-      zs[hh] += w;
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = i0 + u * kGathWaves * 4;
+      const bool ok = i < U;
+      const int n = ok ? upos[i] : t0;
+      mem[u] = ok ? umem[i] : 0u;
+      const int pg = s_pg[(n - t0) >> 6];
+      v[u] = *reinterpret_cast<const uint4*>(vbase + size_t(pg) * vpage + size_t(n & 63) * kHeadDim);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] += w * vf[e];
+      for (int hh = 0; hh < G; ++hh)
+        z[u][hh] = ((mem[u] >> hh) & 1u) ? p.scores[(bh0 + hh) * p.n_cap + n] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float vf[8] = {bf16lo(v[u].x), bf16hi(v[u].x), bf16lo(v[u].y), bf16hi(v[u].y),
+                           bf16lo(v[u].z), bf16hi(v[u].z), bf16lo(v[u].w), bf16hi(v[u].w)};
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float w = ((mem[u] >> hh) & 1u) ? expf(z[u][hh] - mref[hh]) : 0.0f;
+        zs[hh] += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[hh][e] += w * vf[e];
+      }
     }
   }
   // sum the 4 rows of each wave, then the waves
@@ -198,10 +203,9 @@ __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) s_acc[wave][hh][r * 8 + e] = acc[hh][e];
   }
-  __syncthreads();  // s_part is reused below
   if (lane == 0) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) s_part[wave][hh] = zs[hh];
+    for (int hh = 0; hh < G; ++hh) s_zs[wave][hh] = zs[hh];
   }
   __syncthreads();
   for (int i = tid; i < G * kHeadDim; i += kGathThreads) {
@@ -213,9 +217,9 @@ __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
   }
   if (tid < G) {
     float z = 0.0f;
-    for (int w = 0; w < kGathWaves; ++w) z += s_part[w][tid];
+    for (int w = 0; w < kGathWaves; ++w) z += s_zs[w][tid];
     float* mz = p.part_mz + ((bh0 + tid) * p.n_tiles + tile) * 2;
-    mz[0] = s_m[tid];
+    mz[0] = mref[tid];
     mz[1] = z;
   }
 }
@@ -241,16 +245,18 @@ __global__ __launch_bounds__(kHeadDim) void merge_kernel(Params p) {
   const int nt = (sg.N + kTile - 1) / kTile;
   const int d = threadIdx.x;
   const float* mz = p.part_mz + size_t(bh) * p.n_tiles * 2;
+  const float* pn = p.part_n + size_t(bh) * p.n_tiles * kHeadDim + d;
   float m = -INFINITY;
-  for (int t = 0; t < nt; ++t)
-    if (mz[2 * t + 1] > 0.0f) m = fmaxf(m, mz[2 * t]);
+#pragma unroll 8
+  for (int t = 0; t < nt; ++t) m = fmaxf(m, mz[2 * t + 1] > 0.0f ? mz[2 * t] : -INFINITY);
   float Z = 0.0f, acc = 0.0f;
-  for (int t = 0; t < nt; ++t) {
-    const float zt = mz[2 * t + 1];
-    if (zt > 0.0f) {
-      const float sc = expf(mz[2 * t] - m);
+  if (m > -INFINITY) {
+#pragma unroll 8
+    for (int t = 0; t < nt; ++t) {
+      const float zt = mz[2 * t + 1];
+      const float sc = zt > 0.0f ? expf(mz[2 * t] - m) : 0.0f;
       Z += sc * zt;
-      acc += sc * p.part_n[(size_t(bh) * p.n_tiles + t) * kHeadDim + d];
+      acc += sc * pn[size_t(t) * kHeadDim];
     }
   }
   p.out[size_t(bh) * kHeadDim + d] = Z > 0.0f ? acc / Z : 0.0f;

@@ -19,28 +19,42 @@ constexpr int kWordsPerTile = kTile / 64;
 // Global histogram stride per head: 4096 fine bins then 64 coarse bins.
 constexpr int kFineBins = 4096;
 constexpr int kHistStride = kFineBins + 64;
-// Candidate list capacity per head (threshold-bucket members).
+// Capacity per head of the dense path's threshold-bucket candidate list.
 constexpr int kCandCapMax = 32768;
 
-// Selection modes chosen from the histogram.
+// Dense-path selection modes chosen from its histogram.
 constexpr uint32_t kModeCand = 1;     // bucket fits the candidate list
 constexpr uint32_t kModeRescan = 2;   // bucket too large: rescan the row
 
+// Sampling: one page in S is scored before the main scan, S a power of two
+// chosen so that at least ~128 pages of a (sequence, KV head) are sampled.
+constexpr int kSampleMinPages = 128;
+constexpr int kSampleMaxLog2 = 5;
+
 struct HeadState {
-  uint32_t b1;        // threshold bucket (fine digit) of the k_eff-th largest
-  uint32_t above1;    // members of M with a larger digit
-  uint32_t need1;     // how many to take from the bucket
-  uint32_t mode;      // kModeCand / kModeRescan / 0 (nothing to select)
-  uint32_t cand_count;
-  uint32_t pad[3];
+  // sparse path
+  uint32_t lo_key;      // candidate threshold (key >= lo_key) from the sample
+  uint32_t cand_count;  // candidates appended by the scan
+  uint32_t max_w;       // order-preserving key of the largest score over W
+  uint32_t max_m;       // ... over M (0 = no position seen)
+  uint32_t dense;       // 1: the sparse path could not decide this head
+  // dense path (only for heads with dense == 1)
+  uint32_t b1;          // threshold bucket (fine digit) of the k_eff-th largest
+  uint32_t above1;      // members of M with a larger digit
+  uint32_t need1;       // how many to take from the bucket
+  uint32_t mode;        // kModeCand / kModeRescan / 0 (nothing to select)
+  uint32_t dcand_count;
+  uint32_t pad[6];
 };
 
 struct WsLayout {
   int64_t n_cap;    // score row stride (positions), a multiple of kTile
   int32_t n_tiles;  // n_cap / kTile
-  int32_t cap;      // candidate capacity per head
-  size_t off_scores, off_hist, off_state, off_seqoff, off_tilecnt, off_bitmap,
-      off_cand, off_part_mz, off_part_n, total;
+  int32_t cap;      // sparse candidate capacity per head
+  int32_t dcap;     // dense threshold-bucket capacity per head
+  size_t off_scores, off_hist, off_dhist, off_state, off_gflag, off_seqoff,
+      off_tilecnt, off_bitmap, off_cand, off_dcand, off_part_mz, off_part_n,
+      total;
 };
 
 // Pure host function; returns false for invalid capacities.
@@ -60,26 +74,32 @@ struct Params {
   int32_t B, H_q, H_kv, G, max_pages, num_pages, max_seq_len, k_max, n_sink,
       window;
   // workspace
-  float* scores;
-  uint32_t* hist;
-  HeadState* state;
-  int64_t* seq_off;   // [B + 1] prefix of H_kv * pages(b)
-  uint32_t* tile_cnt; // [B*H_q][n_tiles]
-  uint64_t* bitmap;   // [B*H_q][n_cap / 64]
-  uint64_t* cand;     // [B*H_q][cap]
-  float* part_mz;     // [B*H_q][n_tiles][2]  (m, Z)
-  float* part_n;      // [B*H_q][n_tiles][128]
+  float* scores;       // [B*H_q][n_cap]: W and selected positions (all
+                       // positions for heads on the dense path)
+  uint32_t* hist;      // [B*H_q][kHistStride] sample histogram
+  uint32_t* dhist;     // [B*H_q][kHistStride] dense-path histogram
+  HeadState* state;    // [B*H_q]
+  uint32_t* gflag;     // [B*H_kv] 1: some head of the group is on the dense path
+  int64_t* seq_off;    // [B + 1] prefix of H_kv * pages(b)
+  uint32_t* tile_cnt;  // [B*H_q][n_tiles]
+  uint64_t* bitmap;    // [B*H_q][n_cap / 64]
+  uint64_t* cand;      // [B*H_q][cap]   key << 32 | ~position
+  uint64_t* dcand;     // [B*H_q][dcap]
+  float* part_mz;      // [B*H_q][n_tiles][2]  (m, Z)
+  float* part_n;       // [B*H_q][n_tiles][128]
   int64_t n_cap;
   int32_t n_tiles;
   int32_t cap;
+  int32_t dcap;
   int32_t num_cus;
 };
 
 // Launchers (each enqueues its kernels on `s`; they never synchronise).
 hipError_t launch_prep(const Params& p, hipStream_t s);
+hipError_t launch_sample(const Params& p, hipStream_t s);
 hipError_t launch_scan(const Params& p, hipStream_t s);
-hipError_t launch_filter(const Params& p, hipStream_t s);
-hipError_t launch_resolve(const Params& p, hipStream_t s);
+hipError_t launch_select(const Params& p, hipStream_t s);
+hipError_t launch_dense(const Params& p, hipStream_t s);   // scan + filter + resolve
 hipError_t launch_gather(const Params& p, hipStream_t s);
 hipError_t launch_merge(const Params& p, hipStream_t s);
 hipError_t launch_kv_append(const ra_kv_layer& kv, const uint16_t* k_new,
@@ -95,6 +115,20 @@ __device__ __forceinline__ uint32_t f2key(float x) {
   x = x + 0.0f;
   uint32_t u = __float_as_uint(x);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of f2key; key 0 (nothing recorded) maps to -inf.
+__device__ __forceinline__ float key2f(uint32_t k) {
+  if (k == 0u) return -INFINITY;
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Reference point of the softmax over W u Omega: the largest score in that
+// set. The top-ranked member of M is in Omega whenever k_eff > 0, so it is
+// max(max over W, max over M) then, and the max over W otherwise.
+__device__ __forceinline__ float softmax_ref(const HeadState& st, int k_eff) {
+  const uint32_t k = k_eff > 0 ? max(st.max_w, st.max_m) : st.max_w;
+  return key2f(k);
 }
 
 struct SeqGeom {
