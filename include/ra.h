@@ -87,7 +87,7 @@ const char* ra_status_str(ra_status s);
 
 /*
  * Bytes of scratch workspace ra_decode_step needs for these capacities
- * (score rows, histograms, selection bitmaps, candidate lists and split-K
+ * (score rows, sample histograms, per-tile candidate lists and split-K
  * partials). Returns 0 if the arguments are invalid.
  */
 size_t ra_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv,
@@ -145,11 +145,14 @@ typedef enum ra_stage {
   RA_STAGE_PREP = 0,   /* clear histograms and counters, sequence offsets */
   RA_STAGE_SAMPLE = 1, /* score a sample of pages: per-head candidate threshold */
   RA_STAGE_SCAN = 2,   /* all scores; keep W and the candidates above it */
-  RA_STAGE_SELECT = 3, /* exact top-k among the candidates, ties to lower n */
-  RA_STAGE_DENSE = 4,  /* exact top-k over every score, only for heads the
-                          sample could not decide (no work otherwise) */
-  RA_STAGE_GATHER = 5, /* out_idx + split-K softmax-V partials */
-  RA_STAGE_MERGE = 6,  /* log-sum-exp merge into out / out_lse, -1 padding */
+  RA_STAGE_SELECT = 3, /* exact top-k threshold over the candidates, ties to
+                          the lower position; flags heads with too few */
+  RA_STAGE_DENSE = 4,  /* flagged heads only (no work otherwise): rescan with
+                          every member of M as a candidate, select again */
+  RA_STAGE_GATHER = 5, /* take the retrieved members per tile, split-K
+                          softmax-V partials */
+  RA_STAGE_MERGE = 6,  /* log-sum-exp merge into out / out_lse; out_idx with
+                          -1 padding */
   RA_STAGE_COUNT = 7
 } ra_stage;
 
@@ -164,10 +167,9 @@ ra_status ra_decode_stages(const uint16_t* q, int32_t H_q,
 /*
  * Where the fp32 score rows live inside a workspace sized for these
  * capacities: z for (b, h, n) is the float at byte offset
- * returned + 4 * ((b * H_q + h) * (*row_stride) + n). After RA_STAGE_SELECT
- * it holds the positions of W and of the retrieved set (after RA_STAGE_DENSE,
- * every position of a head that took the dense path). Returns (size_t)-1 if
- * the arguments are invalid.
+ * returned + 4 * ((b * H_q + h) * (*row_stride) + n). After RA_STAGE_GATHER
+ * it holds the scores of the positions of W and of the retrieved set; other
+ * entries are unspecified. Returns (size_t)-1 if the arguments are invalid.
  */
 size_t ra_workspace_scores_offset(int32_t B, int32_t H_q, int32_t H_kv,
                                   int32_t max_seq_len, int32_t k_max,

@@ -4,22 +4,31 @@
 // Eqs. (3)-(5); backup frame "the normalization identity": merging disjoint
 // partials gives the exact softmax over their union).
 //
-// gather: one block per (sequence, KV head, tile of 8192 positions). The
-//   block takes the union over the group's G query heads of their selected
-//   positions in the tile plus the tile's static positions, in ascending
-//   order, reads each V row (256 contiguous bytes) once, and accumulates for
-//   every head that attends to it: m = max z, Z = sum e^{z - m},
-//   N = sum e^{z - m} v. It also writes the tile's part of out_idx, whose
-//   offset is the sum of the per-tile selection counts before it.
-// merge: one block per (sequence, query head): m = max_t m_t,
-//   out = sum_t e^{m_t - m} N_t / sum_t e^{m_t - m} Z_t, lse = m + ln(...),
-//   and -1 padding of out_idx after k_eff.
+// One block per (sequence, KV head, tile of 8192 positions). The block first
+// takes each head's retrieved members of the tile: the entries of the
+// (head, tile) candidate list at or above the head's exact threshold. It
+// marks them in an LDS bitmap and stores their scores next to the scores of
+// W that the scan left. It then walks the union over the group's G query
+// heads of those positions and the tile's static positions in ascending
+// order, reads each V row (256 contiguous bytes) once, and accumulates for
+// every head that attends to it: Z = sum e^{z - m}, N = sum e^{z - m} v,
+// with m the head's largest score over W u Omega (the scan records it), so
+// no partial can overflow. The sorted retrieved positions of the tile
+// replace the consumed list, with their count.
+//
+// merge (one block per query head) combines the tile partials:
+// out = sum_t e^{m_t - m} N_t / sum_t e^{m_t - m} Z_t, lse = m + ln(...),
+// concatenates the tiles' retrieved positions into out_idx and pads it
+// with -1 after k_eff.
 #include "ra_internal.h"
 
 namespace ra {
 
 constexpr int kGathThreads = 256;
 constexpr int kGathWaves = kGathThreads / 64;
+constexpr int kChunk = 2048;   // union positions listed in LDS at a time
+constexpr int kUnroll = 4;     // V rows per lane in flight
+constexpr int kListBatch = 4;  // list entries per lane in flight
 
 __device__ __forceinline__ uint64_t range_mask(int nw, int a, int c) {
   const int s = max(a - nw, 0);
@@ -33,8 +42,8 @@ __device__ __forceinline__ uint64_t range_mask(int nw, int a, int c) {
 __device__ __forceinline__ float bf16lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
 
-// Exclusive prefix over the block of per-head popcounts packed four heads
-// per 64-bit word (16-bit fields: a tile holds at most 8192 positions).
+// Per-head popcounts packed four heads per 64-bit word (16-bit fields: a
+// tile holds at most 8192 positions), so one block scan ranks them all.
 template <int G>
 struct PackedCounts {
   static constexpr int kWords = (G + 3) / 4;
@@ -48,6 +57,7 @@ __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
   const int b = bg / p.H_kv;
   const int g = bg - b * p.H_kv;
   const SeqGeom sg = seq_geom(p, b);
+  const size_t bh0 = size_t(b) * p.H_q + size_t(g) * G;
   const int t0 = tile * kTile;
   if (t0 >= sg.N) return;
 
@@ -56,40 +66,57 @@ __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
   const int wave = tid >> 6;
   const int row = lane >> 4;
   const int r = lane & 15;
-  const size_t bh0 = size_t(b) * p.H_q + size_t(g) * G;
-  const size_t words_row = size_t(p.n_cap / 64);
   const int wstart = max(sg.N - p.window, 0);  // W = [0, lo) u [wstart, N)
 
   __shared__ uint64_t bm[G][kWordsPerTile];
   __shared__ int32_t s_pg[kWordsPerTile];
-  __shared__ int32_t upos[kTile];
-  __shared__ uint8_t umem[kTile];
-  __shared__ uint32_t s_off[G];
+  __shared__ uint32_t ulist[kChunk];        // offset in tile | heads << 13
   __shared__ float s_zs[kGathWaves][G];
   __shared__ float s_acc[kGathWaves][G][kHeadDim];
   __shared__ int64_t s_tmp[16];
 
-  for (int i = tid; i < G * kWordsPerTile; i += kGathThreads) {
-    const int hh = i / kWordsPerTile;
-    const int w = i - hh * kWordsPerTile;
-    bm[hh][w] = p.bitmap[(bh0 + hh) * words_row + size_t(tile) * kWordsPerTile + w];
-  }
+  for (int i = tid; i < G * kWordsPerTile; i += kGathThreads) (&bm[0][0])[i] = 0ull;
   // a 64-bit word covers exactly one 64-token page
   if (tid < kWordsPerTile)
     s_pg[tid] = (t0 + tid * 64 < sg.N) ? page_of(p, b, (t0 >> 6) + tid) : 0;
-  for (int hh = wave; hh < G; hh += kGathWaves) {
-    uint32_t s = 0;
-    for (int t = lane; t < tile; t += 64) s += p.tile_cnt[(bh0 + hh) * p.n_tiles + t];
-    s = wave_sum(s);
-    if (lane == 0) s_off[hh] = s;
-  }
   float mref[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) mref[hh] = softmax_ref(p.state[bh0 + hh], sg.k_eff);
   __syncthreads();
 
-  // union of the group's selections and W, as an ordered position list, and
-  // each head's rank offsets for its out_idx slice
+  // each head's retrieved members of this tile: the list entries whose
+  // composite (key - lo) << 32 | ~n clears the head's threshold
+  for (int hh = 0; hh < G; ++hh) {
+    const HeadState st = p.state[bh0 + hh];
+    if (st.thr_shift >= 64u) continue;
+    const uint32_t cnt = p.tcnt[(bh0 + hh) * p.n_tiles + tile];
+    const uint64_t* list = p.cand + (bh0 + hh) * p.n_cap + size_t(t0);
+    float* srow = p.scores + (bh0 + hh) * p.n_cap;
+    const uint64_t thr = (uint64_t(st.thr_hi) << 32) | st.thr_lo;
+    for (uint32_t base = 0; base < cnt; base += kGathThreads * kListBatch) {
+      uint64_t v[kListBatch];
+#pragma unroll
+      for (int u = 0; u < kListBatch; ++u) {
+        const uint32_t i = base + u * kGathThreads + tid;
+        v[u] = i < cnt ? list[i] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < kListBatch; ++u) {
+        if (base + u * kGathThreads + tid >= cnt) continue;
+        const uint32_t key = uint32_t(v[u] >> 32);
+        const uint32_t n = uint32_t(v[u]);
+        const uint64_t comp = (uint64_t(key - st.lo_key) << 32) | uint32_t(~n);
+        if ((comp >> st.thr_shift) >= thr) {
+          atomicOr(reinterpret_cast<unsigned long long*>(&bm[hh][(int(n) - t0) >> 6]),
+                   1ull << (n & 63u));
+          srow[n] = key2f(key);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // union of the group's selections and W, and each head's ranks
   uint64_t uw = 0, wm = 0;
   const int nw = t0 + tid * 64;
   PackedCounts<G> pc;
@@ -104,49 +131,31 @@ __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
       pc.v[hh >> 2] |= int64_t(__popcll(bm[hh][tid])) << (16 * (hh & 3));
     }
   }
-  int64_t utotal, unused;
+  int64_t utotal;
   const int64_t ex = block_excl_scan(__popcll(uw), s_tmp, &utotal);
-  PackedCounts<G> px;
+  PackedCounts<G> px, ptot;
 #pragma unroll
-  for (int j = 0; j < PackedCounts<G>::kWords; ++j) px.v[j] = block_excl_scan(pc.v[j], s_tmp, &unused);
+  for (int j = 0; j < PackedCounts<G>::kWords; ++j)
+    px.v[j] = block_excl_scan(pc.v[j], s_tmp, &ptot.v[j]);
+  // the tile's retrieved positions, ascending, replace its consumed lists
   if (tid < kWordsPerTile) {
-    int pos = int(ex);
-    uint64_t x = uw;
-    while (x) {
-      const int bit = __ffsll((unsigned long long)x) - 1;
-      x &= x - 1ull;
-      uint32_t mem = 0;
-      if ((wm >> bit) & 1ull) {
-        mem = (1u << G) - 1u;
-      } else {
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) mem |= uint32_t((bm[hh][tid] >> bit) & 1ull) << hh;
-      }
-      upos[pos] = nw + bit;
-      umem[pos] = uint8_t(mem);
-      ++pos;
-    }
-    if (p.k_max > 0) {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        uint32_t rank = s_off[hh] + uint32_t((px.v[hh >> 2] >> (16 * (hh & 3))) & 0xFFFF);
-        int32_t* dst = p.out_idx + (bh0 + hh) * p.k_max;
-        uint64_t y = bm[hh][tid];
-        while (y) {
-          const int bit = __ffsll((unsigned long long)y) - 1;
-          y &= y - 1ull;
-          if (rank < uint32_t(p.k_max)) dst[rank] = nw + bit;
-          ++rank;
-        }
+    for (int hh = 0; hh < G; ++hh) {
+      uint32_t rank = uint32_t((px.v[hh >> 2] >> (16 * (hh & 3))) & 0xFFFF);
+      int32_t* dst = reinterpret_cast<int32_t*>(p.cand + (bh0 + hh) * p.n_cap + size_t(t0));
+      uint64_t y = bm[hh][tid];
+      while (y) {
+        const int bit = __ffsll((unsigned long long)y) - 1;
+        y &= y - 1ull;
+        dst[rank++] = nw + bit;
       }
     }
   }
-  __syncthreads();
+  if (tid < G)
+    p.scnt[(bh0 + tid) * p.n_tiles + tile] =
+        uint32_t((ptot.v[tid >> 2] >> (16 * (tid & 3))) & 0xFFFF);
   const int U = int(utotal);
 
-  // accumulate e^{z - m} v: 4 rows per wave step, 16 lanes x 8 dims per V
-  // row, kUnroll rows per lane in flight
-  constexpr int kUnroll = 4;
   float acc[G][8];
   float zs[G];
 #pragma unroll
@@ -157,34 +166,62 @@ __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
   }
   const size_t vpage = size_t(p.H_kv) * kPage * kHeadDim;
   const uint16_t* vbase = p.v_pool + size_t(g) * kPage * kHeadDim + r * 8;
-  for (int i0 = wave * 4 + row; i0 < U; i0 += kGathWaves * 4 * kUnroll) {
-    uint4 v[kUnroll];
-    float z[kUnroll][G];
-    uint32_t mem[kUnroll];
+  for (int cb = 0; cb < U; cb += kChunk) {
+    // list this chunk of the union in LDS
+    if (tid < kWordsPerTile) {
+      int pos = int(ex) - cb;
+      uint64_t x = uw;
+      while (x && pos < kChunk) {
+        const int bit = __ffsll((unsigned long long)x) - 1;
+        x &= x - 1ull;
+        if (pos >= 0) {
+          uint32_t mem = 0;
+          if ((wm >> bit) & 1ull) {
+            mem = (1u << G) - 1u;
+          } else {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int i = i0 + u * kGathWaves * 4;
-      const bool ok = i < U;
-      const int n = ok ? upos[i] : t0;
-      mem[u] = ok ? umem[i] : 0u;
-      const int pg = s_pg[(n - t0) >> 6];
-      v[u] = *reinterpret_cast<const uint4*>(vbase + size_t(pg) * vpage + size_t(n & 63) * kHeadDim);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh)
-        z[u][hh] = ((mem[u] >> hh) & 1u) ? p.scores[(bh0 + hh) * p.n_cap + n] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const float vf[8] = {bf16lo(v[u].x), bf16hi(v[u].x), bf16lo(v[u].y), bf16hi(v[u].y),
-                           bf16lo(v[u].z), bf16hi(v[u].z), bf16lo(v[u].w), bf16hi(v[u].w)};
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float w = ((mem[u] >> hh) & 1u) ? expf(z[u][hh] - mref[hh]) : 0.0f;
-        zs[hh] += w;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] += w * vf[e];
+            for (int hh = 0; hh < G; ++hh) mem |= uint32_t((bm[hh][tid] >> bit) & 1ull) << hh;
+          }
+          ulist[pos] = uint32_t(tid * 64 + bit) | (mem << 13);
+        }
+        ++pos;
       }
     }
+    __syncthreads();
+    const int cnt = min(kChunk, U - cb);
+    // 4 rows per wave step, 16 lanes x 8 dims per V row, kUnroll rows per
+    // lane in flight
+    for (int i0 = wave * 4 + row; i0 < cnt; i0 += kGathWaves * 4 * kUnroll) {
+      uint4 v[kUnroll];
+      float z[kUnroll][G];
+      uint32_t mem[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = i0 + u * kGathWaves * 4;
+        const uint32_t e = i < cnt ? ulist[i] : 0u;
+        const int off = int(e & 8191u);
+        const int n = t0 + off;
+        mem[u] = e >> 13;
+        const int pg = s_pg[off >> 6];
+        v[u] = *reinterpret_cast<const uint4*>(vbase + size_t(pg) * vpage + size_t(n & 63) * kHeadDim);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+          z[u][hh] = ((mem[u] >> hh) & 1u) ? p.scores[(bh0 + hh) * p.n_cap + n] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const float vf[8] = {bf16lo(v[u].x), bf16hi(v[u].x), bf16lo(v[u].y), bf16hi(v[u].y),
+                             bf16lo(v[u].z), bf16hi(v[u].z), bf16lo(v[u].w), bf16hi(v[u].w)};
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float w = ((mem[u] >> hh) & 1u) ? expf(z[u][hh] - mref[hh]) : 0.0f;
+          zs[hh] += w;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[hh][e] += w * vf[e];
+        }
+      }
+    }
+    __syncthreads();
   }
   // sum the 4 rows of each wave, then the waves
 #pragma unroll
@@ -222,6 +259,140 @@ __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
     mz[0] = mref[tid];
     mz[1] = z;
   }
+
+}
+
+// ---------------------------------------------------------------- merge
+// One block per (sequence, query head): 8 groups of 32 threads each take
+// every 8th tile, 4 dims per thread (float4 loads issued kMergeUnroll deep),
+// then the groups are summed in LDS in a fixed order.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeGroups = kMergeThreads / 32;
+constexpr int kMergeUnroll = 4;
+constexpr int kMergeWin = 2048;  // tiles per out_idx prefix window
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p) {
+  const int bh = blockIdx.x;
+  const int b = bh / p.H_q;
+  const SeqGeom sg = seq_geom(p, b);
+  const int nt = (sg.N + kTile - 1) / kTile;
+  const int tid = threadIdx.x;
+  const int grp = tid >> 5;
+  const int d0 = (tid & 31) * 4;
+  const float* mz = p.part_mz + size_t(bh) * p.n_tiles * 2;
+  const float* pn = p.part_n + size_t(bh) * p.n_tiles * kHeadDim + d0;
+
+  __shared__ float s_red[kMergeGroups][kHeadDim + 4];
+  __shared__ float s_m[kMergeThreads / 64];
+  __shared__ uint32_t s_pre[kMergeWin];
+  __shared__ int64_t s_tmp[16];
+
+  // m = max over tiles with a non-empty partial
+  float m = -INFINITY;
+  for (int t = tid; t < nt; t += kMergeThreads) m = fmaxf(m, mz[2 * t + 1] > 0.0f ? mz[2 * t] : -INFINITY);
+  m = wave_max(m);
+  if ((tid & 63) == 0) s_m[tid >> 6] = m;
+  __syncthreads();
+  m = s_m[0];
+  for (int w = 1; w < kMergeThreads / 64; ++w) m = fmaxf(m, s_m[w]);
+
+  float Z = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (m > -INFINITY) {
+    for (int t0 = grp; t0 < nt; t0 += kMergeGroups * kMergeUnroll) {
+      float2 w2[kMergeUnroll];
+      float4 v[kMergeUnroll];
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        const int t = t0 + u * kMergeGroups;
+        w2[u] = t < nt ? *reinterpret_cast<const float2*>(mz + 2 * t) : make_float2(0.f, 0.f);
+        v[u] = t < nt ? *reinterpret_cast<const float4*>(pn + size_t(t) * kHeadDim)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        const float sc = w2[u].y > 0.0f ? expf(w2[u].x - m) : 0.0f;
+        Z += sc * w2[u].y;
+        acc.x += sc * v[u].x;
+        acc.y += sc * v[u].y;
+        acc.z += sc * v[u].z;
+        acc.w += sc * v[u].w;
+      }
+    }
+  }
+  s_red[grp][d0 + 0] = acc.x;
+  s_red[grp][d0 + 1] = acc.y;
+  s_red[grp][d0 + 2] = acc.z;
+  s_red[grp][d0 + 3] = acc.w;
+  if ((tid & 31) == 0) s_red[grp][kHeadDim] = Z;
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float a = 0.0f, zz = 0.0f;
+    for (int gI = 0; gI < kMergeGroups; ++gI) {
+      a += s_red[gI][tid];
+      zz += s_red[gI][kHeadDim];
+    }
+    p.out[size_t(bh) * kHeadDim + tid] = zz > 0.0f ? a / zz : 0.0f;
+    if (tid == 0 && p.lse) p.lse[bh] = zz > 0.0f ? m + logf(zz) : -INFINITY;
+  }
+  if (p.k_max > 0) {
+    // out_idx: the tiles' retrieved positions in tile order (ascending),
+    // a window of kMergeWin tiles at a time located by a prefix in LDS
+    int32_t* dst = p.out_idx + size_t(bh) * p.k_max;
+    const uint32_t* sc = p.scnt + size_t(bh) * p.n_tiles;
+    const int32_t* src = reinterpret_cast<const int32_t*>(p.cand + size_t(bh) * p.n_cap);
+    uint32_t done = 0;
+    for (int w0 = 0; w0 < nt; w0 += kMergeWin) {
+      const int nw = min(kMergeWin, nt - w0);
+      constexpr int per = kMergeWin / kMergeThreads;
+      uint32_t c[per];
+      int64_t sum = 0;
+#pragma unroll
+      for (int u = 0; u < per; ++u) {
+        const int i = tid * per + u;
+        c[u] = i < nw ? sc[w0 + i] : 0u;
+        sum += c[u];
+      }
+      int64_t total;
+      int64_t run = block_excl_scan(sum, s_tmp, &total);
+#pragma unroll
+      for (int u = 0; u < per; ++u) {
+        s_pre[tid * per + u] = uint32_t(run);
+        run += c[u];
+      }
+      __syncthreads();
+      for (uint32_t base = 0; base < uint32_t(total); base += kMergeThreads * kMergeUnroll) {
+        int32_t v[kMergeUnroll];
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) {
+          const uint32_t i = base + u * kMergeThreads + tid;
+          v[u] = 0;
+          if (i < uint32_t(total)) {
+            int a = 0, e = nw - 1;
+            while (a < e) {
+              const int mid = (a + e + 1) >> 1;
+              if (s_pre[mid] <= i) a = mid; else e = mid - 1;
+            }
+            v[u] = src[size_t(w0 + a) * (2 * kTile) + (i - s_pre[a])];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) {
+          const uint32_t i = base + u * kMergeThreads + tid;
+          if (i < uint32_t(total) && done + i < uint32_t(p.k_max)) dst[done + i] = v[u];
+        }
+      }
+      done += uint32_t(total);
+      __syncthreads();
+    }
+    for (int i = int(min(done, uint32_t(p.k_max))) + tid; i < p.k_max; i += kMergeThreads)
+      dst[i] = -1;
+  }
+}
+
+hipError_t launch_merge(const Params& p, hipStream_t s) {
+  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(p.B * p.H_q)), dim3(kMergeThreads), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_gather(const Params& p, hipStream_t s) {
@@ -234,41 +405,6 @@ hipError_t launch_gather(const Params& p, hipStream_t s) {
     case 8: hipLaunchKernelGGL(gather_kernel<8>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------- merge
-__global__ __launch_bounds__(kHeadDim) void merge_kernel(Params p) {
-  const int bh = blockIdx.x;
-  const int b = bh / p.H_q;
-  const SeqGeom sg = seq_geom(p, b);
-  const int nt = (sg.N + kTile - 1) / kTile;
-  const int d = threadIdx.x;
-  const float* mz = p.part_mz + size_t(bh) * p.n_tiles * 2;
-  const float* pn = p.part_n + size_t(bh) * p.n_tiles * kHeadDim + d;
-  float m = -INFINITY;
-#pragma unroll 8
-  for (int t = 0; t < nt; ++t) m = fmaxf(m, mz[2 * t + 1] > 0.0f ? mz[2 * t] : -INFINITY);
-  float Z = 0.0f, acc = 0.0f;
-  if (m > -INFINITY) {
-#pragma unroll 8
-    for (int t = 0; t < nt; ++t) {
-      const float zt = mz[2 * t + 1];
-      const float sc = zt > 0.0f ? expf(mz[2 * t] - m) : 0.0f;
-      Z += sc * zt;
-      acc += sc * pn[size_t(t) * kHeadDim];
-    }
-  }
-  p.out[size_t(bh) * kHeadDim + d] = Z > 0.0f ? acc / Z : 0.0f;
-  if (d == 0 && p.lse) p.lse[bh] = Z > 0.0f ? m + logf(Z) : -INFINITY;
-  if (p.k_max > 0) {
-    int32_t* dst = p.out_idx + size_t(bh) * p.k_max;
-    for (int i = sg.k_eff + d; i < p.k_max; i += kHeadDim) dst[i] = -1;
-  }
-}
-
-hipError_t launch_merge(const Params& p, hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(p.B * p.H_q)), dim3(kHeadDim), 0, s, p);
   return hipGetLastError();
 }
 

@@ -24,9 +24,6 @@ bool ws_layout(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seq_len,
   if (heads > 65535) return false;  // grid y limit of the per-head kernels
   L->n_cap = (int64_t(max_seq_len) + kTile - 1) / kTile * kTile;
   L->n_tiles = int32_t(L->n_cap / kTile);
-  // sparse candidates: the sampled threshold aims at ~1.2 k plus a margin
-  L->cap = int32_t(std::min<int64_t>(L->n_cap, 2 * int64_t(k_max) + 8192));
-  L->dcap = int32_t(std::min<int64_t>(kCandCapMax, L->n_cap));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -35,14 +32,14 @@ bool ws_layout(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seq_len,
   };
   L->off_scores = take(size_t(heads) * L->n_cap * sizeof(float));
   L->off_hist = take(size_t(heads) * kHistStride * sizeof(uint32_t));
-  L->off_dhist = take(size_t(heads) * kHistStride * sizeof(uint32_t));
   L->off_state = take(size_t(heads) * sizeof(HeadState));
   L->off_gflag = take(size_t(B) * H_kv * sizeof(uint32_t));
+  L->off_misc = take(64);
   L->off_seqoff = take(size_t(B + 1) * sizeof(int64_t));
-  L->off_tilecnt = take(size_t(heads) * L->n_tiles * sizeof(uint32_t));
-  L->off_bitmap = take(size_t(heads) * (L->n_cap / 64) * sizeof(uint64_t));
-  L->off_cand = take(size_t(heads) * L->cap * sizeof(uint64_t));
-  L->off_dcand = take(size_t(heads) * L->dcap * sizeof(uint64_t));
+  L->off_sampoff = take(size_t(B + 1) * sizeof(int64_t));
+  L->off_tcnt = take(size_t(heads) * L->n_tiles * sizeof(uint32_t));
+  L->off_scnt = take(size_t(heads) * L->n_tiles * sizeof(uint32_t));
+  L->off_cand = take(size_t(heads) * L->n_cap * sizeof(uint64_t));
   L->off_part_mz = take(size_t(heads) * L->n_tiles * 2 * sizeof(float));
   L->off_part_n = take(size_t(heads) * L->n_tiles * kHeadDim * sizeof(float));
   L->total = off;
@@ -130,20 +127,18 @@ static Params make_params(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
   p.window = window;
   p.scores = reinterpret_cast<float*>(base + L.off_scores);
   p.hist = reinterpret_cast<uint32_t*>(base + L.off_hist);
-  p.dhist = reinterpret_cast<uint32_t*>(base + L.off_dhist);
   p.state = reinterpret_cast<HeadState*>(base + L.off_state);
   p.gflag = reinterpret_cast<uint32_t*>(base + L.off_gflag);
+  p.any_dense = reinterpret_cast<uint32_t*>(base + L.off_misc);
   p.seq_off = reinterpret_cast<int64_t*>(base + L.off_seqoff);
-  p.tile_cnt = reinterpret_cast<uint32_t*>(base + L.off_tilecnt);
-  p.bitmap = reinterpret_cast<uint64_t*>(base + L.off_bitmap);
+  p.samp_off = reinterpret_cast<int64_t*>(base + L.off_sampoff);
+  p.tcnt = reinterpret_cast<uint32_t*>(base + L.off_tcnt);
+  p.scnt = reinterpret_cast<uint32_t*>(base + L.off_scnt);
   p.cand = reinterpret_cast<uint64_t*>(base + L.off_cand);
-  p.dcand = reinterpret_cast<uint64_t*>(base + L.off_dcand);
   p.part_mz = reinterpret_cast<float*>(base + L.off_part_mz);
   p.part_n = reinterpret_cast<float*>(base + L.off_part_n);
   p.n_cap = L.n_cap;
   p.n_tiles = L.n_tiles;
-  p.cap = L.cap;
-  p.dcap = L.dcap;
   return p;
 }
 
@@ -214,8 +209,8 @@ ra_status ra_decode_stages(const uint16_t* q, int32_t H_q,
   p.num_cus = cu_count();
   using Launcher = hipError_t (*)(const Params&, hipStream_t);
   static const Launcher stages[RA_STAGE_COUNT] = {
-      launch_prep,  launch_sample, launch_scan, launch_select,
-      launch_dense, launch_gather, launch_merge};
+      launch_prep,   launch_sample, launch_scan,  launch_select,
+      launch_dense,  launch_gather, launch_merge};
   for (int s = first_stage; s <= last_stage; ++s) {
     if (stages[s](p, stream) != hipSuccess) return RA_ERR_HIP;
   }

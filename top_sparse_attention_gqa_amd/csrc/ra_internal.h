@@ -19,42 +19,33 @@ constexpr int kWordsPerTile = kTile / 64;
 // Global histogram stride per head: 4096 fine bins then 64 coarse bins.
 constexpr int kFineBins = 4096;
 constexpr int kHistStride = kFineBins + 64;
-// Capacity per head of the dense path's threshold-bucket candidate list.
-constexpr int kCandCapMax = 32768;
-
-// Dense-path selection modes chosen from its histogram.
-constexpr uint32_t kModeCand = 1;     // bucket fits the candidate list
-constexpr uint32_t kModeRescan = 2;   // bucket too large: rescan the row
-
 // Sampling: one page in S is scored before the main scan, S a power of two
-// chosen so that at least ~128 pages of a (sequence, KV head) are sampled.
-constexpr int kSampleMinPages = 128;
-constexpr int kSampleMaxLog2 = 5;
+// chosen so that at least kSampleMinPages pages of a (sequence, KV head)
+// are sampled, and S <= 2^kSampleMaxLog2.
+constexpr int kSampleMinPages = 32;
+constexpr int kSampleMaxLog2 = 6;
+
+// Candidate entries: key << 32 | position (order-preserving score key).
+// They are kept per (head, tile) in a list of capacity kTile, so a tile's
+// list can hold every position of the tile.
 
 struct HeadState {
-  // sparse path
-  uint32_t lo_key;      // candidate threshold (key >= lo_key) from the sample
-  uint32_t cand_count;  // candidates appended by the scan
+  uint32_t lo_key;      // candidates are the members of M with key >= lo_key
   uint32_t max_w;       // order-preserving key of the largest score over W
   uint32_t max_m;       // ... over M (0 = no position seen)
-  uint32_t dense;       // 1: the sparse path could not decide this head
-  // dense path (only for heads with dense == 1)
-  uint32_t b1;          // threshold bucket (fine digit) of the k_eff-th largest
-  uint32_t above1;      // members of M with a larger digit
-  uint32_t need1;       // how many to take from the bucket
-  uint32_t mode;        // kModeCand / kModeRescan / 0 (nothing to select)
-  uint32_t dcand_count;
-  uint32_t pad[6];
+  uint32_t dense;       // 1: too few candidates; rescanned with lo_key = 0
+  // decision: a candidate with composite c = (key - lo_key) << 32 | ~n is
+  // retrieved iff thr_shift < 64 and (c >> thr_shift) >= thr
+  uint32_t thr_shift;
+  uint32_t thr_lo, thr_hi;
+  uint32_t pad;
 };
 
 struct WsLayout {
-  int64_t n_cap;    // score row stride (positions), a multiple of kTile
+  int64_t n_cap;    // row stride (positions), a multiple of kTile
   int32_t n_tiles;  // n_cap / kTile
-  int32_t cap;      // sparse candidate capacity per head
-  int32_t dcap;     // dense threshold-bucket capacity per head
-  size_t off_scores, off_hist, off_dhist, off_state, off_gflag, off_seqoff,
-      off_tilecnt, off_bitmap, off_cand, off_dcand, off_part_mz, off_part_n,
-      total;
+  size_t off_scores, off_hist, off_state, off_gflag, off_misc, off_seqoff,
+      off_sampoff, off_tcnt, off_scnt, off_cand, off_part_mz, off_part_n, total;
 };
 
 // Pure host function; returns false for invalid capacities.
@@ -74,23 +65,22 @@ struct Params {
   int32_t B, H_q, H_kv, G, max_pages, num_pages, max_seq_len, k_max, n_sink,
       window;
   // workspace
-  float* scores;       // [B*H_q][n_cap]: W and selected positions (all
-                       // positions for heads on the dense path)
+  float* scores;       // [B*H_q][n_cap]: W scores (scan) and the retrieved
+                       // positions' scores of a tile (its gather block)
   uint32_t* hist;      // [B*H_q][kHistStride] sample histogram
-  uint32_t* dhist;     // [B*H_q][kHistStride] dense-path histogram
   HeadState* state;    // [B*H_q]
-  uint32_t* gflag;     // [B*H_kv] 1: some head of the group is on the dense path
+  uint32_t* gflag;     // [B*H_kv] 1: some head of the group needs the rescan
+  uint32_t* any_dense; // heads flagged for the rescan in this call
   int64_t* seq_off;    // [B + 1] prefix of H_kv * pages(b)
-  uint32_t* tile_cnt;  // [B*H_q][n_tiles]
-  uint64_t* bitmap;    // [B*H_q][n_cap / 64]
-  uint64_t* cand;      // [B*H_q][cap]   key << 32 | ~position
-  uint64_t* dcand;     // [B*H_q][dcap]
+  int64_t* samp_off;   // [B + 1] prefix of H_kv * sampled pages(b)
+  uint32_t* tcnt;      // [B*H_q][n_tiles] candidates per (head, tile)
+  uint32_t* scnt;      // [B*H_q][n_tiles] retrieved per (head, tile)
+  uint64_t* cand;      // [B*H_q][n_cap] per-tile candidate lists; after the
+                       // gather, a tile's retrieved positions (int32, sorted)
   float* part_mz;      // [B*H_q][n_tiles][2]  (m, Z)
   float* part_n;       // [B*H_q][n_tiles][128]
   int64_t n_cap;
   int32_t n_tiles;
-  int32_t cap;
-  int32_t dcap;
   int32_t num_cus;
 };
 
@@ -99,7 +89,7 @@ hipError_t launch_prep(const Params& p, hipStream_t s);
 hipError_t launch_sample(const Params& p, hipStream_t s);
 hipError_t launch_scan(const Params& p, hipStream_t s);
 hipError_t launch_select(const Params& p, hipStream_t s);
-hipError_t launch_dense(const Params& p, hipStream_t s);   // scan + filter + resolve
+hipError_t launch_dense(const Params& p, hipStream_t s);   // rescan + reselect
 hipError_t launch_gather(const Params& p, hipStream_t s);
 hipError_t launch_merge(const Params& p, hipStream_t s);
 hipError_t launch_kv_append(const ra_kv_layer& kv, const uint16_t* k_new,

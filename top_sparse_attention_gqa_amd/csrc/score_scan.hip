@@ -18,10 +18,10 @@
 // scores one page in S and histograms the sample; from it every head gets a
 // conservative threshold such that, with a wide statistical margin, more
 // than k_eff members of M score at or above it. The scan then keeps only
-// those candidates (staged in LDS and written in bursts per segment) plus
-// the scores of the static set W. The selection checks the margin exactly
-// (it needs at least k_eff candidates and a list that did not overflow);
-// heads that fail it take the dense path below, which stores every score.
+// those candidates, staged in LDS and written in bursts (every <= 64 pages)
+// to per-(head, tile) lists, plus the scores of the static set W. The
+// selection checks the margin exactly (it needs at least k_eff candidates);
+// heads that fail it are rescanned with every member of M as a candidate.
 #include "ra_internal.h"
 
 namespace ra {
@@ -31,8 +31,8 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kScanThreads = 512;
 constexpr int kScanWaves = kScanThreads / 64;
-constexpr int kSampleBlocks = 16;  // blocks per (sequence, KV head) in the sample
 constexpr int kStage = 6144;       // LDS candidate staging entries per block
+constexpr int kFlushPages = 64;    // pages between flushes: at most 2 tiles
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
 
 template <int G>
@@ -220,71 +220,90 @@ __device__ __forceinline__ void flush_hist(uint32_t* lhist, uint32_t* gbase, con
   }
 }
 
-// ---------------------------------------------------------------- prep
-// Clears the histograms, per-head state and group flags, and writes the
-// prefix seq_off[b] = sum_{b' < b} H_kv * pages(b') that maps the scan's
-// linear page index to (sequence, KV head, page).
-__global__ __launch_bounds__(1024) void prep_kernel(Params p) {
-  const size_t heads = size_t(p.B) * p.H_q;
-  const size_t n4 = heads * kHistStride / 4;
-  uint4* h4 = reinterpret_cast<uint4*>(p.hist);
-  uint4* d4 = reinterpret_cast<uint4*>(p.dhist);
-  const size_t stride = size_t(gridDim.x) * blockDim.x;
-  const size_t t0 = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  for (size_t i = t0; i < n4; i += stride) {
-    h4[i] = make_uint4(0, 0, 0, 0);
-    d4[i] = make_uint4(0, 0, 0, 0);
-  }
-  for (size_t i = t0; i < heads; i += stride) {
-    HeadState& st = p.state[i];
-    st.lo_key = 0;
-    st.cand_count = 0;
-    st.max_w = 0;
-    st.max_m = 0;
-    st.dense = 0;
-    st.mode = 0;
-    st.dcand_count = 0;
-  }
-  for (size_t i = t0; i < size_t(p.B) * p.H_kv; i += stride) p.gflag[i] = 0;
-  if (blockIdx.x != 0) return;
-  __shared__ int64_t tmp[16];
-  const int per = (p.B + int(blockDim.x) - 1) / int(blockDim.x);
-  int64_t s = 0;
-  for (int i = 0; i < per; ++i) {
-    const int b = threadIdx.x * per + i;
-    if (b < p.B) s += int64_t(p.H_kv) * ((seq_geom(p, b).N + kPage - 1) / kPage);
-  }
-  int64_t total;
-  int64_t run = block_excl_scan(s, tmp, &total);
-  for (int i = 0; i < per; ++i) {
-    const int b = threadIdx.x * per + i;
-    if (b < p.B) {
-      p.seq_off[b] = run;
-      run += int64_t(p.H_kv) * ((seq_geom(p, b).N + kPage - 1) / kPage);
-    }
-  }
-  if (threadIdx.x == 0) p.seq_off[p.B] = total;
-}
-
-hipError_t launch_prep(const Params& p, hipStream_t s) {
-  const size_t n4 = size_t(p.B) * p.H_q * kHistStride / 4;
-  unsigned blocks = unsigned((n4 + 1023) / 1024);
-  if (blocks < 1) blocks = 1;
-  if (blocks > 256) blocks = 256;
-  hipLaunchKernelGGL(prep_kernel, dim3(blocks), dim3(1024), 0, s, p);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------- sample
+// ---------------------------------------------------------------- sample stride
 // Sample stride S = 2^s: at least kSampleMinPages pages of a (b, g) are
 // scored, at most one in 2^kSampleMaxLog2. Short sequences are scored whole,
-// which makes their threshold exact.
+// which makes their threshold exact. Page j is sampled iff j % S == S / 2.
 __device__ __forceinline__ int sample_log2(int P) {
   int s = 0;
   while (s < kSampleMaxLog2 && (P >> (s + 1)) >= kSampleMinPages) ++s;
   return s;
 }
 
+__device__ __forceinline__ int sampled_pages(int P) {
+  const int S = 1 << sample_log2(P);
+  const int half = S >> 1;
+  return P > half ? (P - half + S - 1) / S : 0;
+}
+
+// ---------------------------------------------------------------- prep
+// Clears the sample histograms, per-head state, group flags and candidate
+// counts, and writes the prefixes
+//   seq_off[b]  = sum_{b' < b} H_kv * pages(b')          (scan)
+//   samp_off[b] = sum_{b' < b} H_kv * sampled_pages(b')  (sample)
+// that map a linear page index to (sequence, KV head, page).
+__global__ __launch_bounds__(1024) void prep_kernel(Params p) {
+  const size_t heads = size_t(p.B) * p.H_q;
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  const size_t t0 = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const size_t n4 = heads * kHistStride / 4;
+  uint4* h4 = reinterpret_cast<uint4*>(p.hist);
+  for (size_t i = t0; i < n4; i += stride) h4[i] = make_uint4(0, 0, 0, 0);
+  for (size_t i = t0; i < heads * size_t(p.n_tiles); i += stride) p.tcnt[i] = 0;
+  for (size_t i = t0; i < heads; i += stride) {
+    HeadState& st = p.state[i];
+    st.lo_key = 0;
+    st.max_w = 0;
+    st.max_m = 0;
+    st.dense = 0;
+    st.thr_shift = 64;  // nothing passes an unset threshold
+    st.thr_lo = 0xFFFFFFFFu;
+    st.thr_hi = 0xFFFFFFFFu;
+  }
+  for (size_t i = t0; i < size_t(p.B) * p.H_kv; i += stride) p.gflag[i] = 0;
+  if (t0 == 0) *p.any_dense = 0;
+  if (blockIdx.x != 0) return;
+  __shared__ int64_t tmp[16];
+  const int per = (p.B + int(blockDim.x) - 1) / int(blockDim.x);
+  int64_t s = 0, ss = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = threadIdx.x * per + i;
+    if (b < p.B) {
+      const int P = (seq_geom(p, b).N + kPage - 1) / kPage;
+      s += int64_t(p.H_kv) * P;
+      ss += int64_t(p.H_kv) * sampled_pages(P);
+    }
+  }
+  int64_t total, stotal;
+  int64_t run = block_excl_scan(s, tmp, &total);
+  int64_t srun = block_excl_scan(ss, tmp, &stotal);
+  for (int i = 0; i < per; ++i) {
+    const int b = threadIdx.x * per + i;
+    if (b < p.B) {
+      const int P = (seq_geom(p, b).N + kPage - 1) / kPage;
+      p.seq_off[b] = run;
+      p.samp_off[b] = srun;
+      run += int64_t(p.H_kv) * P;
+      srun += int64_t(p.H_kv) * sampled_pages(P);
+    }
+  }
+  if (threadIdx.x == 0) {
+    p.seq_off[p.B] = total;
+    p.samp_off[p.B] = stotal;
+  }
+}
+
+hipError_t launch_prep(const Params& p, hipStream_t s) {
+  hipLaunchKernelGGL(prep_kernel, dim3(unsigned(2 * (p.num_cus > 0 ? p.num_cus : 256))), dim3(1024),
+                     0, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- sample
+// Persistent over the linear index of sampled pages (same (b, g, page)
+// order as the scan): each block takes one contiguous range, histograms the
+// scores of M per head in LDS and adds them to the global sample histogram
+// at the end of every (b, g) run.
 template <int G>
 __global__ __launch_bounds__(kScanThreads) void sample_kernel(Params p) {
   using C = ScanCfg<G>;
@@ -292,40 +311,61 @@ __global__ __launch_bounds__(kScanThreads) void sample_kernel(Params p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Lane<G> L;
-  const int bg = blockIdx.y;
-  const int b = bg / p.H_kv;
-  const int g = bg - b * p.H_kv;
-  const SeqGeom sg = seq_geom(p, b);
-  const int P = (sg.N + kPage - 1) / kPage;
-  const int S = 1 << sample_log2(P);
-  const int half = S >> 1;
-  const int nsamp = P > half ? (P - half + S - 1) / S : 0;
-  if (int(blockIdx.x) >= nsamp) return;
-
   for (int i = tid; i < G * C::NC * 65; i += kScanThreads) lhist[i] = 0;
-  uint4 qreg[G];
-  load_q<G>(p, b, g, L, qreg);
-  __syncthreads();
-  uint32_t* lh = lhist + L.F * C::NC * 65;
-  for (int t = blockIdx.x + wave * gridDim.x; t < nsamp; t += gridDim.x * kScanWaves) {
-    const int j = half + t * S;
-    float z[G];
-    page_scores<G>(p, page_of(p, b, j), g, L, qreg, z);
+
+  const int64_t T = p.samp_off[p.B];
+  const int64_t L0 = T * blockIdx.x / gridDim.x;
+  const int64_t L1 = T * (blockIdx.x + 1) / gridDim.x;
+  for (int64_t Lx = L0; Lx < L1;) {
+    // the largest b with samp_off[b] <= Lx (it has at least one sampled page)
+    int blo = 0, bhi = p.B - 1;
+    while (blo < bhi) {
+      const int mid = (blo + bhi + 1) >> 1;
+      if (p.samp_off[mid] <= Lx) blo = mid; else bhi = mid - 1;
+    }
+    const int b = blo;
+    const SeqGeom sg = seq_geom(p, b);
+    const int P = (sg.N + kPage - 1) / kPage;
+    const int S = 1 << sample_log2(P);
+    const int half = S >> 1;
+    const int ns = sampled_pages(P);
+    const int64_t rel = Lx - p.samp_off[b];
+    const int g = int(rel / ns);
+    const int t0 = int(rel - int64_t(g) * ns);
+    const int64_t end = min(L1, p.samp_off[b] + int64_t(g + 1) * ns);
+    const int n = int(end - Lx);
+    uint4 qreg[G];
+    load_q<G>(p, b, g, L, qreg);
+    __syncthreads();
+    uint32_t* lh = lhist + L.F * C::NC * 65;
+    for (int t = t0 + wave; t < t0 + n; t += kScanWaves) {
+      const int j = half + t * S;
+      float z[G];
+      page_scores<G>(p, page_of(p, b, j), g, L, qreg, z);
 #pragma unroll
-    for (int s = 0; s < G; ++s) {
-      const int n = j * kPage + L.tok(s);
-      if (n >= sg.lo && n < sg.hi) {
-        const uint32_t dg = f2key(z[s]) >> C::SHIFT;
-        atomicAdd(&lh[dg + (dg >> 6)], 1u);
+      for (int s = 0; s < G; ++s) {
+        const int pos = j * kPage + L.tok(s);
+        if (pos >= sg.lo && pos < sg.hi) {
+          const uint32_t dg = f2key(z[s]) >> C::SHIFT;
+          atomicAdd(&lh[dg + (dg >> 6)], 1u);
+        }
       }
     }
+    __syncthreads();
+    flush_hist<G>(lhist, p.hist, p, b, g);
+    __syncthreads();
+    Lx = end;
   }
-  __syncthreads();
-  flush_hist<G>(lhist, p.hist, p, b, g);
 }
 
 hipError_t launch_sample(const Params& p, hipStream_t s) {
-  const dim3 grid{unsigned(kSampleBlocks), unsigned(p.B * p.H_kv)}, block{unsigned(kScanThreads)};
+  const int64_t pages_max =
+      int64_t(p.B) * p.H_kv * ((int64_t(p.max_seq_len) + kPage - 1) / kPage);
+  int64_t blocks = (pages_max + 8 * kScanWaves - 1) / (8 * kScanWaves);
+  const int64_t cap = p.num_cus > 0 ? p.num_cus : 256;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid{unsigned(blocks)}, block{unsigned(kScanThreads)};
   switch (p.G) {
     case 1: hipLaunchKernelGGL(sample_kernel<1>, grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL(sample_kernel<2>, grid, block, 0, s, p); break;
@@ -389,7 +429,9 @@ __device__ uint32_t candidate_threshold(const Params& p, int bh, const SeqGeom& 
 
 // ---------------------------------------------------------------- scan
 // Persistent over the linear page index: each block takes one contiguous
-// range and works through it as segments of one (b, g).
+// range and works through it as segments of one (b, g), flushing its LDS
+// candidate staging every kFlushPages pages (such a run spans at most two
+// tiles, so one reservation per (head, tile) suffices).
 template <int G>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
   __shared__ uint32_t st_key[kStage];
@@ -397,7 +439,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
   __shared__ uint32_t s_fill;
   __shared__ uint32_t s_lo[G];
   __shared__ uint32_t lmax[G][2];     // max key over W, over M
-  __shared__ uint32_t s_hcnt[G], s_hbase[G];
+  __shared__ uint32_t s_cnt[G][2], s_base[G][2];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -426,44 +468,78 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
     __syncthreads();
     const uint32_t lo_f = s_lo[L.F];
     float* srow = p.scores + (bh0 + L.F) * p.n_cap;
+    uint64_t* crow = p.cand + (bh0 + L.F) * p.n_cap;
+    uint32_t* trow = p.tcnt + (bh0 + L.F) * p.n_tiles;
     uint32_t mw = 0u, mm = 0u;  // running max keys of head F over W and M
 
-    for (int jj = wave; jj < seg.npages; jj += kScanWaves) {
-      const int j = seg.j0 + jj;
-      float z[G];
-      page_scores<G>(p, page_of(p, b, j), g, L, qreg, z);
+    for (int sub0 = 0; sub0 < seg.npages; sub0 += kFlushPages) {
+      const int subn = min(kFlushPages, seg.npages - sub0);
+      const int tile0 = ((seg.j0 + sub0) * kPage) / kTile;
+      for (int jj = wave; jj < subn; jj += kScanWaves) {
+        const int j = seg.j0 + sub0 + jj;
+        float z[G];
+        page_scores<G>(p, page_of(p, b, j), g, L, qreg, z);
 #pragma unroll
-      for (int s = 0; s < G; ++s) {
-        const int n = j * kPage + L.tok(s);
-        const uint32_t key = f2key(z[s]);
-        const bool in_m = n >= sg.lo && n < sg.hi;
-        const bool in_w = !in_m && n < sg.N;
-        if (in_w) {
-          srow[n] = z[s];
-          mw = max(mw, key);
-        }
-        if (in_m) mm = max(mm, key);
-        const bool cand = in_m && key >= lo_f;
-        const uint64_t cm = __ballot(cand);
-        if (cm) {
-          const int leader = __ffsll((unsigned long long)cm) - 1;
-          uint32_t base = 0;
-          if (L.lane == leader) base = atomicAdd(&s_fill, uint32_t(__popcll(cm)));
-          base = __shfl(base, leader);
-          if (cand) {
-            const uint32_t idx = base + uint32_t(__popcll(cm & ((1ull << L.lane) - 1ull)));
-            if (idx < uint32_t(kStage)) {
-              st_key[idx] = key;
-              st_nh[idx] = uint32_t(n) | (uint32_t(L.F) << 27);
-            } else {
-              // staging full: append straight to the head's list
-              const uint32_t gi = atomicAdd(&p.state[bh0 + L.F].cand_count, 1u);
-              if (gi < uint32_t(p.cap))
-                p.cand[(bh0 + L.F) * p.cap + gi] = (uint64_t(key) << 32) | uint32_t(~uint32_t(n));
+        for (int s = 0; s < G; ++s) {
+          const int n = j * kPage + L.tok(s);
+          const uint32_t key = f2key(z[s]);
+          const bool in_m = n >= sg.lo && n < sg.hi;
+          const bool in_w = !in_m && n < sg.N;
+          if (in_w) {
+            srow[n] = z[s];
+            mw = max(mw, key);
+          }
+          if (in_m) mm = max(mm, key);
+          const bool cand = in_m && key >= lo_f;
+          const uint64_t cm = __ballot(cand);
+          if (cm) {
+            const int leader = __ffsll((unsigned long long)cm) - 1;
+            uint32_t base = 0;
+            if (L.lane == leader) base = atomicAdd(&s_fill, uint32_t(__popcll(cm)));
+            base = __shfl(base, leader);
+            if (cand) {
+              const uint32_t idx = base + uint32_t(__popcll(cm & ((1ull << L.lane) - 1ull)));
+              if (idx < uint32_t(kStage)) {
+                st_key[idx] = key;
+                st_nh[idx] = uint32_t(n) | (uint32_t(L.F) << 27);
+              } else {
+                // staging full: append straight to the (head, tile) list
+                const int t = n / kTile;
+                const uint32_t gi = atomicAdd(&trow[t], 1u);
+                crow[size_t(t) * kTile + gi] = (uint64_t(key) << 32) | uint32_t(n);
+              }
             }
           }
         }
       }
+      if (tid < 2 * G) s_cnt[tid >> 1][tid & 1] = 0;
+      __syncthreads();
+      // burst the staged candidates into the per-(head, tile) lists
+      const uint32_t nst = min(s_fill, uint32_t(kStage));
+      for (uint32_t i = tid; i < nst; i += kScanThreads) {
+        const uint32_t nh = st_nh[i];
+        const int n = int(nh & ((1u << 27) - 1u));
+        atomicAdd(&s_cnt[nh >> 27][n / kTile - tile0], 1u);
+      }
+      __syncthreads();
+      if (tid < 2 * G) {
+        const int hh = tid >> 1, ts = tid & 1;
+        const uint32_t c = s_cnt[hh][ts];
+        s_base[hh][ts] = c ? atomicAdd(&p.tcnt[(bh0 + hh) * p.n_tiles + tile0 + ts], c) : 0u;
+        s_cnt[hh][ts] = 0;
+      }
+      __syncthreads();
+      for (uint32_t i = tid; i < nst; i += kScanThreads) {
+        const uint32_t nh = st_nh[i];
+        const uint32_t hh = nh >> 27;
+        const int n = int(nh & ((1u << 27) - 1u));
+        const int t = n / kTile;
+        const uint32_t gi = s_base[hh][t - tile0] + atomicAdd(&s_cnt[hh][t - tile0], 1u);
+        p.cand[(bh0 + hh) * p.n_cap + size_t(t) * kTile + gi] = (uint64_t(st_key[i]) << 32) | uint32_t(n);
+      }
+      __syncthreads();
+      if (tid == 0) s_fill = 0;
+      __syncthreads();
     }
     // maxima: reduce over the lanes that carry the same head, then LDS
 #pragma unroll
@@ -479,35 +555,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
       if (mw) atomicMax(&lmax[L.F][0], mw);
       if (mm) atomicMax(&lmax[L.F][1], mm);
     }
-    if (tid < G) s_hcnt[tid] = 0;
     __syncthreads();
-
-    // burst the staged candidates into the per-head lists
-    const uint32_t nst = min(s_fill, uint32_t(kStage));
-    for (uint32_t i = tid; i < nst; i += kScanThreads) atomicAdd(&s_hcnt[st_nh[i] >> 27], 1u);
-    __syncthreads();
-    if (tid < G) {
-      const uint32_t c = s_hcnt[tid];
-      s_hbase[tid] = c ? atomicAdd(&p.state[bh0 + tid].cand_count, c) : 0u;
-      s_hcnt[tid] = 0;
-    }
-    if (tid >= 64 && tid < 64 + 2 * G) {
-      const int hh = (tid - 64) >> 1;
+    if (tid < 2 * G) {
+      const int hh = tid >> 1;
       const uint32_t v = lmax[hh][tid & 1];
       if (v) atomicMax((tid & 1) ? &p.state[bh0 + hh].max_m : &p.state[bh0 + hh].max_w, v);
       lmax[hh][tid & 1] = 0u;
     }
-    __syncthreads();
-    for (uint32_t i = tid; i < nst; i += kScanThreads) {
-      const uint32_t nh = st_nh[i];
-      const uint32_t hh = nh >> 27;
-      const uint32_t n = nh & ((1u << 27) - 1u);
-      const uint32_t gi = s_hbase[hh] + atomicAdd(&s_hcnt[hh], 1u);
-      if (gi < uint32_t(p.cap))
-        p.cand[(bh0 + hh) * p.cap + gi] = (uint64_t(st_key[i]) << 32) | uint32_t(~n);
-    }
-    __syncthreads();
-    if (tid == 0) s_fill = 0;
     __syncthreads();
     Lx = seg.end;
   }
@@ -535,19 +589,17 @@ hipError_t launch_scan(const Params& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- dense scan
-// For groups flagged by the selection: store every score and build the exact
-// per-head histogram of M (the dense path's filter and resolve start from
-// it). Blocks skip unflagged segments, so without flags nothing is read.
+// ---------------------------------------------------------------- rescan
+// For groups with a head whose candidates fell short: every member of M of
+// those heads becomes a candidate, written at its place in the tile list
+// (the list of tile t holds positions max(t * kTile, lo) .. in order).
+// Blocks skip unflagged segments, so without flags nothing is read.
 template <int G>
 __global__ __launch_bounds__(kScanThreads) void dense_scan_kernel(Params p) {
-  using C = ScanCfg<G>;
-  __shared__ uint32_t lhist[G * C::NC * 65];
+  if (*p.any_dense == 0u) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Lane<G> L;
-  bool cleared = false;
-
   const int64_t T = p.seq_off[p.B];
   const int64_t L0 = T * blockIdx.x / gridDim.x;
   const int64_t L1 = T * (blockIdx.x + 1) / gridDim.x;
@@ -556,16 +608,12 @@ __global__ __launch_bounds__(kScanThreads) void dense_scan_kernel(Params p) {
     Lx = seg.end;
     const int b = seg.b, g = seg.g;
     if (!p.gflag[size_t(b) * p.H_kv + g]) continue;
-    if (!cleared) {
-      for (int i = tid; i < G * C::NC * 65; i += kScanThreads) lhist[i] = 0;
-      cleared = true;
-    }
     const SeqGeom sg = seq_geom(p, b);
+    const size_t bh = size_t(b) * p.H_q + size_t(g) * G + L.F;
+    const bool mine = p.state[bh].dense != 0u;
     uint4 qreg[G];
     load_q<G>(p, b, g, L, qreg);
-    __syncthreads();
-    float* srow = p.scores + (size_t(b) * p.H_q + size_t(g) * G + L.F) * p.n_cap;
-    uint32_t* lh = lhist + L.F * C::NC * 65;
+    uint64_t* crow = p.cand + bh * p.n_cap;
     for (int jj = wave; jj < seg.npages; jj += kScanWaves) {
       const int j = seg.j0 + jj;
       float z[G];
@@ -573,16 +621,12 @@ __global__ __launch_bounds__(kScanThreads) void dense_scan_kernel(Params p) {
 #pragma unroll
       for (int s = 0; s < G; ++s) {
         const int n = j * kPage + L.tok(s);
-        srow[n] = z[s];
-        if (n >= sg.lo && n < sg.hi) {
-          const uint32_t dg = f2key(z[s]) >> C::SHIFT;
-          atomicAdd(&lh[dg + (dg >> 6)], 1u);
+        if (mine && n >= sg.lo && n < sg.hi) {
+          const int t0 = (n / kTile) * kTile;
+          crow[size_t(t0) + (n - max(t0, sg.lo))] = (uint64_t(f2key(z[s])) << 32) | uint32_t(n);
         }
       }
     }
-    __syncthreads();
-    flush_hist<G>(lhist, p.dhist, p, b, g);
-    __syncthreads();
   }
 }
 

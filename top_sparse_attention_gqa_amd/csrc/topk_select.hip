@@ -5,61 +5,115 @@
 //
 // Scores are compared through an order-preserving uint32 key, and the
 // choice among members is made on the composite  c = key' << 32 | ~n
-// (key' = key relative to a known lower bound): a larger composite is a
-// larger score, then a lower position, and all composites are distinct, so
-// "the need largest composites" is the unique tie-broken top-k.
+// (key' = key minus a known lower bound): a larger composite is a larger
+// score, then a lower position, and all composites are distinct, so "the
+// k_eff largest composites" is the unique tie-broken top-k.
 //
-// select (common path, one block per head): the scan left every member of M
-// scoring at or above the head's sampled threshold in a candidate list. If
-// the list holds at least k_eff entries and did not overflow, the top-k of M
-// is the top-k of the list; a radix select on the composite finds it (the
-// bucket around the k-th entry is finished in LDS). The block writes the
-// head's selection bitmap, per-tile counts and the selected scores.
-// Otherwise the head is flagged for the dense path:
-//  dense scan   - every score stored, exact histogram of M;
-//  dense filter - threshold bucket from the histogram; keys above it go
-//                 straight into the bitmap, keys inside it to a list;
-//  dense resolve- the same radix select inside the bucket (or over the row
-//                 if the bucket overflowed the list).
+// select (one block per head): the scan left every member of M scoring at
+// or above the head's sampled threshold in per-tile candidate lists. If they
+// hold at least k_eff entries, the top-k of M is the top-k of the lists; a
+// radix select on the composite finds the exact threshold (the bucket around
+// the k-th entry is finished in LDS) and records it in the head state. The
+// members are taken later, tile by tile, by the gather blocks. A head with
+// too few candidates is flagged; the dense stage rescans its group with
+// every member of M as a candidate and selects again.
 #include "ra_internal.h"
 
 namespace ra {
 
-constexpr int kFiltThreads = 256;  // 4 waves x 2048 positions = one tile
-constexpr int kFiltIters = kTile / kFiltThreads;  // 32 positions per lane
 constexpr int kSelThreads = 1024;
+constexpr int kWin = 2048;                 // tiles per LDS prefix window
 constexpr int kSubCap = 4096;              // LDS list for one radix sub-bucket
-constexpr int kMaxTiles = RA_MAX_SEQ_LEN / kTile;
 
 // ---------------------------------------------------------------- sources
 // Each source enumerates composites of members with (c, n).
 
-// Sparse candidate list: c = (key - lo) << 32 | ~n.
-struct CandSource {
-  const uint64_t* c;
-  uint32_t count;
-  uint32_t lo;
-  template <typename Fn>
-  __device__ __forceinline__ void for_each(Fn&& fn) const {
-    for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) {
-      const uint64_t v = c[i];
-      const uint32_t notn = uint32_t(v);
-      fn((uint64_t(uint32_t(v >> 32) - lo) << 32) | notn, int(~notn));
-    }
-  }
-};
+// Entries loaded per thread before any is used, so that a pass over a list
+// costs a few memory round trips rather than one per entry.
+constexpr int kBatch = 8;
 
-// Dense-path bucket list: c = (key & low_mask) << 32 | ~n.
-struct BucketList {
-  const uint64_t* c;
-  uint32_t count;
-  uint64_t low_mask;
+// A head's per-tile candidate lists (entries key << 32 | n; the list of
+// tile t holds tcnt[t] entries from list + t * kTile), enumerated as
+// composites c = (key - lo) << 32 | ~n. The list lengths of a window of
+// kWin tiles are prefix-summed in LDS; entry i of the window is found by a
+// binary search over that prefix. In dense mode the lengths follow from the
+// geometry: every member of M is in its tile's list.
+struct TileLists {
+  const uint64_t* list;
+  const uint32_t* tcnt;
+  uint32_t* pre;      // LDS [kWin + 1]
+  int32_t* s_w0;      // LDS: first tile of the window held in pre (-1: none)
+  int64_t* tmp;       // LDS [16]
+  int t_lo, t_hi;     // tiles that overlap M
+  int m_lo, m_hi;     // M
+  uint32_t lo;
+  bool dense;
+
+  __device__ __forceinline__ uint32_t tile_count(int t) const {
+    if (!dense) return tcnt[t];
+    const int a = max(t * kTile, m_lo), e = min((t + 1) * kTile, m_hi);
+    return e > a ? uint32_t(e - a) : 0u;
+  }
+
+  // Prefix of the list lengths of tiles [w0, w0 + nw). Block-wide.
+  __device__ void load(int w0, int nw) const {
+    if (*s_w0 == w0) return;
+    constexpr int per = kWin / kSelThreads;
+    const int tid = threadIdx.x;
+    uint32_t c[per];
+    int64_t sum = 0;
+#pragma unroll
+    for (int u = 0; u < per; ++u) {
+      const int i = tid * per + u;
+      c[u] = i < nw ? tile_count(w0 + i) : 0u;
+      sum += c[u];
+    }
+    int64_t total;
+    int64_t run = block_excl_scan(sum, tmp, &total);
+#pragma unroll
+    for (int u = 0; u < per; ++u) {
+      pre[tid * per + u] = uint32_t(run);
+      run += c[u];
+    }
+    if (tid == 0) {
+      pre[kWin] = uint32_t(total);
+      *s_w0 = w0;
+    }
+    __syncthreads();
+  }
+
   template <typename Fn>
   __device__ __forceinline__ void for_each(Fn&& fn) const {
-    for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) {
-      const uint64_t v = c[i];
-      const uint32_t notn = uint32_t(v);
-      fn((uint64_t(uint32_t(v >> 32)) & low_mask) << 32 | notn, int(~notn));
+    const uint32_t l = lo;
+    for (int w0 = t_lo; w0 < t_hi; w0 += kWin) {
+      const int nw = min(kWin, t_hi - w0);
+      load(w0, nw);
+      const uint32_t total = pre[kWin];
+      const uint32_t step = blockDim.x * kBatch;
+      for (uint32_t base = 0; base < total; base += step) {
+        uint64_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const uint32_t i = base + u * blockDim.x + threadIdx.x;
+          v[u] = 0ull;
+          if (i < total) {
+            int a = 0, e = nw - 1;
+            while (a < e) {
+              const int mid = (a + e + 1) >> 1;
+              if (pre[mid] <= i) a = mid; else e = mid - 1;
+            }
+            v[u] = list[size_t(w0 + a) * kTile + (i - pre[a])];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (base + u * blockDim.x + threadIdx.x < total) {
+            const uint32_t n = uint32_t(v[u]);
+            fn((uint64_t(uint32_t(v[u] >> 32) - l) << 32) | uint32_t(~n), int(n));
+          }
+        }
+      }
+      if (t_hi - t_lo > kWin) __syncthreads();
     }
   }
 };
@@ -73,24 +127,6 @@ struct LdsSource {
     for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) {
       const uint64_t v = c[i];
       fn(v, int(~uint32_t(v)));
-    }
-  }
-};
-
-// A head's whole score row filtered to one bucket (dense path, when the
-// bucket overflowed its list).
-struct RowSource {
-  const float* row;
-  int lo, hi;
-  uint32_t b1;
-  int shift;
-  uint64_t low_mask;
-  template <typename Fn>
-  __device__ __forceinline__ void for_each(Fn&& fn) const {
-    for (int n = lo + int(threadIdx.x); n < hi; n += int(blockDim.x)) {
-      const uint32_t key = f2key(row[n]);
-      if ((key >> shift) != b1) continue;
-      fn((uint64_t(key) & low_mask) << 32 | uint32_t(~uint32_t(n)), n);
     }
   }
 };
@@ -162,95 +198,90 @@ __device__ void radix_finish(const Src& src, const Radix& rx, int TB, uint32_t& 
   }
 }
 
-// Take every composite whose top plen bits are >= prefix.
-template <typename Src, typename Take>
-__device__ void take_from(const Src& src, int TB, uint64_t prefix, int plen, Take&& take) {
-  src.for_each([&](uint64_t c, int n) {
-    if ((c >> (TB - plen)) >= prefix) take(c, n);
-  });
-}
-
-// The need largest composites of a source: one pass over it; if that does not
-// settle it and the chosen sub-bucket fits LDS, members above it are taken
-// at once and the sub-bucket is finished in LDS.
-template <typename Src, typename Take>
-__device__ void select_top(const Src& src, const Radix& rx, int TB, uint32_t need,
-                           uint64_t* sub, uint32_t* s_n, Take&& take) {
-  uint64_t prefix = 0;
-  int plen = 0;
+// Composite prefix (top plen of TB bits) of the need-th largest member of a
+// source: one pass over it; if that does not settle it and the chosen
+// sub-bucket fits LDS, the sub-bucket is copied there and finished in LDS.
+// Members whose top plen bits are >= the returned prefix are exactly the
+// need largest.
+template <typename Src>
+__device__ void find_threshold(const Src& src, const Radix& rx, int TB, uint32_t need,
+                               uint64_t* sub, uint32_t* s_n, uint64_t& prefix, int& plen) {
+  prefix = 0;
+  plen = 0;
   const uint32_t cnt1 = radix_pass(src, rx, TB, need, prefix, plen);
-  if (cnt1 == need || plen >= TB) {
-    take_from(src, TB, prefix, plen, take);
-    return;
-  }
+  if (cnt1 == need || plen >= TB) return;
   if (cnt1 > uint32_t(kSubCap)) {
     radix_finish(src, rx, TB, need, prefix, plen);
-    take_from(src, TB, prefix, plen, take);
     return;
   }
   if (threadIdx.x == 0) *s_n = 0;
   __syncthreads();
   const uint64_t pf = prefix;
   const int pl = plen;
-  src.for_each([&](uint64_t c, int n) {
-    const uint64_t top = c >> (TB - pl);
-    if (top > pf) {
-      take(c, n);
-    } else if (top == pf) {
-      sub[atomicAdd(s_n, 1u)] = c;
-    }
+  src.for_each([&](uint64_t c, int) {
+    if ((c >> (TB - pl)) == pf) sub[atomicAdd(s_n, 1u)] = c;
   });
   __syncthreads();
   const LdsSource lds{sub, *s_n};
   radix_finish(lds, rx, TB, need, prefix, plen);
-  take_from(lds, TB, prefix, plen, take);
 }
 
 // ---------------------------------------------------------------- select
+__device__ __forceinline__ int bit_length(uint32_t x) { return 32 - __clz(x); }
+
+// Exact threshold of head bh over its lists; writes it into the head state.
+__device__ void decide(const Params& p, int bh, const SeqGeom& sg, uint32_t lo, uint32_t max_m,
+                       bool dense) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t s_d, s_above, s_cnt, s_n;
+  __shared__ uint64_t sub[kSubCap];
+  __shared__ uint32_t pre[kWin + 1];
+  __shared__ int32_t s_w0;
+  __shared__ int64_t tmp[16];
+  if (threadIdx.x == 0) s_w0 = -1;
+  __syncthreads();
+  const uint32_t span = max_m > lo ? max_m - lo : 1u;
+  const int TB = 32 + bit_length(span);
+  const TileLists src{p.cand + size_t(bh) * p.n_cap, p.tcnt + size_t(bh) * p.n_tiles, pre, &s_w0,
+                      tmp, sg.lo / kTile, (sg.hi - 1) / kTile + 1, sg.lo, sg.hi, lo, dense};
+  const Radix rx{hist, &s_d, &s_above, &s_cnt};
+  uint64_t prefix;
+  int plen;
+  find_threshold(src, rx, TB, uint32_t(sg.k_eff), sub, &s_n, prefix, plen);
+  if (threadIdx.x == 0) {
+    HeadState& w = p.state[bh];
+    w.lo_key = lo;
+    w.thr_shift = uint32_t(TB - plen);
+    w.thr_lo = uint32_t(prefix);
+    w.thr_hi = uint32_t(prefix >> 32);
+  }
+}
+
+// One block per head: count the candidates; decide the threshold, or flag
+// the head (and its group) for the rescan when there are fewer than k_eff.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
   const int bh = blockIdx.x;
   const int b = bh / p.H_q;
   const int g = (bh - b * p.H_q) / p.G;
   const SeqGeom sg = seq_geom(p, b);
-  const int nt = (sg.N + kTile - 1) / kTile;
-  const int tid = threadIdx.x;
-
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t s_d, s_above, s_cnt, s_n;
-  __shared__ uint64_t sub[kSubCap];
-  __shared__ uint32_t tcnt[kMaxTiles];
-
+  if (sg.k_eff == 0) return;  // the unset threshold takes nothing
+  __shared__ int64_t tmp[16];
+  const int t_lo = sg.lo / kTile, t_hi = (sg.hi - 1) / kTile + 1;
+  const uint32_t* tc = p.tcnt + size_t(bh) * p.n_tiles;
+  int64_t c = 0;
+  for (int t = t_lo + int(threadIdx.x); t < t_hi; t += kSelThreads) c += tc[t];
+  int64_t m;
+  block_excl_scan(c, tmp, &m);
   const HeadState st = p.state[bh];
-  const uint32_t m = st.cand_count;
-  if (sg.k_eff > 0 && (m < uint32_t(sg.k_eff) || m > uint32_t(p.cap))) {
-    // the sample's margin did not hold: decide this head on the dense path
-    if (tid == 0) {
+  if (m < sg.k_eff) {
+    if (threadIdx.x == 0) {
       p.state[bh].dense = 1u;
       atomicOr(&p.gflag[size_t(b) * p.H_kv + g], 1u);
+      atomicAdd(p.any_dense, 1u);
     }
     return;
   }
-
-  uint64_t* bm = p.bitmap + size_t(bh) * (p.n_cap / 64);
-  for (int i = tid; i < nt * kWordsPerTile; i += kSelThreads) bm[i] = 0ull;
-  for (int i = tid; i < nt; i += kSelThreads) tcnt[i] = 0u;
-  __syncthreads();
-
-  if (sg.k_eff > 0) {
-    const uint32_t lo = st.lo_key;
-    const uint32_t span = st.max_m > lo ? st.max_m - lo : 1u;
-    const int TB = 32 + (32 - __clz(span));
-    const CandSource src{p.cand + size_t(bh) * p.cap, m, lo};
-    const Radix rx{hist, &s_d, &s_above, &s_cnt};
-    float* srow = p.scores + size_t(bh) * p.n_cap;
-    select_top(src, rx, TB, uint32_t(sg.k_eff), sub, &s_n, [&](uint64_t c, int n) {
-      atomicOr(reinterpret_cast<unsigned long long*>(&bm[n >> 6]), 1ull << (n & 63));
-      atomicAdd(&tcnt[n / kTile], 1u);
-      srow[n] = key2f(uint32_t(c >> 32) + lo);
-    });
-  }
-  __syncthreads();
-  for (int i = tid; i < nt; i += kSelThreads) p.tile_cnt[size_t(bh) * p.n_tiles + i] = tcnt[i];
+  decide(p, bh, sg, st.lo_key, st.max_m, false);
 }
 
 hipError_t launch_select(const Params& p, hipStream_t s) {
@@ -259,151 +290,21 @@ hipError_t launch_select(const Params& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- dense
-__global__ __launch_bounds__(kFiltThreads) void dense_filter_kernel(Params p) {
-  const int tile = blockIdx.x;
-  const int bh = blockIdx.y;
-  const int b = bh / p.H_q;
-  const SeqGeom sg = seq_geom(p, b);
-  const int t0 = tile * kTile;
-  if (t0 >= sg.N || !p.state[bh].dense) return;
-
-  const int HB = hist_bits(p.G);
-  const int SHIFT = 32 - HB;
-  const int NC = 1 << (HB - 6);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-
-  __shared__ uint32_t s_b1, s_mode, s_cbase;
-  __shared__ uint32_t s_cnt[kFiltThreads / 64], s_cc[kFiltThreads / 64];
-
-  // issue every score load of this lane before anything waits
-  const float* row = p.scores + size_t(bh) * p.n_cap;
-  const int wbase = t0 + wave * (kTile / 4);
-  float z[kFiltIters];
-#pragma unroll
-  for (int it = 0; it < kFiltIters; ++it) z[it] = row[wbase + it * 64 + lane];
-
-  if (wave == 0) {
-    uint32_t b1 = 0xFFFFFFFFu, mode = 0, above = 0, need = 0;
-    if (sg.k_eff > 0) {
-      const uint32_t* gh = p.dhist + size_t(bh) * kHistStride;
-      const uint32_t k = uint32_t(sg.k_eff);
-      // coarse bucket holding the k-th largest (from the top)
-      const uint32_t c = lane < NC ? gh[kFineBins + lane] : 0u;
-      const uint32_t suf = wave_suffix_sum(c);
-      const uint64_t mc = __ballot(suf >= k);
-      const int cs = mc ? 63 - __clzll(mc) : 0;
-      const uint32_t above_c = __shfl(suf - c, cs);
-      // fine bucket inside it
-      const uint32_t f = gh[cs * 64 + lane];
-      const uint32_t fsuf = wave_suffix_sum(f) + above_c;
-      const uint64_t mf = __ballot(fsuf >= k);
-      const int fl = mf ? 63 - __clzll(mf) : 0;
-      b1 = uint32_t(cs * 64 + fl);
-      above = __shfl(fsuf - f, fl);
-      const uint32_t cnt = __shfl(f, fl);
-      need = k - above;
-      mode = cnt <= uint32_t(p.dcap) ? kModeCand : kModeRescan;
-    }
-    if (lane == 0) {
-      s_b1 = b1;
-      s_mode = mode;
-      if (tile == 0) {
-        HeadState& st = p.state[bh];
-        st.b1 = b1;
-        st.above1 = above;
-        st.need1 = need;
-        st.mode = mode;
-      }
-    }
-  }
-  __syncthreads();
-  const uint32_t b1 = s_b1;
-  const bool cand_mode = s_mode == kModeCand;
-
-  // above-bucket members become bitmap words (lane it keeps word it)
-  uint64_t myword = 0;
-  uint32_t cnt = 0, ccnt = 0;
-#pragma unroll
-  for (int it = 0; it < kFiltIters; ++it) {
-    const int n = wbase + it * 64 + lane;
-    const bool valid = n >= sg.lo && n < sg.hi;
-    const uint32_t dg = f2key(z[it]) >> SHIFT;
-    const uint64_t m = __ballot(valid && dg > b1);
-    if (lane == it) myword = m;
-    cnt += uint32_t(__popcll(m));
-    ccnt += uint32_t(__popcll(__ballot(cand_mode && valid && dg == b1)));
-  }
-  if (lane < kFiltIters) p.bitmap[size_t(bh) * (p.n_cap / 64) + (wbase >> 6) + lane] = myword;
-  if (lane == 0) {
-    s_cnt[wave] = cnt;
-    s_cc[wave] = ccnt;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t t = 0, c = 0;
-    for (int w = 0; w < kFiltThreads / 64; ++w) {
-      t += s_cnt[w];
-      c += s_cc[w];
-    }
-    p.tile_cnt[size_t(bh) * p.n_tiles + tile] = t;
-    // one reservation per block in the head's bucket list
-    s_cbase = c ? atomicAdd(&p.state[bh].dcand_count, c) : 0u;
-  }
-  __syncthreads();
-  if (cand_mode && ccnt) {
-    uint32_t base = s_cbase;
-    for (int w = 0; w < wave; ++w) base += s_cc[w];
-    uint64_t* cl = p.dcand + size_t(bh) * p.dcap;
-#pragma unroll
-    for (int it = 0; it < kFiltIters; ++it) {
-      const int n = wbase + it * 64 + lane;
-      const bool valid = n >= sg.lo && n < sg.hi;
-      const uint32_t key = f2key(z[it]);
-      const bool cd = valid && (key >> SHIFT) == b1;
-      const uint64_t cm = __ballot(cd);
-      if (cd) {
-        const uint32_t idx = base + uint32_t(__popcll(cm & ((1ull << lane) - 1ull)));
-        if (idx < uint32_t(p.dcap)) cl[idx] = (uint64_t(key) << 32) | uint32_t(~uint32_t(n));
-      }
-      base += uint32_t(__popcll(cm));
-    }
-  }
-}
-
-__global__ __launch_bounds__(kSelThreads) void dense_resolve_kernel(Params p) {
+// After the rescan: the flagged heads select over every member of M (their
+// lists now hold all of it, so the candidate counts are the tile sizes).
+__global__ __launch_bounds__(kSelThreads) void reselect_kernel(Params p) {
+  if (*p.any_dense == 0u) return;
   const int bh = blockIdx.x;
-  const int b = bh / p.H_q;
-  const SeqGeom sg = seq_geom(p, b);
-  if (sg.k_eff == 0) return;
   const HeadState st = p.state[bh];
-  if (!st.dense || st.mode == 0) return;
-
-  const int HB = hist_bits(p.G);
-  const int TB = 64 - HB;
-  const uint64_t low_mask = (1ull << (32 - HB)) - 1ull;
-
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t s_d, s_above, s_cnt, s_n;
-  __shared__ uint64_t sub[kSubCap];
-  const Radix rx{hist, &s_d, &s_above, &s_cnt};
-  uint64_t* bm = p.bitmap + size_t(bh) * (p.n_cap / 64);
-  auto take = [&](uint64_t, int n) {
-    atomicOr(reinterpret_cast<unsigned long long*>(&bm[n >> 6]), 1ull << (n & 63));
-    atomicAdd(&p.tile_cnt[size_t(bh) * p.n_tiles + n / kTile], 1u);
-  };
-  if (st.mode == kModeRescan) {
-    const RowSource src{p.scores + size_t(bh) * p.n_cap, sg.lo, sg.hi, st.b1, 32 - HB, low_mask};
-    uint32_t need = st.need1;
-    uint64_t prefix = 0;
-    int plen = 0;
-    radix_finish(src, rx, TB, need, prefix, plen);
-    take_from(src, TB, prefix, plen, take);
-    return;
+  if (!st.dense) return;
+  const SeqGeom sg = seq_geom(p, bh / p.H_q);
+  const int t_lo = sg.lo / kTile, t_hi = (sg.hi - 1) / kTile + 1;
+  uint32_t* tc = p.tcnt + size_t(bh) * p.n_tiles;
+  for (int t = t_lo + int(threadIdx.x); t < t_hi; t += kSelThreads) {
+    const int a = max(t * kTile, sg.lo), e = min((t + 1) * kTile, sg.hi);
+    tc[t] = uint32_t(e - a);
   }
-  const BucketList src{p.dcand + size_t(bh) * p.dcap, min(st.dcand_count, uint32_t(p.dcap)), low_mask};
-  select_top(src, rx, TB, st.need1, sub, &s_n, take);
+  decide(p, bh, sg, 0u, st.max_m, true);
 }
 
 hipError_t launch_dense_scan(const Params& p, hipStream_t s);  // score_scan.hip
@@ -411,12 +312,7 @@ hipError_t launch_dense_scan(const Params& p, hipStream_t s);  // score_scan.hip
 hipError_t launch_dense(const Params& p, hipStream_t s) {
   hipError_t e = launch_dense_scan(p, s);
   if (e != hipSuccess) return e;
-  const unsigned tiles = unsigned((int64_t(p.max_seq_len) + kTile - 1) / kTile);
-  hipLaunchKernelGGL(dense_filter_kernel, dim3(tiles, unsigned(p.B * p.H_q)),
-                     dim3(kFiltThreads), 0, s, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dense_resolve_kernel, dim3(unsigned(p.B * p.H_q)), dim3(kSelThreads), 0, s, p);
+  hipLaunchKernelGGL(reselect_kernel, dim3(unsigned(p.B * p.H_q)), dim3(kSelThreads), 0, s, p);
   return hipGetLastError();
 }
 
