@@ -49,7 +49,7 @@ extern "C" {
 #define RA_ABI_VERSION 1
 #define RA_HEAD_DIM 128
 #define RA_PAGE_SIZE 64
-#define RA_MAX_SEQ_LEN (1 << 27)
+#define RA_MAX_SEQ_LEN (1 << 24) /* 16,777,216 positions per sequence */
 #define RA_MAX_BATCH 65535
 
 typedef enum ra_status {
@@ -136,14 +136,15 @@ ra_status ra_decode_step(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
 
 /*
  * The kernels of one decode step, in launch order. ra_decode_step runs
- * stages RA_STAGE_PREP .. RA_STAGE_MERGE; ra_decode_stages runs a contiguous
+ * stages RA_STAGE_SAMPLE .. RA_STAGE_MERGE; ra_decode_stages runs a contiguous
  * sub-range of them with the same arguments, so each kernel can be timed or
  * inspected on its own. State passes between stages through `ws`, so a range
  * must start where the previous range on the same workspace ended.
  */
 typedef enum ra_stage {
-  RA_STAGE_PREP = 0,   /* clear histograms and counters, sequence offsets */
-  RA_STAGE_SAMPLE = 1, /* score a sample of pages: per-head candidate threshold */
+  RA_STAGE_SAMPLE = 0, /* score one page in S (S <= 64) of every sequence */
+  RA_STAGE_THRESHOLD = 1, /* per head: candidate threshold from the sample,
+                             reset of the per-call state */
   RA_STAGE_SCAN = 2,   /* all scores; keep W and the candidates above it */
   RA_STAGE_SELECT = 3, /* exact top-k threshold over the candidates, ties to
                           the lower position; flags heads with too few */

@@ -52,7 +52,8 @@ def test_workspace_size():
     assert ra.decode_workspace_bytes(1, 30, 8, 1024, 1) == 0   # H_q % H_kv
     assert ra.decode_workspace_bytes(1, 32, 8, 0, 1) == 0
     assert ra.decode_workspace_bytes(1, 32, 8, 1024, -1) == 0
-    assert ra.decode_workspace_bytes(1, 32, 8, (1 << 27) + 1, 1) == 0
+    assert ra.decode_workspace_bytes(1, 32, 8, (1 << 24) + 1, 1) == 0
+    assert ra.decode_workspace_bytes(1, 32, 8, 1 << 24, 1) > 0
     off, stride = ra.workspace_scores_offset(2, 4, 1, 5000, 64)
     assert off == 0 and stride % 8192 == 0 and stride >= 5000
 

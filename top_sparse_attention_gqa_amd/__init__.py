@@ -21,10 +21,10 @@ from ._lib import (  # noqa: F401
     STAGE_GATHER,
     STAGE_MERGE,
     STAGE_NAMES,
-    STAGE_PREP,
     STAGE_SAMPLE,
     STAGE_SCAN,
     STAGE_SELECT,
+    STAGE_THRESHOLD,
     KVLayer,
     KVLayerStruct,
     RAError,

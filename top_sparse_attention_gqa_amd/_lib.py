@@ -29,10 +29,10 @@ RA_ERR_WORKSPACE = 2
 RA_ERR_UNSUPPORTED = 3
 RA_ERR_HIP = 4
 
-(STAGE_PREP, STAGE_SAMPLE, STAGE_SCAN, STAGE_SELECT, STAGE_DENSE, STAGE_GATHER,
+(STAGE_SAMPLE, STAGE_THRESHOLD, STAGE_SCAN, STAGE_SELECT, STAGE_DENSE, STAGE_GATHER,
  STAGE_MERGE) = range(7)
 STAGE_COUNT = 7
-STAGE_NAMES = ["prep", "sample", "scan", "select", "dense", "gather", "merge"]
+STAGE_NAMES = ["sample", "threshold", "scan", "select", "dense", "gather", "merge"]
 
 HEAD_DIM = 128
 PAGE_SIZE = 64
@@ -162,7 +162,7 @@ def kv_append(kv: KVLayer, k_new, v_new, pos, stream=None) -> None:
 
 
 def decode_stages(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, window,
-                  out, out_lse, out_idx, ws, first=STAGE_PREP, last=STAGE_MERGE,
+                  out, out_lse, out_idx, ws, first=STAGE_SAMPLE, last=STAGE_MERGE,
                   stream=None) -> None:
     """ra_decode_stages (ra_decode_step when first..last covers every stage)."""
     B, H_q = q.shape[0], q.shape[1]
@@ -194,9 +194,8 @@ def decode_step(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, window,
 
 
 def scores_view(ws: torch.Tensor, B, H_q, H_kv, max_seq_len, k_max) -> torch.Tensor:
-    """The fp32 score rows [B][H_q][row_stride] inside a workspace: W and
-    the retrieved positions after the select stage (every position of a head
-    that took the dense path)."""
+    """The fp32 score rows [B][H_q][row_stride] inside a workspace: after the
+    gather stage they hold the scores of W and of the retrieved positions."""
     off, stride = workspace_scores_offset(B, H_q, H_kv, max_seq_len, k_max)
     n = B * H_q * stride
     return ws[off:off + 4 * n].view(torch.float32).view(B, H_q, stride)

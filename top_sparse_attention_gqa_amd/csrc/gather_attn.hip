@@ -4,22 +4,21 @@
 // Eqs. (3)-(5); backup frame "the normalization identity": merging disjoint
 // partials gives the exact softmax over their union).
 //
-// One block per (sequence, KV head, tile of 8192 positions). The block first
-// takes each head's retrieved members of the tile: the entries of the
-// (head, tile) candidate list at or above the head's exact threshold. It
-// marks them in an LDS bitmap and stores their scores next to the scores of
-// W that the scan left. It then walks the union over the group's G query
-// heads of those positions and the tile's static positions in ascending
-// order, reads each V row (256 contiguous bytes) once, and accumulates for
-// every head that attends to it: Z = sum e^{z - m}, N = sum e^{z - m} v,
-// with m the head's largest score over W u Omega (the scan records it), so
-// no partial can overflow. The sorted retrieved positions of the tile
-// replace the consumed list, with their count.
+// One block per (sequence, KV head, tile of 8192 positions = two units). The
+// block first takes each head's retrieved members of the tile: the entries
+// of the tile's (head, unit) candidate lists at or above the head's exact
+// threshold. It marks them in an LDS bitmap, stores their scores next to the
+// scores of W that the scan left, and writes their positions, ascending, to
+// out_idx from the offset the selection computed for the tile. It then walks
+// the union over the group's G query heads of those positions and the
+// tile's static positions in ascending order, reads each V row (256
+// contiguous bytes) once, and accumulates for every head that attends to
+// it: Z = sum e^{z - m}, N = sum e^{z - m} v, with m the head's largest
+// score over W u Omega (the scan records it), so no partial can overflow.
 //
 // merge (one block per query head) combines the tile partials:
 // out = sum_t e^{m_t - m} N_t / sum_t e^{m_t - m} Z_t, lse = m + ln(...),
-// concatenates the tiles' retrieved positions into out_idx and pads it
-// with -1 after k_eff.
+// and pads out_idx with -1 after k_eff.
 #include "ra_internal.h"
 
 namespace ra {
@@ -86,30 +85,35 @@ __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
 
   // each head's retrieved members of this tile: the list entries whose
   // composite (key - lo) << 32 | ~n clears the head's threshold
+  const int units_seq = (sg.N + kUnit - 1) / kUnit;
   for (int hh = 0; hh < G; ++hh) {
     const HeadState st = p.state[bh0 + hh];
     if (st.thr_shift >= 64u) continue;
-    const uint32_t cnt = p.tcnt[(bh0 + hh) * p.n_tiles + tile];
-    const uint64_t* list = p.cand + (bh0 + hh) * p.n_cap + size_t(t0);
-    float* srow = p.scores + (bh0 + hh) * p.n_cap;
     const uint64_t thr = (uint64_t(st.thr_hi) << 32) | st.thr_lo;
-    for (uint32_t base = 0; base < cnt; base += kGathThreads * kListBatch) {
-      uint64_t v[kListBatch];
+    float* srow = p.scores + (bh0 + hh) * p.n_cap;
+    for (int uu = 0; uu < 2; ++uu) {
+      const int unit = 2 * tile + uu;
+      if (unit >= units_seq) break;
+      const uint32_t cnt = p.ucnt[(bh0 + hh) * p.n_units + unit];
+      const uint64_t* list = p.cand + (bh0 + hh) * p.n_cap + size_t(unit) * kUnit;
+      for (uint32_t base = 0; base < cnt; base += kGathThreads * kListBatch) {
+        uint64_t v[kListBatch];
 #pragma unroll
-      for (int u = 0; u < kListBatch; ++u) {
-        const uint32_t i = base + u * kGathThreads + tid;
-        v[u] = i < cnt ? list[i] : 0ull;
-      }
+        for (int u = 0; u < kListBatch; ++u) {
+          const uint32_t i = base + u * kGathThreads + tid;
+          v[u] = i < cnt ? list[i] : 0ull;
+        }
 #pragma unroll
-      for (int u = 0; u < kListBatch; ++u) {
-        if (base + u * kGathThreads + tid >= cnt) continue;
-        const uint32_t key = uint32_t(v[u] >> 32);
-        const uint32_t n = uint32_t(v[u]);
-        const uint64_t comp = (uint64_t(key - st.lo_key) << 32) | uint32_t(~n);
-        if ((comp >> st.thr_shift) >= thr) {
-          atomicOr(reinterpret_cast<unsigned long long*>(&bm[hh][(int(n) - t0) >> 6]),
-                   1ull << (n & 63u));
-          srow[n] = key2f(key);
+        for (int u = 0; u < kListBatch; ++u) {
+          if (base + u * kGathThreads + tid >= cnt) continue;
+          const uint32_t key = uint32_t(v[u] >> 32);
+          const uint32_t n = uint32_t(v[u]);
+          const uint64_t comp = (uint64_t(key - st.lo_key) << 32) | uint32_t(~n);
+          if ((comp >> st.thr_shift) >= thr) {
+            atomicOr(reinterpret_cast<unsigned long long*>(&bm[hh][(int(n) - t0) >> 6]),
+                     1ull << (n & 63u));
+            srow[n] = key2f(key);
+          }
         }
       }
     }
@@ -131,29 +135,28 @@ __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
       pc.v[hh >> 2] |= int64_t(__popcll(bm[hh][tid])) << (16 * (hh & 3));
     }
   }
-  int64_t utotal;
+  int64_t utotal, unused;
   const int64_t ex = block_excl_scan(__popcll(uw), s_tmp, &utotal);
-  PackedCounts<G> px, ptot;
+  PackedCounts<G> px;
 #pragma unroll
-  for (int j = 0; j < PackedCounts<G>::kWords; ++j)
-    px.v[j] = block_excl_scan(pc.v[j], s_tmp, &ptot.v[j]);
-  // the tile's retrieved positions, ascending, replace its consumed lists
-  if (tid < kWordsPerTile) {
+  for (int j = 0; j < PackedCounts<G>::kWords; ++j) px.v[j] = block_excl_scan(pc.v[j], s_tmp, &unused);
+  // the tile's retrieved positions, ascending, from the tile's offset
+  if (tid < kWordsPerTile && p.k_max > 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      uint32_t rank = uint32_t((px.v[hh >> 2] >> (16 * (hh & 3))) & 0xFFFF);
-      int32_t* dst = reinterpret_cast<int32_t*>(p.cand + (bh0 + hh) * p.n_cap + size_t(t0));
       uint64_t y = bm[hh][tid];
+      if (!y) continue;
+      uint32_t rank = p.usel[(bh0 + hh) * p.n_units + 2 * tile] +
+                      uint32_t((px.v[hh >> 2] >> (16 * (hh & 3))) & 0xFFFF);
+      int32_t* dst = p.out_idx + (bh0 + hh) * p.k_max;
       while (y) {
         const int bit = __ffsll((unsigned long long)y) - 1;
         y &= y - 1ull;
-        dst[rank++] = nw + bit;
+        if (rank < uint32_t(p.k_max)) dst[rank] = nw + bit;
+        ++rank;
       }
     }
   }
-  if (tid < G)
-    p.scnt[(bh0 + tid) * p.n_tiles + tile] =
-        uint32_t((ptot.v[tid >> 2] >> (16 * (tid & 3))) & 0xFFFF);
   const int U = int(utotal);
 
   float acc[G][8];
@@ -269,7 +272,6 @@ __global__ __launch_bounds__(kGathThreads) void gather_kernel(Params p) {
 constexpr int kMergeThreads = 256;
 constexpr int kMergeGroups = kMergeThreads / 32;
 constexpr int kMergeUnroll = 4;
-constexpr int kMergeWin = 2048;  // tiles per out_idx prefix window
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p) {
   const int bh = blockIdx.x;
@@ -284,8 +286,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p) {
 
   __shared__ float s_red[kMergeGroups][kHeadDim + 4];
   __shared__ float s_m[kMergeThreads / 64];
-  __shared__ uint32_t s_pre[kMergeWin];
-  __shared__ int64_t s_tmp[16];
+
 
   // m = max over tiles with a non-empty partial
   float m = -INFINITY;
@@ -336,57 +337,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p) {
     if (tid == 0 && p.lse) p.lse[bh] = zz > 0.0f ? m + logf(zz) : -INFINITY;
   }
   if (p.k_max > 0) {
-    // out_idx: the tiles' retrieved positions in tile order (ascending),
-    // a window of kMergeWin tiles at a time located by a prefix in LDS
     int32_t* dst = p.out_idx + size_t(bh) * p.k_max;
-    const uint32_t* sc = p.scnt + size_t(bh) * p.n_tiles;
-    const int32_t* src = reinterpret_cast<const int32_t*>(p.cand + size_t(bh) * p.n_cap);
-    uint32_t done = 0;
-    for (int w0 = 0; w0 < nt; w0 += kMergeWin) {
-      const int nw = min(kMergeWin, nt - w0);
-      constexpr int per = kMergeWin / kMergeThreads;
-      uint32_t c[per];
-      int64_t sum = 0;
-#pragma unroll
-      for (int u = 0; u < per; ++u) {
-        const int i = tid * per + u;
-        c[u] = i < nw ? sc[w0 + i] : 0u;
-        sum += c[u];
-      }
-      int64_t total;
-      int64_t run = block_excl_scan(sum, s_tmp, &total);
-#pragma unroll
-      for (int u = 0; u < per; ++u) {
-        s_pre[tid * per + u] = uint32_t(run);
-        run += c[u];
-      }
-      __syncthreads();
-      for (uint32_t base = 0; base < uint32_t(total); base += kMergeThreads * kMergeUnroll) {
-        int32_t v[kMergeUnroll];
-#pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
-          const uint32_t i = base + u * kMergeThreads + tid;
-          v[u] = 0;
-          if (i < uint32_t(total)) {
-            int a = 0, e = nw - 1;
-            while (a < e) {
-              const int mid = (a + e + 1) >> 1;
-              if (s_pre[mid] <= i) a = mid; else e = mid - 1;
-            }
-            v[u] = src[size_t(w0 + a) * (2 * kTile) + (i - s_pre[a])];
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
-          const uint32_t i = base + u * kMergeThreads + tid;
-          if (i < uint32_t(total) && done + i < uint32_t(p.k_max)) dst[done + i] = v[u];
-        }
-      }
-      done += uint32_t(total);
-      __syncthreads();
-    }
-    for (int i = int(min(done, uint32_t(p.k_max))) + tid; i < p.k_max; i += kMergeThreads)
-      dst[i] = -1;
+    for (int i = sg.k_eff + tid; i < p.k_max; i += kMergeThreads) dst[i] = -1;
   }
 }
 

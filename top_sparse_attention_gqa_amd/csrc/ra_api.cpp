@@ -24,6 +24,10 @@ bool ws_layout(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seq_len,
   if (heads > 65535) return false;  // grid y limit of the per-head kernels
   L->n_cap = (int64_t(max_seq_len) + kTile - 1) / kTile * kTile;
   L->n_tiles = int32_t(L->n_cap / kTile);
+  L->n_units = int32_t(L->n_cap / kUnit);
+  // sampled_pages(P) is not monotone below 2048 pages (the stride doubles
+  // as P grows) but stays <= 64 there, and is monotone above.
+  L->samp_cap = std::max(64, sampled_pages((max_seq_len + kPage - 1) / kPage)) * kPage;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -31,14 +35,13 @@ bool ws_layout(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seq_len,
     return o;
   };
   L->off_scores = take(size_t(heads) * L->n_cap * sizeof(float));
-  L->off_hist = take(size_t(heads) * kHistStride * sizeof(uint32_t));
+  L->off_samp = take(size_t(heads) * L->samp_cap * sizeof(uint32_t));
   L->off_state = take(size_t(heads) * sizeof(HeadState));
   L->off_gflag = take(size_t(B) * H_kv * sizeof(uint32_t));
   L->off_misc = take(64);
-  L->off_seqoff = take(size_t(B + 1) * sizeof(int64_t));
-  L->off_sampoff = take(size_t(B + 1) * sizeof(int64_t));
-  L->off_tcnt = take(size_t(heads) * L->n_tiles * sizeof(uint32_t));
-  L->off_scnt = take(size_t(heads) * L->n_tiles * sizeof(uint32_t));
+  L->off_unitoff = take(size_t(B + 1) * sizeof(int64_t));
+  L->off_ucnt = take(size_t(heads) * L->n_units * sizeof(uint32_t));
+  L->off_usel = take(size_t(heads) * L->n_units * sizeof(uint32_t));
   L->off_cand = take(size_t(heads) * L->n_cap * sizeof(uint64_t));
   L->off_part_mz = take(size_t(heads) * L->n_tiles * 2 * sizeof(float));
   L->off_part_n = take(size_t(heads) * L->n_tiles * kHeadDim * sizeof(float));
@@ -126,19 +129,20 @@ static Params make_params(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
   p.n_sink = n_sink;
   p.window = window;
   p.scores = reinterpret_cast<float*>(base + L.off_scores);
-  p.hist = reinterpret_cast<uint32_t*>(base + L.off_hist);
+  p.samp = reinterpret_cast<uint32_t*>(base + L.off_samp);
   p.state = reinterpret_cast<HeadState*>(base + L.off_state);
   p.gflag = reinterpret_cast<uint32_t*>(base + L.off_gflag);
   p.any_dense = reinterpret_cast<uint32_t*>(base + L.off_misc);
-  p.seq_off = reinterpret_cast<int64_t*>(base + L.off_seqoff);
-  p.samp_off = reinterpret_cast<int64_t*>(base + L.off_sampoff);
-  p.tcnt = reinterpret_cast<uint32_t*>(base + L.off_tcnt);
-  p.scnt = reinterpret_cast<uint32_t*>(base + L.off_scnt);
+  p.unit_off = reinterpret_cast<int64_t*>(base + L.off_unitoff);
+  p.ucnt = reinterpret_cast<uint32_t*>(base + L.off_ucnt);
+  p.usel = reinterpret_cast<uint32_t*>(base + L.off_usel);
   p.cand = reinterpret_cast<uint64_t*>(base + L.off_cand);
   p.part_mz = reinterpret_cast<float*>(base + L.off_part_mz);
   p.part_n = reinterpret_cast<float*>(base + L.off_part_n);
   p.n_cap = L.n_cap;
   p.n_tiles = L.n_tiles;
+  p.n_units = L.n_units;
+  p.samp_cap = L.samp_cap;
   return p;
 }
 
@@ -209,8 +213,8 @@ ra_status ra_decode_stages(const uint16_t* q, int32_t H_q,
   p.num_cus = cu_count();
   using Launcher = hipError_t (*)(const Params&, hipStream_t);
   static const Launcher stages[RA_STAGE_COUNT] = {
-      launch_prep,   launch_sample, launch_scan,  launch_select,
-      launch_dense,  launch_gather, launch_merge};
+      launch_sample, launch_threshold, launch_scan,  launch_select,
+      launch_dense,  launch_gather,    launch_merge};
   for (int s = first_stage; s <= last_stage; ++s) {
     if (stages[s](p, stream) != hipSuccess) return RA_ERR_HIP;
   }
@@ -225,7 +229,7 @@ ra_status ra_decode_step(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
                          size_t ws_bytes, hipStream_t stream) {
   return ra_decode_stages(q, H_q, kv, seq_lens, B, max_seq_len, k, k_max,
                           n_sink, window, out, out_lse, out_idx, ws, ws_bytes,
-                          RA_STAGE_PREP, RA_STAGE_MERGE, stream);
+                          RA_STAGE_SAMPLE, RA_STAGE_MERGE, stream);
 }
 
 }  // extern "C"

@@ -13,21 +13,37 @@ namespace ra {
 
 constexpr int kHeadDim = 128;
 constexpr int kPage = 64;
-// Positions per filter / gather tile: one tile is one split-K partial.
-constexpr int kTile = 8192;
+// Candidate lists are kept per (query head, unit of 64 pages): the scan
+// block that owns a unit writes its lists and counts without atomics.
+constexpr int kUnitPages = 64;
+constexpr int kUnit = kUnitPages * kPage;  // 4096 positions
+// Positions per gather tile (two units): one tile is one split-K partial.
+constexpr int kTile = 2 * kUnit;
 constexpr int kWordsPerTile = kTile / 64;
-// Global histogram stride per head: 4096 fine bins then 64 coarse bins.
-constexpr int kFineBins = 4096;
-constexpr int kHistStride = kFineBins + 64;
+// Largest number of units of one sequence (RA_MAX_SEQ_LEN / kUnit).
+constexpr int kMaxUnits = RA_MAX_SEQ_LEN / kUnit;
 // Sampling: one page in S is scored before the main scan, S a power of two
 // chosen so that at least kSampleMinPages pages of a (sequence, KV head)
-// are sampled, and S <= 2^kSampleMaxLog2.
+// are sampled, and S <= 2^kSampleMaxLog2. Page j is sampled iff
+// j % S == S / 2.
 constexpr int kSampleMinPages = 32;
 constexpr int kSampleMaxLog2 = 6;
 
+__host__ __device__ inline int sample_log2(int P) {
+  int s = 0;
+  while (s < kSampleMaxLog2 && (P >> (s + 1)) >= kSampleMinPages) ++s;
+  return s;
+}
+
+__host__ __device__ inline int sampled_pages(int P) {
+  const int S = 1 << sample_log2(P);
+  const int half = S >> 1;
+  return P > half ? (P - half + S - 1) / S : 0;
+}
+
 // Candidate entries: key << 32 | position (order-preserving score key).
-// They are kept per (head, tile) in a list of capacity kTile, so a tile's
-// list can hold every position of the tile.
+// The list of (head, unit u) starts at entry u * kUnit of the head's row and
+// has capacity kUnit, so it can hold every position of the unit.
 
 struct HeadState {
   uint32_t lo_key;      // candidates are the members of M with key >= lo_key
@@ -44,8 +60,10 @@ struct HeadState {
 struct WsLayout {
   int64_t n_cap;    // row stride (positions), a multiple of kTile
   int32_t n_tiles;  // n_cap / kTile
-  size_t off_scores, off_hist, off_state, off_gflag, off_misc, off_seqoff,
-      off_sampoff, off_tcnt, off_scnt, off_cand, off_part_mz, off_part_n, total;
+  int32_t n_units;  // n_cap / kUnit
+  int32_t samp_cap; // sampled key slots per head
+  size_t off_scores, off_samp, off_state, off_gflag, off_misc, off_unitoff,
+      off_ucnt, off_usel, off_cand, off_part_mz, off_part_n, total;
 };
 
 // Pure host function; returns false for invalid capacities.
@@ -67,26 +85,27 @@ struct Params {
   // workspace
   float* scores;       // [B*H_q][n_cap]: W scores (scan) and the retrieved
                        // positions' scores of a tile (its gather block)
-  uint32_t* hist;      // [B*H_q][kHistStride] sample histogram
+  uint32_t* samp;      // [B*H_q][samp_cap] keys of the sampled positions
+                       // (0: not a member of M)
   HeadState* state;    // [B*H_q]
   uint32_t* gflag;     // [B*H_kv] 1: some head of the group needs the rescan
   uint32_t* any_dense; // heads flagged for the rescan in this call
-  int64_t* seq_off;    // [B + 1] prefix of H_kv * pages(b)
-  int64_t* samp_off;   // [B + 1] prefix of H_kv * sampled pages(b)
-  uint32_t* tcnt;      // [B*H_q][n_tiles] candidates per (head, tile)
-  uint32_t* scnt;      // [B*H_q][n_tiles] retrieved per (head, tile)
-  uint64_t* cand;      // [B*H_q][n_cap] per-tile candidate lists; after the
-                       // gather, a tile's retrieved positions (int32, sorted)
+  int64_t* unit_off;   // [B + 1] prefix of H_kv * units(b)
+  uint32_t* ucnt;      // [B*H_q][n_units] candidates per (head, unit)
+  uint32_t* usel;      // [B*H_q][n_units] retrieved before the unit (prefix)
+  uint64_t* cand;      // [B*H_q][n_cap] per-unit candidate lists
   float* part_mz;      // [B*H_q][n_tiles][2]  (m, Z)
   float* part_n;       // [B*H_q][n_tiles][128]
   int64_t n_cap;
   int32_t n_tiles;
+  int32_t n_units;
+  int32_t samp_cap;
   int32_t num_cus;
 };
 
 // Launchers (each enqueues its kernels on `s`; they never synchronise).
-hipError_t launch_prep(const Params& p, hipStream_t s);
 hipError_t launch_sample(const Params& p, hipStream_t s);
+hipError_t launch_threshold(const Params& p, hipStream_t s);
 hipError_t launch_scan(const Params& p, hipStream_t s);
 hipError_t launch_select(const Params& p, hipStream_t s);
 hipError_t launch_dense(const Params& p, hipStream_t s);   // rescan + reselect
@@ -148,10 +167,28 @@ __device__ __forceinline__ int page_of(const Params& p, int b, int j) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-// Histogram digit width for a GQA group size: 12 bits (4096 fine bins in 64
-// coarse bins of 64) up to G = 4, 11 bits for G = 8 so the per-block LDS
-// histogram stays at 64 KiB.
-__device__ __forceinline__ int hist_bits(int G) { return G <= 4 ? 12 : 11; }
+// Unit x of the linear unit index over (sequence, KV head, unit), unit
+// fastest: unit_off[b] = sum_{b' < b} H_kv * units(b').
+struct UnitRef {
+  int b, g, u, npages;
+};
+
+__device__ __forceinline__ UnitRef unit_at(const Params& p, int64_t x) {
+  int blo = 0, bhi = p.B - 1;
+  while (blo < bhi) {
+    const int mid = (blo + bhi + 1) >> 1;
+    if (p.unit_off[mid] <= x) blo = mid; else bhi = mid - 1;
+  }
+  UnitRef r;
+  r.b = blo;
+  const int P = (seq_geom(p, blo).N + kPage - 1) / kPage;
+  const int nu = (P + kUnitPages - 1) / kUnitPages;
+  const int64_t rel = x - p.unit_off[blo];
+  r.g = int(rel / nu);
+  r.u = int(rel - int64_t(r.g) * nu);
+  r.npages = min(kUnitPages, P - r.u * kUnitPages);
+  return r;
+}
 
 // Sum over this lane and every higher lane of the wave.
 __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {

@@ -15,11 +15,11 @@
 //
 // HBM writes interleaved with this read stream cost far more than their
 // bytes, so the scan does not store the score rows. A sampling pass first
-// scores one page in S and histograms the sample; from it every head gets a
-// conservative threshold such that, with a wide statistical margin, more
-// than k_eff members of M score at or above it. The scan then keeps only
-// those candidates, staged in LDS and written in bursts (every <= 64 pages)
-// to per-(head, tile) lists, plus the scores of the static set W. The
+// scores one page in S; from the sample every head gets a conservative
+// threshold such that, with a wide statistical margin, at least k_eff
+// members of M score at or above it. The scan then keeps only those
+// candidates, staged in LDS and written in one burst per unit of 64 pages
+// to per-(head, unit) lists, plus the scores of the static set W. The
 // selection checks the margin exactly (it needs at least k_eff candidates);
 // heads that fail it are rescanned with every member of M as a candidate.
 #include "ra_internal.h"
@@ -32,15 +32,12 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kScanThreads = 512;
 constexpr int kScanWaves = kScanThreads / 64;
 constexpr int kStage = 6144;       // LDS candidate staging entries per block
-constexpr int kFlushPages = 64;    // pages between flushes: at most 2 tiles
+constexpr int kSampleWaves = 8;    // sampled pages per sample block (one per wave)
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
 
 template <int G>
 struct ScanCfg {
-  static constexpr int HB = G <= 4 ? 12 : 11;  // histogram digit bits
-  static constexpr int SHIFT = 32 - HB;
-  static constexpr int NC = 1 << (HB - 6);     // coarse bins of 64 fine bins
-  static constexpr int D = 16 / G;             // lanes of a row sharing a head
+  static constexpr int D = 16 / G;  // lanes of a row sharing a head
 };
 
 // Head whose full dot product lane r (0..15 within its row) holds after the
@@ -170,202 +167,40 @@ __device__ __forceinline__ void page_scores(const Params& p, int pg, int g, cons
   }
 }
 
-// A run of pages of one (sequence, KV head) inside a block's range of the
-// linear page index L over (b, g, page), page fastest.
-struct Segment {
-  int b, g, j0, npages;
-  int64_t end;
-};
-
-__device__ __forceinline__ Segment segment_at(const Params& p, int64_t L, int64_t L1) {
-  // the largest b with seq_off[b] <= L (it has at least one page)
-  int blo = 0, bhi = p.B - 1;
-  while (blo < bhi) {
-    const int mid = (blo + bhi + 1) >> 1;
-    if (p.seq_off[mid] <= L) blo = mid; else bhi = mid - 1;
-  }
-  Segment s;
-  s.b = blo;
-  const int P = (seq_geom(p, blo).N + kPage - 1) / kPage;
-  const int64_t rel = L - p.seq_off[blo];
-  s.g = int(rel / P);
-  s.j0 = int(rel - int64_t(s.g) * P);
-  s.end = min(L1, p.seq_off[blo] + int64_t(s.g + 1) * P);
-  s.npages = int(s.end - L);
-  return s;
-}
-
-// Flush an LDS histogram [G][NC][65] into the global per-head histograms of
-// group (b, g), one atomic per non-empty bin, and clear it.
-template <int G>
-__device__ __forceinline__ void flush_hist(uint32_t* lhist, uint32_t* gbase, const Params& p,
-                                           int b, int g) {
-  using C = ScanCfg<G>;
-  const int tid = threadIdx.x;
-  if (tid < G * C::NC) {
-    const int hh = tid / C::NC;
-    const int c = tid - hh * C::NC;
-    uint32_t* rowp = lhist + (hh * C::NC + c) * 65;
-    uint32_t* gh = gbase + (size_t(b) * p.H_q + size_t(g) * G + hh) * kHistStride;
-    uint32_t sum = 0;
-    for (int i = 0; i < 64; ++i) {
-      const uint32_t v = rowp[i];
-      if (v) {
-        atomicAdd(&gh[c * 64 + i], v);
-        sum += v;
-        rowp[i] = 0;
-      }
-    }
-    if (sum) atomicAdd(&gh[kFineBins + c], sum);
-  }
-}
-
-// ---------------------------------------------------------------- sample stride
-// Sample stride S = 2^s: at least kSampleMinPages pages of a (b, g) are
-// scored, at most one in 2^kSampleMaxLog2. Short sequences are scored whole,
-// which makes their threshold exact. Page j is sampled iff j % S == S / 2.
-__device__ __forceinline__ int sample_log2(int P) {
-  int s = 0;
-  while (s < kSampleMaxLog2 && (P >> (s + 1)) >= kSampleMinPages) ++s;
-  return s;
-}
-
-__device__ __forceinline__ int sampled_pages(int P) {
-  const int S = 1 << sample_log2(P);
-  const int half = S >> 1;
-  return P > half ? (P - half + S - 1) / S : 0;
-}
-
-// ---------------------------------------------------------------- prep
-// Clears the sample histograms, per-head state, group flags and candidate
-// counts, and writes the prefixes
-//   seq_off[b]  = sum_{b' < b} H_kv * pages(b')          (scan)
-//   samp_off[b] = sum_{b' < b} H_kv * sampled_pages(b')  (sample)
-// that map a linear page index to (sequence, KV head, page).
-__global__ __launch_bounds__(1024) void prep_kernel(Params p) {
-  const size_t heads = size_t(p.B) * p.H_q;
-  const size_t stride = size_t(gridDim.x) * blockDim.x;
-  const size_t t0 = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const size_t n4 = heads * kHistStride / 4;
-  uint4* h4 = reinterpret_cast<uint4*>(p.hist);
-  for (size_t i = t0; i < n4; i += stride) h4[i] = make_uint4(0, 0, 0, 0);
-  for (size_t i = t0; i < heads * size_t(p.n_tiles); i += stride) p.tcnt[i] = 0;
-  for (size_t i = t0; i < heads; i += stride) {
-    HeadState& st = p.state[i];
-    st.lo_key = 0;
-    st.max_w = 0;
-    st.max_m = 0;
-    st.dense = 0;
-    st.thr_shift = 64;  // nothing passes an unset threshold
-    st.thr_lo = 0xFFFFFFFFu;
-    st.thr_hi = 0xFFFFFFFFu;
-  }
-  for (size_t i = t0; i < size_t(p.B) * p.H_kv; i += stride) p.gflag[i] = 0;
-  if (t0 == 0) *p.any_dense = 0;
-  if (blockIdx.x != 0) return;
-  __shared__ int64_t tmp[16];
-  const int per = (p.B + int(blockDim.x) - 1) / int(blockDim.x);
-  int64_t s = 0, ss = 0;
-  for (int i = 0; i < per; ++i) {
-    const int b = threadIdx.x * per + i;
-    if (b < p.B) {
-      const int P = (seq_geom(p, b).N + kPage - 1) / kPage;
-      s += int64_t(p.H_kv) * P;
-      ss += int64_t(p.H_kv) * sampled_pages(P);
-    }
-  }
-  int64_t total, stotal;
-  int64_t run = block_excl_scan(s, tmp, &total);
-  int64_t srun = block_excl_scan(ss, tmp, &stotal);
-  for (int i = 0; i < per; ++i) {
-    const int b = threadIdx.x * per + i;
-    if (b < p.B) {
-      const int P = (seq_geom(p, b).N + kPage - 1) / kPage;
-      p.seq_off[b] = run;
-      p.samp_off[b] = srun;
-      run += int64_t(p.H_kv) * P;
-      srun += int64_t(p.H_kv) * sampled_pages(P);
-    }
-  }
-  if (threadIdx.x == 0) {
-    p.seq_off[p.B] = total;
-    p.samp_off[p.B] = stotal;
-  }
-}
-
-hipError_t launch_prep(const Params& p, hipStream_t s) {
-  hipLaunchKernelGGL(prep_kernel, dim3(unsigned(2 * (p.num_cus > 0 ? p.num_cus : 256))), dim3(1024),
-                     0, s, p);
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------- sample
-// Persistent over the linear index of sampled pages (same (b, g, page)
-// order as the scan): each block takes one contiguous range, histograms the
-// scores of M per head in LDS and adds them to the global sample histogram
-// at the end of every (b, g) run.
+// Grid (B * H_kv, chunks): block (bg, c) scores the sampled pages
+// c * kSampleWaves .. of group bg, one page per wave, and stores the keys of
+// the sampled positions per head (0 for positions outside M).
 template <int G>
 __global__ __launch_bounds__(kScanThreads) void sample_kernel(Params p) {
-  using C = ScanCfg<G>;
-  __shared__ uint32_t lhist[G * C::NC * 65];
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bg = blockIdx.x;
+  const int b = bg / p.H_kv;
+  const int g = bg - b * p.H_kv;
+  const SeqGeom sg = seq_geom(p, b);
+  const int P = (sg.N + kPage - 1) / kPage;
+  const int ns = sampled_pages(P);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = blockIdx.y * kSampleWaves + wave;
+  if (t >= ns) return;
   const Lane<G> L;
-  for (int i = tid; i < G * C::NC * 65; i += kScanThreads) lhist[i] = 0;
-
-  const int64_t T = p.samp_off[p.B];
-  const int64_t L0 = T * blockIdx.x / gridDim.x;
-  const int64_t L1 = T * (blockIdx.x + 1) / gridDim.x;
-  for (int64_t Lx = L0; Lx < L1;) {
-    // the largest b with samp_off[b] <= Lx (it has at least one sampled page)
-    int blo = 0, bhi = p.B - 1;
-    while (blo < bhi) {
-      const int mid = (blo + bhi + 1) >> 1;
-      if (p.samp_off[mid] <= Lx) blo = mid; else bhi = mid - 1;
-    }
-    const int b = blo;
-    const SeqGeom sg = seq_geom(p, b);
-    const int P = (sg.N + kPage - 1) / kPage;
-    const int S = 1 << sample_log2(P);
-    const int half = S >> 1;
-    const int ns = sampled_pages(P);
-    const int64_t rel = Lx - p.samp_off[b];
-    const int g = int(rel / ns);
-    const int t0 = int(rel - int64_t(g) * ns);
-    const int64_t end = min(L1, p.samp_off[b] + int64_t(g + 1) * ns);
-    const int n = int(end - Lx);
-    uint4 qreg[G];
-    load_q<G>(p, b, g, L, qreg);
-    __syncthreads();
-    uint32_t* lh = lhist + L.F * C::NC * 65;
-    for (int t = t0 + wave; t < t0 + n; t += kScanWaves) {
-      const int j = half + t * S;
-      float z[G];
-      page_scores<G>(p, page_of(p, b, j), g, L, qreg, z);
+  const int S = 1 << sample_log2(P);
+  const int j = (S >> 1) + t * S;
+  uint4 qreg[G];
+  load_q<G>(p, b, g, L, qreg);
+  float z[G];
+  page_scores<G>(p, page_of(p, b, j), g, L, qreg, z);
+  uint32_t* row = p.samp + (size_t(b) * p.H_q + size_t(g) * G + L.F) * p.samp_cap + size_t(t) * kPage;
 #pragma unroll
-      for (int s = 0; s < G; ++s) {
-        const int pos = j * kPage + L.tok(s);
-        if (pos >= sg.lo && pos < sg.hi) {
-          const uint32_t dg = f2key(z[s]) >> C::SHIFT;
-          atomicAdd(&lh[dg + (dg >> 6)], 1u);
-        }
-      }
-    }
-    __syncthreads();
-    flush_hist<G>(lhist, p.hist, p, b, g);
-    __syncthreads();
-    Lx = end;
+  for (int s = 0; s < G; ++s) {
+    const int pos = j * kPage + L.tok(s);
+    row[L.tok(s)] = (pos >= sg.lo && pos < sg.hi) ? f2key(z[s]) : 0u;
   }
 }
 
 hipError_t launch_sample(const Params& p, hipStream_t s) {
-  const int64_t pages_max =
-      int64_t(p.B) * p.H_kv * ((int64_t(p.max_seq_len) + kPage - 1) / kPage);
-  int64_t blocks = (pages_max + 8 * kScanWaves - 1) / (8 * kScanWaves);
-  const int64_t cap = p.num_cus > 0 ? p.num_cus : 256;
-  if (blocks > cap) blocks = cap;
-  if (blocks < 1) blocks = 1;
-  const dim3 grid{unsigned(blocks)}, block{unsigned(kScanThreads)};
+  const int ns_max = p.samp_cap / kPage;
+  const unsigned chunks = unsigned(ns_max > 0 ? (ns_max + kSampleWaves - 1) / kSampleWaves : 1);
+  const dim3 grid{unsigned(p.B * p.H_kv), chunks}, block{unsigned(kScanThreads)};
   switch (p.G) {
     case 1: hipLaunchKernelGGL(sample_kernel<1>, grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL(sample_kernel<2>, grid, block, 0, s, p); break;
@@ -376,172 +211,133 @@ hipError_t launch_sample(const Params& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- threshold
-// Candidate threshold of one head from its sample histogram (run by one
-// wave; returns the same key in every lane). With the sample a fraction
-// 1/r of M, the threshold is placed where the sample count from the top
-// reaches 1.2 k_eff / r + 5 sqrt(k_eff / r) + 8, interpolating linearly
-// inside the fine bucket; the expected population above it is then at least
-// 1.2 k_eff with a margin of five standard deviations of the sample count.
-// A sample that covers all of M gives the exact bucket's lower edge; k_eff
-// = 0 gives a threshold no finite score reaches.
-__device__ uint32_t candidate_threshold(const Params& p, int bh, const SeqGeom& sg) {
-  const int lane = lane_id();
-  if (sg.k_eff == 0) return 0xFFFFFFFFu;
-  const int HB = hist_bits(p.G);
-  const int NC = 1 << (HB - 6);
-  const uint32_t* gh = p.hist + size_t(bh) * kHistStride;
-  const uint32_t c = lane < NC ? gh[kFineBins + lane] : 0u;
-  const uint32_t suf = wave_suffix_sum(c);
-  const uint32_t m_s = __shfl(suf, 0);
-  const uint32_t m_all = uint32_t(sg.hi - sg.lo);
-  if (m_s == 0) return 0u;
-  const bool exact = m_s >= m_all;
-  float target;
-  if (exact) {
-    target = float(sg.k_eff);
-  } else {
-    const float kr = float(sg.k_eff) * float(m_s) / float(m_all);
-    target = 1.2f * kr + 5.0f * sqrtf(kr) + 8.0f;
-  }
-  if (target >= float(m_s)) return 0u;  // keep every member of M
-  const uint64_t mc = __ballot(float(suf) >= target);
-  const int cs = mc ? 63 - __clzll(mc) : 0;
-  const uint32_t above_c = __shfl(suf - c, cs);
-  const uint32_t f = gh[cs * 64 + lane];
-  const uint32_t fsuf = wave_suffix_sum(f) + above_c;
-  const uint64_t mf = __ballot(float(fsuf) >= target);
-  const int fl = mf ? 63 - __clzll(mf) : 0;
-  const uint32_t d = uint32_t(cs * 64 + fl);
-  const uint32_t above = __shfl(fsuf - f, fl);
-  const uint32_t cnt = __shfl(f, fl);
-  const int shift = 32 - HB;
-  const uint32_t lo_edge = d << shift;
-  if (exact || cnt == 0) return lo_edge;
-  // keys of bucket d span [d << shift, (d + 1) << shift)
-  const float frac = fminf(1.0f, (target - float(above)) / float(cnt));
-  const uint32_t width = 1u << shift;
-  const uint32_t back = uint32_t(frac * float(width));
-  const uint64_t top = (uint64_t(d) + 1) << shift;
-  const uint64_t key = top - (back >= width ? width : back);
-  return uint32_t(key > lo_edge ? key : lo_edge);
-}
-
 // ---------------------------------------------------------------- scan
-// Persistent over the linear page index: each block takes one contiguous
-// range and works through it as segments of one (b, g), flushing its LDS
-// candidate staging every kFlushPages pages (such a run spans at most two
-// tiles, so one reservation per (head, tile) suffices).
+// Persistent over the linear unit index (sequence, KV head, unit of 64
+// pages): each block takes a contiguous range of units. Per unit, the
+// candidates (members of M scoring at or above the head's threshold) are
+// staged in LDS and written after the unit to the (head, unit) lists with
+// their counts; the block owns the unit, so no global atomics are needed.
+// W scores go straight to the score rows. Running maxima over W and M per
+// head are folded into the head state whenever the block moves to another
+// (sequence, KV head) and at its end.
 template <int G>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
   __shared__ uint32_t st_key[kStage];
   __shared__ uint32_t st_nh[kStage];  // position | head << 27
   __shared__ uint32_t s_fill;
   __shared__ uint32_t s_lo[G];
+  __shared__ uint32_t s_cnt[G];
   __shared__ uint32_t lmax[G][2];     // max key over W, over M
-  __shared__ uint32_t s_cnt[G][2], s_base[G][2];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Lane<G> L;
   if (tid == 0) s_fill = 0;
+  if (tid < G) s_cnt[tid] = 0;
   if (tid < 2 * G) lmax[tid >> 1][tid & 1] = 0u;
-  __syncthreads();
 
-  const int64_t T = p.seq_off[p.B];
-  const int64_t L0 = T * blockIdx.x / gridDim.x;
-  const int64_t L1 = T * (blockIdx.x + 1) / gridDim.x;
-  for (int64_t Lx = L0; Lx < L1;) {
-    const Segment seg = segment_at(p, Lx, L1);
-    const int b = seg.b, g = seg.g;
+  const int64_t T = p.unit_off[p.B];
+  const int64_t X0 = T * blockIdx.x / gridDim.x;
+  const int64_t X1 = T * (blockIdx.x + 1) / gridDim.x;
+  uint32_t mw = 0u, mm = 0u;  // running max keys of head F over W and M
+  int cur_b = -1, cur_g = -1;
+  uint4 qreg[G];
+  for (int64_t x = X0; x < X1; ++x) {
+    const UnitRef ur = unit_at(p, x);
+    const int b = ur.b, g = ur.g;
     const SeqGeom sg = seq_geom(p, b);
     const size_t bh0 = size_t(b) * p.H_q + size_t(g) * G;
-    if (wave < G) {
-      const uint32_t lo = candidate_threshold(p, int(bh0) + wave, sg);
-      if (L.lane == 0) {
-        s_lo[wave] = lo;
-        if (seg.j0 == 0) p.state[bh0 + wave].lo_key = lo;
+    if (b != cur_b || g != cur_g) {
+      if (cur_b >= 0) {
+        // fold the maxima of the previous group
+        const size_t pbh0 = size_t(cur_b) * p.H_q + size_t(cur_g) * G;
+#pragma unroll
+        for (int m = 1; m < ScanCfg<G>::D; m <<= 1) {
+          mw = max(mw, uint32_t(__shfl_xor(int(mw), m)));
+          mm = max(mm, uint32_t(__shfl_xor(int(mm), m)));
+        }
+        mw = max(mw, uint32_t(__shfl_xor(int(mw), 16)));
+        mm = max(mm, uint32_t(__shfl_xor(int(mm), 16)));
+        mw = max(mw, uint32_t(__shfl_xor(int(mw), 32)));
+        mm = max(mm, uint32_t(__shfl_xor(int(mm), 32)));
+        if (L.row == 0 && L.qsel == 0) {
+          if (mw) atomicMax(&lmax[L.F][0], mw);
+          if (mm) atomicMax(&lmax[L.F][1], mm);
+        }
+        __syncthreads();
+        if (tid < 2 * G) {
+          const int hh = tid >> 1;
+          const uint32_t v = lmax[hh][tid & 1];
+          if (v) atomicMax((tid & 1) ? &p.state[pbh0 + hh].max_m : &p.state[pbh0 + hh].max_w, v);
+          lmax[hh][tid & 1] = 0u;
+        }
+        mw = mm = 0u;
       }
+      cur_b = b;
+      cur_g = g;
+      if (tid < G) s_lo[tid] = p.state[bh0 + tid].lo_key;
+      load_q<G>(p, b, g, L, qreg);
     }
-    uint4 qreg[G];
-    load_q<G>(p, b, g, L, qreg);
     __syncthreads();
     const uint32_t lo_f = s_lo[L.F];
     float* srow = p.scores + (bh0 + L.F) * p.n_cap;
-    uint64_t* crow = p.cand + (bh0 + L.F) * p.n_cap;
-    uint32_t* trow = p.tcnt + (bh0 + L.F) * p.n_tiles;
-    uint32_t mw = 0u, mm = 0u;  // running max keys of head F over W and M
-
-    for (int sub0 = 0; sub0 < seg.npages; sub0 += kFlushPages) {
-      const int subn = min(kFlushPages, seg.npages - sub0);
-      const int tile0 = ((seg.j0 + sub0) * kPage) / kTile;
-      for (int jj = wave; jj < subn; jj += kScanWaves) {
-        const int j = seg.j0 + sub0 + jj;
-        float z[G];
-        page_scores<G>(p, page_of(p, b, j), g, L, qreg, z);
+    const size_t ubase = size_t(ur.u) * kUnit;
+    uint64_t* crow = p.cand + (bh0 + L.F) * p.n_cap + ubase;
+    for (int jj = wave; jj < ur.npages; jj += kScanWaves) {
+      const int j = ur.u * kUnitPages + jj;
+      float z[G];
+      page_scores<G>(p, page_of(p, b, j), g, L, qreg, z);
 #pragma unroll
-        for (int s = 0; s < G; ++s) {
-          const int n = j * kPage + L.tok(s);
-          const uint32_t key = f2key(z[s]);
-          const bool in_m = n >= sg.lo && n < sg.hi;
-          const bool in_w = !in_m && n < sg.N;
-          if (in_w) {
-            srow[n] = z[s];
-            mw = max(mw, key);
-          }
-          if (in_m) mm = max(mm, key);
-          const bool cand = in_m && key >= lo_f;
-          const uint64_t cm = __ballot(cand);
-          if (cm) {
-            const int leader = __ffsll((unsigned long long)cm) - 1;
-            uint32_t base = 0;
-            if (L.lane == leader) base = atomicAdd(&s_fill, uint32_t(__popcll(cm)));
-            base = __shfl(base, leader);
-            if (cand) {
-              const uint32_t idx = base + uint32_t(__popcll(cm & ((1ull << L.lane) - 1ull)));
-              if (idx < uint32_t(kStage)) {
-                st_key[idx] = key;
-                st_nh[idx] = uint32_t(n) | (uint32_t(L.F) << 27);
-              } else {
-                // staging full: append straight to the (head, tile) list
-                const int t = n / kTile;
-                const uint32_t gi = atomicAdd(&trow[t], 1u);
-                crow[size_t(t) * kTile + gi] = (uint64_t(key) << 32) | uint32_t(n);
-              }
+      for (int s = 0; s < G; ++s) {
+        const int n = j * kPage + L.tok(s);
+        const uint32_t key = f2key(z[s]);
+        const bool in_m = n >= sg.lo && n < sg.hi;
+        const bool in_w = !in_m && n < sg.N;
+        if (in_w) {
+          srow[n] = z[s];
+          mw = max(mw, key);
+        }
+        if (in_m) mm = max(mm, key);
+        const bool cand = in_m && key >= lo_f;
+        const uint64_t cm = __ballot(cand);
+        if (cm) {
+          const int leader = __ffsll((unsigned long long)cm) - 1;
+          uint32_t base = 0;
+          if (L.lane == leader) base = atomicAdd(&s_fill, uint32_t(__popcll(cm)));
+          base = __shfl(base, leader);
+          if (cand) {
+            const uint32_t idx = base + uint32_t(__popcll(cm & ((1ull << L.lane) - 1ull)));
+            if (idx < uint32_t(kStage)) {
+              st_key[idx] = key;
+              st_nh[idx] = uint32_t(n) | (uint32_t(L.F) << 27);
+            } else {
+              // staging full: take a slot of the list at once
+              const uint32_t slot = atomicAdd(&s_cnt[L.F], 1u);
+              crow[slot] = (uint64_t(key) << 32) | uint32_t(n);
             }
           }
         }
       }
-      if (tid < 2 * G) s_cnt[tid >> 1][tid & 1] = 0;
-      __syncthreads();
-      // burst the staged candidates into the per-(head, tile) lists
-      const uint32_t nst = min(s_fill, uint32_t(kStage));
-      for (uint32_t i = tid; i < nst; i += kScanThreads) {
-        const uint32_t nh = st_nh[i];
-        const int n = int(nh & ((1u << 27) - 1u));
-        atomicAdd(&s_cnt[nh >> 27][n / kTile - tile0], 1u);
-      }
-      __syncthreads();
-      if (tid < 2 * G) {
-        const int hh = tid >> 1, ts = tid & 1;
-        const uint32_t c = s_cnt[hh][ts];
-        s_base[hh][ts] = c ? atomicAdd(&p.tcnt[(bh0 + hh) * p.n_tiles + tile0 + ts], c) : 0u;
-        s_cnt[hh][ts] = 0;
-      }
-      __syncthreads();
-      for (uint32_t i = tid; i < nst; i += kScanThreads) {
-        const uint32_t nh = st_nh[i];
-        const uint32_t hh = nh >> 27;
-        const int n = int(nh & ((1u << 27) - 1u));
-        const int t = n / kTile;
-        const uint32_t gi = s_base[hh][t - tile0] + atomicAdd(&s_cnt[hh][t - tile0], 1u);
-        p.cand[(bh0 + hh) * p.n_cap + size_t(t) * kTile + gi] = (uint64_t(st_key[i]) << 32) | uint32_t(n);
-      }
-      __syncthreads();
-      if (tid == 0) s_fill = 0;
-      __syncthreads();
     }
-    // maxima: reduce over the lanes that carry the same head, then LDS
+    __syncthreads();
+    // burst the staged candidates into the (head, unit) lists
+    const uint32_t nst = min(s_fill, uint32_t(kStage));
+    for (uint32_t i = tid; i < nst; i += kScanThreads) {
+      const uint32_t nh = st_nh[i];
+      const uint32_t hh = nh >> 27;
+      const uint32_t slot = atomicAdd(&s_cnt[hh], 1u);
+      p.cand[(bh0 + hh) * p.n_cap + ubase + slot] =
+          (uint64_t(st_key[i]) << 32) | (nh & ((1u << 27) - 1u));
+    }
+    __syncthreads();
+    if (tid < G) {
+      p.ucnt[(bh0 + tid) * p.n_units + ur.u] = s_cnt[tid];
+      s_cnt[tid] = 0;
+    }
+    if (tid == 0) s_fill = 0;
+  }
+  if (cur_b >= 0) {
+    const size_t pbh0 = size_t(cur_b) * p.H_q + size_t(cur_g) * G;
 #pragma unroll
     for (int m = 1; m < ScanCfg<G>::D; m <<= 1) {
       mw = max(mw, uint32_t(__shfl_xor(int(mw), m)));
@@ -559,20 +355,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
     if (tid < 2 * G) {
       const int hh = tid >> 1;
       const uint32_t v = lmax[hh][tid & 1];
-      if (v) atomicMax((tid & 1) ? &p.state[bh0 + hh].max_m : &p.state[bh0 + hh].max_w, v);
-      lmax[hh][tid & 1] = 0u;
+      if (v) atomicMax((tid & 1) ? &p.state[pbh0 + hh].max_m : &p.state[pbh0 + hh].max_w, v);
     }
-    __syncthreads();
-    Lx = seg.end;
   }
 }
 
 static unsigned scan_blocks(const Params& p) {
-  const int64_t pages_max =
-      int64_t(p.B) * p.H_kv * ((int64_t(p.max_seq_len) + kPage - 1) / kPage);
-  int64_t blocks = (pages_max + kScanWaves - 1) / kScanWaves;
+  const int64_t units_max = int64_t(p.B) * p.H_kv *
+      ((int64_t(p.max_seq_len) + kUnit - 1) / kUnit);
   const int64_t cap = int64_t(2) * (p.num_cus > 0 ? p.num_cus : 256);
-  if (blocks > cap) blocks = cap;
+  int64_t blocks = units_max < cap ? units_max : cap;
   if (blocks < 1) blocks = 1;
   return unsigned(blocks);
 }
@@ -591,40 +383,38 @@ hipError_t launch_scan(const Params& p, hipStream_t s) {
 
 // ---------------------------------------------------------------- rescan
 // For groups with a head whose candidates fell short: every member of M of
-// those heads becomes a candidate, written at its place in the tile list
-// (the list of tile t holds positions max(t * kTile, lo) .. in order).
-// Blocks skip unflagged segments, so without flags nothing is read.
+// those heads becomes a candidate, written at its place in its unit's list
+// (the list of unit u holds positions max(u * kUnit, lo) .. in order).
+// Blocks skip unflagged groups, so without flags nothing is read.
 template <int G>
 __global__ __launch_bounds__(kScanThreads) void dense_scan_kernel(Params p) {
   if (*p.any_dense == 0u) return;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const Lane<G> L;
-  const int64_t T = p.seq_off[p.B];
-  const int64_t L0 = T * blockIdx.x / gridDim.x;
-  const int64_t L1 = T * (blockIdx.x + 1) / gridDim.x;
-  for (int64_t Lx = L0; Lx < L1;) {
-    const Segment seg = segment_at(p, Lx, L1);
-    Lx = seg.end;
-    const int b = seg.b, g = seg.g;
+  const int64_t T = p.unit_off[p.B];
+  const int64_t X0 = T * blockIdx.x / gridDim.x;
+  const int64_t X1 = T * (blockIdx.x + 1) / gridDim.x;
+  for (int64_t x = X0; x < X1; ++x) {
+    const UnitRef ur = unit_at(p, x);
+    const int b = ur.b, g = ur.g;
     if (!p.gflag[size_t(b) * p.H_kv + g]) continue;
     const SeqGeom sg = seq_geom(p, b);
     const size_t bh = size_t(b) * p.H_q + size_t(g) * G + L.F;
     const bool mine = p.state[bh].dense != 0u;
     uint4 qreg[G];
     load_q<G>(p, b, g, L, qreg);
-    uint64_t* crow = p.cand + bh * p.n_cap;
-    for (int jj = wave; jj < seg.npages; jj += kScanWaves) {
-      const int j = seg.j0 + jj;
+    const int u0 = ur.u * kUnit;
+    uint64_t* crow = p.cand + bh * p.n_cap + size_t(u0);
+    const int first = max(u0, sg.lo);
+    for (int jj = wave; jj < ur.npages; jj += kScanWaves) {
+      const int j = ur.u * kUnitPages + jj;
       float z[G];
       page_scores<G>(p, page_of(p, b, j), g, L, qreg, z);
 #pragma unroll
       for (int s = 0; s < G; ++s) {
         const int n = j * kPage + L.tok(s);
-        if (mine && n >= sg.lo && n < sg.hi) {
-          const int t0 = (n / kTile) * kTile;
-          crow[size_t(t0) + (n - max(t0, sg.lo))] = (uint64_t(f2key(z[s])) << 32) | uint32_t(n);
-        }
+        if (mine && n >= sg.lo && n < sg.hi)
+          crow[n - first] = (uint64_t(f2key(z[s])) << 32) | uint32_t(n);
       }
     }
   }

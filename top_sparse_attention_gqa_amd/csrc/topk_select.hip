@@ -9,21 +9,25 @@
 // score, then a lower position, and all composites are distinct, so "the
 // k_eff largest composites" is the unique tie-broken top-k.
 //
-// select (one block per head): the scan left every member of M scoring at
-// or above the head's sampled threshold in per-tile candidate lists. If they
-// hold at least k_eff entries, the top-k of M is the top-k of the lists; a
-// radix select on the composite finds the exact threshold (the bucket around
-// the k-th entry is finished in LDS) and records it in the head state. The
-// members are taken later, tile by tile, by the gather blocks. A head with
-// too few candidates is flagged; the dense stage rescans its group with
-// every member of M as a candidate and selects again.
+// threshold (one block per head, before the scan): from the keys of the
+// sampled positions, the key of the R-th largest sampled member, with R a
+// conservative stand-in for the rank of the k-th largest member of M in the
+// sample. Members at or above it are the head's candidates.
+//
+// select (one block per head, after the scan): if the per-unit candidate
+// lists hold at least k_eff entries, the top-k of M is the top-k of the
+// lists; a radix select on the composite finds the exact threshold (the
+// bucket around the k-th entry is finished in LDS). The same passes count
+// the retrieved members of every unit, whose prefix tells each gather block
+// where its positions go in out_idx. A head with too few candidates is
+// flagged; the dense stage rescans its group with every member of M as a
+// candidate and selects again.
 #include "ra_internal.h"
 
 namespace ra {
 
 constexpr int kSelThreads = 1024;
-constexpr int kWin = 2048;                 // tiles per LDS prefix window
-constexpr int kSubCap = 4096;              // LDS list for one radix sub-bucket
+constexpr int kSubCap = 2048;              // LDS list for one radix sub-bucket
 
 // ---------------------------------------------------------------- sources
 // Each source enumerates composites of members with (c, n).
@@ -32,88 +36,66 @@ constexpr int kSubCap = 4096;              // LDS list for one radix sub-bucket
 // costs a few memory round trips rather than one per entry.
 constexpr int kBatch = 8;
 
-// A head's per-tile candidate lists (entries key << 32 | n; the list of
-// tile t holds tcnt[t] entries from list + t * kTile), enumerated as
-// composites c = (key - lo) << 32 | ~n. The list lengths of a window of
-// kWin tiles are prefix-summed in LDS; entry i of the window is found by a
-// binary search over that prefix. In dense mode the lengths follow from the
-// geometry: every member of M is in its tile's list.
-struct TileLists {
+// A head's per-unit candidate lists (entries key << 32 | n; the list of
+// unit u holds cnt(u) entries from list + u * kUnit), enumerated as
+// composites c = (key - lo) << 32 | ~n. The list lengths of the units that
+// overlap M are prefix-summed in LDS once; entry i is found by a binary
+// search over that prefix. In dense mode every member of M is in its unit's
+// list, so the lengths follow from the geometry.
+struct UnitLists {
   const uint64_t* list;
-  const uint32_t* tcnt;
-  uint32_t* pre;      // LDS [kWin + 1]
-  int32_t* s_w0;      // LDS: first tile of the window held in pre (-1: none)
-  int64_t* tmp;       // LDS [16]
-  int t_lo, t_hi;     // tiles that overlap M
-  int m_lo, m_hi;     // M
+  const uint32_t* pre;  // LDS [nu + 1]
+  int u_lo, nu;         // units u_lo .. u_lo + nu - 1 overlap M
   uint32_t lo;
-  bool dense;
-
-  __device__ __forceinline__ uint32_t tile_count(int t) const {
-    if (!dense) return tcnt[t];
-    const int a = max(t * kTile, m_lo), e = min((t + 1) * kTile, m_hi);
-    return e > a ? uint32_t(e - a) : 0u;
-  }
-
-  // Prefix of the list lengths of tiles [w0, w0 + nw). Block-wide.
-  __device__ void load(int w0, int nw) const {
-    if (*s_w0 == w0) return;
-    constexpr int per = kWin / kSelThreads;
-    const int tid = threadIdx.x;
-    uint32_t c[per];
-    int64_t sum = 0;
-#pragma unroll
-    for (int u = 0; u < per; ++u) {
-      const int i = tid * per + u;
-      c[u] = i < nw ? tile_count(w0 + i) : 0u;
-      sum += c[u];
-    }
-    int64_t total;
-    int64_t run = block_excl_scan(sum, tmp, &total);
-#pragma unroll
-    for (int u = 0; u < per; ++u) {
-      pre[tid * per + u] = uint32_t(run);
-      run += c[u];
-    }
-    if (tid == 0) {
-      pre[kWin] = uint32_t(total);
-      *s_w0 = w0;
-    }
-    __syncthreads();
-  }
 
   template <typename Fn>
   __device__ __forceinline__ void for_each(Fn&& fn) const {
     const uint32_t l = lo;
-    for (int w0 = t_lo; w0 < t_hi; w0 += kWin) {
-      const int nw = min(kWin, t_hi - w0);
-      load(w0, nw);
-      const uint32_t total = pre[kWin];
-      const uint32_t step = blockDim.x * kBatch;
-      for (uint32_t base = 0; base < total; base += step) {
-        uint64_t v[kBatch];
+    const uint32_t total = pre[nu];
+    const uint32_t step = blockDim.x * kBatch;
+    for (uint32_t base = 0; base < total; base += step) {
+      uint64_t v[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const uint32_t i = base + u * blockDim.x + threadIdx.x;
-          v[u] = 0ull;
-          if (i < total) {
-            int a = 0, e = nw - 1;
-            while (a < e) {
-              const int mid = (a + e + 1) >> 1;
-              if (pre[mid] <= i) a = mid; else e = mid - 1;
-            }
-            v[u] = list[size_t(w0 + a) * kTile + (i - pre[a])];
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t i = base + u * blockDim.x + threadIdx.x;
+        v[u] = 0ull;
+        if (i < total) {
+          int a = 0, e = nu - 1;
+          while (a < e) {
+            const int mid = (a + e + 1) >> 1;
+            if (pre[mid] <= i) a = mid; else e = mid - 1;
           }
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          if (base + u * blockDim.x + threadIdx.x < total) {
-            const uint32_t n = uint32_t(v[u]);
-            fn((uint64_t(uint32_t(v[u] >> 32) - l) << 32) | uint32_t(~n), int(n));
-          }
+          v[u] = list[size_t(u_lo + a) * kUnit + (i - pre[a])];
         }
       }
-      if (t_hi - t_lo > kWin) __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (base + u * blockDim.x + threadIdx.x < total) {
+          const uint32_t n = uint32_t(v[u]);
+          fn((uint64_t(uint32_t(v[u] >> 32) - l) << 32) | uint32_t(~n), int(n));
+        }
+      }
+    }
+  }
+};
+
+// Keys of a head's sampled positions; 0 marks a position outside M.
+struct SampleKeys {
+  const uint32_t* keys;
+  uint32_t count;
+  template <typename Fn>
+  __device__ __forceinline__ void for_each(Fn&& fn) const {
+    const uint32_t step = blockDim.x * kBatch;
+    for (uint32_t base = 0; base < count; base += step) {
+      uint32_t v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t i = base + u * blockDim.x + threadIdx.x;
+        v[u] = i < count ? keys[i] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (v[u] != 0u) fn(uint64_t(v[u]), 0);
     }
   }
 };
@@ -226,35 +208,221 @@ __device__ void find_threshold(const Src& src, const Radix& rx, int TB, uint32_t
   radix_finish(lds, rx, TB, need, prefix, plen);
 }
 
-// ---------------------------------------------------------------- select
+// ---------------------------------------------------------------- threshold
 __device__ __forceinline__ int bit_length(uint32_t x) { return 32 - __clz(x); }
 
-// Exact threshold of head bh over its lists; writes it into the head state.
-__device__ void decide(const Params& p, int bh, const SeqGeom& sg, uint32_t lo, uint32_t max_m,
-                       bool dense) {
+// One block per head. Also resets the per-call state the later stages
+// accumulate into (head state, group flags, the rescan counter) and writes
+// the unit prefix the scan distributes its work by.
+__global__ __launch_bounds__(kSelThreads) void threshold_kernel(Params p) {
+  const int bh = blockIdx.x;
+  const int b = bh / p.H_q;
+  const int hq = bh - b * p.H_q;
+  const int tid = threadIdx.x;
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t s_d, s_above, s_cnt, s_n;
   __shared__ uint64_t sub[kSubCap];
-  __shared__ uint32_t pre[kWin + 1];
-  __shared__ int32_t s_w0;
   __shared__ int64_t tmp[16];
-  if (threadIdx.x == 0) s_w0 = -1;
-  __syncthreads();
+
+  if (bh == 0) {
+    // unit prefix over the batch
+    const int per = (p.B + kSelThreads - 1) / kSelThreads;
+    int64_t sum = 0;
+    for (int i = 0; i < per; ++i) {
+      const int bb = tid * per + i;
+      if (bb < p.B) {
+        const int P = (seq_geom(p, bb).N + kPage - 1) / kPage;
+        sum += int64_t(p.H_kv) * ((P + kUnitPages - 1) / kUnitPages);
+      }
+    }
+    int64_t total;
+    int64_t run = block_excl_scan(sum, tmp, &total);
+    for (int i = 0; i < per; ++i) {
+      const int bb = tid * per + i;
+      if (bb < p.B) {
+        const int P = (seq_geom(p, bb).N + kPage - 1) / kPage;
+        p.unit_off[bb] = run;
+        run += int64_t(p.H_kv) * ((P + kUnitPages - 1) / kUnitPages);
+      }
+    }
+    if (tid == 0) {
+      p.unit_off[p.B] = total;
+      *p.any_dense = 0u;
+    }
+  }
+  if (tid == 0 && hq % p.G == 0) p.gflag[size_t(b) * p.H_kv + hq / p.G] = 0u;
+
+  const SeqGeom sg = seq_geom(p, b);
+  uint32_t lo = 0xFFFFFFFFu;  // k_eff == 0: no candidates
+  if (sg.k_eff > 0) {
+    // sampled members of M: overlap of every sampled page with [lo, hi)
+    const int P = (sg.N + kPage - 1) / kPage;
+    const int ns = sampled_pages(P);
+    const int S = 1 << sample_log2(P);
+    int64_t c = 0;
+    for (int t = tid; t < ns; t += kSelThreads) {
+      const int j = (S >> 1) + t * S;
+      const int a = max(j * kPage, sg.lo), e = min(j * kPage + kPage, sg.hi);
+      c += e > a ? e - a : 0;
+    }
+    int64_t m_s;
+    block_excl_scan(c, tmp, &m_s);
+    const int64_t m_all = sg.hi - sg.lo;
+    uint32_t R;
+    if (m_s >= m_all) {
+      R = uint32_t(sg.k_eff);  // the sample is all of M: exact
+    } else {
+      const float kr = float(sg.k_eff) * float(m_s) / float(m_all);
+      R = uint32_t(ceilf(1.05f * kr + 5.0f * sqrtf(kr) + 8.0f));
+    }
+    if (m_s == 0 || int64_t(R) >= m_s) {
+      lo = 0u;  // keep every member of M
+    } else {
+      const SampleKeys src{p.samp + size_t(bh) * p.samp_cap, uint32_t(ns * kPage)};
+      const Radix rx{hist, &s_d, &s_above, &s_cnt};
+      uint64_t prefix;
+      int plen;
+      find_threshold(src, rx, 32, R, sub, &s_n, prefix, plen);
+      lo = uint32_t(prefix << (32 - plen));
+    }
+  }
+  if (tid == 0) {
+    HeadState st;
+    st.lo_key = lo;
+    st.max_w = 0u;
+    st.max_m = 0u;
+    st.dense = 0u;
+    st.thr_shift = 64u;  // nothing passes until select decides
+    st.thr_lo = 0xFFFFFFFFu;
+    st.thr_hi = 0xFFFFFFFFu;
+    st.pad = 0u;
+    p.state[bh] = st;
+  }
+}
+
+hipError_t launch_threshold(const Params& p, hipStream_t s) {
+  hipLaunchKernelGGL(threshold_kernel, dim3(unsigned(p.B * p.H_q)), dim3(kSelThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- select
+// Exact threshold of head bh over its unit lists; writes it into the head
+// state and, per unit of the sequence, the number of retrieved members
+// before it (usel). `pre` holds the prefix of the list lengths.
+__device__ void decide(const Params& p, int bh, const SeqGeom& sg, uint32_t lo, uint32_t max_m,
+                       const uint32_t* pre, int u_lo, int nu) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t s_d, s_above, s_cnt, s_n;
+  __shared__ uint64_t sub[kSubCap];
+  __shared__ uint32_t s_sel[kMaxUnits];
+  __shared__ int64_t tmp[16];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nu; i += kSelThreads) s_sel[i] = 0u;
   const uint32_t span = max_m > lo ? max_m - lo : 1u;
   const int TB = 32 + bit_length(span);
-  const TileLists src{p.cand + size_t(bh) * p.n_cap, p.tcnt + size_t(bh) * p.n_tiles, pre, &s_w0,
-                      tmp, sg.lo / kTile, (sg.hi - 1) / kTile + 1, sg.lo, sg.hi, lo, dense};
+  const UnitLists src{p.cand + size_t(bh) * p.n_cap, pre, u_lo, nu, lo};
   const Radix rx{hist, &s_d, &s_above, &s_cnt};
-  uint64_t prefix;
-  int plen;
-  find_threshold(src, rx, TB, uint32_t(sg.k_eff), sub, &s_n, prefix, plen);
-  if (threadIdx.x == 0) {
+  uint32_t need = uint32_t(sg.k_eff);
+  uint64_t prefix = 0;
+  int plen = 0;
+  const uint32_t cnt1 = radix_pass(src, rx, TB, need, prefix, plen);
+  if (cnt1 <= uint32_t(kSubCap)) {
+    // one more pass: members above the chosen bucket are retrieved (count
+    // them per unit), members inside it go to LDS
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    const uint64_t pf = prefix;
+    const int pl = plen;
+    src.for_each([&](uint64_t c, int n) {
+      const uint64_t top = c >> (TB - pl);
+      if (top > pf) {
+        atomicAdd(&s_sel[n / kUnit - u_lo], 1u);
+      } else if (top == pf) {
+        sub[atomicAdd(&s_n, 1u)] = c;
+      }
+    });
+    __syncthreads();
+    const LdsSource lds{sub, s_n};
+    if (cnt1 != need) radix_finish(lds, rx, TB, need, prefix, plen);
+    const uint64_t pf2 = prefix;
+    const int pl2 = plen;
+    lds.for_each([&](uint64_t c, int n) {
+      if ((c >> (TB - pl2)) >= pf2) atomicAdd(&s_sel[n / kUnit - u_lo], 1u);
+    });
+  } else {
+    radix_finish(src, rx, TB, need, prefix, plen);
+    const uint64_t pf = prefix;
+    const int pl = plen;
+    src.for_each([&](uint64_t c, int n) {
+      if ((c >> (TB - pl)) >= pf) atomicAdd(&s_sel[n / kUnit - u_lo], 1u);
+    });
+  }
+  __syncthreads();
+  // usel: retrieved members before each unit of the sequence
+  const int units = (sg.N + kUnit - 1) / kUnit;
+  constexpr int per = kMaxUnits / kSelThreads;
+  uint32_t c[per];
+  int64_t sum = 0;
+#pragma unroll
+  for (int u = 0; u < per; ++u) {
+    const int i = tid * per + u;
+    c[u] = i < nu ? s_sel[i] : 0u;
+    sum += c[u];
+  }
+  int64_t total;
+  int64_t run = block_excl_scan(sum, tmp, &total);
+  uint32_t* us = p.usel + size_t(bh) * p.n_units;
+#pragma unroll
+  for (int u = 0; u < per; ++u) {
+    const int i = tid * per + u;
+    if (i < nu) us[u_lo + i] = uint32_t(run);
+    run += c[u];
+  }
+  for (int v = tid; v < u_lo; v += kSelThreads) us[v] = 0u;
+  for (int v = u_lo + nu + tid; v < units; v += kSelThreads) us[v] = uint32_t(total);
+  if (tid == 0) {
     HeadState& w = p.state[bh];
     w.lo_key = lo;
     w.thr_shift = uint32_t(TB - plen);
     w.thr_lo = uint32_t(prefix);
     w.thr_hi = uint32_t(prefix >> 32);
   }
+}
+
+// Prefix of the list lengths of units u_lo .. u_lo + nu - 1 into pre
+// (LDS [kMaxUnits + 1]); returns the total. Block-wide.
+__device__ uint32_t unit_prefix(const Params& p, int bh, const SeqGeom& sg, int u_lo, int nu,
+                                bool dense, uint32_t* pre) {
+  __shared__ int64_t tmp[16];
+  constexpr int per = kMaxUnits / kSelThreads;
+  const int tid = threadIdx.x;
+  const uint32_t* uc = p.ucnt + size_t(bh) * p.n_units;
+  uint32_t c[per];
+  int64_t sum = 0;
+#pragma unroll
+  for (int u = 0; u < per; ++u) {
+    const int i = tid * per + u;
+    c[u] = 0u;
+    if (i < nu) {
+      if (dense) {
+        const int v = u_lo + i;
+        c[u] = uint32_t(min((v + 1) * kUnit, sg.hi) - max(v * kUnit, sg.lo));
+      } else {
+        c[u] = uc[u_lo + i];
+      }
+    }
+    sum += c[u];
+  }
+  int64_t total;
+  int64_t run = block_excl_scan(sum, tmp, &total);
+#pragma unroll
+  for (int u = 0; u < per; ++u) {
+    pre[tid * per + u] = uint32_t(run);
+    run += c[u];
+  }
+  if (tid == 0) pre[kMaxUnits] = uint32_t(total);
+  __syncthreads();
+  return uint32_t(total);
 }
 
 // One block per head: count the candidates; decide the threshold, or flag
@@ -265,15 +433,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
   const int g = (bh - b * p.H_q) / p.G;
   const SeqGeom sg = seq_geom(p, b);
   if (sg.k_eff == 0) return;  // the unset threshold takes nothing
-  __shared__ int64_t tmp[16];
-  const int t_lo = sg.lo / kTile, t_hi = (sg.hi - 1) / kTile + 1;
-  const uint32_t* tc = p.tcnt + size_t(bh) * p.n_tiles;
-  int64_t c = 0;
-  for (int t = t_lo + int(threadIdx.x); t < t_hi; t += kSelThreads) c += tc[t];
-  int64_t m;
-  block_excl_scan(c, tmp, &m);
+  __shared__ uint32_t pre[kMaxUnits + 1];
+  const int u_lo = sg.lo / kUnit, nu = (sg.hi - 1) / kUnit + 1 - u_lo;
+  const uint32_t m = unit_prefix(p, bh, sg, u_lo, nu, false, pre);
   const HeadState st = p.state[bh];
-  if (m < sg.k_eff) {
+  if (m < uint32_t(sg.k_eff)) {
     if (threadIdx.x == 0) {
       p.state[bh].dense = 1u;
       atomicOr(&p.gflag[size_t(b) * p.H_kv + g], 1u);
@@ -281,7 +445,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     }
     return;
   }
-  decide(p, bh, sg, st.lo_key, st.max_m, false);
+  decide(p, bh, sg, st.lo_key, st.max_m, pre, u_lo, nu);
 }
 
 hipError_t launch_select(const Params& p, hipStream_t s) {
@@ -291,20 +455,20 @@ hipError_t launch_select(const Params& p, hipStream_t s) {
 
 // ---------------------------------------------------------------- dense
 // After the rescan: the flagged heads select over every member of M (their
-// lists now hold all of it, so the candidate counts are the tile sizes).
+// lists now hold all of it, so the list lengths are the units' overlaps).
 __global__ __launch_bounds__(kSelThreads) void reselect_kernel(Params p) {
   if (*p.any_dense == 0u) return;
   const int bh = blockIdx.x;
   const HeadState st = p.state[bh];
   if (!st.dense) return;
   const SeqGeom sg = seq_geom(p, bh / p.H_q);
-  const int t_lo = sg.lo / kTile, t_hi = (sg.hi - 1) / kTile + 1;
-  uint32_t* tc = p.tcnt + size_t(bh) * p.n_tiles;
-  for (int t = t_lo + int(threadIdx.x); t < t_hi; t += kSelThreads) {
-    const int a = max(t * kTile, sg.lo), e = min((t + 1) * kTile, sg.hi);
-    tc[t] = uint32_t(e - a);
-  }
-  decide(p, bh, sg, 0u, st.max_m, true);
+  __shared__ uint32_t pre[kMaxUnits + 1];
+  const int u_lo = sg.lo / kUnit, nu = (sg.hi - 1) / kUnit + 1 - u_lo;
+  const uint32_t m = unit_prefix(p, bh, sg, u_lo, nu, true, pre);
+  uint32_t* uc = p.ucnt + size_t(bh) * p.n_units;
+  for (int i = threadIdx.x; i < nu; i += kSelThreads) uc[u_lo + i] = pre[i + 1] - pre[i];
+  (void)m;
+  decide(p, bh, sg, 0u, st.max_m, pre, u_lo, nu);
 }
 
 hipError_t launch_dense_scan(const Params& p, hipStream_t s);  // score_scan.hip
