@@ -41,7 +41,7 @@ bool ws_layout(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seq_len,
   L->off_misc = take(64);
   L->off_unitoff = take(size_t(B + 1) * sizeof(int64_t));
   L->off_ucnt = take(size_t(heads) * L->n_units * sizeof(uint32_t));
-  L->off_usel = take(size_t(heads) * L->n_units * sizeof(uint32_t));
+  L->off_scnt = take(size_t(heads) * L->n_tiles * sizeof(uint32_t));
   L->off_cand = take(size_t(heads) * L->n_cap * sizeof(uint64_t));
   L->off_part_mz = take(size_t(heads) * L->n_tiles * 2 * sizeof(float));
   L->off_part_n = take(size_t(heads) * L->n_tiles * kHeadDim * sizeof(float));
@@ -135,7 +135,7 @@ static Params make_params(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
   p.any_dense = reinterpret_cast<uint32_t*>(base + L.off_misc);
   p.unit_off = reinterpret_cast<int64_t*>(base + L.off_unitoff);
   p.ucnt = reinterpret_cast<uint32_t*>(base + L.off_ucnt);
-  p.usel = reinterpret_cast<uint32_t*>(base + L.off_usel);
+  p.scnt = reinterpret_cast<uint32_t*>(base + L.off_scnt);
   p.cand = reinterpret_cast<uint64_t*>(base + L.off_cand);
   p.part_mz = reinterpret_cast<float*>(base + L.off_part_mz);
   p.part_n = reinterpret_cast<float*>(base + L.off_part_n);

@@ -63,7 +63,7 @@ struct WsLayout {
   int32_t n_units;  // n_cap / kUnit
   int32_t samp_cap; // sampled key slots per head
   size_t off_scores, off_samp, off_state, off_gflag, off_misc, off_unitoff,
-      off_ucnt, off_usel, off_cand, off_part_mz, off_part_n, total;
+      off_ucnt, off_scnt, off_cand, off_part_mz, off_part_n, total;
 };
 
 // Pure host function; returns false for invalid capacities.
@@ -92,8 +92,10 @@ struct Params {
   uint32_t* any_dense; // heads flagged for the rescan in this call
   int64_t* unit_off;   // [B + 1] prefix of H_kv * units(b)
   uint32_t* ucnt;      // [B*H_q][n_units] candidates per (head, unit)
-  uint32_t* usel;      // [B*H_q][n_units] retrieved before the unit (prefix)
-  uint64_t* cand;      // [B*H_q][n_cap] per-unit candidate lists
+  uint32_t* scnt;      // [B*H_q][n_tiles] retrieved per (head, tile)
+  uint64_t* cand;      // [B*H_q][n_cap] per-unit candidate lists; after the
+                       // gather, tile t's region holds its retrieved
+                       // positions (int32, ascending)
   float* part_mz;      // [B*H_q][n_tiles][2]  (m, Z)
   float* part_n;       // [B*H_q][n_tiles][128]
   int64_t n_cap;

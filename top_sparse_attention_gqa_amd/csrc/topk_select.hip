@@ -17,76 +17,143 @@
 // select (one block per head, after the scan): if the per-unit candidate
 // lists hold at least k_eff entries, the top-k of M is the top-k of the
 // lists; a radix select on the composite finds the exact threshold (the
-// bucket around the k-th entry is finished in LDS). The same passes count
-// the retrieved members of every unit, whose prefix tells each gather block
-// where its positions go in out_idx. A head with too few candidates is
-// flagged; the dense stage rescans its group with every member of M as a
-// candidate and selects again.
+// bucket around the k-th entry is finished in LDS). The lists are read once
+// into registers when they fit. A head with too few candidates is flagged;
+// the dense stage rescans its group with every member of M as a candidate
+// and selects again.
 #include "ra_internal.h"
 
 namespace ra {
 
-constexpr int kSelThreads = 1024;
-constexpr int kSubCap = 2048;              // LDS list for one radix sub-bucket
+constexpr int kSelThreads = 512;
+constexpr int kSubCap = 2048;     // LDS list for one radix sub-bucket
+constexpr int kBatch = 8;         // global entries per lane in flight per pass
+constexpr int kRegEntries = 64;   // candidate entries per lane kept in registers
+constexpr int kRegKeys = 32;      // sampled keys per lane kept in registers
+
+// ---------------------------------------------------------------- wave helpers
+// Every lane of the wave must call these.
+
+// Append v to an LDS list (capacity cap) for every lane with `flag`: one
+// atomic per wave.
+__device__ __forceinline__ void wave_append(uint64_t* list, uint32_t* n, uint32_t cap, uint64_t v,
+                                            bool flag) {
+  const uint64_t m = __ballot(flag);
+  if (!m) return;
+  const int lane = lane_id();
+  const int leader = __ffsll((unsigned long long)m) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(n, uint32_t(__popcll(m)));
+  base = __shfl(base, leader);
+  if (flag) {
+    const uint32_t i = base + uint32_t(__popcll(m & ((1ull << lane) - 1ull)));
+    if (i < cap) list[i] = v;
+  }
+}
 
 // ---------------------------------------------------------------- sources
-// Each source enumerates composites of members with (c, n).
+// A source enumerates composites: for_each(fn) calls fn(c, n, valid) in
+// lockstep over the wave (valid is false for padding slots).
 
-// Entries loaded per thread before any is used, so that a pass over a list
-// costs a few memory round trips rather than one per entry.
-constexpr int kBatch = 8;
-
-// A head's per-unit candidate lists (entries key << 32 | n; the list of
-// unit u holds cnt(u) entries from list + u * kUnit), enumerated as
-// composites c = (key - lo) << 32 | ~n. The list lengths of the units that
-// overlap M are prefix-summed in LDS once; entry i is found by a binary
-// search over that prefix. In dense mode every member of M is in its unit's
-// list, so the lengths follow from the geometry.
+// A head's per-unit candidate lists in global memory (entries key << 32 | n;
+// the list of unit u holds cnt(u) entries from list + u * kUnit), enumerated
+// as composites c = (key - lo) << 32 | ~n. The list lengths of the units that
+// overlap M are prefix-summed in LDS; entry i is found by a branch-free
+// binary search over that prefix whose kBatch lookups proceed in lockstep.
 struct UnitLists {
   const uint64_t* list;
   const uint32_t* pre;  // LDS [nu + 1]
   int u_lo, nu;         // units u_lo .. u_lo + nu - 1 overlap M
   uint32_t lo;
 
+  __device__ __forceinline__ void locate(const uint32_t (&idx)[kBatch], int (&a)[kBatch]) const {
+    const int top = nu > 1 ? 1 << (31 - __clz(nu - 1)) : 0;  // largest power of two < nu
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) a[u] = 0;
+    for (int step = top; step > 0; step >>= 1) {
+      uint32_t pv[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) pv[u] = pre[min(a[u] + step, nu - 1)];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) a[u] += (a[u] + step < nu && pv[u] <= idx[u]) ? step : 0;
+    }
+  }
+
   template <typename Fn>
   __device__ __forceinline__ void for_each(Fn&& fn) const {
     const uint32_t l = lo;
     const uint32_t total = pre[nu];
-    const uint32_t step = blockDim.x * kBatch;
-    for (uint32_t base = 0; base < total; base += step) {
+    for (uint32_t base = 0; base < total; base += blockDim.x * kBatch) {
+      uint32_t idx[kBatch];
+      int a[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) idx[u] = base + u * blockDim.x + threadIdx.x;
+      locate(idx, a);
       uint64_t v[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const uint32_t i = base + u * blockDim.x + threadIdx.x;
-        v[u] = 0ull;
-        if (i < total) {
-          int a = 0, e = nu - 1;
-          while (a < e) {
-            const int mid = (a + e + 1) >> 1;
-            if (pre[mid] <= i) a = mid; else e = mid - 1;
-          }
-          v[u] = list[size_t(u_lo + a) * kUnit + (i - pre[a])];
-        }
-      }
+      for (int u = 0; u < kBatch; ++u)
+        v[u] = idx[u] < total ? list[size_t(u_lo + a[u]) * kUnit + (idx[u] - pre[a[u]])] : 0ull;
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        if (base + u * blockDim.x + threadIdx.x < total) {
-          const uint32_t n = uint32_t(v[u]);
-          fn((uint64_t(uint32_t(v[u] >> 32) - l) << 32) | uint32_t(~n), int(n));
-        }
+        const uint32_t n = uint32_t(v[u]);
+        fn((uint64_t(uint32_t(v[u] >> 32) - l) << 32) | uint32_t(~n), int(n), idx[u] < total);
       }
     }
   }
 };
 
-// Keys of a head's sampled positions; 0 marks a position outside M.
+// The same lists read once into registers (entry r * blockDim + t in slot r
+// of thread t), for heads with at most kRegEntries * blockDim candidates.
+template <int NR>
+struct RegLists {
+  uint64_t c[NR];
+  uint32_t total;
+
+  __device__ __forceinline__ void load(const UnitLists& src) {
+    total = src.pre[src.nu];
+    const uint32_t l = src.lo;
+#pragma unroll
+    for (int r0 = 0; r0 < NR; r0 += kBatch) {
+      if (uint32_t(r0) * blockDim.x >= total) break;  // uniform
+      uint32_t idx[kBatch];
+      int a[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) idx[u] = (r0 + u) * blockDim.x + threadIdx.x;
+      src.locate(idx, a);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        uint64_t v = 0ull;
+        if (idx[u] < total)
+          v = src.list[size_t(src.u_lo + a[u]) * kUnit + (idx[u] - src.pre[a[u]])];
+        c[r0 + u] = v;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint32_t n = uint32_t(c[r]);
+      c[r] = (uint64_t(uint32_t(c[r] >> 32) - l) << 32) | uint32_t(~n);
+    }
+  }
+
+  template <typename Fn>
+  __device__ __forceinline__ void for_each(Fn&& fn) const {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      if (uint32_t(r) * blockDim.x >= total) break;  // uniform
+      const uint32_t i = r * blockDim.x + threadIdx.x;
+      fn(c[r], int(~uint32_t(c[r])), i < total);
+    }
+  }
+};
+
+// Keys of a head's sampled positions in global memory; 0 marks a position
+// outside M (and is skipped).
 struct SampleKeys {
   const uint32_t* keys;
   uint32_t count;
   template <typename Fn>
   __device__ __forceinline__ void for_each(Fn&& fn) const {
-    const uint32_t step = blockDim.x * kBatch;
-    for (uint32_t base = 0; base < count; base += step) {
+    for (uint32_t base = 0; base < count; base += blockDim.x * kBatch) {
       uint32_t v[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
@@ -94,8 +161,30 @@ struct SampleKeys {
         v[u] = i < count ? keys[i] : 0u;
       }
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (v[u] != 0u) fn(uint64_t(v[u]), 0);
+      for (int u = 0; u < kBatch; ++u) fn(uint64_t(v[u]), 0, v[u] != 0u);
+    }
+  }
+};
+
+// The same keys read once into registers.
+template <int NR>
+struct RegKeys {
+  uint32_t k[NR];
+  uint32_t count;
+  __device__ __forceinline__ void load(const uint32_t* keys, uint32_t n) {
+    count = n;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint32_t i = r * blockDim.x + threadIdx.x;
+      k[r] = i < count ? keys[i] : 0u;
+    }
+  }
+  template <typename Fn>
+  __device__ __forceinline__ void for_each(Fn&& fn) const {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      if (uint32_t(r) * blockDim.x >= count) break;  // uniform
+      fn(uint64_t(k[r]), 0, k[r] != 0u);
     }
   }
 };
@@ -106,9 +195,10 @@ struct LdsSource {
   uint32_t count;
   template <typename Fn>
   __device__ __forceinline__ void for_each(Fn&& fn) const {
-    for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) {
-      const uint64_t v = c[i];
-      fn(v, int(~uint32_t(v)));
+    for (uint32_t base = 0; base < count; base += blockDim.x) {
+      const uint32_t i = base + threadIdx.x;
+      const uint64_t v = i < count ? c[i] : 0ull;
+      fn(v, int(~uint32_t(v)), i < count);
     }
   }
 };
@@ -125,7 +215,7 @@ struct Radix {
 // the top reaches need. Updates need/prefix/plen; returns the chosen digit's
 // population (all block threads get the same values).
 template <typename Src>
-__device__ uint32_t radix_pass(const Src& src, const Radix& rx, int TB, uint32_t& need,
+__device__ __forceinline__ uint32_t radix_pass(const Src& src, const Radix& rx, int TB, uint32_t& need,
                                uint64_t& prefix, int& plen) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -137,28 +227,28 @@ __device__ uint32_t radix_pass(const Src& src, const Radix& rx, int TB, uint32_t
   const int pl = plen;
   const uint64_t pf = prefix;
   const uint32_t dmask = (1u << w) - 1u;
-  src.for_each([&](uint64_t c, int) {
-    if (pl == 0 || (c >> (TB - pl)) == pf) atomicAdd(&rx.hist[uint32_t(c >> shift) & dmask], 1u);
+  src.for_each([&](uint64_t c, int, bool valid) {
+    if (valid && (pl == 0 || (c >> (TB - pl)) == pf))
+      atomicAdd(&rx.hist[uint32_t(c >> shift) & dmask], 1u);
   });
   __syncthreads();
   if (wave == 0) {
+    // lane l sums bins 32 l .. 32 l + 31; the lane where the count from the
+    // top reaches need owns the digit, found among its 32 bins in parallel
     uint32_t s = 0;
     for (int i = 0; i < 32; ++i) s += rx.hist[lane * 32 + i];
     const uint32_t suf = wave_suffix_sum(s);
     const uint64_t m = __ballot(suf >= need);
     const int L = m ? 63 - __clzll(m) : 0;
-    if (lane == L) {
-      uint32_t acc = suf - s;
-      for (int i = 31; i >= 0; --i) {
-        const uint32_t v = rx.hist[lane * 32 + i];
-        if (acc + v >= need || i == 0) {
-          *rx.s_d = uint32_t(lane * 32 + i);
-          *rx.s_above = acc;
-          *rx.s_cnt = v;
-          break;
-        }
-        acc += v;
-      }
+    const uint32_t above_l = __shfl(suf - s, L);
+    const uint32_t v = lane < 32 ? rx.hist[L * 32 + lane] : 0u;
+    const uint32_t fsuf = wave_suffix_sum(v) + above_l;
+    const uint64_t mf = __ballot(lane < 32 && fsuf >= need);
+    const int F = mf ? 63 - __clzll(mf) : 0;
+    if (lane == F) {
+      *rx.s_d = uint32_t(L * 32 + F);
+      *rx.s_above = fsuf - v;
+      *rx.s_cnt = v;
     }
   }
   __syncthreads();
@@ -173,7 +263,7 @@ __device__ uint32_t radix_pass(const Src& src, const Radix& rx, int TB, uint32_t
 // Passes until the chosen digit's whole population is needed (or every bit
 // is fixed, where the population is one).
 template <typename Src>
-__device__ void radix_finish(const Src& src, const Radix& rx, int TB, uint32_t& need,
+__device__ __forceinline__ void radix_finish(const Src& src, const Radix& rx, int TB, uint32_t& need,
                              uint64_t& prefix, int& plen) {
   while (plen < TB) {
     if (radix_pass(src, rx, TB, need, prefix, plen) == need) break;
@@ -184,9 +274,9 @@ __device__ void radix_finish(const Src& src, const Radix& rx, int TB, uint32_t& 
 // source: one pass over it; if that does not settle it and the chosen
 // sub-bucket fits LDS, the sub-bucket is copied there and finished in LDS.
 // Members whose top plen bits are >= the returned prefix are exactly the
-// need largest.
+// need largest (all of them when every bit is fixed and values tie).
 template <typename Src>
-__device__ void find_threshold(const Src& src, const Radix& rx, int TB, uint32_t need,
+__device__ __forceinline__ void find_threshold(const Src& src, const Radix& rx, int TB, uint32_t need,
                                uint64_t* sub, uint32_t* s_n, uint64_t& prefix, int& plen) {
   prefix = 0;
   plen = 0;
@@ -200,8 +290,8 @@ __device__ void find_threshold(const Src& src, const Radix& rx, int TB, uint32_t
   __syncthreads();
   const uint64_t pf = prefix;
   const int pl = plen;
-  src.for_each([&](uint64_t c, int) {
-    if ((c >> (TB - pl)) == pf) sub[atomicAdd(s_n, 1u)] = c;
+  src.for_each([&](uint64_t c, int, bool valid) {
+    wave_append(sub, s_n, kSubCap, c, valid && (c >> (TB - pl)) == pf);
   });
   __syncthreads();
   const LdsSource lds{sub, *s_n};
@@ -255,10 +345,15 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(Params p) {
   const SeqGeom sg = seq_geom(p, b);
   uint32_t lo = 0xFFFFFFFFu;  // k_eff == 0: no candidates
   if (sg.k_eff > 0) {
-    // sampled members of M: overlap of every sampled page with [lo, hi)
     const int P = (sg.N + kPage - 1) / kPage;
     const int ns = sampled_pages(P);
     const int S = 1 << sample_log2(P);
+    const uint32_t* keys = p.samp + size_t(bh) * p.samp_cap;
+    const uint32_t count = uint32_t(ns * kPage);
+    RegKeys<kRegKeys> rk;
+    const bool in_regs = count <= uint32_t(kRegKeys * kSelThreads);
+    if (in_regs) rk.load(keys, count);  // in flight while the count below runs
+    // sampled members of M: overlap of every sampled page with [lo, hi)
     int64_t c = 0;
     for (int t = tid; t < ns; t += kSelThreads) {
       const int j = (S >> 1) + t * S;
@@ -278,11 +373,14 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(Params p) {
     if (m_s == 0 || int64_t(R) >= m_s) {
       lo = 0u;  // keep every member of M
     } else {
-      const SampleKeys src{p.samp + size_t(bh) * p.samp_cap, uint32_t(ns * kPage)};
       const Radix rx{hist, &s_d, &s_above, &s_cnt};
       uint64_t prefix;
       int plen;
-      find_threshold(src, rx, 32, R, sub, &s_n, prefix, plen);
+      if (in_regs) {
+        find_threshold(rk, rx, 32, R, sub, &s_n, prefix, plen);
+      } else {
+        find_threshold(SampleKeys{keys, count}, rx, 32, R, sub, &s_n, prefix, plen);
+      }
       lo = uint32_t(prefix << (32 - plen));
     }
   }
@@ -306,94 +404,18 @@ hipError_t launch_threshold(const Params& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- select
-// Exact threshold of head bh over its unit lists; writes it into the head
-// state and, per unit of the sequence, the number of retrieved members
-// before it (usel). `pre` holds the prefix of the list lengths.
-__device__ void decide(const Params& p, int bh, const SeqGeom& sg, uint32_t lo, uint32_t max_m,
-                       const uint32_t* pre, int u_lo, int nu) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t s_d, s_above, s_cnt, s_n;
-  __shared__ uint64_t sub[kSubCap];
-  __shared__ uint32_t s_sel[kMaxUnits];
-  __shared__ int64_t tmp[16];
-  const int tid = threadIdx.x;
-  for (int i = tid; i < nu; i += kSelThreads) s_sel[i] = 0u;
-  const uint32_t span = max_m > lo ? max_m - lo : 1u;
-  const int TB = 32 + bit_length(span);
-  const UnitLists src{p.cand + size_t(bh) * p.n_cap, pre, u_lo, nu, lo};
-  const Radix rx{hist, &s_d, &s_above, &s_cnt};
-  uint32_t need = uint32_t(sg.k_eff);
-  uint64_t prefix = 0;
-  int plen = 0;
-  const uint32_t cnt1 = radix_pass(src, rx, TB, need, prefix, plen);
-  if (cnt1 <= uint32_t(kSubCap)) {
-    // one more pass: members above the chosen bucket are retrieved (count
-    // them per unit), members inside it go to LDS
-    if (tid == 0) s_n = 0;
-    __syncthreads();
-    const uint64_t pf = prefix;
-    const int pl = plen;
-    src.for_each([&](uint64_t c, int n) {
-      const uint64_t top = c >> (TB - pl);
-      if (top > pf) {
-        atomicAdd(&s_sel[n / kUnit - u_lo], 1u);
-      } else if (top == pf) {
-        sub[atomicAdd(&s_n, 1u)] = c;
-      }
-    });
-    __syncthreads();
-    const LdsSource lds{sub, s_n};
-    if (cnt1 != need) radix_finish(lds, rx, TB, need, prefix, plen);
-    const uint64_t pf2 = prefix;
-    const int pl2 = plen;
-    lds.for_each([&](uint64_t c, int n) {
-      if ((c >> (TB - pl2)) >= pf2) atomicAdd(&s_sel[n / kUnit - u_lo], 1u);
-    });
-  } else {
-    radix_finish(src, rx, TB, need, prefix, plen);
-    const uint64_t pf = prefix;
-    const int pl = plen;
-    src.for_each([&](uint64_t c, int n) {
-      if ((c >> (TB - pl)) >= pf) atomicAdd(&s_sel[n / kUnit - u_lo], 1u);
-    });
-  }
-  __syncthreads();
-  // usel: retrieved members before each unit of the sequence
-  const int units = (sg.N + kUnit - 1) / kUnit;
-  constexpr int per = kMaxUnits / kSelThreads;
-  uint32_t c[per];
-  int64_t sum = 0;
-#pragma unroll
-  for (int u = 0; u < per; ++u) {
-    const int i = tid * per + u;
-    c[u] = i < nu ? s_sel[i] : 0u;
-    sum += c[u];
-  }
-  int64_t total;
-  int64_t run = block_excl_scan(sum, tmp, &total);
-  uint32_t* us = p.usel + size_t(bh) * p.n_units;
-#pragma unroll
-  for (int u = 0; u < per; ++u) {
-    const int i = tid * per + u;
-    if (i < nu) us[u_lo + i] = uint32_t(run);
-    run += c[u];
-  }
-  for (int v = tid; v < u_lo; v += kSelThreads) us[v] = 0u;
-  for (int v = u_lo + nu + tid; v < units; v += kSelThreads) us[v] = uint32_t(total);
-  if (tid == 0) {
-    HeadState& w = p.state[bh];
-    w.lo_key = lo;
-    w.thr_shift = uint32_t(TB - plen);
-    w.thr_lo = uint32_t(prefix);
-    w.thr_hi = uint32_t(prefix >> 32);
-  }
-}
+struct SelLds {
+  uint32_t pre[kMaxUnits + 1];  // prefix of the list lengths
+  uint32_t hist[2048];
+  uint64_t sub[kSubCap];
+  uint32_t s_d, s_above, s_cnt, s_n;
+  int64_t tmp[16];
+};
 
-// Prefix of the list lengths of units u_lo .. u_lo + nu - 1 into pre
-// (LDS [kMaxUnits + 1]); returns the total. Block-wide.
+// Prefix of the list lengths of units u_lo .. u_lo + nu - 1 into L.pre;
+// returns the total. Block-wide.
 __device__ uint32_t unit_prefix(const Params& p, int bh, const SeqGeom& sg, int u_lo, int nu,
-                                bool dense, uint32_t* pre) {
-  __shared__ int64_t tmp[16];
+                                bool dense, SelLds& L) {
   constexpr int per = kMaxUnits / kSelThreads;
   const int tid = threadIdx.x;
   const uint32_t* uc = p.ucnt + size_t(bh) * p.n_units;
@@ -414,15 +436,49 @@ __device__ uint32_t unit_prefix(const Params& p, int bh, const SeqGeom& sg, int 
     sum += c[u];
   }
   int64_t total;
-  int64_t run = block_excl_scan(sum, tmp, &total);
+  int64_t run = block_excl_scan(sum, L.tmp, &total);
 #pragma unroll
   for (int u = 0; u < per; ++u) {
-    pre[tid * per + u] = uint32_t(run);
+    L.pre[tid * per + u] = uint32_t(run);
     run += c[u];
   }
-  if (tid == 0) pre[kMaxUnits] = uint32_t(total);
+  if (tid == 0) L.pre[kMaxUnits] = uint32_t(total);
   __syncthreads();
   return uint32_t(total);
+}
+
+// Exact threshold of head bh over its candidates (source src), written
+// into the head state.
+template <typename Src>
+__device__ __forceinline__ void decide(const Params& p, int bh, const SeqGeom& sg, const Src& src,
+                                       int TB, uint32_t lo, SelLds& L) {
+  const Radix rx{L.hist, &L.s_d, &L.s_above, &L.s_cnt};
+  uint64_t prefix;
+  int plen;
+  find_threshold(src, rx, TB, uint32_t(sg.k_eff), L.sub, &L.s_n, prefix, plen);
+  if (threadIdx.x == 0) {
+    HeadState& w = p.state[bh];
+    w.lo_key = lo;
+    w.thr_shift = uint32_t(TB - plen);
+    w.thr_lo = uint32_t(prefix);
+    w.thr_hi = uint32_t(prefix >> 32);
+  }
+}
+
+// Select over the lists of head bh (whose prefix is in L.pre), from
+// registers when they fit.
+__device__ __forceinline__ void select_head(const Params& p, int bh, const SeqGeom& sg, int u_lo, int nu,
+                            uint32_t lo, uint32_t max_m, SelLds& L) {
+  const uint32_t span = max_m > lo ? max_m - lo : 1u;
+  const int TB = 32 + bit_length(span);
+  const UnitLists gl{p.cand + size_t(bh) * p.n_cap, L.pre, u_lo, nu, lo};
+  if (L.pre[kMaxUnits] <= uint32_t(kRegEntries * kSelThreads)) {
+    RegLists<kRegEntries> rl;
+    rl.load(gl);
+    decide(p, bh, sg, rl, TB, lo, L);
+  } else {
+    decide(p, bh, sg, gl, TB, lo, L);
+  }
 }
 
 // One block per head: count the candidates; decide the threshold, or flag
@@ -433,9 +489,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
   const int g = (bh - b * p.H_q) / p.G;
   const SeqGeom sg = seq_geom(p, b);
   if (sg.k_eff == 0) return;  // the unset threshold takes nothing
-  __shared__ uint32_t pre[kMaxUnits + 1];
+  __shared__ SelLds L;
   const int u_lo = sg.lo / kUnit, nu = (sg.hi - 1) / kUnit + 1 - u_lo;
-  const uint32_t m = unit_prefix(p, bh, sg, u_lo, nu, false, pre);
+  const uint32_t m = unit_prefix(p, bh, sg, u_lo, nu, false, L);
   const HeadState st = p.state[bh];
   if (m < uint32_t(sg.k_eff)) {
     if (threadIdx.x == 0) {
@@ -445,7 +501,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     }
     return;
   }
-  decide(p, bh, sg, st.lo_key, st.max_m, pre, u_lo, nu);
+  select_head(p, bh, sg, u_lo, nu, st.lo_key, st.max_m, L);
 }
 
 hipError_t launch_select(const Params& p, hipStream_t s) {
@@ -462,13 +518,12 @@ __global__ __launch_bounds__(kSelThreads) void reselect_kernel(Params p) {
   const HeadState st = p.state[bh];
   if (!st.dense) return;
   const SeqGeom sg = seq_geom(p, bh / p.H_q);
-  __shared__ uint32_t pre[kMaxUnits + 1];
+  __shared__ SelLds L;
   const int u_lo = sg.lo / kUnit, nu = (sg.hi - 1) / kUnit + 1 - u_lo;
-  const uint32_t m = unit_prefix(p, bh, sg, u_lo, nu, true, pre);
+  unit_prefix(p, bh, sg, u_lo, nu, true, L);
   uint32_t* uc = p.ucnt + size_t(bh) * p.n_units;
-  for (int i = threadIdx.x; i < nu; i += kSelThreads) uc[u_lo + i] = pre[i + 1] - pre[i];
-  (void)m;
-  decide(p, bh, sg, 0u, st.max_m, pre, u_lo, nu);
+  for (int i = threadIdx.x; i < nu; i += kSelThreads) uc[u_lo + i] = L.pre[i + 1] - L.pre[i];
+  select_head(p, bh, sg, u_lo, nu, 0u, st.max_m, L);
 }
 
 hipError_t launch_dense_scan(const Params& p, hipStream_t s);  // score_scan.hip
