@@ -17,7 +17,7 @@ Source pages (cited by title and slide/equation, never by line):
     disjoint partials gives the exact softmax on their union.
   - frame "The bottleneck is both storage and KV access": Table 1, KV capacity.
 
-Readings of points the pages leave open (listed in the design notes too):
+Readings of points the pages leave open:
 
 * d in 1/sqrt(d) is the head dimension (128).
 * The retrieved set is searched over M = [0, N) minus W, so it never holds a
