@@ -40,14 +40,17 @@ WORKLOAD_TEXT = {
     "C3_2": "Llama-3-8B layer: H_q=32, H_kv=8, d=128, N=1048576, k=2% (20971), n_sink=128, window=512",
     "C3_3": "Llama-3-8B layer: H_q=32, H_kv=8, d=128, N=1048576, k=3% (31457), n_sink=128, window=512",
     "C4": "16 ragged sequences (N uniform in [32768, 131072]) of a Llama-3-8B layer, 64-token pages in shuffled order, k=2% of each length",
+    "C5": "32 Llama-3-8B layers (H_q=32, H_kv=8, d=128) at N=1048576, k=1% of the current length, KV of every layer resident in HBM; each token step appends one K/V row per layer and runs the decode step of all 32 layers",
 }
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 200; 1000 token steps for C5)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps (default 20; 2 token steps for C5)")
     ap.add_argument("--workload", default="C3_1", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
@@ -161,13 +164,27 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    model = args.workload == "C5"
+    if args.steps is None:
+        args.steps = 1000 if model else 200
+    if args.warmup is None:
+        args.warmup = 2 if model else 20
 
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    if model:
+        run_model(args)
+    else:
+        run_layer(args)
+
+
+def run_layer(args):
     import numpy as np
     import torch
 
     import top_sparse_attention_gqa_amd as ra
 
-    assert torch.cuda.is_available(), "bench.py needs the GPU"
     dev = "cuda"
     c, lens, ks, layers = make_inputs(args.workload, dev)
     B, H_q, H_kv = len(lens), c.H_q, c.H_kv
@@ -283,6 +300,124 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else int(round(traffic)),
+                     "algorithmic_bytes_per_launch": scan_bytes,
+                     "avg_launch_us": round(scan_s * 1e6, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_model(args):
+    """C5: every token step appends one K/V row to each of the 32 layers and
+    runs each layer's decode step; value = ms per token step."""
+    import numpy as np
+    import torch
+
+    import synth
+    import top_sparse_attention_gqa_amd as ra
+
+    dev = "cuda"
+    c = synth.config("C5")
+    n_layers, H_q, H_kv = c.n_layers, c.H_q, c.H_kv
+    N0 = c.seq_lens[0]
+    total = args.warmup + args.steps
+    layers = [synth.make_layer(H_q, H_kv, [N0], [c.k_for(N0)], c.n_sink, c.window,
+                               c.needles_per_head, c.seed + l, dev, reserve_tokens=total)
+              for l in range(n_layers)]
+    streams = [synth.make_decode_stream(1, H_q, H_kv, L.u, total, 10_000 + l, dev)
+               for l, L in enumerate(layers)]
+    lens = [N0 + s + 1 for s in range(total)]          # length after the append
+    ks = [c.k_for(n) for n in lens]
+    seq_all = torch.tensor(lens, dtype=torch.int32, device=dev).view(total, 1)
+    pos_all = (seq_all - 1).contiguous()
+    k_all = torch.tensor(ks, dtype=torch.int32, device=dev).view(total, 1)
+    max_seq_len = N0 + total
+    k_max = max(ks)
+    ws = ra.alloc_workspace(1, H_q, H_kv, max_seq_len, k_max, device=dev)
+    outs = [torch.empty(1, H_q, 128, device=dev) for _ in layers]
+    lses = [torch.empty(1, H_q, device=dev) for _ in layers]
+    idxs = [torch.empty(1, H_q, k_max, dtype=torch.int32, device=dev) for _ in layers]
+    kvs = [ra.KVLayer(L.k_pool, L.v_pool, L.block_table) for L in layers]
+    n_stage = ra._lib.STAGE_COUNT
+    S = ra.STAGE_SCAN
+
+    def token_step(s, ev=None):
+        for l in range(n_layers):
+            q, kn, vn = streams[l][0][s], streams[l][1][s], streams[l][2][s]
+            ra.kv_append(kvs[l], kn, vn, pos_all[s])
+            a = (q, kvs[l], seq_all[s], max_seq_len, k_all[s], k_max, c.n_sink, c.window,
+                 outs[l], lses[l], idxs[l], ws)
+            if ev is None:
+                ra.decode_step(*a)
+            else:
+                ra.decode_stages(*a, 0, S - 1)
+                ev[2 * l].record()
+                ra.decode_stages(*a, S, S)
+                ev[2 * l + 1].record()
+                ra.decode_stages(*a, S + 1, n_stage - 1)
+
+    for s in range(args.warmup):
+        token_step(s)
+    torch.cuda.synchronize()
+    every = max(1, args.steps // 100)                  # scan events on every 10th step
+    ev = {s: [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_layers)]
+          for s in range(0, args.steps, every)}
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        token_step(args.warmup + i, ev.get(i))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    scan_ms = np.array([e[2 * l].elapsed_time(e[2 * l + 1]) for e in ev.values()
+                        for l in range(n_layers)])
+
+    # algorithmic bytes of the last token step, from each layer's retrieved sets
+    n_last = lens[-1]
+    kb = vb = small = 0
+    for l in range(n_layers):
+        a, b_, sm = algorithmic_bytes(c, [n_last], [ks[-1]], idxs[l].cpu().numpy(), c.n_sink,
+                                      c.window)
+        kb, vb, small = kb + a, vb + b_, small + sm + 2 * H_kv * 256 * 2
+    step_bytes = kb + vb + small
+    n_mean = N0 + args.warmup + (args.steps + 1) / 2.0
+    scan_bytes = int(n_mean * H_kv * 256 + H_q * 256)
+    scan_s = float(scan_ms.mean()) * 1e-3
+    achieved = scan_bytes / scan_s / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        one = cpu_baseline(c, layers[0], [N0], [c.k_for(N0)])
+        one["value"] = round(one["value"] * n_layers, 3)
+        one["sample"] += f"; times {n_layers} layers for one token step"
+        cpu = one
+
+    line = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: OOD q vs K, 64 planted needles per query head, x4 sink keys)",
+        "config": {"workload": f"C5: {WORKLOAD_TEXT['C5']}", "n_layers": n_layers,
+                   "B": 1, "H_q": H_q, "H_kv": H_kv, "head_dim": 128,
+                   "seq_len": [N0 + args.warmup + 1, lens[-1]], "k": [ks[args.warmup], ks[-1]],
+                   "n_sink": c.n_sink, "window": c.window, "accumulate": "fp32",
+                   "kv_bytes_resident": int(sum(L.k_pool.numel() * 4 for L in layers))},
+        "kv_tokens_per_s": round(n_layers * n_mean / (ms_per_step * 1e-3), 1),
+        "step_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes": {"K": kb, "V": vb, "q_out_idx_append": small, "step": step_bytes},
+        "roofline": {"kernel": "scan_kernel (score scan + candidate staging)",
+                     "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None,
                      "algorithmic_bytes_per_launch": scan_bytes,
                      "avg_launch_us": round(scan_s * 1e6, 2)},
         "cpu_baseline": cpu,

@@ -62,11 +62,13 @@ typedef enum ra_status {
 
 /*
  * One layer's paged KV cache.
- *  k_pool, v_pool: device bf16 [num_pages][H_kv][64][128]; the 64 x 128 block
- *                  of one (page, KV head) is contiguous (16 KiB).
+ *  k_pool, v_pool: device bf16 [num_pages][H_kv][64][128], 16-byte aligned;
+ *                  the 64 x 128 block of one (page, KV head) is contiguous
+ *                  (16 KiB).
  *  block_table:    device int32 [B][max_pages]; entry [b][j] is the physical
  *                  page holding positions 64 j .. 64 j + 63 of sequence b.
- * Page allocation is the caller's job.
+ * Page allocation is the caller's job. Misaligned pointers are rejected with
+ * RA_ERR_INVALID_ARGUMENT (int32 and fp32 arrays need 4-byte alignment).
  */
 typedef struct ra_kv_layer {
   uint16_t* k_pool;
@@ -98,7 +100,7 @@ size_t ra_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv,
  * and v_new[b][g] to slot pos[b] % 64 of page block_table[b][pos[b] / 64].
  * This is the "decode one new token at a time" step of the slides' setting
  * frame ("One question: how can decoding read less KV?").
- *  k_new, v_new: device bf16 [B][H_kv][128].
+ *  k_new, v_new: device bf16 [B][H_kv][128], 16-byte aligned.
  *  pos:          device int32 [B], the new token's position (its sequence's
  *                length before the append). Positions outside
  *                [0, 64 * max_pages) are skipped.
@@ -109,7 +111,8 @@ ra_status ra_kv_append(const ra_kv_layer* kv, const uint16_t* k_new,
 
 /*
  * One decode step (see the top of this file for what it computes).
- *  q:           device bf16 [B][H_q][128], the new token's queries.
+ *  q:           device bf16 [B][H_q][128], the new token's queries,
+ *               16-byte aligned.
  *  seq_lens:    device int32 [B], lengths N_b after the append, so the recent
  *               window includes the new token.
  *  max_seq_len: host capacity >= every N_b; sizes the grids and workspace.

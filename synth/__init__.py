@@ -14,6 +14,7 @@ from .gen import (  # noqa: F401
     bf16_bits,
     depage,
     draw_lengths,
+    make_decode_stream,
     make_layer,
     make_new_tokens,
 )

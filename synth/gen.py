@@ -183,6 +183,20 @@ def make_new_tokens(B: int, H_kv: int, u: torch.Tensor, seed: int, device):
     return k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
+def make_decode_stream(B: int, H_q: int, H_kv: int, u: torch.Tensor, steps: int, seed: int,
+                       device):
+    """Inputs of `steps` consecutive decode steps of one layer, drawn like the
+    layer's own: per step a query (N(0,1) - 0.5 u, bf16 [B][H_q][128]) and
+    one new K row (N(0,1) + 0.5 u) and V row (N(0,1)) per (sequence, KV head).
+    Returns (q [steps][B][H_q][128], k_new, v_new [steps][B][H_kv][128])."""
+    g = torch.Generator(device=torch.device(device)).manual_seed(seed)
+    u = u.to(device)
+    q = torch.randn(steps, B, H_q, HEAD_DIM, generator=g, device=device) - 0.5 * u
+    k = torch.randn(steps, B, H_kv, HEAD_DIM, generator=g, device=device) + 0.5 * u
+    v = torch.randn(steps, B, H_kv, HEAD_DIM, generator=g, device=device)
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Raw bf16 bit patterns of a tensor, as a host uint16 array."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

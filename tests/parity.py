@@ -72,11 +72,12 @@ def gpu_decode(L: synth.LayerInputs, max_seq_len: int | None = None, k_max: int 
                sc.cpu().numpy() if sc is not None else None)
 
 
-def host_seq(L: synth.LayerInputs, b: int):
-    """q bits [H_q][128], K and V bits [N][H_kv][128] of sequence b."""
+def host_seq(L: synth.LayerInputs, b: int, kv_heads=None):
+    """q bits [H_q][128], K and V bits [N][H_kv][128] of sequence b (only the
+    KV heads listed in kv_heads, if given)."""
     n = L.seq_lens[b]
-    return (synth.bf16_bits(L.q[b]), synth.depage(L.k_pool, L.block_table, b, n),
-            synth.depage(L.v_pool, L.block_table, b, n))
+    return (synth.bf16_bits(L.q[b]), synth.depage(L.k_pool, L.block_table, b, n, heads=kv_heads),
+            synth.depage(L.v_pool, L.block_table, b, n, heads=kv_heads))
 
 
 def score_bound(q_bits, K_bits) -> np.ndarray:
@@ -140,17 +141,17 @@ def check_out(o_gpu, o_ref, what="out") -> None:
 def compare_sequence(L: synth.LayerInputs, run: Run, b: int, heads=None, ks=None,
                      n_sink=None, window=None, check_score_rows=True) -> dict:
     """Oracle for sequence b and full comparison. Returns stats."""
-    q, K, V = host_seq(L, b)
     k = (L.ks if ks is None else ks)[b]
     n_sink = L.n_sink if n_sink is None else n_sink
     window = L.window if window is None else window
     if heads is not None:
-        q = q[heads]
         G = L.H_q // L.H_kv
         grp = sorted({h // G for h in heads})
         assert len(grp) == 1, "sampled heads must share one KV head"
-        K, V = K[:, grp[0]:grp[0] + 1], V[:, grp[0]:grp[0] + 1]
+        q, K, V = host_seq(L, b, kv_heads=grp)
+        q = q[heads]
     else:
+        q, K, V = host_seq(L, b)
         heads = list(range(L.H_q))
     res = oracle.decode(q, K, V, k=k, n_sink=n_sink, window=window)
     bound = score_bound(q, K)

@@ -95,6 +95,9 @@ def _decode(kv=None, **kw):
     (dict(n_sink=-1), ra.RA_ERR_INVALID_ARGUMENT),
     (dict(window=-5), ra.RA_ERR_INVALID_ARGUMENT),
     (dict(ws=FAKE + 16), ra.RA_ERR_INVALID_ARGUMENT),
+    (dict(q=FAKE + 8), ra.RA_ERR_INVALID_ARGUMENT),        # q rows are read 16 B at a time
+    (dict(seq_lens=FAKE + 2), ra.RA_ERR_INVALID_ARGUMENT),
+    (dict(out_idx=FAKE + 1), ra.RA_ERR_INVALID_ARGUMENT),
     (dict(ws_bytes=1024), ra.RA_ERR_WORKSPACE),
     (dict(H_q=16), ra.RA_ERR_UNSUPPORTED),   # G = 16
 ])
@@ -110,6 +113,8 @@ def test_decode_validation_of_the_kv_descriptor():
     assert _decode(kv=_kv(k_pool=None)) == ra.RA_ERR_INVALID_ARGUMENT
     assert _decode(kv=_kv(block_table=None)) == ra.RA_ERR_INVALID_ARGUMENT
     assert _decode(kv=_kv(num_pages=0)) == ra.RA_ERR_INVALID_ARGUMENT
+    assert _decode(kv=_kv(k_pool=FAKE + 4)) == ra.RA_ERR_INVALID_ARGUMENT
+    assert _decode(kv=_kv(block_table=FAKE + 2)) == ra.RA_ERR_INVALID_ARGUMENT
     assert _decode(kv=_kv(H_kv=3)) == ra.RA_ERR_INVALID_ARGUMENT  # 4 % 3
     assert _lib.raw.ra_decode_step(FAKE, 4, None, FAKE, 1, 640, FAKE, 8, 4, 8, FAKE, None,
                                    FAKE, FAKE, 1 << 40, None) == ra.RA_ERR_INVALID_ARGUMENT
@@ -135,6 +140,7 @@ def test_kv_append_validation():
     assert f(ctypes.byref(kv), None, FAKE, FAKE, 1, None) == ra.RA_ERR_INVALID_ARGUMENT
     assert f(ctypes.byref(kv), FAKE, FAKE, None, 1, None) == ra.RA_ERR_INVALID_ARGUMENT
     assert f(ctypes.byref(kv), FAKE, FAKE, FAKE, 0, None) == ra.RA_ERR_INVALID_ARGUMENT
+    assert f(ctypes.byref(kv), FAKE + 8, FAKE, FAKE, 1, None) == ra.RA_ERR_INVALID_ARGUMENT
     bad = _kv(head_dim=256)
     assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, 1, None) == ra.RA_ERR_UNSUPPORTED
 

@@ -1,0 +1,97 @@
+"""Parity at the workloads' full sizes, in the launch configuration that
+bench.py times.
+
+* One Llama-3-8B layer (H_q=32, H_kv=8) at N = 1,048,576 with k = 1, 2 and
+  3 % of N: the whole step runs on the GPU; the oracle checks the first and
+  the last KV group (8 of the 32 query heads) element by element, and every
+  planted needle of every head must be retrieved.
+* The 32-layer workload: layers 0, 15 and 31 (seeds 0, 15, 31) run the same
+  1002 append + decode token steps as the benchmark (2 warm-up steps, then
+  1000), with the same capacity; the oracle checks two KV groups of each of
+  them after the first, a middle and the last step.
+
+Oracle time is about a second per KV group at N = 1M, so the groups are
+sampled; layers are independent, so the sampled layers see exactly what
+they see in the 32-layer run.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import top_sparse_attention_gqa_amd as ra
+from tests.parity import Run, compare_sequence, gpu_decode, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+SAMPLED_GROUPS = ([0, 1, 2, 3], [28, 29, 30, 31])
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+
+
+@pytest.mark.parametrize("name", ["C3_1", "C3_2", "C3_3"])
+def test_one_layer_at_a_million_tokens(name):
+    c = synth.config(name)
+    n = c.seq_lens[0]
+    say(f"case {name}: H_q=32 H_kv=8 N={n} k={c.k_for(n)} (groups 0 and 7 checked)")
+    L = synth.make_layer(c.H_q, c.H_kv, [n], [c.k_for(n)], c.n_sink, c.window,
+                         c.needles_per_head, c.seed, DEV)
+    run = gpu_decode(L, with_scores=True)
+    for heads in SAMPLED_GROUPS:
+        st = compare_sequence(L, run, 0, heads=heads)
+        say(f"  heads {heads[0]}..{heads[-1]}: band differences {st['band_diffs']}")
+    missed = [(pos, h) for pos, h in L.needles[0] if pos not in run.idx[0, h]]
+    assert not missed, f"{len(missed)} needles not retrieved, e.g. {missed[:4]}"
+
+
+def test_32_layer_workload_sampled_layers_over_1000_steps():
+    c = synth.config("C5")
+    N0 = c.seq_lens[0]
+    warmup, steps = 2, c.extra["steps"]
+    total = warmup + steps
+    checks = {0, warmup + steps // 2, total - 1}
+    sampled = (0, 15, 31)
+    say(f"case C5: layers {sampled} of 32, N0={N0}, {total} append+decode steps, "
+        f"checks after steps {sorted(checks)}")
+    H_q, H_kv = c.H_q, c.H_kv
+    layers = {l: synth.make_layer(H_q, H_kv, [N0], [c.k_for(N0)], c.n_sink, c.window,
+                                  c.needles_per_head, c.seed + l, DEV, reserve_tokens=total)
+              for l in sampled}
+    streams = {l: synth.make_decode_stream(1, H_q, H_kv, layers[l].u, total, 10_000 + l, DEV)
+               for l in sampled}
+    lens = [N0 + s + 1 for s in range(total)]
+    ks = [c.k_for(n) for n in lens]
+    seq_all = torch.tensor(lens, dtype=torch.int32, device=DEV).view(total, 1)
+    pos_all = (seq_all - 1).contiguous()
+    k_all = torch.tensor(ks, dtype=torch.int32, device=DEV).view(total, 1)
+    max_seq_len = N0 + total
+    k_max = max(ks)
+    ws = ra.alloc_workspace(1, H_q, H_kv, max_seq_len, k_max, device=DEV)
+    out = torch.empty(1, H_q, 128, device=DEV)
+    lse = torch.empty(1, H_q, device=DEV)
+    idx = torch.empty(1, H_q, k_max, dtype=torch.int32, device=DEV)
+    kvs = {l: ra.KVLayer(layers[l].k_pool, layers[l].v_pool, layers[l].block_table)
+           for l in sampled}
+    for s in range(total):
+        for l in sampled:
+            q, kn, vn = streams[l][0][s], streams[l][1][s], streams[l][2][s]
+            ra.kv_append(kvs[l], kn, vn, pos_all[s])
+            ra.decode_step(q, kvs[l], seq_all[s], max_seq_len, k_all[s], k_max, c.n_sink,
+                           c.window, out, lse, idx, ws)
+            if s in checks:
+                torch.cuda.synchronize()
+                run = Run(out.cpu().numpy().astype(np.float64),
+                          lse.cpu().numpy().astype(np.float64),
+                          idx.cpu().numpy())
+                view = dataclasses.replace(layers[l], q=q, seq_lens=[lens[s]], ks=[ks[s]])
+                for heads in SAMPLED_GROUPS:
+                    st = compare_sequence(view, run, 0, heads=heads, check_score_rows=False)
+                    say(f"  step {s} layer {l} heads {heads[0]}..{heads[-1]}: "
+                        f"band differences {st['band_diffs']}")

@@ -94,7 +94,7 @@ def workspace_scores_offset(B, H_q, H_kv, max_seq_len, k_max):
     return int(off), int(stride.value)
 
 
-def _ptr(t, dtype, name, nullable=False):
+def _ptr(t, dtype, name, nullable=False, align=4):
     if t is None:
         if nullable:
             return None
@@ -107,8 +107,8 @@ def _ptr(t, dtype, name, nullable=False):
         raise ValueError(f"{name} must be contiguous")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor")
-    if t.data_ptr() % 16:
-        raise ValueError(f"{name} must be 16-byte aligned")
+    if t.data_ptr() % align:
+        raise ValueError(f"{name} must be {align}-byte aligned")
     return t.data_ptr()
 
 
@@ -134,7 +134,7 @@ class KVLayer:
             raise ValueError("block_table must be [B][max_pages]")
         self.k_pool, self.v_pool, self.block_table = k_pool, v_pool, block_table
         self.struct = KVLayerStruct(
-            _ptr(k_pool, torch.bfloat16, "k_pool"), _ptr(v_pool, torch.bfloat16, "v_pool"),
+            _ptr(k_pool, torch.bfloat16, "k_pool", align=16), _ptr(v_pool, torch.bfloat16, "v_pool", align=16),
             _ptr(block_table, torch.int32, "block_table"), k_pool.shape[0],
             block_table.shape[1], k_pool.shape[1], HEAD_DIM, PAGE_SIZE)
 
@@ -154,8 +154,8 @@ def kv_append(kv: KVLayer, k_new, v_new, pos, stream=None) -> None:
     """ra_kv_append: write one token's K/V rows ([B][H_kv][128] bf16) at
     positions pos ([B] int32)."""
     B = pos.shape[0]
-    st = _lib.ra_kv_append(ctypes.byref(kv.struct), _ptr(k_new, torch.bfloat16, "k_new"),
-                           _ptr(v_new, torch.bfloat16, "v_new"), _ptr(pos, torch.int32, "pos"),
+    st = _lib.ra_kv_append(ctypes.byref(kv.struct), _ptr(k_new, torch.bfloat16, "k_new", align=16),
+                           _ptr(v_new, torch.bfloat16, "v_new", align=16), _ptr(pos, torch.int32, "pos"),
                            B, _stream(stream))
     if st != RA_OK:
         raise RAError(st, "ra_kv_append")
@@ -167,12 +167,12 @@ def decode_stages(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, windo
     """ra_decode_stages (ra_decode_step when first..last covers every stage)."""
     B, H_q = q.shape[0], q.shape[1]
     st = _lib.ra_decode_stages(
-        _ptr(q, torch.bfloat16, "q"), H_q, ctypes.byref(kv.struct),
+        _ptr(q, torch.bfloat16, "q", align=16), H_q, ctypes.byref(kv.struct),
         _ptr(seq_lens, torch.int32, "seq_lens"), B, max_seq_len, _ptr(k, torch.int32, "k"),
         k_max, n_sink, window, _ptr(out, torch.float32, "out"),
         _ptr(out_lse, torch.float32, "out_lse", nullable=True),
         _ptr(out_idx, torch.int32, "out_idx", nullable=(k_max == 0)),
-        _ptr(ws, torch.uint8, "ws"), ws.numel() if not isinstance(ws, int) else 0,
+        _ptr(ws, torch.uint8, "ws", align=256), ws.numel() if not isinstance(ws, int) else 0,
         first, last, _stream(stream))
     if st != RA_OK:
         raise RAError(st, "ra_decode_stages")
@@ -183,12 +183,12 @@ def decode_step(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, window,
     """ra_decode_step: one exact top-k sparse GQA decode step."""
     B, H_q = q.shape[0], q.shape[1]
     st = _lib.ra_decode_step(
-        _ptr(q, torch.bfloat16, "q"), H_q, ctypes.byref(kv.struct),
+        _ptr(q, torch.bfloat16, "q", align=16), H_q, ctypes.byref(kv.struct),
         _ptr(seq_lens, torch.int32, "seq_lens"), B, max_seq_len, _ptr(k, torch.int32, "k"),
         k_max, n_sink, window, _ptr(out, torch.float32, "out"),
         _ptr(out_lse, torch.float32, "out_lse", nullable=True),
         _ptr(out_idx, torch.int32, "out_idx", nullable=(k_max == 0)),
-        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream))
+        _ptr(ws, torch.uint8, "ws", align=256), ws.numel(), _stream(stream))
     if st != RA_OK:
         raise RAError(st, "ra_decode_step")
 

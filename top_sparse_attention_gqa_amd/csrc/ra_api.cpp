@@ -67,8 +67,17 @@ static int cu_count() {
   return cache[dev];
 }
 
+// Vector loads need 16-byte aligned rows; scalar arrays need their element
+// alignment.
+static bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
 static ra_status check_kv(const ra_kv_layer* kv) {
   if (!kv || !kv->k_pool || !kv->v_pool || !kv->block_table)
+    return RA_ERR_INVALID_ARGUMENT;
+  if (!aligned(kv->k_pool, 16) || !aligned(kv->v_pool, 16) ||
+      !aligned(kv->block_table, 4))
     return RA_ERR_INVALID_ARGUMENT;
   if (kv->num_pages <= 0 || kv->max_pages <= 0 || kv->H_kv <= 0)
     return RA_ERR_INVALID_ARGUMENT;
@@ -88,6 +97,9 @@ static ra_status validate_decode(const uint16_t* q, int32_t H_q,
   if (st != RA_OK) return st;
   if (!q || !seq_lens || !k || !out || !ws) return RA_ERR_INVALID_ARGUMENT;
   if (k_max > 0 && !out_idx) return RA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(seq_lens, 4) || !aligned(k, 4) ||
+      !aligned(out, 4) || (out_idx && !aligned(out_idx, 4)))
+    return RA_ERR_INVALID_ARGUMENT;
   if (B <= 0 || B > RA_MAX_BATCH || H_q <= 0 || max_seq_len <= 0 ||
       max_seq_len > RA_MAX_SEQ_LEN || k_max < 0 || n_sink < 0 || window < 0)
     return RA_ERR_INVALID_ARGUMENT;
@@ -187,6 +199,8 @@ ra_status ra_kv_append(const ra_kv_layer* kv, const uint16_t* k_new,
   ra_status st = check_kv(kv);
   if (st != RA_OK) return st;
   if (!k_new || !v_new || !pos || B <= 0 || B > RA_MAX_BATCH)
+    return RA_ERR_INVALID_ARGUMENT;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos, 4))
     return RA_ERR_INVALID_ARGUMENT;
   if (launch_kv_append(*kv, k_new, v_new, pos, B, stream) != hipSuccess)
     return RA_ERR_HIP;
