@@ -4,19 +4,27 @@
 // Eqs. (3)-(5); backup frame "the normalization identity": merging disjoint
 // partials gives the exact softmax over their union).
 //
-// One block per (sequence, KV head, tile of 8192 positions = two units). The
-// block first takes each head's retrieved members of the tile: the entries
-// of the tile's (head, unit) candidate lists at or above the head's exact
-// threshold. It marks them in an LDS bitmap, stores their scores next to the
-// scores of W that the scan left, and writes their positions, ascending, with
-// their count, over the tile's consumed lists. It then walks
-// the union over the group's G query heads of those positions and the
-// tile's static positions in ascending order, reads each V row (256
-// contiguous bytes) once, and accumulates for every head that attends to
-// it: Z = sum e^{z - m}, N = sum e^{z - m} v, with m the head's largest
-// score over W u Omega (the scan records it), so no partial can overflow.
+// The attended set of head h is split into disjoint parts, one partial per
+// tile of 8192 positions (two units): the tile's retrieved positions, plus a
+// slice of the static set W (W's rows are dealt out evenly over the
+// sequence's tiles, so every block has about the same work). Every partial
+// of a head uses the same reference m (its largest score over W u Omega,
+// which the scan records), so none can overflow: Z = sum e^{z - m},
+// N = sum e^{z - m} v.
 //
-// merge: per query head, one block combines the tile partials,
+// gather, one block per (sequence, KV head, tile): the block takes each
+// head's retrieved members of its tile (the entries of the tile's
+// (head, unit) candidate lists at or above the head's exact threshold),
+// marks them in an LDS bitmap, stores their scores, and writes their
+// positions, ascending, with their count, over the tile's consumed lists.
+// Its rows are the union over the group's G query heads of those positions,
+// in ascending order, then its slice of W (attended by every head; the scan
+// left those scores). Each V row (256 contiguous bytes) is read once per
+// group: the weights e^{z - m} of every (row, head) are put in LDS (the
+// retrieved scores are staged in LDS by the filter, the W scores loaded up
+// front), then a V phase accumulates Z and N for every member head.
+//
+// merge: per query head, one block combines the partials,
 // out = sum_t e^{m_t - m} N_t / sum_t e^{m_t - m} Z_t, lse = m + ln(...),
 // and pads out_idx with -1 after k_eff; further blocks each copy the
 // retrieved positions of kMergeTiles tiles into out_idx at the offset the
@@ -27,18 +35,12 @@ namespace ra {
 
 constexpr int kGathThreads = 256;
 constexpr int kGathWaves = kGathThreads / 64;
-constexpr int kChunk = 1024;   // union positions listed in LDS at a time
-constexpr int kWBatch = 8;     // (row, head) weights per lane in flight
+constexpr int kChunk = 512;    // rows listed in LDS at a time
 constexpr int kListBatch = 8;  // list entries per lane in flight
-
-__device__ __forceinline__ uint64_t range_mask(int nw, int a, int c) {
-  const int s = max(a - nw, 0);
-  const int e = min(c - nw, 64);
-  if (e <= s) return 0ull;
-  const uint64_t hi = e == 64 ? ~0ull : ((1ull << e) - 1ull);
-  const uint64_t lo = (1ull << s) - 1ull;
-  return hi & ~lo;
-}
+constexpr int kSpec = 64;      // entries per candidate list read up front
+constexpr int kSel = 2048;     // retrieved entries of a tile staged in LDS
+constexpr uint32_t kPosMask = (1u << 24) - 1u;  // row = position | heads << 24
+constexpr int kWPre = 64;      // W-slice rows whose pages the prologue loads
 
 __device__ __forceinline__ float bf16lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
@@ -51,8 +53,57 @@ struct PackedCounts {
   int64_t v[kWords];
 };
 
+// V phase for rows [0, cnt) of a chunk: s_row (position | member heads << 24),
+// s_rpg (physical page) and s_w (weight e^{z - m} of (row, head), 0 if the
+// head does not attend the row) are in LDS. Adds the rows' contribution to
+// acc (this lane's 8 dims, for the 4 rows its 16-lane group covers) and to
+// zs (lane r == 0 of each group sums the weights of its rows). Block-wide.
 template <int G>
-__global__ __launch_bounds__(kGathThreads) __attribute__((amdgpu_waves_per_eu(4))) void gather_kernel(Params p) {
+__device__ __forceinline__ void accumulate_rows(const Params& p, int g, int cnt,
+                                                const uint32_t* s_row, const int32_t* s_rpg,
+                                                const float (*s_w)[G], float (&acc)[G][8],
+                                                float (&zs)[G]) {
+  constexpr int kVRows = G <= 4 ? 8 : 4;  // V rows per lane in flight
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int row = lane >> 4;
+  const int r = lane & 15;
+  // 4 rows per wave step, 16 lanes x 8 dims per V row
+  const size_t vpage = size_t(p.H_kv) * kPage * kHeadDim;
+  const uint16_t* vbase = p.v_pool + size_t(g) * kPage * kHeadDim + r * 8;
+  for (int i0 = wave * 4 + row; i0 < cnt; i0 += kGathWaves * 4 * kVRows) {
+    uint4 v[kVRows];
+#pragma unroll
+    for (int u = 0; u < kVRows; ++u) {
+      const int i = i0 + u * kGathWaves * 4;
+      v[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < cnt) {
+        const uint32_t pos = s_row[i] & kPosMask;
+        v[u] = *reinterpret_cast<const uint4*>(vbase + size_t(s_rpg[i]) * vpage +
+                                               size_t(pos & 63u) * kHeadDim);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kVRows; ++u) {
+      const int i = i0 + u * kGathWaves * 4;
+      if (i >= cnt) break;
+      const float vf[8] = {bf16lo(v[u].x), bf16hi(v[u].x), bf16lo(v[u].y), bf16hi(v[u].y),
+                           bf16lo(v[u].z), bf16hi(v[u].z), bf16lo(v[u].w), bf16hi(v[u].w)};
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float w = s_w[i][hh];
+        if (r == 0) zs[hh] += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[hh][e] += w * vf[e];
+      }
+    }
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(kGathThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void gather_kernel(Params p) {
   const int tile = blockIdx.x;
   const int bg = blockIdx.y;
   const int b = bg / p.H_kv;
@@ -65,58 +116,124 @@ __global__ __launch_bounds__(kGathThreads) __attribute__((amdgpu_waves_per_eu(4)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int row = lane >> 4;
   const int r = lane & 15;
-  const int wstart = max(sg.N - p.window, 0);  // W = [0, lo) u [wstart, N)
-  constexpr int kVRows = G <= 4 ? 8 : 4;       // V rows per lane in flight
-  constexpr int kCh = G <= 4 ? kChunk : kChunk / 2;  // union rows per chunk
+  constexpr int kCh = kChunk;
+  constexpr int kSpecPer = (2 * G * kSpec + kGathThreads - 1) / kGathThreads;
+  constexpr int kWzPer = (kWPre * G + kGathThreads - 1) / kGathThreads;
 
   __shared__ uint64_t bm[G][kWordsPerTile];
+  __shared__ uint64_t s_uw[kWordsPerTile];  // union of the heads' bitmaps
+  __shared__ int32_t s_ex[kWordsPerTile];   // union rows before each word
   __shared__ int32_t s_pg[kWordsPerTile];
-  __shared__ uint32_t ulist[kCh];           // offset in tile | heads << 13
-  __shared__ float s_w[kCh][G];             // softmax weight of (row, head), 0 if absent
+  __shared__ uint32_t s_row[kCh];
+  __shared__ int32_t s_rpg[kCh];
+  __shared__ float s_w[kCh][G];             // e^{z - m} of (row, head), 0 if absent
+  // the staged retrieved entries (offset in tile | head << 13, and score)
+  // share LDS with the final per-wave sums of N
+  constexpr int kStageBytes = kSel * 8;
+  constexpr int kAccBytes = kGathWaves * G * kHeadDim * 4;
+  __shared__ __align__(16) unsigned char s_raw[kStageBytes > kAccBytes ? kStageBytes : kAccBytes];
+  uint32_t* s_sel = reinterpret_cast<uint32_t*>(s_raw);
+  float* s_selz = reinterpret_cast<float*>(s_raw + kSel * 4);
+  float (*s_acc)[G][kHeadDim] = reinterpret_cast<float (*)[G][kHeadDim]>(s_raw);
+  __shared__ uint32_t s_nsel;
   __shared__ float s_zs[kGathWaves][G];
-  __shared__ float s_acc[kGathWaves][G][kHeadDim];
   __shared__ int64_t s_tmp[16];
   __shared__ HeadState s_st[G];
+  __shared__ float s_mref[G];
   __shared__ uint32_t s_lc[2 * G];          // list j: head j / 2, unit 2 tile + j % 2
   __shared__ uint32_t s_lpre[2 * G + 1];
+  __shared__ int32_t s_wpg[kWPre];          // pages of the first rows of the W slice
 
-  // every small load of the block at once: page numbers, list lengths,
-  // head states and the tile's out_idx offsets
-  for (int i = tid; i < G * kWordsPerTile; i += kGathThreads) (&bm[0][0])[i] = 0ull;
+  // this block's slice [w0, w1) of the rows of W = [0, lo) u [hi, N)
+  const int nt = (sg.N + kTile - 1) / kTile;
+  const int wsize = sg.lo + (sg.N - sg.hi);
+  const int wper = (wsize + nt - 1) / nt;
+  const int w0 = min(wsize, tile * wper);
+  const int w1 = min(wsize, w0 + wper);
+  auto w_pos = [&](int rr) { return rr < sg.lo ? rr : sg.hi + (rr - sg.lo); };
+
+  // Every load the block can issue up front, in one round: page numbers,
+  // list lengths, head states, the pages and scores of the W slice, and the
+  // first kSpec entries of each of the 2 G candidate lists (read before
+  // their lengths are known; entries past a list's end are dropped).
   const int units_seq = (sg.N + kUnit - 1) / kUnit;
   if (tid < kWordsPerTile) {
     // a 64-bit word covers exactly one 64-token page
     s_pg[tid] = (t0 + tid * 64 < sg.N) ? page_of(p, b, (t0 >> 6) + tid) : 0;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) bm[hh][tid] = 0ull;
   } else if (tid < kWordsPerTile + 2 * G) {
     const int j = tid - kWordsPerTile;
     const int unit = 2 * tile + (j & 1);
     s_lc[j] = unit < units_seq ? p.ucnt[(bh0 + (j >> 1)) * p.n_units + unit] : 0u;
-  } else if (tid >= kWordsPerTile + 64 && tid < kWordsPerTile + 64 + G) {
-    const int hh = tid - kWordsPerTile - 64;
+  } else if (tid >= kWordsPerTile + 32 && tid < kWordsPerTile + 32 + G) {
+    const int hh = tid - kWordsPerTile - 32;
     s_st[hh] = p.state[bh0 + hh];
+  } else if (tid >= kGathThreads - kWPre) {
+    const int i = tid - (kGathThreads - kWPre);
+    if (w0 + i < w1) s_wpg[i] = page_of(p, b, w_pos(w0 + i) >> 6);
+  }
+  if (tid == 0) s_nsel = 0u;
+  uint64_t spec[kSpecPer];
+#pragma unroll
+  for (int u = 0; u < kSpecPer; ++u) {
+    const int e = u * kGathThreads + tid;
+    const int j = e / kSpec, i = e - j * kSpec;
+    const int unit = 2 * tile + (j & 1);
+    spec[u] = (j < 2 * G && unit < units_seq)
+                  ? p.cand[(bh0 + (j >> 1)) * p.n_cap + size_t(unit) * kUnit + i]
+                  : 0ull;
+  }
+  float wz[kWzPer];  // score of W-slice row q / G for head q % G, q = u * 256 + tid
+#pragma unroll
+  for (int u = 0; u < kWzPer; ++u) {
+    const int q = u * kGathThreads + tid;
+    const int i = q / G;
+    wz[u] = (i < kWPre && w0 + i < w1)
+                ? p.scores[(bh0 + q % G) * p.n_cap + w_pos(w0 + i)]
+                : 0.0f;
   }
   __syncthreads();
+  if (tid < G) s_mref[tid] = softmax_ref(s_st[tid], sg.k_eff);
+
+  // Each head's retrieved members of this tile: the list entries whose
+  // composite (key - lo) << 32 | ~n clears the head's threshold. They are
+  // marked in the bitmap, their scores stored, and staged in LDS.
+  auto take = [&](int hh, uint64_t v) {
+    const uint32_t key = uint32_t(v >> 32);
+    const uint32_t n = uint32_t(v);
+    const uint64_t comp = (uint64_t(key - s_st[hh].lo_key) << 32) | uint32_t(~n);
+    const uint64_t thr = (uint64_t(s_st[hh].thr_hi) << 32) | s_st[hh].thr_lo;
+    if ((comp >> s_st[hh].thr_shift) < thr) return;
+    const int off = int(n) - t0;
+    atomicOr(reinterpret_cast<unsigned long long*>(&bm[hh][off >> 6]), 1ull << (off & 63));
+    const float z = key2f(key);
+    p.scores[(bh0 + hh) * p.n_cap + n] = z;
+    const uint32_t at = atomicAdd(&s_nsel, 1u);
+    if (at < uint32_t(kSel)) {
+      s_sel[at] = uint32_t(off) | (uint32_t(hh) << 13);
+      s_selz[at] = z;
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < kSpecPer; ++u) {
+    const int e = u * kGathThreads + tid;
+    const int j = e / kSpec, i = e - j * kSpec;
+    if (j < 2 * G && uint32_t(i) < s_lc[j] && s_st[j >> 1].thr_shift < 64u) take(j >> 1, spec[u]);
+  }
+  // the rest of the lists (past kSpec entries), as one index space
   if (tid == 0) {
     uint32_t run = 0;
     for (int j = 0; j < 2 * G; ++j) {
       s_lpre[j] = run;
-      if (s_st[j >> 1].thr_shift < 64u) run += s_lc[j];
+      if (s_st[j >> 1].thr_shift < 64u && s_lc[j] > uint32_t(kSpec)) run += s_lc[j] - kSpec;
     }
     s_lpre[2 * G] = run;
   }
-  float mref[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) mref[hh] = softmax_ref(s_st[hh], sg.k_eff);
   __syncthreads();
-
-  // each head's retrieved members of this tile: the list entries whose
-  // composite (key - lo) << 32 | ~n clears the head's threshold. The 2 G
-  // lists are walked as one index space, kListBatch entries per lane in
-  // flight.
-  const uint32_t total = s_lpre[2 * G];
-  for (uint32_t base = 0; base < total; base += kGathThreads * kListBatch) {
+  const uint32_t rest = s_lpre[2 * G];
+  for (uint32_t base = 0; base < rest; base += kGathThreads * kListBatch) {
     uint64_t v[kListBatch];
     int jl[kListBatch];
 #pragma unroll
@@ -124,40 +241,27 @@ __global__ __launch_bounds__(kGathThreads) __attribute__((amdgpu_waves_per_eu(4)
       const uint32_t i = base + u * kGathThreads + tid;
       v[u] = 0ull;
       jl[u] = -1;
-      if (i < total) {
+      if (i < rest) {
         int j = 0;
         while (j + 1 < 2 * G && s_lpre[j + 1] <= i) ++j;
         jl[u] = j;
-        v[u] = p.cand[(bh0 + (j >> 1)) * p.n_cap + size_t(2 * tile + (j & 1)) * kUnit +
+        v[u] = p.cand[(bh0 + (j >> 1)) * p.n_cap + size_t(2 * tile + (j & 1)) * kUnit + kSpec +
                       (i - s_lpre[j])];
       }
     }
 #pragma unroll
-    for (int u = 0; u < kListBatch; ++u) {
-      if (jl[u] < 0) continue;
-      const int hh = jl[u] >> 1;
-      const uint32_t key = uint32_t(v[u] >> 32);
-      const uint32_t n = uint32_t(v[u]);
-      const uint64_t comp = (uint64_t(key - s_st[hh].lo_key) << 32) | uint32_t(~n);
-      const uint64_t thr = (uint64_t(s_st[hh].thr_hi) << 32) | s_st[hh].thr_lo;
-      if ((comp >> s_st[hh].thr_shift) >= thr) {
-        atomicOr(reinterpret_cast<unsigned long long*>(&bm[hh][(int(n) - t0) >> 6]),
-                 1ull << (n & 63u));
-        p.scores[(bh0 + hh) * p.n_cap + n] = key2f(key);
-      }
-    }
+    for (int u = 0; u < kListBatch; ++u)
+      if (jl[u] >= 0) take(jl[u] >> 1, v[u]);
   }
   __syncthreads();
 
-  // union of the group's selections and W, and each head's ranks
-  uint64_t uw = 0, wm = 0;
+  // union over the group's heads, and each head's ranks
+  uint64_t uw = 0;
   const int nw = t0 + tid * 64;
   PackedCounts<G> pc;
 #pragma unroll
   for (int j = 0; j < PackedCounts<G>::kWords; ++j) pc.v[j] = 0;
   if (tid < kWordsPerTile) {
-    wm = range_mask(nw, 0, sg.lo) | range_mask(nw, wstart, sg.N);
-    uw = wm;
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       uw |= bm[hh][tid];
@@ -170,9 +274,11 @@ __global__ __launch_bounds__(kGathThreads) __attribute__((amdgpu_waves_per_eu(4)
 #pragma unroll
   for (int j = 0; j < PackedCounts<G>::kWords; ++j)
     px.v[j] = block_excl_scan(pc.v[j], s_tmp, &ptot.v[j]);
-  // the tile's retrieved positions, ascending, replace its consumed lists
-  // (the merge concatenates the tiles into out_idx)
   if (tid < kWordsPerTile) {
+    s_uw[tid] = uw;
+    s_ex[tid] = int32_t(ex);
+    // the tile's retrieved positions, ascending, replace its consumed lists
+    // (the merge concatenates the tiles into out_idx)
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       uint64_t y = bm[hh][tid];
@@ -188,29 +294,22 @@ __global__ __launch_bounds__(kGathThreads) __attribute__((amdgpu_waves_per_eu(4)
   if (tid < G)
     p.scnt[(bh0 + tid) * p.n_tiles + tile] =
         uint32_t((ptot.v[tid >> 2] >> (16 * (tid & 3))) & 0xFFFF);
-  const int U = int(utotal);
+  const bool staged = s_nsel <= uint32_t(kSel);
 
-  // Two phases per chunk of the union: (A) the weights e^{z - m} of every
-  // (row, head) pair into LDS, one head per lane (lane t serves head
-  // t % G), all score loads in flight at once; (B) the V rows, kVRows per
-  // lane in flight, accumulated with the weights from LDS.
-  float acc[G][8];
+  float acc[G][8], zs[G];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
+  for (int hh = 0; hh < G; ++hh) {
+    zs[hh] = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
-  const int my_h = tid % G;
-  float zsum = 0.0f;  // this lane's share of Z for head my_h
-  float mref_h = mref[0];
-#pragma unroll
-  for (int hh = 1; hh < G; ++hh)
-    if (my_h == hh) mref_h = mref[hh];
-  const float* zrow = p.scores + (bh0 + my_h) * p.n_cap;
-  const size_t vpage = size_t(p.H_kv) * kPage * kHeadDim;
-  const uint16_t* vbase = p.v_pool + size_t(g) * kPage * kHeadDim + r * 8;
-  for (int cb = 0; cb < U; cb += kCh) {
-    // list this chunk of the union in LDS
-    if (tid < kWordsPerTile) {
+  }
+  // rows: the union (U rows, ascending), then the W slice
+  const int U = int(utotal);
+  const int R = U + (w1 - w0);
+  for (int cb = 0; cb < R; cb += kCh) {
+    const int cnt = min(kCh, R - cb);
+    // list this chunk of the rows in LDS, weights cleared
+    if (tid < kWordsPerTile && cb < U) {
       int pos = int(ex) - cb;
       uint64_t x = uw;
       while (x && pos < kCh) {
@@ -218,88 +317,72 @@ __global__ __launch_bounds__(kGathThreads) __attribute__((amdgpu_waves_per_eu(4)
         x &= x - 1ull;
         if (pos >= 0) {
           uint32_t mem = 0;
-          if ((wm >> bit) & 1ull) {
-            mem = (1u << G) - 1u;
-          } else {
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) mem |= uint32_t((bm[hh][tid] >> bit) & 1ull) << hh;
-          }
-          ulist[pos] = uint32_t(tid * 64 + bit) | (mem << 13);
+          for (int hh = 0; hh < G; ++hh) mem |= uint32_t((bm[hh][tid] >> bit) & 1ull) << hh;
+          s_row[pos] = uint32_t(nw + bit) | (mem << 24);
+          s_rpg[pos] = s_pg[tid];
         }
         ++pos;
       }
     }
+    const int cw0 = max(cb, U), cw1 = cb + cnt;
+    for (int i = cw0 + tid; i < cw1; i += kGathThreads) {
+      const int wi = i - U;  // row of the slice
+      const int pos = w_pos(w0 + wi);
+      s_row[i - cb] = uint32_t(pos) | (((1u << G) - 1u) << 24);
+      s_rpg[i - cb] = wi < kWPre ? s_wpg[wi] : page_of(p, b, pos >> 6);
+    }
+    for (int i = tid; i < cnt * G; i += kGathThreads) (&s_w[0][0])[i] = 0.0f;
     __syncthreads();
-    const int cnt = min(kCh, U - cb);
-    // (A) pair q = i * G + h: row i, head h = my_h; kWBatch pairs per lane
-    // in flight
-    for (int q0 = 0; q0 < cnt * G; q0 += kGathThreads * kWBatch) {
-      float z[kWBatch];
-      bool in[kWBatch];
-#pragma unroll
-      for (int u = 0; u < kWBatch; ++u) {
-        const int i = (q0 + u * kGathThreads + tid) / G;
-        in[u] = false;
-        z[u] = 0.0f;
-        if (i < cnt) {
-          const uint32_t e = ulist[i];
-          in[u] = ((e >> (13 + my_h)) & 1u) != 0u;
-          if (in[u]) z[u] = zrow[t0 + int(e & 8191u)];
-        }
+    // weights of the retrieved rows in this chunk
+    if (staged) {
+      const uint32_t ns = s_nsel;
+      for (uint32_t e = tid; e < ns; e += kGathThreads) {
+        const uint32_t sv = s_sel[e];
+        const int off = int(sv & 8191u), hh = int(sv >> 13);
+        const int word = off >> 6, bit = off & 63;
+        const int rr = s_ex[word] + __popcll(s_uw[word] & ((1ull << bit) - 1ull)) - cb;
+        if (rr >= 0 && rr < cnt) s_w[rr][hh] = expf(s_selz[e] - s_mref[hh]);
       }
-#pragma unroll
-      for (int u = 0; u < kWBatch; ++u) {
-        const int i = (q0 + u * kGathThreads + tid) / G;
-        const float w = in[u] ? expf(z[u] - mref_h) : 0.0f;
-        zsum += w;
-        if (i < cnt) s_w[i][my_h] = w;
+    } else {
+      // too many retrieved rows to stage: read their scores back
+      for (int q = tid; q < min(cnt, U - cb) * G; q += kGathThreads) {
+        const int i = q / G, hh = q % G;
+        const uint32_t e = s_row[i];
+        if ((e >> (24 + hh)) & 1u)
+          s_w[i][hh] = expf(p.scores[(bh0 + hh) * p.n_cap + (e & kPosMask)] - s_mref[hh]);
       }
     }
-    __syncthreads();
-    // (B) 4 rows per wave step, 16 lanes x 8 dims per V row
-    for (int i0 = wave * 4 + row; i0 < cnt; i0 += kGathWaves * 4 * kVRows) {
-      uint4 v[kVRows];
+    // weights of the W rows in this chunk (every head)
 #pragma unroll
-      for (int u = 0; u < kVRows; ++u) {
-        const int i = i0 + u * kGathWaves * 4;
-        const int off = i < cnt ? int(ulist[i] & 8191u) : 0;
-        const int pg = s_pg[off >> 6];
-        v[u] = i < cnt ? *reinterpret_cast<const uint4*>(vbase + size_t(pg) * vpage +
-                                                         size_t((t0 + off) & 63) * kHeadDim)
-                       : make_uint4(0u, 0u, 0u, 0u);
-      }
-#pragma unroll
-      for (int u = 0; u < kVRows; ++u) {
-        const int i = i0 + u * kGathWaves * 4;
-        if (i >= cnt) break;
-        const float vf[8] = {bf16lo(v[u].x), bf16hi(v[u].x), bf16lo(v[u].y), bf16hi(v[u].y),
-                             bf16lo(v[u].z), bf16hi(v[u].z), bf16lo(v[u].w), bf16hi(v[u].w)};
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const float w = s_w[i][hh];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[hh][e] += w * vf[e];
-        }
-      }
+    for (int u = 0; u < kWzPer; ++u) {
+      const int q = u * kGathThreads + tid;
+      const int i = U + q / G - cb;  // chunk row of slice row q / G
+      if (q / G < kWPre && w0 + q / G < w1 && i >= 0 && i < cnt)
+        s_w[i][q % G] = expf(wz[u] - s_mref[q % G]);
     }
+    for (int i = max(cw0, U + kWPre) + tid; i < cw1; i += kGathThreads) {
+      const int pos = w_pos(w0 + i - U);
+      for (int hh = 0; hh < G; ++hh)
+        s_w[i - cb][hh] = expf(p.scores[(bh0 + hh) * p.n_cap + pos] - s_mref[hh]);
+    }
+    __syncthreads();
+    accumulate_rows<G>(p, g, cnt, s_row, s_rpg, s_w, acc, zs);
     __syncthreads();
   }
-  // Z per head: lanes with equal tid % G of each wave, then the waves
-#pragma unroll
-  for (int m = G; m < 64; m <<= 1) zsum += __shfl_xor(zsum, m);
-  float zs[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) zs[hh] = __shfl(zsum, hh);
-  // sum the 4 rows of each wave, then the waves
+
+  // Z and N: sum the 4 row groups of each wave, then the waves
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
+    zs[hh] += __shfl_xor(zs[hh], 16);
+    zs[hh] += __shfl_xor(zs[hh], 32);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       acc[hh][e] += __shfl_xor(acc[hh][e], 16);
       acc[hh][e] += __shfl_xor(acc[hh][e], 32);
     }
   }
-  if (row == 0) {
+  if ((lane >> 4) == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
@@ -321,20 +404,18 @@ __global__ __launch_bounds__(kGathThreads) __attribute__((amdgpu_waves_per_eu(4)
     float z = 0.0f;
     for (int w = 0; w < kGathWaves; ++w) z += s_zs[w][tid];
     float* mz = p.part_mz + ((bh0 + tid) * p.n_tiles + tile) * 2;
-    mz[0] = mref[tid];
+    mz[0] = s_mref[tid];
     mz[1] = z;
   }
-
 }
 
 // ---------------------------------------------------------------- merge
 // One block per (sequence, query head): 8 groups of 32 threads each take
-// every 8th tile, 4 dims per thread (float4 loads issued kMergeUnroll deep),
-// then the groups are summed in LDS in a fixed order.
+// every 8th partial, 4 dims per thread (float4 loads issued kMergeUnroll
+// deep), then the groups are summed in LDS in a fixed order.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeGroups = kMergeThreads / 32;
 constexpr int kMergeUnroll = 4;
-
 constexpr int kMergeTiles = 8;  // tiles per out_idx copy block
 
 // out_idx for tiles [c * kMergeTiles, (c + 1) * kMergeTiles) of head bh.
@@ -402,11 +483,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p) {
   const float* pn = p.part_n + size_t(bh) * p.n_tiles * kHeadDim + d0;
   __shared__ float s_red[kMergeGroups][kHeadDim + 4];
   __shared__ float s_m[kMergeThreads / 64];
+  const int np = nt;
+  auto slot = [](int j) { return j; };
 
-
-  // m = max over tiles with a non-empty partial
+  // m = max over the non-empty partials
   float m = -INFINITY;
-  for (int t = tid; t < nt; t += kMergeThreads) m = fmaxf(m, mz[2 * t + 1] > 0.0f ? mz[2 * t] : -INFINITY);
+  for (int j = tid; j < np; j += kMergeThreads) {
+    const int t = slot(j);
+    m = fmaxf(m, mz[2 * t + 1] > 0.0f ? mz[2 * t] : -INFINITY);
+  }
   m = wave_max(m);
   if ((tid & 63) == 0) s_m[tid >> 6] = m;
   __syncthreads();
@@ -416,14 +501,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p) {
   float Z = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (m > -INFINITY) {
-    for (int t0 = grp; t0 < nt; t0 += kMergeGroups * kMergeUnroll) {
+    for (int j0 = grp; j0 < np; j0 += kMergeGroups * kMergeUnroll) {
       float2 w2[kMergeUnroll];
       float4 v[kMergeUnroll];
 #pragma unroll
       for (int u = 0; u < kMergeUnroll; ++u) {
-        const int t = t0 + u * kMergeGroups;
-        w2[u] = t < nt ? *reinterpret_cast<const float2*>(mz + 2 * t) : make_float2(0.f, 0.f);
-        v[u] = t < nt ? *reinterpret_cast<const float4*>(pn + size_t(t) * kHeadDim)
+        const int j = j0 + u * kMergeGroups;
+        const int t = slot(j);
+        w2[u] = j < np ? *reinterpret_cast<const float2*>(mz + 2 * t) : make_float2(0.f, 0.f);
+        v[u] = j < np ? *reinterpret_cast<const float4*>(pn + size_t(t) * kHeadDim)
                       : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
@@ -466,8 +552,8 @@ hipError_t launch_merge(const Params& p, hipStream_t s) {
 }
 
 hipError_t launch_gather(const Params& p, hipStream_t s) {
-  const unsigned tiles = unsigned((int64_t(p.max_seq_len) + kTile - 1) / kTile);
-  const dim3 grid{tiles, unsigned(p.B * p.H_kv)}, block{unsigned(kGathThreads)};
+  const dim3 grid{unsigned(p.n_tiles), unsigned(p.B * p.H_kv)};
+  const dim3 block{unsigned(kGathThreads)};
   switch (p.G) {
     case 1: hipLaunchKernelGGL(gather_kernel<1>, grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL(gather_kernel<2>, grid, block, 0, s, p); break;
