@@ -10,9 +10,10 @@
 // k_eff largest composites" is the unique tie-broken top-k.
 //
 // threshold (one block per head, before the scan): from the keys of the
-// sampled positions, the key of the R-th largest sampled member, with R a
-// conservative stand-in for the rank of the k-th largest member of M in the
-// sample. Members at or above it are the head's candidates.
+// sampled positions, a key at or just below the R-th largest sampled member
+// (its top 22 bits), with R a conservative stand-in for the rank of the k-th
+// largest member of M in the sample. Members at or above it are the head's
+// candidates.
 //
 // select (one block per head, after the scan): if the per-unit candidate
 // lists hold at least k_eff entries, the top-k of M is the top-k of the
@@ -27,6 +28,7 @@ namespace ra {
 
 constexpr int kSelThreads = 512;
 constexpr int kSubCap = 2048;     // LDS list for one radix sub-bucket
+constexpr uint32_t kRankMax = 256; // sub-buckets up to this size are finished by ranking
 constexpr int kBatch = 8;         // global entries per lane in flight per pass
 constexpr int kRegEntries = 64;   // candidate entries per lane kept in registers
 constexpr int kRegKeys = 32;      // sampled keys per lane kept in registers
@@ -109,24 +111,36 @@ struct RegLists {
   uint64_t c[NR];
   uint32_t total;
 
-  __device__ __forceinline__ void load(const UnitLists& src) {
+  // start: LDS scratch of NR * blockDim / 64 entries. Entry q gets the unit
+  // of list entry 64 q (one search per thread); the lanes of a wave, which
+  // hold 64 consecutive entries, then step forward from their first unit.
+  __device__ __forceinline__ void load(const UnitLists& src, uint16_t* start) {
     total = src.pre[src.nu];
     const uint32_t l = src.lo;
-#pragma unroll
-    for (int r0 = 0; r0 < NR; r0 += kBatch) {
-      if (uint32_t(r0) * blockDim.x >= total) break;  // uniform
+    const uint32_t nq = (total + 63u) / 64u;
+    for (uint32_t q = threadIdx.x; q < nq; q += blockDim.x) {
       uint32_t idx[kBatch];
       int a[kBatch];
+      idx[0] = q * 64u;
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) idx[u] = (r0 + u) * blockDim.x + threadIdx.x;
+      for (int u = 1; u < kBatch; ++u) idx[u] = idx[0];
       src.locate(idx, a);
+      start[q] = uint16_t(a[0]);
+    }
+    __syncthreads();
+    const int wave = threadIdx.x >> 6;
+    const int waves = blockDim.x >> 6;
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        uint64_t v = 0ull;
-        if (idx[u] < total)
-          v = src.list[size_t(src.u_lo + a[u]) * kUnit + (idx[u] - src.pre[a[u]])];
-        c[r0 + u] = v;
+    for (int r = 0; r < NR; ++r) {
+      if (uint32_t(r) * blockDim.x >= total) break;  // uniform
+      const uint32_t i = r * blockDim.x + threadIdx.x;
+      uint64_t v = 0ull;
+      if (i < total) {
+        int a = start[r * waves + wave];
+        while (a + 1 < src.nu && src.pre[a + 1] <= i) ++a;
+        v = src.list[size_t(src.u_lo + a) * kUnit + (i - src.pre[a])];
       }
+      c[r] = v;
     }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -270,9 +284,34 @@ __device__ __forceinline__ void radix_finish(const Src& src, const Radix& rx, in
   }
 }
 
+// The need-th largest of n <= blockDim values in LDS, ties allowed: the
+// value v with #(x > v) < need <= #(x >= v), found by letting each entry
+// count the entries above it (one broadcast pass over LDS instead of
+// several radix passes, for the small buckets left after the first pass).
+__device__ __forceinline__ uint64_t rank_select(const uint64_t* sub, uint32_t n, uint32_t need) {
+  __shared__ uint64_t s_val;
+  const uint32_t t = threadIdx.x;
+  if (t < n) {
+    const uint64_t c = sub[t];
+    uint32_t gt = 0, eq = 0;
+#pragma unroll 8
+    for (uint32_t j = 0; j < n; ++j) {
+      const uint64_t x = sub[j];
+      gt += x > c ? 1u : 0u;
+      eq += x == c ? 1u : 0u;
+    }
+    if (gt < need && gt + eq >= need) s_val = c;
+  }
+  __syncthreads();
+  const uint64_t v = s_val;
+  __syncthreads();
+  return v;
+}
+
 // Composite prefix (top plen of TB bits) of the need-th largest member of a
 // source: one pass over it; if that does not settle it and the chosen
-// sub-bucket fits LDS, the sub-bucket is copied there and finished in LDS.
+// sub-bucket fits LDS, the sub-bucket is copied there and finished in LDS
+// (by ranking when it is small, else by more radix passes).
 // Members whose top plen bits are >= the returned prefix are exactly the
 // need largest (all of them when every bit is fixed and values tie).
 template <typename Src>
@@ -294,7 +333,13 @@ __device__ __forceinline__ void find_threshold(const Src& src, const Radix& rx, 
     wave_append(sub, s_n, kSubCap, c, valid && (c >> (TB - pl)) == pf);
   });
   __syncthreads();
-  const LdsSource lds{sub, *s_n};
+  const uint32_t n = *s_n;
+  if (n <= kRankMax) {
+    prefix = rank_select(sub, n, need);
+    plen = TB;
+    return;
+  }
+  const LdsSource lds{sub, n};
   radix_finish(lds, rx, TB, need, prefix, plen);
 }
 
@@ -310,8 +355,7 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(Params p) {
   const int hq = bh - b * p.H_q;
   const int tid = threadIdx.x;
   __shared__ uint32_t hist[2048];
-  __shared__ uint32_t s_d, s_above, s_cnt, s_n;
-  __shared__ uint64_t sub[kSubCap];
+  __shared__ uint32_t s_d, s_above, s_cnt;
   __shared__ int64_t tmp[16];
 
   if (bh == 0) {
@@ -373,13 +417,19 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(Params p) {
     if (m_s == 0 || int64_t(R) >= m_s) {
       lo = 0u;  // keep every member of M
     } else {
+      // the bound need not be exact, only at or below the R-th largest
+      // sampled key: two radix passes fix its top 22 bits
       const Radix rx{hist, &s_d, &s_above, &s_cnt};
-      uint64_t prefix;
-      int plen;
+      uint64_t prefix = 0;
+      int plen = 0;
+      uint32_t need = R;
       if (in_regs) {
-        find_threshold(rk, rx, 32, R, sub, &s_n, prefix, plen);
+        radix_pass(rk, rx, 32, need, prefix, plen);
+        radix_pass(rk, rx, 32, need, prefix, plen);
       } else {
-        find_threshold(SampleKeys{keys, count}, rx, 32, R, sub, &s_n, prefix, plen);
+        const SampleKeys sk{keys, count};
+        radix_pass(sk, rx, 32, need, prefix, plen);
+        radix_pass(sk, rx, 32, need, prefix, plen);
       }
       lo = uint32_t(prefix << (32 - plen));
     }
@@ -405,6 +455,7 @@ hipError_t launch_threshold(const Params& p, hipStream_t s) {
 
 // ---------------------------------------------------------------- select
 struct SelLds {
+  uint16_t start[kRegEntries * kSelThreads / 64];  // unit of every 64th entry
   uint32_t pre[kMaxUnits + 1];  // prefix of the list lengths
   uint32_t hist[2048];
   uint64_t sub[kSubCap];
@@ -474,7 +525,7 @@ __device__ __forceinline__ void select_head(const Params& p, int bh, const SeqGe
   const UnitLists gl{p.cand + size_t(bh) * p.n_cap, L.pre, u_lo, nu, lo};
   if (L.pre[kMaxUnits] <= uint32_t(kRegEntries * kSelThreads)) {
     RegLists<kRegEntries> rl;
-    rl.load(gl);
+    rl.load(gl, L.start);
     decide(p, bh, sg, rl, TB, lo, L);
   } else {
     decide(p, bh, sg, gl, TB, lo, L);
