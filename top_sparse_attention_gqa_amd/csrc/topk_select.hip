@@ -81,11 +81,12 @@ struct UnitLists {
     }
   }
 
+  // Entries [first, total) of the lists.
   template <typename Fn>
-  __device__ __forceinline__ void for_each(Fn&& fn) const {
+  __device__ __forceinline__ void for_each_from(uint32_t first, Fn&& fn) const {
     const uint32_t l = lo;
     const uint32_t total = pre[nu];
-    for (uint32_t base = 0; base < total; base += blockDim.x * kBatch) {
+    for (uint32_t base = first; base < total; base += blockDim.x * kBatch) {
       uint32_t idx[kBatch];
       int a[kBatch];
 #pragma unroll
@@ -102,20 +103,28 @@ struct UnitLists {
       }
     }
   }
+
+  template <typename Fn>
+  __device__ __forceinline__ void for_each(Fn&& fn) const {
+    for_each_from(0u, fn);
+  }
 };
 
-// The same lists read once into registers (entry r * blockDim + t in slot r
-// of thread t), for heads with at most kRegEntries * blockDim candidates.
+// The same lists with their first NR * blockDim entries read once into
+// registers (entry r * blockDim + t in slot r of thread t); entries past
+// those are streamed from global memory on every pass.
 template <int NR>
 struct RegLists {
   uint64_t c[NR];
-  uint32_t total;
+  uint32_t total;  // entries held in registers
+  UnitLists rest;
 
   // start: LDS scratch of NR * blockDim / 64 entries. Entry q gets the unit
   // of list entry 64 q (one search per thread); the lanes of a wave, which
   // hold 64 consecutive entries, then step forward from their first unit.
   __device__ __forceinline__ void load(const UnitLists& src, uint16_t* start) {
-    total = src.pre[src.nu];
+    rest = src;
+    total = min(src.pre[src.nu], uint32_t(NR) * blockDim.x);
     const uint32_t l = src.lo;
     const uint32_t nq = (total + 63u) / 64u;
     for (uint32_t q = threadIdx.x; q < nq; q += blockDim.x) {
@@ -157,6 +166,7 @@ struct RegLists {
       const uint32_t i = r * blockDim.x + threadIdx.x;
       fn(c[r], int(~uint32_t(c[r])), i < total);
     }
+    rest.for_each_from(uint32_t(NR) * blockDim.x, fn);
   }
 };
 
@@ -523,13 +533,9 @@ __device__ __forceinline__ void select_head(const Params& p, int bh, const SeqGe
   const uint32_t span = max_m > lo ? max_m - lo : 1u;
   const int TB = 32 + bit_length(span);
   const UnitLists gl{p.cand + size_t(bh) * p.n_cap, L.pre, u_lo, nu, lo};
-  if (L.pre[kMaxUnits] <= uint32_t(kRegEntries * kSelThreads)) {
-    RegLists<kRegEntries> rl;
-    rl.load(gl, L.start);
-    decide(p, bh, sg, rl, TB, lo, L);
-  } else {
-    decide(p, bh, sg, gl, TB, lo, L);
-  }
+  RegLists<kRegEntries> rl;
+  rl.load(gl, L.start);
+  decide(p, bh, sg, rl, TB, lo, L);
 }
 
 // One block per head: count the candidates; decide the threshold, or flag
