@@ -33,6 +33,7 @@ constexpr int kScanThreads = 512;
 constexpr int kScanWaves = kScanThreads / 64;
 constexpr int kStage = 6144;       // LDS candidate staging entries per block
 constexpr int kSampleWaves = 8;    // sampled pages per sample block (one per wave)
+constexpr int kSampleThreads = kSampleWaves * 64;
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
 
 template <int G>
@@ -172,7 +173,7 @@ __device__ __forceinline__ void page_scores(const Params& p, int pg, int g, cons
 // c * kSampleWaves .. of group bg, one page per wave, and stores the keys of
 // the sampled positions per head (0 for positions outside M).
 template <int G>
-__global__ __launch_bounds__(kScanThreads) void sample_kernel(Params p) {
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(Params p) {
   const int bg = blockIdx.x;
   const int b = bg / p.H_kv;
   const int g = bg - b * p.H_kv;
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(kScanThreads) void sample_kernel(Params p) {
 hipError_t launch_sample(const Params& p, hipStream_t s) {
   const int ns_max = p.samp_cap / kPage;
   const unsigned chunks = unsigned(ns_max > 0 ? (ns_max + kSampleWaves - 1) / kSampleWaves : 1);
-  const dim3 grid{unsigned(p.B * p.H_kv), chunks}, block{unsigned(kScanThreads)};
+  const dim3 grid{unsigned(p.B * p.H_kv), chunks}, block{unsigned(kSampleThreads)};
   switch (p.G) {
     case 1: hipLaunchKernelGGL(sample_kernel<1>, grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL(sample_kernel<2>, grid, block, 0, s, p); break;
@@ -283,10 +284,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
     float* srow = p.scores + (bh0 + L.F) * p.n_cap;
     const size_t ubase = size_t(ur.u) * kUnit;
     uint64_t* crow = p.cand + (bh0 + L.F) * p.n_cap + ubase;
+    // the physical pages of this wave's pages of the unit, read up front
+    // (lane k holds the page of the wave's k-th page)
+    const int my_pg = L.lane < kUnitPages / kScanWaves && wave + kScanWaves * L.lane < ur.npages
+                          ? page_of(p, b, ur.u * kUnitPages + wave + kScanWaves * L.lane)
+                          : 0;
     for (int jj = wave; jj < ur.npages; jj += kScanWaves) {
       const int j = ur.u * kUnitPages + jj;
       float z[G];
-      page_scores<G>(p, page_of(p, b, j), g, L, qreg, z);
+      page_scores<G>(p, __shfl(my_pg, (jj - wave) / kScanWaves), g, L, qreg, z);
 #pragma unroll
       for (int s = 0; s < G; ++s) {
         const int n = j * kPage + L.tok(s);
