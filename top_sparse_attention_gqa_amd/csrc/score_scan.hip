@@ -366,10 +366,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
   }
 }
 
+// One persistent block per CU: the scan block's registers leave room for
+// one 8-wave block per CU, so a larger grid would only run in two rounds.
 static unsigned scan_blocks(const Params& p) {
   const int64_t units_max = int64_t(p.B) * p.H_kv *
       ((int64_t(p.max_seq_len) + kUnit - 1) / kUnit);
-  const int64_t cap = int64_t(2) * (p.num_cus > 0 ? p.num_cus : 256);
+  const int64_t cap = p.num_cus > 0 ? p.num_cus : 256;
   int64_t blocks = units_max < cap ? units_max : cap;
   if (blocks < 1) blocks = 1;
   return unsigned(blocks);
