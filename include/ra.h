@@ -179,6 +179,17 @@ size_t ra_workspace_scores_offset(int32_t B, int32_t H_q, int32_t H_kv,
                                   int32_t max_seq_len, int32_t k_max,
                                   int64_t* row_stride);
 
+/*
+ * Where a uint32 counter lives inside a workspace sized for these
+ * capacities (byte offset, 4-byte aligned): after RA_STAGE_SELECT of a call
+ * it holds the number of query heads whose candidates fell short of k_eff,
+ * which RA_STAGE_DENSE then decides by the full rescan (0 in the common
+ * case). A diagnostic; the caller reads it from device memory itself.
+ * Returns (size_t)-1 if the arguments are invalid.
+ */
+size_t ra_workspace_rescan_count_offset(int32_t B, int32_t H_q, int32_t H_kv,
+                                        int32_t max_seq_len, int32_t k_max);
+
 #ifdef __cplusplus
 }
 #endif

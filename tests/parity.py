@@ -41,8 +41,9 @@ def say(msg: str) -> None:
 class Run:
     """Outputs of one decode step on the GPU, as host arrays."""
 
-    def __init__(self, out, lse, idx, scores=None):
+    def __init__(self, out, lse, idx, scores=None, rescanned=0):
         self.out, self.lse, self.idx, self.scores = out, lse, idx, scores
+        self.rescanned = rescanned  # heads decided by the full rescan
 
 
 def gpu_decode(L: synth.LayerInputs, max_seq_len: int | None = None, k_max: int | None = None,
@@ -69,7 +70,8 @@ def gpu_decode(L: synth.LayerInputs, max_seq_len: int | None = None, k_max: int 
     torch.cuda.synchronize()
     return Run(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
                idx.cpu().numpy()[:, :, :k_max],
-               sc.cpu().numpy() if sc is not None else None)
+               sc.cpu().numpy() if sc is not None else None,
+               ra.rescan_count(ws, B, H_q, L.H_kv, max_seq_len, k_max))
 
 
 def host_seq(L: synth.LayerInputs, b: int, kv_heads=None):

@@ -135,19 +135,49 @@ def test_constant_keys_rescan_path():
         assert run.idx[0, h].tolist() == list(range(16, 16 + 5000))
 
 
-def test_misleading_sample_takes_the_dense_path():
-    # keys aligned with every query only on the sampled pages (one page in 4
-    # at N = 32768): the sample sees mostly high scores, so its threshold
-    # leaves fewer than k candidates and the head is decided on the dense path
-    say("case sample_misled: N=32768, high keys on sampled pages only, k=9000")
-    L = layer(4, 1, [32768], [9000], 16, 64)
-    qdir = L.q[0].float().sum(0)
+def sample_stride(P):
+    """One page in S is sampled (page j with j % S == S / 2): S is the
+    largest power of two up to 64 that leaves at least 32 sampled pages."""
+    s = 0
+    while s < 6 and (P >> (s + 1)) >= 32:
+        s += 1
+    return 1 << s
+
+
+def plant_on_sampled_pages(L, b, g, boost=3.0):
+    """Keys aligned with the group's queries on exactly the sampled pages of
+    (b, g): the sample then sees only high scores, its threshold leaves fewer
+    than k candidates, and the group takes the full rescan."""
+    G = L.H_q // L.H_kv
+    P = (L.seq_lens[b] + 63) // 64
+    S = sample_stride(P)
+    qdir = L.q[b, g * G:(g + 1) * G].float().sum(0)
     qdir = qdir / qdir.norm()
-    for j in range(2, 512, 4):
-        pg = int(L.block_table[0, j])
-        L.k_pool[pg, 0] = (L.k_pool[pg, 0].float() + 3.0 * qdir).to(torch.bfloat16)
+    for j in range(S // 2, P, S):
+        pg = int(L.block_table[b, j])
+        L.k_pool[pg, g] = (L.k_pool[pg, g].float() + boost * qdir).to(torch.bfloat16)
+
+
+def test_misleading_sample_takes_the_dense_path():
+    say("case sample_misled: N=32768, high keys on the sampled pages only, k=9000")
+    L = layer(4, 1, [32768], [9000], 16, 64)
+    plant_on_sampled_pages(L, 0, 0)
     run = gpu_decode(L, with_scores=True)
+    assert run.rescanned > 0
     compare_sequence(L, run, 0)
+
+
+def test_dense_path_in_some_groups_of_a_batch():
+    # two of four (sequence, KV head) groups are rescanned, by blocks that
+    # also scan units of the other groups; the rest keep their candidates
+    say("case sample_misled_batch: B=2 H_kv=2, groups (0,0) and (1,1) misled")
+    L = layer(8, 2, [32768, 24576 + 37], [9000, 6000], 16, 64, seed=3)
+    plant_on_sampled_pages(L, 0, 0)
+    plant_on_sampled_pages(L, 1, 1)
+    run = gpu_decode(L, with_scores=True)
+    assert run.rescanned > 0
+    compare_sequence(L, run, 0)
+    compare_sequence(L, run, 1)
 
 
 def test_integer_scores_with_many_ties():
@@ -175,6 +205,7 @@ def test_c2_llama_layer_128k_full_parity():
     say("case C2: H_q=32 H_kv=8 N=131072 k=2048")
     L = cfg_layer("C2")
     run = gpu_decode(L, with_scores=True)
+    assert run.rescanned == 0  # the sample's margin holds on this workload
     st = compare_sequence(L, run, 0)
     say(f"  band differences: {st['band_diffs']}")
     for pos, h in L.needles[0]:
@@ -186,6 +217,7 @@ def test_c4_ragged_batch_of_16():
     say("case C4: B=16 lengths in [32768, 131072], shuffled pages, k=2%")
     L = cfg_layer("C4")
     run = gpu_decode(L, max_seq_len=max(L.seq_lens))
+    assert run.rescanned == 0
     for b in range(L.B):
         compare_sequence(L, run, b)
     assert c.B == L.B

@@ -34,7 +34,9 @@ from ._lib import (  # noqa: F401
     decode_step,
     decode_workspace_bytes,
     kv_append,
+    rescan_count,
     scores_view,
     status_str,
+    workspace_rescan_count_offset,
     workspace_scores_offset,
 )

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libra.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m top_sparse_attention_gqa_amd.build`")
+        f"{LIB_PATH} is missing: build it with `python top_sparse_attention_gqa_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -39,7 +39,7 @@ PAGE_SIZE = 64
 
 EXPORTS = ["ra_abi_version", "ra_status_str", "ra_decode_workspace_bytes",
            "ra_kv_append", "ra_decode_step", "ra_decode_stages",
-           "ra_workspace_scores_offset"]
+           "ra_workspace_scores_offset", "ra_workspace_rescan_count_offset"]
 
 
 class KVLayerStruct(ctypes.Structure):
@@ -56,6 +56,8 @@ _lib.ra_decode_workspace_bytes.restype = c_size_t
 _lib.ra_decode_workspace_bytes.argtypes = [c_int32] * 5
 _lib.ra_workspace_scores_offset.restype = c_size_t
 _lib.ra_workspace_scores_offset.argtypes = [c_int32] * 5 + [POINTER(c_int64)]
+_lib.ra_workspace_rescan_count_offset.restype = c_size_t
+_lib.ra_workspace_rescan_count_offset.argtypes = [c_int32] * 5
 _lib.ra_kv_append.restype = c_int
 _lib.ra_kv_append.argtypes = [POINTER(KVLayerStruct), c_void_p, c_void_p, c_void_p, c_int32, c_void_p]
 _DECODE_ARGS = [c_void_p, c_int32, POINTER(KVLayerStruct), c_void_p, c_int32, c_int32,
@@ -92,6 +94,14 @@ def workspace_scores_offset(B, H_q, H_kv, max_seq_len, k_max):
     if off == ctypes.c_size_t(-1).value:
         raise ValueError("invalid capacities")
     return int(off), int(stride.value)
+
+
+def workspace_rescan_count_offset(B, H_q, H_kv, max_seq_len, k_max):
+    """Byte offset of the uint32 count of heads decided by the full rescan."""
+    off = _lib.ra_workspace_rescan_count_offset(B, H_q, H_kv, max_seq_len, k_max)
+    if off == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid capacities")
+    return int(off)
 
 
 def _ptr(t, dtype, name, nullable=False, align=4):
@@ -199,6 +209,13 @@ def scores_view(ws: torch.Tensor, B, H_q, H_kv, max_seq_len, k_max) -> torch.Ten
     off, stride = workspace_scores_offset(B, H_q, H_kv, max_seq_len, k_max)
     n = B * H_q * stride
     return ws[off:off + 4 * n].view(torch.float32).view(B, H_q, stride)
+
+
+def rescan_count(ws: torch.Tensor, B, H_q, H_kv, max_seq_len, k_max) -> int:
+    """Heads of the last call on this workspace whose candidates fell short
+    of k_eff and were decided by the full rescan (reads device memory)."""
+    off = workspace_rescan_count_offset(B, H_q, H_kv, max_seq_len, k_max)
+    return int(ws[off:off + 4].view(torch.int32).item())
 
 
 raw = _lib  # the C entry points, for tests that pass raw pointers

@@ -1,6 +1,8 @@
 """Build the HIP library libra.so in-tree for gfx950 with hipcc.
 
-    python -m top_sparse_attention_gqa_amd.build
+    python top_sparse_attention_gqa_amd/build.py
+
+Run as a script (not with -m): the package itself loads the library.
 
 Always recompiles. Objects go to ``_build/`` (git-ignored); the shared
 library lands next to this file, where the binding loads it.

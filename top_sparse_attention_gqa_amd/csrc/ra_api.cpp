@@ -37,7 +37,7 @@ bool ws_layout(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seq_len,
   L->off_scores = take(size_t(heads) * L->n_cap * sizeof(float));
   L->off_samp = take(size_t(heads) * L->samp_cap * sizeof(uint32_t));
   L->off_state = take(size_t(heads) * sizeof(HeadState));
-  L->off_gflag = take(size_t(B) * H_kv * sizeof(uint32_t));
+  L->off_gflag = take(size_t(B) * H_kv * 2 * sizeof(uint32_t));  // flags, then counts
   L->off_misc = take(64);
   L->off_unitoff = take(size_t(B + 1) * sizeof(int64_t));
   L->off_ucnt = take(size_t(heads) * L->n_units * sizeof(uint32_t));
@@ -144,6 +144,7 @@ static Params make_params(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
   p.samp = reinterpret_cast<uint32_t*>(base + L.off_samp);
   p.state = reinterpret_cast<HeadState*>(base + L.off_state);
   p.gflag = reinterpret_cast<uint32_t*>(base + L.off_gflag);
+  p.gdone = p.gflag + size_t(B) * kv->H_kv;
   p.any_dense = reinterpret_cast<uint32_t*>(base + L.off_misc);
   p.unit_off = reinterpret_cast<int64_t*>(base + L.off_unitoff);
   p.ucnt = reinterpret_cast<uint32_t*>(base + L.off_ucnt);
@@ -191,6 +192,13 @@ size_t ra_workspace_scores_offset(int32_t B, int32_t H_q, int32_t H_kv,
   if (!ws_layout(B, H_q, H_kv, max_seq_len, k_max, &L)) return size_t(-1);
   if (row_stride) *row_stride = L.n_cap;
   return L.off_scores;
+}
+
+size_t ra_workspace_rescan_count_offset(int32_t B, int32_t H_q, int32_t H_kv,
+                                        int32_t max_seq_len, int32_t k_max) {
+  WsLayout L;
+  if (!ws_layout(B, H_q, H_kv, max_seq_len, k_max, &L)) return size_t(-1);
+  return L.off_misc;  // any_dense
 }
 
 ra_status ra_kv_append(const ra_kv_layer* kv, const uint16_t* k_new,

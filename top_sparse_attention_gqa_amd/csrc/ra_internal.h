@@ -89,6 +89,7 @@ struct Params {
                        // (0: not a member of M)
   HeadState* state;    // [B*H_q]
   uint32_t* gflag;     // [B*H_kv] 1: some head of the group needs the rescan
+  uint32_t* gdone;     // [B*H_kv] units of the group rescanned so far
   uint32_t* any_dense; // heads flagged for the rescan in this call
   int64_t* unit_off;   // [B + 1] prefix of H_kv * units(b)
   uint32_t* ucnt;      // [B*H_q][n_units] candidates per (head, unit)
@@ -111,6 +112,9 @@ hipError_t launch_threshold(const Params& p, hipStream_t s);
 hipError_t launch_scan(const Params& p, hipStream_t s);
 hipError_t launch_select(const Params& p, hipStream_t s);
 hipError_t launch_dense(const Params& p, hipStream_t s);   // rescan + reselect
+// Grid of the persistent unit loops (scan, rescan): one block per CU, at
+// most one per unit.
+unsigned scan_blocks(const Params& p);
 hipError_t launch_gather(const Params& p, hipStream_t s);
 hipError_t launch_merge(const Params& p, hipStream_t s);
 hipError_t launch_kv_append(const ra_kv_layer& kv, const uint16_t* k_new,

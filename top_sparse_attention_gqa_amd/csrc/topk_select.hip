@@ -22,7 +22,7 @@
 // into registers when they fit. A head with too few candidates is flagged;
 // the dense stage rescans its group with every member of M as a candidate
 // and selects again.
-#include "ra_internal.h"
+#include "page_scores.h"
 
 namespace ra {
 
@@ -32,6 +32,8 @@ constexpr uint32_t kRankMax = 256; // sub-buckets up to this size are finished b
 constexpr int kBatch = 8;         // global entries per lane in flight per pass
 constexpr int kRegEntries = 64;   // candidate entries per lane kept in registers
 constexpr int kRegKeys = 32;      // sampled keys per lane kept in registers
+constexpr int kStartRows = 4096;  // rows of 64 list entries whose first unit is tabled
+static_assert(kRegEntries * kSelThreads / 64 <= kStartRows, "register rows must be tabled");
 
 // ---------------------------------------------------------------- wave helpers
 // Every lane of the wave must call these.
@@ -59,47 +61,68 @@ __device__ __forceinline__ void wave_append(uint64_t* list, uint32_t* n, uint32_
 
 // A head's per-unit candidate lists in global memory (entries key << 32 | n;
 // the list of unit u holds cnt(u) entries from list + u * kUnit), enumerated
-// as composites c = (key - lo) << 32 | ~n. The list lengths of the units that
-// overlap M are prefix-summed in LDS; entry i is found by a branch-free
-// binary search over that prefix whose kBatch lookups proceed in lockstep.
+// as composites c = (key - lo) << 32 | ~n. In LDS: the non-empty units in
+// order (ne) with the index of their first entry (pb), and for every row of
+// 64 entries the non-empty unit holding its first entry (rowk) and a mask
+// of the lanes where another one starts (rmask). The 64 lanes of a wave hold
+// one row, so a lane finds its unit with a popcount. Rows past the table
+// fall back to a binary search over pb.
 struct UnitLists {
   const uint64_t* list;
-  const uint32_t* pre;  // LDS [nu + 1]
-  int u_lo, nu;         // units u_lo .. u_lo + nu - 1 overlap M
+  const uint16_t* ne;     // LDS [n_ne]
+  const uint32_t* pb;     // LDS [n_ne + 1]
+  const uint16_t* rowk;   // LDS [rows]
+  const uint64_t* rmask;  // LDS [rows]
+  int u_lo, n_ne;         // units u_lo .. overlap M; n_ne of them non-empty
+  uint32_t rows;          // tabled rows
   uint32_t lo;
 
-  __device__ __forceinline__ void locate(const uint32_t (&idx)[kBatch], int (&a)[kBatch]) const {
-    const int top = nu > 1 ? 1 << (31 - __clz(nu - 1)) : 0;  // largest power of two < nu
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) a[u] = 0;
-    for (int step = top; step > 0; step >>= 1) {
-      uint32_t pv[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) pv[u] = pre[min(a[u] + step, nu - 1)];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) a[u] += (a[u] + step < nu && pv[u] <= idx[u]) ? step : 0;
-    }
+  __device__ __forceinline__ const uint64_t* at(int k, uint32_t i) const {
+    return list + size_t(u_lo + ne[k]) * kUnit + (i - pb[k]);
   }
 
-  // Entries [first, total) of the lists.
+  // Entry i of row q (q wave-uniform, < rows).
+  __device__ __forceinline__ const uint64_t* row_entry(uint32_t q, uint32_t i) const {
+    const uint64_t below = (2ull << (i & 63u)) - 1ull;  // lanes 0 .. i % 64
+    return at(int(rowk[q]) + __popcll(rmask[q] & below), i);
+  }
+
+  // Entry i anywhere: the last non-empty unit whose list begins at or
+  // before i.
+  __device__ __forceinline__ const uint64_t* search_entry(uint32_t i) const {
+    int k = 0;
+    for (int step = n_ne > 1 ? 1 << (31 - __clz(n_ne - 1)) : 0; step > 0; step >>= 1)
+      k += (k + step < n_ne && pb[k + step] <= i) ? step : 0;
+    return at(k, i);
+  }
+
+  // Entries [first, total) of the lists; first is a multiple of 64.
   template <typename Fn>
   __device__ __forceinline__ void for_each_from(uint32_t first, Fn&& fn) const {
     const uint32_t l = lo;
-    const uint32_t total = pre[nu];
+    const uint32_t total = pb[n_ne];
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     for (uint32_t base = first; base < total; base += blockDim.x * kBatch) {
-      uint32_t idx[kBatch];
-      int a[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) idx[u] = base + u * blockDim.x + threadIdx.x;
-      locate(idx, a);
       uint64_t v[kBatch];
+      if ((min(base + blockDim.x * kBatch, total) + 63u) / 64u <= rows) {  // uniform: all tabled
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        v[u] = idx[u] < total ? list[size_t(u_lo + a[u]) * kUnit + (idx[u] - pre[a[u]])] : 0ull;
+        for (int u = 0; u < kBatch; ++u) {
+          const uint32_t i = base + u * blockDim.x + threadIdx.x;
+          const uint64_t* e = row_entry(min((base + u * blockDim.x) / 64u + wave, rows - 1u), i);
+          v[u] = *(i < total ? e : list);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const uint32_t i = base + u * blockDim.x + threadIdx.x;
+          v[u] = i < total ? *search_entry(i) : 0ull;
+        }
+      }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
+        const uint32_t i = base + u * blockDim.x + threadIdx.x;
         const uint32_t n = uint32_t(v[u]);
-        fn((uint64_t(uint32_t(v[u] >> 32) - l) << 32) | uint32_t(~n), int(n), idx[u] < total);
+        fn((uint64_t(uint32_t(v[u] >> 32) - l) << 32) | uint32_t(~n), int(n), i < total);
       }
     }
   }
@@ -119,37 +142,27 @@ struct RegLists {
   uint32_t total;  // entries held in registers
   UnitLists rest;
 
-  // start: LDS scratch of NR * blockDim / 64 entries. Entry q gets the unit
-  // of list entry 64 q (one search per thread); the lanes of a wave, which
-  // hold 64 consecutive entries, then step forward from their first unit.
-  __device__ __forceinline__ void load(const UnitLists& src, uint16_t* start) {
+  // Straight-line groups of kBatch slots (no branch inside a group), so the
+  // LDS lookups of a group overlap; lanes past the end load the list's
+  // first entry, which is never used.
+  __device__ __forceinline__ void load(const UnitLists& src) {
+    static_assert(NR % kBatch == 0, "slots come in groups of kBatch");
     rest = src;
-    total = min(src.pre[src.nu], uint32_t(NR) * blockDim.x);
+    total = min(src.pb[src.n_ne], uint32_t(NR) * blockDim.x);
     const uint32_t l = src.lo;
-    const uint32_t nq = (total + 63u) / 64u;
-    for (uint32_t q = threadIdx.x; q < nq; q += blockDim.x) {
-      uint32_t idx[kBatch];
-      int a[kBatch];
-      idx[0] = q * 64u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t waves = blockDim.x >> 6;
+    const uint32_t qmax = src.rows > 0 ? src.rows - 1 : 0;
 #pragma unroll
-      for (int u = 1; u < kBatch; ++u) idx[u] = idx[0];
-      src.locate(idx, a);
-      start[q] = uint16_t(a[0]);
-    }
-    __syncthreads();
-    const int wave = threadIdx.x >> 6;
-    const int waves = blockDim.x >> 6;
+    for (int r0 = 0; r0 < NR; r0 += kBatch) {
+      if (uint32_t(r0) * blockDim.x >= total) break;  // uniform
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      if (uint32_t(r) * blockDim.x >= total) break;  // uniform
-      const uint32_t i = r * blockDim.x + threadIdx.x;
-      uint64_t v = 0ull;
-      if (i < total) {
-        int a = start[r * waves + wave];
-        while (a + 1 < src.nu && src.pre[a + 1] <= i) ++a;
-        v = src.list[size_t(src.u_lo + a) * kUnit + (i - src.pre[a])];
+      for (int r = r0; r < r0 + kBatch; ++r) {
+        const uint32_t i = r * blockDim.x + threadIdx.x;
+        // rows below total / 64 are tabled (the table covers NR * blockDim)
+        const uint64_t* e = src.row_entry(min(r * waves + wave, qmax), i);
+        c[r] = *(i < total ? e : src.list);
       }
-      c[r] = v;
     }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -394,7 +407,10 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(Params p) {
       *p.any_dense = 0u;
     }
   }
-  if (tid == 0 && hq % p.G == 0) p.gflag[size_t(b) * p.H_kv + hq / p.G] = 0u;
+  if (tid == 0 && hq % p.G == 0) {
+    p.gflag[size_t(b) * p.H_kv + hq / p.G] = 0u;
+    p.gdone[size_t(b) * p.H_kv + hq / p.G] = 0u;
+  }
 
   const SeqGeom sg = seq_geom(p, b);
   uint32_t lo = 0xFFFFFFFFu;  // k_eff == 0: no candidates
@@ -465,47 +481,64 @@ hipError_t launch_threshold(const Params& p, hipStream_t s) {
 
 // ---------------------------------------------------------------- select
 struct SelLds {
-  uint16_t start[kRegEntries * kSelThreads / 64];  // unit of every 64th entry
-  uint32_t pre[kMaxUnits + 1];  // prefix of the list lengths
+  uint16_t ne[kMaxUnits];         // non-empty units (relative to u_lo), ascending
+  uint32_t pb[kMaxUnits + 1];     // index of the first entry of each; the total
+  uint16_t rowk[kStartRows];      // non-empty unit holding entry 64 q (index into ne)
+  uint64_t rmask[kStartRows];     // bit l (l > 0): entry 64 q + l starts a unit
   uint32_t hist[2048];
   uint64_t sub[kSubCap];
   uint32_t s_d, s_above, s_cnt, s_n;
   int64_t tmp[16];
 };
 
-// Prefix of the list lengths of units u_lo .. u_lo + nu - 1 into L.pre;
-// returns the total. Block-wide.
-__device__ uint32_t unit_prefix(const Params& p, int bh, const SeqGeom& sg, int u_lo, int nu,
-                                bool dense, SelLds& L) {
+// List lengths of units u_lo .. u_lo + nu - 1 (their overlaps with M when
+// dense), laid out as the non-empty units and their entry ranges, with the
+// row table. Returns the list view. Block-wide.
+__device__ __forceinline__ UnitLists unit_prefix(const Params& p, int bh, const SeqGeom& sg, int u_lo, int nu,
+                                 bool dense, uint32_t lo, SelLds& L) {
   constexpr int per = kMaxUnits / kSelThreads;
   const int tid = threadIdx.x;
   const uint32_t* uc = p.ucnt + size_t(bh) * p.n_units;
+  for (int q = tid; q < kStartRows; q += kSelThreads) L.rmask[q] = 0ull;
   uint32_t c[per];
-  int64_t sum = 0;
+  int64_t v = 0;  // entries << 13 | non-empty units (at most kMaxUnits < 2^13)
 #pragma unroll
   for (int u = 0; u < per; ++u) {
     const int i = tid * per + u;
     c[u] = 0u;
     if (i < nu) {
       if (dense) {
-        const int v = u_lo + i;
-        c[u] = uint32_t(min((v + 1) * kUnit, sg.hi) - max(v * kUnit, sg.lo));
+        const int x = u_lo + i;
+        c[u] = uint32_t(min((x + 1) * kUnit, sg.hi) - max(x * kUnit, sg.lo));
       } else {
         c[u] = uc[u_lo + i];
       }
     }
-    sum += c[u];
+    v += (int64_t(c[u]) << 13) + (c[u] > 0u ? 1 : 0);
   }
-  int64_t total;
-  int64_t run = block_excl_scan(sum, L.tmp, &total);
+  int64_t tot;
+  const int64_t run = block_excl_scan(v, L.tmp, &tot);
+  const uint32_t total = uint32_t(tot >> 13);
+  const int n_ne = int(tot & 8191);
+  const uint32_t rows = min(uint32_t(kStartRows), (total + 63u) / 64u);
+  uint32_t e = uint32_t(run >> 13);
+  int k = int(run & 8191);
 #pragma unroll
   for (int u = 0; u < per; ++u) {
-    L.pre[tid * per + u] = uint32_t(run);
-    run += c[u];
+    if (c[u] > 0u) {
+      L.ne[k] = uint16_t(tid * per + u);
+      L.pb[k] = e;
+      const uint32_t q1 = min((e + c[u] + 63u) / 64u, rows);
+      for (uint32_t q = (e + 63u) / 64u; q < q1; ++q) L.rowk[q] = uint16_t(k);
+      if ((e & 63u) != 0u && e / 64u < rows)
+        atomicOr(reinterpret_cast<unsigned long long*>(&L.rmask[e / 64u]), 1ull << (e & 63u));
+      ++k;
+      e += c[u];
+    }
   }
-  if (tid == 0) L.pre[kMaxUnits] = uint32_t(total);
+  if (tid == 0) L.pb[n_ne] = total;
   __syncthreads();
-  return uint32_t(total);
+  return UnitLists{p.cand + size_t(bh) * p.n_cap, L.ne, L.pb, L.rowk, L.rmask, u_lo, n_ne, rows, lo};
 }
 
 // Exact threshold of head bh over its candidates (source src), written
@@ -526,16 +559,14 @@ __device__ __forceinline__ void decide(const Params& p, int bh, const SeqGeom& s
   }
 }
 
-// Select over the lists of head bh (whose prefix is in L.pre), from
-// registers when they fit.
-__device__ __forceinline__ void select_head(const Params& p, int bh, const SeqGeom& sg, int u_lo, int nu,
-                            uint32_t lo, uint32_t max_m, SelLds& L) {
-  const uint32_t span = max_m > lo ? max_m - lo : 1u;
+// Select over the lists of head bh, from registers when they fit.
+__device__ __forceinline__ void select_head(const Params& p, int bh, const SeqGeom& sg,
+                                            const UnitLists& gl, uint32_t max_m, SelLds& L) {
+  const uint32_t span = max_m > gl.lo ? max_m - gl.lo : 1u;
   const int TB = 32 + bit_length(span);
-  const UnitLists gl{p.cand + size_t(bh) * p.n_cap, L.pre, u_lo, nu, lo};
   RegLists<kRegEntries> rl;
-  rl.load(gl, L.start);
-  decide(p, bh, sg, rl, TB, lo, L);
+  rl.load(gl);
+  decide(p, bh, sg, rl, TB, gl.lo, L);
 }
 
 // One block per head: count the candidates; decide the threshold, or flag
@@ -547,10 +578,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
   const SeqGeom sg = seq_geom(p, b);
   if (sg.k_eff == 0) return;  // the unset threshold takes nothing
   __shared__ SelLds L;
-  const int u_lo = sg.lo / kUnit, nu = (sg.hi - 1) / kUnit + 1 - u_lo;
-  const uint32_t m = unit_prefix(p, bh, sg, u_lo, nu, false, L);
   const HeadState st = p.state[bh];
-  if (m < uint32_t(sg.k_eff)) {
+  const int u_lo = sg.lo / kUnit, nu = (sg.hi - 1) / kUnit + 1 - u_lo;
+  const UnitLists gl = unit_prefix(p, bh, sg, u_lo, nu, false, st.lo_key, L);
+  if (gl.pb[gl.n_ne] < uint32_t(sg.k_eff)) {
     if (threadIdx.x == 0) {
       p.state[bh].dense = 1u;
       atomicOr(&p.gflag[size_t(b) * p.H_kv + g], 1u);
@@ -558,7 +589,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
     }
     return;
   }
-  select_head(p, bh, sg, u_lo, nu, st.lo_key, st.max_m, L);
+  select_head(p, bh, sg, gl, st.max_m, L);
 }
 
 hipError_t launch_select(const Params& p, hipStream_t s) {
@@ -567,28 +598,92 @@ hipError_t launch_select(const Params& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- dense
-// After the rescan: the flagged heads select over every member of M (their
-// lists now hold all of it, so the list lengths are the units' overlaps).
-__global__ __launch_bounds__(kSelThreads) void reselect_kernel(Params p) {
-  if (*p.any_dense == 0u) return;
-  const int bh = blockIdx.x;
+// Without flagged heads every block returns at once. Otherwise the blocks
+// rescan the units of the flagged groups: every member of M of a flagged
+// head becomes a candidate, written at its place in its unit's list (the
+// list of unit u holds positions max(u * kUnit, lo) .. in order). Finished
+// units are counted per group, and the block that finishes a group's last
+// unit selects again, over every member of M, for the group's flagged heads
+// (their lists now hold all of M, so the list lengths are the units'
+// overlaps with it).
+static_assert(kScanThreads == kSelThreads, "the rescan blocks also select");
+
+__device__ __forceinline__ void reselect_head(const Params& p, int bh, SelLds& L) {
   const HeadState st = p.state[bh];
-  if (!st.dense) return;
   const SeqGeom sg = seq_geom(p, bh / p.H_q);
-  __shared__ SelLds L;
   const int u_lo = sg.lo / kUnit, nu = (sg.hi - 1) / kUnit + 1 - u_lo;
-  unit_prefix(p, bh, sg, u_lo, nu, true, L);
+  const UnitLists gl = unit_prefix(p, bh, sg, u_lo, nu, true, 0u, L);
   uint32_t* uc = p.ucnt + size_t(bh) * p.n_units;
-  for (int i = threadIdx.x; i < nu; i += kSelThreads) uc[u_lo + i] = L.pre[i + 1] - L.pre[i];
-  select_head(p, bh, sg, u_lo, nu, 0u, st.max_m, L);
+  for (int i = threadIdx.x; i < nu; i += kSelThreads) {
+    const int x = u_lo + i;
+    uc[x] = uint32_t(min((x + 1) * kUnit, sg.hi) - max(x * kUnit, sg.lo));
+  }
+  // all of M: far more than registers hold, so streamed on every pass
+  const uint32_t span = st.max_m > 0u ? st.max_m : 1u;
+  decide(p, bh, sg, gl, 32 + bit_length(span), 0u, L);
 }
 
-hipError_t launch_dense_scan(const Params& p, hipStream_t s);  // score_scan.hip
+template <int G>
+__global__ __launch_bounds__(kScanThreads) void dense_kernel(Params p) {
+  if (*p.any_dense == 0u) return;
+  __shared__ SelLds S;
+  __shared__ uint32_t s_last;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const Lane<G> L;
+  const int64_t T = p.unit_off[p.B];
+  const int64_t X0 = T * blockIdx.x / gridDim.x;
+  const int64_t X1 = T * (blockIdx.x + 1) / gridDim.x;
+  for (int64_t x = X0; x < X1; ++x) {
+    const UnitRef ur = unit_at(p, x);
+    const int b = ur.b, g = ur.g;
+    const size_t bg = size_t(b) * p.H_kv + g;
+    if (!p.gflag[bg]) continue;  // block-uniform
+    const SeqGeom sg = seq_geom(p, b);
+    const size_t bh = size_t(b) * p.H_q + size_t(g) * G + L.F;
+    const bool mine = p.state[bh].dense != 0u;
+    uint4 qreg[G];
+    load_q<G>(p, b, g, L, qreg);
+    const int u0 = ur.u * kUnit;
+    uint64_t* crow = p.cand + bh * p.n_cap + size_t(u0);
+    const int first = max(u0, sg.lo);
+    for (int jj = wave; jj < ur.npages; jj += kScanWaves) {
+      const int j = ur.u * kUnitPages + jj;
+      float z[G];
+      page_scores<G>(p, page_of(p, b, j), g, L, qreg, z);
+#pragma unroll
+      for (int s = 0; s < G; ++s) {
+        const int n = j * kPage + L.tok(s);
+        if (mine && n >= sg.lo && n < sg.hi)
+          crow[n - first] = (uint64_t(f2key(z[s])) << 32) | uint32_t(n);
+      }
+    }
+    // this unit's lists are complete: make them visible, then count it
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int units = ((sg.N + kPage - 1) / kPage + kUnitPages - 1) / kUnitPages;
+      s_last = atomicAdd(&p.gdone[bg], 1u) == uint32_t(units - 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (s_last) {
+      __threadfence();  // see the lists the other blocks wrote
+      for (int hh = 0; hh < G; ++hh) {
+        const int bhh = b * p.H_q + g * G + hh;
+        if (p.state[bhh].dense) reselect_head(p, bhh, S);
+      }
+    }
+  }
+}
 
 hipError_t launch_dense(const Params& p, hipStream_t s) {
-  hipError_t e = launch_dense_scan(p, s);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(reselect_kernel, dim3(unsigned(p.B * p.H_q)), dim3(kSelThreads), 0, s, p);
+  const dim3 grid{scan_blocks(p)}, block{unsigned(kScanThreads)};
+  switch (p.G) {
+    case 1: hipLaunchKernelGGL(dense_kernel<1>, grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL(dense_kernel<2>, grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL(dense_kernel<4>, grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL(dense_kernel<8>, grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
