@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 1
+#define RA_ABI_VERSION 2
 #define RA_HEAD_DIM 128
 #define RA_PAGE_SIZE 64
 #define RA_MAX_SEQ_LEN (1 << 24) /* 16,777,216 positions per sequence */
@@ -109,6 +109,11 @@ ra_status ra_kv_append(const ra_kv_layer* kv, const uint16_t* k_new,
                        const uint16_t* v_new, const int32_t* pos, int32_t B,
                        hipStream_t stream);
 
+/* Flags of ra_decode_step and ra_decode_stages (other bits are rejected). */
+#define RA_DECODE_KEEP_SCORES 1u /* also leave the scores of the retrieved set
+                                    in the workspace score rows (a check of
+                                    the scores; it costs scattered writes) */
+
 /*
  * One decode step (see the top of this file for what it computes).
  *  q:           device bf16 [B][H_q][128], the new token's queries,
@@ -127,6 +132,7 @@ ra_status ra_kv_append(const ra_kv_layer* kv, const uint16_t* k_new,
  *               H_q, kv->H_kv, max_seq_len, k_max) bytes, 256-byte aligned;
  *               no initial contents are required. Calls that share a
  *               workspace must be ordered on one stream.
+ *  flags:       0 or RA_DECODE_KEEP_SCORES.
  * An empty W u Omega gives out = 0. Launch count and grid sizes depend only on
  * the host arguments, so the call can be captured into a HIP graph.
  */
@@ -135,7 +141,7 @@ ra_status ra_decode_step(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
                          int32_t max_seq_len, const int32_t* k, int32_t k_max,
                          int32_t n_sink, int32_t window, float* out,
                          float* out_lse, int32_t* out_idx, void* ws,
-                         size_t ws_bytes, hipStream_t stream);
+                         size_t ws_bytes, uint32_t flags, hipStream_t stream);
 
 /*
  * The kernels of one decode step, in launch order. ra_decode_step runs
@@ -165,15 +171,17 @@ ra_status ra_decode_stages(const uint16_t* q, int32_t H_q,
                            int32_t B, int32_t max_seq_len, const int32_t* k,
                            int32_t k_max, int32_t n_sink, int32_t window,
                            float* out, float* out_lse, int32_t* out_idx,
-                           void* ws, size_t ws_bytes, int32_t first_stage,
-                           int32_t last_stage, hipStream_t stream);
+                           void* ws, size_t ws_bytes, uint32_t flags,
+                           int32_t first_stage, int32_t last_stage,
+                           hipStream_t stream);
 
 /*
  * Where the fp32 score rows live inside a workspace sized for these
  * capacities: z for (b, h, n) is the float at byte offset
  * returned + 4 * ((b * H_q + h) * (*row_stride) + n). After RA_STAGE_GATHER
- * it holds the scores of the positions of W and of the retrieved set; other
- * entries are unspecified. Returns (size_t)-1 if the arguments are invalid.
+ * it holds the scores of the positions of W, and of the retrieved set if the
+ * call passed RA_DECODE_KEEP_SCORES; other entries are unspecified. Returns
+ * (size_t)-1 if the arguments are invalid.
  */
 size_t ra_workspace_scores_offset(int32_t B, int32_t H_q, int32_t H_kv,
                                   int32_t max_seq_len, int32_t k_max,

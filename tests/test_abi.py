@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert ra.abi_version() == 1
+    assert ra.abi_version() == 2
     assert ra.status_str(ra.RA_OK) == "RA_OK"
     assert ra.status_str(ra.RA_ERR_WORKSPACE) == "RA_ERR_WORKSPACE"
     assert ra.status_str(99) == "RA_ERR_UNKNOWN"
@@ -71,13 +71,13 @@ def _kv(**kw):
 def _decode(kv=None, **kw):
     a = dict(q=FAKE, H_q=4, seq_lens=FAKE, B=1, max_seq_len=640, k=FAKE, k_max=8,
              n_sink=4, window=8, out=FAKE, lse=None, out_idx=FAKE, ws=FAKE,
-             ws_bytes=1 << 40)
+             ws_bytes=1 << 40, flags=0)
     a.update(kw)
     kv = kv if kv is not None else _kv()
     return _lib.raw.ra_decode_step(a["q"], a["H_q"], ctypes.byref(kv), a["seq_lens"], a["B"],
                                    a["max_seq_len"], a["k"], a["k_max"], a["n_sink"],
                                    a["window"], a["out"], a["lse"], a["out_idx"], a["ws"],
-                                   a["ws_bytes"], None)
+                                   a["ws_bytes"], a["flags"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -100,6 +100,8 @@ def _decode(kv=None, **kw):
     (dict(out_idx=FAKE + 1), ra.RA_ERR_INVALID_ARGUMENT),
     (dict(ws_bytes=1024), ra.RA_ERR_WORKSPACE),
     (dict(H_q=16), ra.RA_ERR_UNSUPPORTED),   # G = 16
+    (dict(flags=2), ra.RA_ERR_INVALID_ARGUMENT),  # an unknown flag
+    (dict(flags=1, ws_bytes=1024), ra.RA_ERR_WORKSPACE),  # KEEP_SCORES is known
 ])
 def test_decode_validation(kw, status):
     kw = dict(kw)
@@ -117,7 +119,7 @@ def test_decode_validation_of_the_kv_descriptor():
     assert _decode(kv=_kv(block_table=FAKE + 2)) == ra.RA_ERR_INVALID_ARGUMENT
     assert _decode(kv=_kv(H_kv=3)) == ra.RA_ERR_INVALID_ARGUMENT  # 4 % 3
     assert _lib.raw.ra_decode_step(FAKE, 4, None, FAKE, 1, 640, FAKE, 8, 4, 8, FAKE, None,
-                                   FAKE, FAKE, 1 << 40, None) == ra.RA_ERR_INVALID_ARGUMENT
+                                   FAKE, FAKE, 1 << 40, 0, None) == ra.RA_ERR_INVALID_ARGUMENT
 
 
 def test_k_max_zero_allows_null_out_idx_until_a_later_check():
@@ -128,7 +130,7 @@ def test_k_max_zero_allows_null_out_idx_until_a_later_check():
 
 def test_stage_range_validation():
     kv = _kv()
-    args = [FAKE, 4, ctypes.byref(kv), FAKE, 1, 640, FAKE, 8, 4, 8, FAKE, None, FAKE, FAKE, 1 << 40]
+    args = [FAKE, 4, ctypes.byref(kv), FAKE, 1, 640, FAKE, 8, 4, 8, FAKE, None, FAKE, FAKE, 1 << 40, 0]
     assert _lib.raw.ra_decode_stages(*args, 3, 2, None) == ra.RA_ERR_INVALID_ARGUMENT
     assert _lib.raw.ra_decode_stages(*args, -1, 2, None) == ra.RA_ERR_INVALID_ARGUMENT
     assert _lib.raw.ra_decode_stages(*args, 0, 7, None) == ra.RA_ERR_INVALID_ARGUMENT

@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, c_int, c_int32, c_int64, c_size_t, c_void_p, c_char_p
+from ctypes import POINTER, c_int, c_int32, c_int64, c_size_t, c_uint32, c_void_p, c_char_p
 
 import torch
 
@@ -36,6 +36,7 @@ STAGE_NAMES = ["sample", "threshold", "scan", "select", "dense", "gather", "merg
 
 HEAD_DIM = 128
 PAGE_SIZE = 64
+DECODE_KEEP_SCORES = 1
 
 EXPORTS = ["ra_abi_version", "ra_status_str", "ra_decode_workspace_bytes",
            "ra_kv_append", "ra_decode_step", "ra_decode_stages",
@@ -64,9 +65,9 @@ _DECODE_ARGS = [c_void_p, c_int32, POINTER(KVLayerStruct), c_void_p, c_int32, c_
                 c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                 c_void_p, c_size_t]
 _lib.ra_decode_step.restype = c_int
-_lib.ra_decode_step.argtypes = _DECODE_ARGS + [c_void_p]
+_lib.ra_decode_step.argtypes = _DECODE_ARGS + [c_uint32, c_void_p]
 _lib.ra_decode_stages.restype = c_int
-_lib.ra_decode_stages.argtypes = _DECODE_ARGS + [c_int32, c_int32, c_void_p]
+_lib.ra_decode_stages.argtypes = _DECODE_ARGS + [c_uint32, c_int32, c_int32, c_void_p]
 
 
 class RAError(RuntimeError):
@@ -173,8 +174,9 @@ def kv_append(kv: KVLayer, k_new, v_new, pos, stream=None) -> None:
 
 def decode_stages(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, window,
                   out, out_lse, out_idx, ws, first=STAGE_SAMPLE, last=STAGE_MERGE,
-                  stream=None) -> None:
-    """ra_decode_stages (ra_decode_step when first..last covers every stage)."""
+                  stream=None, keep_scores=False) -> None:
+    """ra_decode_stages (ra_decode_step when first..last covers every stage).
+    keep_scores: also leave the retrieved set's scores in the score rows."""
     B, H_q = q.shape[0], q.shape[1]
     st = _lib.ra_decode_stages(
         _ptr(q, torch.bfloat16, "q", align=16), H_q, ctypes.byref(kv.struct),
@@ -183,14 +185,15 @@ def decode_stages(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, windo
         _ptr(out_lse, torch.float32, "out_lse", nullable=True),
         _ptr(out_idx, torch.int32, "out_idx", nullable=(k_max == 0)),
         _ptr(ws, torch.uint8, "ws", align=256), ws.numel() if not isinstance(ws, int) else 0,
-        first, last, _stream(stream))
+        DECODE_KEEP_SCORES if keep_scores else 0, first, last, _stream(stream))
     if st != RA_OK:
         raise RAError(st, "ra_decode_stages")
 
 
 def decode_step(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, window,
-                out, out_lse, out_idx, ws, stream=None) -> None:
-    """ra_decode_step: one exact top-k sparse GQA decode step."""
+                out, out_lse, out_idx, ws, stream=None, keep_scores=False) -> None:
+    """ra_decode_step: one exact top-k sparse GQA decode step.
+    keep_scores: also leave the retrieved set's scores in the score rows."""
     B, H_q = q.shape[0], q.shape[1]
     st = _lib.ra_decode_step(
         _ptr(q, torch.bfloat16, "q", align=16), H_q, ctypes.byref(kv.struct),
@@ -198,7 +201,8 @@ def decode_step(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, window,
         k_max, n_sink, window, _ptr(out, torch.float32, "out"),
         _ptr(out_lse, torch.float32, "out_lse", nullable=True),
         _ptr(out_idx, torch.int32, "out_idx", nullable=(k_max == 0)),
-        _ptr(ws, torch.uint8, "ws", align=256), ws.numel(), _stream(stream))
+        _ptr(ws, torch.uint8, "ws", align=256), ws.numel(),
+        DECODE_KEEP_SCORES if keep_scores else 0, _stream(stream))
     if st != RA_OK:
         raise RAError(st, "ra_decode_step")
 

@@ -15,14 +15,17 @@
 // gather, one block per (sequence, KV head, tile): the block takes each
 // head's retrieved members of its tile (the entries of the tile's
 // (head, unit) candidate lists at or above the head's exact threshold),
-// marks them in an LDS bitmap, stores their scores, and writes their
+// marks them in an LDS bitmap, stages their scores in LDS, and writes their
 // positions, ascending, with their count, over the tile's consumed lists.
+// (Scattered 4-byte score stores into the score rows cost several times
+// their bytes, so they happen only when the caller keeps the scores, or
+// when the tile's lists overflow the staging and the scores are read back.)
 // Its rows are the union over the group's G query heads of those positions,
 // in ascending order, then its slice of W (attended by every head; the scan
 // left those scores). Each V row (256 contiguous bytes) is read once per
 // group: the weights e^{z - m} of every (row, head) are put in LDS (the
-// retrieved scores are staged in LDS by the filter, the W scores loaded up
-// front), then a V phase accumulates Z and N for every member head.
+// retrieved scores from the staging, the W scores loaded up front), then a
+// V phase accumulates Z and N for every member head.
 //
 // merge: per query head, one block combines the partials,
 // out = sum_t e^{m_t - m} N_t / sum_t e^{m_t - m} Z_t, lse = m + ln(...),
@@ -196,10 +199,17 @@ void gather_kernel(Params p) {
   }
   __syncthreads();
   if (tid < G) s_mref[tid] = softmax_ref(s_st[tid], sg.k_eff);
+  // when the tile's lists fit the LDS staging, the retrieved scores stay in
+  // LDS; otherwise they go to the score rows and are read back
+  uint32_t listed = 0;
+#pragma unroll
+  for (int j = 0; j < 2 * G; ++j) listed += s_lc[j];
+  const bool staged = listed <= uint32_t(kSel);
+  const bool store = p.keep_scores || !staged;
 
   // Each head's retrieved members of this tile: the list entries whose
   // composite (key - lo) << 32 | ~n clears the head's threshold. They are
-  // marked in the bitmap, their scores stored, and staged in LDS.
+  // marked in the bitmap and their scores staged in LDS (or stored).
   auto take = [&](int hh, uint64_t v) {
     const uint32_t key = uint32_t(v >> 32);
     const uint32_t n = uint32_t(v);
@@ -209,9 +219,9 @@ void gather_kernel(Params p) {
     const int off = int(n) - t0;
     atomicOr(reinterpret_cast<unsigned long long*>(&bm[hh][off >> 6]), 1ull << (off & 63));
     const float z = key2f(key);
-    p.scores[(bh0 + hh) * p.n_cap + n] = z;
-    const uint32_t at = atomicAdd(&s_nsel, 1u);
-    if (at < uint32_t(kSel)) {
+    if (store) p.scores[(bh0 + hh) * p.n_cap + n] = z;
+    if (staged) {
+      const uint32_t at = atomicAdd(&s_nsel, 1u);
       s_sel[at] = uint32_t(off) | (uint32_t(hh) << 13);
       s_selz[at] = z;
     }
@@ -294,7 +304,6 @@ void gather_kernel(Params p) {
   if (tid < G)
     p.scnt[(bh0 + tid) * p.n_tiles + tile] =
         uint32_t((ptot.v[tid >> 2] >> (16 * (tid & 3))) & 0xFFFF);
-  const bool staged = s_nsel <= uint32_t(kSel);
 
   float acc[G][8], zs[G];
 #pragma unroll

@@ -220,19 +220,22 @@ ra_status ra_decode_stages(const uint16_t* q, int32_t H_q,
                            int32_t B, int32_t max_seq_len, const int32_t* k,
                            int32_t k_max, int32_t n_sink, int32_t window,
                            float* out, float* out_lse, int32_t* out_idx,
-                           void* ws, size_t ws_bytes, int32_t first_stage,
-                           int32_t last_stage, hipStream_t stream) {
+                           void* ws, size_t ws_bytes, uint32_t flags,
+                           int32_t first_stage, int32_t last_stage,
+                           hipStream_t stream) {
   WsLayout L;
   ra_status st = validate_decode(q, H_q, kv, seq_lens, B, max_seq_len, k,
                                  k_max, n_sink, window, out, out_idx, ws,
                                  ws_bytes, &L);
   if (st != RA_OK) return st;
+  if (flags & ~RA_DECODE_KEEP_SCORES) return RA_ERR_INVALID_ARGUMENT;
   if (first_stage < 0 || last_stage >= RA_STAGE_COUNT ||
       first_stage > last_stage)
     return RA_ERR_INVALID_ARGUMENT;
   Params p = make_params(q, H_q, kv, seq_lens, B, max_seq_len, k, k_max,
                          n_sink, window, out, out_lse, out_idx, ws, L);
   p.num_cus = cu_count();
+  p.keep_scores = (flags & RA_DECODE_KEEP_SCORES) ? 1 : 0;
   using Launcher = hipError_t (*)(const Params&, hipStream_t);
   static const Launcher stages[RA_STAGE_COUNT] = {
       launch_sample, launch_threshold, launch_scan,  launch_select,
@@ -248,10 +251,10 @@ ra_status ra_decode_step(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
                          int32_t max_seq_len, const int32_t* k, int32_t k_max,
                          int32_t n_sink, int32_t window, float* out,
                          float* out_lse, int32_t* out_idx, void* ws,
-                         size_t ws_bytes, hipStream_t stream) {
+                         size_t ws_bytes, uint32_t flags, hipStream_t stream) {
   return ra_decode_stages(q, H_q, kv, seq_lens, B, max_seq_len, k, k_max,
                           n_sink, window, out, out_lse, out_idx, ws, ws_bytes,
-                          RA_STAGE_SAMPLE, RA_STAGE_MERGE, stream);
+                          flags, RA_STAGE_SAMPLE, RA_STAGE_MERGE, stream);
 }
 
 }  // extern "C"

@@ -83,8 +83,10 @@ struct Params {
   int32_t B, H_q, H_kv, G, max_pages, num_pages, max_seq_len, k_max, n_sink,
       window;
   // workspace
-  float* scores;       // [B*H_q][n_cap]: W scores (scan) and the retrieved
+  float* scores;       // [B*H_q][n_cap]: W scores (scan); the retrieved
                        // positions' scores of a tile (its gather block)
+                       // when kept, or when the tile's lists overflow
+                       // the gather's LDS staging
   uint32_t* samp;      // [B*H_q][samp_cap] keys of the sampled positions
                        // (0: not a member of M)
   HeadState* state;    // [B*H_q]
@@ -104,6 +106,7 @@ struct Params {
   int32_t n_units;
   int32_t samp_cap;
   int32_t num_cus;
+  int32_t keep_scores;  // also store the retrieved set's scores in the rows
 };
 
 // Launchers (each enqueues its kernels on `s`; they never synchronise).
