@@ -8,11 +8,12 @@ inputs (OOD queries vs keys, 64 planted needles per query head, x4 sink
 keys). Inputs are resident in HBM before timing starts.
 
 One step = every kernel of ra_decode_step (sample, threshold, scan, select,
-dense, gather, merge). In the timed region each step is launched as three
-ra_decode_stages calls with HIP events around the scan stage only, so the
-scan kernel's own duration is measured live on the stream it runs on; a
-separate, untimed pass with events between all stages gives the per-stage
-breakdown. Prints ONE JSON line.
+gather, merge). In the timed region every SCAN_EVERY-th step is launched as
+three ra_decode_stages calls with HIP events around the scan stage only, so
+the scan kernel's own duration is measured live on the stream it runs on;
+the other steps are single ra_decode_step calls. A separate, untimed pass
+with events between all stages gives the per-stage breakdown. Prints ONE
+JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload C3_1] [--gpus 1]
 """

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 2
+#define RA_ABI_VERSION 3
 #define RA_HEAD_DIM 128
 #define RA_PAGE_SIZE 64
 #define RA_MAX_SEQ_LEN (1 << 24) /* 16,777,216 positions per sequence */
@@ -156,14 +156,14 @@ typedef enum ra_stage {
                              reset of the per-call state */
   RA_STAGE_SCAN = 2,   /* all scores; keep W and the candidates above it */
   RA_STAGE_SELECT = 3, /* exact top-k threshold over the candidates, ties to
-                          the lower position; flags heads with too few */
-  RA_STAGE_DENSE = 4,  /* flagged heads only (no work otherwise): rescan with
-                          every member of M as a candidate, select again */
-  RA_STAGE_GATHER = 5, /* take the retrieved members per tile, split-K
+                          the lower position; heads with fewer candidates
+                          than k are rescanned with every member of M as a
+                          candidate and selected again (no work otherwise) */
+  RA_STAGE_GATHER = 4, /* take the retrieved members per tile, split-K
                           softmax-V partials */
-  RA_STAGE_MERGE = 6,  /* log-sum-exp merge into out / out_lse; out_idx with
+  RA_STAGE_MERGE = 5,  /* log-sum-exp merge into out / out_lse; out_idx with
                           -1 padding */
-  RA_STAGE_COUNT = 7
+  RA_STAGE_COUNT = 6
 } ra_stage;
 
 ra_status ra_decode_stages(const uint16_t* q, int32_t H_q,
@@ -191,8 +191,7 @@ size_t ra_workspace_scores_offset(int32_t B, int32_t H_q, int32_t H_kv,
  * Where a uint32 counter lives inside a workspace sized for these
  * capacities (byte offset, 4-byte aligned): after RA_STAGE_SELECT of a call
  * it holds the number of query heads whose candidates fell short of k_eff,
- * which RA_STAGE_DENSE then decides by the full rescan (0 in the common
- * case). A diagnostic; the caller reads it from device memory itself.
+ * which that stage then decided by the full rescan (0 in the common case). A diagnostic; the caller reads it from device memory itself.
  * Returns (size_t)-1 if the arguments are invalid.
  */
 size_t ra_workspace_rescan_count_offset(int32_t B, int32_t H_q, int32_t H_kv,

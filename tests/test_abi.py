@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert ra.abi_version() == 2
+    assert ra.abi_version() == 3
     assert ra.status_str(ra.RA_OK) == "RA_OK"
     assert ra.status_str(ra.RA_ERR_WORKSPACE) == "RA_ERR_WORKSPACE"
     assert ra.status_str(99) == "RA_ERR_UNKNOWN"
@@ -133,7 +133,7 @@ def test_stage_range_validation():
     args = [FAKE, 4, ctypes.byref(kv), FAKE, 1, 640, FAKE, 8, 4, 8, FAKE, None, FAKE, FAKE, 1 << 40, 0]
     assert _lib.raw.ra_decode_stages(*args, 3, 2, None) == ra.RA_ERR_INVALID_ARGUMENT
     assert _lib.raw.ra_decode_stages(*args, -1, 2, None) == ra.RA_ERR_INVALID_ARGUMENT
-    assert _lib.raw.ra_decode_stages(*args, 0, 7, None) == ra.RA_ERR_INVALID_ARGUMENT
+    assert _lib.raw.ra_decode_stages(*args, 0, 6, None) == ra.RA_ERR_INVALID_ARGUMENT
 
 
 def test_kv_append_validation():

@@ -17,7 +17,6 @@ from ._lib import (  # noqa: F401
     RA_ERR_WORKSPACE,
     RA_OK,
     STAGE_COUNT,
-    STAGE_DENSE,
     STAGE_GATHER,
     STAGE_MERGE,
     STAGE_NAMES,

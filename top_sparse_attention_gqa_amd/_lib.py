@@ -29,10 +29,10 @@ RA_ERR_WORKSPACE = 2
 RA_ERR_UNSUPPORTED = 3
 RA_ERR_HIP = 4
 
-(STAGE_SAMPLE, STAGE_THRESHOLD, STAGE_SCAN, STAGE_SELECT, STAGE_DENSE, STAGE_GATHER,
- STAGE_MERGE) = range(7)
-STAGE_COUNT = 7
-STAGE_NAMES = ["sample", "threshold", "scan", "select", "dense", "gather", "merge"]
+(STAGE_SAMPLE, STAGE_THRESHOLD, STAGE_SCAN, STAGE_SELECT, STAGE_GATHER,
+ STAGE_MERGE) = range(6)
+STAGE_COUNT = 6
+STAGE_NAMES = ["sample", "threshold", "scan", "select", "gather", "merge"]
 
 HEAD_DIM = 128
 PAGE_SIZE = 64

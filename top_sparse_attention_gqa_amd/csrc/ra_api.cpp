@@ -37,7 +37,7 @@ bool ws_layout(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seq_len,
   L->off_scores = take(size_t(heads) * L->n_cap * sizeof(float));
   L->off_samp = take(size_t(heads) * L->samp_cap * sizeof(uint32_t));
   L->off_state = take(size_t(heads) * sizeof(HeadState));
-  L->off_gflag = take(size_t(B) * H_kv * 2 * sizeof(uint32_t));  // flags, then counts
+  L->off_gdone = take(size_t(B) * H_kv * sizeof(uint32_t));
   L->off_misc = take(64);
   L->off_unitoff = take(size_t(B + 1) * sizeof(int64_t));
   L->off_ucnt = take(size_t(heads) * L->n_units * sizeof(uint32_t));
@@ -143,8 +143,7 @@ static Params make_params(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
   p.scores = reinterpret_cast<float*>(base + L.off_scores);
   p.samp = reinterpret_cast<uint32_t*>(base + L.off_samp);
   p.state = reinterpret_cast<HeadState*>(base + L.off_state);
-  p.gflag = reinterpret_cast<uint32_t*>(base + L.off_gflag);
-  p.gdone = p.gflag + size_t(B) * kv->H_kv;
+  p.gdone = reinterpret_cast<uint32_t*>(base + L.off_gdone);
   p.any_dense = reinterpret_cast<uint32_t*>(base + L.off_misc);
   p.unit_off = reinterpret_cast<int64_t*>(base + L.off_unitoff);
   p.ucnt = reinterpret_cast<uint32_t*>(base + L.off_ucnt);
@@ -238,8 +237,8 @@ ra_status ra_decode_stages(const uint16_t* q, int32_t H_q,
   p.keep_scores = (flags & RA_DECODE_KEEP_SCORES) ? 1 : 0;
   using Launcher = hipError_t (*)(const Params&, hipStream_t);
   static const Launcher stages[RA_STAGE_COUNT] = {
-      launch_sample, launch_threshold, launch_scan,  launch_select,
-      launch_dense,  launch_gather,    launch_merge};
+      launch_sample, launch_threshold, launch_scan,
+      launch_select, launch_gather,    launch_merge};
   for (int s = first_stage; s <= last_stage; ++s) {
     if (stages[s](p, stream) != hipSuccess) return RA_ERR_HIP;
   }

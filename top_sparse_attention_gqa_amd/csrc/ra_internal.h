@@ -62,7 +62,7 @@ struct WsLayout {
   int32_t n_tiles;  // n_cap / kTile
   int32_t n_units;  // n_cap / kUnit
   int32_t samp_cap; // sampled key slots per head
-  size_t off_scores, off_samp, off_state, off_gflag, off_misc, off_unitoff,
+  size_t off_scores, off_samp, off_state, off_gdone, off_misc, off_unitoff,
       off_ucnt, off_scnt, off_cand, off_part_mz, off_part_n, total;
 };
 
@@ -90,9 +90,8 @@ struct Params {
   uint32_t* samp;      // [B*H_q][samp_cap] keys of the sampled positions
                        // (0: not a member of M)
   HeadState* state;    // [B*H_q]
-  uint32_t* gflag;     // [B*H_kv] 1: some head of the group needs the rescan
   uint32_t* gdone;     // [B*H_kv] units of the group rescanned so far
-  uint32_t* any_dense; // heads flagged for the rescan in this call
+  uint32_t* any_dense; // heads rescanned in this call
   int64_t* unit_off;   // [B + 1] prefix of H_kv * units(b)
   uint32_t* ucnt;      // [B*H_q][n_units] candidates per (head, unit)
   uint32_t* scnt;      // [B*H_q][n_tiles] retrieved per (head, tile)
@@ -113,8 +112,7 @@ struct Params {
 hipError_t launch_sample(const Params& p, hipStream_t s);
 hipError_t launch_threshold(const Params& p, hipStream_t s);
 hipError_t launch_scan(const Params& p, hipStream_t s);
-hipError_t launch_select(const Params& p, hipStream_t s);
-hipError_t launch_dense(const Params& p, hipStream_t s);   // rescan + reselect
+hipError_t launch_select(const Params& p, hipStream_t s);  // + rescan of short heads
 // Grid of the persistent unit loops (scan, rescan): one block per CU, at
 // most one per unit.
 unsigned scan_blocks(const Params& p);

@@ -407,10 +407,7 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(Params p) {
       *p.any_dense = 0u;
     }
   }
-  if (tid == 0 && hq % p.G == 0) {
-    p.gflag[size_t(b) * p.H_kv + hq / p.G] = 0u;
-    p.gdone[size_t(b) * p.H_kv + hq / p.G] = 0u;
-  }
+  if (tid == 0 && hq % p.G == 0) p.gdone[size_t(b) * p.H_kv + hq / p.G] = 0u;
 
   const SeqGeom sg = seq_geom(p, b);
   uint32_t lo = 0xFFFFFFFFu;  // k_eff == 0: no candidates
@@ -479,7 +476,7 @@ hipError_t launch_threshold(const Params& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- select
+// ---------------------------------------------------------------- select state
 struct SelLds {
   uint16_t ne[kMaxUnits];         // non-empty units (relative to u_lo), ascending
   uint32_t pb[kMaxUnits + 1];     // index of the first entry of each; the total
@@ -569,44 +566,59 @@ __device__ __forceinline__ void select_head(const Params& p, int bh, const SeqGe
   decide(p, bh, sg, rl, TB, gl.lo, L);
 }
 
-// One block per head: count the candidates; decide the threshold, or flag
-// the head (and its group) for the rescan when there are fewer than k_eff.
-__global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
-  const int bh = blockIdx.x;
+// ---------------------------------------------------------------- select
+// One launch, two kinds of blocks. The first B * H_q blocks select, one per
+// head: with at least k_eff candidates the top-k of M is the top-k of the
+// head's lists, whose exact threshold is decided here; a head with fewer
+// is "short" and left to the rescan. The other blocks rescan: they walk the
+// units like the scan, and in a group with a short head every member of M
+// of the short heads becomes a candidate, written at its place in its
+// unit's list (the list of unit u holds positions max(u * kUnit, lo) .. in
+// order). A block decides shortness from the list lengths itself, so the
+// two kinds never wait for each other; without short heads the rescan
+// blocks only read the lengths. Finished units are counted per group, and
+// the block that finishes a group's last unit selects again, over every
+// member of M, for the group's short heads (their lists now hold all of M,
+// so the list lengths are the units' overlaps with it).
+static_assert(kScanThreads == kSelThreads, "the rescan blocks also select");
+
+__device__ __forceinline__ void select_block(const Params& p, int bh, SelLds& L) {
   const int b = bh / p.H_q;
-  const int g = (bh - b * p.H_q) / p.G;
   const SeqGeom sg = seq_geom(p, b);
   if (sg.k_eff == 0) return;  // the unset threshold takes nothing
-  __shared__ SelLds L;
   const HeadState st = p.state[bh];
   const int u_lo = sg.lo / kUnit, nu = (sg.hi - 1) / kUnit + 1 - u_lo;
   const UnitLists gl = unit_prefix(p, bh, sg, u_lo, nu, false, st.lo_key, L);
   if (gl.pb[gl.n_ne] < uint32_t(sg.k_eff)) {
     if (threadIdx.x == 0) {
       p.state[bh].dense = 1u;
-      atomicOr(&p.gflag[size_t(b) * p.H_kv + g], 1u);
-      atomicAdd(p.any_dense, 1u);
+      atomicAdd(p.any_dense, 1u);  // the count of rescanned heads
     }
     return;
   }
   select_head(p, bh, sg, gl, st.max_m, L);
 }
 
-hipError_t launch_select(const Params& p, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3(unsigned(p.B * p.H_q)), dim3(kSelThreads), 0, s, p);
-  return hipGetLastError();
+// Bit hh set: head hh of group (b, g) has fewer than k_eff candidates.
+// Wave hh sums the head's list lengths. Block-wide.
+template <int G>
+__device__ __forceinline__ uint32_t short_heads(const Params& p, int b, int g, uint32_t* s_mask) {
+  const SeqGeom sg = seq_geom(p, b);
+  const int wave = threadIdx.x >> 6;
+  if (threadIdx.x == 0) *s_mask = 0u;
+  __syncthreads();
+  if (wave < G && sg.k_eff > 0) {
+    const size_t bh = size_t(b) * p.H_q + size_t(g) * G + wave;
+    const uint32_t* uc = p.ucnt + bh * p.n_units;
+    const int u_lo = sg.lo / kUnit, u_hi = (sg.hi - 1) / kUnit + 1;
+    uint32_t m = 0;
+    for (int u = u_lo + lane_id(); u < u_hi; u += 64) m += uc[u];
+    m = wave_sum(m);
+    if (lane_id() == 0 && m < uint32_t(sg.k_eff)) atomicOr(s_mask, 1u << wave);
+  }
+  __syncthreads();
+  return *s_mask;
 }
-
-// ---------------------------------------------------------------- dense
-// Without flagged heads every block returns at once. Otherwise the blocks
-// rescan the units of the flagged groups: every member of M of a flagged
-// head becomes a candidate, written at its place in its unit's list (the
-// list of unit u holds positions max(u * kUnit, lo) .. in order). Finished
-// units are counted per group, and the block that finishes a group's last
-// unit selects again, over every member of M, for the group's flagged heads
-// (their lists now hold all of M, so the list lengths are the units'
-// overlaps with it).
-static_assert(kScanThreads == kSelThreads, "the rescan blocks also select");
 
 __device__ __forceinline__ void reselect_head(const Params& p, int bh, SelLds& L) {
   const HeadState st = p.state[bh];
@@ -624,23 +636,27 @@ __device__ __forceinline__ void reselect_head(const Params& p, int bh, SelLds& L
 }
 
 template <int G>
-__global__ __launch_bounds__(kScanThreads) void dense_kernel(Params p) {
-  if (*p.any_dense == 0u) return;
-  __shared__ SelLds S;
-  __shared__ uint32_t s_last;
+__device__ __forceinline__ void rescan_block(const Params& p, int blk, int nblk, SelLds& S) {
+  __shared__ uint32_t s_last, s_mask;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const Lane<G> L;
   const int64_t T = p.unit_off[p.B];
-  const int64_t X0 = T * blockIdx.x / gridDim.x;
-  const int64_t X1 = T * (blockIdx.x + 1) / gridDim.x;
+  const int64_t X0 = T * blk / nblk;
+  const int64_t X1 = T * (blk + 1) / nblk;
+  int cur = -1;          // group whose mask is known
+  uint32_t mask = 0u;
   for (int64_t x = X0; x < X1; ++x) {
     const UnitRef ur = unit_at(p, x);
     const int b = ur.b, g = ur.g;
-    const size_t bg = size_t(b) * p.H_kv + g;
-    if (!p.gflag[bg]) continue;  // block-uniform
+    const int bg = b * p.H_kv + g;
+    if (bg != cur) {  // block-uniform
+      mask = short_heads<G>(p, b, g, &s_mask);
+      cur = bg;
+    }
+    if (mask == 0u) continue;
     const SeqGeom sg = seq_geom(p, b);
     const size_t bh = size_t(b) * p.H_q + size_t(g) * G + L.F;
-    const bool mine = p.state[bh].dense != 0u;
+    const bool mine = (mask >> L.F) & 1u;
     uint4 qreg[G];
     load_q<G>(p, b, g, L, qreg);
     const int u0 = ur.u * kUnit;
@@ -667,21 +683,29 @@ __global__ __launch_bounds__(kScanThreads) void dense_kernel(Params p) {
     __syncthreads();
     if (s_last) {
       __threadfence();  // see the lists the other blocks wrote
-      for (int hh = 0; hh < G; ++hh) {
-        const int bhh = b * p.H_q + g * G + hh;
-        if (p.state[bhh].dense) reselect_head(p, bhh, S);
-      }
+      for (int hh = 0; hh < G; ++hh)
+        if ((mask >> hh) & 1u) reselect_head(p, b * p.H_q + g * G + hh, S);
     }
   }
 }
 
-hipError_t launch_dense(const Params& p, hipStream_t s) {
-  const dim3 grid{scan_blocks(p)}, block{unsigned(kScanThreads)};
+template <int G>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
+  __shared__ SelLds S;
+  const int heads = p.B * p.H_q;
+  if (int(blockIdx.x) < heads)
+    select_block(p, blockIdx.x, S);
+  else
+    rescan_block<G>(p, int(blockIdx.x) - heads, int(gridDim.x) - heads, S);
+}
+
+hipError_t launch_select(const Params& p, hipStream_t s) {
+  const dim3 grid{unsigned(p.B * p.H_q) + scan_blocks(p)}, block{unsigned(kSelThreads)};
   switch (p.G) {
-    case 1: hipLaunchKernelGGL(dense_kernel<1>, grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL(dense_kernel<2>, grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL(dense_kernel<4>, grid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL(dense_kernel<8>, grid, block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL(select_kernel<1>, grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL(select_kernel<2>, grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL(select_kernel<4>, grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL(select_kernel<8>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
