@@ -33,7 +33,17 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-step latency (ms) + KV GB/s vs HBM peak, Llama-3-8B layer @128K/1M"
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E peak
 SCAN_EVERY = 8  # timed-loop steps between the event-timed scan launches
-SCAN_SRC = os.path.join(ROOT, "top_sparse_attention_gqa_amd", "csrc", "score_scan.hip")
+# the scan kernel's sources: a committed counter profile is used only while
+# their hash matches the one recorded with it
+SCAN_SRCS = [os.path.join(ROOT, "top_sparse_attention_gqa_amd", "csrc", f)
+             for f in ("score_scan.hip", "page_scores.h", "ra_internal.h")]
+
+
+def scan_source_sha256():
+    h = hashlib.sha256()
+    for f in SCAN_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 WORKLOAD_TEXT = {
     "C1": "tiny decode step: H_q=4, H_kv=1, N=4096, k=64, n_sink=16, window=64",
@@ -104,8 +114,7 @@ def traffic_from_profile(scan_bytes_per_launch):
         return None
     try:
         d = json.load(open(path))
-        sha = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
-        if d.get("source_sha256") != sha:
+        if d.get("source_sha256") != scan_source_sha256():
             return None
         cal = d["copy_calibration"]
         f_scale = cal["bytes_read"] / (cal["fetch_kib"] * 1024.0)
