@@ -420,12 +420,14 @@ void gather_kernel(Params p) {
 
 // ---------------------------------------------------------------- merge
 // One block per (sequence, query head): 8 groups of 32 threads each take
-// every 8th partial, 4 dims per thread (float4 loads issued kMergeUnroll
-// deep), then the groups are summed in LDS in a fixed order.
+// every 8th partial, 4 dims per thread (float4 loads issued kMergeDepth
+// deep, so up to 128 tiles take one round trip), then the groups are summed
+// in LDS in a fixed order.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeGroups = kMergeThreads / 32;
-constexpr int kMergeUnroll = 4;
-constexpr int kMergeTiles = 8;  // tiles per out_idx copy block
+constexpr int kMergeDepth = 16;
+constexpr int kMergeUnroll = 4;  // positions per thread in flight in the copy
+constexpr int kMergeTiles = 8;   // tiles per out_idx copy block
 
 // out_idx for tiles [c * kMergeTiles, (c + 1) * kMergeTiles) of head bh.
 __device__ void copy_positions(const Params& p, int bh, int c, int nt) {
@@ -510,11 +512,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p) {
   float Z = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (m > -INFINITY) {
-    for (int j0 = grp; j0 < np; j0 += kMergeGroups * kMergeUnroll) {
-      float2 w2[kMergeUnroll];
-      float4 v[kMergeUnroll];
+    for (int j0 = grp; j0 < np; j0 += kMergeGroups * kMergeDepth) {
+      float2 w2[kMergeDepth];
+      float4 v[kMergeDepth];
 #pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u) {
+      for (int u = 0; u < kMergeDepth; ++u) {
         const int j = j0 + u * kMergeGroups;
         const int t = slot(j);
         w2[u] = j < np ? *reinterpret_cast<const float2*>(mz + 2 * t) : make_float2(0.f, 0.f);
@@ -522,7 +524,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p) {
                       : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u) {
+      for (int u = 0; u < kMergeDepth; ++u) {
         const float sc = w2[u].y > 0.0f ? expf(w2[u].x - m) : 0.0f;
         Z += sc * w2[u].y;
         acc.x += sc * v[u].x;

@@ -178,14 +178,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
       }
     }
     __syncthreads();
-    // burst the staged candidates into the (head, unit) lists
+    // burst the staged candidates into the (head, unit) lists; streaming
+    // stores, since cached writes interleaved with the K stream cost it
+    // about twice as much time
     const uint32_t nst = min(s_fill, uint32_t(kStage));
     for (uint32_t i = tid; i < nst; i += kScanThreads) {
       const uint32_t nh = st_nh[i];
       const uint32_t hh = nh >> 27;
       const uint32_t slot = atomicAdd(&s_cnt[hh], 1u);
-      p.cand[(bh0 + hh) * p.n_cap + ubase + slot] =
-          (uint64_t(st_key[i]) << 32) | (nh & ((1u << 27) - 1u));
+      __builtin_nontemporal_store((uint64_t(st_key[i]) << 32) | (nh & ((1u << 27) - 1u)),
+                                  &p.cand[(bh0 + hh) * p.n_cap + ubase + slot]);
     }
     __syncthreads();
     if (tid < G) {
