@@ -77,10 +77,12 @@ def make_inputs(name: str, device: str):
     c = synth.config(name)
     lens = list(c.seq_lens) if c.seq_lens else synth.draw_lengths(c.B, *c.len_range, c.seed)
     ks = [c.k_for(n) for n in lens]
-    kbytes = sum(lens) * c.H_kv * 256
-    # below 1 GiB of keys, rotate independent copies so the 256 MB last-level
-    # cache cannot serve K from one step to the next
-    copies = 1 if kbytes >= (1 << 30) else min(4, -(-(1 << 30) // kbytes))
+    # Rotate four independent copies of the layer: between two steps on the
+    # same copy, three other steps pass their K, V rows and candidate lists
+    # through the 256 MB last-level cache, so nothing a step reads (the
+    # retrieved V rows included, which the streaming K reads would not
+    # evict) is served from the same copy's previous step.
+    copies = 4
     layers = [synth.make_layer(c.H_q, c.H_kv, lens, ks, c.n_sink, c.window,
                                c.needles_per_head, c.seed + 1000 * i, device,
                                shuffle_pages=c.shuffle_pages) for i in range(copies)]
