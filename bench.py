@@ -107,11 +107,11 @@ def algorithmic_bytes(c, lens, ks, idx_np, n_sink, window):
     return kb, vrows * 256, small
 
 
-def traffic_from_profile(scan_bytes_per_launch):
-    """HBM bytes per scan launch from the committed rocprofv3 counter summary,
-    scaled by the copy-kernel calibration; None if absent or if the scan
-    kernel's source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "score_scan_C3_1_pmc.json")
+def traffic_from_profile(workload):
+    """HBM bytes per scan launch from the committed rocprofv3 counter summary
+    of this workload, scaled by the copy-kernel calibration; None if there is
+    none or if the scan kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"score_scan_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     try:
@@ -278,7 +278,7 @@ def run_layer(args):
     scan_bytes = kb + B * H_q * 256
     scan_s = float(scan_ms.mean()) * 1e-3
     achieved = scan_bytes / scan_s / 1e9
-    traffic = traffic_from_profile(scan_bytes)
+    traffic = traffic_from_profile(args.workload)
 
     if args.copy_calib_mib:
         a = torch.empty(args.copy_calib_mib << 20, dtype=torch.uint8, device=dev)

@@ -121,7 +121,8 @@ void gather_kernel(Params p) {
   const int wave = tid >> 6;
   const int r = lane & 15;
   constexpr int kCh = kChunk;
-  constexpr int kSpecPer = (2 * G * kSpec + kGathThreads - 1) / kGathThreads;
+  constexpr int kLists = kUnitsPerTile * G;  // list j: head j / kUnitsPerTile
+  constexpr int kSpecPer = (kLists * kSpec + kGathThreads - 1) / kGathThreads;
   constexpr int kWzPer = (kWPre * G + kGathThreads - 1) / kGathThreads;
 
   __shared__ uint64_t bm[G][kWordsPerTile];
@@ -144,8 +145,8 @@ void gather_kernel(Params p) {
   __shared__ int64_t s_tmp[16];
   __shared__ HeadState s_st[G];
   __shared__ float s_mref[G];
-  __shared__ uint32_t s_lc[2 * G];          // list j: head j / 2, unit 2 tile + j % 2
-  __shared__ uint32_t s_lpre[2 * G + 1];
+  __shared__ uint32_t s_lc[kLists];         // list j: head j / kUnitsPerTile,
+  __shared__ uint32_t s_lpre[kLists + 1];   // unit kUnitsPerTile tile + j % kUnitsPerTile
   __shared__ int32_t s_wpg[kWPre];          // pages of the first rows of the W slice
 
   // this block's slice [w0, w1) of the rows of W = [0, lo) u [hi, N)
@@ -166,10 +167,10 @@ void gather_kernel(Params p) {
     s_pg[tid] = (t0 + tid * 64 < sg.N) ? page_of(p, b, (t0 >> 6) + tid) : 0;
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) bm[hh][tid] = 0ull;
-  } else if (tid < kWordsPerTile + 2 * G) {
+  } else if (tid < kWordsPerTile + kLists) {
     const int j = tid - kWordsPerTile;
-    const int unit = 2 * tile + (j & 1);
-    s_lc[j] = unit < units_seq ? p.ucnt[(bh0 + (j >> 1)) * p.n_units + unit] : 0u;
+    const int unit = kUnitsPerTile * tile + j % kUnitsPerTile;
+    s_lc[j] = unit < units_seq ? p.ucnt[(bh0 + j / kUnitsPerTile) * p.n_units + unit] : 0u;
   } else if (tid >= kWordsPerTile + 32 && tid < kWordsPerTile + 32 + G) {
     const int hh = tid - kWordsPerTile - 32;
     s_st[hh] = p.state[bh0 + hh];
@@ -183,9 +184,9 @@ void gather_kernel(Params p) {
   for (int u = 0; u < kSpecPer; ++u) {
     const int e = u * kGathThreads + tid;
     const int j = e / kSpec, i = e - j * kSpec;
-    const int unit = 2 * tile + (j & 1);
-    spec[u] = (j < 2 * G && unit < units_seq)
-                  ? p.cand[(bh0 + (j >> 1)) * p.n_cap + size_t(unit) * kUnit + i]
+    const int unit = kUnitsPerTile * tile + j % kUnitsPerTile;
+    spec[u] = (j < kLists && unit < units_seq)
+                  ? p.cand[(bh0 + j / kUnitsPerTile) * p.n_cap + size_t(unit) * kUnit + i]
                   : 0ull;
   }
   float wz[kWzPer];  // score of W-slice row q / G for head q % G, q = u * 256 + tid
@@ -203,7 +204,7 @@ void gather_kernel(Params p) {
   // LDS; otherwise they go to the score rows and are read back
   uint32_t listed = 0;
 #pragma unroll
-  for (int j = 0; j < 2 * G; ++j) listed += s_lc[j];
+  for (int j = 0; j < kLists; ++j) listed += s_lc[j];
   const bool staged = listed <= uint32_t(kSel);
   const bool store = p.keep_scores || !staged;
 
@@ -230,19 +231,20 @@ void gather_kernel(Params p) {
   for (int u = 0; u < kSpecPer; ++u) {
     const int e = u * kGathThreads + tid;
     const int j = e / kSpec, i = e - j * kSpec;
-    if (j < 2 * G && uint32_t(i) < s_lc[j] && s_st[j >> 1].thr_shift < 64u) take(j >> 1, spec[u]);
+    if (j < kLists && uint32_t(i) < s_lc[j] && s_st[j / kUnitsPerTile].thr_shift < 64u)
+      take(j / kUnitsPerTile, spec[u]);
   }
   // the rest of the lists (past kSpec entries), as one index space
   if (tid == 0) {
     uint32_t run = 0;
-    for (int j = 0; j < 2 * G; ++j) {
+    for (int j = 0; j < kLists; ++j) {
       s_lpre[j] = run;
-      if (s_st[j >> 1].thr_shift < 64u && s_lc[j] > uint32_t(kSpec)) run += s_lc[j] - kSpec;
+      if (s_st[j / kUnitsPerTile].thr_shift < 64u && s_lc[j] > uint32_t(kSpec)) run += s_lc[j] - kSpec;
     }
-    s_lpre[2 * G] = run;
+    s_lpre[kLists] = run;
   }
   __syncthreads();
-  const uint32_t rest = s_lpre[2 * G];
+  const uint32_t rest = s_lpre[kLists];
   for (uint32_t base = 0; base < rest; base += kGathThreads * kListBatch) {
     uint64_t v[kListBatch];
     int jl[kListBatch];
@@ -253,15 +255,15 @@ void gather_kernel(Params p) {
       jl[u] = -1;
       if (i < rest) {
         int j = 0;
-        while (j + 1 < 2 * G && s_lpre[j + 1] <= i) ++j;
+        while (j + 1 < kLists && s_lpre[j + 1] <= i) ++j;
         jl[u] = j;
-        v[u] = p.cand[(bh0 + (j >> 1)) * p.n_cap + size_t(2 * tile + (j & 1)) * kUnit + kSpec +
-                      (i - s_lpre[j])];
+        v[u] = p.cand[(bh0 + j / kUnitsPerTile) * p.n_cap +
+                      size_t(kUnitsPerTile * tile + j % kUnitsPerTile) * kUnit + kSpec + (i - s_lpre[j])];
       }
     }
 #pragma unroll
     for (int u = 0; u < kListBatch; ++u)
-      if (jl[u] >= 0) take(jl[u] >> 1, v[u]);
+      if (jl[u] >= 0) take(jl[u] / kUnitsPerTile, v[u]);
   }
   __syncthreads();
 

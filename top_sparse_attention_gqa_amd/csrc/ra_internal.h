@@ -17,8 +17,10 @@ constexpr int kPage = 64;
 // block that owns a unit writes its lists and counts without atomics.
 constexpr int kUnitPages = 64;
 constexpr int kUnit = kUnitPages * kPage;  // 4096 positions
-// Positions per gather tile (two units): one tile is one split-K partial.
-constexpr int kTile = 2 * kUnit;
+// Positions per gather tile (a whole number of units): one tile is one
+// split-K partial.
+constexpr int kUnitsPerTile = 2;
+constexpr int kTile = kUnitsPerTile * kUnit;
 constexpr int kWordsPerTile = kTile / 64;
 // Largest number of units of one sequence (RA_MAX_SEQ_LEN / kUnit).
 constexpr int kMaxUnits = RA_MAX_SEQ_LEN / kUnit;

@@ -270,10 +270,12 @@ __device__ __forceinline__ uint32_t radix_pass(const Src& src, const Radix& rx, 
   });
   __syncthreads();
   if (wave == 0) {
-    // lane l sums bins 32 l .. 32 l + 31; the lane where the count from the
-    // top reaches need owns the digit, found among its 32 bins in parallel
+    // lane l sums bins 32 l .. 32 l + 31 (starting at a lane-dependent bin,
+    // so that the lanes read different LDS banks); the lane where the count
+    // from the top reaches need owns the digit, found among its 32 bins in
+    // parallel
     uint32_t s = 0;
-    for (int i = 0; i < 32; ++i) s += rx.hist[lane * 32 + i];
+    for (int i = 0; i < 32; ++i) s += rx.hist[lane * 32 + ((i + lane) & 31)];
     const uint32_t suf = wave_suffix_sum(s);
     const uint64_t m = __ballot(suf >= need);
     const int L = m ? 63 - __clzll(m) : 0;
