@@ -21,6 +21,7 @@ from .ra_oracle import (  # noqa: F401
     kv_bytes_per_token,
     merge,
     partial,
+    prefill_topk,
     scores,
     selection_domain,
     static_set,

@@ -267,6 +267,36 @@ def decode(q, K, V, k: int, n_sink: int, window: int, with_dense: bool = False):
 
 
 # --------------------------------------------------------------------------
+# Prefill: "Prefill queries teach the key graph what matters", step 1: the
+# prefill queries find their exact top-k keys on the GPU, and each query is
+# then linked to those keys to build the key graph. The keys the graph
+# indexes are the members of M (W stays on the GPU), and a query is linked to
+# the best keys of the whole domain (no causal cut: the links describe which
+# keys a query finds important, not an attention step).
+# --------------------------------------------------------------------------
+
+def prefill_topk(Q, K, k: int, n_sink: int, window: int) -> np.ndarray:
+    """Exact top-k keys of every prefill query row and query head.
+
+    Q: [T, H_q, d]; K: [N, H_kv, d] in logical order. For row t and head h
+    the scores are Eq. (1) against every key (``scores`` of that row), and
+    the selection is ``topk`` over M. Returns int64 [T, H_q, k] with each
+    row's k_eff positions ascending, padded with -1.
+    """
+    Qn = np.asarray(Q)
+    T, H_q, _ = Qn.shape
+    N = np.asarray(K).shape[0]
+    M = selection_domain(N, n_sink, window)
+    out = np.full((T, H_q, k), -1, dtype=np.int64)
+    for t in range(T):
+        z = scores(Qn[t], K)
+        for h in range(H_q):
+            sel = topk(z[h], M, k)
+            out[t, h, :sel.size] = sel
+    return out
+
+
+# --------------------------------------------------------------------------
 # KV sizing: "The bottleneck is both storage and KV access", Table 1.
 # --------------------------------------------------------------------------
 

@@ -79,7 +79,21 @@ def _attend_transposed_v(z_h, V_g, S):
     return o[::-1].copy(), l
 
 
+_REAL_PREFILL = ro.prefill_topk
+
+
+def _prefill_rows_reversed(Q, K, k, n_sink, window):
+    return _REAL_PREFILL(np.asarray(Q)[::-1].copy(), K, k, n_sink, window)
+
+
+def _prefill_whole_range(Q, K, k, n_sink, window):
+    # searches all of [0, N) instead of M
+    return _REAL_PREFILL(Q, K, k, 0, 0)
+
+
 MUTANTS = {
+    "prefill_rows_reversed": ("prefill_topk", _prefill_rows_reversed),
+    "prefill_whole_range": ("prefill_topk", _prefill_whole_range),
     "scores_no_scale": ("scores", _scores_no_scale),
     "scores_wrong_group": ("scores", _scores_wrong_group),
     "topk_smallest": ("topk", _topk_smallest),

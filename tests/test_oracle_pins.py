@@ -314,3 +314,67 @@ def test_table1_kv_capacity_row():
     for toks, printed in zip(g["prompt_tokens"], g["printed_capacity_gb"]):
         gib = toks * per_tok / 2 ** 30
         assert float(f"{gib:.3g}") == printed or round(gib, 1) == printed
+
+
+# --------------------------------------------------------------------------
+# Prefill exact top-k ("Prefill queries teach the key graph what matters",
+# step 1): every query row's selection, pinned by plain loops.
+# --------------------------------------------------------------------------
+
+def _dyadic_bf16(rng, shape):
+    """bf16 bit patterns of small dyadic values (exact in fp64 and Fraction)."""
+    vals = rng.integers(-8, 9, size=shape).astype(np.float32) / 4.0
+    return (vals.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _brute_prefill(Q, K, k, n_sink, window):
+    """Exact Fraction scores by explicit loops; each row sorts (-z, n)."""
+    T, H_q, d = Q.shape
+    N, H_kv, _ = K.shape
+    G = H_q // H_kv
+    qf = oracle.as_f64(Q)
+    kf = oracle.as_f64(K)
+    M = [n for n in range(N) if n >= min(n_sink, N) and n < max(N - window, min(n_sink, N))]
+    out = np.full((T, H_q, k), -1, dtype=np.int64)
+    for t in range(T):
+        for h in range(H_q):
+            g = h // G
+            z = {n: sum(Fraction(float(qf[t, h, j])) * Fraction(float(kf[n, g, j])) for j in range(d))
+                 for n in M}
+            best = sorted(M, key=lambda n: (-z[n], n))[:k]
+            out[t, h, :len(best)] = sorted(best)
+    return out
+
+
+@pytest.mark.parametrize("seed,T,H_q,H_kv,N,k,ns,win", [
+    (0, 3, 2, 1, 12, 3, 2, 3),
+    (1, 2, 4, 2, 20, 5, 0, 0),
+    (2, 4, 2, 2, 9, 20, 1, 1),      # k > |M|: all of M, padded
+    (3, 1, 8, 1, 16, 1, 4, 4),
+])
+def test_prefill_topk_matches_loops_on_dyadic_inputs(seed, T, H_q, H_kv, N, k, ns, win):
+    rng = np.random.default_rng(seed)
+    d = oracle.HEAD_DIM
+    Q = _dyadic_bf16(rng, (T, H_q, d))
+    K = _dyadic_bf16(rng, (N, H_kv, d))
+    got = oracle.prefill_topk(Q, K, k, ns, win)
+    assert np.array_equal(got, _brute_prefill(Q, K, k, ns, win))
+
+
+def test_prefill_topk_rows_are_independent_and_planted_keys_win():
+    # key 7 + t is aligned with query row t of head 1 only: each row finds its
+    # own key first; head 0 has a zero query, so all its scores tie and it
+    # takes the lowest position
+    rng = np.random.default_rng(5)
+    T, H_q, H_kv, N, d = 4, 2, 2, 40, oracle.HEAD_DIM
+    Q = np.zeros((T, H_q, d), dtype=np.float32)
+    K = rng.standard_normal((N, H_kv, d)).astype(np.float32) * 0.01
+    for t in range(T):
+        Q[t, 1, t] = 1.0
+        K[7 + t, 1, t] = 4.0
+    Qb = (Q.view(np.uint32) >> 16).astype(np.uint16)
+    Kb = (K.view(np.uint32) >> 16).astype(np.uint16)
+    got = oracle.prefill_topk(Qb, Kb, 1, 0, 0)
+    for t in range(T):
+        assert got[t, 1, 0] == 7 + t
+        assert got[t, 0, 0] == 0
