@@ -197,6 +197,45 @@ size_t ra_workspace_scores_offset(int32_t B, int32_t H_q, int32_t H_kv,
 size_t ra_workspace_rescan_count_offset(int32_t B, int32_t H_q, int32_t H_kv,
                                         int32_t max_seq_len, int32_t k_max);
 
+/* ------------------------------------------------------------------ */
+/* Prefill: exact top-k keys of a block of prefill queries.             */
+/* ------------------------------------------------------------------ */
+
+#define RA_PREFILL_MAX_K 256
+
+/*
+ * Bytes of workspace ra_prefill_topk needs for T query rows of H_q heads
+ * against N keys with budget k. Returns 0 if the arguments are invalid.
+ */
+size_t ra_prefill_workspace_bytes(int32_t T, int32_t H_q, int32_t N, int32_t k);
+
+/*
+ * For every prefill query row t and query head h: the exact top-k keys of
+ * one sequence by z = q . k / sqrt(128), over M = [n_sink, N - window) as in
+ * the decode step, ties to the lower position. This is the first step of the
+ * slides' index frame ("Prefill queries teach the key graph what matters":
+ * prefill queries find their exact top-k keys on the GPU, and each query is
+ * linked to those keys). No causal cut is applied: every row is linked to
+ * the best keys of the whole domain.
+ *  q:       device bf16 [T][H_q][128], 16-byte aligned.
+ *  kv:      the paged layer; seq selects the block-table row of the
+ *           sequence (trusted, like device contents), N its key count
+ *           (1 <= N <= 64 * max_pages).
+ *  k:       host budget, 0 <= k <= RA_PREFILL_MAX_K; k_eff = min(k, |M|).
+ *  out_idx: device int32 [T][H_q][k]: each row's k_eff positions ascending,
+ *           then -1.
+ *  ws, ws_bytes: device workspace of at least ra_prefill_workspace_bytes
+ *           bytes, 256-byte aligned, no initial contents required.
+ * The scores run on MFMA twice (page maxima, then a filter at a per-row
+ * threshold that provably keeps the whole top-k); nothing else is stored.
+ * Validation and ownership as for ra_decode_step.
+ */
+ra_status ra_prefill_topk(const uint16_t* q, int32_t T, int32_t H_q,
+                          const ra_kv_layer* kv, int32_t seq, int32_t N,
+                          int32_t k, int32_t n_sink, int32_t window,
+                          int32_t* out_idx, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

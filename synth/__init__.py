@@ -16,5 +16,6 @@ from .gen import (  # noqa: F401
     draw_lengths,
     make_decode_stream,
     make_layer,
+    make_prefill_queries,
     make_new_tokens,
 )

@@ -197,6 +197,14 @@ def make_decode_stream(B: int, H_q: int, H_kv: int, u: torch.Tensor, steps: int,
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
+def make_prefill_queries(T: int, H_q: int, u: torch.Tensor, seed: int, device) -> torch.Tensor:
+    """T prefill query rows of a layer, drawn like its decode queries
+    (N(0,1) - 0.5 u): bf16 [T][H_q][128]."""
+    g = torch.Generator(device=torch.device(device)).manual_seed(seed)
+    q = torch.randn(T, H_q, HEAD_DIM, generator=g, device=device) - 0.5 * u.to(device)
+    return q.to(torch.bfloat16)
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Raw bf16 bit patterns of a tensor, as a host uint16 array."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

@@ -154,3 +154,45 @@ def test_binding_rejects_cpu_tensors():
         _lib._ptr(q, torch.bfloat16, "q")
     with pytest.raises(TypeError):
         _lib._ptr(q.float(), torch.bfloat16, "q")
+
+
+def _prefill(kv=None, **kw):
+    a = dict(q=FAKE, T=16, H_q=4, seq=0, N=640, k=8, n_sink=4, window=8, out_idx=FAKE,
+             ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    kv = kv if kv is not None else _kv()
+    return _lib.raw.ra_prefill_topk(a["q"], a["T"], a["H_q"], ctypes.byref(kv), a["seq"], a["N"],
+                                    a["k"], a["n_sink"], a["window"], a["out_idx"], a["ws"],
+                                    a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ra.RA_ERR_INVALID_ARGUMENT),
+    (dict(out_idx=None), ra.RA_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), ra.RA_ERR_INVALID_ARGUMENT),
+    (dict(T=0), ra.RA_ERR_INVALID_ARGUMENT),
+    (dict(H_q=0), ra.RA_ERR_INVALID_ARGUMENT),
+    (dict(seq=-1), ra.RA_ERR_INVALID_ARGUMENT),
+    (dict(N=0), ra.RA_ERR_INVALID_ARGUMENT),
+    (dict(N=641), ra.RA_ERR_INVALID_ARGUMENT),          # beyond 64 * max_pages
+    (dict(k=-1), ra.RA_ERR_INVALID_ARGUMENT),
+    (dict(k=257), ra.RA_ERR_INVALID_ARGUMENT),          # above RA_PREFILL_MAX_K
+    (dict(n_sink=-1), ra.RA_ERR_INVALID_ARGUMENT),
+    (dict(q=FAKE + 8), ra.RA_ERR_INVALID_ARGUMENT),
+    (dict(ws=FAKE + 64), ra.RA_ERR_INVALID_ARGUMENT),
+    (dict(ws_bytes=1024), ra.RA_ERR_WORKSPACE),
+    (dict(H_q=16), ra.RA_ERR_UNSUPPORTED),              # G = 16
+])
+def test_prefill_validation(kw, status):
+    assert _prefill(**kw) == status
+
+
+def test_prefill_workspace_size():
+    a = ra.prefill_workspace_bytes(1024, 32, 131072, 100)
+    # dominated by the candidate lists: rows * 64 k entries of 8 bytes
+    assert a >= 1024 * 32 * 64 * 100 * 8
+    assert ra.prefill_workspace_bytes(0, 32, 1000, 10) == 0
+    assert ra.prefill_workspace_bytes(4, 32, 1000, 257) == 0
+    assert ra.prefill_workspace_bytes(4, 32, 0, 10) == 0
+    # k = 0 needs no work but still validates; a null out_idx is allowed then
+    assert _prefill(k=0, out_idx=None, ws_bytes=1 << 40) == ra.RA_OK

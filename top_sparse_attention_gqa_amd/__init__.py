@@ -28,11 +28,14 @@ from ._lib import (  # noqa: F401
     KVLayerStruct,
     RAError,
     abi_version,
+    alloc_prefill_workspace,
     alloc_workspace,
     decode_stages,
     decode_step,
     decode_workspace_bytes,
     kv_append,
+    prefill_topk,
+    prefill_workspace_bytes,
     rescan_count,
     scores_view,
     status_str,

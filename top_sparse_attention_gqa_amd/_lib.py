@@ -37,10 +37,12 @@ STAGE_NAMES = ["sample", "threshold", "scan", "select", "gather", "merge"]
 HEAD_DIM = 128
 PAGE_SIZE = 64
 DECODE_KEEP_SCORES = 1
+PREFILL_MAX_K = 256
 
 EXPORTS = ["ra_abi_version", "ra_status_str", "ra_decode_workspace_bytes",
            "ra_kv_append", "ra_decode_step", "ra_decode_stages",
-           "ra_workspace_scores_offset", "ra_workspace_rescan_count_offset"]
+           "ra_workspace_scores_offset", "ra_workspace_rescan_count_offset",
+           "ra_prefill_workspace_bytes", "ra_prefill_topk"]
 
 
 class KVLayerStruct(ctypes.Structure):
@@ -57,6 +59,12 @@ _lib.ra_decode_workspace_bytes.restype = c_size_t
 _lib.ra_decode_workspace_bytes.argtypes = [c_int32] * 5
 _lib.ra_workspace_scores_offset.restype = c_size_t
 _lib.ra_workspace_scores_offset.argtypes = [c_int32] * 5 + [POINTER(c_int64)]
+_lib.ra_prefill_workspace_bytes.restype = c_size_t
+_lib.ra_prefill_workspace_bytes.argtypes = [c_int32] * 4
+_lib.ra_prefill_topk.restype = c_int
+_lib.ra_prefill_topk.argtypes = [c_void_p, c_int32, c_int32, POINTER(KVLayerStruct), c_int32,
+                                 c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                 c_size_t, c_void_p]
 _lib.ra_workspace_rescan_count_offset.restype = c_size_t
 _lib.ra_workspace_rescan_count_offset.argtypes = [c_int32] * 5
 _lib.ra_kv_append.restype = c_int
@@ -220,6 +228,32 @@ def rescan_count(ws: torch.Tensor, B, H_q, H_kv, max_seq_len, k_max) -> int:
     of k_eff and were decided by the full rescan (reads device memory)."""
     off = workspace_rescan_count_offset(B, H_q, H_kv, max_seq_len, k_max)
     return int(ws[off:off + 4].view(torch.int32).item())
+
+
+def prefill_workspace_bytes(T: int, H_q: int, N: int, k: int) -> int:
+    return int(_lib.ra_prefill_workspace_bytes(T, H_q, N, k))
+
+
+def alloc_prefill_workspace(T, H_q, N, k, device="cuda") -> torch.Tensor:
+    n = prefill_workspace_bytes(T, H_q, N, k)
+    if n == 0:
+        raise ValueError("invalid capacities")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def prefill_topk(q, kv: KVLayer, seq: int, N: int, k: int, n_sink: int, window: int,
+                 out_idx, ws, stream=None) -> None:
+    """ra_prefill_topk: exact top-k keys of every prefill query row and head.
+    q: bf16 [T][H_q][128]; out_idx: int32 [T][H_q][k] (ascending, -1 padded)."""
+    T, H_q = q.shape[0], q.shape[1]
+    if k > 0 and tuple(out_idx.shape) != (T, H_q, k):
+        raise ValueError("out_idx must be [T][H_q][k]")
+    st = _lib.ra_prefill_topk(
+        _ptr(q, torch.bfloat16, "q", align=16), T, H_q, ctypes.byref(kv.struct), seq, N, k,
+        n_sink, window, _ptr(out_idx, torch.int32, "out_idx", nullable=(k == 0)),
+        _ptr(ws, torch.uint8, "ws", align=256), ws.numel(), _stream(stream))
+    if st != RA_OK:
+        raise RAError(st, "ra_prefill_topk")
 
 
 raw = _lib  # the C entry points, for tests that pass raw pointers

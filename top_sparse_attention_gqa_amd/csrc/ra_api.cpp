@@ -49,6 +49,27 @@ bool ws_layout(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seq_len,
   return true;
 }
 
+bool pf_layout(int32_t T, int32_t H_q, int32_t N, int32_t k, PfLayout* L) {
+  if (T <= 0 || H_q <= 0 || N <= 0 || N > RA_MAX_SEQ_LEN || k < 0 || k > RA_PREFILL_MAX_K)
+    return false;
+  const int64_t rows = int64_t(T) * H_q;
+  if (rows > (int64_t(1) << 30)) return false;
+  const int64_t P = (int64_t(N) + kPage - 1) / kPage;
+  const int64_t cap = int64_t(kPage) * k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L->off_pmax = take(size_t(rows) * P * sizeof(uint32_t));
+  L->off_tau = take(size_t(rows) * sizeof(uint64_t));
+  L->off_cnt = take(size_t(rows) * sizeof(uint32_t));
+  L->off_cand = take(size_t(rows) * cap * sizeof(uint64_t));
+  L->total = off;
+  return true;
+}
+
 static int cu_count() {
   // CU count per device, read once.
   static std::mutex mu;
@@ -254,6 +275,63 @@ ra_status ra_decode_step(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
   return ra_decode_stages(q, H_q, kv, seq_lens, B, max_seq_len, k, k_max,
                           n_sink, window, out, out_lse, out_idx, ws, ws_bytes,
                           flags, RA_STAGE_SAMPLE, RA_STAGE_MERGE, stream);
+}
+
+size_t ra_prefill_workspace_bytes(int32_t T, int32_t H_q, int32_t N, int32_t k) {
+  PfLayout L;
+  if (!pf_layout(T, H_q, N, k, &L)) return 0;
+  return L.total;
+}
+
+ra_status ra_prefill_topk(const uint16_t* q, int32_t T, int32_t H_q,
+                          const ra_kv_layer* kv, int32_t seq, int32_t N,
+                          int32_t k, int32_t n_sink, int32_t window,
+                          int32_t* out_idx, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  ra_status st = check_kv(kv);
+  if (st != RA_OK) return st;
+  if (!q || !ws || (k > 0 && !out_idx)) return RA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || (out_idx && !aligned(out_idx, 4)) || !aligned(ws, 256))
+    return RA_ERR_INVALID_ARGUMENT;
+  if (T <= 0 || H_q <= 0 || seq < 0 || n_sink < 0 || window < 0 || k < 0 ||
+      k > RA_PREFILL_MAX_K)
+    return RA_ERR_INVALID_ARGUMENT;
+  if (H_q % kv->H_kv != 0) return RA_ERR_INVALID_ARGUMENT;
+  const int G = H_q / kv->H_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return RA_ERR_UNSUPPORTED;
+  if (N <= 0 || int64_t(N) > int64_t(kv->max_pages) * kPage) return RA_ERR_INVALID_ARGUMENT;
+  PfLayout L;
+  if (!pf_layout(T, H_q, N, k, &L)) return RA_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < L.total) return RA_ERR_WORKSPACE;
+  if (k == 0) return RA_OK;  // nothing to retrieve, nothing to write
+  PfParams p{};
+  char* base = static_cast<char*>(ws);
+  p.q = q;
+  p.k_pool = kv->k_pool;
+  p.block_table = kv->block_table + size_t(seq) * kv->max_pages;
+  p.T = T;
+  p.H_q = H_q;
+  p.H_kv = kv->H_kv;
+  p.N = N;
+  p.P = (N + kPage - 1) / kPage;
+  p.num_pages = kv->num_pages;
+  p.lo = std::min(n_sink, N);
+  p.hi = std::max(N - window, p.lo);
+  p.k = k;
+  p.k_eff = std::min(k, p.hi - p.lo);
+  p.cap = kPage * k;
+  p.pmax = reinterpret_cast<uint32_t*>(base + L.off_pmax);
+  p.tau = reinterpret_cast<uint64_t*>(base + L.off_tau);
+  p.cnt = reinterpret_cast<uint32_t*>(base + L.off_cnt);
+  p.cand = reinterpret_cast<uint64_t*>(base + L.off_cand);
+  p.out_idx = out_idx;
+  // enough blocks to fill the GPU a few times over: split the pages
+  const int64_t row_blocks = (int64_t(T) * G + 127) / 128;
+  const int64_t want = 4 * int64_t(cu_count());
+  const int64_t have = row_blocks * kv->H_kv;
+  p.splits = int32_t(std::max<int64_t>(1, std::min<int64_t>(p.P, (want + have - 1) / have)));
+  if (launch_prefill(p, stream) != hipSuccess) return RA_ERR_HIP;
+  return RA_OK;
 }
 
 }  // extern "C"

@@ -110,6 +110,28 @@ struct Params {
   int32_t keep_scores;  // also store the retrieved set's scores in the rows
 };
 
+// Prefill top-k (prefill_topk.hip).
+struct PfParams {
+  const uint16_t* q;          // [T][H_q][128]
+  const uint16_t* k_pool;
+  const int32_t* block_table; // the sequence's row
+  int32_t T, H_q, H_kv, N, P, num_pages;
+  int32_t lo, hi;             // M = [lo, hi)
+  int32_t k, k_eff, cap, splits;
+  uint32_t* pmax;   // [T*H_q][P] largest score key per page over M (0: none)
+  uint64_t* tau;    // [T*H_q] threshold pair (key << 32 | ~page)
+  uint32_t* cnt;    // [T*H_q] candidates
+  uint64_t* cand;   // [T*H_q][cap] candidates (key << 32 | ~n)
+  int32_t* out_idx; // [T][H_q][k]
+};
+
+struct PfLayout {
+  size_t off_pmax, off_tau, off_cnt, off_cand, total;
+};
+
+bool pf_layout(int32_t T, int32_t H_q, int32_t N, int32_t k, PfLayout* out);
+hipError_t launch_prefill(const PfParams& p, hipStream_t s);
+
 // Launchers (each enqueues its kernels on `s`; they never synchronise).
 hipError_t launch_sample(const Params& p, hipStream_t s);
 hipError_t launch_threshold(const Params& p, hipStream_t s);
