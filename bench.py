@@ -52,6 +52,7 @@ WORKLOAD_TEXT = {
     "C3_2": "Llama-3-8B layer: H_q=32, H_kv=8, d=128, N=1048576, k=2% (20971), n_sink=128, window=512",
     "C3_3": "Llama-3-8B layer: H_q=32, H_kv=8, d=128, N=1048576, k=3% (31457), n_sink=128, window=512",
     "C4": "16 ragged sequences (N uniform in [32768, 131072]) of a Llama-3-8B layer, 64-token pages in shuffled order, k=2% of each length",
+    "P1": "prefill exact top-k: T=1024 query rows of a Llama-3-8B layer (H_q=32, H_kv=8, d=128) against N=131072 keys, k=100, n_sink=128, window=512",
     "C5": "32 Llama-3-8B layers (H_q=32, H_kv=8, d=128) at N=1048576, k=1% of the current length, KV of every layer resident in HBM; each token step appends one K/V row per layer and runs the decode step of all 32 layers",
 }
 
@@ -178,16 +179,19 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     model = args.workload == "C5"
+    prefill = args.workload == "P1"
     if args.steps is None:
-        args.steps = 1000 if model else 200
+        args.steps = 1000 if model else (50 if prefill else 200)
     if args.warmup is None:
-        args.warmup = 2 if model else 20
+        args.warmup = 2 if model else (5 if prefill else 20)
 
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     if model:
         run_model(args)
+    elif prefill:
+        run_prefill(args)
     else:
         run_layer(args)
 
@@ -440,6 +444,144 @@ def run_model(args):
                      "traffic": None,
                      "algorithmic_bytes_per_launch": scan_bytes,
                      "avg_launch_us": round(scan_s * 1e6, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+
+# prefill exact top-k (the key-graph build's input): one "step" is one
+# ra_prefill_topk call over T query rows
+PF_T, PF_H_Q, PF_H_KV, PF_N, PF_K, PF_SINK, PF_WINDOW = 1024, 32, 8, 131072, 100, 128, 512
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
+
+
+def prefill_cpu_baseline(L, Q, budget_s=12.0):
+    """Time the fp64 oracle's prefill_topk on query rows of the same workload
+    until the budget is spent and scale to one full call (T rows)."""
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = len(os.sched_getaffinity(0))
+    K = synth.depage(L.k_pool, L.block_table, 0, PF_N)
+    Qb = synth.bf16_bits(Q)
+    spent, rows = 0.0, 0
+    while spent < budget_s and rows < PF_T:
+        t = time.perf_counter()
+        oracle.prefill_topk(Qb[rows:rows + 1], K, PF_K, PF_SINK, PF_WINDOW)
+        spent += time.perf_counter() - t
+        rows += 1
+    return {
+        "value": round(spent / rows * PF_T * 1e3, 1),
+        "unit": "ms",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle prefill_topk (scores of all {PF_H_Q} heads, exact top-{PF_K} "
+                   f"over M) on {rows} of the {PF_T} query rows, {spent:.1f} s of CPU time, "
+                   f"scaled x{PF_T / rows:.1f} to one full call"),
+    }
+
+
+def run_prefill(args):
+    import numpy as np
+    import torch
+
+    import synth
+    import top_sparse_attention_gqa_amd as ra
+
+    dev = "cuda"
+    copies = 4  # rotated, as for the decode step: no call reads what the last left in cache
+    layers = [synth.make_layer(PF_H_Q, PF_H_KV, [PF_N], [PF_K], PF_SINK, PF_WINDOW, 64,
+                               7000 + 1000 * i, dev) for i in range(copies)]
+    Qs = [synth.make_prefill_queries(PF_T, PF_H_Q, L.u, 17 + i, dev) for i, L in enumerate(layers)]
+    kvs = [ra.KVLayer(L.k_pool, L.v_pool, L.block_table) for L in layers]
+    out = torch.empty(PF_T, PF_H_Q, PF_K, dtype=torch.int32, device=dev)
+    ws = ra.alloc_prefill_workspace(PF_T, PF_H_Q, PF_N, PF_K, device=dev)
+    names = list(ra.PF_STAGE_NAMES)
+    n_stage = len(names)
+
+    def call(i, first=0, last=n_stage - 1):
+        j = i % copies
+        ra.prefill_stages(Qs[j], kvs[j], 0, PF_N, PF_K, PF_SINK, PF_WINDOW, out, ws, first, last)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+
+    # every SCAN_EVERY-th call is split around its first contraction (the
+    # page-maxima kernel), which events time on the launching stream
+    events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+              for i in range(0, args.steps, SCAN_EVERY)}
+    loop_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    loop_ev[0].record()
+    for i in range(args.steps):
+        ev = events.get(i)
+        if ev is None:
+            call(i)
+        else:
+            ev[0].record()
+            call(i, 0, 0)
+            ev[1].record()
+            call(i, 1, n_stage - 1)
+    loop_ev[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    gpu_ms = loop_ev[0].elapsed_time(loop_ev[1]) / args.steps
+    k1_s = float(np.mean([e[0].elapsed_time(e[1]) for e in events.values()])) * 1e-3
+
+    n_break = min(args.steps, 20)
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_stage + 1)] for _ in range(n_break)]
+    for i in range(n_break):
+        bev[i][0].record()
+        for s_ in range(n_stage):
+            call(i, s_, s_)
+            bev[i][s_ + 1].record()
+    torch.cuda.synchronize()
+    stage_ms = np.array([[e[s_].elapsed_time(e[s_ + 1]) for s_ in range(n_stage)] for e in bev])
+
+    # one contraction pass: every (row, head) against every key, 2 d flops each
+    flops = PF_T * PF_H_Q * PF_N * 2 * 128
+    achieved = flops / k1_s / 1e12
+    call(0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(layers[0], Qs[0])
+
+    line = {
+        "metric": "prefill exact top-k latency (ms), Llama-3-8B layer, 1024 queries @128K",
+        "value": round(ms, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: OOD prefill queries vs K, 64 planted needles per query head, x4 sink keys)",
+        "config": {"workload": f"P1: {WORKLOAD_TEXT['P1']}", "T": PF_T, "H_q": PF_H_Q,
+                   "H_kv": PF_H_KV, "head_dim": 128, "seq_len": PF_N, "k": PF_K,
+                   "n_sink": PF_SINK, "window": PF_WINDOW, "kv_copies_rotated": copies,
+                   "accumulate": "fp32"},
+        "query_rows_per_s": round(PF_T / (ms * 1e-3), 1),
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "contraction_tflops_per_step": round(2 * flops / (ms * 1e-3) / 1e12, 1),
+        "stages_us": {n: round(float(stage_ms[:, i].mean()) * 1e3, 2) for i, n in enumerate(names)},
+        "rows_filled": int((got[:, :, -1] >= 0).sum()),
+        "roofline": {"kernel": "pf_scores_kernel<4, false> (page maxima contraction)",
+                     "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": flops,
+                     "avg_launch_us": round(k1_s * 1e6, 2)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

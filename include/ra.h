@@ -236,6 +236,25 @@ ra_status ra_prefill_topk(const uint16_t* q, int32_t T, int32_t H_q,
                           int32_t* out_idx, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/*
+ * The kernels of ra_prefill_topk, in launch order; ra_prefill_stages runs a
+ * contiguous sub-range with the same arguments (as ra_decode_stages does).
+ */
+typedef enum ra_prefill_stage {
+  RA_PF_STAGE_MAXIMA = 0,    /* contraction 1: largest score per (row, page) */
+  RA_PF_STAGE_THRESHOLD = 1, /* per row: the k-th largest (page max, page) */
+  RA_PF_STAGE_FILTER = 2,    /* contraction 2: keys at or above it */
+  RA_PF_STAGE_SELECT = 3,    /* per row: exact top-k, ascending */
+  RA_PF_STAGE_COUNT = 4
+} ra_prefill_stage;
+
+ra_status ra_prefill_stages(const uint16_t* q, int32_t T, int32_t H_q,
+                            const ra_kv_layer* kv, int32_t seq, int32_t N,
+                            int32_t k, int32_t n_sink, int32_t window,
+                            int32_t* out_idx, void* ws, size_t ws_bytes,
+                            int32_t first_stage, int32_t last_stage,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -196,3 +196,11 @@ def test_prefill_workspace_size():
     assert ra.prefill_workspace_bytes(4, 32, 0, 10) == 0
     # k = 0 needs no work but still validates; a null out_idx is allowed then
     assert _prefill(k=0, out_idx=None, ws_bytes=1 << 40) == ra.RA_OK
+
+
+def test_prefill_stage_range_validation():
+    kv = _kv()
+    args = [FAKE, 16, 4, ctypes.byref(kv), 0, 640, 8, 4, 8, FAKE, FAKE, 1 << 40]
+    assert _lib.raw.ra_prefill_stages(*args, 2, 1, None) == ra.RA_ERR_INVALID_ARGUMENT
+    assert _lib.raw.ra_prefill_stages(*args, -1, 1, None) == ra.RA_ERR_INVALID_ARGUMENT
+    assert _lib.raw.ra_prefill_stages(*args, 0, 4, None) == ra.RA_ERR_INVALID_ARGUMENT

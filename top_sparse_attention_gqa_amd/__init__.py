@@ -11,6 +11,13 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     HEAD_DIM,
     PAGE_SIZE,
+    PF_STAGE_COUNT,
+    PF_STAGE_FILTER,
+    PF_STAGE_MAXIMA,
+    PF_STAGE_NAMES,
+    PF_STAGE_SELECT,
+    PF_STAGE_THRESHOLD,
+    PREFILL_MAX_K,
     RA_ERR_HIP,
     RA_ERR_INVALID_ARGUMENT,
     RA_ERR_UNSUPPORTED,
@@ -34,6 +41,7 @@ from ._lib import (  # noqa: F401
     decode_step,
     decode_workspace_bytes,
     kv_append,
+    prefill_stages,
     prefill_topk,
     prefill_workspace_bytes,
     rescan_count,

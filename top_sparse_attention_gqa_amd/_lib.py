@@ -38,11 +38,14 @@ HEAD_DIM = 128
 PAGE_SIZE = 64
 DECODE_KEEP_SCORES = 1
 PREFILL_MAX_K = 256
+(PF_STAGE_MAXIMA, PF_STAGE_THRESHOLD, PF_STAGE_FILTER, PF_STAGE_SELECT) = range(4)
+PF_STAGE_COUNT = 4
+PF_STAGE_NAMES = ["maxima", "threshold", "filter", "select"]
 
 EXPORTS = ["ra_abi_version", "ra_status_str", "ra_decode_workspace_bytes",
            "ra_kv_append", "ra_decode_step", "ra_decode_stages",
            "ra_workspace_scores_offset", "ra_workspace_rescan_count_offset",
-           "ra_prefill_workspace_bytes", "ra_prefill_topk"]
+           "ra_prefill_workspace_bytes", "ra_prefill_topk", "ra_prefill_stages"]
 
 
 class KVLayerStruct(ctypes.Structure):
@@ -65,6 +68,8 @@ _lib.ra_prefill_topk.restype = c_int
 _lib.ra_prefill_topk.argtypes = [c_void_p, c_int32, c_int32, POINTER(KVLayerStruct), c_int32,
                                  c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                  c_size_t, c_void_p]
+_lib.ra_prefill_stages.restype = c_int
+_lib.ra_prefill_stages.argtypes = _lib.ra_prefill_topk.argtypes[:-1] + [c_int32, c_int32, c_void_p]
 _lib.ra_workspace_rescan_count_offset.restype = c_size_t
 _lib.ra_workspace_rescan_count_offset.argtypes = [c_int32] * 5
 _lib.ra_kv_append.restype = c_int
@@ -239,6 +244,21 @@ def alloc_prefill_workspace(T, H_q, N, k, device="cuda") -> torch.Tensor:
     if n == 0:
         raise ValueError("invalid capacities")
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def prefill_stages(q, kv: KVLayer, seq: int, N: int, k: int, n_sink: int, window: int,
+                   out_idx, ws, first=PF_STAGE_MAXIMA, last=PF_STAGE_SELECT, stream=None) -> None:
+    """ra_prefill_stages (ra_prefill_topk when first..last covers every stage).
+    q: bf16 [T][H_q][128]; out_idx: int32 [T][H_q][k] (ascending, -1 padded)."""
+    T, H_q = q.shape[0], q.shape[1]
+    if k > 0 and tuple(out_idx.shape) != (T, H_q, k):
+        raise ValueError("out_idx must be [T][H_q][k]")
+    st = _lib.ra_prefill_stages(
+        _ptr(q, torch.bfloat16, "q", align=16), T, H_q, ctypes.byref(kv.struct), seq, N, k,
+        n_sink, window, _ptr(out_idx, torch.int32, "out_idx", nullable=(k == 0)),
+        _ptr(ws, torch.uint8, "ws", align=256), ws.numel(), first, last, _stream(stream))
+    if st != RA_OK:
+        raise RAError(st, "ra_prefill_stages")
 
 
 def prefill_topk(q, kv: KVLayer, seq: int, N: int, k: int, n_sink: int, window: int,

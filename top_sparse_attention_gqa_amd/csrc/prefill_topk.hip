@@ -273,21 +273,24 @@ static void launch_pf_scores(const PfParams& p, bool filter, hipStream_t s) {
     hipLaunchKernelGGL((pf_scores_kernel<G, false>), grid, dim3(kPfThreads), 0, s, p);
 }
 
-hipError_t launch_prefill(const PfParams& p, hipStream_t s) {
+hipError_t launch_prefill(const PfParams& p, int first, int last, hipStream_t s) {
   const int G = p.H_q / p.H_kv;
   const unsigned row_waves = unsigned((int64_t(p.T) * p.H_q + kPfSelWaves - 1) / kPfSelWaves);
-  for (int pass = 0; pass < 2; ++pass) {
-    switch (G) {
-      case 1: launch_pf_scores<1>(p, pass == 1, s); break;
-      case 2: launch_pf_scores<2>(p, pass == 1, s); break;
-      case 4: launch_pf_scores<4>(p, pass == 1, s); break;
-      case 8: launch_pf_scores<8>(p, pass == 1, s); break;
-      default: return hipErrorInvalidValue;
-    }
-    if (pass == 0)
+  for (int st = first; st <= last; ++st) {
+    if (st == 0 || st == 2) {
+      switch (G) {
+        case 1: launch_pf_scores<1>(p, st == 2, s); break;
+        case 2: launch_pf_scores<2>(p, st == 2, s); break;
+        case 4: launch_pf_scores<4>(p, st == 2, s); break;
+        case 8: launch_pf_scores<8>(p, st == 2, s); break;
+        default: return hipErrorInvalidValue;
+      }
+    } else if (st == 1) {
       hipLaunchKernelGGL(pf_threshold_kernel, dim3(row_waves), dim3(kPfSelWaves * 64), 0, s, p);
+    } else {
+      hipLaunchKernelGGL(pf_select_kernel, dim3(row_waves), dim3(kPfSelWaves * 64), 0, s, p);
+    }
   }
-  hipLaunchKernelGGL(pf_select_kernel, dim3(row_waves), dim3(kPfSelWaves * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -288,6 +288,16 @@ ra_status ra_prefill_topk(const uint16_t* q, int32_t T, int32_t H_q,
                           int32_t k, int32_t n_sink, int32_t window,
                           int32_t* out_idx, void* ws, size_t ws_bytes,
                           hipStream_t stream) {
+  return ra_prefill_stages(q, T, H_q, kv, seq, N, k, n_sink, window, out_idx, ws,
+                           ws_bytes, RA_PF_STAGE_MAXIMA, RA_PF_STAGE_SELECT, stream);
+}
+
+ra_status ra_prefill_stages(const uint16_t* q, int32_t T, int32_t H_q,
+                            const ra_kv_layer* kv, int32_t seq, int32_t N,
+                            int32_t k, int32_t n_sink, int32_t window,
+                            int32_t* out_idx, void* ws, size_t ws_bytes,
+                            int32_t first_stage, int32_t last_stage,
+                            hipStream_t stream) {
   ra_status st = check_kv(kv);
   if (st != RA_OK) return st;
   if (!q || !ws || (k > 0 && !out_idx)) return RA_ERR_INVALID_ARGUMENT;
@@ -303,6 +313,8 @@ ra_status ra_prefill_topk(const uint16_t* q, int32_t T, int32_t H_q,
   PfLayout L;
   if (!pf_layout(T, H_q, N, k, &L)) return RA_ERR_INVALID_ARGUMENT;
   if (ws_bytes < L.total) return RA_ERR_WORKSPACE;
+  if (first_stage < 0 || last_stage >= RA_PF_STAGE_COUNT || first_stage > last_stage)
+    return RA_ERR_INVALID_ARGUMENT;
   if (k == 0) return RA_OK;  // nothing to retrieve, nothing to write
   PfParams p{};
   char* base = static_cast<char*>(ws);
@@ -330,7 +342,7 @@ ra_status ra_prefill_topk(const uint16_t* q, int32_t T, int32_t H_q,
   const int64_t want = 4 * int64_t(cu_count());
   const int64_t have = row_blocks * kv->H_kv;
   p.splits = int32_t(std::max<int64_t>(1, std::min<int64_t>(p.P, (want + have - 1) / have)));
-  if (launch_prefill(p, stream) != hipSuccess) return RA_ERR_HIP;
+  if (launch_prefill(p, first_stage, last_stage, stream) != hipSuccess) return RA_ERR_HIP;
   return RA_OK;
 }
 

@@ -130,7 +130,7 @@ struct PfLayout {
 };
 
 bool pf_layout(int32_t T, int32_t H_q, int32_t N, int32_t k, PfLayout* out);
-hipError_t launch_prefill(const PfParams& p, hipStream_t s);
+hipError_t launch_prefill(const PfParams& p, int first, int last, hipStream_t s);
 
 // Launchers (each enqueues its kernels on `s`; they never synchronise).
 hipError_t launch_sample(const Params& p, hipStream_t s);
