@@ -2,13 +2,16 @@
 // index is built from (RetrievalAttention slides, "Prefill queries teach the
 // key graph what matters", step 1: prefill queries find their exact top-k
 // keys on the GPU; each query is then linked to those keys). For every query
-// row t and query head h: the k_eff largest z = q . k / sqrt(128) (Eq. (1))
-// over the domain M of one sequence, ties to the lower position, ascending.
+// row t and query head h: the k_eff largest q . k (Eq. (1) without the
+// positive factor 1 / sqrt(d), which orders the keys the same way) over the
+// domain M of one sequence, ties to the lower position, ascending.
 //
-// Per KV head the scores form a dense (T G) x N contraction, so they run on
-// MFMA: v_mfma_f32_32x32x16_bf16 takes, per lane, 16 contiguous bytes of a
-// q row (A) and of a K row (B) and leaves a 32 x 32 tile of fp32 scores. The
-// score matrix is never stored; the contraction runs twice:
+// Per KV head the scores form a dense (T G) x N contraction with K = 128, so
+// they run on MFMA. v_mfma_f32_32x32x16_bf16 takes 32 keys as its rows (A)
+// and 32 query rows as its columns (B), so a lane's 16 results are 16 keys
+// of one query: a page maximum is an in-lane max plus one swap between the
+// two lane halves. The score matrix is never stored; the contraction runs
+// twice:
 //   1. page maxima: for every row and page of 64 keys, the largest score
 //      over the page's members of M;
 //   2. threshold (one wave per row): the k_eff-th largest pair
@@ -23,6 +26,13 @@
 // page). Candidates lie in those k_eff pages only, so a row has at most
 // 64 k_eff of them. Both passes issue the same MFMA sequence on the same
 // inputs, so a key's score is bit-identical in both.
+//
+// Contraction block: 8 waves, each holding the B fragments of 64 query rows
+// in registers (512 rows of one KV head per block), walking a range of pages.
+// A page's 64 K rows (16 KB) are loaded once per block with coalesced 16-byte
+// loads, staged through a double-buffered LDS ring (row chunks XOR-swizzled
+// by row so the 16-byte fragment reads are conflict-free), and read by every
+// wave. The next page is in flight in registers while the current one runs.
 #include "ra_internal.h"
 
 namespace ra {
@@ -30,134 +40,338 @@ namespace ra {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kPfWaves = 4;
+constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * 64;
-constexpr int kPfRows = kPfWaves * 32;     // query rows per block (32 per wave)
-constexpr float kPfScale = 0.08838834764831845f;  // 1 / sqrt(128)
+constexpr int kPfQG = 2;                         // 32-row query groups per wave
+static_assert(kPfWaves * kPfQG * 32 == kPfBlockRows, "block rows");
+constexpr int kPfRec = 128;  // score records a wave buffers before it sifts them (filter)
+constexpr int kPfPageChunks = kPage * kHeadDim * 2 / 16;    // 16-byte chunks per page: 1024
+constexpr int kPfLoads = kPfPageChunks / kPfThreads;         // per thread per page: 2
+
+// The block table is read-only here: read it as constant memory, so the
+// (wave-uniform) page lookup is a scalar load that does not sit in the
+// vector memory counter behind the K loads in flight.
+typedef const __attribute__((address_space(4))) int32_t* pf_const_i32_ptr;
 
 __device__ __forceinline__ int pf_page(const PfParams& p, int j) {
-  const int pg = p.block_table[j];
+  const int pg = ((pf_const_i32_ptr)p.block_table)[j];
   return ((unsigned)pg < (unsigned)p.num_pages) ? pg : 0;
 }
 
-// Row of the score tile held in register r of this lane (MFMA 32x32 layout):
-// rows (r / 4) * 8 + (lane / 32) * 4 + r % 4, column lane % 32.
+// Key row of the score tile held in register r of this lane (MFMA 32x32
+// layout): rows (r / 4) * 8 + (lane / 32) * 4 + r % 4; the query column is
+// lane % 32.
 __device__ __forceinline__ int tile_row(int r, int lane) {
   return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
 }
 
-// Grid (row blocks, H_kv, page splits). Each block: kPfRows query rows of KV
-// head blockIdx.y (local row r is query t = r / G, head g G + r % G) against
-// the pages of its split. FILTER false: page maxima; true: candidates.
-template <int G, bool FILTER>
-__global__ __launch_bounds__(kPfThreads) void pf_scores_kernel(PfParams p) {
-  const int g = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int TG = p.T * G;
-  const int r0 = blockIdx.x * kPfRows + wave * 32;
-  if (r0 >= TG) return;  // wave-uniform
+__device__ __forceinline__ float max16(const f32x16_t& c) {
+  float a = fmaxf(fmaxf(c[0], c[1]), c[2]);
+  float b = fmaxf(fmaxf(c[3], c[4]), c[5]);
+  float d = fmaxf(fmaxf(c[6], c[7]), c[8]);
+  float e = fmaxf(fmaxf(c[9], c[10]), c[11]);
+  float f = fmaxf(fmaxf(c[12], c[13]), c[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), fmaxf(d, e)), fmaxf(f, c[15]));
+}
 
-  // A fragments: row r0 + lane % 32, dims 16 s + 8 (lane / 32) .. + 8
-  bf16x8_t a[8];
-  {
-    const int ra = r0 + (lane & 31);
-    if (ra < TG) {
-      const int t = ra / G, hh = ra - (ra / G) * G;
-      const uint16_t* qr = p.q + (size_t(t) * p.H_q + size_t(g) * G + hh) * kHeadDim + 8 * (lane >> 5);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) a[s] = *reinterpret_cast<const bf16x8_t*>(qr + 16 * s);
-    } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) a[s] = bf16x8_t{};
-    }
+struct PfLds {
+  uint4 ring[2][kPfPageChunks];  // two pages of K, 16-byte chunks, swizzled
+  union {
+    uint32_t pm[kPfWaves][64 * (kPfChunk + 1)];  // page-maxima keys, [query][page]
+    struct {
+      // a record: one lane's 16 scores of a tile whose maximum reached the
+      // row's threshold, with (wave row << 24 | position of its first key)
+      uint4 rec[kPfWaves][kPfRec][4];
+      uint32_t meta[kPfWaves][kPfRec];
+      uint32_t cnt[kPfWaves][64];    // candidates per wave row in this page range
+      uint64_t tau[kPfWaves][64];    // per wave row: threshold pair
+      uint64_t base[kPfWaves][64];   // per wave row: first slot of the range's list
+    } f;
+  } u;
+};
+
+// Block -> (KV head g, page range z, row block rb). With xcd_groups, blocks
+// b, b + 8, b + 16, ... (dispatched to the same XCD) take the row blocks of
+// one (g, z) in turn, so they read the same K pages through one L2.
+__device__ __forceinline__ void pf_block_coords(const PfParams& p, int& g, int& z, int& rb) {
+  const int b = blockIdx.x;
+  int c;
+  if (p.xcd_groups) {
+    const int x = b & 7, i = b >> 3;
+    rb = i % p.row_blocks;
+    c = (i / p.row_blocks) * 8 + x;
+  } else {
+    rb = b % p.row_blocks;
+    c = b / p.row_blocks;
   }
-  // the rows this lane's registers hold, as global row indices t H_q + h
-  int R[16];
-  bool rv[16];
+  g = c / p.splits;
+  z = c - g * p.splits;
+}
+
+template <int G, bool FILTER>
+__global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
+  __shared__ PfLds sm;
+  int g, z, rb;
+  pf_block_coords(p, g, z, rb);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hl = lane >> 5;
+  const int TG = p.T * G;
+  const int rw = rb * kPfBlockRows + wave * (kPfQG * 32);  // wave's first local row
+
+  // B fragments: query row rw + 32 q + lane % 32, dims 16 s + 8 hl .. + 8
+  bf16x8_t qf[kPfQG][8];
+  int R[kPfQG];        // this lane's query column, as a global row t H_q + h
+  bool rv[kPfQG];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int lr = r0 + tile_row(r, lane);
-    rv[r] = lr < TG;
-    const int t = lr / G, hh = lr - (lr / G) * G;
-    R[r] = rv[r] ? t * p.H_q + g * G + hh : 0;
+  for (int q = 0; q < kPfQG; ++q) {
+    const int r = rw + 32 * q + (lane & 31);
+    rv[q] = r < TG;
+    const int t = r / G, hh = r - (r / G) * G;
+    R[q] = rv[q] ? t * p.H_q + g * G + hh : 0;
+    const uint16_t* qr = p.q + size_t(R[q]) * kHeadDim + 8 * hl;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qf[q][s] = rv[q] ? *reinterpret_cast<const bf16x8_t*>(qr + 16 * s) : bf16x8_t{};
   }
-  uint64_t tau[16];
+  float thr[kPfQG];  // a score below it is no candidate
   if constexpr (FILTER) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) tau[r] = rv[r] ? p.tau[R[r]] : ~0ull;
+    for (int q = 0; q < kPfQG; ++q) {
+      const uint64_t t = rv[q] ? p.tau[R[q]] : ~0ull;
+      thr[q] = key2f(uint32_t(t >> 32));  // key 0: -inf, every score passes
+      if (t == ~0ull) thr[q] = __uint_as_float(0x7FC00000u);  // nothing passes
+      // lane l keeps the wave row l (group l / 32, column l % 32)
+      if (q == hl) {
+        sm.u.f.cnt[wave][lane] = 0u;
+        sm.u.f.tau[wave][lane] = t;
+        sm.u.f.base[wave][lane] =
+            rv[q] ? size_t(R[q]) * p.cap + p.seg_off[size_t(R[q]) * p.splits + z] : 0ull;
+      }
+    }
   }
 
-  const int j0 = int(int64_t(p.P) * blockIdx.z / gridDim.z);
-  const int j1 = int(int64_t(p.P) * (blockIdx.z + 1) / gridDim.z);
-  for (int j = j0; j < j1; ++j) {
-    const uint16_t* kb = p.k_pool + (size_t(pf_page(p, j)) * p.H_kv + g) * (kPage * kHeadDim) +
-                         8 * (lane >> 5);
-    float m[16];
+  const int chunks = p.Ppad / kPfChunk;
+  const int j0 = int(int64_t(chunks) * z / p.splits) * kPfChunk;
+  const int j1 = min(p.P, int(int64_t(chunks) * (z + 1) / p.splits) * kPfChunk);
+  if (j0 >= j1) return;  // block-uniform
+
+  const size_t head_off = size_t(g) * (kPage * kHeadDim);
+  static_assert(kPfLoads == 2, "two 16-byte loads per thread per page");
+  // Issued unconditionally (past the range it re-reads the last page), so
+  // every iteration has the same loads in flight and the waits before the
+  // LDS writes cover only the page being written.
+  auto gload = [&](uint4& x0, uint4& x1, int j) {
+    const uint4* kb = reinterpret_cast<const uint4*>(
+        p.k_pool + size_t(pf_page(p, min(j, j1 - 1))) * p.H_kv * (kPage * kHeadDim) + head_off);
+    x0 = kb[tid];
+    x1 = kb[tid + kPfThreads];
+  };
+  // chunk c % 16 of key row c / 16 goes to position (c % 16) ^ (row % 16)
+  const int c0 = tid, c1 = tid + kPfThreads;
+  const int w0 = (c0 >> 4) * 16 + ((c0 & 15) ^ ((c0 >> 4) & 15));
+  const int w1 = (c1 >> 4) * 16 + ((c1 & 15) ^ ((c1 >> 4) & 15));
+  auto lwrite = [&](const uint4& x0, const uint4& x1, int slot) {
+    sm.ring[slot][w0] = x0;
+    sm.ring[slot][w1] = x1;
+  };
+
+  // Sift the buffered records, one per lane: every score whose pair
+  // (score, page) reaches the row's threshold is appended to the row's list.
+  uint32_t n_rec = 0;  // wave-uniform
+  auto sift = [&]() {
+    for (uint32_t i0 = 0; i0 < n_rec; i0 += 64) {
+      const uint32_t i = i0 + lane;
+      if (i < n_rec) {
+        const uint32_t meta = sm.u.f.meta[wave][i];
+        const uint32_t qi = meta >> 24, n0 = meta & 0xFFFFFFu;
+        const uint32_t npg = ~(n0 >> 6);  // ~page
+        const uint64_t t = sm.u.f.tau[wave][qi];
+        uint64_t* list = p.cand + sm.u.f.base[wave][qi];
+        float v[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) m[r] = -INFINITY;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int col = half * 32 + (lane & 31);  // key within the page
-      const int n = j * kPage + col;
-      bf16x8_t b[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) b[s] = *reinterpret_cast<const bf16x8_t*>(kb + col * kHeadDim + 16 * s);
-      f32x16_t c = {};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b[s], c, 0, 0, 0);
-      const bool in_m = n >= p.lo && n < p.hi;
-      if constexpr (!FILTER) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) m[r] = in_m ? fmaxf(m[r], c[r]) : m[r];
-      } else {
+        for (int c = 0; c < 4; ++c) {
+          const uint4 x = sm.u.f.rec[wave][i][c];
+          v[4 * c] = __uint_as_float(x.x);
+          v[4 * c + 1] = __uint_as_float(x.y);
+          v[4 * c + 2] = __uint_as_float(x.z);
+          v[4 * c + 3] = __uint_as_float(x.w);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t key = f2key(c[r] * kPfScale);
-          const uint64_t pair = (uint64_t(key) << 32) | uint32_t(~uint32_t(j));
-          if (in_m && rv[r] && pair >= tau[r]) {
-            const uint32_t slot = atomicAdd(&p.cnt[R[r]], 1u);
-            if (slot < uint32_t(p.cap))
-              p.cand[size_t(R[r]) * p.cap + slot] = (uint64_t(key) << 32) | uint32_t(~uint32_t(n));
+          const uint32_t key = f2key(v[r]);
+          const bool ok = v[r] == v[r] && ((uint64_t(key) << 32) | npg) >= t;
+          const uint32_t at = atomicAdd(&sm.u.f.cnt[wave][qi], ok ? 1u : 0u);
+          const uint32_t n = n0 + uint32_t((r >> 2) * 8 + (r & 3));
+          if (ok) list[at] = (uint64_t(key) << 32) | uint32_t(~n);
+        }
+      }
+    }
+    n_rec = 0;
+  };
+  auto pm_flush = [&](int cs) {
+    // rows of this wave x pages cs .. cs + 15: four lanes per row, 16 bytes each
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qi = 16 * i + (lane >> 2);
+      const int r = rw + qi;
+      if (r < TG) {
+        const int t = r / G, hh = r - (r / G) * G;
+        const size_t Rg = size_t(t) * p.H_q + g * G + hh;
+        const int e0 = 4 * (lane & 3);
+        uint32_t v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = cs + e0 + e < j1 ? sm.u.pm[wave][qi * (kPfChunk + 1) + e0 + e] : 0u;
+        *reinterpret_cast<uint4*>(p.pmax + Rg * p.Ppad + cs + e0) = uint4{v[0], v[1], v[2], v[3]};
+      }
+    }
+  };
+
+  auto compute = [&](int j, int slot) {
+    const int nb = j * kPage;
+    const bool full = nb >= p.lo && nb + kPage <= p.hi;
+    float pm[kPfQG];
+#pragma unroll
+    for (int q = 0; q < kPfQG; ++q) pm[q] = -INFINITY;
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      const int kr = tile * 32 + (lane & 31);
+      bf16x8_t a[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        a[s] = *reinterpret_cast<const bf16x8_t*>(&sm.ring[slot][kr * 16 + ((2 * s + hl) ^ (kr & 15))]);
+      f32x16_t acc[kPfQG];
+#pragma unroll
+      for (int q = 0; q < kPfQG; ++q) {
+        acc[q] = f32x16_t{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], qf[q][s], acc[q], 0, 0, 0);
+      }
+      if (!full) {
+        // keys outside M (or past N) become NaN: ignored by the maxima,
+        // never at or above a threshold
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int n = nb + tile * 32 + tile_row(r, lane);
+          if (n < p.lo || n >= p.hi) {
+#pragma unroll
+            for (int q = 0; q < kPfQG; ++q) acc[q][r] = __uint_as_float(0x7FC00000u);
+          }
+        }
+      }
+      if constexpr (!FILTER) {
+#pragma unroll
+        for (int q = 0; q < kPfQG; ++q) pm[q] = fmaxf(pm[q], max16(acc[q]));
+      } else {
+        // a lane whose 16 scores of a group reach its row's threshold
+        // buffers them as a record
+#pragma unroll
+        for (int q = 0; q < kPfQG; ++q) {
+          const bool hit = max16(acc[q]) >= thr[q];
+          const uint64_t m = __ballot(hit);
+          if (m) {
+            if (n_rec + 64 > uint32_t(kPfRec)) sift();
+            if (hit) {
+              const uint32_t at = n_rec + uint32_t(__popcll(m & ((1ull << lane) - 1ull)));
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                sm.u.f.rec[wave][at][c] = uint4{__float_as_uint(acc[q][4 * c]), __float_as_uint(acc[q][4 * c + 1]),
+                                                __float_as_uint(acc[q][4 * c + 2]), __float_as_uint(acc[q][4 * c + 3])};
+              sm.u.f.meta[wave][at] = (uint32_t(32 * q + (lane & 31)) << 24) |
+                                      uint32_t(nb + tile * 32 + hl * 4);
+            }
+            n_rec += uint32_t(__popcll(m));
           }
         }
       }
     }
     if constexpr (!FILTER) {
-      // maximum over the 32 columns of each half-wave
+      // both lane halves hold 32 of the page's keys; lane l then records
+      // query row l of the wave (group l / 32)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) m[r] = fmaxf(m[r], __shfl_xor(m[r], off));
-      }
-      if ((lane & 31) == 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (rv[r]) p.pmax[size_t(R[r]) * p.P + j] = m[r] == -INFINITY ? 0u : f2key(m[r] * kPfScale);
-      }
+      for (int q = 0; q < kPfQG; ++q) pm[q] = fmaxf(pm[q], __shfl_xor(pm[q], 32));
+      const float mv = hl ? pm[1] : pm[0];
+      sm.u.pm[wave][lane * (kPfChunk + 1) + (j & (kPfChunk - 1))] = mv == -INFINITY ? 0u : f2key(mv);
+      if ((j & (kPfChunk - 1)) == kPfChunk - 1 || j == j1 - 1) pm_flush(j & ~(kPfChunk - 1));
     }
+  };
+
+  uint4 sa0, sa1, sb0, sb1;
+  gload(sa0, sa1, j0);
+  gload(sb0, sb1, j0 + 1);
+  lwrite(sa0, sa1, 0);
+  gload(sa0, sa1, j0 + 2);
+  __syncthreads();
+  for (int j = j0; j < j1; j += 2) {
+    // page j is in ring slot 0, page j + 1 in sb, page j + 2 in sa
+    if (j + 1 < j1) lwrite(sb0, sb1, 1);
+    gload(sb0, sb1, j + 3);
+    compute(j, 0);
+    __syncthreads();
+    if (j + 1 >= j1) break;
+    if (j + 2 < j1) lwrite(sa0, sa1, 0);
+    gload(sa0, sa1, j + 4);
+    compute(j + 1, 1);
+    __syncthreads();
+  }
+  if constexpr (FILTER) {
+    sift();
+    // lane l: the wave's query row l (group l / 32, column l % 32)
+    const bool valid = hl ? rv[1] : rv[0];
+    const int Rl = hl ? R[1] : R[0];
+    if (valid) p.seg_cnt[size_t(Rl) * p.splits + z] = sm.u.f.cnt[wave][lane];
   }
 }
 
 // ---------------------------------------------------------------- wave select
-// The need-th largest of the non-zero values get(0 .. n - 1) (distinct), by
-// an 8-bit radix over the 64-bit values held in global memory; hist is this
-// wave's 256 LDS bins. Returns a bound t such that exactly `need` of the
-// values are >= t. Every lane of the wave calls it with the same arguments.
-template <typename Get>
-__device__ __forceinline__ uint64_t wave_kth(Get&& get, uint32_t n, uint32_t need, uint32_t* hist) {
+// Split z of S covers page chunks [chunks z / S, chunks (z + 1) / S).
+__device__ __forceinline__ int pf_split_first_chunk(int z, int chunks, int S) {
+  return int(int64_t(chunks) * z / S);
+}
+
+// The bits shared by every non-zero value (and_all over them, or_all over
+// them): their count and the shared prefix, as the starting point of a radix
+// select that skips the digits every value has in common.
+__device__ __forceinline__ int common_prefix_len(uint64_t and_all, uint64_t or_all, int width) {
+  const uint64_t diff = and_all ^ or_all;
+  return diff == 0 ? width : __clzll((long long)diff) - (64 - width);
+}
+
+// The need-th largest of the non-zero values a wave visits (visit(fn) calls
+// fn(v) for each value of this lane; the values are distinct), by an 8-bit
+// radix below their common prefix; hist is this wave's 256 LDS bins. Returns
+// a bound t such that exactly `need` of the values are >= t. Every lane of
+// the wave calls it with the same arguments; at least `need` values exist.
+template <typename Visit>
+__device__ __forceinline__ uint64_t wave_kth(Visit&& visit, uint32_t need, uint32_t* hist) {
   const int lane = lane_id();
-  uint64_t prefix = 0;
-  int plen = 0;
+  uint64_t and_all = ~0ull, or_all = 0ull;
+  visit([&](uint64_t v) {
+    if (v != 0ull) {
+      and_all &= v;
+      or_all |= v;
+    }
+  });
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    and_all &= __shfl_xor(and_all, off);
+    or_all |= __shfl_xor(or_all, off);
+  }
+  int plen = common_prefix_len(and_all, or_all, 64);
+  if (plen == 64) return and_all;  // a single value
+  uint64_t prefix = plen == 0 ? 0ull : and_all >> (64 - plen);
   for (;;) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) hist[lane * 4 + i] = 0u;
-    const int sh = 56 - plen;
-    for (uint32_t i = lane; i < n; i += 64) {
-      const uint64_t v = get(i);
+    const int d = min(8, 64 - plen);
+    const int sh = 64 - plen - d;
+    visit([&](uint64_t v) {
       if (v != 0ull && (plen == 0 || (v >> (64 - plen)) == prefix))
-        atomicAdd(&hist[uint32_t(v >> sh) & 255u], 1u);
-    }
+        atomicAdd(&hist[uint32_t(v >> sh) & ((1u << d) - 1u)], 1u);
+    });
     // lane l holds bins 255 - 4 l .. 252 - 4 l (largest digits first)
     uint32_t c[4], s = 0;
 #pragma unroll
@@ -188,44 +402,247 @@ __device__ __forceinline__ uint64_t wave_kth(Get&& get, uint32_t n, uint32_t nee
     digit = __shfl(digit, L);
     above = __shfl(above, L);
     cd = __shfl(cd, L);
-    prefix = (prefix << 8) | digit;
-    plen += 8;
+    prefix = (prefix << d) | digit;
+    plen += d;
     need -= above;
     if (cd == need || plen == 64) return prefix << (64 - plen);
   }
 }
 
-// One wave per row: the threshold pair over the row's page maxima, and the
-// row's candidate count reset.
-constexpr int kPfSelWaves = 4;
-
-__global__ __launch_bounds__(kPfSelWaves * 64) void pf_threshold_kernel(PfParams p) {
-  __shared__ uint32_t s_hist[kPfSelWaves][256];
-  const int wave = threadIdx.x >> 6;
-  const int R = blockIdx.x * kPfSelWaves + wave;
-  if (R >= p.T * p.H_q) return;
-  const uint32_t* pm = p.pmax + size_t(R) * p.P;
-  auto pair = [&](uint32_t j) -> uint64_t {
-    const uint32_t key = pm[j];
-    return key ? (uint64_t(key) << 32) | uint32_t(~j) : 0ull;
-  };
-  uint32_t present = 0;
-  for (uint32_t j = lane_id(); j < uint32_t(p.P); j += 64) present += pm[j] ? 1u : 0u;
-  present = wave_sum(present);
-  uint64_t t;
-  if (p.k_eff == 0)
-    t = ~0ull;                      // nothing is retrieved
-  else if (present <= uint32_t(p.k_eff))
-    t = 1ull;                       // every member of M is a candidate
-  else
-    t = wave_kth(pair, uint32_t(p.P), uint32_t(p.k_eff), s_hist[wave]);
-  if (lane_id() == 0) {
-    p.tau[R] = t;
-    p.cnt[R] = 0u;
+// ---------------------------------------------------------------- threshold
+// The need-th largest of the non-zero keys v (NV per lane, repeats allowed),
+// by 8-bit radix passes over registers below the keys' common prefix; hist
+// is this wave's 256 LDS bins. Requires at least `need` non-zero keys.
+// Returns the key and, in *above, how many keys are strictly larger.
+template <int NV>
+__device__ __forceinline__ uint32_t reg_kth(const uint32_t (&v)[NV], uint32_t need,
+                                            uint32_t* hist, uint32_t* above_out) {
+  const int lane = lane_id();
+  uint32_t and_all = ~0u, or_all = 0u;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (v[i] != 0u) {
+      and_all &= v[i];
+      or_all |= v[i];
+    }
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    and_all &= __shfl_xor(and_all, off);
+    or_all |= __shfl_xor(or_all, off);
+  }
+  int rem = 32 - common_prefix_len(and_all, or_all, 32);  // bits still open
+  uint32_t prefix = rem == 32 ? 0u : and_all & ~((1u << rem) - 1u);
+  uint32_t above_all = 0;
+#pragma unroll 1
+  while (rem > 0) {
+    const int d = min(8, rem);
+    const int sh = rem - d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hist[lane * 4 + i] = 0u;
+    // the bits above the digit must equal the prefix's
+    const uint32_t hi_mask = sh + d == 32 ? 0u : ~((1u << (sh + d)) - 1u);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const uint32_t x = v[i];
+      if (x != 0u && (x & hi_mask) == prefix) atomicAdd(&hist[(x >> sh) & ((1u << d) - 1u)], 1u);
+    }
+    uint32_t c[4], s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = hist[255 - 4 * lane - i];
+      s += c[i];
+    }
+    uint32_t incl = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    const uint64_t reach = __ballot(incl >= need);
+    const int L = reach ? __ffsll((unsigned long long)reach) - 1 : 63;
+    uint32_t run = incl - s, digit = 0, above = 0;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!found && run + c[i] >= need) {
+        found = true;
+        digit = 255u - 4u * uint32_t(lane) - uint32_t(i);
+        above = run;
+      }
+      run += c[i];
+    }
+    digit = __shfl(digit, L);
+    above = __shfl(above, L);
+    prefix |= digit << sh;
+    need -= above;
+    above_all += above;
+    rem = sh;
+  }
+  *above_out = above_all;
+  return prefix;
 }
 
-// One wave per row: the exact top k_eff of the row's candidates, ascending.
+// One wave per row: the threshold pair over the row's page maxima and the
+// first candidate slot of each page range (64 per page at or above the
+// threshold: no other page holds a candidate).
+constexpr int kPfSelWaves = 4;
+
+__device__ __forceinline__ bool pf_pair_at_least(uint32_t key, int page, uint64_t t) {
+  return key != 0u && ((uint64_t(key) << 32) | uint32_t(~uint32_t(page))) >= t;
+}
+
+// Lane l holds pages 256 i + 4 l + e in registers.
+template <int NV>
+__global__ __launch_bounds__(kPfSelWaves * 64) void pf_threshold_kernel(PfParams p) {
+  __shared__ uint32_t s_hist[kPfSelWaves][256];
+  __shared__ uint32_t s_pre[kPfSelWaves][NV * 16 / 4 + 1];  // per chunk, then prefix
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int R = blockIdx.x * kPfSelWaves + wave;
+  if (R >= p.T * p.H_q) return;
+  const uint32_t* pm = p.pmax + size_t(R) * p.Ppad;
+  uint32_t v[NV];
+  uint32_t present = 0;
+#pragma unroll
+  for (int i = 0; i < NV / 4; ++i) {
+    const int j = 256 * i + 4 * lane;
+    const uint4 x = j < p.Ppad ? *reinterpret_cast<const uint4*>(pm + j) : uint4{0u, 0u, 0u, 0u};
+    v[4 * i] = x.x;
+    v[4 * i + 1] = x.y;
+    v[4 * i + 2] = x.z;
+    v[4 * i + 3] = x.w;
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) present += v[i] ? 1u : 0u;
+  present = wave_sum(present);
+  uint64_t t;
+  if (p.k_eff == 0) {
+    t = ~0ull;  // nothing is retrieved
+  } else if (present <= uint32_t(p.k_eff)) {
+    t = 1ull;   // every member of M is a candidate
+  } else {
+    uint32_t above;
+    const uint32_t key = reg_kth<NV>(v, uint32_t(p.k_eff), s_hist[wave], &above);
+    // the pair's page: the (k_eff - above)-th lowest page whose maximum is key
+    uint32_t need = uint32_t(p.k_eff) - above;
+    int page = 0;
+#pragma unroll
+    for (int i = 0; i < NV / 4; ++i) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c += v[4 * i + e] == key ? 1u : 0u;
+      uint32_t incl = c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t u = __shfl_up(incl, off);
+        if (lane >= off) incl += u;
+      }
+      const uint32_t tot = __shfl(incl, 63);
+      if (need <= tot) {
+        const uint64_t reach = __ballot(incl >= need);
+        const int L = __ffsll((unsigned long long)reach) - 1;
+        uint32_t run = incl - c;
+        int pg = 0;
+        bool found = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (v[4 * i + e] == key) {
+            ++run;
+            if (!found && run == need) {
+              found = true;
+              pg = 256 * i + 4 * lane + e;
+            }
+          }
+        }
+        page = __shfl(pg, L);
+        break;
+      }
+      need -= tot;
+    }
+    t = (uint64_t(key) << 32) | uint32_t(~uint32_t(page));
+  }
+  // pages at or above t per chunk of 16 (lanes 4 m .. 4 m + 3 share chunk
+  // 16 i + m), then the exclusive prefix over chunks
+  const int chunks = p.Ppad / kPfChunk;
+#pragma unroll
+  for (int i = 0; i < NV / 4; ++i) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c += pf_pair_at_least(v[4 * i + e], 256 * i + 4 * lane + e, t) ? 1u : 0u;
+    c += __shfl_xor(c, 1);
+    c += __shfl_xor(c, 2);
+    if ((lane & 3) == 0) s_pre[wave][16 * i + (lane >> 2)] = c;
+  }
+  {
+    constexpr int kPer = NV * 16 / 4 / 64;  // chunks per lane
+    uint32_t c[kPer], sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      c[i] = s_pre[wave][kPer * lane + i];
+      sum += c[i];
+    }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t u = __shfl_up(incl, off);
+      if (lane >= off) incl += u;
+    }
+    uint32_t run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      s_pre[wave][kPer * lane + i] = run;
+      run += c[i];
+    }
+  }
+  if (lane < p.splits)
+    p.seg_off[size_t(R) * p.splits + lane] =
+        uint32_t(kPage) * s_pre[wave][pf_split_first_chunk(lane, chunks, p.splits)];
+  if (lane == 0) p.tau[R] = t;
+}
+
+// Rows with more pages than registers hold: the same pair, by the radix
+// over the 64-bit pairs read from global memory, and the same offsets.
+__global__ __launch_bounds__(kPfSelWaves * 64) void pf_threshold_wide_kernel(PfParams p) {
+  __shared__ uint32_t s_hist[kPfSelWaves][256];
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int R = blockIdx.x * kPfSelWaves + wave;
+  if (R >= p.T * p.H_q) return;
+  const uint32_t* pm = p.pmax + size_t(R) * p.Ppad;
+  uint32_t present = 0;
+  for (int j = lane; j < p.P; j += 64) present += pm[j] ? 1u : 0u;
+  present = wave_sum(present);
+  uint64_t t;
+  if (p.k_eff == 0) {
+    t = ~0ull;
+  } else if (present <= uint32_t(p.k_eff)) {
+    t = 1ull;
+  } else {
+    auto visit = [&](auto&& fn) {
+      for (int j = lane; j < p.P; j += 64) {
+        const uint32_t key = pm[j];
+        fn(key ? (uint64_t(key) << 32) | uint32_t(~uint32_t(j)) : 0ull);
+      }
+    };
+    t = wave_kth(visit, uint32_t(p.k_eff), s_hist[wave]);
+  }
+  const int chunks = p.Ppad / kPfChunk;
+  uint32_t before = 0;  // pages at or above t in the ranges so far
+  for (int z = 0; z < p.splits; ++z) {
+    const int a = pf_split_first_chunk(z, chunks, p.splits) * kPfChunk;
+    const int b = min(p.P, pf_split_first_chunk(z + 1, chunks, p.splits) * kPfChunk);
+    uint32_t c = 0;
+    for (int j = a + lane; j < b; j += 64) c += pf_pair_at_least(pm[j], j, t) ? 1u : 0u;
+    c = wave_sum(c);
+    if (lane == 0) p.seg_off[size_t(R) * p.splits + z] = uint32_t(kPage) * before;
+    before += c;
+  }
+  if (lane == 0) p.tau[R] = t;
+}
+
+// One wave per row: the exact top k_eff of the row's candidates (the page
+// ranges' lists, in range order), ascending.
 __global__ __launch_bounds__(kPfSelWaves * 64) void pf_select_kernel(PfParams p) {
   __shared__ uint32_t s_hist[kPfSelWaves][256];
   __shared__ int32_t s_pos[kPfSelWaves][RA_PREFILL_MAX_K];
@@ -236,20 +653,33 @@ __global__ __launch_bounds__(kPfSelWaves * 64) void pf_select_kernel(PfParams p)
   int32_t* out = p.out_idx + size_t(R) * p.k;
   const uint32_t ke = uint32_t(p.k_eff);
   if (ke > 0) {
-    const uint32_t n = min(p.cnt[R], uint32_t(p.cap));
     const uint64_t* cl = p.cand + size_t(R) * p.cap;
-    auto get = [&](uint32_t i) -> uint64_t { return cl[i]; };
-    const uint64_t th = n > ke ? wave_kth(get, n, ke, s_hist[wave]) : 1ull;
+    const uint32_t* so = p.seg_off + size_t(R) * p.splits;
+    const uint32_t* sc = p.seg_cnt + size_t(R) * p.splits;
+    uint32_t n = 0;
+    for (int z = 0; z < p.splits; ++z) n += sc[z];
+    auto visit = [&](auto&& fn) {
+      for (int z = 0; z < p.splits; ++z) {
+        const uint32_t cnt = sc[z];
+        const uint64_t* b = cl + so[z];
+        for (uint32_t i = lane; i < cnt; i += 64) fn(b[i]);
+      }
+    };
+    const uint64_t th = n > ke ? wave_kth(visit, ke, s_hist[wave]) : 1ull;
     // the winners' positions, in list order
     uint32_t filled = 0;
-    for (uint32_t base = 0; base < n; base += 64) {
-      const uint32_t i = base + lane;
-      const uint64_t v = i < n ? cl[i] : 0ull;
-      const bool win = i < n && v >= th;
-      const uint64_t m = __ballot(win);
-      const uint32_t at = filled + uint32_t(__popcll(m & ((1ull << lane) - 1ull)));
-      if (win && at < ke) s_pos[wave][at] = int32_t(~uint32_t(v));
-      filled += uint32_t(__popcll(m));
+    for (int z = 0; z < p.splits; ++z) {
+      const uint32_t cnt = sc[z];
+      const uint64_t* b = cl + so[z];
+      for (uint32_t base = 0; base < cnt; base += 64) {
+        const uint32_t i = base + lane;
+        const uint64_t v = i < cnt ? b[i] : 0ull;
+        const bool win = i < cnt && v >= th;
+        const uint64_t m = __ballot(win);
+        const uint32_t at = filled + uint32_t(__popcll(m & ((1ull << lane) - 1ull)));
+        if (win && at < ke) s_pos[wave][at] = int32_t(~uint32_t(v));
+        filled += uint32_t(__popcll(m));
+      }
     }
     // ascending: each winner's rank is the number of smaller positions
     for (uint32_t i = lane; i < ke; i += 64) {
@@ -264,13 +694,12 @@ __global__ __launch_bounds__(kPfSelWaves * 64) void pf_select_kernel(PfParams p)
 
 // ---------------------------------------------------------------- launch
 template <int G>
-static void launch_pf_scores(const PfParams& p, bool filter, hipStream_t s) {
-  const unsigned row_blocks = unsigned((int64_t(p.T) * G + kPfRows - 1) / kPfRows);
-  const dim3 grid{row_blocks, unsigned(p.H_kv), unsigned(p.splits)};
+static void launch_pf_contract(const PfParams& p, bool filter, hipStream_t s) {
+  const dim3 grid{unsigned(p.H_kv) * unsigned(p.splits) * unsigned(p.row_blocks)};
   if (filter)
-    hipLaunchKernelGGL((pf_scores_kernel<G, true>), grid, dim3(kPfThreads), 0, s, p);
+    hipLaunchKernelGGL((pf_contract_kernel<G, true>), grid, dim3(kPfThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((pf_scores_kernel<G, false>), grid, dim3(kPfThreads), 0, s, p);
+    hipLaunchKernelGGL((pf_contract_kernel<G, false>), grid, dim3(kPfThreads), 0, s, p);
 }
 
 hipError_t launch_prefill(const PfParams& p, int first, int last, hipStream_t s) {
@@ -279,14 +708,20 @@ hipError_t launch_prefill(const PfParams& p, int first, int last, hipStream_t s)
   for (int st = first; st <= last; ++st) {
     if (st == 0 || st == 2) {
       switch (G) {
-        case 1: launch_pf_scores<1>(p, st == 2, s); break;
-        case 2: launch_pf_scores<2>(p, st == 2, s); break;
-        case 4: launch_pf_scores<4>(p, st == 2, s); break;
-        case 8: launch_pf_scores<8>(p, st == 2, s); break;
+        case 1: launch_pf_contract<1>(p, st == 2, s); break;
+        case 2: launch_pf_contract<2>(p, st == 2, s); break;
+        case 4: launch_pf_contract<4>(p, st == 2, s); break;
+        case 8: launch_pf_contract<8>(p, st == 2, s); break;
         default: return hipErrorInvalidValue;
       }
     } else if (st == 1) {
-      hipLaunchKernelGGL(pf_threshold_kernel, dim3(row_waves), dim3(kPfSelWaves * 64), 0, s, p);
+      const dim3 grid(row_waves), block(kPfSelWaves * 64);
+      if (p.Ppad <= 2048)
+        hipLaunchKernelGGL(pf_threshold_kernel<32>, grid, block, 0, s, p);
+      else if (p.Ppad <= 4096)
+        hipLaunchKernelGGL(pf_threshold_kernel<64>, grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL(pf_threshold_wide_kernel, grid, block, 0, s, p);
     } else {
       hipLaunchKernelGGL(pf_select_kernel, dim3(row_waves), dim3(kPfSelWaves * 64), 0, s, p);
     }

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <numeric>
 
 #include "ra.h"
 #include "ra_internal.h"
@@ -55,6 +56,7 @@ bool pf_layout(int32_t T, int32_t H_q, int32_t N, int32_t k, PfLayout* L) {
   const int64_t rows = int64_t(T) * H_q;
   if (rows > (int64_t(1) << 30)) return false;
   const int64_t P = (int64_t(N) + kPage - 1) / kPage;
+  const int64_t Ppad = (P + kPfChunk - 1) / kPfChunk * kPfChunk;
   const int64_t cap = int64_t(kPage) * k;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -62,9 +64,10 @@ bool pf_layout(int32_t T, int32_t H_q, int32_t N, int32_t k, PfLayout* L) {
     off = align256(off + bytes);
     return o;
   };
-  L->off_pmax = take(size_t(rows) * P * sizeof(uint32_t));
+  L->off_pmax = take(size_t(rows) * Ppad * sizeof(uint32_t));
   L->off_tau = take(size_t(rows) * sizeof(uint64_t));
-  L->off_cnt = take(size_t(rows) * sizeof(uint32_t));
+  L->off_seg_off = take(size_t(rows) * kPfMaxSplits * sizeof(uint32_t));
+  L->off_seg_cnt = take(size_t(rows) * kPfMaxSplits * sizeof(uint32_t));
   L->off_cand = take(size_t(rows) * cap * sizeof(uint64_t));
   L->total = off;
   return true;
@@ -334,14 +337,24 @@ ra_status ra_prefill_stages(const uint16_t* q, int32_t T, int32_t H_q,
   p.cap = kPage * k;
   p.pmax = reinterpret_cast<uint32_t*>(base + L.off_pmax);
   p.tau = reinterpret_cast<uint64_t*>(base + L.off_tau);
-  p.cnt = reinterpret_cast<uint32_t*>(base + L.off_cnt);
+  p.seg_off = reinterpret_cast<uint32_t*>(base + L.off_seg_off);
+  p.seg_cnt = reinterpret_cast<uint32_t*>(base + L.off_seg_cnt);
   p.cand = reinterpret_cast<uint64_t*>(base + L.off_cand);
   p.out_idx = out_idx;
-  // enough blocks to fill the GPU a few times over: split the pages
-  const int64_t row_blocks = (int64_t(T) * G + 127) / 128;
-  const int64_t want = 4 * int64_t(cu_count());
-  const int64_t have = row_blocks * kv->H_kv;
-  p.splits = int32_t(std::max<int64_t>(1, std::min<int64_t>(p.P, (want + have - 1) / have)));
+  p.Ppad = (p.P + kPfChunk - 1) / kPfChunk * kPfChunk;
+  // one contraction block per CU: split the page chunks over enough blocks
+  // to fill the GPU; the row blocks of one page range share an XCD (its L2)
+  // when the (KV head, range) pairs divide evenly over the eight XCDs
+  const int64_t chunks = p.Ppad / kPfChunk;
+  p.row_blocks = int32_t((int64_t(T) * G + kPfBlockRows - 1) / kPfBlockRows);
+  const int64_t have = int64_t(p.row_blocks) * kv->H_kv;
+  const int64_t S_max = std::min<int64_t>(chunks, kPfMaxSplits);
+  int64_t S = std::max<int64_t>(1, std::min<int64_t>(S_max, (cu_count() + have - 1) / have));
+  const int64_t step = 8 / std::gcd<int64_t>(kv->H_kv, 8);
+  const int64_t S8 = (S + step - 1) / step * step;
+  if (S8 <= S_max) S = S8;
+  p.splits = int32_t(S);
+  p.xcd_groups = (int64_t(kv->H_kv) * S) % 8 == 0 ? 1 : 0;
   if (launch_prefill(p, first_stage, last_stage, stream) != hipSuccess) return RA_ERR_HIP;
   return RA_OK;
 }

@@ -111,22 +111,31 @@ struct Params {
 };
 
 // Prefill top-k (prefill_topk.hip).
+constexpr int kPfChunk = 16;       // pages per page-maxima row segment
+constexpr int kPfBlockRows = 512;  // query rows (of one KV head) per contraction block
+constexpr int kPfMaxSplits = 64;   // page ranges per (KV head, row block), at most
+
 struct PfParams {
   const uint16_t* q;          // [T][H_q][128]
   const uint16_t* k_pool;
   const int32_t* block_table; // the sequence's row
   int32_t T, H_q, H_kv, N, P, num_pages;
+  int32_t Ppad;               // P rounded up to kPfChunk: row stride of pmax
   int32_t lo, hi;             // M = [lo, hi)
-  int32_t k, k_eff, cap, splits;
-  uint32_t* pmax;   // [T*H_q][P] largest score key per page over M (0: none)
+  int32_t k, k_eff, cap;
+  int32_t row_blocks;         // contraction row blocks per KV head
+  int32_t splits;             // page ranges per (KV head, row block), <= kPfMaxSplits
+  int32_t xcd_groups;         // 1: the row blocks of a page range share an XCD
+  uint32_t* pmax;   // [T*H_q][Ppad] largest score key per page over M (0: none)
   uint64_t* tau;    // [T*H_q] threshold pair (key << 32 | ~page)
-  uint32_t* cnt;    // [T*H_q] candidates
-  uint64_t* cand;   // [T*H_q][cap] candidates (key << 32 | ~n)
+  uint32_t* seg_off;  // [T*H_q][splits] first candidate slot of each page range
+  uint32_t* seg_cnt;  // [T*H_q][splits] candidates found in each page range
+  uint64_t* cand;   // [T*H_q][cap] candidates (key << 32 | ~n), by page range
   int32_t* out_idx; // [T][H_q][k]
 };
 
 struct PfLayout {
-  size_t off_pmax, off_tau, off_cnt, off_cand, total;
+  size_t off_pmax, off_tau, off_seg_off, off_seg_cnt, off_cand, total;
 };
 
 bool pf_layout(int32_t T, int32_t H_q, int32_t N, int32_t k, PfLayout* out);
