@@ -40,10 +40,14 @@ namespace ra {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kPfWaves = 8;
+#ifndef PF_WAVES
+#define PF_WAVES 8
+#endif
+constexpr int kPfWaves = PF_WAVES;
 constexpr int kPfThreads = kPfWaves * 64;
-constexpr int kPfQG = 2;                         // 32-row query groups per wave
-static_assert(kPfWaves * kPfQG * 32 == kPfBlockRows, "block rows");
+constexpr int kPfQG = kPfBlockRows / (kPfWaves * 32);  // 32-row query groups per wave
+constexpr int kPfWaveRows = kPfQG * 32;
+static_assert(kPfQG % 2 == 0 && kPfWaves * kPfWaveRows == kPfBlockRows, "block rows");
 constexpr int kPfRec = 128;  // score records a wave buffers before it sifts them (filter)
 constexpr int kPfPageChunks = kPage * kHeadDim * 2 / 16;    // 16-byte chunks per page: 1024
 constexpr int kPfLoads = kPfPageChunks / kPfThreads;         // per thread per page: 2
@@ -74,18 +78,25 @@ __device__ __forceinline__ float max16(const f32x16_t& c) {
   return fmaxf(fmaxf(fmaxf(a, b), fmaxf(d, e)), fmaxf(f, c[15]));
 }
 
+// This thread's share of one page of K, in flight. Named members passed by
+// value, not an array, so it stays in registers.
+struct PfStage {
+  uint4 a, b, c, d;
+};
+static_assert(kPfLoads == 2 || kPfLoads == 4, "two or four 16-byte loads per thread per page");
+
 struct PfLds {
   uint4 ring[2][kPfPageChunks];  // two pages of K, 16-byte chunks, swizzled
   union {
-    uint32_t pm[kPfWaves][64 * (kPfChunk + 1)];  // page-maxima keys, [query][page]
+    uint32_t pm[kPfWaves][kPfWaveRows * (kPfChunk + 1)];  // page-maxima keys, [row][page]
     struct {
       // a record: one lane's 16 scores of a tile whose maximum reached the
       // row's threshold, with (wave row << 24 | position of its first key)
       uint4 rec[kPfWaves][kPfRec][4];
       uint32_t meta[kPfWaves][kPfRec];
-      uint32_t cnt[kPfWaves][64];    // candidates per wave row in this page range
-      uint64_t tau[kPfWaves][64];    // per wave row: threshold pair
-      uint64_t base[kPfWaves][64];   // per wave row: first slot of the range's list
+      uint32_t cnt[kPfWaves][kPfWaveRows];   // candidates per wave row in this page range
+      uint64_t tau[kPfWaves][kPfWaveRows];   // per wave row: threshold pair
+      uint64_t base[kPfWaves][kPfWaveRows];  // per wave row: first slot of the range's list
     } f;
   } u;
 };
@@ -118,7 +129,7 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
   const int wave = tid >> 6;
   const int hl = lane >> 5;
   const int TG = p.T * G;
-  const int rw = rb * kPfBlockRows + wave * (kPfQG * 32);  // wave's first local row
+  const int rw = rb * kPfBlockRows + wave * kPfWaveRows;  // wave's first local row
 
   // B fragments: query row rw + 32 q + lane % 32, dims 16 s + 8 hl .. + 8
   bf16x8_t qf[kPfQG][8];
@@ -142,11 +153,12 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
       const uint64_t t = rv[q] ? p.tau[R[q]] : ~0ull;
       thr[q] = key2f(uint32_t(t >> 32));  // key 0: -inf, every score passes
       if (t == ~0ull) thr[q] = __uint_as_float(0x7FC00000u);  // nothing passes
-      // lane l keeps the wave row l (group l / 32, column l % 32)
-      if (q == hl) {
-        sm.u.f.cnt[wave][lane] = 0u;
-        sm.u.f.tau[wave][lane] = t;
-        sm.u.f.base[wave][lane] =
+      // lane l keeps the wave rows 64 i + l (group 2 i + l / 32, column l % 32)
+      if ((q & 1) == hl) {
+        const int wr = 32 * q + (lane & 31);
+        sm.u.f.cnt[wave][wr] = 0u;
+        sm.u.f.tau[wave][wr] = t;
+        sm.u.f.base[wave][wr] =
             rv[q] ? size_t(R[q]) * p.cap + p.seg_off[size_t(R[q]) * p.splits + z] : 0ull;
       }
     }
@@ -158,37 +170,51 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
   if (j0 >= j1) return;  // block-uniform
 
   const size_t head_off = size_t(g) * (kPage * kHeadDim);
-  static_assert(kPfLoads == 2, "two 16-byte loads per thread per page");
   // Issued unconditionally (past the range it re-reads the last page), so
   // every iteration has the same loads in flight and the waits before the
   // LDS writes cover only the page being written.
-  auto gload = [&](uint4& x0, uint4& x1, int j) {
+  auto gload = [&](int j) {
     const uint4* kb = reinterpret_cast<const uint4*>(
         p.k_pool + size_t(pf_page(p, min(j, j1 - 1))) * p.H_kv * (kPage * kHeadDim) + head_off);
-    x0 = kb[tid];
-    x1 = kb[tid + kPfThreads];
+    PfStage st;
+    st.a = kb[tid];
+    st.b = kb[tid + kPfThreads];
+    if constexpr (kPfLoads == 4) {
+      st.c = kb[tid + 2 * kPfThreads];
+      st.d = kb[tid + 3 * kPfThreads];
+    }
+    return st;
   };
   // chunk c % 16 of key row c / 16 goes to position (c % 16) ^ (row % 16)
-  const int c0 = tid, c1 = tid + kPfThreads;
-  const int w0 = (c0 >> 4) * 16 + ((c0 & 15) ^ ((c0 >> 4) & 15));
-  const int w1 = (c1 >> 4) * 16 + ((c1 & 15) ^ ((c1 >> 4) & 15));
-  auto lwrite = [&](const uint4& x0, const uint4& x1, int slot) {
-    sm.ring[slot][w0] = x0;
-    sm.ring[slot][w1] = x1;
+  auto pos = [&](int i) {
+    const int c = tid + kPfThreads * i;
+    return (c >> 4) * 16 + ((c & 15) ^ ((c >> 4) & 15));
   };
+  auto lwrite = [&](const PfStage st, int slot) {
+    sm.ring[slot][pos(0)] = st.a;
+    sm.ring[slot][pos(1)] = st.b;
+    if constexpr (kPfLoads == 4) {
+      sm.ring[slot][pos(2)] = st.c;
+      sm.ring[slot][pos(3)] = st.d;
+    }
+  };
+
+
 
   // Sift the buffered records, one per lane: every score whose pair
   // (score, page) reaches the row's threshold is appended to the row's list.
-  uint32_t n_rec = 0;  // wave-uniform
-  auto sift = [&]() {
-    for (uint32_t i0 = 0; i0 < n_rec; i0 += 64) {
-      const uint32_t i = i0 + lane;
-      if (i < n_rec) {
+  // The buffer is a ring: records r_head .. r_tail - 1 (mod kPfRec) wait;
+  // they are sifted 64 at a time (the rest at the end of the range).
+  uint32_t r_head = 0, r_tail = 0;  // wave-uniform
+  auto sift = [&](bool all) {
+    while (r_tail - r_head >= 64u || (all && r_tail != r_head)) {
+      const uint32_t n = min(64u, r_tail - r_head);
+      if (uint32_t(lane) < n) {
+        const uint32_t i = (r_head + lane) % uint32_t(kPfRec);
         const uint32_t meta = sm.u.f.meta[wave][i];
         const uint32_t qi = meta >> 24, n0 = meta & 0xFFFFFFu;
         const uint32_t npg = ~(n0 >> 6);  // ~page
         const uint64_t t = sm.u.f.tau[wave][qi];
-        uint64_t* list = p.cand + sm.u.f.base[wave][qi];
         float v[16];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -198,22 +224,30 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
           v[4 * c + 2] = __uint_as_float(x.z);
           v[4 * c + 3] = __uint_as_float(x.w);
         }
+        uint32_t okm = 0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t key = f2key(v[r]);
-          const bool ok = v[r] == v[r] && ((uint64_t(key) << 32) | npg) >= t;
-          const uint32_t at = atomicAdd(&sm.u.f.cnt[wave][qi], ok ? 1u : 0u);
-          const uint32_t n = n0 + uint32_t((r >> 2) * 8 + (r & 3));
-          if (ok) list[at] = (uint64_t(key) << 32) | uint32_t(~n);
+          const bool ok = v[r] == v[r] && ((uint64_t(f2key(v[r])) << 32) | npg) >= t;
+          okm |= ok ? (1u << r) : 0u;
+        }
+        // one reservation per record, then its keys in order
+        uint32_t at = atomicAdd(&sm.u.f.cnt[wave][qi], uint32_t(__popc(okm)));
+        uint64_t* list = p.cand + sm.u.f.base[wave][qi];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (okm & (1u << r)) {
+            const uint32_t pos = n0 + uint32_t((r >> 2) * 8 + (r & 3));
+            list[at++] = (uint64_t(f2key(v[r])) << 32) | uint32_t(~pos);
+          }
         }
       }
+      r_head += n;
     }
-    n_rec = 0;
   };
   auto pm_flush = [&](int cs) {
     // rows of this wave x pages cs .. cs + 15: four lanes per row, 16 bytes each
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kPfWaveRows / 16; ++i) {
       const int qi = 16 * i + (lane >> 2);
       const int r = rw + qi;
       if (r < TG) {
@@ -273,9 +307,10 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
           const bool hit = max16(acc[q]) >= thr[q];
           const uint64_t m = __ballot(hit);
           if (m) {
-            if (n_rec + 64 > uint32_t(kPfRec)) sift();
+            if (r_tail - r_head > uint32_t(kPfRec - 64)) sift(false);
             if (hit) {
-              const uint32_t at = n_rec + uint32_t(__popcll(m & ((1ull << lane) - 1ull)));
+              const uint32_t at =
+                  (r_tail + uint32_t(__popcll(m & ((1ull << lane) - 1ull)))) % uint32_t(kPfRec);
 #pragma unroll
               for (int c = 0; c < 4; ++c)
                 sm.u.f.rec[wave][at][c] = uint4{__float_as_uint(acc[q][4 * c]), __float_as_uint(acc[q][4 * c + 1]),
@@ -283,46 +318,52 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
               sm.u.f.meta[wave][at] = (uint32_t(32 * q + (lane & 31)) << 24) |
                                       uint32_t(nb + tile * 32 + hl * 4);
             }
-            n_rec += uint32_t(__popcll(m));
+            r_tail += uint32_t(__popcll(m));
           }
         }
       }
     }
     if constexpr (!FILTER) {
       // both lane halves hold 32 of the page's keys; lane l then records
-      // query row l of the wave (group l / 32)
+      // the wave rows 64 i + l (group 2 i + l / 32)
 #pragma unroll
       for (int q = 0; q < kPfQG; ++q) pm[q] = fmaxf(pm[q], __shfl_xor(pm[q], 32));
-      const float mv = hl ? pm[1] : pm[0];
-      sm.u.pm[wave][lane * (kPfChunk + 1) + (j & (kPfChunk - 1))] = mv == -INFINITY ? 0u : f2key(mv);
+#pragma unroll
+      for (int i = 0; i < kPfQG / 2; ++i) {
+        const float mv = hl ? pm[2 * i + 1] : pm[2 * i];
+        sm.u.pm[wave][(64 * i + lane) * (kPfChunk + 1) + (j & (kPfChunk - 1))] =
+            mv == -INFINITY ? 0u : f2key(mv);
+      }
       if ((j & (kPfChunk - 1)) == kPfChunk - 1 || j == j1 - 1) pm_flush(j & ~(kPfChunk - 1));
     }
   };
 
-  uint4 sa0, sa1, sb0, sb1;
-  gload(sa0, sa1, j0);
-  gload(sb0, sb1, j0 + 1);
-  lwrite(sa0, sa1, 0);
-  gload(sa0, sa1, j0 + 2);
+  PfStage sa = gload(j0);
+  PfStage sb = gload(j0 + 1);
+  lwrite(sa, 0);
+  sa = gload(j0 + 2);
   __syncthreads();
   for (int j = j0; j < j1; j += 2) {
     // page j is in ring slot 0, page j + 1 in sb, page j + 2 in sa
-    if (j + 1 < j1) lwrite(sb0, sb1, 1);
-    gload(sb0, sb1, j + 3);
+    if (j + 1 < j1) lwrite(sb, 1);
+    sb = gload(j + 3);
     compute(j, 0);
     __syncthreads();
     if (j + 1 >= j1) break;
-    if (j + 2 < j1) lwrite(sa0, sa1, 0);
-    gload(sa0, sa1, j + 4);
+    if (j + 2 < j1) lwrite(sa, 0);
+    sa = gload(j + 4);
     compute(j + 1, 1);
     __syncthreads();
   }
   if constexpr (FILTER) {
-    sift();
-    // lane l: the wave's query row l (group l / 32, column l % 32)
-    const bool valid = hl ? rv[1] : rv[0];
-    const int Rl = hl ? R[1] : R[0];
-    if (valid) p.seg_cnt[size_t(Rl) * p.splits + z] = sm.u.f.cnt[wave][lane];
+    sift(true);
+    // lane l: the wave rows 64 i + l (group 2 i + l / 32, column l % 32)
+#pragma unroll
+    for (int i = 0; i < kPfQG / 2; ++i) {
+      const bool valid = hl ? rv[2 * i + 1] : rv[2 * i];
+      const int Rl = hl ? R[2 * i + 1] : R[2 * i];
+      if (valid) p.seg_cnt[size_t(Rl) * p.splits + z] = sm.u.f.cnt[wave][64 * i + lane];
+    }
   }
 }
 
