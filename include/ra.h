@@ -212,7 +212,9 @@ size_t ra_prefill_workspace_bytes(int32_t T, int32_t H_q, int32_t N, int32_t k);
 /*
  * For every prefill query row t and query head h: the exact top-k keys of
  * one sequence by z = q . k / sqrt(128), over M = [n_sink, N - window) as in
- * the decode step, ties to the lower position. This is the first step of the
+ * the decode step, ties to the lower position. Keys are ranked by q . k in
+ * fp32 (bf16 products, fp32 MFMA accumulation): the positive factor does
+ * not change the order. This is the first step of the
  * slides' index frame ("Prefill queries teach the key graph what matters":
  * prefill queries find their exact top-k keys on the GPU, and each query is
  * linked to those keys). No causal cut is applied: every row is linked to
@@ -239,6 +241,10 @@ ra_status ra_prefill_topk(const uint16_t* q, int32_t T, int32_t H_q,
 /*
  * The kernels of ra_prefill_topk, in launch order; ra_prefill_stages runs a
  * contiguous sub-range with the same arguments (as ra_decode_stages does).
+ * A stage reads what the stages before it left in the workspace, so the
+ * ranges must be run in order on the same workspace. first_stage >
+ * last_stage, or either outside [0, RA_PF_STAGE_COUNT), returns
+ * RA_ERR_INVALID_ARGUMENT.
  */
 typedef enum ra_prefill_stage {
   RA_PF_STAGE_MAXIMA = 0,    /* contraction 1: largest score per (row, page) */
