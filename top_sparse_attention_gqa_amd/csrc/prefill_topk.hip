@@ -85,8 +85,12 @@ struct PfStage {
 };
 static_assert(kPfLoads == 2 || kPfLoads == 4, "two or four 16-byte loads per thread per page");
 
+struct PfFrags {
+  bf16x8_t a[8];  // one tile's A fragments (32 keys x 128 dims)
+};
+
 struct PfLds {
-  uint4 ring[2][kPfPageChunks];  // two pages of K, 16-byte chunks, swizzled
+  uint4 ring[4][kPfPageChunks];  // four pages of K, 16-byte chunks, swizzled
   union {
     uint32_t pm[kPfWaves][kPfWaveRows * (kPfChunk + 1)];  // page-maxima keys, [row][page]
     struct {
@@ -263,96 +267,151 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
     }
   };
 
+  // The 8 A fragments of one tile: keys half * 32 + lane % 32 of the page in
+  // ring slot `slot`, dims 16 s + 8 hl .. + 8.
+  auto frags = [&](int slot, int half) {
+    PfFrags f;
+    const int kr = half * 32 + (lane & 31);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      f.a[s] = *reinterpret_cast<const bf16x8_t*>(&sm.ring[slot][kr * 16 + ((2 * s + hl) ^ (kr & 15))]);
+    return f;
+  };
+  auto mma = [&](const PfFrags& f, f32x16_t (&acc)[kPfQG]) {
+#pragma unroll
+    for (int q = 0; q < kPfQG; ++q) {
+      acc[q] = f32x16_t{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[s], qf[q][s], acc[q], 0, 0, 0);
+    }
+  };
+  // Keys outside M (or past N) become NaN: ignored by the maxima, never at
+  // or above a threshold. nt: position of the tile's first key.
+  auto mask = [&](f32x16_t (&acc)[kPfQG], int nt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int n = nt + tile_row(r, lane);
+      if (n < p.lo || n >= p.hi) {
+#pragma unroll
+        for (int q = 0; q < kPfQG; ++q) acc[q][r] = __uint_as_float(0x7FC00000u);
+      }
+    }
+  };
+  // The tile's scores: into the page maxima pm, or (filter) a lane whose 16
+  // scores of a group reach its row's threshold buffers them as a record.
+  auto tile_out = [&](const f32x16_t (&acc)[kPfQG], int nt, float (&pm)[kPfQG]) {
+    if constexpr (!FILTER) {
+#pragma unroll
+      for (int q = 0; q < kPfQG; ++q) pm[q] = fmaxf(pm[q], max16(acc[q]));
+    } else {
+#pragma unroll
+      for (int q = 0; q < kPfQG; ++q) {
+        const bool hit = max16(acc[q]) >= thr[q];
+        const uint64_t m = __ballot(hit);
+        if (m) {
+          if (r_tail - r_head > uint32_t(kPfRec - 64)) sift(false);
+          if (hit) {
+            const uint32_t at =
+                (r_tail + uint32_t(__popcll(m & ((1ull << lane) - 1ull)))) % uint32_t(kPfRec);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              sm.u.f.rec[wave][at][c] = uint4{__float_as_uint(acc[q][4 * c]), __float_as_uint(acc[q][4 * c + 1]),
+                                              __float_as_uint(acc[q][4 * c + 2]), __float_as_uint(acc[q][4 * c + 3])};
+            sm.u.f.meta[wave][at] = (uint32_t(32 * q + (lane & 31)) << 24) | uint32_t(nt + hl * 4);
+          }
+          r_tail += uint32_t(__popcll(m));
+        }
+      }
+    }
+  };
+  // Page j's maxima: both lane halves hold 32 of the page's keys; lane l
+  // then records the wave rows 64 i + l (group 2 i + l / 32).
+  auto page_out = [&](float (&pm)[kPfQG], int j) {
+#pragma unroll
+    for (int q = 0; q < kPfQG; ++q) pm[q] = fmaxf(pm[q], __shfl_xor(pm[q], 32));
+#pragma unroll
+    for (int i = 0; i < kPfQG / 2; ++i) {
+      const float mv = hl ? pm[2 * i + 1] : pm[2 * i];
+      sm.u.pm[wave][(64 * i + lane) * (kPfChunk + 1) + (j & (kPfChunk - 1))] =
+          mv == -INFINITY ? 0u : f2key(mv);
+    }
+  };
+  auto chunk_end = [&](int j) { return (j & (kPfChunk - 1)) == kPfChunk - 1 || j == j1 - 1; };
+
+  // One page; keys outside M are masked on pages at the edges of M.
   auto compute = [&](int j, int slot) {
-    const int nb = j * kPage;
-    const bool full = nb >= p.lo && nb + kPage <= p.hi;
+    const bool full = j * kPage >= p.lo && (j + 1) * kPage <= p.hi;
     float pm[kPfQG];
 #pragma unroll
     for (int q = 0; q < kPfQG; ++q) pm[q] = -INFINITY;
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      const int kr = tile * 32 + (lane & 31);
-      bf16x8_t a[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        a[s] = *reinterpret_cast<const bf16x8_t*>(&sm.ring[slot][kr * 16 + ((2 * s + hl) ^ (kr & 15))]);
+    for (int half = 0; half < 2; ++half) {
       f32x16_t acc[kPfQG];
-#pragma unroll
-      for (int q = 0; q < kPfQG; ++q) {
-        acc[q] = f32x16_t{};
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-          acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], qf[q][s], acc[q], 0, 0, 0);
-      }
-      if (!full) {
-        // keys outside M (or past N) become NaN: ignored by the maxima,
-        // never at or above a threshold
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int n = nb + tile * 32 + tile_row(r, lane);
-          if (n < p.lo || n >= p.hi) {
-#pragma unroll
-            for (int q = 0; q < kPfQG; ++q) acc[q][r] = __uint_as_float(0x7FC00000u);
-          }
-        }
-      }
-      if constexpr (!FILTER) {
-#pragma unroll
-        for (int q = 0; q < kPfQG; ++q) pm[q] = fmaxf(pm[q], max16(acc[q]));
-      } else {
-        // a lane whose 16 scores of a group reach its row's threshold
-        // buffers them as a record
-#pragma unroll
-        for (int q = 0; q < kPfQG; ++q) {
-          const bool hit = max16(acc[q]) >= thr[q];
-          const uint64_t m = __ballot(hit);
-          if (m) {
-            if (r_tail - r_head > uint32_t(kPfRec - 64)) sift(false);
-            if (hit) {
-              const uint32_t at =
-                  (r_tail + uint32_t(__popcll(m & ((1ull << lane) - 1ull)))) % uint32_t(kPfRec);
-#pragma unroll
-              for (int c = 0; c < 4; ++c)
-                sm.u.f.rec[wave][at][c] = uint4{__float_as_uint(acc[q][4 * c]), __float_as_uint(acc[q][4 * c + 1]),
-                                                __float_as_uint(acc[q][4 * c + 2]), __float_as_uint(acc[q][4 * c + 3])};
-              sm.u.f.meta[wave][at] = (uint32_t(32 * q + (lane & 31)) << 24) |
-                                      uint32_t(nb + tile * 32 + hl * 4);
-            }
-            r_tail += uint32_t(__popcll(m));
-          }
-        }
-      }
+      mma(frags(slot, half), acc);
+      if (!full) mask(acc, j * kPage + half * 32);
+      tile_out(acc, j * kPage + half * 32, pm);
     }
     if constexpr (!FILTER) {
-      // both lane halves hold 32 of the page's keys; lane l then records
-      // the wave rows 64 i + l (group 2 i + l / 32)
+      page_out(pm, j);
+      if (chunk_end(j)) pm_flush(j & ~(kPfChunk - 1));
+    }
+  };
+  // Pages j and j + 1, both wholly inside M: four tiles in straight-line
+  // code, each tile's fragments read while the previous tile's MFMAs run.
+  // Odd waves take the two pages in the other order, so the waves do not
+  // all read the same fragments at once.
+  auto compute_pair = [&](int j, int s0) {
+    const int odd = wave & 1;
+    const int pa = j + odd, pb = j + 1 - odd;
+    const int sa_ = s0 + odd, sb_ = s0 + 1 - odd;
+    float pmA[kPfQG], pmB[kPfQG];
 #pragma unroll
-      for (int q = 0; q < kPfQG; ++q) pm[q] = fmaxf(pm[q], __shfl_xor(pm[q], 32));
-#pragma unroll
-      for (int i = 0; i < kPfQG / 2; ++i) {
-        const float mv = hl ? pm[2 * i + 1] : pm[2 * i];
-        sm.u.pm[wave][(64 * i + lane) * (kPfChunk + 1) + (j & (kPfChunk - 1))] =
-            mv == -INFINITY ? 0u : f2key(mv);
-      }
-      if ((j & (kPfChunk - 1)) == kPfChunk - 1 || j == j1 - 1) pm_flush(j & ~(kPfChunk - 1));
+    for (int q = 0; q < kPfQG; ++q) pmA[q] = pmB[q] = -INFINITY;
+    f32x16_t acc[kPfQG];
+    PfFrags f = frags(sa_, 0);
+    PfFrags g = frags(sa_, 1);
+    mma(f, acc);
+    tile_out(acc, pa * kPage, pmA);
+    f = frags(sb_, 0);
+    mma(g, acc);
+    tile_out(acc, pa * kPage + 32, pmA);
+    g = frags(sb_, 1);
+    mma(f, acc);
+    tile_out(acc, pb * kPage, pmB);
+    mma(g, acc);
+    tile_out(acc, pb * kPage + 32, pmB);
+    if constexpr (!FILTER) {
+      page_out(pmA, pa);
+      page_out(pmB, pb);
+      if (chunk_end(j + 1)) pm_flush(j & ~(kPfChunk - 1));
     }
   };
 
+
+  // Ring of four pages: pages j, j + 1 are computed between two barriers
+  // while pages j + 2, j + 3 wait in registers to be written.
   PfStage sa = gload(j0);
   PfStage sb = gload(j0 + 1);
   lwrite(sa, 0);
+  lwrite(sb, 1);
   sa = gload(j0 + 2);
+  sb = gload(j0 + 3);
   __syncthreads();
   for (int j = j0; j < j1; j += 2) {
-    // page j is in ring slot 0, page j + 1 in sb, page j + 2 in sa
-    if (j + 1 < j1) lwrite(sb, 1);
-    sb = gload(j + 3);
-    compute(j, 0);
-    __syncthreads();
-    if (j + 1 >= j1) break;
-    if (j + 2 < j1) lwrite(sa, 0);
+    const int s0 = j & 3;  // j0 is a multiple of 16
+    if (j + 2 < j1) lwrite(sa, (j + 2) & 3);
+    if (j + 3 < j1) lwrite(sb, (j + 3) & 3);
     sa = gload(j + 4);
-    compute(j + 1, 1);
+    sb = gload(j + 5);
+    // (the filter's record path leaves no registers for the pair's
+    // prefetched fragments: it takes the pages one by one)
+    if (!FILTER && j + 1 < j1 && j * kPage >= p.lo && (j + 2) * kPage <= p.hi) {
+      compute_pair(j, s0);
+    } else {
+      compute(j, s0);
+      if (j + 1 < j1) compute(j + 1, s0 + 1);
+    }
     __syncthreads();
   }
   if constexpr (FILTER) {
