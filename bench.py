@@ -52,6 +52,7 @@ WORKLOAD_TEXT = {
     "C3_2": "Llama-3-8B layer: H_q=32, H_kv=8, d=128, N=1048576, k=2% (20971), n_sink=128, window=512",
     "C3_3": "Llama-3-8B layer: H_q=32, H_kv=8, d=128, N=1048576, k=3% (31457), n_sink=128, window=512",
     "C4": "16 ragged sequences (N uniform in [32768, 131072]) of a Llama-3-8B layer, 64-token pages in shuffled order, k=2% of each length",
+    "C5P": "C5 with a pyramid-shaped per-layer budget: k_l falls linearly with depth (slope 0.5, 1.5 to 0.5 times the mean) around the uniform 1% of the current length, with the same total",
     "P1": "prefill exact top-k: T=1024 query rows of a Llama-3-8B layer (H_q=32, H_kv=8, d=128) against N=131072 keys, k=100, n_sink=128, window=512",
     "C5": "32 Llama-3-8B layers (H_q=32, H_kv=8, d=128) at N=1048576, k=1% of the current length, KV of every layer resident in HBM; each token step appends one K/V row per layer and runs the decode step of all 32 layers",
 }
@@ -178,7 +179,7 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    model = args.workload == "C5"
+    model = args.workload in ("C5", "C5P")
     prefill = args.workload == "P1"
     if args.steps is None:
         args.steps = 1000 if model else (50 if prefill else 200)
@@ -333,7 +334,8 @@ def run_layer(args):
 
 def run_model(args):
     """C5: every token step appends one K/V row to each of the 32 layers and
-    runs each layer's decode step; value = ms per token step."""
+    runs each layer's decode step; value = ms per token step. C5P: the same
+    with per-layer budgets from ra_layer_budgets (slope 0.5)."""
     import numpy as np
     import torch
 
@@ -352,11 +354,14 @@ def run_model(args):
                for l, L in enumerate(layers)]
     lens = [N0 + s + 1 for s in range(total)]          # length after the append
     ks = [c.k_for(n) for n in lens]
+    slope = PYRAMID_SLOPE_PERMILLE if args.workload == "C5P" else 0
+    # per (token step, layer) budgets: the uniform k, or its pyramid schedule
+    k_tab = [ra.layer_budgets(n_layers, k, slope) for k in ks]
     seq_all = torch.tensor(lens, dtype=torch.int32, device=dev).view(total, 1)
     pos_all = (seq_all - 1).contiguous()
-    k_all = torch.tensor(ks, dtype=torch.int32, device=dev).view(total, 1)
+    k_all = torch.tensor(k_tab, dtype=torch.int32, device=dev).view(total, n_layers, 1)
     max_seq_len = N0 + total
-    k_max = max(ks)
+    k_max = max(max(r) for r in k_tab)
     ws = ra.alloc_workspace(1, H_q, H_kv, max_seq_len, k_max, device=dev)
     outs = [torch.empty(1, H_q, 128, device=dev) for _ in layers]
     lses = [torch.empty(1, H_q, device=dev) for _ in layers]
@@ -369,7 +374,7 @@ def run_model(args):
         for l in range(n_layers):
             q, kn, vn = streams[l][0][s], streams[l][1][s], streams[l][2][s]
             ra.kv_append(kvs[l], kn, vn, pos_all[s])
-            a = (q, kvs[l], seq_all[s], max_seq_len, k_all[s], k_max, c.n_sink, c.window,
+            a = (q, kvs[l], seq_all[s], max_seq_len, k_all[s, l], k_max, c.n_sink, c.window,
                  outs[l], lses[l], idxs[l], ws)
             if ev is None:
                 ra.decode_step(*a)
@@ -399,8 +404,8 @@ def run_model(args):
     n_last = lens[-1]
     kb = vb = small = 0
     for l in range(n_layers):
-        a, b_, sm = algorithmic_bytes(c, [n_last], [ks[-1]], idxs[l].cpu().numpy(), c.n_sink,
-                                      c.window)
+        a, b_, sm = algorithmic_bytes(c, [n_last], [k_tab[-1][l]], idxs[l].cpu().numpy(),
+                                      c.n_sink, c.window)
         kb, vb, small = kb + a, vb + b_, small + sm + 2 * H_kv * 256 * 2
     step_bytes = kb + vb + small
     n_mean = N0 + args.warmup + (args.steps + 1) / 2.0
@@ -428,9 +433,10 @@ def run_model(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded: OOD q vs K, 64 planted needles per query head, x4 sink keys)",
-        "config": {"workload": f"C5: {WORKLOAD_TEXT['C5']}", "n_layers": n_layers,
+        "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}", "n_layers": n_layers,
                    "B": 1, "H_q": H_q, "H_kv": H_kv, "head_dim": 128,
                    "seq_len": [N0 + args.warmup + 1, lens[-1]], "k": [ks[args.warmup], ks[-1]],
+                   "k_per_layer_last_step": k_tab[-1],
                    "n_sink": c.n_sink, "window": c.window, "accumulate": "fp32",
                    "kv_bytes_resident": int(sum(L.k_pool.numel() * 4 for L in layers))},
         "kv_tokens_per_s": round(n_layers * n_mean / (ms_per_step * 1e-3), 1),
@@ -453,7 +459,8 @@ def run_model(args):
 # prefill exact top-k (the key-graph build's input): one "step" is one
 # ra_prefill_topk call over T query rows
 PF_T, PF_H_Q, PF_H_KV, PF_N, PF_K, PF_SINK, PF_WINDOW = 1024, 32, 8, 131072, 100, 128, 512
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PYRAMID_SLOPE_PERMILLE = 500  # C5P: budgets from 1.5x to 0.5x the mean  # MI355X published dense bf16 matrix peak
 
 
 def prefill_cpu_baseline(L, Q, budget_s=12.0):

@@ -261,6 +261,29 @@ ra_status ra_prefill_stages(const uint16_t* q, int32_t T, int32_t H_q,
                             int32_t first_stage, int32_t last_stage,
                             hipStream_t stream);
 
+/* ------------------------------------------------------------------ */
+/* Per-layer retrieval budgets.                                         */
+/* ------------------------------------------------------------------ */
+
+/*
+ * A pyramid-shaped schedule of per-layer budgets with the total of a uniform
+ * budget k_mean per layer (slides, frame "Extra experiments show where
+ * budget matters": a PyramidKV-style layer budget, more keys for the lower
+ * layers): k_l = k_mean (1 + s (L - 1 - 2 l) / (L - 1)) for layers
+ * l = 0 .. L - 1 with slope s = slope_permille / 1000 in [0, 1], rounded to
+ * integers that sum to L k_mean exactly (each layer gets the floor; the
+ * L k_mean - sum of floors layers with the largest fractional parts get one
+ * more, ties to the lower layer). s = 0 is the uniform budget. Host
+ * arithmetic only: each layer's decode step then takes its k_l (the
+ * kernels are unchanged).
+ *  n_layers: 1 .. 4096; k_mean >= 0; slope_permille in [0, 1000].
+ *  k_out:    host int32 [n_layers].
+ * Returns RA_ERR_INVALID_ARGUMENT for arguments outside these ranges or a
+ * null k_out.
+ */
+ra_status ra_layer_budgets(int32_t n_layers, int32_t k_mean, int32_t slope_permille,
+                           int32_t* k_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,7 @@ from .ra_oracle import (  # noqa: F401
     decode_head,
     dense,
     kv_bytes_per_token,
+    layer_budgets,
     merge,
     partial,
     prefill_topk,

@@ -16,6 +16,8 @@ Source pages (cited by title and slide/equation, never by line):
   - backup frame "the normalization identity": N_S, Z_S, and that merging
     disjoint partials gives the exact softmax on their union.
   - frame "The bottleneck is both storage and KV access": Table 1, KV capacity.
+  - frame "Extra experiments show where budget matters": a PyramidKV-style
+    per-layer budget (more keys for the lower layers).
 
 Readings of points the pages leave open:
 
@@ -32,6 +34,8 @@ Every quantity is float64 after exact widening of the bf16 inputs.
 """
 
 from __future__ import annotations
+
+from fractions import Fraction
 
 import math
 
@@ -303,3 +307,33 @@ def prefill_topk(Q, K, k: int, n_sink: int, window: int) -> np.ndarray:
 def kv_bytes_per_token(n_layers: int, H_kv: int, head_dim: int, elem_bytes: int) -> int:
     """Bytes of K plus V per cached token across all layers: 2*L*H_kv*d*b."""
     return 2 * n_layers * H_kv * head_dim * elem_bytes
+
+
+# --------------------------------------------------------------------------
+# Per-layer budgets: "Extra experiments show where budget matters" (a
+# PyramidKV-style layer budget). The slides give no formula; the reading
+# here is a budget falling linearly with depth that keeps the total of the
+# uniform budget.
+# --------------------------------------------------------------------------
+
+def layer_budgets(n_layers: int, k_mean: int, slope_permille: int) -> list:
+    """Integer budgets k_0 >= ... >= k_{L-1} summing to L * k_mean.
+
+    The exact budget of layer l is k_mean * (1 + s * (L-1-2l) / (L-1)),
+    s = slope_permille / 1000 (a straight line through k_mean at the middle
+    layer; s = 0 is uniform). Each layer gets its floor; the layers with
+    the largest fractional parts get one more until the total is reached,
+    ties to the lower layer.
+    """
+    L = int(n_layers)
+    if L == 1:
+        return [int(k_mean)]
+    s = Fraction(int(slope_permille), 1000)
+    exact = [Fraction(int(k_mean)) * (1 + s * Fraction(L - 1 - 2 * l, L - 1)) for l in range(L)]
+    ks = [math.floor(x) for x in exact]
+    short = L * int(k_mean) - sum(ks)
+    by_fraction = sorted(range(L), key=lambda l: (-(exact[l] - ks[l]), l))
+    for l in by_fraction[:short]:
+        ks[l] += 1
+    return ks
+

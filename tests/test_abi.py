@@ -204,3 +204,19 @@ def test_prefill_stage_range_validation():
     assert _lib.raw.ra_prefill_stages(*args, 2, 1, None) == ra.RA_ERR_INVALID_ARGUMENT
     assert _lib.raw.ra_prefill_stages(*args, -1, 1, None) == ra.RA_ERR_INVALID_ARGUMENT
     assert _lib.raw.ra_prefill_stages(*args, 0, 4, None) == ra.RA_ERR_INVALID_ARGUMENT
+
+
+def test_layer_budgets_match_the_oracle():
+    # host arithmetic of the library against the oracle's exact rationals
+    import oracle
+    for L in (1, 2, 3, 5, 8, 31, 32, 80):
+        for k in (0, 1, 7, 100, 10485, 31457):
+            for slope in (0, 1, 333, 500, 999, 1000):
+                assert ra.layer_budgets(L, k, slope) == oracle.layer_budgets(L, k, slope), (L, k, slope)
+
+
+def test_layer_budgets_reject_bad_arguments():
+    buf = (ctypes.c_int32 * 4)()
+    for args in ((0, 5, 0), (4, -1, 0), (4, 5, -1), (4, 5, 1001), (5000, 5, 0)):
+        assert _lib.raw.ra_layer_budgets(*args, ctypes.cast(buf, ctypes.c_void_p)) == ra.RA_ERR_INVALID_ARGUMENT
+    assert _lib.raw.ra_layer_budgets(4, 5, 0, None) == ra.RA_ERR_INVALID_ARGUMENT

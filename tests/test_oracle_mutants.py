@@ -3,6 +3,7 @@ one pin in test_oracle_pins.py fails for each: the pins are strong enough
 to catch a dropped term, a wrong sign or index, or a transposed operand."""
 
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -91,7 +92,39 @@ def _prefill_whole_range(Q, K, k, n_sink, window):
     return _REAL_PREFILL(Q, K, k, 0, 0)
 
 
+_REAL_BUDGETS = ro.layer_budgets
+
+
+def _budgets_rising(L, k, slope):
+    # more keys for the upper layers instead of the lower ones
+    return _REAL_BUDGETS(L, k, slope)[::-1]
+
+
+def _budgets_floor_only(L, k, slope):
+    # the rounding that restores the total is dropped
+    if L == 1:
+        return [k]
+    s = Fraction(slope, 1000)
+    return [math.floor(Fraction(k) * (1 + s * Fraction(L - 1 - 2 * l, L - 1))) for l in range(L)]
+
+
+def _budgets_ties_high(L, k, slope):
+    # extra units go to the higher layer on equal fractional parts
+    if L == 1:
+        return [k]
+    s = Fraction(slope, 1000)
+    exact = [Fraction(k) * (1 + s * Fraction(L - 1 - 2 * l, L - 1)) for l in range(L)]
+    ks = [math.floor(x) for x in exact]
+    order = sorted(range(L), key=lambda l: (-(exact[l] - ks[l]), -l))
+    for l in order[:L * k - sum(ks)]:
+        ks[l] += 1
+    return ks
+
+
 MUTANTS = {
+    "budgets_rising": ("layer_budgets", _budgets_rising),
+    "budgets_floor_only": ("layer_budgets", _budgets_floor_only),
+    "budgets_ties_high": ("layer_budgets", _budgets_ties_high),
     "prefill_rows_reversed": ("prefill_topk", _prefill_rows_reversed),
     "prefill_whole_range": ("prefill_topk", _prefill_whole_range),
     "scores_no_scale": ("scores", _scores_no_scale),

@@ -378,3 +378,51 @@ def test_prefill_topk_rows_are_independent_and_planted_keys_win():
     for t in range(T):
         assert got[t, 1, 0] == 7 + t
         assert got[t, 0, 0] == 0
+
+
+# --------------------------------------------------------------------------
+# Per-layer budgets (slides, frame "Extra experiments show where budget
+# matters": a PyramidKV-style layer budget). Pinned by the properties the
+# reading fixes and by brute force over every rounding on small cases.
+# --------------------------------------------------------------------------
+
+BUDGET_CASES = [(1, 7, 300), (2, 5, 1000), (3, 10, 500), (4, 60, 600), (5, 3, 250),
+                (7, 11, 999), (8, 0, 700), (32, 10485, 500), (32, 20971, 0), (6, 9, 1000)]
+
+
+@pytest.mark.parametrize("L,k,slope", BUDGET_CASES)
+def test_layer_budgets_keep_the_total_and_fall_with_depth(L, k, slope):
+    ks = oracle.layer_budgets(L, k, slope)
+    assert len(ks) == L and all(isinstance(x, int) and x >= 0 for x in ks)
+    assert sum(ks) == L * k
+    assert all(a >= b for a, b in zip(ks, ks[1:]))
+    if slope == 0 or L == 1:
+        assert ks == [k] * L
+    # the line through k at the middle layer: layers l and L-1-l pair up
+    for l in range(L):
+        assert abs(ks[l] + ks[L - 1 - l] - 2 * k) <= 1
+
+
+def test_layer_budgets_endpoints_of_the_steepest_schedule():
+    # slope 1: the first layer gets twice the mean and the last none
+    assert oracle.layer_budgets(5, 8, 1000) == [16, 12, 8, 4, 0]
+    assert oracle.layer_budgets(2, 5, 1000) == [10, 0]
+    assert oracle.layer_budgets(3, 6, 500) == [9, 6, 3]
+
+
+@pytest.mark.parametrize("L,k,slope", [(3, 5, 333), (4, 7, 450), (5, 3, 250), (6, 4, 700),
+                                       (4, 1, 999), (5, 2, 100), (4, 1, 500), (6, 3, 500)])
+def test_layer_budgets_round_like_brute_force(L, k, slope):
+    # among all integer vectors with the total L*k and every entry within 1 of
+    # the exact line, the one closest to it (least squares), then the one
+    # that gives the extra units to the lowest layers
+    exact = [Fraction(k) * (1 + Fraction(slope, 1000) * Fraction(L - 1 - 2 * l, L - 1))
+             for l in range(L)]
+    best = None
+    for v in itertools.product(*[range(math.floor(x) - 1, math.ceil(x) + 2) for x in exact]):
+        if sum(v) != L * k or min(v) < 0:
+            continue
+        key = (sum((Fraction(a) - x) ** 2 for a, x in zip(v, exact)), [-a for a in v])
+        if best is None or key < best[0]:
+            best = (key, list(v))
+    assert oracle.layer_budgets(L, k, slope) == best[1]

@@ -41,6 +41,7 @@ from ._lib import (  # noqa: F401
     decode_step,
     decode_workspace_bytes,
     kv_append,
+    layer_budgets,
     prefill_stages,
     prefill_topk,
     prefill_workspace_bytes,

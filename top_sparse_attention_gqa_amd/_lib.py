@@ -45,7 +45,8 @@ PF_STAGE_NAMES = ["maxima", "threshold", "filter", "select"]
 EXPORTS = ["ra_abi_version", "ra_status_str", "ra_decode_workspace_bytes",
            "ra_kv_append", "ra_decode_step", "ra_decode_stages",
            "ra_workspace_scores_offset", "ra_workspace_rescan_count_offset",
-           "ra_prefill_workspace_bytes", "ra_prefill_topk", "ra_prefill_stages"]
+           "ra_prefill_workspace_bytes", "ra_prefill_topk", "ra_prefill_stages",
+           "ra_layer_budgets"]
 
 
 class KVLayerStruct(ctypes.Structure):
@@ -68,6 +69,8 @@ _lib.ra_prefill_topk.restype = c_int
 _lib.ra_prefill_topk.argtypes = [c_void_p, c_int32, c_int32, POINTER(KVLayerStruct), c_int32,
                                  c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                  c_size_t, c_void_p]
+_lib.ra_layer_budgets.restype = c_int
+_lib.ra_layer_budgets.argtypes = [c_int32, c_int32, c_int32, c_void_p]
 _lib.ra_prefill_stages.restype = c_int
 _lib.ra_prefill_stages.argtypes = _lib.ra_prefill_topk.argtypes[:-1] + [c_int32, c_int32, c_void_p]
 _lib.ra_workspace_rescan_count_offset.restype = c_size_t
@@ -277,3 +280,13 @@ def prefill_topk(q, kv: KVLayer, seq: int, N: int, k: int, n_sink: int, window: 
 
 
 raw = _lib  # the C entry points, for tests that pass raw pointers
+
+
+def layer_budgets(n_layers: int, k_mean: int, slope_permille: int) -> list:
+    """ra_layer_budgets: pyramid-shaped per-layer budgets with the total of
+    k_mean per layer (slope 0: uniform)."""
+    buf = (ctypes.c_int32 * max(n_layers, 1))()
+    st = _lib.ra_layer_budgets(n_layers, k_mean, slope_permille, ctypes.cast(buf, c_void_p))
+    if st != RA_OK:
+        raise RAError(st, "ra_layer_budgets")
+    return [int(x) for x in buf[:n_layers]]

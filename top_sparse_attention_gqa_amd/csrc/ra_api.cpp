@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <mutex>
 #include <numeric>
+#include <vector>
 
 #include "ra.h"
 #include "ra_internal.h"
@@ -356,6 +357,35 @@ ra_status ra_prefill_stages(const uint16_t* q, int32_t T, int32_t H_q,
   p.splits = int32_t(S);
   p.xcd_groups = (int64_t(kv->H_kv) * S) % 8 == 0 ? 1 : 0;
   if (launch_prefill(p, first_stage, last_stage, stream) != hipSuccess) return RA_ERR_HIP;
+  return RA_OK;
+}
+
+ra_status ra_layer_budgets(int32_t n_layers, int32_t k_mean, int32_t slope_permille,
+                           int32_t* k_out) {
+  if (!k_out || n_layers <= 0 || n_layers > 4096 || k_mean < 0 || slope_permille < 0 ||
+      slope_permille > 1000)
+    return RA_ERR_INVALID_ARGUMENT;
+  const int64_t L = n_layers;
+  if (L == 1) {
+    k_out[0] = k_mean;
+    return RA_OK;
+  }
+  // k_l = num_l / den exactly; num_l >= 0 since the slope is at most 1
+  const int64_t den = 1000 * (L - 1);
+  std::vector<int64_t> rem(static_cast<size_t>(L), 0);
+  int64_t left = L * k_mean;
+  for (int64_t l = 0; l < L; ++l) {
+    const int64_t num = int64_t(k_mean) * (den + int64_t(slope_permille) * (L - 1 - 2 * l));
+    k_out[l] = int32_t(num / den);
+    rem[size_t(l)] = num % den;
+    left -= num / den;
+  }
+  // the fractional parts sum to `left` (< L): one more for the largest ones
+  std::vector<int32_t> order(static_cast<size_t>(L));
+  for (int32_t l = 0; l < n_layers; ++l) order[size_t(l)] = l;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return rem[size_t(a)] > rem[size_t(b)]; });
+  for (int64_t i = 0; i < left; ++i) ++k_out[order[size_t(i)]];
   return RA_OK;
 }
 
