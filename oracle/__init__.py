@@ -18,11 +18,14 @@ from .ra_oracle import (  # noqa: F401
     decode,
     decode_head,
     dense,
+    graph_build,
+    graph_search,
     kv_bytes_per_token,
     layer_budgets,
     merge,
     partial,
     prefill_topk,
+    score_f32_ordered,
     scores,
     selection_domain,
     static_set,

@@ -18,6 +18,9 @@ Source pages (cited by title and slide/equation, never by line):
   - frame "The bottleneck is both storage and KV access": Table 1, KV capacity.
   - frame "Extra experiments show where budget matters": a PyramidKV-style
     per-layer budget (more keys for the lower layers).
+  - frame "Prefill queries teach the key graph what matters": prefill
+    queries' exact top-k keys, query-key links projected into a key-only
+    graph (the RoarGraph idea), searched with each decode query.
 
 Readings of points the pages leave open:
 
@@ -336,4 +339,91 @@ def layer_budgets(n_layers: int, k_mean: int, slope_permille: int) -> list:
     for l in by_fraction[:short]:
         ks[l] += 1
     return ks
+
+
+# --------------------------------------------------------------------------
+# Query-aware key graph: "Prefill queries teach the key graph what matters"
+# (steps 2-4: link each prefill query to its exact top keys, project the
+# links into a key-only graph, search it with each decode query). The
+# slides give the steps, not their parameters; the readings here are the
+# plainest deterministic ones.
+# --------------------------------------------------------------------------
+
+def score_f32_ordered(q, K, positions) -> np.ndarray:
+    """Scores of one query against the keys at ``positions`` as a graph
+    search compares them: q . k in fp32, the (exact) products of the bf16
+    inputs added one dimension after another, 0 to d-1, each sum rounded to
+    fp32. The search only ranks keys, so the positive factor 1/sqrt(d) is
+    left out. q: [d] raw bf16 bits; K: [N, d] raw bf16 bits (one KV head)."""
+    qf = (np.asarray(q).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    P = np.asarray(positions, dtype=np.int64)
+    Kf = (np.asarray(K)[P].astype(np.uint32) << np.uint32(16)).view(np.float32)
+    s = np.zeros(P.size, dtype=np.float32)
+    for i in range(qf.size):
+        s = (s + Kf[:, i] * qf[i]).astype(np.float32)
+    return s
+
+
+def graph_build(hubs, lists, N: int, D: int):
+    """Key-only graph from prefill query-key links.
+
+    hubs[t]: the best key of prefill query t (-1: none); lists[t]: its top
+    keys (-1 padded). For t = 0, 1, ... and each other key b of lists[t] in
+    ascending position, the hub and b are linked both ways. A key keeps its
+    first D distinct neighbours. The entry point is the key that is the hub
+    of the most queries (ties to the lower position), -1 if there is none.
+    Returns (nbr int64 [N, D] padded with -1, entry).
+    """
+    nbr = [[] for _ in range(N)]
+
+    def link(a, b):
+        if a != b and len(nbr[a]) < D and b not in nbr[a]:
+            nbr[a].append(b)
+
+    hub_count = {}
+    for t, a in enumerate(np.asarray(hubs).tolist()):
+        if a < 0:
+            continue
+        hub_count[a] = hub_count.get(a, 0) + 1
+        for b in sorted(x for x in np.asarray(lists[t]).tolist() if x >= 0):
+            if b != a:
+                link(a, b)
+                link(b, a)
+    out = np.full((N, D), -1, dtype=np.int64)
+    for a in range(N):
+        out[a, :len(nbr[a])] = nbr[a]
+    entry = min(hub_count, key=lambda a: (-hub_count[a], a)) if hub_count else -1
+    return out, entry
+
+
+def graph_search(q, K, nbr, entry: int, ef: int, k: int):
+    """Best-first search of the key graph with one decode query.
+
+    A result list R keeps the ef best visited keys by (score, lower
+    position), scores from ``score_f32_ordered``. Starting from the entry
+    point, the best key of R not yet expanded is expanded: each neighbour not
+    visited before is visited, scored and offered to R. The search ends when
+    every key in R has been expanded. Returns (the best min(k, |R|) keys of R
+    in ascending position, the number of keys visited).
+    """
+    if entry < 0:
+        return np.zeros(0, dtype=np.int64), 0
+    nbr = np.asarray(nbr)
+    visited = {int(entry)}
+    R = [(float(score_f32_ordered(q, K, [entry])[0]), int(entry), False)]
+    while True:
+        R.sort(key=lambda e: (-e[0], e[1]))
+        c = next((i for i, e in enumerate(R) if not e[2]), None)
+        if c is None:
+            break
+        R[c] = (R[c][0], R[c][1], True)
+        new = [int(u) for u in nbr[R[c][1]] if u >= 0 and int(u) not in visited]
+        visited.update(new)
+        if new:
+            sc = score_f32_ordered(q, K, new)
+            R.extend((float(x), u, False) for x, u in zip(sc, new))
+            R.sort(key=lambda e: (-e[0], e[1]))
+            del R[ef:]
+    best = sorted(e[1] for e in R[:k])
+    return np.asarray(best, dtype=np.int64), len(visited)
 

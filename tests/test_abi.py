@@ -220,3 +220,42 @@ def test_layer_budgets_reject_bad_arguments():
     for args in ((0, 5, 0), (4, -1, 0), (4, 5, -1), (4, 5, 1001), (5000, 5, 0)):
         assert _lib.raw.ra_layer_budgets(*args, ctypes.cast(buf, ctypes.c_void_p)) == ra.RA_ERR_INVALID_ARGUMENT
     assert _lib.raw.ra_layer_budgets(4, 5, 0, None) == ra.RA_ERR_INVALID_ARGUMENT
+
+
+def test_graph_build_matches_the_oracle():
+    # host build of the library against the oracle's projection
+    import numpy as np
+
+    import oracle
+    r = np.random.default_rng(7)
+    for N, T, K, D in ((50, 20, 5, 3), (300, 120, 8, 16), (1000, 400, 16, 64), (64, 0, 4, 8)):
+        lists = np.stack([r.choice(N, K, replace=False) for _ in range(T)]).astype(np.int32) \
+            if T else np.zeros((0, K), np.int32)
+        if T:
+            lists[r.random((T, K)) < 0.1] = -1       # some padding
+        hubs = np.array([l[l >= 0][0] if (l >= 0).any() else -1 for l in lists], np.int32)
+        if T:
+            hubs[::7] = -1                            # some queries without a hub
+        nbr, entry = ra.graph_build(hubs, lists, N, D)
+        want, want_entry = oracle.graph_build(hubs, lists, N, D)
+        assert np.array_equal(nbr, want) and entry == want_entry
+
+
+def test_graph_arguments_are_checked():
+    import numpy as np
+    with pytest.raises(ra.RAError):
+        ra.graph_build(np.array([5], np.int32), np.array([[1, 2]], np.int32), 4, 2)   # hub >= N
+    with pytest.raises(ra.RAError):
+        ra.graph_build(np.array([0], np.int32), np.array([[1, 2]], np.int32), 4, 65)  # D > 64
+    # every call below fails validation, so nothing is launched
+    kv = _kv()
+    base = [FAKE, 4, ctypes.byref(kv), 0, 640, FAKE, 8, FAKE, 8, 4, FAKE, FAKE, FAKE, 1 << 30, None]
+    bad = list(base); bad[9] = 9                  # k > ef
+    assert _lib.raw.ra_graph_search(*bad) == ra.RA_ERR_INVALID_ARGUMENT
+    bad = list(base); bad[8] = 257                # ef > 256
+    assert _lib.raw.ra_graph_search(*bad) == ra.RA_ERR_INVALID_ARGUMENT
+    bad = list(base); bad[6] = 65                 # D > 64
+    assert _lib.raw.ra_graph_search(*bad) == ra.RA_ERR_INVALID_ARGUMENT
+    bad = list(base); bad[13] = 16                # workspace too small
+    assert _lib.raw.ra_graph_search(*bad) == ra.RA_ERR_WORKSPACE
+    assert ra.graph_search_workspace_bytes(4, 640) == 512  # 4 heads x 20 words, 256-B aligned

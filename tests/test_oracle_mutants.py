@@ -121,7 +121,40 @@ def _budgets_ties_high(L, k, slope):
     return ks
 
 
+_REAL_BUILD = ro.graph_build
+_REAL_SEARCH = ro.graph_search
+_REAL_F32 = ro.score_f32_ordered
+
+
+def _build_one_way(hubs, lists, N, D):
+    # only hub -> key links, no way back
+    nbr = [[] for _ in range(N)]
+    for t, a in enumerate(np.asarray(hubs).tolist()):
+        if a < 0:
+            continue
+        for b in sorted(x for x in np.asarray(lists[t]).tolist() if x >= 0):
+            if b != a and len(nbr[a]) < D and b not in nbr[a]:
+                nbr[a].append(b)
+    out = np.full((N, D), -1, dtype=np.int64)
+    for a in range(N):
+        out[a, :len(nbr[a])] = nbr[a]
+    return out, _REAL_BUILD(hubs, lists, N, D)[1]
+
+
+def _search_worst_first(q, K, nbr, entry, ef, k):
+    # expands the worst key of the result list instead of the best
+    return _REAL_SEARCH(np.asarray(q) ^ np.uint16(0x8000), K, nbr, entry, ef, k)
+
+
+def _f32_reversed(q, K, positions):
+    # adds the dimensions in the opposite order
+    return _REAL_F32(np.asarray(q)[::-1].copy(), np.asarray(K)[:, ::-1].copy(), positions)
+
+
 MUTANTS = {
+    "graph_build_one_way": ("graph_build", _build_one_way),
+    "graph_search_worst_first": ("graph_search", _search_worst_first),
+    "score_f32_reversed_order": ("score_f32_ordered", _f32_reversed),
     "budgets_rising": ("layer_budgets", _budgets_rising),
     "budgets_floor_only": ("layer_budgets", _budgets_floor_only),
     "budgets_ties_high": ("layer_budgets", _budgets_ties_high),

@@ -426,3 +426,120 @@ def test_layer_budgets_round_like_brute_force(L, k, slope):
         if best is None or key < best[0]:
             best = (key, list(v))
     assert oracle.layer_budgets(L, k, slope) == best[1]
+
+
+# --------------------------------------------------------------------------
+# Query-aware key graph (slides, frame "Prefill queries teach the key graph
+# what matters"): the fixed-order fp32 score, the projection build and the
+# best-first search.
+# --------------------------------------------------------------------------
+
+def _bits(x):
+    return to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def test_ordered_score_rounds_one_dimension_after_another():
+    # 2^24 + 1 is not an fp32 value: summed in order the 1 is lost, so the
+    # score is 0 although the exact dot product is 1
+    q = np.zeros(D, dtype=np.float32)
+    q[:3] = [2.0 ** 24, 1.0, -(2.0 ** 24)]
+    K = np.ones((1, D), dtype=np.float32)
+    assert oracle.score_f32_ordered(_bits(q), _bits(K), [0])[0] == 0.0
+    # the same terms with the small one last: exact
+    q[:3] = [2.0 ** 24, -(2.0 ** 24), 1.0]
+    assert oracle.score_f32_ordered(_bits(q), _bits(K), [0])[0] == 1.0
+
+
+def test_ordered_score_is_exact_on_small_integers_and_within_the_rounding_bound():
+    r = rng(31)
+    qi = r.integers(-3, 4, D).astype(np.float32)
+    Ki = r.integers(-3, 4, (40, D)).astype(np.float32)
+    got = oracle.score_f32_ordered(_bits(qi), _bits(Ki), np.arange(40))
+    assert np.array_equal(got.astype(np.float64), Ki.astype(np.float64) @ qi.astype(np.float64))
+    q = r.standard_normal(D).astype(np.float32)
+    K = r.standard_normal((60, D)).astype(np.float32)
+    qb, Kb = _bits(q), _bits(K)
+    qf = oracle.as_f64(qb)
+    Kf = oracle.as_f64(Kb)
+    exact = Kf @ qf
+    bound = D * 2.0 ** -24 / (1 - D * 2.0 ** -24) * (np.abs(Kf) @ np.abs(qf))
+    got = oracle.score_f32_ordered(qb, Kb, np.arange(60)).astype(np.float64)
+    assert np.all(np.abs(got - exact) <= bound)
+    # positions pick rows
+    assert np.array_equal(oracle.score_f32_ordered(qb, Kb, [5, 2]), got[[5, 2]].astype(np.float32))
+
+
+def test_graph_build_on_a_worked_example():
+    # hubs 3, 3, 1; degree cap 2; links in query order, ascending in a list
+    nbr, entry = oracle.graph_build([3, 3, 1], [[1, 3, 5], [3, 4, -1], [0, 1, 2]], 6, 2)
+    assert nbr.tolist() == [[1, -1], [3, 0], [1, -1], [1, 5], [3, -1], [3, -1]]
+    assert entry == 3
+
+
+def test_graph_build_is_symmetric_below_the_cap_and_respects_it():
+    r = rng(32)
+    N, T, K = 200, 60, 6
+    lists = np.stack([r.choice(N, K, replace=False) for _ in range(T)])
+    hubs = lists[:, 0].copy()
+    nbr, entry = oracle.graph_build(hubs, lists, N, 1000)
+    edges = {(a, int(b)) for a in range(N) for b in nbr[a] if b >= 0}
+    assert all((b, a) in edges for a, b in edges)
+    expect = set()
+    for t in range(T):
+        for b in lists[t]:
+            if b != hubs[t]:
+                expect |= {(int(hubs[t]), int(b)), (int(b), int(hubs[t]))}
+    assert edges == expect
+    counts = np.bincount(hubs, minlength=N)
+    assert entry == int(np.flatnonzero(counts == counts.max())[0])
+    capped, _ = oracle.graph_build(hubs, lists, N, 3)
+    assert ((capped >= 0).sum(axis=1) <= 3).all()
+    for a in range(N):  # a capped list is the start of the uncapped one
+        full = [int(x) for x in nbr[a] if x >= 0]
+        assert [int(x) for x in capped[a] if x >= 0] == full[:3]
+
+
+def _random_keys(seed, N):
+    r = rng(seed)
+    return _bits(r.standard_normal(D)), _bits(r.standard_normal((N, D)))
+
+
+def test_graph_search_on_a_complete_graph_is_the_exact_top_k():
+    q, K = _random_keys(33, 50)
+    nbr = np.array([[b for b in range(50) if b != a] for a in range(50)])
+    s = oracle.score_f32_ordered(q, K, np.arange(50)).astype(np.float64)
+    order = np.lexsort((np.arange(50), -s))          # best score, then lower position
+    for k in (1, 7, 50):
+        got, visited = oracle.graph_search(q, K, nbr, 13, ef=64, k=k)
+        assert visited == 50
+        assert got.tolist() == sorted(order[:k].tolist())
+
+
+def test_graph_search_never_leaves_the_entry_component():
+    q, K = _random_keys(34, 40)
+    nbr = np.full((40, 39), -1)
+    for comp in (range(0, 20), range(20, 40)):
+        for a in comp:
+            others = [b for b in comp if b != a]
+            nbr[a, :len(others)] = others
+    got, visited = oracle.graph_search(q, K, nbr, 25, ef=40, k=30)
+    assert visited == 20 and set(got.tolist()) <= set(range(20, 40)) and got.size == 20
+
+
+def test_greedy_graph_search_stops_at_a_local_maximum_and_walks_a_chain():
+    q, K = _random_keys(35, 60)
+    r = rng(36)
+    nbr = np.stack([r.choice(60, 4, replace=False) for _ in range(60)])
+    s = oracle.score_f32_ordered(q, K, np.arange(60))
+    got, _ = oracle.graph_search(q, K, nbr, 0, ef=1, k=1)
+    c = int(got[0])
+    for u in nbr[c]:
+        assert (s[u], -u) <= (s[c], -c) or u == c
+    # a chain whose scores rise along it: greedy search walks to its end
+    chain = np.argsort(s)                     # lowest to highest score
+    cn = np.full((60, 2), -1)
+    for i in range(59):
+        cn[chain[i], 0] = chain[i + 1]
+        cn[chain[i + 1], 1] = chain[i]
+    got, visited = oracle.graph_search(q, K, cn, int(chain[0]), ef=1, k=1)
+    assert got.tolist() == [int(chain[-1])] and visited == 60

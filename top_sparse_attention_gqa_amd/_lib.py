@@ -46,7 +46,8 @@ EXPORTS = ["ra_abi_version", "ra_status_str", "ra_decode_workspace_bytes",
            "ra_kv_append", "ra_decode_step", "ra_decode_stages",
            "ra_workspace_scores_offset", "ra_workspace_rescan_count_offset",
            "ra_prefill_workspace_bytes", "ra_prefill_topk", "ra_prefill_stages",
-           "ra_layer_budgets"]
+           "ra_layer_budgets", "ra_graph_build", "ra_graph_search_workspace_bytes",
+           "ra_graph_search"]
 
 
 class KVLayerStruct(ctypes.Structure):
@@ -69,6 +70,15 @@ _lib.ra_prefill_topk.restype = c_int
 _lib.ra_prefill_topk.argtypes = [c_void_p, c_int32, c_int32, POINTER(KVLayerStruct), c_int32,
                                  c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                  c_size_t, c_void_p]
+_lib.ra_graph_build.restype = c_int
+_lib.ra_graph_build.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                c_void_p, c_void_p]
+_lib.ra_graph_search_workspace_bytes.restype = c_size_t
+_lib.ra_graph_search_workspace_bytes.argtypes = [c_int32, c_int32]
+_lib.ra_graph_search.restype = c_int
+_lib.ra_graph_search.argtypes = [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p,
+                                 c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                 c_void_p, c_size_t, c_void_p]
 _lib.ra_layer_budgets.restype = c_int
 _lib.ra_layer_budgets.argtypes = [c_int32, c_int32, c_int32, c_void_p]
 _lib.ra_prefill_stages.restype = c_int
@@ -290,3 +300,49 @@ def layer_budgets(n_layers: int, k_mean: int, slope_permille: int) -> list:
     if st != RA_OK:
         raise RAError(st, "ra_layer_budgets")
     return [int(x) for x in buf[:n_layers]]
+
+GRAPH_MAX_DEGREE = 64
+GRAPH_MAX_EF = 256
+
+
+def graph_build(hubs, lists, N: int, D: int):
+    """ra_graph_build (host): one query head's key graph from its prefill
+    queries' best keys hubs [T] and top keys lists [T][K] (int32 arrays,
+    -1 padded). Returns (nbr int32 [N][D], entry)."""
+    import numpy as np
+    h = np.ascontiguousarray(np.asarray(hubs, dtype=np.int32))
+    L = np.ascontiguousarray(np.asarray(lists, dtype=np.int32))
+    T = int(h.shape[0])
+    K = int(L.shape[1]) if L.ndim == 2 else 1
+    if T and (L.ndim != 2 or L.shape[0] != T):
+        raise ValueError("lists must be [T][K]")
+    nbr = np.empty((N, D), dtype=np.int32)
+    entry = ctypes.c_int32(-1)
+    st = _lib.ra_graph_build(h.ctypes.data if T else None, L.ctypes.data if T else None, T, K,
+                             N, D, nbr.ctypes.data, ctypes.addressof(entry))
+    if st != RA_OK:
+        raise RAError(st, "ra_graph_build")
+    return nbr, int(entry.value)
+
+
+def graph_search_workspace_bytes(H_q: int, N: int) -> int:
+    return int(_lib.ra_graph_search_workspace_bytes(H_q, N))
+
+
+def graph_search(q, kv: KVLayer, seq: int, N: int, nbr, entry, ef: int, k: int, out_idx,
+                 out_visited, ws, stream=None) -> None:
+    """ra_graph_search: best-first search of each query head's key graph.
+    q bf16 [H_q][128]; nbr int32 [H_q][N][D]; entry int32 [H_q];
+    out_idx int32 [H_q][k]; out_visited int32 [H_q] (all device)."""
+    H_q = q.shape[0]
+    D = nbr.shape[-1]
+    if tuple(nbr.shape) != (H_q, N, D) or tuple(out_idx.shape) != (H_q, k):
+        raise ValueError("nbr must be [H_q][N][D] and out_idx [H_q][k]")
+    st = _lib.ra_graph_search(
+        _ptr(q, torch.bfloat16, "q", align=16), H_q, ctypes.byref(kv.struct), seq, N,
+        _ptr(nbr, torch.int32, "nbr"), D, _ptr(entry, torch.int32, "entry"), ef, k,
+        _ptr(out_idx, torch.int32, "out_idx"), _ptr(out_visited, torch.int32, "out_visited"),
+        _ptr(ws, torch.uint8, "ws", align=256), ws.numel(), _stream(stream))
+    if st != RA_OK:
+        raise RAError(st, "ra_graph_search")
+

@@ -389,4 +389,88 @@ ra_status ra_layer_budgets(int32_t n_layers, int32_t k_mean, int32_t slope_permi
   return RA_OK;
 }
 
+ra_status ra_graph_build(const int32_t* hubs, const int32_t* lists, int32_t T, int32_t K,
+                         int32_t N, int32_t D, int32_t* nbr, int32_t* entry) {
+  if (!nbr || !entry || (T > 0 && (!hubs || !lists)) || T < 0 || K < 1 || N < 1 || D < 1 ||
+      D > RA_GRAPH_MAX_DEGREE)
+    return RA_ERR_INVALID_ARGUMENT;
+  for (int64_t i = 0; i < int64_t(T); ++i)
+    if (hubs[i] < -1 || hubs[i] >= N) return RA_ERR_INVALID_ARGUMENT;
+  for (int64_t i = 0; i < int64_t(T) * K; ++i)
+    if (lists[i] < -1 || lists[i] >= N) return RA_ERR_INVALID_ARGUMENT;
+  std::fill(nbr, nbr + size_t(N) * D, -1);
+  std::vector<int32_t> deg(static_cast<size_t>(N), 0), hub_count(static_cast<size_t>(N), 0);
+  auto link = [&](int32_t a, int32_t b) {
+    int32_t* row = nbr + size_t(a) * D;
+    int32_t& n = deg[size_t(a)];
+    if (a == b || n >= D) return;
+    for (int32_t i = 0; i < n; ++i)
+      if (row[i] == b) return;
+    row[n++] = b;
+  };
+  std::vector<int32_t> keys(static_cast<size_t>(K));
+  for (int32_t t = 0; t < T; ++t) {
+    const int32_t a = hubs[t];
+    if (a < 0) continue;
+    ++hub_count[size_t(a)];
+    const int32_t* L = lists + size_t(t) * K;
+    keys.assign(L, L + K);
+    std::sort(keys.begin(), keys.end());
+    for (int32_t b : keys) {
+      if (b < 0 || b == a) continue;
+      link(a, b);
+      link(b, a);
+    }
+  }
+  int32_t best = -1;
+  for (int32_t a = 0; a < N; ++a)
+    if (hub_count[size_t(a)] > 0 && (best < 0 || hub_count[size_t(a)] > hub_count[size_t(best)]))
+      best = a;
+  *entry = best;
+  return RA_OK;
+}
+
+size_t ra_graph_search_workspace_bytes(int32_t H_q, int32_t N) {
+  if (H_q <= 0 || N <= 0 || N > RA_MAX_SEQ_LEN) return 0;
+  return align256(size_t(H_q) * ((size_t(N) + 31) / 32) * sizeof(uint32_t));
+}
+
+ra_status ra_graph_search(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv, int32_t seq,
+                          int32_t N, const int32_t* nbr, int32_t D, const int32_t* entry,
+                          int32_t ef, int32_t k, int32_t* out_idx, int32_t* out_visited,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  ra_status st = check_kv(kv);
+  if (st != RA_OK) return st;
+  if (!q || !nbr || !entry || !out_idx || !out_visited || !ws) return RA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(ws, 256) || !aligned(nbr, 4) || !aligned(out_idx, 4))
+    return RA_ERR_INVALID_ARGUMENT;
+  if (H_q <= 0 || seq < 0 || D < 1 || D > RA_GRAPH_MAX_DEGREE || k < 1 || ef < k ||
+      ef > RA_GRAPH_MAX_EF)
+    return RA_ERR_INVALID_ARGUMENT;
+  if (H_q % kv->H_kv != 0) return RA_ERR_INVALID_ARGUMENT;
+  if (N <= 0 || int64_t(N) > int64_t(kv->max_pages) * kPage) return RA_ERR_INVALID_ARGUMENT;
+  const size_t need = ra_graph_search_workspace_bytes(H_q, N);
+  if (need == 0) return RA_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < need) return RA_ERR_WORKSPACE;
+  GsParams p{};
+  p.q = q;
+  p.k_pool = kv->k_pool;
+  p.block_table = kv->block_table + size_t(seq) * kv->max_pages;
+  p.H_q = H_q;
+  p.H_kv = kv->H_kv;
+  p.N = N;
+  p.num_pages = kv->num_pages;
+  p.nbr = nbr;
+  p.entry = entry;
+  p.D = D;
+  p.ef = ef;
+  p.k = k;
+  p.vis_words = (N + 31) / 32;
+  p.visited = static_cast<uint32_t*>(ws);
+  p.out_idx = out_idx;
+  p.out_visited = out_visited;
+  if (launch_graph_search(p, stream) != hipSuccess) return RA_ERR_HIP;
+  return RA_OK;
+}
+
 }  // extern "C"

@@ -138,6 +138,22 @@ struct PfLayout {
   size_t off_pmax, off_tau, off_seg_off, off_seg_cnt, off_cand, total;
 };
 
+// Key-graph search (graph_search.hip).
+struct GsParams {
+  const uint16_t* q;          // [H_q][128]
+  const uint16_t* k_pool;
+  const int32_t* block_table; // the sequence's row
+  int32_t H_q, H_kv, N, num_pages;
+  const int32_t* nbr;         // [H_q][N][D], -1 padded
+  const int32_t* entry;       // [H_q]
+  int32_t D, ef, k, g;        // g: set per block
+  int32_t vis_words;          // bitmap words per head
+  uint32_t* visited;          // [H_q][vis_words]
+  int32_t* out_idx;           // [H_q][k]
+  int32_t* out_visited;       // [H_q]
+};
+hipError_t launch_graph_search(const GsParams& p, hipStream_t s);
+
 bool pf_layout(int32_t T, int32_t H_q, int32_t N, int32_t k, PfLayout* out);
 hipError_t launch_prefill(const PfParams& p, int first, int last, hipStream_t s);
 
