@@ -53,6 +53,7 @@ WORKLOAD_TEXT = {
     "C3_3": "Llama-3-8B layer: H_q=32, H_kv=8, d=128, N=1048576, k=3% (31457), n_sink=128, window=512",
     "C4": "16 ragged sequences (N uniform in [32768, 131072]) of a Llama-3-8B layer, 64-token pages in shuffled order, k=2% of each length",
     "C5P": "C5 with a pyramid-shaped per-layer budget: k_l falls linearly with depth (slope 0.5, 1.5 to 0.5 times the mean) around the uniform 1% of the current length, with the same total",
+    "G1": "query-aware key graph of a Llama-3-8B layer (H_q=32, H_kv=8, d=128) at N=131072, n_sink=128, window=512: built from the exact top-32 keys of all N prefill rows (degree 32), searched per decode query (ef=128) for the top 100; queries around 32 shared directions per head (spread 0.35), prefill rows and decode queries alike",
     "P1": "prefill exact top-k: T=1024 query rows of a Llama-3-8B layer (H_q=32, H_kv=8, d=128) against N=131072 keys, k=100, n_sink=128, window=512",
     "C5": "32 Llama-3-8B layers (H_q=32, H_kv=8, d=128) at N=1048576, k=1% of the current length, KV of every layer resident in HBM; each token step appends one K/V row per layer and runs the decode step of all 32 layers",
 }
@@ -181,8 +182,9 @@ def main():
         sys.exit(2)
     model = args.workload in ("C5", "C5P")
     prefill = args.workload == "P1"
+    graph = args.workload == "G1"
     if args.steps is None:
-        args.steps = 1000 if model else (50 if prefill else 200)
+        args.steps = 1000 if model else (50 if prefill or graph else 200)
     if args.warmup is None:
         args.warmup = 2 if model else (5 if prefill else 20)
 
@@ -193,6 +195,8 @@ def main():
         run_model(args)
     elif prefill:
         run_prefill(args)
+    elif graph:
+        run_graph(args)
     else:
         run_layer(args)
 
@@ -597,6 +601,190 @@ def run_prefill(args):
         "maxima_contraction": {"kernel": "pf_contract_kernel<4, false>",
                                "achieved_tflops": round(flops / k1_s / 1e12, 1),
                                "avg_launch_us": round(k1_s * 1e6, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+# query-aware key graph: one "step" is one ra_graph_search call (all query
+# heads of one decode query) over the index built from the prefill rows
+GR_H_Q, GR_H_KV, GR_N, GR_SINK, GR_WINDOW = 32, 8, 131072, 128, 512
+GR_LIST_K, GR_D, GR_EF, GR_K = 32, 32, 128, 100
+GR_QUERIES = 16       # decode queries for the recall figures
+GR_MAX_EF = 256
+GR_CHUNK = 4096       # prefill rows per ra_prefill_topk call
+GR_TOPIC_SEED, GR_TOPICS, GR_SPREAD = 9500, 32, 0.35   # shared query directions per head
+
+
+def run_graph(args):
+    import numpy as np
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+
+    import synth
+    import top_sparse_attention_gqa_amd as ra
+
+    dev = "cuda"
+    L = synth.make_layer(GR_H_Q, GR_H_KV, [GR_N], [GR_K], GR_SINK, GR_WINDOW, 64, 9100, dev)
+    kv = ra.KVLayer(L.k_pool, L.v_pool, L.block_table)
+    seq = torch.tensor([GR_N], dtype=torch.int32, device=dev)
+    kt = torch.tensor([GR_K], dtype=torch.int32, device=dev)
+    ws_d = ra.alloc_workspace(1, GR_H_Q, GR_H_KV, GR_N, GR_K, device=dev)
+    out = torch.empty(1, GR_H_Q, 128, device=dev)
+    lse = torch.empty(1, GR_H_Q, device=dev)
+    exact_idx = torch.empty(1, GR_H_Q, GR_K, dtype=torch.int32, device=dev)
+    gidx = torch.empty(GR_H_Q, GR_K, dtype=torch.int32, device=dev)
+    gvis = torch.empty(GR_H_Q, dtype=torch.int32, device=dev)
+    M = GR_N - GR_SINK - GR_WINDOW
+
+    def recall_of(nbr, entry, decode_queries, ef):
+        recalls, scanned = [], []
+        for q in decode_queries:
+            ra.decode_step(q.view(1, GR_H_Q, 128), kv, seq, GR_N, kt, GR_K, GR_SINK, GR_WINDOW,
+                           out, lse, exact_idx, ws_d)
+            ra.graph_search(q, kv, 0, GR_N, nbr, entry, ef, GR_K, gidx, gvis)
+            torch.cuda.synchronize()
+            ex_ = exact_idx.cpu().numpy()[0]
+            gi = gidx.cpu().numpy()
+            for h in range(GR_H_Q):
+                recalls.append(np.intersect1d(ex_[h], gi[h][gi[h] >= 0]).size / GR_K)
+            scanned.extend((gvis.cpu().numpy() / M).tolist())
+        return recalls, scanned
+
+    def index_and_recall(rows, decode_queries, tag):
+        """Steps 1-3 of the index (every prefill row's exact top-K keys and
+        best key, one graph per query head), then step 4 for each decode
+        query against the exact decode path's top-k."""
+        t_setup = time.perf_counter()
+        lists = np.empty((GR_N, GR_H_Q, GR_LIST_K), dtype=np.int32)
+        hubs = np.empty((GR_N, GR_H_Q), dtype=np.int32)
+        ws_l = ra.alloc_prefill_workspace(GR_CHUNK, GR_H_Q, GR_N, GR_LIST_K, device=dev)
+        ws_h = ra.alloc_prefill_workspace(GR_CHUNK, GR_H_Q, GR_N, 1, device=dev)
+        ol = torch.empty(GR_CHUNK, GR_H_Q, GR_LIST_K, dtype=torch.int32, device=dev)
+        oh = torch.empty(GR_CHUNK, GR_H_Q, 1, dtype=torch.int32, device=dev)
+        for t0 in range(0, GR_N, GR_CHUNK):
+            Q = rows(t0)
+            ra.prefill_topk(Q, kv, 0, GR_N, GR_LIST_K, GR_SINK, GR_WINDOW, ol, ws_l)
+            ra.prefill_topk(Q, kv, 0, GR_N, 1, GR_SINK, GR_WINDOW, oh, ws_h)
+            lists[t0:t0 + GR_CHUNK] = ol.cpu().numpy()
+            hubs[t0:t0 + GR_CHUNK] = oh.cpu().numpy()[:, :, 0]
+        del ws_l, ws_h
+        t_lists = time.perf_counter() - t_setup
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=16) as ex:
+            graphs = list(ex.map(lambda h: ra.graph_build(hubs[:, h], lists[:, h, :], GR_N, GR_D),
+                                 range(GR_H_Q)))
+        t_build = time.perf_counter() - t0
+        print(f"G1 {tag}: prefill top-k lists of {GR_N} rows in {t_lists:.1f} s, "
+              f"{GR_H_Q} graphs in {t_build:.1f} s", file=sys.stderr, flush=True)
+        nbr = torch.tensor(np.stack([g[0] for g in graphs]), dtype=torch.int32, device=dev)
+        entry = torch.tensor([g[1] for g in graphs], dtype=torch.int32, device=dev)
+        recalls, scanned = recall_of(nbr, entry, decode_queries, GR_EF)
+        return graphs, nbr, entry, recalls, scanned, {"prefill_top_k": round(t_lists, 2),
+                                                      "graph_build_host": round(t_build, 2)}
+
+    # queries drawn independently (no structure shared by prefill and decode)
+    iso_q = [L.q[0]] + [synth.make_prefill_queries(1, GR_H_Q, L.u, 9900 + i, dev)[0]
+                        for i in range(GR_QUERIES - 1)]
+    _, nbr, entry, iso_rec, iso_scan, _ = index_and_recall(
+        lambda t0: synth.make_prefill_queries(GR_CHUNK, GR_H_Q, L.u, 9200 + t0, dev), iso_q,
+        "independent queries")
+    del nbr, entry
+    # queries around shared directions (prefill rows and decode queries alike)
+    qs = list(synth.make_topic_queries(GR_QUERIES, GR_H_Q, L.u, GR_TOPIC_SEED, GR_TOPICS,
+                                       GR_SPREAD, 9990, dev))
+    graphs, nbr, entry, recalls, scanned, build_s = index_and_recall(
+        lambda t0: synth.make_topic_queries(GR_CHUNK, GR_H_Q, L.u, GR_TOPIC_SEED, GR_TOPICS,
+                                            GR_SPREAD, 9300 + t0, dev), qs, "topic queries")
+
+    sweep = {}
+    for ef in (GR_K, 128, 192, GR_MAX_EF):
+        r_, s_ = recall_of(nbr, entry, qs, ef)
+        sweep[str(ef)] = {"recall_at_100": round(float(np.mean(r_)), 4),
+                          "keys_scanned_frac": round(float(np.mean(s_)), 5)}
+    # timing: searches of the decode queries in turn
+    def call(i):
+        ra.graph_search(qs[i % len(qs)], kv, 0, GR_N, nbr, entry, GR_EF, GR_K, gidx, gvis)
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(args.steps):
+        call(i)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    gpu_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    # exact decode step on the same layer, for comparison
+    for _ in range(5):
+        ra.decode_step(qs[0].view(1, GR_H_Q, 128), kv, seq, GR_N, kt, GR_K, GR_SINK, GR_WINDOW,
+                       out, lse, exact_idx, ws_d)
+    torch.cuda.synchronize()
+    e2 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e2[0].record()
+    for _ in range(20):
+        ra.decode_step(qs[0].view(1, GR_H_Q, 128), kv, seq, GR_N, kt, GR_K, GR_SINK, GR_WINDOW,
+                       out, lse, exact_idx, ws_d)
+    e2[1].record()
+    torch.cuda.synchronize()
+    exact_ms = e2[0].elapsed_time(e2[1]) / 20
+    mean_scanned = float(np.mean(scanned))
+    # bytes one search call reads: a K row per visited key, a neighbour row
+    # per expanded key (at most one per visited key)
+    bytes_call = mean_scanned * M * GR_H_Q * (256 + GR_D * 4)
+    achieved = bytes_call / (gpu_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        K0 = synth.depage(L.k_pool, L.block_table, 0, GR_N, heads=[0])[:, 0, :]
+        qb = synth.bf16_bits(qs[0])
+        nb0 = graphs[0][0]
+        tt = time.perf_counter()
+        done = 0
+        while time.perf_counter() - tt < 12.0 and done < 4:
+            oracle.graph_search(qb[done % (GR_H_Q // GR_H_KV)], K0, nb0, graphs[0][1], GR_EF, GR_K,
+                                batch=ra.GRAPH_BATCH)
+            done += 1
+        spent = time.perf_counter() - tt
+        cpu = {"value": round(spent / done * GR_H_Q * 1e3, 1), "unit": "ms", "cores": 1,
+               "kind": "oracle",
+               "sample": f"oracle graph_search (Python, fp32 ordered scores) for {done} query "
+                         f"heads of KV head 0 on head 0's graph, {spent:.1f} s, scaled to "
+                         f"{GR_H_Q} heads"}
+
+    line = {
+        "metric": "key-graph search latency (ms) + Recall@100 vs exact top-100, Llama-3-8B layer @128K",
+        "value": round(ms, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: OOD queries vs K around 32 shared directions per head, prefill and decode alike; x4 sink keys)",
+        "config": {"workload": f"G1: {WORKLOAD_TEXT['G1']}", "H_q": GR_H_Q, "H_kv": GR_H_KV,
+                   "head_dim": 128, "seq_len": GR_N, "prefill_rows": GR_N,
+                   "list_k": GR_LIST_K, "degree": GR_D, "ef": GR_EF, "k": GR_K,
+                   "n_sink": GR_SINK, "window": GR_WINDOW, "decode_queries": GR_QUERIES},
+        "recall_at_100": round(float(np.mean(recalls)), 4),
+        "recall_at_100_min_head": round(float(np.min(recalls)), 4),
+        "keys_scanned_frac": round(mean_scanned, 5),
+        "ef_sweep": sweep,
+        "independent_queries": {"recall_at_100": round(float(np.mean(iso_rec)), 4),
+                                "keys_scanned_frac": round(float(np.mean(iso_scan)), 5)},
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "exact_decode_step_ms": round(exact_ms, 4),
+        "build_s": build_s,
+        "roofline": {"kernel": "graph_search_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 5),
+                     "traffic": None, "algorithmic_bytes_per_launch": int(bytes_call),
+                     "avg_launch_us": round(gpu_ms * 1e3, 2)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

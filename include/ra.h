@@ -293,6 +293,8 @@ ra_status ra_layer_budgets(int32_t n_layers, int32_t k_mean, int32_t slope_permi
 
 #define RA_GRAPH_MAX_DEGREE 64
 #define RA_GRAPH_MAX_EF 256
+#define RA_GRAPH_MAX_N (1 << 20) /* keys a graph spans (the visited set is in LDS) */
+#define RA_GRAPH_BATCH 4         /* keys a search expands per round */
 
 /*
  * Build one query head's key graph on the host from its prefill queries'
@@ -310,34 +312,31 @@ ra_status ra_layer_budgets(int32_t n_layers, int32_t k_mean, int32_t slope_permi
 ra_status ra_graph_build(const int32_t* hubs, const int32_t* lists, int32_t T, int32_t K,
                          int32_t N, int32_t D, int32_t* nbr, int32_t* entry);
 
-/* Workspace bytes of ra_graph_search: the visited bitmaps. */
-size_t ra_graph_search_workspace_bytes(int32_t H_q, int32_t N);
-
 /*
  * Step 4 of the frame: each query head h searches its key graph (nbr[h],
  * entry[h], over keys [0, N) of sequence seq, KV head h / G) best-first: a
  * result list of the ef best keys visited so far by (score, lower
- * position); the best key of the list not yet expanded is expanded (each
- * neighbour not visited before is visited, scored and offered to the list)
- * until every key in the list has been expanded. A score is q . k in fp32:
+ * position); each round expands the RA_GRAPH_BATCH best keys of the list
+ * not yet expanded (each neighbour not visited before is visited, scored
+ * and offered to the list) until every key in the list has been expanded. A score is q . k in fp32:
  * the bf16 products added dimension by dimension, 0 to 127, each sum
  * rounded (an fma chain).
  *  q:           device bf16 [H_q][128], 16-byte aligned.
  *  nbr:         device int32 [H_q][N][D] (neighbours outside [0, N) are
  *               skipped); entry: device int32 [H_q] (outside [0, N): no
  *               search, no keys).
- *  1 <= D <= RA_GRAPH_MAX_DEGREE, 1 <= k <= ef <= RA_GRAPH_MAX_EF.
+ *  1 <= D <= RA_GRAPH_MAX_DEGREE, 1 <= k <= ef <= RA_GRAPH_MAX_EF,
+ *  1 <= N <= RA_GRAPH_MAX_N.
  *  out_idx:     device int32 [H_q][k]: the best min(k, list size) keys in
  *               ascending position, then -1.
  *  out_visited: device int32 [H_q]: keys visited (scored) by the search.
- *  ws:          device, ra_graph_search_workspace_bytes, 256-byte aligned.
- * One wave per query head; async on `stream`; validation as for
- * ra_decode_step.
+ * One block of RA_GRAPH_BATCH waves per query head, no workspace; async on
+ * `stream`; validation as for ra_decode_step.
  */
 ra_status ra_graph_search(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv, int32_t seq,
                           int32_t N, const int32_t* nbr, int32_t D, const int32_t* entry,
                           int32_t ef, int32_t k, int32_t* out_idx, int32_t* out_visited,
-                          void* ws, size_t ws_bytes, hipStream_t stream);
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

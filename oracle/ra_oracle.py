@@ -396,15 +396,16 @@ def graph_build(hubs, lists, N: int, D: int):
     return out, entry
 
 
-def graph_search(q, K, nbr, entry: int, ef: int, k: int):
+def graph_search(q, K, nbr, entry: int, ef: int, k: int, batch: int = 1):
     """Best-first search of the key graph with one decode query.
 
     A result list R keeps the ef best visited keys by (score, lower
     position), scores from ``score_f32_ordered``. Starting from the entry
-    point, the best key of R not yet expanded is expanded: each neighbour not
-    visited before is visited, scored and offered to R. The search ends when
-    every key in R has been expanded. Returns (the best min(k, |R|) keys of R
-    in ascending position, the number of keys visited).
+    point, each round expands the ``batch`` best keys of R not yet expanded
+    (fewer if fewer are left): every neighbour of theirs not visited before
+    is visited, scored and offered to R. The search ends when every key in R
+    has been expanded. Returns (the best min(k, |R|) keys of R in ascending
+    position, the number of keys visited).
     """
     if entry < 0:
         return np.zeros(0, dtype=np.int64), 0
@@ -413,12 +414,17 @@ def graph_search(q, K, nbr, entry: int, ef: int, k: int):
     R = [(float(score_f32_ordered(q, K, [entry])[0]), int(entry), False)]
     while True:
         R.sort(key=lambda e: (-e[0], e[1]))
-        c = next((i for i, e in enumerate(R) if not e[2]), None)
-        if c is None:
+        todo = [i for i, e in enumerate(R) if not e[2]][:batch]
+        if not todo:
             break
-        R[c] = (R[c][0], R[c][1], True)
-        new = [int(u) for u in nbr[R[c][1]] if u >= 0 and int(u) not in visited]
-        visited.update(new)
+        new = []
+        for i in todo:
+            R[i] = (R[i][0], R[i][1], True)
+            for u in nbr[R[i][1]]:
+                u = int(u)
+                if u >= 0 and u not in visited:
+                    visited.add(u)
+                    new.append(u)
         if new:
             sc = score_f32_ordered(q, K, new)
             R.extend((float(x), u, False) for x, u in zip(sc, new))
@@ -426,4 +432,3 @@ def graph_search(q, K, nbr, entry: int, ef: int, k: int):
             del R[ef:]
     best = sorted(e[1] for e in R[:k])
     return np.asarray(best, dtype=np.int64), len(visited)
-

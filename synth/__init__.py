@@ -17,5 +17,6 @@ from .gen import (  # noqa: F401
     make_decode_stream,
     make_layer,
     make_prefill_queries,
+    make_topic_queries,
     make_new_tokens,
 )

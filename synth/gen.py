@@ -205,6 +205,23 @@ def make_prefill_queries(T: int, H_q: int, u: torch.Tensor, seed: int, device) -
     return q.to(torch.bfloat16)
 
 
+def make_topic_queries(T: int, H_q: int, u: torch.Tensor, topics_seed: int, n_topics: int,
+                       spread: float, seed: int, device) -> torch.Tensor:
+    """T query rows drawn around a few shared directions per head: row t of
+    head h is topic[h][c] + spread * N(0,1) - 0.5 u with c uniform over
+    n_topics and topic ~ N(0,1) drawn from topics_seed, so rows drawn with
+    the same topics_seed (prefill rows, later decode queries) resemble each
+    other. bf16 [T][H_q][128]."""
+    dev = torch.device(device)
+    gt = torch.Generator(device=dev).manual_seed(topics_seed)
+    topics = torch.randn(H_q, n_topics, HEAD_DIM, generator=gt, device=dev)
+    g = torch.Generator(device=dev).manual_seed(seed)
+    c = torch.randint(0, n_topics, (T, H_q), generator=g, device=dev)
+    base = topics[torch.arange(H_q, device=dev).view(1, H_q), c]        # [T][H_q][128]
+    q = base + spread * torch.randn(T, H_q, HEAD_DIM, generator=g, device=dev) - 0.5 * u.to(dev)
+    return q.to(torch.bfloat16)
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Raw bf16 bit patterns of a tensor, as a host uint16 array."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

@@ -249,13 +249,14 @@ def test_graph_arguments_are_checked():
         ra.graph_build(np.array([0], np.int32), np.array([[1, 2]], np.int32), 4, 65)  # D > 64
     # every call below fails validation, so nothing is launched
     kv = _kv()
-    base = [FAKE, 4, ctypes.byref(kv), 0, 640, FAKE, 8, FAKE, 8, 4, FAKE, FAKE, FAKE, 1 << 30, None]
+    base = [FAKE, 4, ctypes.byref(kv), 0, 640, FAKE, 8, FAKE, 8, 4, FAKE, FAKE, None]
     bad = list(base); bad[9] = 9                  # k > ef
     assert _lib.raw.ra_graph_search(*bad) == ra.RA_ERR_INVALID_ARGUMENT
     bad = list(base); bad[8] = 257                # ef > 256
     assert _lib.raw.ra_graph_search(*bad) == ra.RA_ERR_INVALID_ARGUMENT
     bad = list(base); bad[6] = 65                 # D > 64
     assert _lib.raw.ra_graph_search(*bad) == ra.RA_ERR_INVALID_ARGUMENT
-    bad = list(base); bad[13] = 16                # workspace too small
-    assert _lib.raw.ra_graph_search(*bad) == ra.RA_ERR_WORKSPACE
-    assert ra.graph_search_workspace_bytes(4, 640) == 512  # 4 heads x 20 words, 256-B aligned
+    bad = list(base); bad[4] = 641                # N beyond the table's pages
+    assert _lib.raw.ra_graph_search(*bad) == ra.RA_ERR_INVALID_ARGUMENT
+    bad = list(base); bad[10] = None              # no output
+    assert _lib.raw.ra_graph_search(*bad) == ra.RA_ERR_INVALID_ARGUMENT

@@ -4,7 +4,8 @@ queries teach the key graph what matters"). The oracle builds its own graph
 (oracle.graph_build) from the same links; the GPU side uses the library's
 build. The search's decisions follow from fp32 scores both sides compute in
 the same order, so the retrieved keys and the number of keys visited must
-be equal exactly."""
+be equal exactly. Each round of the search expands the GRAPH_BATCH best
+unexpanded keys; the oracle is run with the same batch."""
 
 import numpy as np
 import pytest
@@ -32,10 +33,8 @@ def gpu_search(L, q, seq, N, graphs, ef, k):
     entry = torch.tensor([g[1] for g in graphs], dtype=torch.int32, device=DEV)
     out = torch.full((H_q, k), -7, dtype=torch.int32, device=DEV)
     vis = torch.full((H_q,), -7, dtype=torch.int32, device=DEV)
-    ws = torch.empty(ra.graph_search_workspace_bytes(H_q, N) + 256, dtype=torch.uint8, device=DEV)
-    ws.fill_(0xA5)
     kv = ra.KVLayer(L.k_pool, L.v_pool, L.block_table)
-    ra.graph_search(q, kv, seq, N, nbr, entry, ef, k, out, vis, ws)
+    ra.graph_search(q, kv, seq, N, nbr, entry, ef, k, out, vis)
     torch.cuda.synchronize()
     return out.cpu().numpy(), vis.cpu().numpy()
 
@@ -50,7 +49,7 @@ def compare(L, q, seq, N, links, D, ef, k):
     for h in range(H_q):
         K = synth.depage(L.k_pool, L.block_table, seq, N, heads=[h // G])[:, 0, :]
         nbr, entry = oracle.graph_build(links[h][0], links[h][1], N, D)
-        want, want_vis = oracle.graph_search(qb[h], K, nbr, entry, ef, k)
+        want, want_vis = oracle.graph_search(qb[h], K, nbr, entry, ef, k, batch=ra.GRAPH_BATCH)
         row = got[h]
         assert np.array_equal(row[:want.size], want), (h, row[:want.size], want)
         assert (row[want.size:] == -1).all()

@@ -141,9 +141,9 @@ def _build_one_way(hubs, lists, N, D):
     return out, _REAL_BUILD(hubs, lists, N, D)[1]
 
 
-def _search_worst_first(q, K, nbr, entry, ef, k):
-    # expands the worst key of the result list instead of the best
-    return _REAL_SEARCH(np.asarray(q) ^ np.uint16(0x8000), K, nbr, entry, ef, k)
+def _search_worst_first(q, K, nbr, entry, ef, k, batch=1):
+    # ranks the keys upside down (the worst first)
+    return _REAL_SEARCH(np.asarray(q) ^ np.uint16(0x8000), K, nbr, entry, ef, k, batch)
 
 
 def _f32_reversed(q, K, positions):

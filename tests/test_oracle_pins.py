@@ -543,3 +543,23 @@ def test_greedy_graph_search_stops_at_a_local_maximum_and_walks_a_chain():
         cn[chain[i + 1], 1] = chain[i]
     got, visited = oracle.graph_search(q, K, cn, int(chain[0]), ef=1, k=1)
     assert got.tolist() == [int(chain[-1])] and visited == 60
+
+
+def test_batched_graph_search_on_a_complete_graph_and_a_chain():
+    # a batch of b expands the b best unexpanded keys per round; on a
+    # complete graph every batch visits everything and returns the exact
+    # top-k, and on a rising chain it still walks to the end
+    q, K = _random_keys(37, 300)
+    s = oracle.score_f32_ordered(q, K, np.arange(300)).astype(np.float64)
+    full = np.array([[b for b in range(300) if b != a] for a in range(300)])
+    for batch in (1, 4):
+        got, visited = oracle.graph_search(q, K, full, 0, ef=300, k=25, batch=batch)
+        assert visited == 300
+        assert got.tolist() == sorted(np.lexsort((np.arange(300), -s))[:25].tolist())
+    chain = np.argsort(s)
+    cn = np.full((300, 2), -1)
+    for i in range(299):
+        cn[chain[i], 0] = chain[i + 1]
+        cn[chain[i + 1], 1] = chain[i]
+    got, visited = oracle.graph_search(q, K, cn, int(chain[0]), ef=2, k=1, batch=2)
+    assert got.tolist() == [int(chain[-1])] and visited == 300

@@ -46,8 +46,7 @@ EXPORTS = ["ra_abi_version", "ra_status_str", "ra_decode_workspace_bytes",
            "ra_kv_append", "ra_decode_step", "ra_decode_stages",
            "ra_workspace_scores_offset", "ra_workspace_rescan_count_offset",
            "ra_prefill_workspace_bytes", "ra_prefill_topk", "ra_prefill_stages",
-           "ra_layer_budgets", "ra_graph_build", "ra_graph_search_workspace_bytes",
-           "ra_graph_search"]
+           "ra_layer_budgets", "ra_graph_build", "ra_graph_search"]
 
 
 class KVLayerStruct(ctypes.Structure):
@@ -73,12 +72,10 @@ _lib.ra_prefill_topk.argtypes = [c_void_p, c_int32, c_int32, POINTER(KVLayerStru
 _lib.ra_graph_build.restype = c_int
 _lib.ra_graph_build.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                 c_void_p, c_void_p]
-_lib.ra_graph_search_workspace_bytes.restype = c_size_t
-_lib.ra_graph_search_workspace_bytes.argtypes = [c_int32, c_int32]
 _lib.ra_graph_search.restype = c_int
 _lib.ra_graph_search.argtypes = [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p,
                                  c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
-                                 c_void_p, c_size_t, c_void_p]
+                                 c_void_p]
 _lib.ra_layer_budgets.restype = c_int
 _lib.ra_layer_budgets.argtypes = [c_int32, c_int32, c_int32, c_void_p]
 _lib.ra_prefill_stages.restype = c_int
@@ -303,6 +300,8 @@ def layer_budgets(n_layers: int, k_mean: int, slope_permille: int) -> list:
 
 GRAPH_MAX_DEGREE = 64
 GRAPH_MAX_EF = 256
+GRAPH_MAX_N = 1 << 20
+GRAPH_BATCH = 4  # keys a search expands per round
 
 
 def graph_build(hubs, lists, N: int, D: int):
@@ -325,12 +324,8 @@ def graph_build(hubs, lists, N: int, D: int):
     return nbr, int(entry.value)
 
 
-def graph_search_workspace_bytes(H_q: int, N: int) -> int:
-    return int(_lib.ra_graph_search_workspace_bytes(H_q, N))
-
-
 def graph_search(q, kv: KVLayer, seq: int, N: int, nbr, entry, ef: int, k: int, out_idx,
-                 out_visited, ws, stream=None) -> None:
+                 out_visited, stream=None) -> None:
     """ra_graph_search: best-first search of each query head's key graph.
     q bf16 [H_q][128]; nbr int32 [H_q][N][D]; entry int32 [H_q];
     out_idx int32 [H_q][k]; out_visited int32 [H_q] (all device)."""
@@ -342,7 +337,7 @@ def graph_search(q, kv: KVLayer, seq: int, N: int, nbr, entry, ef: int, k: int, 
         _ptr(q, torch.bfloat16, "q", align=16), H_q, ctypes.byref(kv.struct), seq, N,
         _ptr(nbr, torch.int32, "nbr"), D, _ptr(entry, torch.int32, "entry"), ef, k,
         _ptr(out_idx, torch.int32, "out_idx"), _ptr(out_visited, torch.int32, "out_visited"),
-        _ptr(ws, torch.uint8, "ws", align=256), ws.numel(), _stream(stream))
+        _stream(stream))
     if st != RA_OK:
         raise RAError(st, "ra_graph_search")
 

@@ -1,11 +1,12 @@
 // Search of a query-aware key graph with decode queries (RetrievalAttention
 // slides, frame "Prefill queries teach the key graph what matters", step 4:
 // each new decode query searches the key-only graph projected from the
-// prefill queries' top-k links). One wave per query head runs a best-first
-// search: a result list R holds the ef best keys visited so far by
-// (score, lower position); the best key of R not yet expanded is expanded,
-// every neighbour not visited before is visited, scored and offered to R;
-// the search ends when every key of R has been expanded.
+// prefill queries' top-k links). One block of kGsWaves waves per query head
+// runs a best-first search: a result list R holds the ef best keys visited
+// so far by (score, lower position); each round expands the kGsWaves best
+// keys of R not yet expanded, one per wave; every neighbour not visited
+// before is visited, scored and offered to R; the search ends when every
+// key of R has been expanded.
 //
 // A score is q . k in fp32 with the bf16 products (exact in fp32) added one
 // dimension after another, 0 to 127, each sum rounded (an fma chain): the
@@ -13,9 +14,9 @@
 // reproduce bit for bit. The factor 1/sqrt(d) is left out (it does not
 // change the order).
 //
-// Lane i scores the i-th neighbour of the expanded key (degree <= 64). The
-// visited set is a bitmap in the workspace (one bit per position); R is
-// kept sorted in LDS, and the new keys of an expansion are merged into it
+// Lane i of a wave scores the i-th neighbour of its key (degree <= 64).
+// The visited set is a bitmap in LDS (one bit per position, N <= 2^20);
+// R is kept sorted in LDS, and the new keys of a round are merged into it
 // by rank: an existing entry moves down by the number of new keys better
 // than it, a new key lands after the entries and new keys better than it.
 #include <climits>
@@ -25,13 +26,18 @@
 namespace ra {
 
 constexpr int kGsMaxEf = RA_GRAPH_MAX_EF;
+constexpr int kGsWaves = kGsBatch;          // keys expanded per round, one per wave
+constexpr int kGsThreads = kGsWaves * 64;
+static_assert(kGsThreads >= kGsMaxEf, "one thread per entry of R");
 
 struct GsLds {
   float rs[2][kGsMaxEf];  // R, double-buffered: score, position, expanded
   int32_t rp[2][kGsMaxEf];
   int32_t rx[2][kGsMaxEf];
-  float ns[64];           // the keys new in this expansion
-  int32_t nu[64];
+  float ns[kGsThreads];   // the keys new in this round
+  int32_t nu[kGsThreads];
+  int32_t cand[kGsWaves]; // the keys expanded in this round
+  int32_t cnt[kGsWaves];  // per wave: unexpanded entries, then new keys
 };
 
 // a ranks before b: larger score, then lower position
@@ -39,12 +45,12 @@ __device__ __forceinline__ bool gs_better(float sa, int32_t pa, float sb, int32_
   return sa > sb || (sa == sb && pa < pb);
 }
 
-__device__ __forceinline__ float gs_score(const GsParams& p, const uint32_t (&qw)[64], int32_t u) {
-  const int jp = u >> 6;
-  int32_t pg = p.block_table[jp];
+__device__ __forceinline__ float gs_score(const GsParams& p, int g, const uint32_t (&qw)[64],
+                                          int32_t u) {
+  int32_t pg = p.block_table[u >> 6];
   pg = ((unsigned)pg < (unsigned)p.num_pages) ? pg : 0;
   const uint4* kr = reinterpret_cast<const uint4*>(
-      p.k_pool + ((size_t(pg) * p.H_kv + p.g) * kPage + (u & 63)) * kHeadDim);
+      p.k_pool + ((size_t(pg) * p.H_kv + g) * kPage + (u & 63)) * kHeadDim);
   float s = 0.0f;
 #pragma unroll
   for (int c = 0; c < 16; ++c) {
@@ -61,24 +67,32 @@ __device__ __forceinline__ float gs_score(const GsParams& p, const uint32_t (&qw
   return s;
 }
 
-__global__ __launch_bounds__(64) void graph_search_kernel(GsParams p0) {
+// Sum of v over the waves before this one, and over all waves (v in LDS,
+// one entry per wave, written before the last barrier).
+__device__ __forceinline__ void gs_wave_prefix(const int32_t* v, int wave, int& before, int& total) {
+  before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kGsWaves; ++w) {
+    before += w < wave ? v[w] : 0;
+    total += v[w];
+  }
+}
+
+__global__ __launch_bounds__(kGsThreads) void graph_search_kernel(GsParams p) {
+  extern __shared__ uint32_t vis[];  // visited bitmap, p.vis_words words
   __shared__ GsLds sm;
   const int h = blockIdx.x;
-  const int lane = threadIdx.x;
-  GsParams p = p0;
-  p.g = h / (p.H_q / p.H_kv);
+  const int g = h / (p.H_q / p.H_kv);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = p.N, D = p.D, ef = p.ef;
-  uint32_t* vis = p.visited + size_t(h) * p.vis_words;
   int32_t* out = p.out_idx + size_t(h) * p.k;
 
-  for (int i = lane; i < p.vis_words; i += 64) vis[i] = 0u;
-  __threadfence();
-  __builtin_amdgcn_wave_barrier();
-
+  for (int i = tid; i < p.vis_words; i += kGsThreads) vis[i] = 0u;
   const int32_t e = p.entry[h];
-  if (e < 0 || e >= N) {
-    for (int i = lane; i < p.k; i += 64) out[i] = -1;
-    if (lane == 0) p.out_visited[h] = 0;
+  if (e < 0 || e >= N) {  // block-uniform
+    for (int i = tid; i < p.k; i += kGsThreads) out[i] = -1;
+    if (tid == 0) p.out_visited[h] = 0;
     return;
   }
   uint32_t qw[64];
@@ -94,65 +108,80 @@ __global__ __launch_bounds__(64) void graph_search_kernel(GsParams p0) {
     }
   }
   const int32_t* nbr = p.nbr + size_t(h) * N * D;
-
-  int cur = 0, nr = 1;
-  uint32_t visited = 1;
-  if (lane == 0) {
-    atomicOr(&vis[e >> 5], 1u << (e & 31));
-    sm.rs[0][0] = gs_score(p, qw, e);
+  __syncthreads();
+  if (tid == 0) {
+    vis[e >> 5] |= 1u << (e & 31);
+    sm.rs[0][0] = gs_score(p, g, qw, e);
     sm.rp[0][0] = e;
     sm.rx[0][0] = 0;
   }
-  __builtin_amdgcn_wave_barrier();
+  int cur = 0, nr = 1;
+  uint32_t visited = 1;
+  __syncthreads();
 
-  // every pass expands one key of R and every key enters R at most once
+  // every round expands at least one key of R and a key enters R once
   for (int iter = 0; iter <= N; ++iter) {
-    // the best key of R not yet expanded (R is sorted)
-    int best = INT_MAX;
-    for (int i = lane; i < nr; i += 64)
-      if (!sm.rx[cur][i]) best = min(best, i);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) best = min(best, __shfl_xor(best, off));
-    if (best == INT_MAX) break;
-    const int32_t c = sm.rp[cur][best];
-    __builtin_amdgcn_wave_barrier();
-    if (lane == 0) sm.rx[cur][best] = 1;
-
-    int32_t u = lane < D ? nbr[size_t(c) * D + lane] : -1;
-    bool fresh = false;
-    if (u >= 0 && u < N) {
-      const uint32_t bit = 1u << (u & 31);
-      fresh = (atomicOr(&vis[u >> 5], bit) & bit) == 0u;
+    // the kGsWaves best unexpanded entries of R (sorted), in order
+    const bool un = tid < nr && !sm.rx[cur][tid];
+    uint64_t bal = __ballot(un);
+    if (lane == 0) sm.cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int before, total;
+    gs_wave_prefix(sm.cnt, wave, before, total);
+    const int nb = min(total, kGsWaves);
+    if (nb == 0) break;  // block-uniform
+    if (un) {
+      const int r = before + __popcll(bal & ((1ull << lane) - 1ull));
+      if (r < kGsWaves) {
+        sm.cand[r] = sm.rp[cur][tid];
+        sm.rx[cur][tid] = 1;
+      }
     }
-    const float s = fresh ? gs_score(p, qw, u) : 0.0f;
-    const uint64_t mask = __ballot(fresh);
-    const int m = __popcll(mask);
-    if (m == 0) continue;
-    visited += uint32_t(m);
+    __syncthreads();
+
+    // wave w expands the w-th of them; lane i takes its i-th neighbour
+    bool fresh = false;
+    int32_t u = -1;
+    if (wave < nb && lane < D) {
+      u = nbr[size_t(sm.cand[wave]) * D + lane];
+      if (u >= 0 && u < N) {
+        const uint32_t bit = 1u << (u & 31);
+        fresh = (atomicOr(&vis[u >> 5], bit) & bit) == 0u;
+      }
+    }
+    const float s = fresh ? gs_score(p, g, qw, u) : 0.0f;
+    bal = __ballot(fresh);
+    __syncthreads();  // every wave has read sm.cnt
+    if (lane == 0) sm.cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int m;
+    gs_wave_prefix(sm.cnt, wave, before, m);
     if (fresh) {
-      const int slot = __popcll(mask & ((1ull << lane) - 1ull));
+      const int slot = before + __popcll(bal & ((1ull << lane) - 1ull));
       sm.ns[slot] = s;
       sm.nu[slot] = u;
     }
-    __builtin_amdgcn_wave_barrier();
+    __syncthreads();
+    if (m == 0) continue;  // block-uniform
+    visited += uint32_t(m);
 
     // merge by rank into the other buffer, keeping the best ef
     const int nxt = cur ^ 1;
-    for (int i = lane; i < nr; i += 64) {
-      const float si = sm.rs[cur][i];
-      const int32_t pi = sm.rp[cur][i];
+    if (tid < nr) {
+      const float si = sm.rs[cur][tid];
+      const int32_t pi = sm.rp[cur][tid];
       int shift = 0;
       for (int j = 0; j < m; ++j) shift += gs_better(sm.ns[j], sm.nu[j], si, pi) ? 1 : 0;
-      const int pos = i + shift;
+      const int pos = tid + shift;
       if (pos < ef) {
         sm.rs[nxt][pos] = si;
         sm.rp[nxt][pos] = pi;
-        sm.rx[nxt][pos] = sm.rx[cur][i];
+        sm.rx[nxt][pos] = sm.rx[cur][tid];
       }
     }
-    if (lane < m) {
-      const float sx = sm.ns[lane];
-      const int32_t ux = sm.nu[lane];
+    if (tid < m) {
+      const float sx = sm.ns[tid];
+      const int32_t ux = sm.nu[tid];
       int lo = 0, hi = nr;  // entries of R better than the new key
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
@@ -167,25 +196,26 @@ __global__ __launch_bounds__(64) void graph_search_kernel(GsParams p0) {
         sm.rx[nxt][pos] = 0;
       }
     }
-    __builtin_amdgcn_wave_barrier();
+    __syncthreads();
     nr = min(ef, nr + m);
     cur = nxt;
   }
 
   // the best min(k, |R|) keys, ascending by position
   const int kk = min(p.k, nr);
-  for (int i = lane; i < kk; i += 64) {
-    const int32_t pi = sm.rp[cur][i];
+  if (tid < kk) {
+    const int32_t pi = sm.rp[cur][tid];
     int rank = 0;
     for (int j = 0; j < kk; ++j) rank += sm.rp[cur][j] < pi ? 1 : 0;
     out[rank] = pi;
   }
-  for (int i = kk + lane; i < p.k; i += 64) out[i] = -1;
-  if (lane == 0) p.out_visited[h] = int32_t(visited);
+  for (int i = kk + tid; i < p.k; i += kGsThreads) out[i] = -1;
+  if (tid == 0) p.out_visited[h] = int32_t(visited);
 }
 
 hipError_t launch_graph_search(const GsParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(graph_search_kernel, dim3(p.H_q), dim3(64), 0, s, p);
+  const size_t lds = size_t(p.vis_words) * sizeof(uint32_t);
+  hipLaunchKernelGGL(graph_search_kernel, dim3(p.H_q), dim3(kGsThreads), lds, s, p);
   return hipGetLastError();
 }
 

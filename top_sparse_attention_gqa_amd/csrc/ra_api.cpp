@@ -430,28 +430,22 @@ ra_status ra_graph_build(const int32_t* hubs, const int32_t* lists, int32_t T, i
   return RA_OK;
 }
 
-size_t ra_graph_search_workspace_bytes(int32_t H_q, int32_t N) {
-  if (H_q <= 0 || N <= 0 || N > RA_MAX_SEQ_LEN) return 0;
-  return align256(size_t(H_q) * ((size_t(N) + 31) / 32) * sizeof(uint32_t));
-}
-
 ra_status ra_graph_search(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv, int32_t seq,
                           int32_t N, const int32_t* nbr, int32_t D, const int32_t* entry,
                           int32_t ef, int32_t k, int32_t* out_idx, int32_t* out_visited,
-                          void* ws, size_t ws_bytes, hipStream_t stream) {
+                          hipStream_t stream) {
   ra_status st = check_kv(kv);
   if (st != RA_OK) return st;
-  if (!q || !nbr || !entry || !out_idx || !out_visited || !ws) return RA_ERR_INVALID_ARGUMENT;
-  if (!aligned(q, 16) || !aligned(ws, 256) || !aligned(nbr, 4) || !aligned(out_idx, 4))
+  if (!q || !nbr || !entry || !out_idx || !out_visited) return RA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(nbr, 4) || !aligned(out_idx, 4) || !aligned(entry, 4) ||
+      !aligned(out_visited, 4))
     return RA_ERR_INVALID_ARGUMENT;
   if (H_q <= 0 || seq < 0 || D < 1 || D > RA_GRAPH_MAX_DEGREE || k < 1 || ef < k ||
       ef > RA_GRAPH_MAX_EF)
     return RA_ERR_INVALID_ARGUMENT;
   if (H_q % kv->H_kv != 0) return RA_ERR_INVALID_ARGUMENT;
-  if (N <= 0 || int64_t(N) > int64_t(kv->max_pages) * kPage) return RA_ERR_INVALID_ARGUMENT;
-  const size_t need = ra_graph_search_workspace_bytes(H_q, N);
-  if (need == 0) return RA_ERR_INVALID_ARGUMENT;
-  if (ws_bytes < need) return RA_ERR_WORKSPACE;
+  if (N <= 0 || N > RA_GRAPH_MAX_N || int64_t(N) > int64_t(kv->max_pages) * kPage)
+    return RA_ERR_INVALID_ARGUMENT;
   GsParams p{};
   p.q = q;
   p.k_pool = kv->k_pool;
@@ -466,7 +460,6 @@ ra_status ra_graph_search(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
   p.ef = ef;
   p.k = k;
   p.vis_words = (N + 31) / 32;
-  p.visited = static_cast<uint32_t*>(ws);
   p.out_idx = out_idx;
   p.out_visited = out_visited;
   if (launch_graph_search(p, stream) != hipSuccess) return RA_ERR_HIP;

@@ -139,6 +139,7 @@ struct PfLayout {
 };
 
 // Key-graph search (graph_search.hip).
+constexpr int kGsBatch = RA_GRAPH_BATCH;  // keys expanded per round of the search
 struct GsParams {
   const uint16_t* q;          // [H_q][128]
   const uint16_t* k_pool;
@@ -146,9 +147,8 @@ struct GsParams {
   int32_t H_q, H_kv, N, num_pages;
   const int32_t* nbr;         // [H_q][N][D], -1 padded
   const int32_t* entry;       // [H_q]
-  int32_t D, ef, k, g;        // g: set per block
-  int32_t vis_words;          // bitmap words per head
-  uint32_t* visited;          // [H_q][vis_words]
+  int32_t D, ef, k;
+  int32_t vis_words;          // visited-bitmap words (in LDS)
   int32_t* out_idx;           // [H_q][k]
   int32_t* out_visited;       // [H_q]
 };
