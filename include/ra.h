@@ -338,6 +338,49 @@ ra_status ra_graph_search(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
                           int32_t ef, int32_t k, int32_t* out_idx, int32_t* out_visited,
                           hipStream_t stream);
 
+/* ------------------------------------------------------------------ */
+/* Two KV tiers: attention over listed positions, and the merge of two   */
+/* partial outputs (slides, frames "The GPU keeps 640 fixed positions":  */
+/* W attended from GPU memory, the retrieved set from CPU memory, and    */
+/* "Two local softmax outputs need global weights", Eqs. (3)-(5)).       */
+/* ------------------------------------------------------------------ */
+
+#define RA_SPARSE_MAX_K 4096
+
+/*
+ * For each query head h: softmax of z = q . k / sqrt(128) over the positions
+ * idx[h][0 .. k) of sequence seq (entries outside [0, N) are skipped), times
+ * V: out[h] and out_lse[h] = m + ln sum e^(z - m). No listed position gives
+ * out = 0, lse = -inf. The pools of kv may be GPU memory or pinned host
+ * memory mapped for the device (see ra_host_device_pointer): the kernel
+ * reads host-resident rows over the host link directly.
+ *  q: device bf16 [H_q][128], 16-byte aligned; idx: device int32 [H_q][k];
+ *  out: device fp32 [H_q][128]; out_lse: device fp32 [H_q].
+ *  1 <= k <= RA_SPARSE_MAX_K. Validation as for ra_decode_step.
+ */
+ra_status ra_sparse_attend(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv, int32_t seq,
+                           int32_t N, const int32_t* idx, int32_t k, float* out, float* out_lse,
+                           hipStream_t stream);
+
+/*
+ * Merge two partial outputs per head (Eqs. (3)-(5)): with m = max(lse_a,
+ * lse_b), out = (e^(lse_a - m) out_a + e^(lse_b - m) out_b) / (e^(lse_a - m)
+ * + e^(lse_b - m)) and lse = m + ln of the denominator; a partial with
+ * lse = -inf weighs 0, and two give out = 0, lse = -inf. All buffers device
+ * fp32 ([H][128] and [H]); out/lse may alias out_a/lse_a.
+ */
+ra_status ra_merge_partials(const float* out_a, const float* lse_a, const float* out_b,
+                            const float* lse_b, int32_t H, float* out, float* lse,
+                            hipStream_t stream);
+
+/*
+ * The device address of pinned host memory (allocated with hipHostMalloc,
+ * or torch's pin_memory), through hipHostGetDevicePointer: what the pools
+ * of a host-resident ra_kv_layer must hold. RA_ERR_HIP if the memory is not
+ * mapped for the current device.
+ */
+ra_status ra_host_device_pointer(const void* host, void** dev);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,6 +16,7 @@ from .gen import (  # noqa: F401
     draw_lengths,
     make_decode_stream,
     make_layer,
+    copy_pages,
     make_prefill_queries,
     make_topic_queries,
     make_new_tokens,

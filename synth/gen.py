@@ -222,6 +222,18 @@ def make_topic_queries(T: int, H_q: int, u: torch.Tensor, topics_seed: int, n_to
     return q.to(torch.bfloat16)
 
 
+def copy_pages(pool: torch.Tensor, block_table: torch.Tensor, b: int, positions, device):
+    """A small pool holding only the pages of sequence b that contain the
+    given positions, and a block table [1][max_pages] mapping those pages
+    into it (the other entries point at its page 0). Pure data movement."""
+    pages = sorted({int(n) // PAGE for n in positions})
+    src = block_table[b, pages].long().to(pool.device)
+    small = pool[src].to(device).contiguous()
+    table = torch.zeros(1, block_table.shape[1], dtype=torch.int32)
+    table[0, pages] = torch.arange(len(pages), dtype=torch.int32)
+    return small, table.to(device)
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Raw bf16 bit patterns of a tensor, as a host uint16 array."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

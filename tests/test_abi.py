@@ -260,3 +260,21 @@ def test_graph_arguments_are_checked():
     assert _lib.raw.ra_graph_search(*bad) == ra.RA_ERR_INVALID_ARGUMENT
     bad = list(base); bad[10] = None              # no output
     assert _lib.raw.ra_graph_search(*bad) == ra.RA_ERR_INVALID_ARGUMENT
+
+
+def test_tier_entry_points_check_arguments():
+    # every call below fails validation, so nothing is launched
+    kv = _kv()
+    a = [FAKE, 4, ctypes.byref(kv), 0, 640, FAKE, 8, FAKE, FAKE, None]
+    bad = list(a); bad[6] = 0                      # k = 0
+    assert _lib.raw.ra_sparse_attend(*bad) == ra.RA_ERR_INVALID_ARGUMENT
+    bad = list(a); bad[6] = 4097                   # k > RA_SPARSE_MAX_K
+    assert _lib.raw.ra_sparse_attend(*bad) == ra.RA_ERR_INVALID_ARGUMENT
+    bad = list(a); bad[4] = 641                    # N beyond the table
+    assert _lib.raw.ra_sparse_attend(*bad) == ra.RA_ERR_INVALID_ARGUMENT
+    bad = list(a); bad[7] = None                   # no output
+    assert _lib.raw.ra_sparse_attend(*bad) == ra.RA_ERR_INVALID_ARGUMENT
+    assert _lib.raw.ra_merge_partials(FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == ra.RA_ERR_INVALID_ARGUMENT
+    assert _lib.raw.ra_merge_partials(FAKE, None, FAKE, FAKE, 4, FAKE, FAKE, None) == ra.RA_ERR_INVALID_ARGUMENT
+    dev = ctypes.c_void_p()
+    assert _lib.raw.ra_host_device_pointer(None, ctypes.byref(dev)) == ra.RA_ERR_INVALID_ARGUMENT

@@ -46,7 +46,8 @@ EXPORTS = ["ra_abi_version", "ra_status_str", "ra_decode_workspace_bytes",
            "ra_kv_append", "ra_decode_step", "ra_decode_stages",
            "ra_workspace_scores_offset", "ra_workspace_rescan_count_offset",
            "ra_prefill_workspace_bytes", "ra_prefill_topk", "ra_prefill_stages",
-           "ra_layer_budgets", "ra_graph_build", "ra_graph_search"]
+           "ra_layer_budgets", "ra_graph_build", "ra_graph_search", "ra_sparse_attend",
+           "ra_merge_partials", "ra_host_device_pointer"]
 
 
 class KVLayerStruct(ctypes.Structure):
@@ -76,6 +77,13 @@ _lib.ra_graph_search.restype = c_int
 _lib.ra_graph_search.argtypes = [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p,
                                  c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                  c_void_p]
+_lib.ra_sparse_attend.restype = c_int
+_lib.ra_sparse_attend.argtypes = [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_int32,
+                                  c_void_p, c_void_p, c_void_p]
+_lib.ra_merge_partials.restype = c_int
+_lib.ra_merge_partials.argtypes = [c_void_p] * 4 + [c_int32, c_void_p, c_void_p, c_void_p]
+_lib.ra_host_device_pointer.restype = c_int
+_lib.ra_host_device_pointer.argtypes = [c_void_p, POINTER(c_void_p)]
 _lib.ra_layer_budgets.restype = c_int
 _lib.ra_layer_budgets.argtypes = [c_int32, c_int32, c_int32, c_void_p]
 _lib.ra_prefill_stages.restype = c_int
@@ -154,9 +162,34 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+def host_device_pointer(t) -> int:
+    """ra_host_device_pointer: the device address of a pinned host tensor."""
+    if t.device.type != "cpu" or not t.is_pinned():
+        raise ValueError("a host-resident pool must be a pinned CPU tensor")
+    dev = c_void_p()
+    st = _lib.ra_host_device_pointer(t.data_ptr(), ctypes.byref(dev))
+    if st != RA_OK:
+        raise RAError(st, "ra_host_device_pointer")
+    return int(dev.value)
+
+
+def _pool_ptr(t, name):
+    # GPU pools by address; pinned host pools by their device mapping
+    if t.device.type == "cpu":
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor")
+        p = host_device_pointer(t)
+        if p % 16:
+            raise ValueError(f"{name} must be 16-byte aligned")
+        return p
+    return _ptr(t, torch.bfloat16, name, align=16)
+
+
 class KVLayer:
     """One layer's paged KV cache: bf16 pools [num_pages][H_kv][64][128] and
-    an int32 block table [B][max_pages]."""
+    an int32 block table [B][max_pages] (on the GPU). The pools may be GPU
+    tensors or pinned host tensors, which the kernels then read over the
+    host link (a host-resident tier)."""
 
     def __init__(self, k_pool, v_pool, block_table):
         for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool")):
@@ -168,7 +201,7 @@ class KVLayer:
             raise ValueError("block_table must be [B][max_pages]")
         self.k_pool, self.v_pool, self.block_table = k_pool, v_pool, block_table
         self.struct = KVLayerStruct(
-            _ptr(k_pool, torch.bfloat16, "k_pool", align=16), _ptr(v_pool, torch.bfloat16, "v_pool", align=16),
+            _pool_ptr(k_pool, "k_pool"), _pool_ptr(v_pool, "v_pool"),
             _ptr(block_table, torch.int32, "block_table"), k_pool.shape[0],
             block_table.shape[1], k_pool.shape[1], HEAD_DIM, PAGE_SIZE)
 
@@ -340,4 +373,32 @@ def graph_search(q, kv: KVLayer, seq: int, N: int, nbr, entry, ef: int, k: int, 
         _stream(stream))
     if st != RA_OK:
         raise RAError(st, "ra_graph_search")
+
+SPARSE_MAX_K = 4096
+
+
+def sparse_attend(q, kv: KVLayer, seq: int, N: int, idx, out, out_lse, stream=None) -> None:
+    """ra_sparse_attend: softmax . V over the positions idx [H_q][k] (int32,
+    -1 skipped) for each query head; out fp32 [H_q][128], out_lse [H_q]."""
+    H_q = q.shape[0]
+    k = idx.shape[1]
+    if idx.shape[0] != H_q or tuple(out.shape) != (H_q, HEAD_DIM) or tuple(out_lse.shape) != (H_q,):
+        raise ValueError("idx must be [H_q][k], out [H_q][128], out_lse [H_q]")
+    st = _lib.ra_sparse_attend(
+        _ptr(q, torch.bfloat16, "q", align=16), H_q, ctypes.byref(kv.struct), seq, N,
+        _ptr(idx, torch.int32, "idx"), k, _ptr(out, torch.float32, "out"),
+        _ptr(out_lse, torch.float32, "out_lse"), _stream(stream))
+    if st != RA_OK:
+        raise RAError(st, "ra_sparse_attend")
+
+
+def merge_partials(out_a, lse_a, out_b, lse_b, out, lse, stream=None) -> None:
+    """ra_merge_partials: the LSE merge of two partial outputs per head."""
+    H = lse_a.shape[0]
+    st = _lib.ra_merge_partials(
+        _ptr(out_a, torch.float32, "out_a"), _ptr(lse_a, torch.float32, "lse_a"),
+        _ptr(out_b, torch.float32, "out_b"), _ptr(lse_b, torch.float32, "lse_b"), H,
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), _stream(stream))
+    if st != RA_OK:
+        raise RAError(st, "ra_merge_partials")
 

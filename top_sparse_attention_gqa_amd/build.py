@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libra.so")
 
 SOURCES = ["ra_api.cpp", "kv_append.hip", "score_scan.hip", "topk_select.hip",
-           "gather_attn.hip", "prefill_topk.hip", "graph_search.hip"]
+           "gather_attn.hip", "prefill_topk.hip", "graph_search.hip", "sparse_attend.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -466,4 +466,51 @@ ra_status ra_graph_search(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
   return RA_OK;
 }
 
+ra_status ra_sparse_attend(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv, int32_t seq,
+                           int32_t N, const int32_t* idx, int32_t k, float* out, float* out_lse,
+                           hipStream_t stream) {
+  ra_status st = check_kv(kv);
+  if (st != RA_OK) return st;
+  if (!q || !idx || !out || !out_lse) return RA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(idx, 4) || !aligned(out, 4) || !aligned(out_lse, 4))
+    return RA_ERR_INVALID_ARGUMENT;
+  if (H_q <= 0 || seq < 0 || k < 1 || k > RA_SPARSE_MAX_K) return RA_ERR_INVALID_ARGUMENT;
+  if (H_q % kv->H_kv != 0) return RA_ERR_INVALID_ARGUMENT;
+  if (N <= 0 || int64_t(N) > int64_t(kv->max_pages) * kPage) return RA_ERR_INVALID_ARGUMENT;
+  SaParams p{};
+  p.q = q;
+  p.k_pool = kv->k_pool;
+  p.v_pool = kv->v_pool;
+  p.block_table = kv->block_table + size_t(seq) * kv->max_pages;
+  p.H_q = H_q;
+  p.H_kv = kv->H_kv;
+  p.N = N;
+  p.num_pages = kv->num_pages;
+  p.k = k;
+  p.idx = idx;
+  p.out = out;
+  p.out_lse = out_lse;
+  if (launch_sparse_attend(p, stream) != hipSuccess) return RA_ERR_HIP;
+  return RA_OK;
+}
+
+ra_status ra_merge_partials(const float* out_a, const float* lse_a, const float* out_b,
+                            const float* lse_b, int32_t H, float* out, float* lse,
+                            hipStream_t stream) {
+  if (!out_a || !lse_a || !out_b || !lse_b || !out || !lse || H <= 0)
+    return RA_ERR_INVALID_ARGUMENT;
+  if (launch_merge_partials(out_a, lse_a, out_b, lse_b, H, out, lse, stream) != hipSuccess)
+    return RA_ERR_HIP;
+  return RA_OK;
+}
+
+ra_status ra_host_device_pointer(const void* host, void** dev) {
+  if (!host || !dev) return RA_ERR_INVALID_ARGUMENT;
+  if (hipHostGetDevicePointer(dev, const_cast<void*>(host), 0) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error
+    return RA_ERR_HIP;
+  }
+  return RA_OK;
+}
+
 }  // extern "C"

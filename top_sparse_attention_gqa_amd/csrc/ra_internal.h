@@ -138,6 +138,23 @@ struct PfLayout {
   size_t off_pmax, off_tau, off_seg_off, off_seg_cnt, off_cand, total;
 };
 
+// Attention over listed positions, and the merge of two partials
+// (sparse_attend.hip).
+struct SaParams {
+  const uint16_t* q;          // [H_q][128]
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_table; // the sequence's row
+  int32_t H_q, H_kv, N, num_pages, k;
+  const int32_t* idx;         // [H_q][k]
+  float* out;                 // [H_q][128]
+  float* out_lse;             // [H_q]
+};
+hipError_t launch_sparse_attend(const SaParams& p, hipStream_t s);
+hipError_t launch_merge_partials(const float* oa, const float* la, const float* ob,
+                                 const float* lb, int32_t H, float* out, float* lse,
+                                 hipStream_t s);
+
 // Key-graph search (graph_search.hip).
 constexpr int kGsBatch = RA_GRAPH_BATCH;  // keys expanded per round of the search
 struct GsParams {
