@@ -54,6 +54,7 @@ WORKLOAD_TEXT = {
     "C4": "16 ragged sequences (N uniform in [32768, 131072]) of a Llama-3-8B layer, 64-token pages in shuffled order, k=2% of each length",
     "C5P": "C5 with a pyramid-shaped per-layer budget: k_l falls linearly with depth (slope 0.5, 1.5 to 0.5 times the mean) around the uniform 1% of the current length, with the same total",
     "G1": "query-aware key graph of a Llama-3-8B layer (H_q=32, H_kv=8, d=128) at N=131072, n_sink=128, window=512: built from the exact top-32 keys of all N prefill rows (degree 32), searched per decode query (ef=128) for the top 100; queries around 32 shared directions per head (spread 0.35), prefill rows and decode queries alike",
+    "O1": "one Llama-3-8B layer (H_q=32, H_kv=8, d=128) at N=1048576 with its KV in pinned host memory and W (n_sink=128 + window=512) in HBM; Omega (top 100) retrieved by the key graph (from 262144 prefill rows, degree 32, ef=128) reading host-resident keys, attended from host memory, merged with W",
     "P1": "prefill exact top-k: T=1024 query rows of a Llama-3-8B layer (H_q=32, H_kv=8, d=128) against N=131072 keys, k=100, n_sink=128, window=512",
     "C5": "32 Llama-3-8B layers (H_q=32, H_kv=8, d=128) at N=1048576, k=1% of the current length, KV of every layer resident in HBM; each token step appends one K/V row per layer and runs the decode step of all 32 layers",
 }
@@ -183,8 +184,9 @@ def main():
     model = args.workload in ("C5", "C5P")
     prefill = args.workload == "P1"
     graph = args.workload == "G1"
+    offload = args.workload == "O1"
     if args.steps is None:
-        args.steps = 1000 if model else (50 if prefill or graph else 200)
+        args.steps = 1000 if model else (50 if prefill or graph or offload else 200)
     if args.warmup is None:
         args.warmup = 2 if model else (5 if prefill else 20)
 
@@ -197,6 +199,8 @@ def main():
         run_prefill(args)
     elif graph:
         run_graph(args)
+    elif offload:
+        run_offload(args)
     else:
         run_layer(args)
 
@@ -787,6 +791,177 @@ def run_graph(args):
                      "avg_launch_us": round(gpu_ms * 1e3, 2)},
         "cpu_baseline": cpu,
     }
+    print(json.dumps(line), flush=True)
+
+
+# two KV tiers: one "step" is one layer's decode with its KV in host memory
+OF_N, OF_PREFILL_ROWS = 1048576, 262144
+
+
+def run_offload(args):
+    import numpy as np
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+
+    import synth
+    import top_sparse_attention_gqa_amd as ra
+
+    dev = "cuda"
+    H_q, H_kv, N, ns, win, k = GR_H_Q, GR_H_KV, OF_N, GR_SINK, GR_WINDOW, GR_K
+    L = synth.make_layer(H_q, H_kv, [N], [k], ns, win, 64, 9600, dev)
+    kv_dev = ra.KVLayer(L.k_pool, L.v_pool, L.block_table)
+    # the index is built at prefill time, while the layer is still in HBM
+    t0 = time.perf_counter()
+    lists = np.empty((OF_PREFILL_ROWS, H_q, GR_LIST_K), dtype=np.int32)
+    hubs = np.empty((OF_PREFILL_ROWS, H_q), dtype=np.int32)
+    ws_l = ra.alloc_prefill_workspace(GR_CHUNK, H_q, N, GR_LIST_K, device=dev)
+    ol = torch.empty(GR_CHUNK, H_q, GR_LIST_K, dtype=torch.int32, device=dev)
+    oh = torch.empty(GR_CHUNK, H_q, 1, dtype=torch.int32, device=dev)
+    for c0 in range(0, OF_PREFILL_ROWS, GR_CHUNK):
+        Q = synth.make_topic_queries(GR_CHUNK, H_q, L.u, GR_TOPIC_SEED, GR_TOPICS, GR_SPREAD,
+                                     9700 + c0, dev)
+        ra.prefill_topk(Q, kv_dev, 0, N, GR_LIST_K, ns, win, ol, ws_l)
+        lists[c0:c0 + GR_CHUNK] = ol.cpu().numpy()
+        ra.prefill_topk(Q, kv_dev, 0, N, 1, ns, win, oh, ws_l)
+        hubs[c0:c0 + GR_CHUNK] = oh.cpu().numpy()[:, :, 0]
+        if c0 % (16 * GR_CHUNK) == 0:
+            print(f"O1: prefill rows {c0 + GR_CHUNK}/{OF_PREFILL_ROWS}", file=sys.stderr, flush=True)
+    del ws_l
+    t_lists = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        graphs = list(ex.map(lambda h: ra.graph_build(hubs[:, h], lists[:, h, :], N, GR_D),
+                             range(H_q)))
+    t_build = time.perf_counter() - t0
+    del lists, hubs
+    nbr = torch.tensor(np.stack([g[0] for g in graphs]), dtype=torch.int32, device=dev)
+    entry = torch.tensor([g[1] for g in graphs], dtype=torch.int32, device=dev)
+    graph0 = graphs[0]
+    del graphs
+    print(f"O1: index built ({t_lists:.1f} s prefill top-k, {t_build:.1f} s projection)",
+          file=sys.stderr, flush=True)
+    # offload: the pools to pinned host memory, W's pages kept in HBM
+    kp = L.k_pool.cpu().pin_memory()
+    vp = L.v_pool.cpu().pin_memory()
+    kv_host = ra.KVLayer(kp, vp, L.block_table)
+    W = np.r_[0:ns, N - win:N].astype(np.int32)
+    kd, td = synth.copy_pages(L.k_pool, L.block_table, 0, W, dev)
+    vd, _ = synth.copy_pages(L.v_pool, L.block_table, 0, W, dev)
+    kv_w = ra.KVLayer(kd, vd, td)
+    widx = torch.tensor(np.tile(W, (H_q, 1)), device=dev)
+    host_bytes = kp.numel() * 2 + vp.numel() * 2
+    qs = list(synth.make_topic_queries(GR_QUERIES, H_q, L.u, GR_TOPIC_SEED, GR_TOPICS, GR_SPREAD,
+                                       9990, dev))
+    omega = torch.empty(H_q, k, dtype=torch.int32, device=dev)
+    vis = torch.empty(H_q, dtype=torch.int32, device=dev)
+    o_om, l_om = torch.empty(H_q, 128, device=dev), torch.empty(H_q, device=dev)
+    o_w, l_w = torch.empty(H_q, 128, device=dev), torch.empty(H_q, device=dev)
+    out, lse = torch.empty(H_q, 128, device=dev), torch.empty(H_q, device=dev)
+
+    def step(q):
+        ra.graph_search(q, kv_host, 0, N, nbr, entry, GR_EF, k, omega, vis)
+        ra.sparse_attend(q, kv_host, 0, N, omega, o_om, l_om)
+        ra.sparse_attend(q, kv_w, 0, N, widx, o_w, l_w)
+        ra.merge_partials(o_w, l_w, o_om, l_om, out, lse)
+
+    # recall against the exact decode path on the HBM copy
+    seq = torch.tensor([N], dtype=torch.int32, device=dev)
+    kt = torch.tensor([k], dtype=torch.int32, device=dev)
+    ws_d = ra.alloc_workspace(1, H_q, H_kv, N, k, device=dev)
+    ex_out = torch.empty(1, H_q, 128, device=dev)
+    ex_lse = torch.empty(1, H_q, device=dev)
+    ex_idx = torch.empty(1, H_q, k, dtype=torch.int32, device=dev)
+    recalls, scanned, out_err = [], [], []
+    M = N - ns - win
+    for q in qs:
+        ra.decode_step(q.view(1, H_q, 128), kv_dev, seq, N, kt, k, ns, win, ex_out, ex_lse, ex_idx, ws_d)
+        step(q)
+        torch.cuda.synchronize()
+        e_i, g_i = ex_idx.cpu().numpy()[0], omega.cpu().numpy()
+        for h in range(H_q):
+            recalls.append(np.intersect1d(e_i[h], g_i[h][g_i[h] >= 0]).size / k)
+        scanned.extend((vis.cpu().numpy() / M).tolist())
+        out_err.append(float((out - ex_out[0]).abs().max()))
+    for i in range(args.warmup):
+        step(qs[i % len(qs)])
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(args.steps):
+        step(qs[i % len(qs)])
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    gpu_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    # the exact step on the same host-resident layer: every key over the host link
+    ra.decode_step(qs[0].view(1, H_q, 128), kv_host, seq, N, kt, k, ns, win, ex_out, ex_lse, ex_idx, ws_d)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        ra.decode_step(qs[0].view(1, H_q, 128), kv_host, seq, N, kt, k, ns, win, ex_out, ex_lse,
+                       ex_idx, ws_d)
+    torch.cuda.synchronize()
+    exact_host_ms = (time.perf_counter() - t0) * 1e3 / 3
+    t0 = time.perf_counter()
+    for _ in range(10):
+        ra.decode_step(qs[0].view(1, H_q, 128), kv_dev, seq, N, kt, k, ns, win, ex_out, ex_lse,
+                       ex_idx, ws_d)
+    torch.cuda.synchronize()
+    exact_dev_ms = (time.perf_counter() - t0) * 1e3 / 10
+    sc = float(np.mean(scanned))
+    # bytes a step reads from host memory: a K row per visited key (search),
+    # a K and a V row per retrieved key (attention)
+    link_bytes = sc * M * H_q * 256 + H_q * k * 512
+    line = {
+        "metric": "two-tier decode-step latency (ms) with KV in host memory + Recall@100, Llama-3-8B layer @1M",
+        "value": round(ms, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: OOD queries vs K around 32 shared directions per head, prefill and decode alike; x4 sink keys)",
+        "config": {"workload": f"O1: {WORKLOAD_TEXT['O1']}", "H_q": H_q, "H_kv": H_kv,
+                   "head_dim": 128, "seq_len": N, "k": k, "n_sink": ns, "window": win,
+                   "prefill_rows": OF_PREFILL_ROWS, "list_k": GR_LIST_K, "degree": GR_D,
+                   "ef": GR_EF, "kv_bytes_in_host_memory": host_bytes,
+                   "w_bytes_in_hbm": int(kd.numel() * 4)},
+        "recall_at_100": round(float(np.mean(recalls)), 4),
+        "keys_scanned_frac": round(sc, 5),
+        "out_max_abs_diff_vs_exact": round(float(np.max(out_err)), 5),
+        "host_link_bytes_per_step": int(link_bytes),
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "exact_step_from_host_memory_ms": round(exact_host_ms, 3),
+        "exact_step_from_hbm_ms": round(exact_dev_ms, 4),
+        "build_s": {"prefill_top_k": round(t_lists, 2), "graph_build_host": round(t_build, 2)},
+        "roofline": {"kernel": "graph_search_kernel + sparse_attend_kernel over host memory",
+                     "bound": "hbm", "achieved": round(link_bytes / (gpu_ms * 1e-3) / 1e9, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(link_bytes / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 6),
+                     "traffic": None, "algorithmic_bytes_per_launch": int(link_bytes),
+                     "avg_launch_us": round(gpu_ms * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        K0 = synth.depage(L.k_pool, L.block_table, 0, N, heads=[0])[:, 0, :]
+        qb = synth.bf16_bits(qs[0])
+        tt = time.perf_counter()
+        done = 0
+        while time.perf_counter() - tt < 12.0 and done < H_q // H_kv:
+            oracle.graph_search(qb[done], K0, graph0[0], graph0[1], GR_EF, k, batch=ra.GRAPH_BATCH)
+            done += 1
+        spent = time.perf_counter() - tt
+        line["cpu_baseline"] = {
+            "value": round(spent / done * H_q * 1e3, 1), "unit": "ms", "cores": 1, "kind": "oracle",
+            "sample": f"oracle graph_search (Python, fp32 ordered scores, keys in host memory) for "
+                      f"{done} query heads of KV head 0 on head 0's graph, {spent:.1f} s, scaled "
+                      f"to {H_q} heads (the search part of the step)"}
     print(json.dumps(line), flush=True)
 
 

@@ -28,7 +28,7 @@ __device__ __forceinline__ float wave_sum_f(float v) {
 __global__ __launch_bounds__(kSaThreads) void sparse_attend_kernel(SaParams p) {
   __shared__ float z[RA_SPARSE_MAX_K];
   __shared__ float red[kSaThreads / 64];
-  __shared__ float part[kSaThreads / 128][kHeadDim];
+  __shared__ float part[kSaThreads / 64][kHeadDim];
   const int h = blockIdx.x;
   const int g = h / (p.H_q / p.H_kv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -101,21 +101,34 @@ __global__ __launch_bounds__(kSaThreads) void sparse_attend_kernel(SaParams p) {
   float Z = 0.0f;
 #pragma unroll
   for (int w = 0; w < kSaThreads / 64; ++w) Z += red[w];
-  // weighted V rows: half hv of the block takes the positions i = hv mod 2,
-  // thread d of the half one dimension (a V row is 256 coalesced bytes)
-  const int hv = tid >> 7, d = tid & 127;
-  float acc = 0.0f;
-  for (int i = hv; i < p.k; i += 2) {
-    const float w = z[i];
-    if (w != 0.0f) {
-      const uint16_t v = row(p.v_pool, idx[i])[d];
-      acc = fmaf(w, __uint_as_float(uint32_t(v) << 16), acc);
+  // weighted V rows: wave w takes the positions i = w mod 4, lane l the
+  // dimensions 2 l, 2 l + 1 (a row is 256 coalesced bytes); four rows are
+  // in flight at a time
+  constexpr int kW = kSaThreads / 64;
+  float a0 = 0.0f, a1 = 0.0f;
+  for (int i0 = wave; i0 < p.k; i0 += 4 * kW) {
+    uint32_t v[4];
+    float w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + r * kW;
+      w[r] = i < p.k ? z[i] : 0.0f;
+      v[r] = w[r] != 0.0f ? reinterpret_cast<const uint32_t*>(row(p.v_pool, idx[i]))[lane] : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      a0 = fmaf(w[r], __uint_as_float(v[r] << 16), a0);
+      a1 = fmaf(w[r], __uint_as_float(v[r] & 0xFFFF0000u), a1);
     }
   }
-  part[hv][d] = acc;
+  part[wave][2 * lane] = a0;
+  part[wave][2 * lane + 1] = a1;
   __syncthreads();
   if (tid < kHeadDim) {
-    p.out[size_t(h) * kHeadDim + tid] = (part[0][tid] + part[1][tid]) / Z;
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) t += part[w][tid];
+    p.out[size_t(h) * kHeadDim + tid] = t / Z;
     if (tid == 0) p.out_lse[h] = m + logf(Z);
   }
 }
