@@ -342,7 +342,8 @@ def run_layer(args):
 
 def run_model(args):
     """C5: every token step appends one K/V row to each of the 32 layers and
-    runs each layer's decode step; value = ms per token step. C5P: the same
+    runs each layer's decode step (ra_append_decode_step: the rows are
+    written inside the step); value = ms per token step. C5P: the same
     with per-layer budgets from ra_layer_budgets (slope 0.5)."""
     import numpy as np
     import torch
@@ -381,12 +382,13 @@ def run_model(args):
     def token_step(s, ev=None):
         for l in range(n_layers):
             q, kn, vn = streams[l][0][s], streams[l][1][s], streams[l][2][s]
-            ra.kv_append(kvs[l], kn, vn, pos_all[s])
             a = (q, kvs[l], seq_all[s], max_seq_len, k_all[s, l], k_max, c.n_sink, c.window,
                  outs[l], lses[l], idxs[l], ws)
             if ev is None:
-                ra.decode_step(*a)
+                # the append is written inside the step (one launch fewer)
+                ra.append_decode_step(kn, vn, pos_all[s], *a)
             else:
+                ra.kv_append(kvs[l], kn, vn, pos_all[s])
                 ra.decode_stages(*a, 0, S - 1)
                 ev[2 * l].record()
                 ra.decode_stages(*a, S, S)

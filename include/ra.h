@@ -144,6 +144,24 @@ ra_status ra_decode_step(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
                          size_t ws_bytes, uint32_t flags, hipStream_t stream);
 
 /*
+ * ra_kv_append followed by ra_decode_step, in one call and one launch
+ * fewer: the new token's rows (k_new, v_new: device bf16 [B][H_kv][128],
+ * 16-byte aligned; pos: device int32 [B], as for ra_kv_append) are written
+ * by the step's second kernel, after the sampled bound's kernel (which may
+ * then read the slot's previous contents: that only bounds the candidates)
+ * and before every kernel whose reads decide the result. seq_lens must
+ * count the new token, as after ra_kv_append. Results equal those of the
+ * two separate calls. Validation and errors as for both.
+ */
+ra_status ra_append_decode_step(const uint16_t* k_new, const uint16_t* v_new,
+                                const int32_t* pos, const uint16_t* q, int32_t H_q,
+                                const ra_kv_layer* kv, const int32_t* seq_lens, int32_t B,
+                                int32_t max_seq_len, const int32_t* k, int32_t k_max,
+                                int32_t n_sink, int32_t window, float* out, float* out_lse,
+                                int32_t* out_idx, void* ws, size_t ws_bytes, uint32_t flags,
+                                hipStream_t stream);
+
+/*
  * The kernels of one decode step, in launch order. ra_decode_step runs
  * stages RA_STAGE_SAMPLE .. RA_STAGE_MERGE; ra_decode_stages runs a contiguous
  * sub-range of them with the same arguments, so each kernel can be timed or

@@ -47,7 +47,7 @@ EXPORTS = ["ra_abi_version", "ra_status_str", "ra_decode_workspace_bytes",
            "ra_workspace_scores_offset", "ra_workspace_rescan_count_offset",
            "ra_prefill_workspace_bytes", "ra_prefill_topk", "ra_prefill_stages",
            "ra_layer_budgets", "ra_graph_build", "ra_graph_search", "ra_sparse_attend",
-           "ra_merge_partials", "ra_host_device_pointer"]
+           "ra_merge_partials", "ra_host_device_pointer", "ra_append_decode_step"]
 
 
 class KVLayerStruct(ctypes.Structure):
@@ -99,6 +99,8 @@ _lib.ra_decode_step.restype = c_int
 _lib.ra_decode_step.argtypes = _DECODE_ARGS + [c_uint32, c_void_p]
 _lib.ra_decode_stages.restype = c_int
 _lib.ra_decode_stages.argtypes = _DECODE_ARGS + [c_uint32, c_int32, c_int32, c_void_p]
+_lib.ra_append_decode_step.restype = c_int
+_lib.ra_append_decode_step.argtypes = [c_void_p, c_void_p, c_void_p] + _DECODE_ARGS + [c_uint32, c_void_p]
 
 
 class RAError(RuntimeError):
@@ -262,6 +264,25 @@ def decode_step(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, window,
     if st != RA_OK:
         raise RAError(st, "ra_decode_step")
 
+
+def append_decode_step(k_new, v_new, pos, q, kv: KVLayer, seq_lens, max_seq_len, k, k_max,
+                       n_sink, window, out, out_lse, out_idx, ws, stream=None,
+                       keep_scores=False) -> None:
+    """ra_append_decode_step: kv_append of (k_new, v_new) at pos, then the
+    decode step, with one launch fewer (the rows are written inside it)."""
+    B, H_q = q.shape[0], q.shape[1]
+    st = _lib.ra_append_decode_step(
+        _ptr(k_new, torch.bfloat16, "k_new", align=16), _ptr(v_new, torch.bfloat16, "v_new", align=16),
+        _ptr(pos, torch.int32, "pos"),
+        _ptr(q, torch.bfloat16, "q", align=16), H_q, ctypes.byref(kv.struct),
+        _ptr(seq_lens, torch.int32, "seq_lens"), B, max_seq_len, _ptr(k, torch.int32, "k"),
+        k_max, n_sink, window, _ptr(out, torch.float32, "out"),
+        _ptr(out_lse, torch.float32, "out_lse", nullable=True),
+        _ptr(out_idx, torch.int32, "out_idx", nullable=(k_max == 0)),
+        _ptr(ws, torch.uint8, "ws", align=256), ws.numel(),
+        DECODE_KEEP_SCORES if keep_scores else 0, _stream(stream))
+    if st != RA_OK:
+        raise RAError(st, "ra_append_decode_step")
 
 def scores_view(ws: torch.Tensor, B, H_q, H_kv, max_seq_len, k_max) -> torch.Tensor:
     """The fp32 score rows [B][H_q][row_stride] inside a workspace: after the

@@ -270,6 +270,36 @@ ra_status ra_decode_stages(const uint16_t* q, int32_t H_q,
   return RA_OK;
 }
 
+ra_status ra_append_decode_step(const uint16_t* k_new, const uint16_t* v_new,
+                                const int32_t* pos, const uint16_t* q, int32_t H_q,
+                                const ra_kv_layer* kv, const int32_t* seq_lens, int32_t B,
+                                int32_t max_seq_len, const int32_t* k, int32_t k_max,
+                                int32_t n_sink, int32_t window, float* out, float* out_lse,
+                                int32_t* out_idx, void* ws, size_t ws_bytes, uint32_t flags,
+                                hipStream_t stream) {
+  if (!k_new || !v_new || !pos) return RA_ERR_INVALID_ARGUMENT;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos, 4))
+    return RA_ERR_INVALID_ARGUMENT;
+  WsLayout L;
+  ra_status st = validate_decode(q, H_q, kv, seq_lens, B, max_seq_len, k,
+                                 k_max, n_sink, window, out, out_idx, ws,
+                                 ws_bytes, &L);
+  if (st != RA_OK) return st;
+  if (flags & ~RA_DECODE_KEEP_SCORES) return RA_ERR_INVALID_ARGUMENT;
+  Params p = make_params(q, H_q, kv, seq_lens, B, max_seq_len, k, k_max,
+                         n_sink, window, out, out_lse, out_idx, ws, L);
+  p.num_cus = cu_count();
+  p.keep_scores = (flags & RA_DECODE_KEEP_SCORES) ? 1 : 0;
+  p.app_k = k_new;
+  p.app_v = v_new;
+  p.app_pos = pos;
+  if (launch_sample(p, stream) != hipSuccess || launch_threshold(p, stream) != hipSuccess ||
+      launch_scan(p, stream) != hipSuccess || launch_select(p, stream) != hipSuccess ||
+      launch_gather(p, stream) != hipSuccess || launch_merge(p, stream) != hipSuccess)
+    return RA_ERR_HIP;
+  return RA_OK;
+}
+
 ra_status ra_decode_step(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
                          const int32_t* seq_lens, int32_t B,
                          int32_t max_seq_len, const int32_t* k, int32_t k_max,

@@ -73,6 +73,10 @@ bool ws_layout(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seq_len,
                int32_t k_max, WsLayout* out);
 
 struct Params {
+  // a token's K and V rows to append before the scan (null: none)
+  const uint16_t* app_k;     // [B][H_kv][128]
+  const uint16_t* app_v;
+  const int32_t* app_pos;    // [B]
   const uint16_t* q;
   const uint16_t* k_pool;
   const uint16_t* v_pool;

@@ -383,6 +383,26 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(Params p) {
   __shared__ uint32_t s_d, s_above, s_cnt;
   __shared__ int64_t tmp[16];
 
+  if (p.app_pos != nullptr && hq % p.G == 0 && tid < 32) {
+    // the step's new token: the group's first head writes its K and V rows
+    // (lanes 0..15 K, 16..31 V, 16 bytes each). The sample kernel ran
+    // before and the scan runs after this launch: the sample only bounds
+    // the candidates (a stale row there costs at most the rescan), and
+    // everything that reads keys or values for the result comes later.
+    const int g = hq / p.G;
+    const int ps = p.app_pos[b];
+    if (ps >= 0 && ps < p.max_pages * kPage) {
+      const int pg = p.block_table[size_t(b) * p.max_pages + ps / kPage];
+      if ((unsigned)pg < (unsigned)p.num_pages) {
+        const int part = tid >> 4, c = tid & 15;
+        const uint16_t* src = (part ? p.app_v : p.app_k) + (size_t(b) * p.H_kv + g) * kHeadDim + c * 8;
+        uint16_t* dst = const_cast<uint16_t*>(part ? p.v_pool : p.k_pool) +
+                        ((size_t(pg) * p.H_kv + g) * kPage + (ps & (kPage - 1))) * kHeadDim + c * 8;
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      }
+    }
+  }
+
   if (bh == 0) {
     // unit prefix over the batch
     const int per = (p.B + kSelThreads - 1) / kSelThreads;
