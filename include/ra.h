@@ -312,7 +312,7 @@ ra_status ra_layer_budgets(int32_t n_layers, int32_t k_mean, int32_t slope_permi
 #define RA_GRAPH_MAX_DEGREE 64
 #define RA_GRAPH_MAX_EF 256
 #define RA_GRAPH_MAX_N (1 << 20) /* keys a graph spans (the visited set is in LDS) */
-#define RA_GRAPH_BATCH 4         /* keys a search expands per round */
+#define RA_GRAPH_BATCH 16        /* keys a search expands per round */
 
 /*
  * Build one query head's key graph on the host from its prefill queries'

@@ -355,7 +355,7 @@ def layer_budgets(n_layers: int, k_mean: int, slope_permille: int) -> list:
 GRAPH_MAX_DEGREE = 64
 GRAPH_MAX_EF = 256
 GRAPH_MAX_N = 1 << 20
-GRAPH_BATCH = 4  # keys a search expands per round
+GRAPH_BATCH = 16  # keys a search expands per round
 
 
 def graph_build(hubs, lists, N: int, D: int):
