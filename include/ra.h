@@ -246,8 +246,13 @@ size_t ra_prefill_workspace_bytes(int32_t T, int32_t H_q, int32_t N, int32_t k);
  *           then -1.
  *  ws, ws_bytes: device workspace of at least ra_prefill_workspace_bytes
  *           bytes, 256-byte aligned, no initial contents required.
- * The scores run on MFMA twice (page maxima, then a filter at a per-row
- * threshold that provably keeps the whole top-k); nothing else is stored.
+ * The scores run on MFMA: page maxima over one page in 8, a per-row bound
+ * from them, then a filter over every key at that bound. A row whose filter
+ * kept at least k_eff keys, all of them stored, has its exact top-k among
+ * them (every key below the bound ranks below every key kept); any other
+ * row is flagged and recomputed, with the row blocks holding it, by the
+ * exact pass (page maxima of every page, whose k_eff-th largest provably
+ * keeps the whole top-k). The score matrix is never stored.
  * Validation and ownership as for ra_decode_step.
  */
 ra_status ra_prefill_topk(const uint16_t* q, int32_t T, int32_t H_q,
@@ -265,12 +270,23 @@ ra_status ra_prefill_topk(const uint16_t* q, int32_t T, int32_t H_q,
  * RA_ERR_INVALID_ARGUMENT.
  */
 typedef enum ra_prefill_stage {
-  RA_PF_STAGE_MAXIMA = 0,    /* contraction 1: largest score per (row, page) */
-  RA_PF_STAGE_THRESHOLD = 1, /* per row: the k-th largest (page max, page) */
-  RA_PF_STAGE_FILTER = 2,    /* contraction 2: keys at or above it */
-  RA_PF_STAGE_SELECT = 3,    /* per row: exact top-k, ascending */
-  RA_PF_STAGE_COUNT = 4
+  RA_PF_STAGE_SAMPLE = 0,        /* contraction over one page in 16: sampled page maxima */
+  RA_PF_STAGE_BOUND = 1,         /* per row: the sampled bound (R-th largest sampled pair) */
+  RA_PF_STAGE_FILTER = 2,        /* contraction: keys at or above the bound */
+  RA_PF_STAGE_SELECT = 3,        /* per row: exact top-k, or the row is flagged */
+  RA_PF_STAGE_EXACT_MAXIMA = 4,  /* flagged row blocks: page maxima of every page */
+  RA_PF_STAGE_EXACT_THRESHOLD = 5, /* the k-th largest (page max, page) */
+  RA_PF_STAGE_EXACT_FILTER = 6,  /* keys at or above it */
+  RA_PF_STAGE_EXACT_SELECT = 7,  /* exact top-k of the flagged rows */
+  RA_PF_STAGE_COUNT = 8
 } ra_prefill_stage;
+
+/*
+ * Where the per-row flags of the last call live in its workspace: uint32
+ * [T * H_q], 1 for a row whose sampled bound fell short (it was then
+ * computed by the exact stages). For tests and diagnostics.
+ */
+size_t ra_prefill_workspace_fail_offset(int32_t T, int32_t H_q, int32_t N, int32_t k);
 
 ra_status ra_prefill_stages(const uint16_t* q, int32_t T, int32_t H_q,
                             const ra_kv_layer* kv, int32_t seq, int32_t N,

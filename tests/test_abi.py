@@ -203,7 +203,16 @@ def test_prefill_stage_range_validation():
     args = [FAKE, 16, 4, ctypes.byref(kv), 0, 640, 8, 4, 8, FAKE, FAKE, 1 << 40]
     assert _lib.raw.ra_prefill_stages(*args, 2, 1, None) == ra.RA_ERR_INVALID_ARGUMENT
     assert _lib.raw.ra_prefill_stages(*args, -1, 1, None) == ra.RA_ERR_INVALID_ARGUMENT
-    assert _lib.raw.ra_prefill_stages(*args, 0, 4, None) == ra.RA_ERR_INVALID_ARGUMENT
+    assert _lib.raw.ra_prefill_stages(*args, 0, ra.PF_STAGE_COUNT, None) == ra.RA_ERR_INVALID_ARGUMENT
+    assert ra.PF_STAGE_COUNT == 8 and len(ra.PF_STAGE_NAMES) == 8
+
+
+def test_prefill_fail_flags_lie_inside_the_workspace():
+    for T, H_q, N, k in [(16, 4, 640, 8), (1024, 32, 131072, 100), (3, 8, 70, 256)]:
+        off = ra.prefill_workspace_fail_offset(T, H_q, N, k)
+        assert off > 0 and off % 256 == 0
+        assert off + 4 * T * H_q <= ra.prefill_workspace_bytes(T, H_q, N, k)
+    assert ra.prefill_workspace_fail_offset(0, 4, 640, 8) == 0
 
 
 def test_layer_budgets_match_the_oracle():

@@ -24,7 +24,7 @@ def _need_gpu():
     assert torch.cuda.is_available(), "GPU tests need an MI355X"
 
 
-def gpu_prefill(L, Q, seq, N, k, ns, win):
+def gpu_prefill(L, Q, seq, N, k, ns, win, flags=False):
     T, H_q = Q.shape[0], Q.shape[1]
     kv = ra.KVLayer(L.k_pool, L.v_pool, L.block_table)
     out = torch.full((T, H_q, max(k, 1)), -7, dtype=torch.int32, device=DEV)
@@ -32,7 +32,10 @@ def gpu_prefill(L, Q, seq, N, k, ns, win):
     ws.fill_(0xA5)  # no initial contents are required
     ra.prefill_topk(Q, kv, seq, N, k, ns, win, out if k else None, ws)
     torch.cuda.synchronize()
-    return out.cpu().numpy()[:, :, :k]
+    got = out.cpu().numpy()[:, :, :k]
+    if not flags:
+        return got
+    return got, ra.prefill_fail_flags(ws, T, H_q, N, k).cpu().numpy()
 
 
 def compare_rows(L, Q, seq, N, k, ns, win, got, rows=None) -> int:
@@ -81,8 +84,11 @@ def test_prefill_constant_keys_take_the_lowest_positions():
     L = synth.make_layer(8, 2, [3000], [8], 16, 64, 2, 3, DEV)
     L.k_pool.fill_(0.125)
     Q = synth.make_prefill_queries(20, 8, L.u, 4, DEV)
-    got = gpu_prefill(L, Q, 0, 3000, 40, 16, 64)
+    got, fail = gpu_prefill(L, Q, 0, 3000, 40, 16, 64, flags=True)
     assert np.array_equal(got, np.broadcast_to(np.arange(16, 56), got.shape))
+    # every key ties: the sampled bound admits all 2920 members of M, more
+    # than a row's lists hold, so every row is decided by the exact pass
+    assert fail.all()
 
 
 def test_prefill_integer_scores_resolve_ties_exactly():
@@ -126,9 +132,41 @@ def test_prefill_index_build_workload_sampled_rows():
     say("case prefill P1: H_q=32 H_kv=8 N=131072 T=1024 k=100 (6 rows checked)")
     L = synth.make_layer(32, 8, [131072], [2048], 128, 512, 64, 0, DEV)
     Q = synth.make_prefill_queries(1024, 32, L.u, 1, DEV)
-    got = gpu_prefill(L, Q, 0, 131072, 100, 128, 512)
+    got, fail = gpu_prefill(L, Q, 0, 131072, 100, 128, 512, flags=True)
     d = compare_rows(L, Q, 0, 131072, 100, 128, 512, got, rows=[0, 1, 127, 128, 511, 1023])
-    say(f"  band differences: {d}")
+    say(f"  band differences: {d}; rows left to the exact pass: {int(fail.sum())}")
+    # the sampled bound decides (nearly) every row here
+    assert fail.sum() <= fail.size // 100
+
+
+def test_prefill_exact_pass_on_flagged_rows():
+    # The sampled half runs, then chosen rows are flagged (their output
+    # poisoned) and the exact half recomputes them: rows in several row
+    # blocks of each KV head, one row block with no flagged row.
+    T, H_q, H_kv, N, k, ns, win = 300, 8, 2, 20000 + 11, 48, 32, 96
+    say(f"case prefill forced exact pass: H_q={H_q} H_kv={H_kv} N={N} T={T} k={k}")
+    L = synth.make_layer(H_q, H_kv, [N], [8], ns, win, 2, 21, DEV)
+    Q = synth.make_prefill_queries(T, H_q, L.u, 22, DEV)
+    kv = ra.KVLayer(L.k_pool, L.v_pool, L.block_table)
+    out = torch.full((T, H_q, k), -7, dtype=torch.int32, device=DEV)
+    ws = ra.alloc_prefill_workspace(T, H_q, N, k, device=DEV)
+    ws.fill_(0xA5)
+    ra.prefill_stages(Q, kv, 0, N, k, ns, win, out, ws, ra.PF_STAGE_SAMPLE, ra.PF_STAGE_SELECT)
+    torch.cuda.synchronize()
+    fail = ra.prefill_fail_flags(ws, T, H_q, N, k)
+    natural = fail.cpu().numpy().copy()
+    forced = [(5, 0), (5, 3), (150, 6), (151, 1), (299, 7)]  # local rows 20, 23, 602, 605, 1199
+    for t, h in forced:
+        fail[t, h] = 1
+        out[t, h] = -7
+    ra.prefill_stages(Q, kv, 0, N, k, ns, win, out, ws, ra.PF_STAGE_EXACT_MAXIMA,
+                      ra.PF_STAGE_EXACT_SELECT)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert (got != -7).all()
+    rows = sorted({t for t, _ in forced} | {0, 100, 200} | set(np.nonzero(natural)[0][:4].tolist()))
+    d = compare_rows(L, Q, 0, N, k, ns, win, got, rows=rows)
+    say(f"  natural exact-pass rows: {int(natural.sum())}; band differences: {d}")
 
 
 def test_prefill_ignores_nan_in_unused_page_slots():

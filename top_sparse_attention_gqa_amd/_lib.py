@@ -38,14 +38,18 @@ HEAD_DIM = 128
 PAGE_SIZE = 64
 DECODE_KEEP_SCORES = 1
 PREFILL_MAX_K = 256
-(PF_STAGE_MAXIMA, PF_STAGE_THRESHOLD, PF_STAGE_FILTER, PF_STAGE_SELECT) = range(4)
-PF_STAGE_COUNT = 4
-PF_STAGE_NAMES = ["maxima", "threshold", "filter", "select"]
+(PF_STAGE_SAMPLE, PF_STAGE_BOUND, PF_STAGE_FILTER, PF_STAGE_SELECT,
+ PF_STAGE_EXACT_MAXIMA, PF_STAGE_EXACT_THRESHOLD, PF_STAGE_EXACT_FILTER,
+ PF_STAGE_EXACT_SELECT) = range(8)
+PF_STAGE_COUNT = 8
+PF_STAGE_NAMES = ["sample", "bound", "filter", "select",
+                  "exact_maxima", "exact_threshold", "exact_filter", "exact_select"]
 
 EXPORTS = ["ra_abi_version", "ra_status_str", "ra_decode_workspace_bytes",
            "ra_kv_append", "ra_decode_step", "ra_decode_stages",
            "ra_workspace_scores_offset", "ra_workspace_rescan_count_offset",
            "ra_prefill_workspace_bytes", "ra_prefill_topk", "ra_prefill_stages",
+           "ra_prefill_workspace_fail_offset",
            "ra_layer_budgets", "ra_graph_build", "ra_graph_search", "ra_sparse_attend",
            "ra_merge_partials", "ra_host_device_pointer", "ra_append_decode_step"]
 
@@ -66,6 +70,8 @@ _lib.ra_workspace_scores_offset.restype = c_size_t
 _lib.ra_workspace_scores_offset.argtypes = [c_int32] * 5 + [POINTER(c_int64)]
 _lib.ra_prefill_workspace_bytes.restype = c_size_t
 _lib.ra_prefill_workspace_bytes.argtypes = [c_int32] * 4
+_lib.ra_prefill_workspace_fail_offset.restype = c_size_t
+_lib.ra_prefill_workspace_fail_offset.argtypes = [c_int32] * 4
 _lib.ra_prefill_topk.restype = c_int
 _lib.ra_prefill_topk.argtypes = [c_void_p, c_int32, c_int32, POINTER(KVLayerStruct), c_int32,
                                  c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
@@ -303,6 +309,17 @@ def prefill_workspace_bytes(T: int, H_q: int, N: int, k: int) -> int:
     return int(_lib.ra_prefill_workspace_bytes(T, H_q, N, k))
 
 
+def prefill_workspace_fail_offset(T: int, H_q: int, N: int, k: int) -> int:
+    return int(_lib.ra_prefill_workspace_fail_offset(T, H_q, N, k))
+
+
+def prefill_fail_flags(ws, T: int, H_q: int, N: int, k: int) -> torch.Tensor:
+    """View of the per-row flags in a prefill workspace: int32 [T][H_q], 1 for
+    a row the exact pass decided (its sampled bound fell short)."""
+    off = prefill_workspace_fail_offset(T, H_q, N, k)
+    return ws[off:off + 4 * T * H_q].view(torch.int32).view(T, H_q)
+
+
 def alloc_prefill_workspace(T, H_q, N, k, device="cuda") -> torch.Tensor:
     n = prefill_workspace_bytes(T, H_q, N, k)
     if n == 0:
@@ -311,7 +328,8 @@ def alloc_prefill_workspace(T, H_q, N, k, device="cuda") -> torch.Tensor:
 
 
 def prefill_stages(q, kv: KVLayer, seq: int, N: int, k: int, n_sink: int, window: int,
-                   out_idx, ws, first=PF_STAGE_MAXIMA, last=PF_STAGE_SELECT, stream=None) -> None:
+                   out_idx, ws, first=PF_STAGE_SAMPLE, last=PF_STAGE_EXACT_SELECT,
+                   stream=None) -> None:
     """ra_prefill_stages (ra_prefill_topk when first..last covers every stage).
     q: bf16 [T][H_q][128]; out_idx: int32 [T][H_q][k] (ascending, -1 padded)."""
     T, H_q = q.shape[0], q.shape[1]

@@ -10,29 +10,32 @@
 // they run on MFMA. v_mfma_f32_32x32x16_bf16 takes 32 keys as its rows (A)
 // and 32 query rows as its columns (B), so a lane's 16 results are 16 keys
 // of one query: a page maximum is an in-lane max plus one swap between the
-// two lane halves. The score matrix is never stored; the contraction runs
-// twice:
-//   1. page maxima: for every row and page of 64 keys, the largest score
-//      over the page's members of M;
-//   2. threshold (one wave per row): the k_eff-th largest pair
-//      (page maximum, page), ordered by maximum, then lower page first;
-//   3. filter: the contraction again; a key is a candidate iff its pair
-//      (score, page) is at or above the threshold;
-//   4. select (one wave per row): the exact top k_eff of the candidates by
-//      (score, lower position), written ascending.
-// Every member of the top-k is a candidate: the k_eff pages whose pairs
-// clear the threshold each hold a key (their maximum) that beats any key
-// whose pair falls below it (a larger score, or an equal one on an earlier
-// page). Candidates lie in those k_eff pages only, so a row has at most
-// 64 k_eff of them. Both passes issue the same MFMA sequence on the same
-// inputs, so a key's score is bit-identical in both.
+// two lane halves. The score matrix is never stored. Keys compare by the
+// pair (score, page), larger score first, then lower page; a set C of keys
+// holding every key whose pair reaches some bound t is an upper set of the
+// ranking (score, lower position): each key outside C ranks below each key
+// in C. So if |C| >= k_eff, the top k_eff of C are the exact answer,
+// whatever t is. Two passes use this:
+//   sampled (stages 0-3): maxima of one page in 8 (page 8 j + 4); the bound
+//      is the need_s-th largest sampled pair, chosen so that about 8 need_s
+//      pages reach it; the filter contraction over every page keeps the
+//      keys at or above it in fixed-size lists; the select takes the top
+//      k_eff, or flags the row if fewer than k_eff were kept or a list
+//      overflowed;
+//   exact (stages 4-7, flagged rows and the row blocks holding them): maxima
+//      of every page; the bound is the k_eff-th largest page pair, which k_eff
+//      pages reach, each holding a key (its maximum) at or above it, so
+//      |C| >= k_eff and C lies in those pages (|C| <= 64 k_eff); filter and
+//      select as before.
+// Every pass issues the same MFMA sequence per key on the same inputs, so a
+// key's score is bit-identical in all of them.
 //
 // Contraction block: 8 waves, each holding the B fragments of 64 query rows
 // in registers (512 rows of one KV head per block), walking a range of pages.
 // A page's 64 K rows (16 KB) are loaded once per block with coalesced 16-byte
-// loads, staged through a double-buffered LDS ring (row chunks XOR-swizzled
-// by row so the 16-byte fragment reads are conflict-free), and read by every
-// wave. The next page is in flight in registers while the current one runs.
+// loads, staged through a four-page LDS ring (row chunks XOR-swizzled by row
+// so the 16-byte fragment reads are conflict-free), and read by every wave.
+// The next two pages are in flight in registers while two are computed.
 #include "ra_internal.h"
 
 namespace ra {
@@ -150,6 +153,18 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
     for (int s = 0; s < 8; ++s)
       qf[q][s] = rv[q] ? *reinterpret_cast<const bf16x8_t*>(qr + 16 * s) : bf16x8_t{};
   }
+  if (p.subset) {
+    // the exact pass: only row blocks holding a flagged row run, and the
+    // filter keeps candidates of flagged rows only
+    bool any = false;
+#pragma unroll
+    for (int q = 0; q < kPfQG; ++q) {
+      const bool f = rv[q] && p.fail[R[q]] != 0u;
+      any = any || f;
+      if (FILTER) rv[q] = f;
+    }
+    if (!__syncthreads_or(any)) return;  // block-uniform
+  }
   float thr[kPfQG];  // a score below it is no candidate
   if constexpr (FILTER) {
 #pragma unroll
@@ -168,9 +183,13 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
     }
   }
 
-  const int chunks = p.Ppad / kPfChunk;
+  // The maxima of the sampled pass walk the sampled pages: index j stands
+  // for page 8 j + 4 (the last page, in a short last group).
+  const bool samp = !FILTER && p.sampled;
+  auto page_at = [&](int j) { return samp ? min(kPfStride * j + kPfStride / 2, p.P - 1) : j; };
+  const int chunks = (samp ? p.Ps_pad : p.Ppad) / kPfChunk;
   const int j0 = int(int64_t(chunks) * z / p.splits) * kPfChunk;
-  const int j1 = min(p.P, int(int64_t(chunks) * (z + 1) / p.splits) * kPfChunk);
+  const int j1 = min(samp ? p.Ps : p.P, int(int64_t(chunks) * (z + 1) / p.splits) * kPfChunk);
   if (j0 >= j1) return;  // block-uniform
 
   const size_t head_off = size_t(g) * (kPage * kHeadDim);
@@ -179,7 +198,7 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
   // LDS writes cover only the page being written.
   auto gload = [&](int j) {
     const uint4* kb = reinterpret_cast<const uint4*>(
-        p.k_pool + size_t(pf_page(p, min(j, j1 - 1))) * p.H_kv * (kPage * kHeadDim) + head_off);
+        p.k_pool + size_t(pf_page(p, page_at(min(j, j1 - 1)))) * p.H_kv * (kPage * kHeadDim) + head_off);
     PfStage st;
     st.a = kb[tid];
     st.b = kb[tid + kPfThreads];
@@ -208,8 +227,11 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
   // Sift the buffered records, one per lane: every score whose pair
   // (score, page) reaches the row's threshold is appended to the row's list.
   // The buffer is a ring: records r_head .. r_tail - 1 (mod kPfRec) wait;
-  // they are sifted 64 at a time (the rest at the end of the range).
+  // they are sifted 64 at a time (the rest at the end of the range). Under
+  // the sampled bound a list holds seg_cap slots: the count goes on past it,
+  // the keys are not written.
   uint32_t r_head = 0, r_tail = 0;  // wave-uniform
+  const uint32_t lim = p.sampled ? uint32_t(p.seg_cap) : 0xFFFFFFFFu;
   auto sift = [&](bool all) {
     while (r_tail - r_head >= 64u || (all && r_tail != r_head)) {
       const uint32_t n = min(64u, r_tail - r_head);
@@ -241,13 +263,16 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
         for (int r = 0; r < 16; ++r) {
           if (okm & (1u << r)) {
             const uint32_t pos = n0 + uint32_t((r >> 2) * 8 + (r & 3));
-            list[at++] = (uint64_t(f2key(v[r])) << 32) | uint32_t(~pos);
+            if (at < lim) list[at] = (uint64_t(f2key(v[r])) << 32) | uint32_t(~pos);
+            ++at;
           }
         }
       }
       r_head += n;
     }
   };
+  uint32_t* const pm_dst = samp ? p.smax : p.pmax;
+  const int pm_stride = samp ? p.Ps_pad : p.Ppad;
   auto pm_flush = [&](int cs) {
     // rows of this wave x pages cs .. cs + 15: four lanes per row, 16 bytes each
 #pragma unroll
@@ -262,7 +287,7 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           v[e] = cs + e0 + e < j1 ? sm.u.pm[wave][qi * (kPfChunk + 1) + e0 + e] : 0u;
-        *reinterpret_cast<uint4*>(p.pmax + Rg * p.Ppad + cs + e0) = uint4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<uint4*>(pm_dst + Rg * pm_stride + cs + e0) = uint4{v[0], v[1], v[2], v[3]};
       }
     }
   };
@@ -341,7 +366,8 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
 
   // One page; keys outside M are masked on pages at the edges of M.
   auto compute = [&](int j, int slot) {
-    const bool full = j * kPage >= p.lo && (j + 1) * kPage <= p.hi;
+    const int n0 = page_at(j) * kPage;
+    const bool full = n0 >= p.lo && n0 + kPage <= p.hi;
     float pm[kPfQG];
 #pragma unroll
     for (int q = 0; q < kPfQG; ++q) pm[q] = -INFINITY;
@@ -349,18 +375,18 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
     for (int half = 0; half < 2; ++half) {
       f32x16_t acc[kPfQG];
       mma(frags(slot, half), acc);
-      if (!full) mask(acc, j * kPage + half * 32);
-      tile_out(acc, j * kPage + half * 32, pm);
+      if (!full) mask(acc, n0 + half * 32);
+      tile_out(acc, n0 + half * 32, pm);
     }
     if constexpr (!FILTER) {
       page_out(pm, j);
       if (chunk_end(j)) pm_flush(j & ~(kPfChunk - 1));
     }
   };
-  // Pages j and j + 1, both wholly inside M: four tiles in straight-line
-  // code, each tile's fragments read while the previous tile's MFMAs run.
-  // Odd waves take the two pages in the other order, so the waves do not
-  // all read the same fragments at once.
+  // Pages j and j + 1 of the pass, both wholly inside M (maxima only): four
+  // tiles in straight-line code, each tile's fragments read while the
+  // previous tile's MFMAs run. Odd waves take the two pages in the other
+  // order, so the waves do not all read the same fragments at once.
   auto compute_pair = [&](int j, int s0) {
     const int odd = wave & 1;
     const int pa = j + odd, pb = j + 1 - odd;
@@ -406,7 +432,7 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
     sb = gload(j + 5);
     // (the filter's record path leaves no registers for the pair's
     // prefetched fragments: it takes the pages one by one)
-    if (!FILTER && j + 1 < j1 && j * kPage >= p.lo && (j + 2) * kPage <= p.hi) {
+    if (!FILTER && j + 1 < j1 && page_at(j) * kPage >= p.lo && (page_at(j + 1) + 1) * kPage <= p.hi) {
       compute_pair(j, s0);
     } else {
       compute(j, s0);
@@ -585,8 +611,20 @@ __device__ __forceinline__ uint32_t reg_kth(const uint32_t (&v)[NV], uint32_t ne
 
 // One wave per row: the threshold pair over the row's page maxima and the
 // first candidate slot of each page range (64 per page at or above the
-// threshold: no other page holds a candidate).
+// threshold: no other page holds a candidate). Under the sampled bound the
+// pair is the need_s-th largest over the sampled pages' maxima, and every
+// page range gets seg_cap slots.
 constexpr int kPfSelWaves = 4;
+
+// Page of entry j of a row's maxima: page j, or sampled page 8 j + 4.
+__device__ __forceinline__ int pf_entry_page(const PfParams& p, int j) {
+  return p.sampled ? min(kPfStride * j + kPfStride / 2, p.P - 1) : j;
+}
+
+// The bound's rank among the row's maxima.
+__device__ __forceinline__ uint32_t pf_need(const PfParams& p) {
+  return p.sampled ? uint32_t(p.need_s) : uint32_t(p.k_eff);
+}
 
 __device__ __forceinline__ bool pf_pair_at_least(uint32_t key, int page, uint64_t t) {
   return key != 0u && ((uint64_t(key) << 32) | uint32_t(~uint32_t(page))) >= t;
@@ -601,13 +639,15 @@ __global__ __launch_bounds__(kPfSelWaves * 64) void pf_threshold_kernel(PfParams
   const int lane = lane_id();
   const int R = blockIdx.x * kPfSelWaves + wave;
   if (R >= p.T * p.H_q) return;
-  const uint32_t* pm = p.pmax + size_t(R) * p.Ppad;
+  if (p.subset && p.fail[R] == 0u) return;
+  const int width = p.sampled ? p.Ps_pad : p.Ppad;
+  const uint32_t* pm = p.sampled ? p.smax + size_t(R) * p.Ps_pad : p.pmax + size_t(R) * p.Ppad;
   uint32_t v[NV];
   uint32_t present = 0;
 #pragma unroll
   for (int i = 0; i < NV / 4; ++i) {
     const int j = 256 * i + 4 * lane;
-    const uint4 x = j < p.Ppad ? *reinterpret_cast<const uint4*>(pm + j) : uint4{0u, 0u, 0u, 0u};
+    const uint4 x = j < width ? *reinterpret_cast<const uint4*>(pm + j) : uint4{0u, 0u, 0u, 0u};
     v[4 * i] = x.x;
     v[4 * i + 1] = x.y;
     v[4 * i + 2] = x.z;
@@ -616,16 +656,17 @@ __global__ __launch_bounds__(kPfSelWaves * 64) void pf_threshold_kernel(PfParams
 #pragma unroll
   for (int i = 0; i < NV; ++i) present += v[i] ? 1u : 0u;
   present = wave_sum(present);
+  const uint32_t need0 = pf_need(p);
   uint64_t t;
   if (p.k_eff == 0) {
     t = ~0ull;  // nothing is retrieved
-  } else if (present <= uint32_t(p.k_eff)) {
+  } else if (present <= need0) {
     t = 1ull;   // every member of M is a candidate
   } else {
     uint32_t above;
-    const uint32_t key = reg_kth<NV>(v, uint32_t(p.k_eff), s_hist[wave], &above);
-    // the pair's page: the (k_eff - above)-th lowest page whose maximum is key
-    uint32_t need = uint32_t(p.k_eff) - above;
+    const uint32_t key = reg_kth<NV>(v, need0, s_hist[wave], &above);
+    // the pair's page: the (need0 - above)-th lowest page whose maximum is key
+    uint32_t need = need0 - above;
     int page = 0;
 #pragma unroll
     for (int i = 0; i < NV / 4; ++i) {
@@ -660,7 +701,12 @@ __global__ __launch_bounds__(kPfSelWaves * 64) void pf_threshold_kernel(PfParams
       }
       need -= tot;
     }
-    t = (uint64_t(key) << 32) | uint32_t(~uint32_t(page));
+    t = (uint64_t(key) << 32) | uint32_t(~uint32_t(pf_entry_page(p, page)));
+  }
+  if (p.sampled) {
+    if (lane < p.splits) p.seg_off[size_t(R) * p.splits + lane] = uint32_t(lane) * uint32_t(p.seg_cap);
+    if (lane == 0) p.tau[R] = t;
+    return;
   }
   // pages at or above t per chunk of 16 (lanes 4 m .. 4 m + 3 share chunk
   // 16 i + m), then the exclusive prefix over chunks
@@ -675,11 +721,12 @@ __global__ __launch_bounds__(kPfSelWaves * 64) void pf_threshold_kernel(PfParams
     if ((lane & 3) == 0) s_pre[wave][16 * i + (lane >> 2)] = c;
   }
   {
-    constexpr int kPer = NV * 16 / 4 / 64;  // chunks per lane
+    constexpr int kCh = NV * 4;               // chunks of 16 pages held
+    constexpr int kPer = (kCh + 63) / 64;     // chunks per lane
     uint32_t c[kPer], sum = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      c[i] = s_pre[wave][kPer * lane + i];
+      c[i] = kPer * lane + i < kCh ? s_pre[wave][kPer * lane + i] : 0u;
       sum += c[i];
     }
     uint32_t incl = sum;
@@ -691,7 +738,7 @@ __global__ __launch_bounds__(kPfSelWaves * 64) void pf_threshold_kernel(PfParams
     uint32_t run = incl - sum;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      s_pre[wave][kPer * lane + i] = run;
+      if (kPer * lane + i < kCh) s_pre[wave][kPer * lane + i] = run;
       run += c[i];
     }
   }
@@ -709,23 +756,31 @@ __global__ __launch_bounds__(kPfSelWaves * 64) void pf_threshold_wide_kernel(PfP
   const int lane = lane_id();
   const int R = blockIdx.x * kPfSelWaves + wave;
   if (R >= p.T * p.H_q) return;
-  const uint32_t* pm = p.pmax + size_t(R) * p.Ppad;
+  if (p.subset && p.fail[R] == 0u) return;
+  const int count = p.sampled ? p.Ps : p.P;
+  const uint32_t* pm = p.sampled ? p.smax + size_t(R) * p.Ps_pad : p.pmax + size_t(R) * p.Ppad;
   uint32_t present = 0;
-  for (int j = lane; j < p.P; j += 64) present += pm[j] ? 1u : 0u;
+  for (int j = lane; j < count; j += 64) present += pm[j] ? 1u : 0u;
   present = wave_sum(present);
+  const uint32_t need0 = pf_need(p);
   uint64_t t;
   if (p.k_eff == 0) {
     t = ~0ull;
-  } else if (present <= uint32_t(p.k_eff)) {
+  } else if (present <= need0) {
     t = 1ull;
   } else {
     auto visit = [&](auto&& fn) {
-      for (int j = lane; j < p.P; j += 64) {
+      for (int j = lane; j < count; j += 64) {
         const uint32_t key = pm[j];
-        fn(key ? (uint64_t(key) << 32) | uint32_t(~uint32_t(j)) : 0ull);
+        fn(key ? (uint64_t(key) << 32) | uint32_t(~uint32_t(pf_entry_page(p, j))) : 0ull);
       }
     };
-    t = wave_kth(visit, uint32_t(p.k_eff), s_hist[wave]);
+    t = wave_kth(visit, need0, s_hist[wave]);
+  }
+  if (p.sampled) {
+    if (lane < p.splits) p.seg_off[size_t(R) * p.splits + lane] = uint32_t(lane) * uint32_t(p.seg_cap);
+    if (lane == 0) p.tau[R] = t;
+    return;
   }
   const int chunks = p.Ppad / kPfChunk;
   uint32_t before = 0;  // pages at or above t in the ranges so far
@@ -742,7 +797,9 @@ __global__ __launch_bounds__(kPfSelWaves * 64) void pf_threshold_wide_kernel(PfP
 }
 
 // One wave per row: the exact top k_eff of the row's candidates (the page
-// ranges' lists, in range order), ascending.
+// ranges' lists, in range order), ascending. Under the sampled bound a row
+// whose candidates are fewer than k_eff, or did not all fit their lists, is
+// flagged instead and left to the exact pass.
 __global__ __launch_bounds__(kPfSelWaves * 64) void pf_select_kernel(PfParams p) {
   __shared__ uint32_t s_hist[kPfSelWaves][256];
   __shared__ int32_t s_pos[kPfSelWaves][RA_PREFILL_MAX_K];
@@ -750,14 +807,25 @@ __global__ __launch_bounds__(kPfSelWaves * 64) void pf_select_kernel(PfParams p)
   const int lane = lane_id();
   const int R = blockIdx.x * kPfSelWaves + wave;
   if (R >= p.T * p.H_q) return;
+  if (p.subset && p.fail[R] == 0u) return;
   int32_t* out = p.out_idx + size_t(R) * p.k;
   const uint32_t ke = uint32_t(p.k_eff);
+  if (p.sampled && ke == 0 && lane == 0) p.fail[R] = 0u;
   if (ke > 0) {
     const uint64_t* cl = p.cand + size_t(R) * p.cap;
     const uint32_t* so = p.seg_off + size_t(R) * p.splits;
     const uint32_t* sc = p.seg_cnt + size_t(R) * p.splits;
     uint32_t n = 0;
-    for (int z = 0; z < p.splits; ++z) n += sc[z];
+    bool over = false;
+    for (int z = 0; z < p.splits; ++z) {
+      n += sc[z];
+      over = over || sc[z] > uint32_t(p.seg_cap);
+    }
+    if (p.sampled) {
+      const bool short_ = over || n < ke;
+      if (lane == 0) p.fail[R] = short_ ? 1u : 0u;
+      if (short_) return;
+    }
     auto visit = [&](auto&& fn) {
       for (int z = 0; z < p.splits; ++z) {
         const uint32_t cnt = sc[z];
@@ -802,23 +870,41 @@ static void launch_pf_contract(const PfParams& p, bool filter, hipStream_t s) {
     hipLaunchKernelGGL((pf_contract_kernel<G, false>), grid, dim3(kPfThreads), 0, s, p);
 }
 
-hipError_t launch_prefill(const PfParams& p, int first, int last, hipStream_t s) {
-  const int G = p.H_q / p.H_kv;
-  const unsigned row_waves = unsigned((int64_t(p.T) * p.H_q + kPfSelWaves - 1) / kPfSelWaves);
+// Stages 0-3 run under the sampled bound, 4-7 the exact pass on the rows
+// stage 3 flagged; within each half: maxima, threshold, filter, select.
+hipError_t launch_prefill(const PfParams& p0, int first, int last, hipStream_t s) {
+  const int G = p0.H_q / p0.H_kv;
+  const unsigned row_waves = unsigned((int64_t(p0.T) * p0.H_q + kPfSelWaves - 1) / kPfSelWaves);
   for (int st = first; st <= last; ++st) {
-    if (st == 0 || st == 2) {
+    PfParams p = p0;
+    p.sampled = st < 4 ? 1 : 0;
+    p.subset = st < 4 ? 0 : 1;
+    const int kind = st & 3;
+    if (kind == 0 && p.sampled) {
+      // the sampled maxima have 1/8 of the pages: fewer page ranges
+      p.splits = min(p.splits, p.Ps_pad / kPfChunk);
+      p.xcd_groups = (p.H_kv * p.splits) % 8 == 0 ? 1 : 0;
+    }
+    if (kind == 0 || kind == 2) {
       switch (G) {
-        case 1: launch_pf_contract<1>(p, st == 2, s); break;
-        case 2: launch_pf_contract<2>(p, st == 2, s); break;
-        case 4: launch_pf_contract<4>(p, st == 2, s); break;
-        case 8: launch_pf_contract<8>(p, st == 2, s); break;
+        case 1: launch_pf_contract<1>(p, kind == 2, s); break;
+        case 2: launch_pf_contract<2>(p, kind == 2, s); break;
+        case 4: launch_pf_contract<4>(p, kind == 2, s); break;
+        case 8: launch_pf_contract<8>(p, kind == 2, s); break;
         default: return hipErrorInvalidValue;
       }
-    } else if (st == 1) {
+    } else if (kind == 1) {
       const dim3 grid(row_waves), block(kPfSelWaves * 64);
-      if (p.Ppad <= 2048)
+      const int width = p.sampled ? p.Ps_pad : p.Ppad;
+      if (width <= 256)
+        hipLaunchKernelGGL(pf_threshold_kernel<4>, grid, block, 0, s, p);
+      else if (width <= 512)
+        hipLaunchKernelGGL(pf_threshold_kernel<8>, grid, block, 0, s, p);
+      else if (width <= 1024)
+        hipLaunchKernelGGL(pf_threshold_kernel<16>, grid, block, 0, s, p);
+      else if (width <= 2048)
         hipLaunchKernelGGL(pf_threshold_kernel<32>, grid, block, 0, s, p);
-      else if (p.Ppad <= 4096)
+      else if (width <= 4096)
         hipLaunchKernelGGL(pf_threshold_kernel<64>, grid, block, 0, s, p);
       else
         hipLaunchKernelGGL(pf_threshold_wide_kernel, grid, block, 0, s, p);

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <numeric>
 #include <vector>
@@ -58,7 +59,11 @@ bool pf_layout(int32_t T, int32_t H_q, int32_t N, int32_t k, PfLayout* L) {
   if (rows > (int64_t(1) << 30)) return false;
   const int64_t P = (int64_t(N) + kPage - 1) / kPage;
   const int64_t Ppad = (P + kPfChunk - 1) / kPfChunk * kPfChunk;
-  const int64_t cap = int64_t(kPage) * k;
+  // 64 per page of the exact threshold's k pages, and room for the sampled
+  // bound's larger candidate sets at small k
+  const int64_t cap = int64_t(kPage) * std::max<int64_t>(k, kPfMinCapPages);
+  L->cap = cap;
+  const int64_t Ps_pad = (pf_sampled_pages(int(P)) + kPfChunk - 1) / kPfChunk * kPfChunk;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -70,6 +75,8 @@ bool pf_layout(int32_t T, int32_t H_q, int32_t N, int32_t k, PfLayout* L) {
   L->off_seg_off = take(size_t(rows) * kPfMaxSplits * sizeof(uint32_t));
   L->off_seg_cnt = take(size_t(rows) * kPfMaxSplits * sizeof(uint32_t));
   L->off_cand = take(size_t(rows) * cap * sizeof(uint64_t));
+  L->off_smax = take(size_t(rows) * Ps_pad * sizeof(uint32_t));
+  L->off_fail = take(size_t(rows) * sizeof(uint32_t));
   L->total = off;
   return true;
 }
@@ -311,6 +318,12 @@ ra_status ra_decode_step(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
                           flags, RA_STAGE_SAMPLE, RA_STAGE_MERGE, stream);
 }
 
+size_t ra_prefill_workspace_fail_offset(int32_t T, int32_t H_q, int32_t N, int32_t k) {
+  PfLayout L;
+  if (!pf_layout(T, H_q, N, k, &L)) return 0;
+  return L.off_fail;
+}
+
 size_t ra_prefill_workspace_bytes(int32_t T, int32_t H_q, int32_t N, int32_t k) {
   PfLayout L;
   if (!pf_layout(T, H_q, N, k, &L)) return 0;
@@ -323,7 +336,7 @@ ra_status ra_prefill_topk(const uint16_t* q, int32_t T, int32_t H_q,
                           int32_t* out_idx, void* ws, size_t ws_bytes,
                           hipStream_t stream) {
   return ra_prefill_stages(q, T, H_q, kv, seq, N, k, n_sink, window, out_idx, ws,
-                           ws_bytes, RA_PF_STAGE_MAXIMA, RA_PF_STAGE_SELECT, stream);
+                           ws_bytes, RA_PF_STAGE_SAMPLE, RA_PF_STAGE_EXACT_SELECT, stream);
 }
 
 ra_status ra_prefill_stages(const uint16_t* q, int32_t T, int32_t H_q,
@@ -365,8 +378,10 @@ ra_status ra_prefill_stages(const uint16_t* q, int32_t T, int32_t H_q,
   p.hi = std::max(N - window, p.lo);
   p.k = k;
   p.k_eff = std::min(k, p.hi - p.lo);
-  p.cap = kPage * k;
+  p.cap = int32_t(L.cap);
   p.pmax = reinterpret_cast<uint32_t*>(base + L.off_pmax);
+  p.smax = reinterpret_cast<uint32_t*>(base + L.off_smax);
+  p.fail = reinterpret_cast<uint32_t*>(base + L.off_fail);
   p.tau = reinterpret_cast<uint64_t*>(base + L.off_tau);
   p.seg_off = reinterpret_cast<uint32_t*>(base + L.off_seg_off);
   p.seg_cnt = reinterpret_cast<uint32_t*>(base + L.off_seg_cnt);
@@ -386,6 +401,20 @@ ra_status ra_prefill_stages(const uint16_t* q, int32_t T, int32_t H_q,
   if (S8 <= S_max) S = S8;
   p.splits = int32_t(S);
   p.xcd_groups = (int64_t(kv->H_kv) * S) % 8 == 0 ? 1 : 0;
+  // The sampled bound is the R-th largest maximum over the sampled pages
+  // (one page in 8). About 8 R pages of the row then have a maximum at or
+  // above it, with a spread of about 8 sqrt(R) for keys in no particular
+  // order; R is the least with R - z sqrt(R) >= k_eff / 8, z = 4.5, so that
+  // fewer than k_eff candidates (the row then falls to the exact pass) is a
+  // 4.5-sigma event.
+  p.Ps = int32_t(pf_sampled_pages(p.P));
+  p.Ps_pad = int32_t((p.Ps + kPfChunk - 1) / kPfChunk * kPfChunk);
+  {
+    const double z = 4.5, kf = double(p.k_eff) * double(p.Ps) / double(p.P);
+    const double r = 0.5 * z + std::sqrt(0.25 * z * z + kf);
+    p.need_s = int32_t(std::ceil(r * r));
+  }
+  p.seg_cap = int32_t(p.cap / S);
   if (launch_prefill(p, first_stage, last_stage, stream) != hipSuccess) return RA_ERR_HIP;
   return RA_OK;
 }

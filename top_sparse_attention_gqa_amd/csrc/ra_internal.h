@@ -118,6 +118,11 @@ struct Params {
 constexpr int kPfChunk = 16;       // pages per page-maxima row segment
 constexpr int kPfBlockRows = 512;  // query rows (of one KV head) per contraction block
 constexpr int kPfMaxSplits = 64;   // page ranges per (KV head, row block), at most
+constexpr int kPfMinCapPages = 32; // candidate slots per row: 64 x max(k, this)
+constexpr int kPfStride = 8;       // the sampled pass takes page 8 j + 4 of every 8
+
+// Sampled pages of a row of P pages: ceil(P / 8), each inside its group.
+__host__ __device__ inline int pf_sampled_pages(int P) { return (P + kPfStride - 1) / kPfStride; }
 
 struct PfParams {
   const uint16_t* q;          // [T][H_q][128]
@@ -130,6 +135,15 @@ struct PfParams {
   int32_t row_blocks;         // contraction row blocks per KV head
   int32_t splits;             // page ranges per (KV head, row block), <= kPfMaxSplits
   int32_t xcd_groups;         // 1: the row blocks of a page range share an XCD
+  // set per launch: sampled = the pass over the sampled pages (page
+  // 8 j + 4 of each group j of 8 pages) and the bound they give; subset = the
+  // exact pass, restricted to flagged rows (and the row blocks holding one)
+  int32_t sampled, subset;
+  int32_t Ps, Ps_pad;         // sampled pages; row stride of smax
+  int32_t need_s;             // rank of the sampled bound among a row's sampled maxima
+  int32_t seg_cap;            // slots of a (row, page range) list (sampled bound)
+  uint32_t* smax;   // [T*H_q][Ps_pad] maxima of the sampled pages
+  uint32_t* fail;   // [T*H_q] 1: the row's sampled filter fell short
   uint32_t* pmax;   // [T*H_q][Ppad] largest score key per page over M (0: none)
   uint64_t* tau;    // [T*H_q] threshold pair (key << 32 | ~page)
   uint32_t* seg_off;  // [T*H_q][splits] first candidate slot of each page range
@@ -139,7 +153,8 @@ struct PfParams {
 };
 
 struct PfLayout {
-  size_t off_pmax, off_tau, off_seg_off, off_seg_cnt, off_cand, total;
+  size_t off_pmax, off_tau, off_seg_off, off_seg_cnt, off_cand, off_smax, off_fail, total;
+  int64_t cap;  // candidate slots per row
 };
 
 // Attention over listed positions, and the merge of two partials
