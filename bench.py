@@ -570,10 +570,10 @@ def run_prefill(args):
     stage_ms = np.array([[e[s_].elapsed_time(e[s_ + 1]) for s_ in range(n_stage)] for e in bev])
 
     # one contraction pass: every (row, head) against every key, 2 d flops each;
-    # the sampled maxima take one page in 16
+    # the sampled maxima take one page in 8
     flops = PF_T * PF_H_Q * PF_N * 2 * 128
     n_pages = (PF_N + 63) // 64
-    flops_s = PF_T * PF_H_Q * ((n_pages + 15) // 16) * 64 * 2 * 128
+    flops_s = PF_T * PF_H_Q * ((n_pages + 7) // 8) * 64 * 2 * 128
     achieved = flops / k2_s / 1e12
     call(0)
     torch.cuda.synchronize()

@@ -239,8 +239,11 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
         const uint32_t i = (r_head + lane) % uint32_t(kPfRec);
         const uint32_t meta = sm.u.f.meta[wave][i];
         const uint32_t qi = meta >> 24, n0 = meta & 0xFFFFFFu;
-        const uint32_t npg = ~(n0 >> 6);  // ~page
         const uint64_t t = sm.u.f.tau[wave][qi];
+        // a score above the bound's passes, one below fails, NaN fails; an
+        // equal one (ties, or -0 against +0) is decided by the full pair
+        const float th = key2f(uint32_t(t >> 32));
+        const float* rs = reinterpret_cast<const float*>(&sm.u.f.rec[wave][i][0]);
         float v[16];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -250,22 +253,29 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
           v[4 * c + 2] = __uint_as_float(x.z);
           v[4 * c + 3] = __uint_as_float(x.w);
         }
-        uint32_t okm = 0;
+        uint32_t okm = 0, eqm = 0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const bool ok = v[r] == v[r] && ((uint64_t(f2key(v[r])) << 32) | npg) >= t;
-          okm |= ok ? (1u << r) : 0u;
+          okm |= v[r] > th ? (1u << r) : 0u;
+          eqm |= v[r] == th ? (1u << r) : 0u;
+        }
+        if (eqm) {
+          const uint32_t npg = ~(n0 >> 6);  // ~page
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (((eqm >> r) & 1u) && ((uint64_t(f2key(v[r])) << 32) | npg) >= t) okm |= 1u << r;
         }
         // one reservation per record, then its keys in order
         uint32_t at = atomicAdd(&sm.u.f.cnt[wave][qi], uint32_t(__popc(okm)));
         uint64_t* list = p.cand + sm.u.f.base[wave][qi];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (okm & (1u << r)) {
+        while (okm) {
+          const int r = __ffs(okm) - 1;
+          okm &= okm - 1u;
+          if (at < lim) {
             const uint32_t pos = n0 + uint32_t((r >> 2) * 8 + (r & 3));
-            if (at < lim) list[at] = (uint64_t(f2key(v[r])) << 32) | uint32_t(~pos);
-            ++at;
+            list[at] = (uint64_t(f2key(rs[r])) << 32) | uint32_t(~pos);
           }
+          ++at;
         }
       }
       r_head += n;
@@ -800,9 +810,12 @@ __global__ __launch_bounds__(kPfSelWaves * 64) void pf_threshold_wide_kernel(PfP
 // ranges' lists, in range order), ascending. Under the sampled bound a row
 // whose candidates are fewer than k_eff, or did not all fit their lists, is
 // flagged instead and left to the exact pass.
+constexpr uint32_t kPfSelLds = 512;  // candidates a row copies to LDS before its radix
+
 __global__ __launch_bounds__(kPfSelWaves * 64) void pf_select_kernel(PfParams p) {
   __shared__ uint32_t s_hist[kPfSelWaves][256];
-  __shared__ int32_t s_pos[kPfSelWaves][RA_PREFILL_MAX_K];
+  __shared__ __align__(16) int32_t s_pos[kPfSelWaves][RA_PREFILL_MAX_K];
+  __shared__ uint64_t s_cand[kPfSelWaves][kPfSelLds];
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
   const int R = blockIdx.x * kPfSelWaves + wave;
@@ -813,32 +826,27 @@ __global__ __launch_bounds__(kPfSelWaves * 64) void pf_select_kernel(PfParams p)
   if (p.sampled && ke == 0 && lane == 0) p.fail[R] = 0u;
   if (ke > 0) {
     const uint64_t* cl = p.cand + size_t(R) * p.cap;
-    const uint32_t* so = p.seg_off + size_t(R) * p.splits;
-    const uint32_t* sc = p.seg_cnt + size_t(R) * p.splits;
-    uint32_t n = 0;
-    bool over = false;
-    for (int z = 0; z < p.splits; ++z) {
-      n += sc[z];
-      over = over || sc[z] > uint32_t(p.seg_cap);
+    // lane z holds page range z's list: its count, first slot, and where
+    // it starts in the concatenation of the lists
+    const int S = p.splits;
+    const uint32_t cnt_z = lane < S ? p.seg_cnt[size_t(R) * S + lane] : 0u;
+    const uint32_t off_z = lane < S ? p.seg_off[size_t(R) * S + lane] : 0u;
+    uint32_t pre_z = cnt_z;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = __shfl_up(pre_z, o);
+      if (lane >= o) pre_z += t;
     }
+    const uint32_t n = __shfl(pre_z, 63);
+    pre_z -= cnt_z;
     if (p.sampled) {
-      const bool short_ = over || n < ke;
+      const bool short_ = __ballot(cnt_z > uint32_t(p.seg_cap)) != 0ull || n < ke;
       if (lane == 0) p.fail[R] = short_ ? 1u : 0u;
       if (short_) return;
     }
-    auto visit = [&](auto&& fn) {
-      for (int z = 0; z < p.splits; ++z) {
-        const uint32_t cnt = sc[z];
-        const uint64_t* b = cl + so[z];
-        for (uint32_t i = lane; i < cnt; i += 64) fn(b[i]);
-      }
-    };
-    const uint64_t th = n > ke ? wave_kth(visit, ke, s_hist[wave]) : 1ull;
     // the winners' positions, in list order
     uint32_t filled = 0;
-    for (int z = 0; z < p.splits; ++z) {
-      const uint32_t cnt = sc[z];
-      const uint64_t* b = cl + so[z];
+    auto winners = [&](const uint64_t* b, uint32_t cnt, uint64_t th) {
       for (uint32_t base = 0; base < cnt; base += 64) {
         const uint32_t i = base + lane;
         const uint64_t v = i < cnt ? b[i] : 0ull;
@@ -848,12 +856,56 @@ __global__ __launch_bounds__(kPfSelWaves * 64) void pf_select_kernel(PfParams p)
         if (win && at < ke) s_pos[wave][at] = int32_t(~uint32_t(v));
         filled += uint32_t(__popcll(m));
       }
+    };
+    if (n <= kPfSelLds) {
+      // the lists, concatenated in LDS (four loads in flight per lane); the
+      // radix passes then read LDS. Entry c is in the last range whose
+      // start is <= c.
+      uint64_t* sv = s_cand[wave];
+      for (uint32_t c0 = 0; c0 < n; c0 += 256) {
+        uint64_t x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t c = c0 + 64u * u + uint32_t(lane);
+          int zs = 0;
+          for (int z = 1; z < S; ++z) zs = __shfl(pre_z, z) <= c ? z : zs;
+          const uint32_t src = __shfl(off_z, zs) + (c - __shfl(pre_z, zs));
+          x[u] = c < n ? cl[src] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t c = c0 + 64u * u + uint32_t(lane);
+          if (c < n) sv[c] = x[u];
+        }
+      }
+      auto visit = [&](auto&& fn) {
+        for (uint32_t i = lane; i < n; i += 64) fn(sv[i]);
+      };
+      const uint64_t th = n > ke ? wave_kth(visit, ke, s_hist[wave]) : 1ull;
+      winners(sv, n, th);
+    } else {
+      auto visit = [&](auto&& fn) {
+        for (int z = 0; z < S; ++z) {
+          const uint32_t cnt = __shfl(cnt_z, z);
+          const uint64_t* b = cl + __shfl(off_z, z);
+          for (uint32_t i = lane; i < cnt; i += 64) fn(b[i]);
+        }
+      };
+      const uint64_t th = n > ke ? wave_kth(visit, ke, s_hist[wave]) : 1ull;
+      for (int z = 0; z < S; ++z) winners(cl + __shfl(off_z, z), __shfl(cnt_z, z), th);
     }
     // ascending: each winner's rank is the number of smaller positions
+    // (four at a time; the slots past ke rank above every position)
+    const uint32_t ke4 = (ke + 3u) & ~3u;
+    if (uint32_t(lane) < ke4 - ke) s_pos[wave][ke + lane] = INT32_MAX;
+    const int4* s4 = reinterpret_cast<const int4*>(s_pos[wave]);
     for (uint32_t i = lane; i < ke; i += 64) {
       const int32_t x = s_pos[wave][i];
       uint32_t rank = 0;
-      for (uint32_t j = 0; j < ke; ++j) rank += s_pos[wave][j] < x ? 1u : 0u;
+      for (uint32_t j = 0; j < ke4 / 4; ++j) {
+        const int4 y = s4[j];
+        rank += (y.x < x ? 1u : 0u) + (y.y < x ? 1u : 0u) + (y.z < x ? 1u : 0u) + (y.w < x ? 1u : 0u);
+      }
       out[rank] = x;
     }
   }
