@@ -270,7 +270,7 @@ ra_status ra_prefill_topk(const uint16_t* q, int32_t T, int32_t H_q,
  * RA_ERR_INVALID_ARGUMENT.
  */
 typedef enum ra_prefill_stage {
-  RA_PF_STAGE_SAMPLE = 0,        /* contraction over one page in 16: sampled page maxima */
+  RA_PF_STAGE_SAMPLE = 0,        /* contraction over one page in 8: sampled page maxima */
   RA_PF_STAGE_BOUND = 1,         /* per row: the sampled bound (R-th largest sampled pair) */
   RA_PF_STAGE_FILTER = 2,        /* contraction: keys at or above the bound */
   RA_PF_STAGE_SELECT = 3,        /* per row: exact top-k, or the row is flagged */
