@@ -53,8 +53,8 @@ WORKLOAD_TEXT = {
     "C3_3": "Llama-3-8B layer: H_q=32, H_kv=8, d=128, N=1048576, k=3% (31457), n_sink=128, window=512",
     "C4": "16 ragged sequences (N uniform in [32768, 131072]) of a Llama-3-8B layer, 64-token pages in shuffled order, k=2% of each length",
     "C5P": "C5 with a pyramid-shaped per-layer budget: k_l falls linearly with depth (slope 0.5, 1.5 to 0.5 times the mean) around the uniform 1% of the current length, with the same total",
-    "G1": "query-aware key graph of a Llama-3-8B layer (H_q=32, H_kv=8, d=128) at N=131072, n_sink=128, window=512: built from the exact top-32 keys of all N prefill rows (degree 32), searched per decode query (ef=128) for the top 100; queries around 32 shared directions per head (spread 0.35), prefill rows and decode queries alike",
-    "O1": "one Llama-3-8B layer (H_q=32, H_kv=8, d=128) at N=1048576 with its KV in pinned host memory and W (n_sink=128 + window=512) in HBM; Omega (top 100) retrieved by the key graph (from 262144 prefill rows, degree 32, ef=128) reading host-resident keys, attended from host memory, merged with W",
+    "G1": "query-aware key graph of a Llama-3-8B layer (H_q=32, H_kv=8, d=128) at N=131072, n_sink=128, window=512: built from the exact top-64 keys of all N prefill rows (degree 64), searched per decode query (ef=128) for the top 100; queries around 32 shared directions per head (spread 0.35), prefill rows and decode queries alike",
+    "O1": "one Llama-3-8B layer (H_q=32, H_kv=8, d=128) at N=1048576 with its KV in pinned host memory and W (n_sink=128 + window=512) in HBM; Omega (top 100) retrieved by the key graph (from 262144 prefill rows, top-64 lists, degree 64, ef=128) reading host-resident keys, attended from host memory, merged with W",
     "P1": "prefill exact top-k: T=1024 query rows of a Llama-3-8B layer (H_q=32, H_kv=8, d=128) against N=131072 keys, k=100, n_sink=128, window=512",
     "C5": "32 Llama-3-8B layers (H_q=32, H_kv=8, d=128) at N=1048576, k=1% of the current length, KV of every layer resident in HBM; each token step appends one K/V row per layer and runs the decode step of all 32 layers",
 }
@@ -621,7 +621,7 @@ def run_prefill(args):
 # query-aware key graph: one "step" is one ra_graph_search call (all query
 # heads of one decode query) over the index built from the prefill rows
 GR_H_Q, GR_H_KV, GR_N, GR_SINK, GR_WINDOW = 32, 8, 131072, 128, 512
-GR_LIST_K, GR_D, GR_EF, GR_K = 32, 32, 128, 100
+GR_LIST_K, GR_D, GR_EF, GR_K = 64, 64, 128, 100
 GR_QUERIES = 16       # decode queries for the recall figures
 GR_MAX_EF = 256
 GR_CHUNK = 4096       # prefill rows per ra_prefill_topk call
