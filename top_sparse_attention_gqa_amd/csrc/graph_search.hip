@@ -37,7 +37,8 @@ struct GsLds {
   float ns[kGsThreads];   // the keys new in this round
   int32_t nu[kGsThreads];
   int32_t cand[kGsWaves]; // the keys expanded in this round
-  int32_t cnt[kGsWaves];  // per wave: unexpanded entries, then new keys
+  int32_t cnt[kGsWaves];  // per wave: unexpanded entries, then new keys kept
+  int32_t fcnt[kGsWaves]; // per wave: keys visited for the first time
 };
 
 // a ranks before b: larger score, then lower position
@@ -150,20 +151,29 @@ __global__ __launch_bounds__(kGsThreads) void graph_search_kernel(GsParams p) {
       }
     }
     const float s = fresh ? gs_score(p, g, qw, u) : 0.0f;
-    bal = __ballot(fresh);
+    // a key that ranks below the last entry of a full R can never enter it:
+    // it counts as visited, and only the others are merged
+    const bool full = nr >= ef;
+    const bool keep = fresh && (!full || gs_better(s, u, sm.rs[cur][ef - 1], sm.rp[cur][ef - 1]));
+    const uint64_t fb = __ballot(fresh);
+    bal = __ballot(keep);
     __syncthreads();  // every wave has read sm.cnt
-    if (lane == 0) sm.cnt[wave] = __popcll(bal);
+    if (lane == 0) {
+      sm.cnt[wave] = __popcll(bal);
+      sm.fcnt[wave] = __popcll(fb);
+    }
     __syncthreads();
-    int m;
+    int m, nf;
+    gs_wave_prefix(sm.fcnt, wave, before, nf);
     gs_wave_prefix(sm.cnt, wave, before, m);
-    if (fresh) {
+    visited += uint32_t(nf);
+    if (keep) {
       const int slot = before + __popcll(bal & ((1ull << lane) - 1ull));
       sm.ns[slot] = s;
       sm.nu[slot] = u;
     }
     __syncthreads();
     if (m == 0) continue;  // block-uniform
-    visited += uint32_t(m);
 
     // merge by rank into the other buffer, keeping the best ef
     const int nxt = cur ^ 1;
