@@ -66,6 +66,9 @@ def random_links(r, N, T, K):
     (3000, 16, 64, 20, 400, 8),
     (5000 + 37, 32, 128, 100, 600, 16),
     (700, 64, 256, 256, 300, 32),
+    # past about 800K keys the visited bitmap leaves no room for the block
+    # table in LDS, and the search reads it from global memory
+    (2**20 - 5, 16, 64, 20, 3000, 8),
 ])
 def test_graph_search_parity_on_random_links(N, D, ef, k, T, K):
     say(f"case graph random links: N={N} D={D} ef={ef} k={k}")

@@ -29,13 +29,18 @@ constexpr int kGsMaxEf = RA_GRAPH_MAX_EF;
 constexpr int kGsWaves = kGsBatch;          // keys expanded per round, one per wave
 constexpr int kGsThreads = kGsWaves * 64;
 static_assert(kGsThreads >= kGsMaxEf, "one thread per entry of R");
+// Rounds with more new keys than this sort them first (bitonic, in LDS), so
+// that every rank is a binary search; fewer are ranked by counting.
+constexpr int kGsSortMin = 128;
 
 struct GsLds {
   float rs[2][kGsMaxEf];  // R, double-buffered: score, position, expanded
   int32_t rp[2][kGsMaxEf];
   int32_t rx[2][kGsMaxEf];
-  float ns[kGsThreads];   // the keys new in this round
-  int32_t nu[kGsThreads];
+  // the keys new in this round, then padding to a multiple of 4 that ranks
+  // below every key (read four at a time by the merge)
+  __align__(16) float ns[kGsThreads];
+  __align__(16) int32_t nu[kGsThreads];
   int32_t cand[kGsWaves]; // the keys expanded in this round
   int32_t cnt[kGsWaves];  // per wave: unexpanded entries, then new keys kept
   int32_t fcnt[kGsWaves]; // per wave: keys visited for the first time
@@ -46,10 +51,17 @@ __device__ __forceinline__ bool gs_better(float sa, int32_t pa, float sb, int32_
   return sa > sb || (sa == sb && pa < pb);
 }
 
+// bt: the block table's entries, already checked, in LDS; or null (read
+// it from global memory).
 __device__ __forceinline__ float gs_score(const GsParams& p, int g, const uint32_t (&qw)[64],
-                                          int32_t u) {
-  int32_t pg = p.block_table[u >> 6];
-  pg = ((unsigned)pg < (unsigned)p.num_pages) ? pg : 0;
+                                          int32_t u, const int32_t* bt) {
+  int32_t pg;
+  if (bt) {
+    pg = bt[u >> 6];
+  } else {
+    pg = p.block_table[u >> 6];
+    pg = ((unsigned)pg < (unsigned)p.num_pages) ? pg : 0;
+  }
   const uint4* kr = reinterpret_cast<const uint4*>(
       p.k_pool + ((size_t(pg) * p.H_kv + g) * kPage + (u & 63)) * kHeadDim);
   float s = 0.0f;
@@ -80,6 +92,8 @@ __device__ __forceinline__ void gs_wave_prefix(const int32_t* v, int wave, int& 
   }
 }
 
+// BT_LDS: the block table's entries for [0, N) follow the bitmap in LDS.
+template <bool BT_LDS>
 __global__ __launch_bounds__(kGsThreads) void graph_search_kernel(GsParams p) {
   extern __shared__ uint32_t vis[];  // visited bitmap, p.vis_words words
   __shared__ GsLds sm;
@@ -90,6 +104,14 @@ __global__ __launch_bounds__(kGsThreads) void graph_search_kernel(GsParams p) {
   int32_t* out = p.out_idx + size_t(h) * p.k;
 
   for (int i = tid; i < p.vis_words; i += kGsThreads) vis[i] = 0u;
+  int32_t* bt = nullptr;
+  if constexpr (BT_LDS) {
+    bt = reinterpret_cast<int32_t*>(vis + p.vis_words);
+    for (int i = tid; i < (N + kPage - 1) / kPage; i += kGsThreads) {
+      const int32_t pg = p.block_table[i];
+      bt[i] = ((unsigned)pg < (unsigned)p.num_pages) ? pg : 0;
+    }
+  }
   const int32_t e = p.entry[h];
   if (e < 0 || e >= N) {  // block-uniform
     for (int i = tid; i < p.k; i += kGsThreads) out[i] = -1;
@@ -112,7 +134,7 @@ __global__ __launch_bounds__(kGsThreads) void graph_search_kernel(GsParams p) {
   __syncthreads();
   if (tid == 0) {
     vis[e >> 5] |= 1u << (e & 31);
-    sm.rs[0][0] = gs_score(p, g, qw, e);
+    sm.rs[0][0] = gs_score(p, g, qw, e, bt);
     sm.rp[0][0] = e;
     sm.rx[0][0] = 0;
   }
@@ -150,7 +172,7 @@ __global__ __launch_bounds__(kGsThreads) void graph_search_kernel(GsParams p) {
         fresh = (atomicOr(&vis[u >> 5], bit) & bit) == 0u;
       }
     }
-    const float s = fresh ? gs_score(p, g, qw, u) : 0.0f;
+    const float s = fresh ? gs_score(p, g, qw, u, bt) : 0.0f;
     // a key that ranks below the last entry of a full R can never enter it:
     // it counts as visited, and only the others are merged
     const bool full = nr >= ef;
@@ -172,16 +194,98 @@ __global__ __launch_bounds__(kGsThreads) void graph_search_kernel(GsParams p) {
       sm.ns[slot] = s;
       sm.nu[slot] = u;
     }
+    const int m4 = (m + 3) & ~3;
+    if (tid >= m && tid < m4) {
+      sm.ns[tid] = -INFINITY;
+      sm.nu[tid] = INT_MAX;
+    }
     __syncthreads();
     if (m == 0) continue;  // block-uniform
 
     // merge by rank into the other buffer, keeping the best ef
     const int nxt = cur ^ 1;
+    const bool sorted = m > kGsSortMin;  // block-uniform
+    if (sorted) {
+      // best first over P = the power of two >= m (the padding, ranking
+      // below every key, ends up behind them)
+      int P = 4;
+      while (P < m) P <<= 1;
+      for (int i = m4 + tid; i < P; i += kGsThreads) {
+        sm.ns[i] = -INFINITY;
+        sm.nu[i] = INT_MAX;
+      }
+      __syncthreads();
+      // Partners less than 64 apart are in the same wave: those steps run
+      // in registers with shuffles, the others through LDS. P >= 256 is a
+      // whole number of waves.
+      const bool inP = tid < P;  // wave-uniform
+      auto wave_steps = [&](int kb, int j) {
+        float a = sm.ns[tid];
+        int32_t ua = sm.nu[tid];
+        for (; j > 0; j >>= 1) {
+          const float b = __shfl_xor(a, j);
+          const int32_t ub = __shfl_xor(ua, j);
+          // the lower slot of an ascending pair, or the upper of a
+          // descending one, takes the better key
+          const bool want_better = ((tid & j) == 0) == ((tid & kb) == 0);
+          const bool take = want_better ? gs_better(b, ub, a, ua) : gs_better(a, ua, b, ub);
+          if (take) {
+            a = b;
+            ua = ub;
+          }
+        }
+        sm.ns[tid] = a;
+        sm.nu[tid] = ua;
+      };
+      if (inP) {
+        for (int kb = 2; kb <= 64; kb <<= 1) wave_steps(kb, kb >> 1);
+      }
+      __syncthreads();
+      for (int kb = 128; kb <= P; kb <<= 1) {
+        for (int j = kb >> 1; j >= 64; j >>= 1) {
+          const int l = tid ^ j;
+          if (inP && l > tid) {
+            const float a = sm.ns[tid], b = sm.ns[l];
+            const int32_t ua = sm.nu[tid], ub = sm.nu[l];
+            const bool sw = (tid & kb) == 0 ? gs_better(b, ub, a, ua) : gs_better(a, ua, b, ub);
+            if (sw) {
+              sm.ns[tid] = b;
+              sm.ns[l] = a;
+              sm.nu[tid] = ub;
+              sm.nu[l] = ua;
+            }
+          }
+          __syncthreads();
+        }
+        if (inP) wave_steps(kb, 32);
+        __syncthreads();
+      }
+    }
+    const float4* ns4 = reinterpret_cast<const float4*>(sm.ns);
+    const int4* nu4 = reinterpret_cast<const int4*>(sm.nu);
+    // how many of the new keys rank before (s, u)
+    auto new_before = [&](float s, int32_t u) {
+      int c = 0;
+      if (sorted) {
+        int hi = m;  // the new keys better than (s, u) are a prefix
+        while (c < hi) {
+          const int mid = (c + hi) >> 1;
+          if (gs_better(sm.ns[mid], sm.nu[mid], s, u)) c = mid + 1; else hi = mid;
+        }
+        return c;
+      }
+      for (int j = 0; j < m4 / 4; ++j) {
+        const float4 a = ns4[j];
+        const int4 b = nu4[j];
+        c += (gs_better(a.x, b.x, s, u) ? 1 : 0) + (gs_better(a.y, b.y, s, u) ? 1 : 0) +
+             (gs_better(a.z, b.z, s, u) ? 1 : 0) + (gs_better(a.w, b.w, s, u) ? 1 : 0);
+      }
+      return c;
+    };
     if (tid < nr) {
       const float si = sm.rs[cur][tid];
       const int32_t pi = sm.rp[cur][tid];
-      int shift = 0;
-      for (int j = 0; j < m; ++j) shift += gs_better(sm.ns[j], sm.nu[j], si, pi) ? 1 : 0;
+      const int shift = new_before(si, pi);
       const int pos = tid + shift;
       if (pos < ef) {
         sm.rs[nxt][pos] = si;
@@ -197,9 +301,7 @@ __global__ __launch_bounds__(kGsThreads) void graph_search_kernel(GsParams p) {
         const int mid = (lo + hi) >> 1;
         if (gs_better(sm.rs[cur][mid], sm.rp[cur][mid], sx, ux)) lo = mid + 1; else hi = mid;
       }
-      int rn = 0;
-      for (int j = 0; j < m; ++j) rn += gs_better(sm.ns[j], sm.nu[j], sx, ux) ? 1 : 0;
-      const int pos = lo + rn;
+      const int pos = lo + new_before(sx, ux);
       if (pos < ef) {
         sm.rs[nxt][pos] = sx;
         sm.rp[nxt][pos] = ux;
@@ -224,8 +326,13 @@ __global__ __launch_bounds__(kGsThreads) void graph_search_kernel(GsParams p) {
 }
 
 hipError_t launch_graph_search(const GsParams& p, hipStream_t s) {
-  const size_t lds = size_t(p.vis_words) * sizeof(uint32_t);
-  hipLaunchKernelGGL(graph_search_kernel, dim3(p.H_q), dim3(kGsThreads), lds, s, p);
+  const size_t vis = size_t(p.vis_words) * sizeof(uint32_t);
+  const size_t bt = size_t((p.N + kPage - 1) / kPage) * sizeof(int32_t);
+  // the block table joins the bitmap in LDS when both fit a CU's 160 KB
+  if (vis + bt + sizeof(GsLds) + 1024 <= 160 * 1024)
+    hipLaunchKernelGGL(graph_search_kernel<true>, dim3(p.H_q), dim3(kGsThreads), vis + bt, s, p);
+  else
+    hipLaunchKernelGGL(graph_search_kernel<false>, dim3(p.H_q), dim3(kGsThreads), vis, s, p);
   return hipGetLastError();
 }
 
