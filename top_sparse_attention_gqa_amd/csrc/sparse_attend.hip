@@ -16,7 +16,13 @@
 
 namespace ra {
 
-constexpr int kSaThreads = 256;
+// One block of 16 waves per query head. The kernel is bound by the latency
+// of its dependent reads (index, page entry, K row; then V rows), most of
+// all when the pools are in host memory: every wave keeps many rows in
+// flight, and the scores take one position per thread.
+constexpr int kSaThreads = 1024;
+constexpr int kSaWaves = kSaThreads / 64;
+constexpr int kSaRows = 8;  // V rows per wave in flight
 constexpr float kScale = 0.08838834764831845f;  // 1 / sqrt(128)
 
 __device__ __forceinline__ float wave_sum_f(float v) {
@@ -27,8 +33,8 @@ __device__ __forceinline__ float wave_sum_f(float v) {
 
 __global__ __launch_bounds__(kSaThreads) void sparse_attend_kernel(SaParams p) {
   __shared__ float z[RA_SPARSE_MAX_K];
-  __shared__ float red[kSaThreads / 64];
-  __shared__ float part[kSaThreads / 64][kHeadDim];
+  __shared__ float red[kSaWaves];
+  __shared__ float part[kSaWaves][kHeadDim];
   const int h = blockIdx.x;
   const int g = h / (p.H_q / p.H_kv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -39,19 +45,17 @@ __global__ __launch_bounds__(kSaThreads) void sparse_attend_kernel(SaParams p) {
     return pool + ((size_t(pg) * p.H_kv + g) * kPage + (n & 63)) * kHeadDim;
   };
 
-  // scores
-  float qf[kHeadDim];
+  // scores: q as bf16 pairs, dimensions 2 i then 2 i + 1
+  uint32_t qw[kHeadDim / 2];
   {
     const uint4* qr = reinterpret_cast<const uint4*>(p.q + size_t(h) * kHeadDim);
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
       const uint4 x = qr[c];
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        qf[8 * c + 2 * i] = __uint_as_float(w[i] << 16);
-        qf[8 * c + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
+      qw[4 * c] = x.x;
+      qw[4 * c + 1] = x.y;
+      qw[4 * c + 2] = x.z;
+      qw[4 * c + 3] = x.w;
     }
   }
   float mx = -INFINITY;
@@ -67,8 +71,9 @@ __global__ __launch_bounds__(kSaThreads) void sparse_attend_kernel(SaParams p) {
         const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          acc = fmaf(qf[8 * c + 2 * j], __uint_as_float(w[j] << 16), acc);
-          acc = fmaf(qf[8 * c + 2 * j + 1], __uint_as_float(w[j] & 0xFFFF0000u), acc);
+          const uint32_t qq = qw[4 * c + j];
+          acc = fmaf(__uint_as_float(qq << 16), __uint_as_float(w[j] << 16), acc);
+          acc = fmaf(__uint_as_float(qq & 0xFFFF0000u), __uint_as_float(w[j] & 0xFFFF0000u), acc);
         }
       }
       s = acc * kScale;
@@ -81,7 +86,7 @@ __global__ __launch_bounds__(kSaThreads) void sparse_attend_kernel(SaParams p) {
   __syncthreads();
   float m = red[0];
 #pragma unroll
-  for (int w = 1; w < kSaThreads / 64; ++w) m = fmaxf(m, red[w]);
+  for (int w = 1; w < kSaWaves; ++w) m = fmaxf(m, red[w]);
   __syncthreads();
   if (m == -INFINITY) {  // nothing listed: an empty partial (block-uniform)
     if (tid < kHeadDim) p.out[size_t(h) * kHeadDim + tid] = 0.0f;
@@ -100,23 +105,22 @@ __global__ __launch_bounds__(kSaThreads) void sparse_attend_kernel(SaParams p) {
   __syncthreads();
   float Z = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kSaThreads / 64; ++w) Z += red[w];
-  // weighted V rows: wave w takes the positions i = w mod 4, lane l the
-  // dimensions 2 l, 2 l + 1 (a row is 256 coalesced bytes); four rows are
-  // in flight at a time
-  constexpr int kW = kSaThreads / 64;
+  for (int w = 0; w < kSaWaves; ++w) Z += red[w];
+  // weighted V rows: wave w takes the positions i = w mod 16, lane l the
+  // dimensions 2 l, 2 l + 1 (a row is 256 coalesced bytes); kSaRows rows
+  // are in flight at a time
   float a0 = 0.0f, a1 = 0.0f;
-  for (int i0 = wave; i0 < p.k; i0 += 4 * kW) {
-    uint32_t v[4];
-    float w[4];
+  for (int i0 = wave; i0 < p.k; i0 += kSaRows * kSaWaves) {
+    uint32_t v[kSaRows];
+    float w[kSaRows];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + r * kW;
+    for (int r = 0; r < kSaRows; ++r) {
+      const int i = i0 + r * kSaWaves;
       w[r] = i < p.k ? z[i] : 0.0f;
       v[r] = w[r] != 0.0f ? reinterpret_cast<const uint32_t*>(row(p.v_pool, idx[i]))[lane] : 0u;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < kSaRows; ++r) {
       a0 = fmaf(w[r], __uint_as_float(v[r] << 16), a0);
       a1 = fmaf(w[r], __uint_as_float(v[r] & 0xFFFF0000u), a1);
     }
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(kSaThreads) void sparse_attend_kernel(SaParams p) {
   if (tid < kHeadDim) {
     float t = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kW; ++w) t += part[w][tid];
+    for (int w = 0; w < kSaWaves; ++w) t += part[w][tid];
     p.out[size_t(h) * kHeadDim + tid] = t / Z;
     if (tid == 0) p.out_lse[h] = m + logf(Z);
   }
