@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 3
+#define RA_ABI_VERSION 4
 #define RA_HEAD_DIM 128
 #define RA_PAGE_SIZE 64
 #define RA_MAX_SEQ_LEN (1 << 24) /* 16,777,216 positions per sequence */

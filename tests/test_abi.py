@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert ra.abi_version() == 3
+    assert ra.abi_version() == 4
     assert ra.status_str(ra.RA_OK) == "RA_OK"
     assert ra.status_str(ra.RA_ERR_WORKSPACE) == "RA_ERR_WORKSPACE"
     assert ra.status_str(99) == "RA_ERR_UNKNOWN"
