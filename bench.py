@@ -39,11 +39,19 @@ SCAN_SRCS = [os.path.join(ROOT, "top_sparse_attention_gqa_amd", "csrc", f)
              for f in ("score_scan.hip", "page_scores.h", "ra_internal.h")]
 
 
-def scan_source_sha256():
+PF_SRCS = [os.path.join(ROOT, "top_sparse_attention_gqa_amd", "csrc", f)
+           for f in ("prefill_topk.hip", "ra_internal.h")]
+
+
+def sources_sha256(paths):
     h = hashlib.sha256()
-    for f in SCAN_SRCS:
+    for f in paths:
         h.update(open(f, "rb").read())
     return h.hexdigest()
+
+
+def scan_source_sha256():
+    return sources_sha256(SCAN_SRCS)
 
 WORKLOAD_TEXT = {
     "C1": "tiny decode step: H_q=4, H_kv=1, N=4096, k=64, n_sink=16, window=64",
@@ -111,16 +119,17 @@ def algorithmic_bytes(c, lens, ks, idx_np, n_sink, window):
     return kb, vrows * 256, small
 
 
-def traffic_from_profile(workload):
-    """HBM bytes per scan launch from the committed rocprofv3 counter summary
-    of this workload, scaled by the copy-kernel calibration; None if there is
-    none or if the scan kernel's sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"score_scan_{workload}_pmc.json")
+def traffic_from_profile(workload, name="score_scan", srcs=None):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary profiles/{name}_{workload}_pmc.json, scaled by the copy-kernel
+    calibration; None if there is none or if the kernel's sources changed
+    since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{name}_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     try:
         d = json.load(open(path))
-        if d.get("source_sha256") != scan_source_sha256():
+        if d.get("source_sha256") != sources_sha256(srcs or SCAN_SRCS):
             return None
         cal = d["copy_calibration"]
         f_scale = cal["bytes_read"] / (cal["fetch_kib"] * 1024.0)
@@ -578,6 +587,14 @@ def run_prefill(args):
     call(0)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
+    traffic = traffic_from_profile("P1", "prefill_filter", PF_SRCS)
+    if args.copy_calib_mib:
+        # the copy the counter runs are calibrated against
+        a = torch.empty(args.copy_calib_mib << 20, dtype=torch.uint8, device=dev)
+        bcopy = torch.empty_like(a)
+        for _ in range(3):
+            bcopy.copy_(a)
+        torch.cuda.synchronize()
     n_exact = int(ra.prefill_fail_flags(ws, PF_T, PF_H_Q, PF_N, PF_K).sum().item())
     cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(layers[0], Qs[0])
 
@@ -608,7 +625,9 @@ def run_prefill(args):
                      "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flops_per_launch": flops,
+                     "traffic": None if traffic is None else round(traffic),
+                     "algorithmic_k_bytes_per_launch": PF_N * PF_H_KV * 256,
+                     "algorithmic_flops_per_launch": flops,
                      "avg_launch_us": round(k2_s * 1e6, 2)},
         "sampled_maxima_contraction": {"kernel": "pf_contract_kernel<4, false>",
                                        "achieved_tflops": round(flops_s / k1_s / 1e12, 1),

@@ -148,14 +148,11 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
     rv[q] = r < TG;
     const int t = r / G, hh = r - (r / G) * G;
     R[q] = rv[q] ? t * p.H_q + g * G + hh : 0;
-    const uint16_t* qr = p.q + size_t(R[q]) * kHeadDim + 8 * hl;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      qf[q][s] = rv[q] ? *reinterpret_cast<const bf16x8_t*>(qr + 16 * s) : bf16x8_t{};
   }
   if (p.subset) {
-    // the exact pass: only row blocks holding a flagged row run, and the
-    // filter keeps candidates of flagged rows only
+    // the exact pass: only row blocks holding a flagged row run (the others
+    // leave before reading anything else), and the filter keeps candidates
+    // of flagged rows only
     bool any = false;
 #pragma unroll
     for (int q = 0; q < kPfQG; ++q) {
@@ -164,6 +161,13 @@ __global__ __launch_bounds__(kPfThreads) void pf_contract_kernel(PfParams p) {
       if (FILTER) rv[q] = f;
     }
     if (!__syncthreads_or(any)) return;  // block-uniform
+  }
+#pragma unroll
+  for (int q = 0; q < kPfQG; ++q) {
+    const uint16_t* qr = p.q + size_t(R[q]) * kHeadDim + 8 * hl;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qf[q][s] = rv[q] ? *reinterpret_cast<const bf16x8_t*>(qr + 16 * s) : bf16x8_t{};
   }
   float thr[kPfQG];  // a score below it is no candidate
   if constexpr (FILTER) {
