@@ -43,10 +43,7 @@ namespace ra {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-#ifndef PF_WAVES
-#define PF_WAVES 8
-#endif
-constexpr int kPfWaves = PF_WAVES;
+constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * 64;
 constexpr int kPfQG = kPfBlockRows / (kPfWaves * 32);  // 32-row query groups per wave
 constexpr int kPfWaveRows = kPfQG * 32;
