@@ -64,6 +64,9 @@ CASES = [
     ("k_one", 8, 2, [2049], 0, 50, 1, 8, 8, False),
     ("second_sequence_shuffled", 8, 2, [1500, 6000 + 5], 1, 45, 32, 16, 64, True),
     ("one_page", 4, 1, [63], 0, 5, 16, 0, 0, False),
+    # k = 256 with a sampled bound below the sampled pages present (the
+    # smaller cases above keep every member of M as a candidate)
+    ("kmax_sampled_bound", 8, 2, [60000 + 17], 0, 24, 256, 64, 256, True),
 ]
 
 
