@@ -965,6 +965,12 @@ def run_offload(args):
         "gpu_ms_per_step": round(gpu_ms, 4),
         "exact_step_from_host_memory_ms": round(exact_host_ms, 3),
         "exact_step_from_hbm_ms": round(exact_dev_ms, 4),
+        # the host link, not HBM, bounds this step: its streaming rate is what
+        # the exact step reads (every key, 256 B per position and KV head)
+        # over its time; the step's own rate is its link bytes over its time
+        "host_link": {"stream_gbps_exact_step": round(N * H_kv * 256 / (exact_host_ms * 1e-3) / 1e9, 1),
+                      "step_gbps": round(link_bytes / (ms * 1e-3) / 1e9, 1),
+                      "frac": round((link_bytes / (ms * 1e-3)) / (N * H_kv * 256 / (exact_host_ms * 1e-3)), 3)},
         "build_s": {"prefill_top_k": round(t_lists, 2), "graph_build_host": round(t_build, 2)},
         "roofline": {"kernel": "graph_search_kernel + sparse_attend_kernel over host memory",
                      "bound": "hbm", "achieved": round(link_bytes / (gpu_ms * 1e-3) / 1e9, 2),
