@@ -25,7 +25,12 @@ bool ws_layout(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seq_len,
     return false;
   const int64_t heads = int64_t(B) * H_q;
   if (heads > 65535) return false;  // grid y limit of the per-head kernels
-  L->n_cap = (int64_t(max_seq_len) + kTile - 1) / kTile * kTile;
+  // Row stride of the per-head score and candidate rows: a whole number of
+  // tile pairs. With an odd number of tiles per row (for lengths just past
+  // 2^20: 2^20 + 8192 entries, a 64 KB offset between heads' candidate rows
+  // mod 128 KB) the scan, which writes those rows while it streams K,
+  // measured 5 % slower; an even number showed no such loss.
+  L->n_cap = (int64_t(max_seq_len) + 2 * kTile - 1) / (2 * kTile) * (2 * kTile);
   L->n_tiles = int32_t(L->n_cap / kTile);
   L->n_units = int32_t(L->n_cap / kUnit);
   // sampled_pages(P) is not monotone below 2048 pages (the stride doubles
