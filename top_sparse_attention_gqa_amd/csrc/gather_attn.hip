@@ -107,8 +107,8 @@ __device__ __forceinline__ void accumulate_rows(const Params& p, int g, int cnt,
 template <int G>
 __global__ __launch_bounds__(kGathThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void gather_kernel(Params p) {
-  const int tile = blockIdx.x;
-  const int bg = blockIdx.y;
+  const int tile = blockIdx.y;
+  const int bg = blockIdx.x;
   const int b = bg / p.H_kv;
   const int g = bg - b * p.H_kv;
   const SeqGeom sg = seq_geom(p, b);
@@ -564,8 +564,15 @@ hipError_t launch_merge(const Params& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Grid (B * H_kv, tiles): blocks are dispatched group-fastest, so the
+// highest tiles come last. When a length runs just past a multiple of the
+// tile (2^20 + t: 129 tiles, 1032 blocks against 1024 resident), the blocks
+// left for a second wave are then the short tail tiles, which finish under
+// the first wave's full ones instead of extending the kernel by a full tile.
 hipError_t launch_gather(const Params& p, hipStream_t s) {
-  const dim3 grid{unsigned(p.n_tiles), unsigned(p.B * p.H_kv)};
+  const int64_t cap = std::min<int64_t>(p.max_seq_len, int64_t(p.max_pages) * kPage);
+  const int64_t tiles = std::max<int64_t>(1, std::min<int64_t>((cap + kTile - 1) / kTile, p.n_tiles));
+  const dim3 grid{unsigned(p.B * p.H_kv), unsigned(tiles)};
   const dim3 block{unsigned(kGathThreads)};
   switch (p.G) {
     case 1: hipLaunchKernelGGL(gather_kernel<1>, grid, block, 0, s, p); break;
