@@ -407,7 +407,7 @@ def run_model(args):
     for s in range(args.warmup):
         token_step(s)
     torch.cuda.synchronize()
-    every = max(1, args.steps // 100)                  # scan events on every 10th step
+    every = max(1, args.steps // 20)                   # scan events on 20 of the steps
     ev = {s: [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_layers)]
           for s in range(0, args.steps, every)}
     t0 = time.perf_counter()
