@@ -282,9 +282,10 @@ typedef enum ra_prefill_stage {
 } ra_prefill_stage;
 
 /*
- * Where the per-row flags of the last call live in its workspace: uint32
- * [T * H_q], 1 for a row whose sampled bound fell short (it was then
- * computed by the exact stages). For tests and diagnostics.
+ * Byte offset in the workspace of the per-row flags the last call left:
+ * uint32 [T * H_q], 1 for a row whose sampled bound fell short (it was then
+ * computed by the exact stages). For tests and diagnostics. Returns 0 if
+ * the arguments are invalid (the flags never start at offset 0).
  */
 size_t ra_prefill_workspace_fail_offset(int32_t T, int32_t H_q, int32_t N, int32_t k);
 
