@@ -80,6 +80,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
   __shared__ uint32_t s_fill;
   __shared__ uint32_t s_lo[G];
   __shared__ uint32_t s_cnt[G];
+  __shared__ uint32_t s_base[G];  // first slot the burst reserved in each head's list (page split)
   __shared__ uint32_t lmax[G][2];     // max key over W, over M
 
   const int tid = threadIdx.x;
@@ -89,9 +90,19 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
   if (tid < G) s_cnt[tid] = 0;
   if (tid < 2 * G) lmax[tid >> 1][tid & 1] = 0u;
 
+  // Units split evenly over the blocks. For one sequence whose units do
+  // not divide evenly (a length just past a multiple of 64 pages leaves a
+  // short last unit per KV head, and some block would take it on top of
+  // full ones) the pages are split instead, and a unit two blocks share
+  // has its list slots reserved with global atomics (3 us less scan at
+  // N = 2^20 + 1000; for ragged batches the unit split measured better).
   const int64_t T = p.unit_off[p.B];
-  const int64_t X0 = T * blockIdx.x / gridDim.x;
-  const int64_t X1 = T * (blockIdx.x + 1) / gridDim.x;
+  const int64_t NB = gridDim.x;
+  const bool split = p.B == 1 && T % NB != 0;  // block-uniform
+  const int64_t TP = T * kUnitPages;
+  const int64_t X0p = split ? TP * blockIdx.x / NB : (T * blockIdx.x / NB) * kUnitPages;
+  const int64_t X1p = split ? TP * (blockIdx.x + 1) / NB : (T * (blockIdx.x + 1) / NB) * kUnitPages;
+  const int64_t X0 = X0p / kUnitPages, X1 = (X1p + kUnitPages - 1) / kUnitPages;
   uint32_t mw = 0u, mm = 0u;  // running max keys of head F over W and M
   int cur_b = -1, cur_g = -1;
   uint4 qreg[G];
@@ -136,15 +147,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
     float* srow = p.scores + (bh0 + L.F) * p.n_cap;
     const size_t ubase = size_t(ur.u) * kUnit;
     uint64_t* crow = p.cand + (bh0 + L.F) * p.n_cap + ubase;
+    // this block's pages of the unit
+    const int pa = int(max<int64_t>(X0p - x * kUnitPages, 0));
+    const int pe = int(min<int64_t>(min<int64_t>(X1p - x * kUnitPages, kUnitPages), ur.npages));
     // the physical pages of this wave's pages of the unit, read up front
     // (lane k holds the page of the wave's k-th page)
-    const int my_pg = L.lane < kUnitPages / kScanWaves && wave + kScanWaves * L.lane < ur.npages
-                          ? page_of(p, b, ur.u * kUnitPages + wave + kScanWaves * L.lane)
+    const int my_pg = L.lane < kUnitPages / kScanWaves && pa + wave + kScanWaves * L.lane < pe
+                          ? page_of(p, b, ur.u * kUnitPages + pa + wave + kScanWaves * L.lane)
                           : 0;
-    for (int jj = wave; jj < ur.npages; jj += kScanWaves) {
+    for (int jj = pa + wave; jj < pe; jj += kScanWaves) {
       const int j = ur.u * kUnitPages + jj;
       float z[G];
-      page_scores<G>(p, __shfl(my_pg, (jj - wave) / kScanWaves), g, L, qreg, z);
+      page_scores<G>(p, __shfl(my_pg, (jj - pa - wave) / kScanWaves), g, L, qreg, z);
 #pragma unroll
       for (int s = 0; s < G; ++s) {
         const int n = j * kPage + L.tok(s);
@@ -168,9 +182,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
             if (idx < uint32_t(kStage)) {
               st_key[idx] = key;
               st_nh[idx] = uint32_t(n) | (uint32_t(L.F) << 27);
+              if (split) atomicAdd(&s_cnt[L.F], 1u);
             } else {
               // staging full: take a slot of the list at once
-              const uint32_t slot = atomicAdd(&s_cnt[L.F], 1u);
+              const uint32_t slot = split ? atomicAdd(&p.ucnt[(bh0 + L.F) * p.n_units + ur.u], 1u)
+                                          : atomicAdd(&s_cnt[L.F], 1u);
               crow[slot] = (uint64_t(key) << 32) | uint32_t(n);
             }
           }
@@ -182,16 +198,23 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
     // stores, since cached writes interleaved with the K stream cost it
     // about twice as much time
     const uint32_t nst = min(s_fill, uint32_t(kStage));
+    if (split) {
+      if (tid < G) {
+        s_base[tid] = s_cnt[tid] ? atomicAdd(&p.ucnt[(bh0 + tid) * p.n_units + ur.u], s_cnt[tid]) : 0u;
+        s_cnt[tid] = 0;
+      }
+      __syncthreads();
+    }
     for (uint32_t i = tid; i < nst; i += kScanThreads) {
       const uint32_t nh = st_nh[i];
       const uint32_t hh = nh >> 27;
-      const uint32_t slot = atomicAdd(&s_cnt[hh], 1u);
+      const uint32_t slot = (split ? s_base[hh] : 0u) + atomicAdd(&s_cnt[hh], 1u);
       __builtin_nontemporal_store((uint64_t(st_key[i]) << 32) | (nh & ((1u << 27) - 1u)),
                                   &p.cand[(bh0 + hh) * p.n_cap + ubase + slot]);
     }
     __syncthreads();
     if (tid < G) {
-      p.ucnt[(bh0 + tid) * p.n_units + ur.u] = s_cnt[tid];
+      if (!split) p.ucnt[(bh0 + tid) * p.n_units + ur.u] = s_cnt[tid];
       s_cnt[tid] = 0;
     }
     if (tid == 0) s_fill = 0;

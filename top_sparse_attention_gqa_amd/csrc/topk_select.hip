@@ -430,6 +430,12 @@ __global__ __launch_bounds__(kSelThreads) void threshold_kernel(Params p) {
     }
   }
   if (tid == 0 && hq % p.G == 0) p.gdone[size_t(b) * p.H_kv + hq / p.G] = 0u;
+  {
+    // the scan may reserve list slots with atomics: its counts start at zero
+    const int Pz = (seq_geom(p, b).N + kPage - 1) / kPage;
+    const int nuz = (Pz + kUnitPages - 1) / kUnitPages;
+    for (int u = tid; u < nuz; u += kSelThreads) p.ucnt[size_t(bh) * p.n_units + u] = 0u;
+  }
 
   const SeqGeom sg = seq_geom(p, b);
   uint32_t lo = 0xFFFFFFFFu;  // k_eff == 0: no candidates
