@@ -241,7 +241,7 @@ def run_layer(args):
         kv = kvs[i % len(layers)]
         a = (L.q, kv, seq, max_seq_len, kt, k_max, c.n_sink, c.window, out, lse, idx, ws)
         if ev is None:
-            ra.decode_step(*a)
+            ra.decode_step_ex(*a)
             return
         ev[0].record()
         ra.decode_stages(*a, 0, S - 1)
@@ -671,7 +671,7 @@ def run_graph(args):
     def recall_of(nbr, entry, decode_queries, ef):
         recalls, scanned = [], []
         for q in decode_queries:
-            ra.decode_step(q.view(1, GR_H_Q, 128), kv, seq, GR_N, kt, GR_K, GR_SINK, GR_WINDOW,
+            ra.decode_step_ex(q.view(1, GR_H_Q, 128), kv, seq, GR_N, kt, GR_K, GR_SINK, GR_WINDOW,
                            out, lse, exact_idx, ws_d)
             ra.graph_search(q, kv, 0, GR_N, nbr, entry, ef, GR_K, gidx, gvis)
             torch.cuda.synchronize()
@@ -750,13 +750,13 @@ def run_graph(args):
     gpu_ms = ev[0].elapsed_time(ev[1]) / args.steps
     # exact decode step on the same layer, for comparison
     for _ in range(5):
-        ra.decode_step(qs[0].view(1, GR_H_Q, 128), kv, seq, GR_N, kt, GR_K, GR_SINK, GR_WINDOW,
+        ra.decode_step_ex(qs[0].view(1, GR_H_Q, 128), kv, seq, GR_N, kt, GR_K, GR_SINK, GR_WINDOW,
                        out, lse, exact_idx, ws_d)
     torch.cuda.synchronize()
     e2 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     e2[0].record()
     for _ in range(20):
-        ra.decode_step(qs[0].view(1, GR_H_Q, 128), kv, seq, GR_N, kt, GR_K, GR_SINK, GR_WINDOW,
+        ra.decode_step_ex(qs[0].view(1, GR_H_Q, 128), kv, seq, GR_N, kt, GR_K, GR_SINK, GR_WINDOW,
                        out, lse, exact_idx, ws_d)
     e2[1].record()
     torch.cuda.synchronize()
@@ -901,7 +901,7 @@ def run_offload(args):
     recalls, scanned, out_err = [], [], []
     M = N - ns - win
     for q in qs:
-        ra.decode_step(q.view(1, H_q, 128), kv_dev, seq, N, kt, k, ns, win, ex_out, ex_lse, ex_idx, ws_d)
+        ra.decode_step_ex(q.view(1, H_q, 128), kv_dev, seq, N, kt, k, ns, win, ex_out, ex_lse, ex_idx, ws_d)
         step(q)
         torch.cuda.synchronize()
         e_i, g_i = ex_idx.cpu().numpy()[0], omega.cpu().numpy()
@@ -922,17 +922,17 @@ def run_offload(args):
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     gpu_ms = ev[0].elapsed_time(ev[1]) / args.steps
     # the exact step on the same host-resident layer: every key over the host link
-    ra.decode_step(qs[0].view(1, H_q, 128), kv_host, seq, N, kt, k, ns, win, ex_out, ex_lse, ex_idx, ws_d)
+    ra.decode_step_ex(qs[0].view(1, H_q, 128), kv_host, seq, N, kt, k, ns, win, ex_out, ex_lse, ex_idx, ws_d)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(3):
-        ra.decode_step(qs[0].view(1, H_q, 128), kv_host, seq, N, kt, k, ns, win, ex_out, ex_lse,
+        ra.decode_step_ex(qs[0].view(1, H_q, 128), kv_host, seq, N, kt, k, ns, win, ex_out, ex_lse,
                        ex_idx, ws_d)
     torch.cuda.synchronize()
     exact_host_ms = (time.perf_counter() - t0) * 1e3 / 3
     t0 = time.perf_counter()
     for _ in range(10):
-        ra.decode_step(qs[0].view(1, H_q, 128), kv_dev, seq, N, kt, k, ns, win, ex_out, ex_lse,
+        ra.decode_step_ex(qs[0].view(1, H_q, 128), kv_dev, seq, N, kt, k, ns, win, ex_out, ex_lse,
                        ex_idx, ws_d)
     torch.cuda.synchronize()
     exact_dev_ms = (time.perf_counter() - t0) * 1e3 / 10

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 4
+#define RA_ABI_VERSION 5
 #define RA_HEAD_DIM 128
 #define RA_PAGE_SIZE 64
 #define RA_MAX_SEQ_LEN (1 << 24) /* 16,777,216 positions per sequence */
@@ -109,13 +109,19 @@ ra_status ra_kv_append(const ra_kv_layer* kv, const uint16_t* k_new,
                        const uint16_t* v_new, const int32_t* pos, int32_t B,
                        hipStream_t stream);
 
-/* Flags of ra_decode_step and ra_decode_stages (other bits are rejected). */
+/* Flags of ra_decode_step_ex, ra_append_decode_step and ra_decode_stages
+   (other bits are rejected). */
 #define RA_DECODE_KEEP_SCORES 1u /* also leave the scores of the retrieved set
                                     in the workspace score rows (a check of
                                     the scores; it costs scattered writes) */
 
 /*
- * One decode step (see the top of this file for what it computes).
+ * One decode step (see the top of this file for what it computes), in the
+ * shape of the problem the slides pose: decode one new token at a time over
+ * a prefilled cache (frame "One question: how can decoding read less KV?"),
+ * with a fixed retrieval budget per query head and the static first/last
+ * positions (frames "Sparse attention renormalizes selected tokens" and "The
+ * GPU keeps 640 fixed positions").
  *  q:           device bf16 [B][H_q][128], the new token's queries,
  *               16-byte aligned.
  *  seq_lens:    device int32 [B], lengths N_b after the append, so the recent
@@ -124,27 +130,41 @@ ra_status ra_kv_append(const ra_kv_layer* kv, const uint16_t* k_new,
  *  k:           device int32 [B], per-sequence budget k_b (0 <= k_b <= k_max).
  *  n_sink, window: sizes of the static set (>= 0).
  *  out:         device fp32 [B][H_q][128].
- *  out_lse:     device fp32 [B][H_q] (may be NULL): log-sum-exp of z over
- *               W u Omega, -inf when that set is empty.
  *  out_idx:     device int32 [B][H_q][k_max]: Omega in ascending position
  *               order, then -1 up to k_max (may be NULL only if k_max == 0).
  *  ws, ws_bytes: device workspace of at least ra_decode_workspace_bytes(B,
  *               H_q, kv->H_kv, max_seq_len, k_max) bytes, 256-byte aligned;
  *               no initial contents are required. Calls that share a
  *               workspace must be ordered on one stream.
- *  flags:       0 or RA_DECODE_KEEP_SCORES.
  * An empty W u Omega gives out = 0. Launch count and grid sizes depend only on
  * the host arguments, so the call can be captured into a HIP graph.
+ * Equivalent to ra_decode_step_ex with out_lse = NULL and flags = 0.
  */
 ra_status ra_decode_step(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
                          const int32_t* seq_lens, int32_t B,
                          int32_t max_seq_len, const int32_t* k, int32_t k_max,
                          int32_t n_sink, int32_t window, float* out,
-                         float* out_lse, int32_t* out_idx, void* ws,
-                         size_t ws_bytes, uint32_t flags, hipStream_t stream);
+                         int32_t* out_idx, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
 
 /*
- * ra_kv_append followed by ra_decode_step, in one call and one launch
+ * ra_decode_step with two additions:
+ *  out_lse:     device fp32 [B][H_q] (may be NULL): log-sum-exp of z over
+ *               W u Omega, -inf when that set is empty, so that the output
+ *               can be merged further by the same identity (frame "Two local
+ *               softmax outputs need global weights", Eqs. (3)-(5)).
+ *  flags:       0 or RA_DECODE_KEEP_SCORES.
+ * Every other argument as for ra_decode_step.
+ */
+ra_status ra_decode_step_ex(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
+                            const int32_t* seq_lens, int32_t B,
+                            int32_t max_seq_len, const int32_t* k, int32_t k_max,
+                            int32_t n_sink, int32_t window, float* out,
+                            float* out_lse, int32_t* out_idx, void* ws,
+                            size_t ws_bytes, uint32_t flags, hipStream_t stream);
+
+/*
+ * ra_kv_append followed by ra_decode_step_ex, in one call and one launch
  * fewer: the new token's rows (k_new, v_new: device bf16 [B][H_kv][128],
  * 16-byte aligned; pos: device int32 [B], as for ra_kv_append) are written
  * by the step's second kernel, after the sampled bound's kernel (which may

@@ -63,7 +63,7 @@ def gpu_decode(L: synth.LayerInputs, max_seq_len: int | None = None, k_max: int 
     idx = torch.full((B, H_q, max(k_max, 1)), -7, dtype=torch.int32, device=dev)
     ws = ra.alloc_workspace(B, H_q, L.H_kv, max_seq_len, k_max, device=dev)
     ws.fill_(0xA5)  # no initial contents are required
-    ra.decode_step(L.q, kv, seq, max_seq_len, kt, k_max, n_sink, window, out, lse,
+    ra.decode_step_ex(L.q, kv, seq, max_seq_len, kt, k_max, n_sink, window, out, lse,
                    idx if k_max else None, ws, keep_scores=with_scores)
     # the score rows hold W and (kept) the retrieved positions after the step
     sc = ra.scores_view(ws, B, H_q, L.H_kv, max_seq_len, k_max).clone() if with_scores else None

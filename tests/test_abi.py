@@ -24,7 +24,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("ra_abi_version", "ra_status_str", "ra_decode_workspace_bytes",
-              "ra_kv_append", "ra_decode_step"):
+              "ra_kv_append", "ra_decode_step", "ra_decode_step_ex"):
         assert n in names
 
 
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert ra.abi_version() == 4
+    assert ra.abi_version() == 5
     assert ra.status_str(ra.RA_OK) == "RA_OK"
     assert ra.status_str(ra.RA_ERR_WORKSPACE) == "RA_ERR_WORKSPACE"
     assert ra.status_str(99) == "RA_ERR_UNKNOWN"
@@ -74,10 +74,22 @@ def _decode(kv=None, **kw):
              ws_bytes=1 << 40, flags=0)
     a.update(kw)
     kv = kv if kv is not None else _kv()
+    return _lib.raw.ra_decode_step_ex(a["q"], a["H_q"], ctypes.byref(kv), a["seq_lens"], a["B"],
+                                      a["max_seq_len"], a["k"], a["k_max"], a["n_sink"],
+                                      a["window"], a["out"], a["lse"], a["out_idx"], a["ws"],
+                                      a["ws_bytes"], a["flags"], None)
+
+
+def _decode_plain(kv=None, **kw):
+    # ra_decode_step: the boundary's own prototype (no out_lse, no flags)
+    a = dict(q=FAKE, H_q=4, seq_lens=FAKE, B=1, max_seq_len=640, k=FAKE, k_max=8,
+             n_sink=4, window=8, out=FAKE, out_idx=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    kv = kv if kv is not None else _kv()
     return _lib.raw.ra_decode_step(a["q"], a["H_q"], ctypes.byref(kv), a["seq_lens"], a["B"],
                                    a["max_seq_len"], a["k"], a["k_max"], a["n_sink"],
-                                   a["window"], a["out"], a["lse"], a["out_idx"], a["ws"],
-                                   a["ws_bytes"], a["flags"], None)
+                                   a["window"], a["out"], a["out_idx"], a["ws"],
+                                   a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -107,6 +119,9 @@ def test_decode_validation(kw, status):
     kw = dict(kw)
     kw.pop("kv", None)
     assert _decode(**kw) == status
+    if "flags" not in kw:
+        # the plain prototype validates the same way
+        assert _decode_plain(**kw) == status
 
 
 def test_decode_validation_of_the_kv_descriptor():
@@ -118,8 +133,11 @@ def test_decode_validation_of_the_kv_descriptor():
     assert _decode(kv=_kv(k_pool=FAKE + 4)) == ra.RA_ERR_INVALID_ARGUMENT
     assert _decode(kv=_kv(block_table=FAKE + 2)) == ra.RA_ERR_INVALID_ARGUMENT
     assert _decode(kv=_kv(H_kv=3)) == ra.RA_ERR_INVALID_ARGUMENT  # 4 % 3
-    assert _lib.raw.ra_decode_step(FAKE, 4, None, FAKE, 1, 640, FAKE, 8, 4, 8, FAKE, None,
-                                   FAKE, FAKE, 1 << 40, 0, None) == ra.RA_ERR_INVALID_ARGUMENT
+    assert _lib.raw.ra_decode_step_ex(FAKE, 4, None, FAKE, 1, 640, FAKE, 8, 4, 8, FAKE, None,
+                                      FAKE, FAKE, 1 << 40, 0, None) == ra.RA_ERR_INVALID_ARGUMENT
+    assert _lib.raw.ra_decode_step(FAKE, 4, None, FAKE, 1, 640, FAKE, 8, 4, 8, FAKE,
+                                   FAKE, FAKE, 1 << 40, None) == ra.RA_ERR_INVALID_ARGUMENT
+    assert _decode_plain(kv=_kv(head_dim=64)) == ra.RA_ERR_UNSUPPORTED
 
 
 def test_k_max_zero_allows_null_out_idx_until_a_later_check():
@@ -134,6 +152,7 @@ def test_stage_range_validation():
     assert _lib.raw.ra_decode_stages(*args, 3, 2, None) == ra.RA_ERR_INVALID_ARGUMENT
     assert _lib.raw.ra_decode_stages(*args, -1, 2, None) == ra.RA_ERR_INVALID_ARGUMENT
     assert _lib.raw.ra_decode_stages(*args, 0, 6, None) == ra.RA_ERR_INVALID_ARGUMENT
+    assert ra.STAGE_COUNT == 6 and len(ra.STAGE_NAMES) == 6
 
 
 def test_kv_append_validation():

@@ -47,7 +47,7 @@ def test_fused_append_equals_append_then_decode(lens, window, k, steps):
         pos = torch.tensor([n + s for n in lens], dtype=torch.int32, device=DEV)
         seq = pos + 1
         ra.kv_append(kv_a, k_s[s], v_s[s], pos)
-        ra.decode_step(q_s[s], kv_a, seq, max_len, kt, k, ns, window, *outs[0], ws_a)
+        ra.decode_step_ex(q_s[s], kv_a, seq, max_len, kt, k, ns, window, *outs[0], ws_a)
         ra.append_decode_step(k_s[s], v_s[s], pos, q_s[s], kv_f, seq, max_len, kt, k, ns, window,
                               *outs[1], ws_f)
         torch.cuda.synchronize()

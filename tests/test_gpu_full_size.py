@@ -2,17 +2,18 @@
 bench.py times.
 
 * One Llama-3-8B layer (H_q=32, H_kv=8) at N = 1,048,576 with k = 1, 2 and
-  3 % of N: the whole step runs on the GPU; the oracle checks the first and
-  the last KV group (8 of the 32 query heads) element by element, and every
-  planted needle of every head must be retrieved.
+  3 % of N: the whole step runs on the GPU; the oracle checks all eight KV
+  groups (all 32 query heads) element by element, and every planted needle
+  of every head must be retrieved.
 * The 32-layer workload: layers 0, 15 and 31 (seeds 0, 15, 31) run the same
-  1002 append + decode token steps as the benchmark (2 warm-up steps, then
-  1000), with the same capacity; the oracle checks two KV groups of each of
-  them after the first, a middle and the last step.
+  1002 token steps as the benchmark (2 warm-up steps, then 1000), each one
+  call of ra_append_decode_step (the new token's rows written inside the
+  step, as the benchmark times it), with the same capacity; the oracle
+  checks all 32 heads of each of them after the first, a middle and the
+  last step.
 
-Oracle time is about a second per KV group at N = 1M, so the groups are
-sampled; layers are independent, so the sampled layers see exactly what
-they see in the 32-layer run.
+Layers are independent, so the sampled layers see exactly what they see in
+the 32-layer run.
 """
 
 import dataclasses
@@ -28,7 +29,7 @@ from tests.parity import Run, compare_sequence, gpu_decode, say
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-SAMPLED_GROUPS = ([0, 1, 2, 3], [28, 29, 30, 31])
+ALL_GROUPS = [list(range(4 * g, 4 * g + 4)) for g in range(8)]
 
 
 @pytest.fixture(autouse=True, scope="module")
@@ -40,12 +41,12 @@ def _need_gpu():
 def test_one_layer_at_a_million_tokens(name):
     c = synth.config(name)
     n = c.seq_lens[0]
-    say(f"case {name}: H_q=32 H_kv=8 N={n} k={c.k_for(n)} (groups 0 and 7 checked)")
+    say(f"case {name}: H_q=32 H_kv=8 N={n} k={c.k_for(n)} (all 32 heads checked)")
     L = synth.make_layer(c.H_q, c.H_kv, [n], [c.k_for(n)], c.n_sink, c.window,
                          c.needles_per_head, c.seed, DEV)
     run = gpu_decode(L, with_scores=True)
     assert run.rescanned == 0  # the sample's margin holds on this workload
-    for heads in SAMPLED_GROUPS:
+    for heads in ALL_GROUPS:
         st = compare_sequence(L, run, 0, heads=heads)
         say(f"  heads {heads[0]}..{heads[-1]}: band differences {st['band_diffs']}")
     missed = [(pos, h) for pos, h in L.needles[0] if pos not in run.idx[0, h]]
@@ -83,16 +84,15 @@ def test_32_layer_workload_sampled_layers_over_1000_steps():
     for s in range(total):
         for l in sampled:
             q, kn, vn = streams[l][0][s], streams[l][1][s], streams[l][2][s]
-            ra.kv_append(kvs[l], kn, vn, pos_all[s])
-            ra.decode_step(q, kvs[l], seq_all[s], max_seq_len, k_all[s], k_max, c.n_sink,
-                           c.window, out, lse, idx, ws)
+            ra.append_decode_step(kn, vn, pos_all[s], q, kvs[l], seq_all[s], max_seq_len,
+                                  k_all[s], k_max, c.n_sink, c.window, out, lse, idx, ws)
             if s in checks:
                 torch.cuda.synchronize()
                 run = Run(out.cpu().numpy().astype(np.float64),
                           lse.cpu().numpy().astype(np.float64),
                           idx.cpu().numpy())
                 view = dataclasses.replace(layers[l], q=q, seq_lens=[lens[s]], ks=[ks[s]])
-                for heads in SAMPLED_GROUPS:
+                for heads in ALL_GROUPS:
                     st = compare_sequence(view, run, 0, heads=heads, check_score_rows=False)
                     say(f"  step {s} layer {l} heads {heads[0]}..{heads[-1]}: "
                         f"band differences {st['band_diffs']}")

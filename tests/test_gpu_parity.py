@@ -45,6 +45,27 @@ def test_c1_tiny_full_parity():
     assert st["band_diffs"] == 0
 
 
+def test_boundary_prototype_equals_the_extended_call():
+    # ra_decode_step (the boundary's own prototype: no out_lse, no flags)
+    # against ra_decode_step_ex on the same inputs: bit-identical out and
+    # out_idx, both equal to the oracle
+    say("case boundary: C1 through ra_decode_step and ra_decode_step_ex")
+    L = cfg_layer("C1")
+    n, k = L.seq_lens[0], L.ks[0]
+    kv = ra.KVLayer(L.k_pool, L.v_pool, L.block_table)
+    seq = torch.tensor([n], dtype=torch.int32, device=DEV)
+    kt = torch.tensor([k], dtype=torch.int32, device=DEV)
+    out = torch.full((1, L.H_q, 128), float("nan"), device=DEV)
+    idx = torch.full((1, L.H_q, k), -7, dtype=torch.int32, device=DEV)
+    ws = ra.alloc_workspace(1, L.H_q, L.H_kv, n, k, device=DEV)
+    ra.decode_step(L.q, kv, seq, n, kt, k, L.n_sink, L.window, out, idx, ws)
+    run = gpu_decode(L)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), run.out)
+    assert np.array_equal(idx.cpu().numpy(), run.idx)
+    compare_sequence(L, run, 0)
+
+
 def test_kv_append_writes_the_right_slot():
     say("case kv_append: B=3 H_kv=2 shuffled pages")
     L = layer(8, 2, [100, 64, 1], [4, 4, 4], 4, 8, shuffle_pages=True, reserve_tokens=130)

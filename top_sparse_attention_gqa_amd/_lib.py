@@ -3,7 +3,11 @@
 Every step of the decode path runs in the library's HIP kernels. If the
 library has not been built this module raises on import: there is no
 fallback. Tensors are torch tensors on the GPU; they are passed as raw
-pointers, with their dtype, shape, contiguity and alignment checked first.
+pointers, with their dtype, contiguity and alignment checked first, and for
+the decode path (kv_append, decode_step, decode_step_ex, decode_stages,
+append_decode_step) their shapes against B, H_q, H_kv and k_max as well, so
+that an undersized output never becomes an out-of-bounds device write.
+Arguments given as raw integer addresses are passed through unchecked.
 """
 
 from __future__ import annotations
@@ -46,7 +50,7 @@ PF_STAGE_NAMES = ["sample", "bound", "filter", "select",
                   "exact_maxima", "exact_threshold", "exact_filter", "exact_select"]
 
 EXPORTS = ["ra_abi_version", "ra_status_str", "ra_decode_workspace_bytes",
-           "ra_kv_append", "ra_decode_step", "ra_decode_stages",
+           "ra_kv_append", "ra_decode_step", "ra_decode_step_ex", "ra_decode_stages",
            "ra_workspace_scores_offset", "ra_workspace_rescan_count_offset",
            "ra_prefill_workspace_bytes", "ra_prefill_topk", "ra_prefill_stages",
            "ra_prefill_workspace_fail_offset",
@@ -102,7 +106,11 @@ _DECODE_ARGS = [c_void_p, c_int32, POINTER(KVLayerStruct), c_void_p, c_int32, c_
                 c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                 c_void_p, c_size_t]
 _lib.ra_decode_step.restype = c_int
-_lib.ra_decode_step.argtypes = _DECODE_ARGS + [c_uint32, c_void_p]
+_lib.ra_decode_step.argtypes = [c_void_p, c_int32, POINTER(KVLayerStruct), c_void_p, c_int32,
+                                c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                c_void_p, c_void_p, c_size_t, c_void_p]
+_lib.ra_decode_step_ex.restype = c_int
+_lib.ra_decode_step_ex.argtypes = _DECODE_ARGS + [c_uint32, c_void_p]
 _lib.ra_decode_stages.restype = c_int
 _lib.ra_decode_stages.argtypes = _DECODE_ARGS + [c_uint32, c_int32, c_int32, c_void_p]
 _lib.ra_append_decode_step.restype = c_int
@@ -225,10 +233,69 @@ def alloc_workspace(B, H_q, H_kv, max_seq_len, k_max, device="cuda") -> torch.Te
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _shape(t, want, name):
+    """Raise ValueError unless tensor t has shape `want` (raw addresses pass)."""
+    if t is None or isinstance(t, int):
+        return
+    if tuple(t.shape) != tuple(want):
+        raise ValueError(f"{name} must have shape {tuple(want)}, got {tuple(t.shape)}")
+
+
+def _numel(t, n, name):
+    if t is None or isinstance(t, int):
+        return
+    if t.numel() != n:
+        raise ValueError(f"{name} must hold {n} elements, got {t.numel()}")
+
+
+def _check_batch(kv: KVLayer, B: int):
+    if B <= 0:
+        raise ValueError("the batch must hold at least one sequence")
+    if kv.block_table.shape[0] < B:
+        raise ValueError(f"block_table has {kv.block_table.shape[0]} rows for a batch of {B}")
+
+
+def _check_decode(q, kv: KVLayer, seq_lens, k, k_max, out, out_lse, out_idx):
+    """Shapes of the decode-step tensors; returns (B, H_q)."""
+    if isinstance(q, int) or q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be a [B][H_q][128] tensor")
+    B, H_q = int(q.shape[0]), int(q.shape[1])
+    if H_q % kv.H_kv != 0:
+        raise ValueError(f"H_q={H_q} is not a multiple of H_kv={kv.H_kv}")
+    if k_max < 0:
+        raise ValueError("k_max must be >= 0")
+    _check_batch(kv, B)
+    _numel(seq_lens, B, "seq_lens")
+    _numel(k, B, "k")
+    _shape(out, (B, H_q, HEAD_DIM), "out")
+    _shape(out_lse, (B, H_q), "out_lse")
+    if k_max > 0:
+        _shape(out_idx, (B, H_q, k_max), "out_idx")
+    return B, H_q
+
+
+def _check_append(kv: KVLayer, k_new, v_new, pos):
+    if isinstance(pos, int):
+        raise ValueError("pos must be a tensor (its length is the batch)")
+    B = int(pos.numel())
+    _check_batch(kv, B)
+    _shape(k_new, (B, kv.H_kv, HEAD_DIM), "k_new")
+    _shape(v_new, (B, kv.H_kv, HEAD_DIM), "v_new")
+    return B
+
+
+def _flags(keep_scores):
+    return DECODE_KEEP_SCORES if keep_scores else 0
+
+
+def _ws_numel(ws):
+    return ws.numel() if not isinstance(ws, int) else 0
+
+
 def kv_append(kv: KVLayer, k_new, v_new, pos, stream=None) -> None:
     """ra_kv_append: write one token's K/V rows ([B][H_kv][128] bf16) at
     positions pos ([B] int32)."""
-    B = pos.shape[0]
+    B = _check_append(kv, k_new, v_new, pos)
     st = _lib.ra_kv_append(ctypes.byref(kv.struct), _ptr(k_new, torch.bfloat16, "k_new", align=16),
                            _ptr(v_new, torch.bfloat16, "v_new", align=16), _ptr(pos, torch.int32, "pos"),
                            B, _stream(stream))
@@ -237,46 +304,67 @@ def kv_append(kv: KVLayer, k_new, v_new, pos, stream=None) -> None:
 
 
 def decode_stages(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, window,
-                  out, out_lse, out_idx, ws, first=STAGE_SAMPLE, last=STAGE_MERGE,
+                  out, out_lse, out_idx, ws, first=0, last=None,
                   stream=None, keep_scores=False) -> None:
-    """ra_decode_stages (ra_decode_step when first..last covers every stage).
+    """ra_decode_stages (the whole step when first..last covers every stage).
     keep_scores: also leave the retrieved set's scores in the score rows."""
-    B, H_q = q.shape[0], q.shape[1]
+    B, H_q = _check_decode(q, kv, seq_lens, k, k_max, out, out_lse, out_idx)
+    last = STAGE_COUNT - 1 if last is None else last
     st = _lib.ra_decode_stages(
         _ptr(q, torch.bfloat16, "q", align=16), H_q, ctypes.byref(kv.struct),
         _ptr(seq_lens, torch.int32, "seq_lens"), B, max_seq_len, _ptr(k, torch.int32, "k"),
         k_max, n_sink, window, _ptr(out, torch.float32, "out"),
         _ptr(out_lse, torch.float32, "out_lse", nullable=True),
         _ptr(out_idx, torch.int32, "out_idx", nullable=(k_max == 0)),
-        _ptr(ws, torch.uint8, "ws", align=256), ws.numel() if not isinstance(ws, int) else 0,
-        DECODE_KEEP_SCORES if keep_scores else 0, first, last, _stream(stream))
+        _ptr(ws, torch.uint8, "ws", align=256), _ws_numel(ws),
+        _flags(keep_scores), first, last, _stream(stream))
     if st != RA_OK:
         raise RAError(st, "ra_decode_stages")
 
 
 def decode_step(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, window,
-                out, out_lse, out_idx, ws, stream=None, keep_scores=False) -> None:
+                out, out_idx, ws, stream=None) -> None:
     """ra_decode_step: one exact top-k sparse GQA decode step.
-    keep_scores: also leave the retrieved set's scores in the score rows."""
-    B, H_q = q.shape[0], q.shape[1]
+    q bf16 [B][H_q][128]; seq_lens, k int32 [B]; out fp32 [B][H_q][128];
+    out_idx int32 [B][H_q][k_max]; ws from alloc_workspace."""
+    B, H_q = _check_decode(q, kv, seq_lens, k, k_max, out, None, out_idx)
     st = _lib.ra_decode_step(
+        _ptr(q, torch.bfloat16, "q", align=16), H_q, ctypes.byref(kv.struct),
+        _ptr(seq_lens, torch.int32, "seq_lens"), B, max_seq_len, _ptr(k, torch.int32, "k"),
+        k_max, n_sink, window, _ptr(out, torch.float32, "out"),
+        _ptr(out_idx, torch.int32, "out_idx", nullable=(k_max == 0)),
+        _ptr(ws, torch.uint8, "ws", align=256), _ws_numel(ws), _stream(stream))
+    if st != RA_OK:
+        raise RAError(st, "ra_decode_step")
+
+
+def decode_step_ex(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, window,
+                   out, out_lse, out_idx, ws, stream=None, keep_scores=False) -> None:
+    """ra_decode_step_ex: decode_step plus the per-head log-sum-exp
+    (out_lse fp32 [B][H_q], or None) and the flags.
+    keep_scores: also leave the retrieved set's scores in the score rows."""
+    B, H_q = _check_decode(q, kv, seq_lens, k, k_max, out, out_lse, out_idx)
+    st = _lib.ra_decode_step_ex(
         _ptr(q, torch.bfloat16, "q", align=16), H_q, ctypes.byref(kv.struct),
         _ptr(seq_lens, torch.int32, "seq_lens"), B, max_seq_len, _ptr(k, torch.int32, "k"),
         k_max, n_sink, window, _ptr(out, torch.float32, "out"),
         _ptr(out_lse, torch.float32, "out_lse", nullable=True),
         _ptr(out_idx, torch.int32, "out_idx", nullable=(k_max == 0)),
-        _ptr(ws, torch.uint8, "ws", align=256), ws.numel(),
-        DECODE_KEEP_SCORES if keep_scores else 0, _stream(stream))
+        _ptr(ws, torch.uint8, "ws", align=256), _ws_numel(ws),
+        _flags(keep_scores), _stream(stream))
     if st != RA_OK:
-        raise RAError(st, "ra_decode_step")
+        raise RAError(st, "ra_decode_step_ex")
 
 
 def append_decode_step(k_new, v_new, pos, q, kv: KVLayer, seq_lens, max_seq_len, k, k_max,
                        n_sink, window, out, out_lse, out_idx, ws, stream=None,
                        keep_scores=False) -> None:
     """ra_append_decode_step: kv_append of (k_new, v_new) at pos, then the
-    decode step, with one launch fewer (the rows are written inside it)."""
-    B, H_q = q.shape[0], q.shape[1]
+    decode step (as decode_step_ex), with one launch fewer (the rows are
+    written inside it)."""
+    B, H_q = _check_decode(q, kv, seq_lens, k, k_max, out, out_lse, out_idx)
+    if _check_append(kv, k_new, v_new, pos) != B:
+        raise ValueError("pos must hold one position per sequence of q")
     st = _lib.ra_append_decode_step(
         _ptr(k_new, torch.bfloat16, "k_new", align=16), _ptr(v_new, torch.bfloat16, "v_new", align=16),
         _ptr(pos, torch.int32, "pos"),
@@ -285,10 +373,11 @@ def append_decode_step(k_new, v_new, pos, q, kv: KVLayer, seq_lens, max_seq_len,
         k_max, n_sink, window, _ptr(out, torch.float32, "out"),
         _ptr(out_lse, torch.float32, "out_lse", nullable=True),
         _ptr(out_idx, torch.int32, "out_idx", nullable=(k_max == 0)),
-        _ptr(ws, torch.uint8, "ws", align=256), ws.numel(),
-        DECODE_KEEP_SCORES if keep_scores else 0, _stream(stream))
+        _ptr(ws, torch.uint8, "ws", align=256), _ws_numel(ws),
+        _flags(keep_scores), _stream(stream))
     if st != RA_OK:
         raise RAError(st, "ra_append_decode_step")
+
 
 def scores_view(ws: torch.Tensor, B, H_q, H_kv, max_seq_len, k_max) -> torch.Tensor:
     """The fp32 score rows [B][H_q][row_stride] inside a workspace: after the

@@ -200,6 +200,14 @@ void gather_kernel(Params p) {
   }
   __syncthreads();
   if (tid < G) s_mref[tid] = softmax_ref(s_st[tid], sg.k_eff);
+  if (tid < kLists && s_st[tid / kUnitsPerTile].dense != 0u) {
+    // a rescanned head's lists hold every member of M at its place: their
+    // lengths are the units' overlaps with M
+    const int unit = kUnitsPerTile * tile + tid % kUnitsPerTile;
+    const int ov = min((unit + 1) * kUnit, sg.hi) - max(unit * kUnit, sg.lo);
+    s_lc[tid] = ov > 0 ? uint32_t(ov) : 0u;
+  }
+  __syncthreads();
   // when the tile's lists fit the LDS staging, the retrieved scores stay in
   // LDS; otherwise they go to the score rows and are read back
   uint32_t listed = 0;

@@ -312,15 +312,25 @@ ra_status ra_append_decode_step(const uint16_t* k_new, const uint16_t* v_new,
   return RA_OK;
 }
 
+ra_status ra_decode_step_ex(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
+                            const int32_t* seq_lens, int32_t B,
+                            int32_t max_seq_len, const int32_t* k, int32_t k_max,
+                            int32_t n_sink, int32_t window, float* out,
+                            float* out_lse, int32_t* out_idx, void* ws,
+                            size_t ws_bytes, uint32_t flags, hipStream_t stream) {
+  return ra_decode_stages(q, H_q, kv, seq_lens, B, max_seq_len, k, k_max,
+                          n_sink, window, out, out_lse, out_idx, ws, ws_bytes,
+                          flags, RA_STAGE_SAMPLE, RA_STAGE_MERGE, stream);
+}
+
 ra_status ra_decode_step(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
                          const int32_t* seq_lens, int32_t B,
                          int32_t max_seq_len, const int32_t* k, int32_t k_max,
                          int32_t n_sink, int32_t window, float* out,
-                         float* out_lse, int32_t* out_idx, void* ws,
-                         size_t ws_bytes, uint32_t flags, hipStream_t stream) {
-  return ra_decode_stages(q, H_q, kv, seq_lens, B, max_seq_len, k, k_max,
-                          n_sink, window, out, out_lse, out_idx, ws, ws_bytes,
-                          flags, RA_STAGE_SAMPLE, RA_STAGE_MERGE, stream);
+                         int32_t* out_idx, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  return ra_decode_step_ex(q, H_q, kv, seq_lens, B, max_seq_len, k, k_max, n_sink,
+                           window, out, nullptr, out_idx, ws, ws_bytes, 0u, stream);
 }
 
 size_t ra_prefill_workspace_fail_offset(int32_t T, int32_t H_q, int32_t N, int32_t k) {

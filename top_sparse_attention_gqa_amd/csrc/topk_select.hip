@@ -607,7 +607,9 @@ __device__ __forceinline__ void select_head(const Params& p, int bh, const SeqGe
 // blocks only read the lengths. Finished units are counted per group, and
 // the block that finishes a group's last unit selects again, over every
 // member of M, for the group's short heads (their lists now hold all of M,
-// so the list lengths are the units' overlaps with it).
+// so the list lengths are the units' overlaps with it). Nothing in this
+// launch rewrites the counts the select blocks read, so it does not matter
+// in which order the two kinds of blocks run.
 static_assert(kScanThreads == kSelThreads, "the rescan blocks also select");
 
 __device__ __forceinline__ void select_block(const Params& p, int bh, SelLds& L) {
@@ -652,12 +654,11 @@ __device__ __forceinline__ void reselect_head(const Params& p, int bh, SelLds& L
   const HeadState st = p.state[bh];
   const SeqGeom sg = seq_geom(p, bh / p.H_q);
   const int u_lo = sg.lo / kUnit, nu = (sg.hi - 1) / kUnit + 1 - u_lo;
+  // the lists hold every member of M now, so their lengths are the units'
+  // overlaps with M; the candidate counts stay as the scan wrote them (the
+  // select blocks of this launch read them, and the gather derives a
+  // rescanned head's lengths from its dense flag instead)
   const UnitLists gl = unit_prefix(p, bh, sg, u_lo, nu, true, 0u, L);
-  uint32_t* uc = p.ucnt + size_t(bh) * p.n_units;
-  for (int i = threadIdx.x; i < nu; i += kSelThreads) {
-    const int x = u_lo + i;
-    uc[x] = uint32_t(min((x + 1) * kUnit, sg.hi) - max(x * kUnit, sg.lo));
-  }
   // all of M: far more than registers hold, so streamed on every pass
   const uint32_t span = st.max_m > 0u ? st.max_m : 1u;
   decide(p, bh, sg, gl, 32 + bit_length(span), 0u, L);
