@@ -164,6 +164,30 @@ ra_status ra_decode_step_ex(const uint16_t* q, int32_t H_q, const ra_kv_layer* k
                             size_t ws_bytes, uint32_t flags, hipStream_t stream);
 
 /*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): ra_decode_step_ex
+ * without a workspace argument. Its workspace is a device array inside the
+ * library of RA_NOALLOC_WS_BYTES bytes, one per GPU it runs on, held until
+ * the process ends; this call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine). Its first call on a device looks up that
+ * device's copy of the array (hipGetSymbolAddress, with the device current).
+ *  Returns RA_ERR_WORKSPACE when ra_decode_workspace_bytes(B, H_q,
+ *  kv->H_kv, max_seq_len, k_max) exceeds RA_NOALLOC_WS_BYTES (64 MiB: one
+ *  Llama-3-8B layer, 32 query heads, up to 131072 tokens), RA_ERR_HIP if the
+ *  array's address cannot be found. Every other argument, the validation and
+ *  the results as for ra_decode_step_ex.
+ *  All calls on one GPU share its array and no initial contents are needed,
+ *  but calls that overlap in time on one GPU (other streams, other host
+ *  threads) race on it: order them on one stream.
+ */
+#define RA_NOALLOC_WS_BYTES (64u << 20)
+ra_status ra_decode_step_noalloc(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
+                                 const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
+                                 const int32_t* k, int32_t k_max, int32_t n_sink,
+                                 int32_t window, float* out, float* out_lse, int32_t* out_idx,
+                                 uint32_t flags, hipStream_t stream);
+
+/*
  * ra_kv_append followed by ra_decode_step_ex, in one call and one launch
  * fewer: the new token's rows (k_new, v_new: device bf16 [B][H_kv][128],
  * 16-byte aligned; pos: device int32 [B], as for ra_kv_append) are written

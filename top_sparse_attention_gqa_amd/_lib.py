@@ -55,7 +55,8 @@ EXPORTS = ["ra_abi_version", "ra_status_str", "ra_decode_workspace_bytes",
            "ra_prefill_workspace_bytes", "ra_prefill_topk", "ra_prefill_stages",
            "ra_prefill_workspace_fail_offset",
            "ra_layer_budgets", "ra_graph_build", "ra_graph_search", "ra_sparse_attend",
-           "ra_merge_partials", "ra_host_device_pointer", "ra_append_decode_step"]
+           "ra_merge_partials", "ra_host_device_pointer", "ra_append_decode_step",
+           "ra_decode_step_noalloc"]
 
 
 class KVLayerStruct(ctypes.Structure):
@@ -113,6 +114,11 @@ _lib.ra_decode_step_ex.restype = c_int
 _lib.ra_decode_step_ex.argtypes = _DECODE_ARGS + [c_uint32, c_void_p]
 _lib.ra_decode_stages.restype = c_int
 _lib.ra_decode_stages.argtypes = _DECODE_ARGS + [c_uint32, c_int32, c_int32, c_void_p]
+_lib.ra_decode_step_noalloc.restype = c_int
+_lib.ra_decode_step_noalloc.argtypes = [c_void_p, c_int32, POINTER(KVLayerStruct), c_void_p, c_int32,
+                                        c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                        c_void_p, c_void_p, c_uint32, c_void_p]
+NOALLOC_WS_BYTES = 64 << 20
 _lib.ra_append_decode_step.restype = c_int
 _lib.ra_append_decode_step.argtypes = [c_void_p, c_void_p, c_void_p] + _DECODE_ARGS + [c_uint32, c_void_p]
 
@@ -354,6 +360,22 @@ def decode_step_ex(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, wind
         _flags(keep_scores), _stream(stream))
     if st != RA_OK:
         raise RAError(st, "ra_decode_step_ex")
+
+
+def decode_step_noalloc(q, kv: KVLayer, seq_lens, max_seq_len, k, k_max, n_sink, window,
+                        out, out_lse, out_idx, stream=None, keep_scores=False) -> None:
+    """ra_decode_step_noalloc: decode_step_ex with the library's own device
+    workspace (NOALLOC_WS_BYTES per GPU); allocates nothing."""
+    B, H_q = _check_decode(q, kv, seq_lens, k, k_max, out, out_lse, out_idx)
+    st = _lib.ra_decode_step_noalloc(
+        _ptr(q, torch.bfloat16, "q", align=16), H_q, ctypes.byref(kv.struct),
+        _ptr(seq_lens, torch.int32, "seq_lens"), B, max_seq_len, _ptr(k, torch.int32, "k"),
+        k_max, n_sink, window, _ptr(out, torch.float32, "out"),
+        _ptr(out_lse, torch.float32, "out_lse", nullable=True),
+        _ptr(out_idx, torch.int32, "out_idx", nullable=(k_max == 0)),
+        _flags(keep_scores), _stream(stream))
+    if st != RA_OK:
+        raise RAError(st, "ra_decode_step_noalloc")
 
 
 def append_decode_step(k_new, v_new, pos, q, kv: KVLayer, seq_lens, max_seq_len, k, k_max,

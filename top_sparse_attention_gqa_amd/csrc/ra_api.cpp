@@ -195,6 +195,35 @@ static Params make_params(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
   return p;
 }
 
+// ------------------------------------------------------------------
+// Workspace of ra_decode_step_noalloc: a file-scope device array, one copy
+// per GPU the library runs on, held until the process ends. In host code
+// `scratch` names a host-side stand-in, never a device address: its device
+// address comes from hipGetSymbolAddress, taken once per device (with that
+// device current) on the entry point's first call there, and only that
+// address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[RA_NOALLOC_WS_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the current device, or null.
+static void* scratch_on_current_device() {
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> g(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();  // clear the sticky error
+      return nullptr;
+    }
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+
 }  // namespace ra
 
 using namespace ra;
@@ -321,6 +350,23 @@ ra_status ra_decode_step_ex(const uint16_t* q, int32_t H_q, const ra_kv_layer* k
   return ra_decode_stages(q, H_q, kv, seq_lens, B, max_seq_len, k, k_max,
                           n_sink, window, out, out_lse, out_idx, ws, ws_bytes,
                           flags, RA_STAGE_SAMPLE, RA_STAGE_MERGE, stream);
+}
+
+ra_status ra_decode_step_noalloc(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
+                                 const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
+                                 const int32_t* k, int32_t k_max, int32_t n_sink,
+                                 int32_t window, float* out, float* out_lse, int32_t* out_idx,
+                                 uint32_t flags, hipStream_t stream) {
+  // sizes beyond the array are rejected before anything else is looked at
+  WsLayout L;
+  if (kv != nullptr && ws_layout(B, H_q, kv->H_kv, max_seq_len, k_max, &L) &&
+      L.total > size_t(RA_NOALLOC_WS_BYTES))
+    return RA_ERR_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return RA_ERR_HIP;
+  return ra_decode_step_ex(q, H_q, kv, seq_lens, B, max_seq_len, k, k_max, n_sink, window,
+                           out, out_lse, out_idx, ws, size_t(RA_NOALLOC_WS_BYTES), flags,
+                           stream);
 }
 
 ra_status ra_decode_step(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
