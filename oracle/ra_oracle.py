@@ -396,22 +396,42 @@ def graph_build(hubs, lists, N: int, D: int):
     return out, entry
 
 
-def graph_search(q, K, nbr, entry: int, ef: int, k: int, batch: int = 1):
+def graph_search(q, K, nbr, entry: int, ef: int, k: int, batch: int = 1,
+                 scoring: str = "f32", trace=None):
     """Best-first search of the key graph with one decode query.
 
     A result list R keeps the ef best visited keys by (score, lower
-    position), scores from ``score_f32_ordered``. Starting from the entry
-    point, each round expands the ``batch`` best keys of R not yet expanded
-    (fewer if fewer are left): every neighbour of theirs not visited before
-    is visited, scored and offered to R. The search ends when every key in R
-    has been expanded. Returns (the best min(k, |R|) keys of R in ascending
-    position, the number of keys visited).
+    position). Starting from the entry point, each round expands the
+    ``batch`` best keys of R not yet expanded (fewer if fewer are left):
+    every neighbour of theirs not visited before is visited, scored and
+    offered to R. The search ends when every key in R has been expanded.
+    Returns (the best min(k, |R|) keys of R in ascending position, the
+    number of keys visited).
+
+    ``scoring``: "f32" ranks by ``score_f32_ordered`` (the dimension-by-
+    dimension fp32 sum); "f64" by the plain definition, q . k summed in
+    float64 after exact widening (Eq. (1) without the 1/sqrt(d), which does
+    not change the order). ``trace``: a list that receives, after every
+    round, (R as [(key, expanded)] in rank order, the sorted visited keys).
+    The batch size and the fp32 order are readings of this build: the frame
+    names a best-first search and no parameters.
     """
     if entry < 0:
         return np.zeros(0, dtype=np.int64), 0
     nbr = np.asarray(nbr)
+    if scoring == "f32":
+        def score(pos):
+            return [float(x) for x in score_f32_ordered(q, K, pos)]
+    elif scoring == "f64":
+        qf = as_f64(q)
+        Kf = np.asarray(K)
+
+        def score(pos):
+            return [float(x) for x in as_f64(Kf[np.asarray(pos, dtype=np.int64)]) @ qf]
+    else:
+        raise ValueError(f"unknown scoring {scoring!r}")
     visited = {int(entry)}
-    R = [(float(score_f32_ordered(q, K, [entry])[0]), int(entry), False)]
+    R = [(score([entry])[0], int(entry), False)]
     while True:
         R.sort(key=lambda e: (-e[0], e[1]))
         todo = [i for i, e in enumerate(R) if not e[2]][:batch]
@@ -426,9 +446,10 @@ def graph_search(q, K, nbr, entry: int, ef: int, k: int, batch: int = 1):
                     visited.add(u)
                     new.append(u)
         if new:
-            sc = score_f32_ordered(q, K, new)
-            R.extend((float(x), u, False) for x, u in zip(sc, new))
+            R.extend((x, u, False) for x, u in zip(score(new), new))
             R.sort(key=lambda e: (-e[0], e[1]))
             del R[ef:]
+        if trace is not None:
+            trace.append(([(e[1], e[2]) for e in R], sorted(visited)))
     best = sorted(e[1] for e in R[:k])
     return np.asarray(best, dtype=np.int64), len(visited)

@@ -5,7 +5,10 @@ queries teach the key graph what matters"). The oracle builds its own graph
 build. The search's decisions follow from fp32 scores both sides compute in
 the same order, so the retrieved keys and the number of keys visited must
 be equal exactly. Each round of the search expands the GRAPH_BATCH best
-unexpanded keys; the oracle is run with the same batch."""
+unexpanded keys; the oracle is run with the same batch. That batch and the
+fp32 order are readings of this build, pinned on the CPU by rounds worked
+by hand; one case here also checks the GPU against a search scored in plain
+float64, on keys no two of which score within the fp32 bound."""
 
 import numpy as np
 import pytest
@@ -125,3 +128,40 @@ def test_graph_search_without_a_graph_returns_nothing():
     got, vis = gpu_search(L, L.q[0], 0, N, [(empty, -1), (empty, 7)], 16, 8)
     assert (got[0] == -1).all() and vis[0] == 0
     assert got[1].tolist() == [7] + [-1] * 7 and vis[1] == 1
+
+
+def test_graph_search_equals_an_fp64_scored_search_when_no_scores_are_close():
+    # Keys whose exact scores are at least 2 fp32 dot-product bounds apart:
+    # key i of head h is c_i times the unit vector of q_h's largest
+    # coordinate (c_i a permutation of 0..255, exact in bf16) plus a 0.01
+    # noise. Then the fp32 sum in any order ranks the keys as the exact dot
+    # product does, and the GPU search must equal the oracle's search scored
+    # in plain float64 (the definition), not only its fp32 reading.
+    N, D, ef, k = 256, 16, 64, 32
+    say(f"case graph vs fp64-scored search: N={N} D={D} ef={ef} k={k}")
+    L = synth.make_layer(2, 2, [N], [8], 0, 0, 2, 26, DEV)
+    r = np.random.default_rng(27)
+    qb = synth.bf16_bits(L.q[0])
+    n = torch.arange(N, device=DEV)
+    pages, slots = L.block_table[0, n // 64].long(), n % 64
+    for h in range(2):
+        qf = oracle.as_f64(qb[h])
+        j = int(np.argmax(np.abs(qf)))
+        K = 0.01 * r.standard_normal((N, 128))
+        K[:, j] = r.permutation(N)
+        L.k_pool[pages, h, slots] = torch.tensor(K, dtype=torch.float32, device=DEV).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    links = [random_links(r, N, 100, 8) for _ in range(2)]
+    graphs = [ra.graph_build(hh, ll, N, D) for hh, ll in links]
+    got, vis = gpu_search(L, L.q[0], 0, N, graphs, ef, k)
+    for h in range(2):
+        Kb = synth.depage(L.k_pool, L.block_table, 0, N, heads=[h])[:, 0, :]
+        exact = oracle.as_f64(Kb) @ oracle.as_f64(qb[h])
+        bound = 128 * 2.0 ** -24 / (1 - 128 * 2.0 ** -24) * (
+            np.abs(oracle.as_f64(Kb)) @ np.abs(oracle.as_f64(qb[h])))
+        assert np.min(np.diff(np.sort(exact))) > 2 * bound.max()
+        nbr, entry = oracle.graph_build(links[h][0], links[h][1], N, D)
+        want, want_vis = oracle.graph_search(qb[h], Kb, nbr, entry, ef, k, batch=ra.GRAPH_BATCH,
+                                             scoring="f64")
+        assert got[h][:want.size].tolist() == want.tolist() and (got[h][want.size:] == -1).all()
+        assert vis[h] == want_vis

@@ -141,9 +141,78 @@ def _build_one_way(hubs, lists, N, D):
     return out, _REAL_BUILD(hubs, lists, N, D)[1]
 
 
-def _search_worst_first(q, K, nbr, entry, ef, k, batch=1):
+def _search_worst_first(q, K, nbr, entry, ef, k, batch=1, scoring="f32", trace=None):
     # ranks the keys upside down (the worst first)
-    return _REAL_SEARCH(np.asarray(q) ^ np.uint16(0x8000), K, nbr, entry, ef, k, batch)
+    return _REAL_SEARCH(np.asarray(q) ^ np.uint16(0x8000), K, nbr, entry, ef, k, batch,
+                        scoring, trace)
+
+
+def _search_one_per_round(q, K, nbr, entry, ef, k, batch=1, scoring="f32", trace=None):
+    # ignores the batch: one key expanded per round
+    return _REAL_SEARCH(q, K, nbr, entry, ef, k, 1, scoring, trace)
+
+
+def _score_fn(q, K, scoring):
+    if scoring == "f64":
+        return lambda pos: [float(x) for x in ro.as_f64(np.asarray(K)[np.asarray(pos)]) @ ro.as_f64(q)]
+    return lambda pos: [float(x) for x in ro.score_f32_ordered(q, K, pos)]
+
+
+def _search_merge_before_marking(q, K, nbr, entry, ef, k, batch=1, scoring="f32", trace=None):
+    # picks a round's keys one at a time, each after the previous key's new
+    # neighbours were merged into R (so a new key can join the same round)
+    if entry < 0:
+        return np.zeros(0, dtype=np.int64), 0
+    score = _score_fn(q, K, scoring)
+    visited = {int(entry)}
+    R = [(score([entry])[0], int(entry), False)]
+    while True:
+        took = 0
+        for _ in range(batch):
+            R.sort(key=lambda e: (-e[0], e[1]))
+            i = next((i for i, e in enumerate(R) if not e[2]), None)
+            if i is None:
+                break
+            took += 1
+            R[i] = (R[i][0], R[i][1], True)
+            new = [int(u) for u in nbr[R[i][1]] if u >= 0 and int(u) not in visited]
+            visited.update(new)
+            if new:
+                R.extend((x, u, False) for x, u in zip(score(new), new))
+                R.sort(key=lambda e: (-e[0], e[1]))
+                del R[ef:]
+        if not took:
+            break
+        if trace is not None:
+            trace.append(([(e[1], e[2]) for e in R], sorted(visited)))
+    return np.asarray(sorted(e[1] for e in R[:k]), dtype=np.int64), len(visited)
+
+
+def _search_resort_mid_round(q, K, nbr, entry, ef, k, batch=1, scoring="f32", trace=None):
+    # re-sorts R after each expansion while the round's remaining keys are
+    # still addressed by their positions from before
+    if entry < 0:
+        return np.zeros(0, dtype=np.int64), 0
+    score = _score_fn(q, K, scoring)
+    visited = {int(entry)}
+    R = [(score([entry])[0], int(entry), False)]
+    while True:
+        R.sort(key=lambda e: (-e[0], e[1]))
+        todo = [i for i, e in enumerate(R) if not e[2]][:batch]
+        if not todo:
+            break
+        for i in todo:
+            if i >= len(R):
+                continue
+            R[i] = (R[i][0], R[i][1], True)
+            new = [int(u) for u in nbr[R[i][1]] if u >= 0 and int(u) not in visited]
+            visited.update(new)
+            R.extend((x, u, False) for x, u in zip(score(new), new))
+            R.sort(key=lambda e: (-e[0], e[1]))
+            del R[ef:]
+        if trace is not None:
+            trace.append(([(e[1], e[2]) for e in R], sorted(visited)))
+    return np.asarray(sorted(e[1] for e in R[:k]), dtype=np.int64), len(visited)
 
 
 def _f32_reversed(q, K, positions):
@@ -154,6 +223,9 @@ def _f32_reversed(q, K, positions):
 MUTANTS = {
     "graph_build_one_way": ("graph_build", _build_one_way),
     "graph_search_worst_first": ("graph_search", _search_worst_first),
+    "graph_search_one_key_per_round": ("graph_search", _search_one_per_round),
+    "graph_search_merge_before_marking": ("graph_search", _search_merge_before_marking),
+    "graph_search_resort_mid_round": ("graph_search", _search_resort_mid_round),
     "score_f32_reversed_order": ("score_f32_ordered", _f32_reversed),
     "budgets_rising": ("layer_budgets", _budgets_rising),
     "budgets_floor_only": ("layer_budgets", _budgets_floor_only),

@@ -563,3 +563,95 @@ def test_batched_graph_search_on_a_complete_graph_and_a_chain():
         cn[chain[i + 1], 1] = chain[i]
     got, visited = oracle.graph_search(q, K, cn, int(chain[0]), ef=2, k=1, batch=2)
     assert got.tolist() == [int(chain[-1])] and visited == 300
+
+
+# A 12-key graph searched by hand (slides, frame "Prefill queries teach the
+# key graph what matters", step 4: best-first search of the key graph).
+# q = e_0 and key i = S[i] e_0, so key i scores S[i] exactly in bf16 and in
+# any summation order; entry 0, ef = 4, k = 3. Key 10 (score 10) is reached
+# only through key 5 (score 3), which no batch keeps long enough to expand.
+_HW_S = [5, 2, 9, 1, 7, 3, 11, 4, 8, 6, 10, 0]
+_HW_NBR = [[1, 2, 3], [0, 4, 5], [0, 6, 7], [0, 8], [1, 9], [1, 10], [2, 11], [2], [3], [4],
+           [5], [6]]
+T, F = True, False
+# per batch: (per round: R as (key, expanded) in rank order, visited keys),
+# the result, the number of keys visited
+_HW_TRACES = {
+    # one key per round: 0; 2 (6, 7 join, 1 and 3 drop); 6 (11 joins and
+    # drops); 7 (nothing new)
+    1: ([([(2, F), (0, T), (1, F), (3, F)], [0, 1, 2, 3]),
+         ([(6, F), (2, T), (0, T), (7, F)], [0, 1, 2, 3, 6, 7]),
+         ([(6, T), (2, T), (0, T), (7, F)], [0, 1, 2, 3, 6, 7, 11]),
+         ([(6, T), (2, T), (0, T), (7, T)], [0, 1, 2, 3, 6, 7, 11])],
+        [0, 2, 6], 7),
+    # two per round: 0; 2 and 1 (6, 7, 4, 5 join; 7 drops); 6 and 4 (11, 9
+    # join, 11 drops, 0 drops); 9 (nothing new)
+    2: ([([(2, F), (0, T), (1, F), (3, F)], [0, 1, 2, 3]),
+         ([(6, F), (2, T), (4, F), (0, T)], [0, 1, 2, 3, 4, 5, 6, 7]),
+         ([(6, T), (2, T), (4, T), (9, F)], [0, 1, 2, 3, 4, 5, 6, 7, 9, 11]),
+         ([(6, T), (2, T), (4, T), (9, T)], [0, 1, 2, 3, 4, 5, 6, 7, 9, 11])],
+        [2, 4, 6], 10),
+    # four per round: 0; 2, 1 and 3 (8 joins as well); 6, 8 and 4 (11 and 9
+    # join and drop); every key in R expanded
+    4: ([([(2, F), (0, T), (1, F), (3, F)], [0, 1, 2, 3]),
+         ([(6, F), (2, T), (8, F), (4, F)], [0, 1, 2, 3, 4, 5, 6, 7, 8]),
+         ([(6, T), (2, T), (8, T), (4, T)], [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 11])],
+        [2, 6, 8], 11),
+}
+
+
+def _hand_graph():
+    q = np.zeros(D, dtype=np.float32)
+    q[0] = 1.0
+    K = np.zeros((12, D), dtype=np.float32)
+    K[:, 0] = _HW_S
+    nbr = np.full((12, 3), -1)
+    for a, row in enumerate(_HW_NBR):
+        nbr[a, :len(row)] = row
+    return _bits(q), _bits(K), nbr
+
+
+@pytest.mark.parametrize("batch", [1, 2, 4])
+def test_graph_search_rounds_on_a_graph_worked_by_hand(batch):
+    q, K, nbr = _hand_graph()
+    rounds, result, n_visited = _HW_TRACES[batch]
+    for scoring in ("f32", "f64"):
+        trace = []
+        got, visited = oracle.graph_search(q, K, nbr, 0, ef=4, k=3, batch=batch,
+                                           scoring=scoring, trace=trace)
+        assert got.tolist() == result and visited == n_visited
+        assert len(trace) == len(rounds)
+        for (R, V), (R_want, V_want) in zip(trace, rounds):
+            assert [(int(a), bool(b)) for a, b in R] == R_want and list(V) == V_want
+
+
+def test_graph_search_in_fp32_order_equals_fp64_when_no_two_scores_are_close():
+    # scores spread far apart along q (gaps of about 0.05 |q|^2, far above
+    # the fp32 dot-product bound): the ordered fp32 sum ranks the keys as
+    # the exact dot product does, so the searches agree round by round
+    r = rng(38)
+    N = 400
+    qf = r.standard_normal(D).astype(np.float32)
+    qh = qf / np.linalg.norm(qf)
+    c = r.permutation(N) * 0.05
+    Kf = (0.01 * r.standard_normal((N, D)) + np.outer(c, qh)).astype(np.float32)
+    q, K = _bits(qf), _bits(Kf)
+    exact = oracle.as_f64(K) @ oracle.as_f64(q)
+    bound = D * 2.0 ** -24 / (1 - D * 2.0 ** -24) * (np.abs(oracle.as_f64(K)) @ np.abs(oracle.as_f64(q)))
+    s = np.sort(exact)
+    assert np.min(np.diff(s)) > 2 * bound.max()
+    nbr = np.stack([r.choice(N, 8, replace=False) for _ in range(N)])
+    for batch in (1, 16):
+        t32, t64 = [], []
+        a = oracle.graph_search(q, K, nbr, 0, ef=32, k=16, batch=batch, scoring="f32", trace=t32)
+        b = oracle.graph_search(q, K, nbr, 0, ef=32, k=16, batch=batch, scoring="f64", trace=t64)
+        assert a[0].tolist() == b[0].tolist() and a[1] == b[1] and t32 == t64
+
+
+def test_graph_search_scored_in_fp64_on_a_complete_graph_is_the_exact_top_k():
+    q, K = _random_keys(39, 80)
+    nbr = np.array([[b for b in range(80) if b != a] for a in range(80)])
+    s = oracle.as_f64(K) @ oracle.as_f64(q)
+    order = np.lexsort((np.arange(80), -s))
+    got, visited = oracle.graph_search(q, K, nbr, 3, ef=80, k=9, batch=16, scoring="f64")
+    assert visited == 80 and got.tolist() == sorted(order[:9].tolist())
