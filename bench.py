@@ -8,12 +8,17 @@ inputs (OOD queries vs keys, 64 planted needles per query head, x4 sink
 keys). Inputs are resident in HBM before timing starts.
 
 One step = every kernel of ra_decode_step (sample, threshold, scan, select,
-gather, merge). In the timed region every SCAN_EVERY-th step is launched as
-three ra_decode_stages calls with HIP events around the scan stage only, so
-the scan kernel's own duration is measured live on the stream it runs on;
-the other steps are single ra_decode_step calls. A separate, untimed pass
-with events between all stages gives the per-stage breakdown. Prints ONE
-JSON line.
+gather, merge). In the timed region a few steps (one in max(10, K/4)) are
+launched as three ra_decode_stages calls with HIP events around the scan
+stage only, so the scan kernel's own duration is measured live on the
+stream it runs on; the other steps are single calls. An event between two
+kernels costs about 3 us of GPU time, so 20 more event-timed scans follow
+right after the timed region instead of perturbing it. Separate untimed
+passes give the per-step latency percentiles (an event at every step
+boundary), the per-stage breakdown (events between all stages) and a plain
+device copy's bandwidth. The cpu_baseline leg times the fp64 oracle on
+a bounded sample and compares the benchmark's own outputs with it (the
+parity fields). Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload C3_1] [--gpus 1]
 """
@@ -32,7 +37,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-step latency (ms) + KV GB/s vs HBM peak, Llama-3-8B layer @128K/1M"
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E peak
-SCAN_EVERY = 8  # timed-loop steps between the event-timed scan launches
+SCAN_SAMPLES = 20  # event-timed scan launches right after the timed region
+IN_REGION_EVERY = 10  # timed-region steps per event-timed scan, at least
+SCAN_LAYER_EVERY = 8  # C5: layers of an event-timed token step whose scan is timed
+PCT_STEPS = 50  # steps of the per-step latency pass
 # the scan kernel's sources: a committed counter profile is used only while
 # their hash matches the one recorded with it
 SCAN_SRCS = [os.path.join(ROOT, "top_sparse_attention_gqa_amd", "csrc", f)
@@ -140,46 +148,164 @@ def traffic_from_profile(workload, name="score_scan", srcs=None):
         return None
 
 
-def cpu_baseline(c, L, lens, ks, budget_s=12.0):
-    """Time the fp64 oracle (as it stands) on a bounded sample of the same
-    workload and scale it to ms per full decode step."""
+def host_cpu():
+    """The host CPU's model name (from /proc/cpuinfo) and the threads this
+    process may use."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        return len(os.sched_getaffinity(0))
+
+
+def copy_bandwidth(dev, mib=1024, reps=5):
+    """GB/s of a plain device-to-device copy of `mib` MiB (bytes read plus
+    bytes written over the time), timed with events; the best of `reps`."""
+    import torch
+
+    a = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3
+        best = t if best is None else min(best, t)
+    del a, b
+    return 2.0 * (mib << 20) / best / 1e9
+
+
+def check_group(res, gpu_out, gpu_lse, gpu_idx, q_g, K_g, k):
+    """Compare one KV group's GPU results with the oracle's (the stated
+    tolerances: indices equal outside the 1e-3 relative band around the
+    k-th score, plus the fp32 dot-product floor; out and lse within
+    2e-3 + 1e-2 |ref|). Returns (band differences, index failures, largest
+    out error, out/lse failures)."""
     import numpy as np
 
     import oracle
-    import synth
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = len(os.sched_getaffinity(0))
-    G = c.H_q // c.H_kv
-    b = 0
-    n = lens[b]
-    q_all = synth.bf16_bits(L.q[b])
-    spent = 0.0
-    groups = 0
-    for g in range(c.H_kv):
-        K = synth.depage(L.k_pool, L.block_table, b, n, heads=[g])
-        V = synth.depage(L.v_pool, L.block_table, b, n, heads=[g])
+    G = q_g.shape[0]
+    qa = np.abs(oracle.as_f64(q_g))
+    Ka = np.abs(oracle.as_f64(K_g[:, 0, :]))
+    u = 2.0 ** -24
+    eps = 130 * u / (1 - 130 * u) * (qa @ Ka.T).max(axis=1) / np.sqrt(128.0)
+    band_diffs = idx_fail = out_fail = 0
+    err_max = 0.0
+    M = res["M"]
+    k_eff = min(k, M.size)
+    for h in range(G):
+        ref = res["idx"][h]
+        sel = gpu_idx[h][:k_eff]
+        ok = (np.all(gpu_idx[h][k_eff:] == -1) and np.all(np.diff(sel) > 0)
+              and np.all(np.isin(sel, M)))
+        if ok and not np.array_equal(sel, ref):
+            z = res["z"][h]
+            zk = z[ref].min()
+            band = np.abs(z - zk) <= 1e-3 * abs(zk) + eps[h]
+            ok = np.array_equal(sel[~band[sel]], ref[~band[ref]])
+            band_diffs += int(np.setdiff1d(sel, ref).size)
+        idx_fail += 0 if ok else 1
+        err = np.abs(gpu_out[h] - res["out"][h])
+        err_max = max(err_max, float(err.max()))
+        bad = np.any(err > 2e-3 + 1e-2 * np.abs(res["out"][h]))
+        bad = bad or abs(gpu_lse[h] - res["lse"][h]) > 2e-3 + 1e-2 * abs(res["lse"][h])
+        out_fail += 1 if bad else 0
+    return band_diffs, idx_fail, err_max, out_fail
+
+
+def oracle_groups(samples, budget_s):
+    """Time the fp64 oracle (as it stands) on (q_g, K, V, k, n_sink, window,
+    gpu) samples of one KV group each, until the budget is spent (at least
+    one); compare each with the GPU results it carries. Returns (seconds
+    spent, groups done, parity dict)."""
+    import numpy as np
+
+    import oracle
+
+    spent, done = 0.0, 0
+    band = idx_fail = out_fail = heads = 0
+    err_max = 0.0
+    for make in samples:
+        q_g, K, V, k, n_sink, window, gpu = make()
         t = time.perf_counter()
-        oracle.decode(q_all[g * G:(g + 1) * G], K, V, ks[b], c.n_sink, c.window)
+        res = oracle.decode(q_g, K, V, k, n_sink, window)
         spent += time.perf_counter() - t
-        groups += 1
-        del K, V
+        done += 1
+        if gpu is not None:
+            b_, i_, e_, o_ = check_group(res, *gpu, q_g, K, k)
+            band, idx_fail, out_fail = band + b_, idx_fail + i_, out_fail + o_
+            err_max = max(err_max, e_)
+            heads += q_g.shape[0]
+        del K, V, res
         if spent >= budget_s:
             break
-    per_seq_groups = c.H_kv * len(lens)
-    scale = per_seq_groups / groups * (np.mean(lens) / n)
+    parity = {"heads_checked": heads, "index_failures": idx_fail,
+              "band_differences": band, "out_lse_failures": out_fail,
+              "out_max_abs_err": float(f"{err_max:.3e}"),
+              "tolerance": "indices equal outside |z - z_k| <= 1e-3 |z_k| + fp32 dot bound; "
+                           "out, lse within 2e-3 + 1e-2 |ref|",
+              "pass": heads > 0 and idx_fail == 0 and out_fail == 0}
+    return spent, done, parity
+
+
+def cpu_baseline(c, L, lens, ks, gpu=None, budget_s=12.0):
+    """Time the fp64 oracle (as it stands) on whole KV groups of the same
+    workload, sequence by sequence, until about budget_s of CPU time, scale
+    it to ms per full decode step, and compare the benchmark's own outputs
+    on those groups (gpu = host (out, lse, idx) of this layer copy)."""
+    import numpy as np
+
+    import synth
+
+    G = c.H_q // c.H_kv
+    model, _ = host_cpu()
+
+    def sample(b, g):
+        def make():
+            n = lens[b]
+            q_g = synth.bf16_bits(L.q[b])[g * G:(g + 1) * G]
+            K = synth.depage(L.k_pool, L.block_table, b, n, heads=[g])
+            V = synth.depage(L.v_pool, L.block_table, b, n, heads=[g])
+            gg = None
+            if gpu is not None:
+                o, l, i = gpu
+                gg = (o[b, g * G:(g + 1) * G], l[b, g * G:(g + 1) * G], i[b, g * G:(g + 1) * G])
+            return q_g, K, V, ks[b], c.n_sink, c.window, gg
+        return make
+
+    samples = [sample(b, g) for b in range(len(lens)) for g in range(c.H_kv)]
+    spent, groups, parity = oracle_groups(samples, budget_s)
+    tok = sum(lens[b] for b in range(len(lens)) for g in range(c.H_kv)
+              if b * c.H_kv + g < groups)
+    scale = sum(lens) * c.H_kv / tok
     return {
-        "value": round(spent / groups * per_seq_groups * (np.mean(lens) / n) * 1e3, 3),
+        "value": round(spent * scale * 1e3, 3),
         "unit": "ms",
-        "cores": int(threads),
+        "cores": int(blas_threads()),
         "kind": "oracle",
+        "cpu_model": model,
         "sample": (f"fp64 oracle (scores, exact top-k, sparse attention) on {groups} of "
-                   f"{c.H_kv} KV groups ({groups * G} query heads) of sequence 0 "
-                   f"(N={n}), {spent:.1f} s of CPU time, scaled x{scale:.2f} to one "
-                   f"full decode step"),
+                   f"{len(lens) * c.H_kv} (sequence, KV head) groups ({groups * G} query heads, "
+                   f"{tok} cached tokens), {spent:.1f} s of CPU time, scaled x{scale:.2f} by "
+                   f"cached tokens to one full decode step"),
+        "parity": parity,
     }
 
 
@@ -243,13 +369,12 @@ def run_layer(args):
         if ev is None:
             ra.decode_step_ex(*a)
             return
-        ev[0].record()
+        # the same kernels in three calls, with events around the scan only
         ra.decode_stages(*a, 0, S - 1)
-        ev[1].record()
+        ev[0].record()
         ra.decode_stages(*a, S, S)
-        ev[2].record()
+        ev[1].record()
         ra.decode_stages(*a, S + 1, n_stage - 1)
-        ev[3].record()
 
     def step_staged(i, ev):
         L = layers[i % len(layers)]
@@ -264,11 +389,14 @@ def run_layer(args):
         step(i)
     torch.cuda.synchronize()
 
-    # The scan's launches are timed by events on every SCAN_EVERY-th step
-    # (those steps are split in three calls around the scan); the other
-    # steps are one call each, so the events barely perturb the loop.
-    events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-              for i in range(0, args.steps, SCAN_EVERY)}
+    # The scan's launches are timed by events in the timed region on a few
+    # steps (every IN_REGION_EVERY-th, those split in three calls around the
+    # scan; the others are one call each): an event between two kernels
+    # costs about 3 us of GPU time, so events on every step would move the
+    # headline. SCAN_SAMPLES more event-timed scans follow right after it.
+    every = max(IN_REGION_EVERY, args.steps // 4)
+    events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+              for i in range(0, args.steps, every)}
     loop_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -278,9 +406,23 @@ def run_layer(args):
     loop_ev[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    scan_ms = np.array([e[1].elapsed_time(e[2]) for e in events.values()])
     gpu_ms_per_step = loop_ev[0].elapsed_time(loop_ev[1]) / args.steps
     ms_per_step = wall * 1e3 / args.steps
+    after = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(SCAN_SAMPLES)]
+    for i in range(SCAN_SAMPLES):
+        step(i, after[i])
+    torch.cuda.synchronize()
+    scan_in = [e[0].elapsed_time(e[1]) for e in events.values()]
+    scan_ms = np.array(scan_in + [e[0].elapsed_time(e[1]) for e in after])
+
+    # per-step latency percentiles: an event at every step boundary
+    pev = [torch.cuda.Event(enable_timing=True) for _ in range(PCT_STEPS + 1)]
+    pev[0].record()
+    for i in range(PCT_STEPS):
+        step(i)
+        pev[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([pev[i].elapsed_time(pev[i + 1]) for i in range(PCT_STEPS)])
 
     # per-stage breakdown (untimed for the headline figure)
     n_break = min(args.steps, 50)
@@ -292,15 +434,19 @@ def run_layer(args):
 
     names = list(ra.STAGE_NAMES)
 
-    # algorithmic bytes from the retrieved sets of copy 0
+    # algorithmic bytes from the retrieved sets of copy 0; its outputs are
+    # what the cpu_baseline leg compares with the oracle
     step(0)
     torch.cuda.synchronize()
-    kb, vb, small = algorithmic_bytes(c, lens, ks, idx.cpu().numpy(), c.n_sink, c.window)
+    gpu0 = (out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+            idx.cpu().numpy())
+    kb, vb, small = algorithmic_bytes(c, lens, ks, gpu0[2], c.n_sink, c.window)
     step_bytes = kb + vb + small
     scan_bytes = kb + B * H_q * 256
     scan_s = float(scan_ms.mean()) * 1e-3
     achieved = scan_bytes / scan_s / 1e9
     traffic = traffic_from_profile(args.workload)
+    copy_gbps = copy_bandwidth(dev)
 
     if args.copy_calib_mib:
         a = torch.empty(args.copy_calib_mib << 20, dtype=torch.uint8, device=dev)
@@ -311,8 +457,10 @@ def run_layer(args):
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(c, layers[0], lens, ks)
+        cpu = cpu_baseline(c, layers[0], lens, ks, gpu=gpu0)
 
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    pct = {f"p{q}": round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)}
     line = {
         "metric": METRIC,
         "value": round(ms_per_step, 4),
@@ -332,9 +480,12 @@ def run_layer(args):
                    "window": c.window, "kv_copies_rotated": len(layers),
                    "accumulate": "fp32"},
         "kv_tokens_per_s": round(sum(lens) / (ms_per_step * 1e-3), 1),
-        "step_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_gbps": round(step_gbps, 1),
+        "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "copy_gbps": round(copy_gbps, 1),
+        "step_frac_of_copy": round(step_gbps / copy_gbps, 4),
         "gpu_ms_per_step": round(gpu_ms_per_step, 4),
+        "step_ms_percentiles": dict(pct, steps=PCT_STEPS),
         "algorithmic_bytes": {"K": kb, "V": vb, "q_out_idx": small, "step": step_bytes},
         "stages_us": {n: round(float(stage_ms[:, i].mean()) * 1e3, 2) for i, n in enumerate(names)},
         "roofline": {"kernel": "scan_kernel (score scan + candidate staging)",
@@ -343,7 +494,10 @@ def run_layer(args):
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else int(round(traffic)),
                      "algorithmic_bytes_per_launch": scan_bytes,
-                     "avg_launch_us": round(scan_s * 1e6, 2)},
+                     "avg_launch_us": round(scan_s * 1e6, 2),
+                     "launches_timed": {"in_timed_region": len(scan_in),
+                                        "right_after_it": SCAN_SAMPLES}},
+        "parity": None if cpu is None else cpu.pop("parity"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -387,13 +541,23 @@ def run_model(args):
     kvs = [ra.KVLayer(L.k_pool, L.v_pool, L.block_table) for L in layers]
     n_stage = ra._lib.STAGE_COUNT
     S = ra.STAGE_SCAN
+    # the oracle's sample: these layers at the first and the last token step
+    sampled = [l for l in (0, n_layers // 2 - 1, n_layers - 1) if l < n_layers]
+    kept = {}
+
+    def keep(s):
+        torch.cuda.synchronize()
+        for l in sampled:
+            kept[(s, l)] = (outs[l][0].cpu().numpy().astype(np.float64),
+                            lses[l][0].cpu().numpy().astype(np.float64),
+                            idxs[l][0].cpu().numpy())
 
     def token_step(s, ev=None):
         for l in range(n_layers):
             q, kn, vn = streams[l][0][s], streams[l][1][s], streams[l][2][s]
             a = (q, kvs[l], seq_all[s], max_seq_len, k_all[s, l], k_max, c.n_sink, c.window,
                  outs[l], lses[l], idxs[l], ws)
-            if ev is None:
+            if ev is None or l % SCAN_LAYER_EVERY:
                 # the append is written inside the step (one launch fewer)
                 ra.append_decode_step(kn, vn, pos_all[s], *a)
             else:
@@ -406,18 +570,27 @@ def run_model(args):
 
     for s in range(args.warmup):
         token_step(s)
+        if s == 0:
+            keep(0)
     torch.cuda.synchronize()
-    every = max(1, args.steps // 20)                   # scan events on 20 of the steps
+    every = max(1, args.steps // SCAN_SAMPLES)         # scan events on 20 of the steps
     ev = {s: [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_layers)]
           for s in range(0, args.steps, every)}
+    bnd = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
+    bnd[0].record()
     for i in range(args.steps):
         token_step(args.warmup + i, ev.get(i))
+        bnd[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     scan_ms = np.array([e[2 * l].elapsed_time(e[2 * l + 1]) for e in ev.values()
-                        for l in range(n_layers)])
+                        for l in range(0, n_layers, SCAN_LAYER_EVERY)])
+    per_step = np.array([bnd[i].elapsed_time(bnd[i + 1]) for i in range(args.steps)])
+    if args.warmup == 0:
+        keep(0)
+    keep(total - 1)
 
     # algorithmic bytes of the last token step, from each layer's retrieved sets
     n_last = lens[-1]
@@ -431,14 +604,14 @@ def run_model(args):
     scan_bytes = int(n_mean * H_kv * 256 + H_q * 256)
     scan_s = float(scan_ms.mean()) * 1e-3
     achieved = scan_bytes / scan_s / 1e9
+    copy_gbps = copy_bandwidth(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
-        one = cpu_baseline(c, layers[0], [N0], [c.k_for(N0)])
-        one["value"] = round(one["value"] * n_layers, 3)
-        one["sample"] += f"; times {n_layers} layers for one token step"
-        cpu = one
+        cpu = model_cpu_baseline(c, layers, streams, lens, k_tab, sampled, kept, total)
 
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    pct = {f"p{q}": round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)}
     line = {
         "metric": METRIC,
         "value": round(ms_per_step, 4),
@@ -459,8 +632,11 @@ def run_model(args):
                    "n_sink": c.n_sink, "window": c.window, "accumulate": "fp32",
                    "kv_bytes_resident": int(sum(L.k_pool.numel() * 4 for L in layers))},
         "kv_tokens_per_s": round(n_layers * n_mean / (ms_per_step * 1e-3), 1),
-        "step_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_gbps": round(step_gbps, 1),
+        "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "copy_gbps": round(copy_gbps, 1),
+        "step_frac_of_copy": round(step_gbps / copy_gbps, 4),
+        "step_ms_percentiles": dict(pct, steps=args.steps),
         "algorithmic_bytes": {"K": kb, "V": vb, "q_out_idx_append": small, "step": step_bytes},
         "roofline": {"kernel": "scan_kernel (score scan + candidate staging)",
                      "bound": "hbm", "achieved": round(achieved, 1),
@@ -468,10 +644,52 @@ def run_model(args):
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None,
                      "algorithmic_bytes_per_launch": scan_bytes,
-                     "avg_launch_us": round(scan_s * 1e6, 2)},
+                     "avg_launch_us": round(scan_s * 1e6, 2),
+                     "launches_timed": int(scan_ms.size)},
+        "parity": None if cpu is None else cpu.pop("parity"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def model_cpu_baseline(c, layers, streams, lens, k_tab, sampled, kept, total):
+    """The fp64 oracle on every KV group of the sampled layers at the first
+    and the last token step (the state each was decoded in: the first
+    lens[s] rows of the layer's pool, the step's query), scaled to a token
+    step of all layers; the GPU outputs kept at those steps are compared."""
+    import synth
+
+    G = c.H_q // c.H_kv
+    model, _ = host_cpu()
+    steps = sorted({0, total - 1})
+
+    def sample(s, l, g):
+        def make():
+            L = layers[l]
+            n = lens[s]
+            q_g = synth.bf16_bits(streams[l][0][s][0])[g * G:(g + 1) * G]
+            K = synth.depage(L.k_pool, L.block_table, 0, n, heads=[g])
+            V = synth.depage(L.v_pool, L.block_table, 0, n, heads=[g])
+            o, lse, i = kept[(s, l)]
+            sl = slice(g * G, (g + 1) * G)
+            return q_g, K, V, k_tab[s][l], c.n_sink, c.window, (o[sl], lse[sl], i[sl])
+        return make
+
+    samples = [sample(s, l, g) for s in steps for l in sampled for g in range(c.H_kv)]
+    spent, groups, parity = oracle_groups(samples, budget_s=1e9)
+    per_step = spent / len(steps) * c.n_layers / len(sampled)
+    return {
+        "value": round(per_step * 1e3, 3),
+        "unit": "ms",
+        "cores": int(blas_threads()),
+        "kind": "oracle",
+        "cpu_model": model,
+        "sample": (f"fp64 oracle on layers {sampled} of {c.n_layers} (all {c.H_kv} KV groups "
+                   f"each) at token steps {steps} (lengths {[lens[s] for s in steps]}), "
+                   f"{spent:.1f} s of CPU time, per token step x{c.n_layers}/{len(sampled)} "
+                   f"for all layers"),
+        "parity": parity,
+    }
 
 
 

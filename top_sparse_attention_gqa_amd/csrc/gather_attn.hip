@@ -431,8 +431,9 @@ void gather_kernel(Params p) {
 // ---------------------------------------------------------------- merge
 // One block per (sequence, query head): 8 groups of 32 threads each take
 // every 8th partial, 4 dims per thread (float4 loads issued kMergeDepth
-// deep, so up to 128 tiles take one round trip), then the groups are summed
-// in LDS in a fixed order.
+// deep, so up to 128 tiles take one round trip, together with the head
+// state that gives the partials' common reference), then the groups are
+// summed in LDS in a fixed order.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeGroups = kMergeThreads / 32;
 constexpr int kMergeDepth = 16;
@@ -440,24 +441,32 @@ constexpr int kMergeUnroll = 4;  // positions per thread in flight in the copy
 constexpr int kMergeTiles = 8;   // tiles per out_idx copy block
 
 // out_idx for tiles [c * kMergeTiles, (c + 1) * kMergeTiles) of head bh.
+// Every count the block needs is loaded in one round: thread t holds tile
+// t's count, the tiles before ta are summed, the block's own go to LDS.
 __device__ void copy_positions(const Params& p, int bh, int c, int nt) {
   const int tid = threadIdx.x;
   const int ta = c * kMergeTiles;
   if (ta >= nt) return;
   const int tb = min(nt, ta + kMergeTiles);
   __shared__ uint32_t s_pre[kMergeTiles + 1];
+  __shared__ uint32_t s_own[kMergeTiles];
   __shared__ uint32_t s_part[kMergeThreads / 64];
   const uint32_t* sc = p.scnt + size_t(bh) * p.n_tiles;
   // offset: retrieved positions of the tiles before ta
   uint32_t before = 0;
-  for (int t = tid; t < ta; t += kMergeThreads) before += sc[t];
+  for (int t = tid; t < tb; t += kMergeThreads) {
+    const uint32_t v = sc[t];
+    if (t < ta) before += v;
+    else s_own[t - ta] = v;
+  }
   before = wave_sum(before);
   if ((tid & 63) == 0) s_part[tid >> 6] = before;
+  __syncthreads();
   if (tid == 0) {
     uint32_t run = 0;
     for (int t = ta; t < tb; ++t) {
       s_pre[t - ta] = run;
-      run += sc[t];
+      run += s_own[t - ta];
     }
     s_pre[tb - ta] = run;
   }
@@ -503,25 +512,17 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p) {
   const float* mz = p.part_mz + size_t(bh) * p.n_tiles * 2;
   const float* pn = p.part_n + size_t(bh) * p.n_tiles * kHeadDim + d0;
   __shared__ float s_red[kMergeGroups][kHeadDim + 4];
-  __shared__ float s_m[kMergeThreads / 64];
   const int np = nt;
   auto slot = [](int j) { return j; };
 
-  // m = max over the non-empty partials
-  float m = -INFINITY;
-  for (int j = tid; j < np; j += kMergeThreads) {
-    const int t = slot(j);
-    m = fmaxf(m, mz[2 * t + 1] > 0.0f ? mz[2 * t] : -INFINITY);
-  }
-  m = wave_max(m);
-  if ((tid & 63) == 0) s_m[tid >> 6] = m;
-  __syncthreads();
-  m = s_m[0];
-  for (int w = 1; w < kMergeThreads / 64; ++w) m = fmaxf(m, s_m[w]);
+  // m: every non-empty partial of the head was taken relative to the same
+  // reference, the head's largest score over W u Omega, which the head
+  // state gives; the state is loaded with the partials, in one round
+  const float m = softmax_ref(p.state[bh], sg.k_eff);
 
   float Z = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (m > -INFINITY) {
+  {
     for (int j0 = grp; j0 < np; j0 += kMergeGroups * kMergeDepth) {
       float2 w2[kMergeDepth];
       float4 v[kMergeDepth];
@@ -535,6 +536,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p) {
       }
 #pragma unroll
       for (int u = 0; u < kMergeDepth; ++u) {
+        // e^{m_t - m}: 1 for every non-empty partial here, kept general
         const float sc = w2[u].y > 0.0f ? expf(w2[u].x - m) : 0.0f;
         Z += sc * w2[u].y;
         acc.x += sc * v[u].x;
