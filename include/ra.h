@@ -254,6 +254,9 @@ size_t ra_workspace_scores_offset(int32_t B, int32_t H_q, int32_t H_kv,
  * capacities (byte offset, 4-byte aligned): after RA_STAGE_SELECT of a call
  * it holds the number of query heads whose candidates fell short of k_eff,
  * which that stage then decided by the full rescan (0 in the common case). A diagnostic; the caller reads it from device memory itself.
+ * In a library built with -DRA_DEBUG (libra_debug.so), the next uint32
+ * holds the bounds checks of the decode kernels that failed in the call,
+ * one bit per check site (their accesses were skipped); 0 when all held.
  * Returns (size_t)-1 if the arguments are invalid.
  */
 size_t ra_workspace_rescan_count_offset(int32_t B, int32_t H_q, int32_t H_kv,

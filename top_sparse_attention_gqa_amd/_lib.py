@@ -12,6 +12,7 @@ Arguments given as raw integer addresses are passed through unchecked.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from ctypes import POINTER, c_int, c_int32, c_int64, c_size_t, c_uint32, c_void_p, c_char_p
@@ -65,62 +66,88 @@ class KVLayerStruct(ctypes.Structure):
                 ("head_dim", c_int32), ("page_size", c_int32)]
 
 
-_lib.ra_abi_version.restype = c_int
-_lib.ra_abi_version.argtypes = []
-_lib.ra_status_str.restype = c_char_p
-_lib.ra_status_str.argtypes = [c_int]
-_lib.ra_decode_workspace_bytes.restype = c_size_t
-_lib.ra_decode_workspace_bytes.argtypes = [c_int32] * 5
-_lib.ra_workspace_scores_offset.restype = c_size_t
-_lib.ra_workspace_scores_offset.argtypes = [c_int32] * 5 + [POINTER(c_int64)]
-_lib.ra_prefill_workspace_bytes.restype = c_size_t
-_lib.ra_prefill_workspace_bytes.argtypes = [c_int32] * 4
-_lib.ra_prefill_workspace_fail_offset.restype = c_size_t
-_lib.ra_prefill_workspace_fail_offset.argtypes = [c_int32] * 4
-_lib.ra_prefill_topk.restype = c_int
-_lib.ra_prefill_topk.argtypes = [c_void_p, c_int32, c_int32, POINTER(KVLayerStruct), c_int32,
-                                 c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
-                                 c_size_t, c_void_p]
-_lib.ra_graph_build.restype = c_int
-_lib.ra_graph_build.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
-                                c_void_p, c_void_p]
-_lib.ra_graph_search.restype = c_int
-_lib.ra_graph_search.argtypes = [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p,
-                                 c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
-                                 c_void_p]
-_lib.ra_sparse_attend.restype = c_int
-_lib.ra_sparse_attend.argtypes = [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_int32,
-                                  c_void_p, c_void_p, c_void_p]
-_lib.ra_merge_partials.restype = c_int
-_lib.ra_merge_partials.argtypes = [c_void_p] * 4 + [c_int32, c_void_p, c_void_p, c_void_p]
-_lib.ra_host_device_pointer.restype = c_int
-_lib.ra_host_device_pointer.argtypes = [c_void_p, POINTER(c_void_p)]
-_lib.ra_layer_budgets.restype = c_int
-_lib.ra_layer_budgets.argtypes = [c_int32, c_int32, c_int32, c_void_p]
-_lib.ra_prefill_stages.restype = c_int
-_lib.ra_prefill_stages.argtypes = _lib.ra_prefill_topk.argtypes[:-1] + [c_int32, c_int32, c_void_p]
-_lib.ra_workspace_rescan_count_offset.restype = c_size_t
-_lib.ra_workspace_rescan_count_offset.argtypes = [c_int32] * 5
-_lib.ra_kv_append.restype = c_int
-_lib.ra_kv_append.argtypes = [POINTER(KVLayerStruct), c_void_p, c_void_p, c_void_p, c_int32, c_void_p]
 _DECODE_ARGS = [c_void_p, c_int32, POINTER(KVLayerStruct), c_void_p, c_int32, c_int32,
                 c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                 c_void_p, c_size_t]
-_lib.ra_decode_step.restype = c_int
-_lib.ra_decode_step.argtypes = [c_void_p, c_int32, POINTER(KVLayerStruct), c_void_p, c_int32,
-                                c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
-                                c_void_p, c_void_p, c_size_t, c_void_p]
-_lib.ra_decode_step_ex.restype = c_int
-_lib.ra_decode_step_ex.argtypes = _DECODE_ARGS + [c_uint32, c_void_p]
-_lib.ra_decode_stages.restype = c_int
-_lib.ra_decode_stages.argtypes = _DECODE_ARGS + [c_uint32, c_int32, c_int32, c_void_p]
-_lib.ra_decode_step_noalloc.restype = c_int
-_lib.ra_decode_step_noalloc.argtypes = [c_void_p, c_int32, POINTER(KVLayerStruct), c_void_p, c_int32,
-                                        c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
-                                        c_void_p, c_void_p, c_uint32, c_void_p]
 NOALLOC_WS_BYTES = 64 << 20
-_lib.ra_append_decode_step.restype = c_int
-_lib.ra_append_decode_step.argtypes = [c_void_p, c_void_p, c_void_p] + _DECODE_ARGS + [c_uint32, c_void_p]
+
+
+def _declare(lib):
+    """Set the ctypes signatures of every entry point of a loaded build."""
+    lib.ra_abi_version.restype = c_int
+    lib.ra_abi_version.argtypes = []
+    lib.ra_status_str.restype = c_char_p
+    lib.ra_status_str.argtypes = [c_int]
+    lib.ra_decode_workspace_bytes.restype = c_size_t
+    lib.ra_decode_workspace_bytes.argtypes = [c_int32] * 5
+    lib.ra_workspace_scores_offset.restype = c_size_t
+    lib.ra_workspace_scores_offset.argtypes = [c_int32] * 5 + [POINTER(c_int64)]
+    lib.ra_prefill_workspace_bytes.restype = c_size_t
+    lib.ra_prefill_workspace_bytes.argtypes = [c_int32] * 4
+    lib.ra_prefill_workspace_fail_offset.restype = c_size_t
+    lib.ra_prefill_workspace_fail_offset.argtypes = [c_int32] * 4
+    lib.ra_prefill_topk.restype = c_int
+    lib.ra_prefill_topk.argtypes = [c_void_p, c_int32, c_int32, POINTER(KVLayerStruct), c_int32,
+                                    c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                    c_size_t, c_void_p]
+    lib.ra_graph_build.restype = c_int
+    lib.ra_graph_build.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                   c_void_p, c_void_p]
+    lib.ra_graph_search.restype = c_int
+    lib.ra_graph_search.argtypes = [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p,
+                                    c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                    c_void_p]
+    lib.ra_sparse_attend.restype = c_int
+    lib.ra_sparse_attend.argtypes = [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_int32,
+                                     c_void_p, c_void_p, c_void_p]
+    lib.ra_merge_partials.restype = c_int
+    lib.ra_merge_partials.argtypes = [c_void_p] * 4 + [c_int32, c_void_p, c_void_p, c_void_p]
+    lib.ra_host_device_pointer.restype = c_int
+    lib.ra_host_device_pointer.argtypes = [c_void_p, POINTER(c_void_p)]
+    lib.ra_layer_budgets.restype = c_int
+    lib.ra_layer_budgets.argtypes = [c_int32, c_int32, c_int32, c_void_p]
+    lib.ra_prefill_stages.restype = c_int
+    lib.ra_prefill_stages.argtypes = lib.ra_prefill_topk.argtypes[:-1] + [c_int32, c_int32, c_void_p]
+    lib.ra_workspace_rescan_count_offset.restype = c_size_t
+    lib.ra_workspace_rescan_count_offset.argtypes = [c_int32] * 5
+    lib.ra_kv_append.restype = c_int
+    lib.ra_kv_append.argtypes = [POINTER(KVLayerStruct), c_void_p, c_void_p, c_void_p, c_int32, c_void_p]
+    lib.ra_decode_step.restype = c_int
+    lib.ra_decode_step.argtypes = [c_void_p, c_int32, POINTER(KVLayerStruct), c_void_p, c_int32,
+                                   c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                   c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.ra_decode_step_ex.restype = c_int
+    lib.ra_decode_step_ex.argtypes = _DECODE_ARGS + [c_uint32, c_void_p]
+    lib.ra_decode_stages.restype = c_int
+    lib.ra_decode_stages.argtypes = _DECODE_ARGS + [c_uint32, c_int32, c_int32, c_void_p]
+    lib.ra_decode_step_noalloc.restype = c_int
+    lib.ra_decode_step_noalloc.argtypes = [c_void_p, c_int32, POINTER(KVLayerStruct), c_void_p, c_int32,
+                                           c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                           c_void_p, c_void_p, c_uint32, c_void_p]
+    lib.ra_append_decode_step.restype = c_int
+    lib.ra_append_decode_step.argtypes = [c_void_p, c_void_p, c_void_p] + _DECODE_ARGS + [c_uint32, c_void_p]
+    return lib
+
+
+_declare(_lib)
+
+
+def load_build(path: str):
+    """Load another build of the library (libra_debug.so, say) with the same
+    signatures; with_build() routes the binding's calls through it."""
+    return _declare(ctypes.CDLL(path))
+
+
+@contextlib.contextmanager
+def with_build(lib):
+    """Within the block, every call of this binding goes to lib (a handle
+    from load_build); the default build is restored on exit."""
+    global _lib
+    saved, _lib = _lib, lib
+    try:
+        yield lib
+    finally:
+        _lib = saved
 
 
 class RAError(RuntimeError):

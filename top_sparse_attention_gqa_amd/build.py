@@ -1,11 +1,14 @@
-"""Build the HIP library libra.so in-tree for gfx950 with hipcc.
+"""Build the HIP library libra.so in-tree for gfx950 with hipcc, and its
+debug build libra_debug.so (-DRA_DEBUG: bounds checks at the decode
+kernels' computed global accesses, reported in the workspace, never a trap).
 
     python top_sparse_attention_gqa_amd/build.py
 
 Run as a script (not with -m): the package itself loads the library.
 
 Always recompiles. Objects go to ``_build/`` (git-ignored); the shared
-library lands next to this file, where the binding loads it.
+libraries land next to this file, where the binding (and the debug-build
+test) load them.
 """
 
 from __future__ import annotations
@@ -21,6 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libra.so")
+LIB_DEBUG = os.path.join(PKG, "libra_debug.so")
 
 SOURCES = ["ra_api.cpp", "kv_append.hip", "score_scan.hip", "topk_select.hip",
            "gather_attn.hip", "prefill_topk.hip", "graph_search.hip", "sparse_attend.hip"]
@@ -33,29 +37,38 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, debug: bool = False) -> str:
     path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD, src + ".o")
+    obj = os.path.join(BUILD, "debug" if debug else "", src + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *lang, "-c", path, "-o", obj]
+    extra = ["-DRA_DEBUG"] if debug else []
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *extra, *lang, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Compile libra.so (and, with debug=True, libra_debug.so)."""
+    os.makedirs(os.path.join(BUILD, "debug"), exist_ok=True)
+    jobs = [(src, False) for src in SOURCES] + ([(src, True) for src in SOURCES] if debug else [])
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    _link(objs[:len(SOURCES)], LIB)
+    if debug:
+        _link(objs[len(SOURCES):], LIB_DEBUG)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB}" + (f" and {LIB_DEBUG}" if debug else ""))
     return LIB
 
 

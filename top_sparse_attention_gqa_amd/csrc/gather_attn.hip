@@ -185,7 +185,8 @@ void gather_kernel(Params p) {
     const int e = u * kGathThreads + tid;
     const int j = e / kSpec, i = e - j * kSpec;
     const int unit = kUnitsPerTile * tile + j % kUnitsPerTile;
-    spec[u] = (j < kLists && unit < units_seq)
+    spec[u] = (j < kLists && unit < units_seq &&
+               RA_IN(size_t(unit) * kUnit + i < size_t(p.n_cap), p, 5))
                   ? p.cand[(bh0 + j / kUnitsPerTile) * p.n_cap + size_t(unit) * kUnit + i]
                   : 0ull;
   }
@@ -228,7 +229,7 @@ void gather_kernel(Params p) {
     const int off = int(n) - t0;
     atomicOr(reinterpret_cast<unsigned long long*>(&bm[hh][off >> 6]), 1ull << (off & 63));
     const float z = key2f(key);
-    if (store) p.scores[(bh0 + hh) * p.n_cap + n] = z;
+    if (store && RA_IN(n < uint32_t(p.n_cap), p, 7)) p.scores[(bh0 + hh) * p.n_cap + n] = z;
     if (staged) {
       const uint32_t at = atomicAdd(&s_nsel, 1u);
       s_sel[at] = uint32_t(off) | (uint32_t(hh) << 13);
@@ -265,8 +266,10 @@ void gather_kernel(Params p) {
         int j = 0;
         while (j + 1 < kLists && s_lpre[j + 1] <= i) ++j;
         jl[u] = j;
-        v[u] = p.cand[(bh0 + j / kUnitsPerTile) * p.n_cap +
-                      size_t(kUnitsPerTile * tile + j % kUnitsPerTile) * kUnit + kSpec + (i - s_lpre[j])];
+        const uint32_t e = kSpec + (i - s_lpre[j]);
+        if (RA_IN(e < uint32_t(kUnit), p, 5))
+          v[u] = p.cand[(bh0 + j / kUnitsPerTile) * p.n_cap +
+                        size_t(kUnitsPerTile * tile + j % kUnitsPerTile) * kUnit + e];
       }
     }
 #pragma unroll
@@ -307,7 +310,8 @@ void gather_kernel(Params p) {
       while (y) {
         const int bit = __ffsll((unsigned long long)y) - 1;
         y &= y - 1ull;
-        dst[rank++] = nw + bit;
+        if (RA_IN(rank < uint32_t(2 * kTile), p, 6)) dst[rank] = nw + bit;
+        ++rank;
       }
     }
   }
@@ -485,12 +489,14 @@ __device__ void copy_positions(const Params& p, int bh, int c, int nt) {
       int j = 0;
       while (j + 1 < tb - ta && s_pre[j + 1] <= i) ++j;
       at[u] = off + i;
-      v[u] = i < total ? src[size_t(ta + j) * (2 * kTile) + (i - s_pre[j])] : 0;
+      v[u] = i < total && RA_IN(i - s_pre[j] < uint32_t(2 * kTile), p, 8)
+                 ? src[size_t(ta + j) * (2 * kTile) + (i - s_pre[j])]
+                 : 0;
     }
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
       const uint32_t i = base + u * kMergeThreads + tid;
-      if (i < total && at[u] < uint32_t(p.k_max)) dst[at[u]] = v[u];
+      if (i < total && RA_IN(at[u] < uint32_t(p.k_max), p, 9)) dst[at[u]] = v[u];
     }
   }
 }

@@ -182,6 +182,7 @@ static Params make_params(const uint16_t* q, int32_t H_q, const ra_kv_layer* kv,
   p.state = reinterpret_cast<HeadState*>(base + L.off_state);
   p.gdone = reinterpret_cast<uint32_t*>(base + L.off_gdone);
   p.any_dense = reinterpret_cast<uint32_t*>(base + L.off_misc);
+  p.dbg = reinterpret_cast<uint32_t*>(base + L.off_misc + 4);
   p.unit_off = reinterpret_cast<int64_t*>(base + L.off_unitoff);
   p.ucnt = reinterpret_cast<uint32_t*>(base + L.off_ucnt);
   p.scnt = reinterpret_cast<uint32_t*>(base + L.off_scnt);
@@ -263,7 +264,7 @@ size_t ra_workspace_rescan_count_offset(int32_t B, int32_t H_q, int32_t H_kv,
                                         int32_t max_seq_len, int32_t k_max) {
   WsLayout L;
   if (!ws_layout(B, H_q, H_kv, max_seq_len, k_max, &L)) return size_t(-1);
-  return L.off_misc;  // any_dense
+  return L.off_misc;  // any_dense; the next word holds a debug build's failed checks
 }
 
 ra_status ra_kv_append(const ra_kv_layer* kv, const uint16_t* k_new,

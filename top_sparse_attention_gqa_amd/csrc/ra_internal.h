@@ -98,6 +98,8 @@ struct Params {
   HeadState* state;    // [B*H_q]
   uint32_t* gdone;     // [B*H_kv] units of the group rescanned so far
   uint32_t* any_dense; // heads rescanned in this call
+  uint32_t* dbg;       // debug builds: bounds checks that failed in this
+                       // call, one bit per check site (reset per call)
   int64_t* unit_off;   // [B + 1] prefix of H_kv * units(b)
   uint32_t* ucnt;      // [B*H_q][n_units] candidates per (head, unit)
   uint32_t* scnt;      // [B*H_q][n_tiles] retrieved per (head, tile)
@@ -209,6 +211,23 @@ hipError_t launch_kv_append(const ra_kv_layer& kv, const uint16_t* k_new,
 
 #if defined(__HIPCC__)
 // ---------------------------------------------------------------- device
+
+// Debug builds (-DRA_DEBUG): bounds checks at the decode kernels' computed
+// global accesses. RA_IN(cond, p, bit) is cond; when it fails, bit `bit`
+// is set in *p.dbg (a workspace word that a debug build's first kernel of
+// the step clears, read back as a diagnostic) and the guarded access is skipped, so a debug run reports an
+// index out of its buffer instead of touching memory outside it; no check
+// ever traps. Release builds compile every check to `true`.
+//   bit 0: a candidate list slot (scan flush)       bit 1: the same, staging full
+//   bit 2: a score row entry (scan, W)              bit 3: a sampled key's row
+//   bit 4: a rescanned list slot                    bit 5: a list entry the gather reads
+//   bit 6: a tile position the gather writes        bit 7: a retrieved score the gather stores
+//   bit 8: a position the merge copies              bit 9: an out_idx slot the merge writes
+#if defined(RA_DEBUG)
+#define RA_IN(cond, p, bit) ((cond) || (atomicOr((p).dbg, 1u << (bit)), false))
+#else
+#define RA_IN(cond, p, bit) true
+#endif
 
 // Order-preserving map fp32 -> uint32 (larger float, larger key); -0 maps
 // like +0 so that equal scores compare equal.

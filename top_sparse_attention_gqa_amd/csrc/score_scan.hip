@@ -46,11 +46,20 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(Params p) {
 #pragma unroll
   for (int s = 0; s < G; ++s) {
     const int pos = j * kPage + L.tok(s);
-    row[L.tok(s)] = (pos >= sg.lo && pos < sg.hi) ? f2key(z[s]) : 0u;
+    if (RA_IN(size_t(t) * kPage + L.tok(s) < size_t(p.samp_cap), p, 3))
+      row[L.tok(s)] = (pos >= sg.lo && pos < sg.hi) ? f2key(z[s]) : 0u;
   }
 }
 
+#if defined(RA_DEBUG)
+// the failed-check word starts each step at zero, before any kernel can set it
+__global__ void dbg_reset_kernel(uint32_t* w) { *w = 0u; }
+#endif
+
 hipError_t launch_sample(const Params& p, hipStream_t s) {
+#if defined(RA_DEBUG)
+  hipLaunchKernelGGL(dbg_reset_kernel, dim3(1), dim3(1), 0, s, p.dbg);
+#endif
   const int ns_max = p.samp_cap / kPage;
   const unsigned chunks = unsigned(ns_max > 0 ? (ns_max + kSampleWaves - 1) / kSampleWaves : 1);
   const dim3 grid{unsigned(p.B * p.H_kv), chunks}, block{unsigned(kSampleThreads)};
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
         const bool in_m = n >= sg.lo && n < sg.hi;
         const bool in_w = !in_m && n < sg.N;
         if (in_w) {
-          srow[n] = z[s];
+          if (RA_IN(n < p.n_cap, p, 2)) srow[n] = z[s];
           mw = max(mw, key);
         }
         if (in_m) mm = max(mm, key);
@@ -187,7 +196,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
               // staging full: take a slot of the list at once
               const uint32_t slot = split ? atomicAdd(&p.ucnt[(bh0 + L.F) * p.n_units + ur.u], 1u)
                                           : atomicAdd(&s_cnt[L.F], 1u);
-              crow[slot] = (uint64_t(key) << 32) | uint32_t(n);
+              if (RA_IN(slot < uint32_t(kUnit), p, 1))
+                crow[slot] = (uint64_t(key) << 32) | uint32_t(n);
             }
           }
         }
@@ -209,8 +219,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
       const uint32_t nh = st_nh[i];
       const uint32_t hh = nh >> 27;
       const uint32_t slot = (split ? s_base[hh] : 0u) + atomicAdd(&s_cnt[hh], 1u);
-      __builtin_nontemporal_store((uint64_t(st_key[i]) << 32) | (nh & ((1u << 27) - 1u)),
-                                  &p.cand[(bh0 + hh) * p.n_cap + ubase + slot]);
+      if (RA_IN(slot < uint32_t(kUnit), p, 0))
+        __builtin_nontemporal_store((uint64_t(st_key[i]) << 32) | (nh & ((1u << 27) - 1u)),
+                                    &p.cand[(bh0 + hh) * p.n_cap + ubase + slot]);
     }
     __syncthreads();
     if (tid < G) {

@@ -698,7 +698,7 @@ __device__ __forceinline__ void rescan_block(const Params& p, int blk, int nblk,
 #pragma unroll
       for (int s = 0; s < G; ++s) {
         const int n = j * kPage + L.tok(s);
-        if (mine && n >= sg.lo && n < sg.hi)
+        if (mine && n >= sg.lo && n < sg.hi && RA_IN(n - first < kUnit, p, 4))
           crow[n - first] = (uint64_t(f2key(z[s])) << 32) | uint32_t(n);
       }
     }
