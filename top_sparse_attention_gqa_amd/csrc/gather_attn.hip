@@ -496,7 +496,7 @@ __device__ void copy_positions(const Params& p, int bh, int c, int nt) {
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
       const uint32_t i = base + u * kMergeThreads + tid;
-      if (i < total && RA_IN(at[u] < uint32_t(p.k_max), p, 9)) dst[at[u]] = v[u];
+      if (i < total && RA_GUARD(at[u] < uint32_t(p.k_max), p, 9)) dst[at[u]] = v[u];
     }
   }
 }

@@ -223,10 +223,13 @@ hipError_t launch_kv_append(const ra_kv_layer& kv, const uint16_t* k_new,
 //   bit 4: a rescanned list slot                    bit 5: a list entry the gather reads
 //   bit 6: a tile position the gather writes        bit 7: a retrieved score the gather stores
 //   bit 8: a position the merge copies              bit 9: an out_idx slot the merge writes
+// RA_GUARD is the same record for a condition that release builds test too.
 #if defined(RA_DEBUG)
 #define RA_IN(cond, p, bit) ((cond) || (atomicOr((p).dbg, 1u << (bit)), false))
+#define RA_GUARD(cond, p, bit) RA_IN(cond, p, bit)
 #else
 #define RA_IN(cond, p, bit) true
+#define RA_GUARD(cond, p, bit) (cond)
 #endif
 
 // Order-preserving map fp32 -> uint32 (larger float, larger key); -0 maps
