@@ -40,6 +40,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E peak
 SCAN_SAMPLES = 20  # event-timed scan launches right after the timed region
 IN_REGION_EVERY = 10  # timed-region steps per event-timed scan, at least
 SCAN_LAYER_EVERY = 8  # C5: layers of an event-timed token step whose scan is timed
+PF_EVERY = 8  # P1: calls timed stage by stage
 PCT_STEPS = 50  # steps of the per-step latency pass
 # the scan kernel's sources: a committed counter profile is used only while
 # their hash matches the one recorded with it
@@ -756,11 +757,11 @@ def run_prefill(args):
         call(i)
     torch.cuda.synchronize()
 
-    # every SCAN_EVERY-th call runs stage by stage with events around the
+    # every PF_EVERY-th call runs stage by stage with events around the
     # two contraction kernels of the sampled pass (maxima of the sampled
     # pages, filter) on the launching stream
     events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-              for i in range(0, args.steps, SCAN_EVERY)}
+              for i in range(0, args.steps, PF_EVERY)}
     loop_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
