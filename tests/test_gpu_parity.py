@@ -134,6 +134,21 @@ def test_ragged_batch_with_shuffled_pages():
         compare_sequence(L, run, b)
 
 
+def test_large_ragged_batches():
+    # 64 and 70 short sequences of random lengths (many with an empty or
+    # tiny M) and budgets, shuffled pages, every sequence against the oracle
+    import random
+    rnd = random.Random(11)
+    for B in (64, 70):
+        lens = [rnd.randint(1, 5000) for _ in range(B)]
+        ks = [rnd.randint(0, 60) for _ in range(B)]
+        say(f"case batch_{B}: H_q=4 H_kv=1 ragged lengths up to 5000, shuffled")
+        L = layer(4, 1, lens, ks, 16, 64, seed=B, shuffle_pages=True)
+        run = gpu_decode(L, with_scores=True)
+        for b in range(B):
+            compare_sequence(L, run, b)
+
+
 def test_constant_keys_tie_to_the_lowest_positions():
     say("case ties_cand: constant keys, N=6000 (bucket fits the candidate list)")
     L = layer(4, 1, [6000], [333], 16, 64)
