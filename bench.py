@@ -655,12 +655,15 @@ def run_model(args):
 
 def model_cpu_baseline(c, layers, streams, lens, k_tab, sampled, kept, total):
     """The fp64 oracle on every KV group of the sampled layers at the first
-    and the last token step (the state each was decoded in: the first
-    lens[s] rows of the layer's pool, the step's query), scaled to a token
-    step of all layers; the GPU outputs kept at those steps are compared."""
+    and the last token step (the state each was decoded in: the layer's
+    first lens[s] rows, the step's query), scaled to a token step of all
+    layers; the GPU outputs kept at those steps are compared. The oracle's
+    rows come from the generator alone (the pool below N0, the appended
+    stream above it)."""
     import synth
 
     G = c.H_q // c.H_kv
+    N0 = c.seq_lens[0]
     model, _ = host_cpu()
     steps = sorted({0, total - 1})
 
@@ -669,8 +672,9 @@ def model_cpu_baseline(c, layers, streams, lens, k_tab, sampled, kept, total):
             L = layers[l]
             n = lens[s]
             q_g = synth.bf16_bits(streams[l][0][s][0])[g * G:(g + 1) * G]
-            K = synth.depage(L.k_pool, L.block_table, 0, n, heads=[g])
-            V = synth.depage(L.v_pool, L.block_table, 0, n, heads=[g])
+            # rows past N0 were appended by the steps: taken from the stream
+            K = synth.history(L.k_pool, L.block_table, 0, N0, streams[l][1], n, heads=[g])
+            V = synth.history(L.v_pool, L.block_table, 0, N0, streams[l][2], n, heads=[g])
             o, lse, i = kept[(s, l)]
             sl = slice(g * G, (g + 1) * G)
             return q_g, K, V, k_tab[s][l], c.n_sink, c.window, (o[sl], lse[sl], i[sl])
@@ -701,9 +705,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 PYRAMID_SLOPE_PERMILLE = 500  # C5P: budgets from 1.5x to 0.5x the mean  # MI355X published dense bf16 matrix peak
 
 
-def prefill_cpu_baseline(L, Q, budget_s=12.0):
+def prefill_cpu_baseline(L, Q, got=None, budget_s=12.0):
     """Time the fp64 oracle's prefill_topk on query rows of the same workload
-    until the budget is spent and scale to one full call (T rows)."""
+    until the budget is spent and scale to one full call (T rows); compare
+    the benchmark's own result on those rows (got: host [T][H_q][k])."""
+    import numpy as np
+
     import oracle
     import synth
 
@@ -715,12 +722,41 @@ def prefill_cpu_baseline(L, Q, budget_s=12.0):
     K = synth.depage(L.k_pool, L.block_table, 0, PF_N)
     Qb = synth.bf16_bits(Q)
     spent, rows = 0.0, 0
+    M = oracle.selection_domain(PF_N, PF_SINK, PF_WINDOW)
+    Ka = np.abs(oracle.as_f64(K))
+    u = 2.0 ** -24
+    heads = idx_fail = band_diffs = 0
     while spent < budget_s and rows < PF_T:
         t = time.perf_counter()
-        oracle.prefill_topk(Qb[rows:rows + 1], K, PF_K, PF_SINK, PF_WINDOW)
+        ref = oracle.prefill_topk(Qb[rows:rows + 1], K, PF_K, PF_SINK, PF_WINDOW)[0]
         spent += time.perf_counter() - t
+        if got is not None:
+            # indices equal outside the tie band around the k-th score (the
+            # fp32 dot-product bound as its floor), else the row is a failure
+            z = oracle.scores(Qb[rows], K)
+            G = PF_H_Q // PF_H_KV
+            for h in range(PF_H_Q):
+                k_eff = min(PF_K, M.size)
+                sel = got[rows, h, :k_eff].astype(np.int64)
+                r = ref[h, :k_eff]
+                ok = (np.all(got[rows, h, k_eff:] == -1) and np.all(np.diff(sel) > 0)
+                      and np.all(np.isin(sel, M)))
+                if ok and not np.array_equal(sel, r):
+                    qa = np.abs(oracle.as_f64(Qb[rows, h]))
+                    eps = 130 * u / (1 - 130 * u) * float((Ka[:, h // G, :] @ qa).max()) / np.sqrt(128.0)
+                    zk = z[h][r].min()
+                    band = np.abs(z[h] - zk) <= 1e-3 * abs(zk) + eps
+                    ok = np.array_equal(sel[~band[sel]], r[~band[r]])
+                    band_diffs += int(np.setdiff1d(sel, r).size)
+                idx_fail += 0 if ok else 1
+                heads += 1
         rows += 1
-    return {
+    parity = None if got is None else {
+        "rows_checked": rows, "row_heads_checked": heads, "index_failures": idx_fail,
+        "band_differences": band_diffs,
+        "tolerance": "indices equal outside |z - z_k| <= 1e-3 |z_k| + fp32 dot bound",
+        "pass": heads > 0 and idx_fail == 0}
+    return parity, {
         "value": round(spent / rows * PF_T * 1e3, 1),
         "unit": "ms",
         "cores": int(threads),
@@ -815,7 +851,10 @@ def run_prefill(args):
             bcopy.copy_(a)
         torch.cuda.synchronize()
     n_exact = int(ra.prefill_fail_flags(ws, PF_T, PF_H_Q, PF_N, PF_K).sum().item())
-    cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(layers[0], Qs[0])
+    call(0)  # copy 0's result, which the cpu_baseline leg checks
+    torch.cuda.synchronize()
+    got0 = out.cpu().numpy()
+    parity, cpu = (None, None) if args.no_cpu_baseline else prefill_cpu_baseline(layers[0], Qs[0], got0)
 
     line = {
         "metric": "prefill exact top-k latency (ms), Llama-3-8B layer, 1024 queries @128K",
@@ -851,6 +890,7 @@ def run_prefill(args):
         "sampled_maxima_contraction": {"kernel": "pf_contract_kernel<4, false>",
                                        "achieved_tflops": round(flops_s / k1_s / 1e12, 1),
                                        "avg_launch_us": round(k1_s * 1e6, 2)},
+        "parity": parity,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

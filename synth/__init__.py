@@ -13,6 +13,7 @@ from .gen import (  # noqa: F401
     LayerInputs,
     bf16_bits,
     depage,
+    history,
     draw_lengths,
     make_decode_stream,
     make_layer,

@@ -183,6 +183,22 @@ def make_new_tokens(B: int, H_kv: int, u: torch.Tensor, seed: int, device):
     return k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
+def history(pool: torch.Tensor, block_table: torch.Tensor, b: int, N0: int,
+            new_rows: torch.Tensor, n: int, heads=None) -> np.ndarray:
+    """Logical rows [0, n) of sequence b as raw bf16 bits, from the generator
+    alone: rows below N0 from the pool as the generator filled it (the rows
+    that decode steps appended sit at N0 and above and are not read back),
+    rows N0 .. n - 1 from new_rows ([steps][B][H_kv][128], the stream those
+    steps appended). Pure data movement."""
+    base = depage(pool, block_table, b, min(n, N0), heads=heads)
+    if n <= N0:
+        return base
+    new = new_rows[:n - N0, b]
+    if heads is not None:
+        new = new[:, list(heads)]
+    return np.concatenate([base, bf16_bits(new)], axis=0)
+
+
 def make_decode_stream(B: int, H_q: int, H_kv: int, u: torch.Tensor, steps: int, seed: int,
                        device):
     """Inputs of `steps` consecutive decode steps of one layer, drawn like the

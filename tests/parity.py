@@ -74,10 +74,17 @@ def gpu_decode(L: synth.LayerInputs, max_seq_len: int | None = None, k_max: int 
                ra.rescan_count(ws, B, H_q, L.H_kv, max_seq_len, k_max))
 
 
-def host_seq(L: synth.LayerInputs, b: int, kv_heads=None):
+def host_seq(L: synth.LayerInputs, b: int, kv_heads=None, appended=None):
     """q bits [H_q][128], K and V bits [N][H_kv][128] of sequence b (only the
-    KV heads listed in kv_heads, if given)."""
+    KV heads listed in kv_heads, if given). appended = (N0, k_rows, v_rows):
+    the rows at N0 and past it were appended by decode steps on the GPU; the
+    oracle takes them from the generator's streams instead of the pools."""
     n = L.seq_lens[b]
+    if appended is not None:
+        N0, kr, vr = appended
+        return (synth.bf16_bits(L.q[b]),
+                synth.history(L.k_pool, L.block_table, b, N0, kr, n, heads=kv_heads),
+                synth.history(L.v_pool, L.block_table, b, N0, vr, n, heads=kv_heads))
     return (synth.bf16_bits(L.q[b]), synth.depage(L.k_pool, L.block_table, b, n, heads=kv_heads),
             synth.depage(L.v_pool, L.block_table, b, n, heads=kv_heads))
 
@@ -141,8 +148,9 @@ def check_out(o_gpu, o_ref, what="out") -> None:
 
 
 def compare_sequence(L: synth.LayerInputs, run: Run, b: int, heads=None, ks=None,
-                     n_sink=None, window=None, check_score_rows=True) -> dict:
-    """Oracle for sequence b and full comparison. Returns stats."""
+                     n_sink=None, window=None, check_score_rows=True, appended=None) -> dict:
+    """Oracle for sequence b and full comparison (appended: see host_seq).
+    Returns stats."""
     k = (L.ks if ks is None else ks)[b]
     n_sink = L.n_sink if n_sink is None else n_sink
     window = L.window if window is None else window
@@ -150,10 +158,10 @@ def compare_sequence(L: synth.LayerInputs, run: Run, b: int, heads=None, ks=None
         G = L.H_q // L.H_kv
         grp = sorted({h // G for h in heads})
         assert len(grp) == 1, "sampled heads must share one KV head"
-        q, K, V = host_seq(L, b, kv_heads=grp)
+        q, K, V = host_seq(L, b, kv_heads=grp, appended=appended)
         q = q[heads]
     else:
-        q, K, V = host_seq(L, b)
+        q, K, V = host_seq(L, b, appended=appended)
         heads = list(range(L.H_q))
     res = oracle.decode(q, K, V, k=k, n_sink=n_sink, window=window)
     bound = score_bound(q, K)

@@ -93,6 +93,8 @@ def test_32_layer_workload_sampled_layers_over_1000_steps():
                           idx.cpu().numpy())
                 view = dataclasses.replace(layers[l], q=q, seq_lens=[lens[s]], ks=[ks[s]])
                 for heads in ALL_GROUPS:
-                    st = compare_sequence(view, run, 0, heads=heads, check_score_rows=False)
+                    # the appended rows come from the stream, not the pool
+                    st = compare_sequence(view, run, 0, heads=heads, check_score_rows=False,
+                                          appended=(N0, streams[l][1], streams[l][2]))
                     say(f"  step {s} layer {l} heads {heads[0]}..{heads[-1]}: "
                         f"band differences {st['band_diffs']}")

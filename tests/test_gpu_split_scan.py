@@ -122,4 +122,4 @@ def test_fused_append_equals_append_then_decode_in_split_mode(H_q, H_kv, N0, cap
     G = H_q // H_kv
     for g in (0, H_kv - 1):
         compare_sequence(view, run, 0, heads=list(range(g * G, (g + 1) * G)),
-                         check_score_rows=False)
+                         check_score_rows=False, appended=(N0, k_s, v_s))

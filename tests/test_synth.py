@@ -101,3 +101,20 @@ def test_oracle_retrieves_every_planted_needle_on_the_tiny_workload():
         for _ in range(20):
             alt = np.union1d(res["W"], r.choice(res["M"], 64, replace=False))
             assert np.exp(full[alt]).sum() < res["mass_recovered"][h]
+
+
+def test_history_takes_appended_rows_from_the_stream():
+    # rows below N0 come from the pool as generated, rows past it from the
+    # appended stream, whatever the pool holds there
+    base = synth.make_layer(4, 2, [300], [10], 4, 8, 2, 0, "cpu", reserve_tokens=5,
+                            shuffle_pages=True)
+    q, k, v = synth.make_decode_stream(1, 4, 2, base.u, 5, 3, "cpu")
+    # what a GPU append would have written at rows 300..304: never read
+    for t in range(300, 305):
+        base.k_pool[int(base.block_table[0, t // PAGE]), :, t % PAGE] = 7.0
+    h = synth.history(base.k_pool, base.block_table, 0, 300, k, 303, heads=[1])
+    assert h.shape == (303, 1, 128)
+    assert np.array_equal(h[:300], synth.depage(base.k_pool, base.block_table, 0, 300, heads=[1]))
+    assert np.array_equal(h[300:], synth.bf16_bits(k[:3, 0][:, [1]]))
+    assert np.array_equal(synth.history(base.k_pool, base.block_table, 0, 300, k, 200),
+                          synth.depage(base.k_pool, base.block_table, 0, 200))
