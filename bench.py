@@ -197,7 +197,9 @@ def check_group(res, gpu_out, gpu_lse, gpu_idx, q_g, K_g, k):
     tolerances: indices equal outside the 1e-3 relative band around the
     k-th score, plus the fp32 dot-product floor; out and lse within
     2e-3 + 1e-2 |ref|). Returns (band differences, index failures, largest
-    out error, out/lse failures)."""
+    out error, out/lse failures, per-head attention mass of the GPU's set:
+    the share of dense softmax weight over [0, N) on W and its retrieved
+    positions, from the oracle's fp64 scores)."""
     import numpy as np
 
     import oracle
@@ -209,6 +211,7 @@ def check_group(res, gpu_out, gpu_lse, gpu_idx, q_g, K_g, k):
     eps = 130 * u / (1 - 130 * u) * (qa @ Ka.T).max(axis=1) / np.sqrt(128.0)
     band_diffs = idx_fail = out_fail = 0
     err_max = 0.0
+    mass = []
     M = res["M"]
     k_eff = min(k, M.size)
     for h in range(G):
@@ -228,14 +231,21 @@ def check_group(res, gpu_out, gpu_lse, gpu_idx, q_g, K_g, k):
         bad = np.any(err > 2e-3 + 1e-2 * np.abs(res["out"][h]))
         bad = bad or abs(gpu_lse[h] - res["lse"][h]) > 2e-3 + 1e-2 * abs(res["lse"][h])
         out_fail += 1 if bad else 0
-    return band_diffs, idx_fail, err_max, out_fail
+        z = res["z"][h]
+        if z.size:
+            S = np.union1d(res["W"], sel[sel >= 0])
+            top = z.max()
+            mass.append(float(np.exp(z[S] - top).sum() / np.exp(z - top).sum()))
+    return band_diffs, idx_fail, err_max, out_fail, mass
 
 
 def oracle_groups(samples, budget_s):
     """Time the fp64 oracle (as it stands) on (q_g, K, V, k, n_sink, window,
-    gpu) samples of one KV group each, until the budget is spent (at least
-    one); compare each with the GPU results it carries. Returns (seconds
-    spent, groups done, parity dict)."""
+    gpu, needles) samples of one KV group each, until the budget is spent
+    (at least one); compare each with the GPU results it carries (needles:
+    (position, head within the group) rows planted in it, each to be
+    retrieved by its head). Returns (seconds spent, groups done, parity
+    dict)."""
     import numpy as np
 
     import oracle
@@ -243,17 +253,23 @@ def oracle_groups(samples, budget_s):
     spent, done = 0.0, 0
     band = idx_fail = out_fail = heads = 0
     err_max = 0.0
+    masses = []
+    needles = found = 0
     for make in samples:
-        q_g, K, V, k, n_sink, window, gpu = make()
+        q_g, K, V, k, n_sink, window, gpu, nd = make()
         t = time.perf_counter()
         res = oracle.decode(q_g, K, V, k, n_sink, window)
         spent += time.perf_counter() - t
         done += 1
         if gpu is not None:
-            b_, i_, e_, o_ = check_group(res, *gpu, q_g, K, k)
+            b_, i_, e_, o_, m_ = check_group(res, *gpu, q_g, K, k)
             band, idx_fail, out_fail = band + b_, idx_fail + i_, out_fail + o_
             err_max = max(err_max, e_)
+            masses += m_
             heads += q_g.shape[0]
+            for pos, hh in nd:
+                needles += 1
+                found += int(pos in gpu[2][hh])
         del K, V, res
         if spent >= budget_s:
             break
@@ -262,7 +278,10 @@ def oracle_groups(samples, budget_s):
               "out_max_abs_err": float(f"{err_max:.3e}"),
               "tolerance": "indices equal outside |z - z_k| <= 1e-3 |z_k| + fp32 dot bound; "
                            "out, lse within 2e-3 + 1e-2 |ref|",
-              "pass": heads > 0 and idx_fail == 0 and out_fail == 0}
+              "pass": heads > 0 and idx_fail == 0 and out_fail == 0,
+              "attention_mass_recovered": None if not masses else {
+                  "mean": round(float(np.mean(masses)), 5), "min": round(float(np.min(masses)), 5)},
+              "needles_retrieved": f"{found}/{needles}"}
     return spent, done, parity
 
 
@@ -288,7 +307,9 @@ def cpu_baseline(c, L, lens, ks, gpu=None, budget_s=12.0):
             if gpu is not None:
                 o, l, i = gpu
                 gg = (o[b, g * G:(g + 1) * G], l[b, g * G:(g + 1) * G], i[b, g * G:(g + 1) * G])
-            return q_g, K, V, ks[b], c.n_sink, c.window, gg
+            nd = [(int(pos), int(h) - g * G) for pos, h in L.needles[b].tolist()
+                  if g * G <= h < (g + 1) * G]
+            return q_g, K, V, ks[b], c.n_sink, c.window, gg, nd
         return make
 
     samples = [sample(b, g) for b in range(len(lens)) for g in range(c.H_kv)]
@@ -612,7 +633,7 @@ def run_model(args):
         cpu = model_cpu_baseline(c, layers, streams, lens, k_tab, sampled, kept, total)
 
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
-    pct = {f"p{q}": round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)}
+    pct = {f"p{q}": round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90, 99)}
     line = {
         "metric": METRIC,
         "value": round(ms_per_step, 4),
@@ -677,7 +698,9 @@ def model_cpu_baseline(c, layers, streams, lens, k_tab, sampled, kept, total):
             V = synth.history(L.v_pool, L.block_table, 0, N0, streams[l][2], n, heads=[g])
             o, lse, i = kept[(s, l)]
             sl = slice(g * G, (g + 1) * G)
-            return q_g, K, V, k_tab[s][l], c.n_sink, c.window, (o[sl], lse[sl], i[sl])
+            nd = [(int(pos), int(h) - g * G) for pos, h in L.needles[0].tolist()
+                  if g * G <= h < (g + 1) * G]
+            return q_g, K, V, k_tab[s][l], c.n_sink, c.window, (o[sl], lse[sl], i[sl]), nd
         return make
 
     samples = [sample(s, l, g) for s in steps for l in sampled for g in range(c.H_kv)]
