@@ -281,7 +281,7 @@ def oracle_groups(samples, budget_s):
               "pass": heads > 0 and idx_fail == 0 and out_fail == 0,
               "attention_mass_recovered": None if not masses else {
                   "mean": round(float(np.mean(masses)), 5), "min": round(float(np.min(masses)), 5)},
-              "needles_retrieved": f"{found}/{needles}"}
+              "needles_retrieved": f"{found}/{needles}" if needles else None}
     return spent, done, parity
 
 
@@ -698,9 +698,9 @@ def model_cpu_baseline(c, layers, streams, lens, k_tab, sampled, kept, total):
             V = synth.history(L.v_pool, L.block_table, 0, N0, streams[l][2], n, heads=[g])
             o, lse, i = kept[(s, l)]
             sl = slice(g * G, (g + 1) * G)
-            nd = [(int(pos), int(h) - g * G) for pos, h in L.needles[0].tolist()
-                  if g * G <= h < (g + 1) * G]
-            return q_g, K, V, k_tab[s][l], c.n_sink, c.window, (o[sl], lse[sl], i[sl]), nd
+            # the layer's needles were planted along its own query, not the
+            # stream's: no needle check here
+            return q_g, K, V, k_tab[s][l], c.n_sink, c.window, (o[sl], lse[sl], i[sl]), []
         return make
 
     samples = [sample(s, l, g) for s in steps for l in sampled for g in range(c.H_kv)]
