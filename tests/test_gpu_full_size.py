@@ -98,3 +98,37 @@ def test_32_layer_workload_sampled_layers_over_1000_steps():
                                           appended=(N0, streams[l][1], streams[l][2]))
                     say(f"  step {s} layer {l} heads {heads[0]}..{heads[-1]}: "
                         f"band differences {st['band_diffs']}")
+
+
+@pytest.mark.parametrize("N", [1 << 24, (1 << 24) - 37])
+def test_longest_sequence_the_library_accepts(N):
+    # RA_MAX_SEQ_LEN positions (and a ragged length just below it): 4096
+    # units per KV head, positions at the top of the 24-bit row fields.
+    # The oracle checks every head; its fp32 error floor is formed tile by
+    # tile (an fp64 copy of all 2^24 keys would be 16 GB).
+    import oracle
+    from tests.parity import U32, check_indices, check_out
+
+    H_q, H_kv, k, ns, win = 4, 1, 2000, 16, 64
+    say(f"case longest: H_q={H_q} H_kv={H_kv} N={N} k={k}")
+    L = synth.make_layer(H_q, H_kv, [N], [k], ns, win, 2, 77, DEV)
+    run = gpu_decode(L, max_seq_len=1 << 24)
+    assert run.rescanned == 0
+    q = synth.bf16_bits(L.q[0])
+    K = synth.depage(L.k_pool, L.block_table, 0, N)
+    V = synth.depage(L.v_pool, L.block_table, 0, N)
+    res = oracle.decode(q, K, V, k=k, n_sink=ns, window=win)
+    qa = np.abs(oracle.as_f64(q))
+    top = np.zeros(H_q)
+    for t0 in range(0, N, 1 << 20):
+        Ka = np.abs(oracle.as_f64(K[t0:t0 + (1 << 20), 0, :]))
+        top = np.maximum(top, (qa @ Ka.T).max(axis=1))
+    eps = 130 * U32 / (1 - 130 * U32) * top / np.sqrt(128.0)
+    band = 0
+    for h in range(H_q):
+        band += check_indices(run.idx[0, h], res, h, k, eps[h])
+        check_out(run.out[0, h], res["out"][h], f"out[h={h}]")
+        check_out(np.array([run.lse[0, h]]), np.array([res["lse"][h]]), f"lse[h={h}]")
+    for pos, h in L.needles[0]:
+        assert pos in run.idx[0, h]
+    say(f"  band differences: {band}")

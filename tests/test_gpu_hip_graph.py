@@ -6,7 +6,6 @@ queries written into the captured input in place, with eager library calls
 and synchronisations between the replays, and requires every replay to
 equal the same step run eagerly, bit for bit."""
 
-import numpy as np
 import pytest
 import torch
 
