@@ -114,7 +114,7 @@ static void check_params_in(const ra::Params& p, const char* ws, size_t total) {
   inside(p.part_mz, h * p.n_tiles * 8);
   inside(p.part_n, h * p.n_tiles * 512);
   CHECK(p.n_cap >= p.max_seq_len && p.n_cap % ra::kTile == 0);
-  CHECK(int64_t(p.n_units) * ra::kUnit == p.n_cap && int64_t(p.n_tiles) * ra::kTile == p.n_cap);
+  CHECK(int64_t(p.n_units) * ra::kUnit == p.n_cap && int64_t(p.n_tiles) * ra::kUnit == p.n_cap);
 }
 
 // ------------------------------------------------------------------ checks

@@ -104,16 +104,26 @@ __device__ __forceinline__ void accumulate_rows(const Params& p, int g, int cnt,
   }
 }
 
-template <int G>
+template <int G, int UPT>
 __global__ __launch_bounds__(kGathThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void gather_kernel(Params p) {
+  // a tile of UPT units: UPT * 4096 positions, one bitmap word per page
+  constexpr int kTileT = UPT * kUnit;
+  constexpr int kWordsT = kTileT / 64;
+  // the prologue deals its loads to thread ranges: page numbers (one per
+  // word), then the list lengths from kWordsT, the head states from
+  // kWordsT + 32, the W-slice pages in the last kWPre threads
+  static_assert(UPT * G <= 32, "list lengths fit their 32 threads");
+  static_assert(kWordsT + 32 + G <= kGathThreads - kWPre, "prologue thread ranges overlap");
+  // staged entries pack the tile offset in 13 bits, per-head counts in 16
+  static_assert(kTileT <= 8192, "tile offsets fit 13 bits");
   const int tile = blockIdx.y;
   const int bg = blockIdx.x;
   const int b = bg / p.H_kv;
   const int g = bg - b * p.H_kv;
   const SeqGeom sg = seq_geom(p, b);
   const size_t bh0 = size_t(b) * p.H_q + size_t(g) * G;
-  const int t0 = tile * kTile;
+  const int t0 = tile * kTileT;
   if (t0 >= sg.N) return;
 
   const int tid = threadIdx.x;
@@ -121,14 +131,14 @@ void gather_kernel(Params p) {
   const int wave = tid >> 6;
   const int r = lane & 15;
   constexpr int kCh = kChunk;
-  constexpr int kLists = kUnitsPerTile * G;  // list j: head j / kUnitsPerTile
+  constexpr int kLists = UPT * G;  // list j: head j / UPT
   constexpr int kSpecPer = (kLists * kSpec + kGathThreads - 1) / kGathThreads;
   constexpr int kWzPer = (kWPre * G + kGathThreads - 1) / kGathThreads;
 
-  __shared__ uint64_t bm[G][kWordsPerTile];
-  __shared__ uint64_t s_uw[kWordsPerTile];  // union of the heads' bitmaps
-  __shared__ int32_t s_ex[kWordsPerTile];   // union rows before each word
-  __shared__ int32_t s_pg[kWordsPerTile];
+  __shared__ uint64_t bm[G][kWordsT];
+  __shared__ uint64_t s_uw[kWordsT];  // union of the heads' bitmaps
+  __shared__ int32_t s_ex[kWordsT];   // union rows before each word
+  __shared__ int32_t s_pg[kWordsT];
   __shared__ uint32_t s_row[kCh];
   __shared__ int32_t s_rpg[kCh];
   __shared__ float s_w[kCh][G];             // e^{z - m} of (row, head), 0 if absent
@@ -145,12 +155,12 @@ void gather_kernel(Params p) {
   __shared__ int64_t s_tmp[16];
   __shared__ HeadState s_st[G];
   __shared__ float s_mref[G];
-  __shared__ uint32_t s_lc[kLists];         // list j: head j / kUnitsPerTile,
-  __shared__ uint32_t s_lpre[kLists + 1];   // unit kUnitsPerTile tile + j % kUnitsPerTile
+  __shared__ uint32_t s_lc[kLists];         // list j: head j / UPT,
+  __shared__ uint32_t s_lpre[kLists + 1];   // unit UPT tile + j % UPT
   __shared__ int32_t s_wpg[kWPre];          // pages of the first rows of the W slice
 
   // this block's slice [w0, w1) of the rows of W = [0, lo) u [hi, N)
-  const int nt = (sg.N + kTile - 1) / kTile;
+  const int nt = (sg.N + kTileT - 1) / kTileT;
   const int wsize = sg.lo + (sg.N - sg.hi);
   const int wper = (wsize + nt - 1) / nt;
   const int w0 = min(wsize, tile * wper);
@@ -162,17 +172,17 @@ void gather_kernel(Params p) {
   // first kSpec entries of each of the 2 G candidate lists (read before
   // their lengths are known; entries past a list's end are dropped).
   const int units_seq = (sg.N + kUnit - 1) / kUnit;
-  if (tid < kWordsPerTile) {
+  if (tid < kWordsT) {
     // a 64-bit word covers exactly one 64-token page
     s_pg[tid] = (t0 + tid * 64 < sg.N) ? page_of(p, b, (t0 >> 6) + tid) : 0;
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) bm[hh][tid] = 0ull;
-  } else if (tid < kWordsPerTile + kLists) {
-    const int j = tid - kWordsPerTile;
-    const int unit = kUnitsPerTile * tile + j % kUnitsPerTile;
-    s_lc[j] = unit < units_seq ? p.ucnt[(bh0 + j / kUnitsPerTile) * p.n_units + unit] : 0u;
-  } else if (tid >= kWordsPerTile + 32 && tid < kWordsPerTile + 32 + G) {
-    const int hh = tid - kWordsPerTile - 32;
+  } else if (tid < kWordsT + kLists) {
+    const int j = tid - kWordsT;
+    const int unit = UPT * tile + j % UPT;
+    s_lc[j] = unit < units_seq ? p.ucnt[(bh0 + j / UPT) * p.n_units + unit] : 0u;
+  } else if (tid >= kWordsT + 32 && tid < kWordsT + 32 + G) {
+    const int hh = tid - kWordsT - 32;
     s_st[hh] = p.state[bh0 + hh];
   } else if (tid >= kGathThreads - kWPre) {
     const int i = tid - (kGathThreads - kWPre);
@@ -184,10 +194,10 @@ void gather_kernel(Params p) {
   for (int u = 0; u < kSpecPer; ++u) {
     const int e = u * kGathThreads + tid;
     const int j = e / kSpec, i = e - j * kSpec;
-    const int unit = kUnitsPerTile * tile + j % kUnitsPerTile;
+    const int unit = UPT * tile + j % UPT;
     spec[u] = (j < kLists && unit < units_seq &&
                RA_IN(size_t(unit) * kUnit + i < size_t(p.n_cap), p, 5))
-                  ? p.cand[(bh0 + j / kUnitsPerTile) * p.n_cap + size_t(unit) * kUnit + i]
+                  ? p.cand[(bh0 + j / UPT) * p.n_cap + size_t(unit) * kUnit + i]
                   : 0ull;
   }
   float wz[kWzPer];  // score of W-slice row q / G for head q % G, q = u * 256 + tid
@@ -201,10 +211,10 @@ void gather_kernel(Params p) {
   }
   __syncthreads();
   if (tid < G) s_mref[tid] = softmax_ref(s_st[tid], sg.k_eff);
-  if (tid < kLists && s_st[tid / kUnitsPerTile].dense != 0u) {
+  if (tid < kLists && s_st[tid / UPT].dense != 0u) {
     // a rescanned head's lists hold every member of M at its place: their
     // lengths are the units' overlaps with M
-    const int unit = kUnitsPerTile * tile + tid % kUnitsPerTile;
+    const int unit = UPT * tile + tid % UPT;
     const int ov = min((unit + 1) * kUnit, sg.hi) - max(unit * kUnit, sg.lo);
     s_lc[tid] = ov > 0 ? uint32_t(ov) : 0u;
   }
@@ -240,15 +250,15 @@ void gather_kernel(Params p) {
   for (int u = 0; u < kSpecPer; ++u) {
     const int e = u * kGathThreads + tid;
     const int j = e / kSpec, i = e - j * kSpec;
-    if (j < kLists && uint32_t(i) < s_lc[j] && s_st[j / kUnitsPerTile].thr_shift < 64u)
-      take(j / kUnitsPerTile, spec[u]);
+    if (j < kLists && uint32_t(i) < s_lc[j] && s_st[j / UPT].thr_shift < 64u)
+      take(j / UPT, spec[u]);
   }
   // the rest of the lists (past kSpec entries), as one index space
   if (tid == 0) {
     uint32_t run = 0;
     for (int j = 0; j < kLists; ++j) {
       s_lpre[j] = run;
-      if (s_st[j / kUnitsPerTile].thr_shift < 64u && s_lc[j] > uint32_t(kSpec)) run += s_lc[j] - kSpec;
+      if (s_st[j / UPT].thr_shift < 64u && s_lc[j] > uint32_t(kSpec)) run += s_lc[j] - kSpec;
     }
     s_lpre[kLists] = run;
   }
@@ -268,13 +278,13 @@ void gather_kernel(Params p) {
         jl[u] = j;
         const uint32_t e = kSpec + (i - s_lpre[j]);
         if (RA_IN(e < uint32_t(kUnit), p, 5))
-          v[u] = p.cand[(bh0 + j / kUnitsPerTile) * p.n_cap +
-                        size_t(kUnitsPerTile * tile + j % kUnitsPerTile) * kUnit + e];
+          v[u] = p.cand[(bh0 + j / UPT) * p.n_cap +
+                        size_t(UPT * tile + j % UPT) * kUnit + e];
       }
     }
 #pragma unroll
     for (int u = 0; u < kListBatch; ++u)
-      if (jl[u] >= 0) take(jl[u] / kUnitsPerTile, v[u]);
+      if (jl[u] >= 0) take(jl[u] / UPT, v[u]);
   }
   __syncthreads();
 
@@ -284,7 +294,7 @@ void gather_kernel(Params p) {
   PackedCounts<G> pc;
 #pragma unroll
   for (int j = 0; j < PackedCounts<G>::kWords; ++j) pc.v[j] = 0;
-  if (tid < kWordsPerTile) {
+  if (tid < kWordsT) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       uw |= bm[hh][tid];
@@ -297,7 +307,7 @@ void gather_kernel(Params p) {
 #pragma unroll
   for (int j = 0; j < PackedCounts<G>::kWords; ++j)
     px.v[j] = block_excl_scan(pc.v[j], s_tmp, &ptot.v[j]);
-  if (tid < kWordsPerTile) {
+  if (tid < kWordsT) {
     s_uw[tid] = uw;
     s_ex[tid] = int32_t(ex);
     // the tile's retrieved positions, ascending, replace its consumed lists
@@ -310,7 +320,7 @@ void gather_kernel(Params p) {
       while (y) {
         const int bit = __ffsll((unsigned long long)y) - 1;
         y &= y - 1ull;
-        if (RA_IN(rank < uint32_t(2 * kTile), p, 6)) dst[rank] = nw + bit;
+        if (RA_IN(rank < uint32_t(2 * kTileT), p, 6)) dst[rank] = nw + bit;
         ++rank;
       }
     }
@@ -332,7 +342,7 @@ void gather_kernel(Params p) {
   for (int cb = 0; cb < R; cb += kCh) {
     const int cnt = min(kCh, R - cb);
     // list this chunk of the rows in LDS, weights cleared
-    if (tid < kWordsPerTile && cb < U) {
+    if (tid < kWordsT && cb < U) {
       int pos = int(ex) - cb;
       uint64_t x = uw;
       while (x && pos < kCh) {
@@ -447,7 +457,7 @@ constexpr int kMergeTiles = 8;   // tiles per out_idx copy block
 // out_idx for tiles [c * kMergeTiles, (c + 1) * kMergeTiles) of head bh.
 // Every count the block needs is loaded in one round: thread t holds tile
 // t's count, the tiles before ta are summed, the block's own go to LDS.
-__device__ void copy_positions(const Params& p, int bh, int c, int nt) {
+__device__ void copy_positions(const Params& p, int bh, int c, int nt, int tile) {
   const int tid = threadIdx.x;
   const int ta = c * kMergeTiles;
   if (ta >= nt) return;
@@ -489,8 +499,8 @@ __device__ void copy_positions(const Params& p, int bh, int c, int nt) {
       int j = 0;
       while (j + 1 < tb - ta && s_pre[j + 1] <= i) ++j;
       at[u] = off + i;
-      v[u] = i < total && RA_IN(i - s_pre[j] < uint32_t(2 * kTile), p, 8)
-                 ? src[size_t(ta + j) * (2 * kTile) + (i - s_pre[j])]
+      v[u] = i < total && RA_IN(i - s_pre[j] < uint32_t(2 * tile), p, 8)
+                 ? src[size_t(ta + j) * (2 * tile) + (i - s_pre[j])]
                  : 0;
     }
 #pragma unroll
@@ -502,14 +512,15 @@ __device__ void copy_positions(const Params& p, int bh, int c, int nt) {
 }
 
 // Grid (1 + copy blocks, B * H_q): x == 0 merges the partials of head y,
-// x > 0 copies positions.
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p) {
+// x > 0 copies positions. tile_units: the gather's tile size, in units.
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p, int tile_units) {
   const int bh = blockIdx.y;
   const int b = bh / p.H_q;
   const SeqGeom sg = seq_geom(p, b);
-  const int nt = (sg.N + kTile - 1) / kTile;
+  const int tile = tile_units * kUnit;
+  const int nt = (sg.N + tile - 1) / tile;
   if (blockIdx.x > 0) {
-    if (p.k_max > 0 && sg.k_eff > 0) copy_positions(p, bh, int(blockIdx.x) - 1, nt);
+    if (p.k_max > 0 && sg.k_eff > 0) copy_positions(p, bh, int(blockIdx.x) - 1, nt, tile);
     return;
   }
   const int tid = threadIdx.x;
@@ -573,10 +584,43 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p) {
   }
 }
 
+// The gather's tile size, in units: one when two-unit tiles would give
+// fewer than two blocks per CU (short contexts, where the blocks would be
+// few and long), else two. Both launches below take it from the same
+// host arguments.
+static int gather_tile_units(const Params& p) {
+  const int64_t cap = std::min<int64_t>(p.max_seq_len, int64_t(p.max_pages) * kPage);
+  const int64_t blocks2 = int64_t(p.B) * p.H_kv * ((cap + 2 * kUnit - 1) / (2 * kUnit));
+  const int64_t cus = p.num_cus > 0 ? p.num_cus : 256;
+  return blocks2 < 2 * cus ? 1 : 2;
+}
+
+static int64_t gather_tiles(const Params& p, int upt) {
+  const int64_t cap = std::min<int64_t>(p.max_seq_len, int64_t(p.max_pages) * kPage);
+  const int64_t tile = int64_t(upt) * kUnit;
+  return std::max<int64_t>(1, std::min<int64_t>((cap + tile - 1) / tile, p.n_tiles));
+}
+
 hipError_t launch_merge(const Params& p, hipStream_t s) {
-  const unsigned copies = p.k_max > 0 ? unsigned((p.n_tiles + kMergeTiles - 1) / kMergeTiles) : 0u;
+  const int upt = gather_tile_units(p);
+  const unsigned copies =
+      p.k_max > 0 ? unsigned((gather_tiles(p, upt) + kMergeTiles - 1) / kMergeTiles) : 0u;
   hipLaunchKernelGGL(merge_kernel, dim3(1 + copies, unsigned(p.B * p.H_q)), dim3(kMergeThreads), 0,
-                     s, p);
+                     s, p, upt);
+  return hipGetLastError();
+}
+
+template <int UPT>
+static hipError_t launch_gather_t(const Params& p, hipStream_t s) {
+  const dim3 grid{unsigned(p.B * p.H_kv), unsigned(gather_tiles(p, UPT))};
+  const dim3 block{unsigned(kGathThreads)};
+  switch (p.G) {
+    case 1: hipLaunchKernelGGL((gather_kernel<1, UPT>), grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((gather_kernel<2, UPT>), grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((gather_kernel<4, UPT>), grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((gather_kernel<8, UPT>), grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -586,18 +630,7 @@ hipError_t launch_merge(const Params& p, hipStream_t s) {
 // left for a second wave are then the short tail tiles, which finish under
 // the first wave's full ones instead of extending the kernel by a full tile.
 hipError_t launch_gather(const Params& p, hipStream_t s) {
-  const int64_t cap = std::min<int64_t>(p.max_seq_len, int64_t(p.max_pages) * kPage);
-  const int64_t tiles = std::max<int64_t>(1, std::min<int64_t>((cap + kTile - 1) / kTile, p.n_tiles));
-  const dim3 grid{unsigned(p.B * p.H_kv), unsigned(tiles)};
-  const dim3 block{unsigned(kGathThreads)};
-  switch (p.G) {
-    case 1: hipLaunchKernelGGL(gather_kernel<1>, grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL(gather_kernel<2>, grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL(gather_kernel<4>, grid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL(gather_kernel<8>, grid, block, 0, s, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return gather_tile_units(p) == 1 ? launch_gather_t<1>(p, s) : launch_gather_t<2>(p, s);
 }
 
 }  // namespace ra

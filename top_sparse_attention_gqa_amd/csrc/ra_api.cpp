@@ -31,7 +31,7 @@ bool ws_layout(int32_t B, int32_t H_q, int32_t H_kv, int32_t max_seq_len,
   // mod 128 KB) the scan, which writes those rows while it streams K,
   // measured 5 % slower; an even number showed no such loss.
   L->n_cap = (int64_t(max_seq_len) + 2 * kTile - 1) / (2 * kTile) * (2 * kTile);
-  L->n_tiles = int32_t(L->n_cap / kTile);
+  L->n_tiles = int32_t(L->n_cap / kUnit);  // tiles of the smallest size (one unit)
   L->n_units = int32_t(L->n_cap / kUnit);
   // sampled_pages(P) is not monotone below 2048 pages (the stride doubles
   // as P grows) but stays <= 64 there, and is monotone above.

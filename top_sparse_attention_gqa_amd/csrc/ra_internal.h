@@ -17,11 +17,9 @@ constexpr int kPage = 64;
 // block that owns a unit writes its lists and counts without atomics.
 constexpr int kUnitPages = 64;
 constexpr int kUnit = kUnitPages * kPage;  // 4096 positions
-// Positions per gather tile (a whole number of units): one tile is one
-// split-K partial.
-constexpr int kUnitsPerTile = 2;
-constexpr int kTile = kUnitsPerTile * kUnit;
-constexpr int kWordsPerTile = kTile / 64;
+// A gather tile (one split-K partial) is one or two units, as the launch
+// picks; kTile is the larger. Workspace rows hold whole pairs of them.
+constexpr int kTile = 2 * kUnit;
 // Largest number of units of one sequence (RA_MAX_SEQ_LEN / kUnit).
 constexpr int kMaxUnits = RA_MAX_SEQ_LEN / kUnit;
 // Sampling: one page in S is scored before the main scan, S a power of two
@@ -61,7 +59,7 @@ struct HeadState {
 
 struct WsLayout {
   int64_t n_cap;    // row stride (positions), a multiple of kTile
-  int32_t n_tiles;  // n_cap / kTile
+  int32_t n_tiles;  // n_cap / kUnit: per-tile arrays hold the smallest tiles
   int32_t n_units;  // n_cap / kUnit
   int32_t samp_cap; // sampled key slots per head
   size_t off_scores, off_samp, off_state, off_gdone, off_misc, off_unitoff,
