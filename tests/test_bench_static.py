@@ -37,3 +37,16 @@ def unbound_names(path):
                                  "synth/gen.py", "synth/configs.py", "oracle/ra_oracle.py"])
 def test_no_unbound_names(rel):
     assert unbound_names(os.path.join(ROOT, rel)) == []
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    # one GPU per box: --gpus N > 1 (or a launcher's WORLD_SIZE > 1) exits
+    # with status 2 and says why, before touching any device
+    import subprocess
+    import sys
+    for args, env in ((["--gpus", "2"], {}), (["--gpus", "1"], {"WORLD_SIZE": "8"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                           capture_output=True, text=True, timeout=120,
+                           env=dict(os.environ, **env))
+        assert r.returncode == 2, (args, r.returncode, r.stderr[-500:])
+        assert "one GPU" in r.stderr
