@@ -216,6 +216,23 @@ def test_dense_path_in_some_groups_of_a_batch():
     compare_sequence(L, run, 1)
 
 
+def test_rescan_in_a_batch_with_more_heads_than_cus():
+    # 70 sequences x 4 query heads with budgets up to 6000: the select runs
+    # two blocks per CU, and the rescan in a launch of its own; one group's
+    # sample is misled, so its heads take the rescan there
+    import random
+    rnd = random.Random(12)
+    lens = [rnd.randint(1000, 4000) for _ in range(69)] + [32768]
+    ks = [rnd.randint(0, 50) for _ in range(69)] + [6000]
+    say("case narrow_select_rescan: B=70 H_q=4 H_kv=1, the last sequence misled, k=6000")
+    L = layer(4, 1, lens, ks, 16, 64, seed=13, shuffle_pages=True)
+    plant_on_sampled_pages(L, 69, 0)
+    run = gpu_decode(L, with_scores=True)
+    assert run.rescanned > 0
+    for b in (0, 1, 35, 68, 69):
+        compare_sequence(L, run, b)
+
+
 def test_integer_scores_with_many_ties():
     say("case ternary: integer-valued dot products, N=12000")
     L = layer(8, 2, [12000], [700], 16, 64)

@@ -30,10 +30,19 @@ constexpr int kSelThreads = 512;
 constexpr int kSubCap = 2048;     // LDS list for one radix sub-bucket
 constexpr uint32_t kRankMax = 256; // sub-buckets up to this size are finished by ranking
 constexpr int kBatch = 8;         // global entries per lane in flight per pass
-constexpr int kRegEntries = 64;   // candidate entries per lane kept in registers
+constexpr int kRegEntries = 64;   // candidate entries per lane kept in registers (wide select)
 constexpr int kRegKeys = 32;      // sampled keys per lane kept in registers
-constexpr int kStartRows = 4096;  // rows of 64 list entries whose first unit is tabled
+constexpr int kStartRows = 4096;  // rows of 64 list entries whose first unit is tabled (wide)
 static_assert(kRegEntries * kSelThreads / 64 <= kStartRows, "register rows must be tabled");
+// The narrow select (select_kernel_narrow) holds 24 entries per lane and
+// tables their 192 rows, so its registers and LDS leave room for two blocks
+// per CU: when a batch has more heads than CUs they select in one round
+// instead of two. It serves budgets up to kNarrowKMax, whose candidates
+// (about 1.5 to 1.7 times k_eff under the sampled bound) fit its 12288
+// register slots; more would be streamed, correctly but slower.
+constexpr int kNarrowEntries = 24;
+constexpr int kNarrowRows = kNarrowEntries * kSelThreads / 64;
+constexpr int kNarrowKMax = 6144;
 
 // ---------------------------------------------------------------- wave helpers
 // Every lane of the wave must call these.
@@ -505,11 +514,12 @@ hipError_t launch_threshold(const Params& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- select state
+template <int ROWS>
 struct SelLds {
   uint16_t ne[kMaxUnits];         // non-empty units (relative to u_lo), ascending
   uint32_t pb[kMaxUnits + 1];     // index of the first entry of each; the total
-  uint16_t rowk[kStartRows];      // non-empty unit holding entry 64 q (index into ne)
-  uint64_t rmask[kStartRows];     // bit l (l > 0): entry 64 q + l starts a unit
+  uint16_t rowk[ROWS];            // non-empty unit holding entry 64 q (index into ne)
+  uint64_t rmask[ROWS];           // bit l (l > 0): entry 64 q + l starts a unit
   uint32_t hist[2048];
   uint64_t sub[kSubCap];
   uint32_t s_d, s_above, s_cnt, s_n;
@@ -519,12 +529,13 @@ struct SelLds {
 // List lengths of units u_lo .. u_lo + nu - 1 (their overlaps with M when
 // dense), laid out as the non-empty units and their entry ranges, with the
 // row table. Returns the list view. Block-wide.
+template <int ROWS>
 __device__ __forceinline__ UnitLists unit_prefix(const Params& p, int bh, const SeqGeom& sg, int u_lo, int nu,
-                                 bool dense, uint32_t lo, SelLds& L) {
+                                 bool dense, uint32_t lo, SelLds<ROWS>& L) {
   constexpr int per = kMaxUnits / kSelThreads;
   const int tid = threadIdx.x;
   const uint32_t* uc = p.ucnt + size_t(bh) * p.n_units;
-  for (int q = tid; q < kStartRows; q += kSelThreads) L.rmask[q] = 0ull;
+  for (int q = tid; q < ROWS; q += kSelThreads) L.rmask[q] = 0ull;
   uint32_t c[per];
   int64_t v = 0;  // entries << 13 | non-empty units (at most kMaxUnits < 2^13)
 #pragma unroll
@@ -545,7 +556,7 @@ __device__ __forceinline__ UnitLists unit_prefix(const Params& p, int bh, const 
   const int64_t run = block_excl_scan(v, L.tmp, &tot);
   const uint32_t total = uint32_t(tot >> 13);
   const int n_ne = int(tot & 8191);
-  const uint32_t rows = min(uint32_t(kStartRows), (total + 63u) / 64u);
+  const uint32_t rows = min(uint32_t(ROWS), (total + 63u) / 64u);
   uint32_t e = uint32_t(run >> 13);
   int k = int(run & 8191);
 #pragma unroll
@@ -568,9 +579,9 @@ __device__ __forceinline__ UnitLists unit_prefix(const Params& p, int bh, const 
 
 // Exact threshold of head bh over its candidates (source src), written
 // into the head state.
-template <typename Src>
+template <typename Src, int ROWS>
 __device__ __forceinline__ void decide(const Params& p, int bh, const SeqGeom& sg, const Src& src,
-                                       int TB, uint32_t lo, SelLds& L) {
+                                       int TB, uint32_t lo, SelLds<ROWS>& L) {
   const Radix rx{L.hist, &L.s_d, &L.s_above, &L.s_cnt};
   uint64_t prefix;
   int plen;
@@ -584,12 +595,15 @@ __device__ __forceinline__ void decide(const Params& p, int bh, const SeqGeom& s
   }
 }
 
-// Select over the lists of head bh, from registers when they fit.
+// Select over the lists of head bh, from registers when they fit (NR
+// entries per lane).
+template <int NR, int ROWS>
 __device__ __forceinline__ void select_head(const Params& p, int bh, const SeqGeom& sg,
-                                            const UnitLists& gl, uint32_t max_m, SelLds& L) {
+                                            const UnitLists& gl, uint32_t max_m, SelLds<ROWS>& L) {
+  static_assert(NR * kSelThreads / 64 <= ROWS, "register rows must be tabled");
   const uint32_t span = max_m > gl.lo ? max_m - gl.lo : 1u;
   const int TB = 32 + bit_length(span);
-  RegLists<kRegEntries> rl;
+  RegLists<NR> rl;
   rl.load(gl);
   decide(p, bh, sg, rl, TB, gl.lo, L);
 }
@@ -612,7 +626,8 @@ __device__ __forceinline__ void select_head(const Params& p, int bh, const SeqGe
 // in which order the two kinds of blocks run.
 static_assert(kScanThreads == kSelThreads, "the rescan blocks also select");
 
-__device__ __forceinline__ void select_block(const Params& p, int bh, SelLds& L) {
+template <int NR, int ROWS>
+__device__ __forceinline__ void select_block(const Params& p, int bh, SelLds<ROWS>& L) {
   const int b = bh / p.H_q;
   const SeqGeom sg = seq_geom(p, b);
   if (sg.k_eff == 0) return;  // the unset threshold takes nothing
@@ -626,7 +641,7 @@ __device__ __forceinline__ void select_block(const Params& p, int bh, SelLds& L)
     }
     return;
   }
-  select_head(p, bh, sg, gl, st.max_m, L);
+  select_head<NR>(p, bh, sg, gl, st.max_m, L);
 }
 
 // Bit hh set: head hh of group (b, g) has fewer than k_eff candidates.
@@ -650,7 +665,8 @@ __device__ __forceinline__ uint32_t short_heads(const Params& p, int b, int g, u
   return *s_mask;
 }
 
-__device__ __forceinline__ void reselect_head(const Params& p, int bh, SelLds& L) {
+template <int ROWS>
+__device__ __forceinline__ void reselect_head(const Params& p, int bh, SelLds<ROWS>& L) {
   const HeadState st = p.state[bh];
   const SeqGeom sg = seq_geom(p, bh / p.H_q);
   const int u_lo = sg.lo / kUnit, nu = (sg.hi - 1) / kUnit + 1 - u_lo;
@@ -664,11 +680,53 @@ __device__ __forceinline__ void reselect_head(const Params& p, int bh, SelLds& L
   decide(p, bh, sg, gl, 32 + bit_length(span), 0u, L);
 }
 
-template <int G>
-__device__ __forceinline__ void rescan_block(const Params& p, int blk, int nblk, SelLds& S) {
-  __shared__ uint32_t s_last, s_mask;
+// Rescan of one unit for a group with short heads (mask), and the
+// reselect when it is the group's last.
+template <int G, int ROWS>
+__device__ __forceinline__ void rescan_unit(const Params& p, UnitRef ur, uint32_t mask,
+                                                      SelLds<ROWS>& S) {
+  __shared__ uint32_t s_last;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const Lane<G> L;
+  const int b = ur.b, g = ur.g;
+  const int bg = b * p.H_kv + g;
+  const SeqGeom sg = seq_geom(p, b);
+  const size_t bh = size_t(b) * p.H_q + size_t(g) * G + L.F;
+  const bool mine = (mask >> L.F) & 1u;
+  uint4 qreg[G];
+  load_q<G>(p, b, g, L, qreg);
+  const int u0 = ur.u * kUnit;
+  uint64_t* crow = p.cand + bh * p.n_cap + size_t(u0);
+  const int first = max(u0, sg.lo);
+  for (int jj = wave; jj < ur.npages; jj += kScanWaves) {
+    const int j = ur.u * kUnitPages + jj;
+    float z[G];
+    page_scores<G>(p, page_of(p, b, j), g, L, qreg, z);
+#pragma unroll
+    for (int s = 0; s < G; ++s) {
+      const int n = j * kPage + L.tok(s);
+      if (mine && n >= sg.lo && n < sg.hi && RA_IN(n - first < kUnit, p, 4))
+        crow[n - first] = (uint64_t(f2key(z[s])) << 32) | uint32_t(n);
+    }
+  }
+  // this unit's lists are complete: make them visible, then count it
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int units = ((sg.N + kPage - 1) / kPage + kUnitPages - 1) / kUnitPages;
+    s_last = atomicAdd(&p.gdone[bg], 1u) == uint32_t(units - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (s_last) {
+    __threadfence();  // see the lists the other blocks wrote
+    for (int hh = 0; hh < G; ++hh)
+      if ((mask >> hh) & 1u) reselect_head(p, b * p.H_q + g * G + hh, S);
+  }
+}
+
+template <int G, int ROWS>
+__device__ __forceinline__ void rescan_block(const Params& p, int blk, int nblk, SelLds<ROWS>& S) {
+  __shared__ uint32_t s_mask;
   const int64_t T = p.unit_off[p.B];
   const int64_t X0 = T * blk / nblk;
   const int64_t X1 = T * (blk + 1) / nblk;
@@ -676,65 +734,73 @@ __device__ __forceinline__ void rescan_block(const Params& p, int blk, int nblk,
   uint32_t mask = 0u;
   for (int64_t x = X0; x < X1; ++x) {
     const UnitRef ur = unit_at(p, x);
-    const int b = ur.b, g = ur.g;
-    const int bg = b * p.H_kv + g;
+    const int bg = ur.b * p.H_kv + ur.g;
     if (bg != cur) {  // block-uniform
-      mask = short_heads<G>(p, b, g, &s_mask);
+      mask = short_heads<G>(p, ur.b, ur.g, &s_mask);
       cur = bg;
     }
-    if (mask == 0u) continue;
-    const SeqGeom sg = seq_geom(p, b);
-    const size_t bh = size_t(b) * p.H_q + size_t(g) * G + L.F;
-    const bool mine = (mask >> L.F) & 1u;
-    uint4 qreg[G];
-    load_q<G>(p, b, g, L, qreg);
-    const int u0 = ur.u * kUnit;
-    uint64_t* crow = p.cand + bh * p.n_cap + size_t(u0);
-    const int first = max(u0, sg.lo);
-    for (int jj = wave; jj < ur.npages; jj += kScanWaves) {
-      const int j = ur.u * kUnitPages + jj;
-      float z[G];
-      page_scores<G>(p, page_of(p, b, j), g, L, qreg, z);
-#pragma unroll
-      for (int s = 0; s < G; ++s) {
-        const int n = j * kPage + L.tok(s);
-        if (mine && n >= sg.lo && n < sg.hi && RA_IN(n - first < kUnit, p, 4))
-          crow[n - first] = (uint64_t(f2key(z[s])) << 32) | uint32_t(n);
-      }
-    }
-    // this unit's lists are complete: make them visible, then count it
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int units = ((sg.N + kPage - 1) / kPage + kUnitPages - 1) / kUnitPages;
-      s_last = atomicAdd(&p.gdone[bg], 1u) == uint32_t(units - 1) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (s_last) {
-      __threadfence();  // see the lists the other blocks wrote
-      for (int hh = 0; hh < G; ++hh)
-        if ((mask >> hh) & 1u) reselect_head(p, b * p.H_q + g * G + hh, S);
-    }
+    if (mask != 0u) rescan_unit<G>(p, ur, mask, S);
   }
 }
 
+// SELECT: blocks 0 .. B * H_q - 1 select; RESCAN: the rest (all blocks
+// when not SELECT) rescan.
+template <int G, int NR, int ROWS, bool SELECT, bool RESCAN>
+__device__ __forceinline__ void select_body(const Params& p, SelLds<ROWS>& S) {
+  const int heads = SELECT ? p.B * p.H_q : 0;
+  if (SELECT && int(blockIdx.x) < heads) {
+    select_block<NR>(p, blockIdx.x, S);
+  } else if (RESCAN) {
+    // after a select launch of its own, whose blocks counted the short
+    // heads: with none, there is nothing to rescan
+    if (!SELECT && *p.any_dense == 0u) return;  // block-uniform
+    rescan_block<G>(p, int(blockIdx.x) - heads, int(gridDim.x) - heads, S);
+  }
+}
+
+// both kinds of blocks in one launch
 template <int G>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(Params p) {
-  __shared__ SelLds S;
-  const int heads = p.B * p.H_q;
-  if (int(blockIdx.x) < heads)
-    select_block(p, blockIdx.x, S);
-  else
-    rescan_block<G>(p, int(blockIdx.x) - heads, int(gridDim.x) - heads, S);
+  __shared__ SelLds<kStartRows> S;
+  select_body<G, kRegEntries, kStartRows, true, true>(p, S);
+}
+
+// For batches with more heads than CUs and budgets up to kNarrowKMax: the
+// select blocks alone, at most 128 registers per lane and 51 KB of LDS, two
+// per CU; the rescan follows in its own launch (its registers would not fit
+// beside them).
+template <int G>
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void select_kernel_narrow(Params p) {
+  __shared__ SelLds<kNarrowRows> S;
+  select_body<G, kNarrowEntries, kNarrowRows, true, false>(p, S);
+}
+
+template <int G>
+__global__ __launch_bounds__(kSelThreads) void rescan_kernel(Params p) {
+  __shared__ SelLds<kStartRows> S;
+  select_body<G, kRegEntries, kStartRows, false, true>(p, S);
+}
+
+template <int G>
+static void launch_select_g(const Params& p, hipStream_t s) {
+  const unsigned heads = unsigned(p.B * p.H_q);
+  const dim3 block{unsigned(kSelThreads)};
+  const int cus = p.num_cus > 0 ? p.num_cus : 256;
+  if (p.k_max <= kNarrowKMax && int64_t(heads) > cus) {
+    hipLaunchKernelGGL(select_kernel_narrow<G>, dim3(heads), block, 0, s, p);
+    hipLaunchKernelGGL(rescan_kernel<G>, dim3(scan_blocks(p)), block, 0, s, p);
+  } else {
+    hipLaunchKernelGGL(select_kernel<G>, dim3(heads + scan_blocks(p)), block, 0, s, p);
+  }
 }
 
 hipError_t launch_select(const Params& p, hipStream_t s) {
-  const dim3 grid{unsigned(p.B * p.H_q) + scan_blocks(p)}, block{unsigned(kSelThreads)};
   switch (p.G) {
-    case 1: hipLaunchKernelGGL(select_kernel<1>, grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL(select_kernel<2>, grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL(select_kernel<4>, grid, block, 0, s, p); break;
-    case 8: hipLaunchKernelGGL(select_kernel<8>, grid, block, 0, s, p); break;
+    case 1: launch_select_g<1>(p, s); break;
+    case 2: launch_select_g<2>(p, s); break;
+    case 4: launch_select_g<4>(p, s); break;
+    case 8: launch_select_g<8>(p, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
