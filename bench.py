@@ -7,11 +7,13 @@ query head and the static set n_sink=128 + window=512; seeded synthetic
 inputs (OOD queries vs keys, 64 planted needles per query head, x4 sink
 keys). Inputs are resident in HBM before timing starts.
 
-One step = every kernel of ra_decode_step (sample, threshold, scan, select,
-gather, merge). In the timed region a few steps (one in max(10, K/4)) are
-launched as three ra_decode_stages calls with HIP events around the scan
-stage only, so the scan kernel's own duration is measured live on the
-stream it runs on; the other steps are single calls. An event between two
+One step = every kernel of ra_decode_step (sample, scan, select, gather,
+merge; the scan computes the heads' candidate bounds itself, so the
+threshold stage launches nothing when it runs in the scan's call). In the
+timed region a few steps (one in max(10, K/4)) are launched as three
+ra_decode_stages calls with HIP events around the threshold and scan stages
+only, so the scan kernel's own duration is measured live on the stream it
+runs on; the other steps are single calls. An event between two
 kernels costs about 3 us of GPU time, so 20 more event-timed scans follow
 right after the timed region instead of perturbing it. Separate untimed
 passes give the per-step latency percentiles (an event at every step
@@ -45,7 +47,7 @@ PCT_STEPS = 50  # steps of the per-step latency pass
 # the scan kernel's sources: a committed counter profile is used only while
 # their hash matches the one recorded with it
 SCAN_SRCS = [os.path.join(ROOT, "top_sparse_attention_gqa_amd", "csrc", f)
-             for f in ("score_scan.hip", "page_scores.h", "ra_internal.h")]
+             for f in ("score_scan.hip", "page_scores.h", "sample_bound.h", "ra_internal.h")]
 
 
 PF_SRCS = [os.path.join(ROOT, "top_sparse_attention_gqa_amd", "csrc", f)
@@ -392,19 +394,29 @@ def run_layer(args):
             ra.decode_step_ex(*a)
             return
         # the same kernels in three calls, with events around the scan only
-        ra.decode_stages(*a, 0, S - 1)
+        # (the threshold stage rides with it: the scan computes the bounds)
+        ra.decode_stages(*a, ra.STAGE_SAMPLE, ra.STAGE_SAMPLE)
         ev[0].record()
-        ra.decode_stages(*a, S, S)
+        ra.decode_stages(*a, ra.STAGE_THRESHOLD, S)
         ev[1].record()
         ra.decode_stages(*a, S + 1, n_stage - 1)
+
+    # stage groups of the per-stage breakdown: the threshold stage runs in
+    # the scan's call, where the scan computes the heads' candidate bounds
+    # itself and no threshold kernel is launched
+    groups = [(ra.STAGE_SAMPLE, ra.STAGE_SAMPLE, "sample"),
+              (ra.STAGE_THRESHOLD, ra.STAGE_SCAN, "scan"),
+              (ra.STAGE_SELECT, ra.STAGE_SELECT, "select"),
+              (ra.STAGE_GATHER, ra.STAGE_GATHER, "gather"),
+              (ra.STAGE_MERGE, ra.STAGE_MERGE, "merge")]
 
     def step_staged(i, ev):
         L = layers[i % len(layers)]
         kv = kvs[i % len(layers)]
         a = (L.q, kv, seq, max_seq_len, kt, k_max, c.n_sink, c.window, out, lse, idx, ws)
         ev[0].record()
-        for s in range(n_stage):
-            ra.decode_stages(*a, s, s)
+        for s, (first, last, _) in enumerate(groups):
+            ra.decode_stages(*a, first, last)
             ev[s + 1].record()
 
     for i in range(args.warmup):
@@ -448,13 +460,14 @@ def run_layer(args):
 
     # per-stage breakdown (untimed for the headline figure)
     n_break = min(args.steps, 50)
-    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_stage + 1)] for _ in range(n_break)]
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(groups) + 1)]
+           for _ in range(n_break)]
     for i in range(n_break):
         step_staged(i, bev[i])
     torch.cuda.synchronize()
-    stage_ms = np.array([[e[s].elapsed_time(e[s + 1]) for s in range(n_stage)] for e in bev])
+    stage_ms = np.array([[e[s].elapsed_time(e[s + 1]) for s in range(len(groups))] for e in bev])
 
-    names = list(ra.STAGE_NAMES)
+    names = [name for _, _, name in groups]
 
     # algorithmic bytes from the retrieved sets of copy 0; its outputs are
     # what the cpu_baseline leg compares with the oracle
@@ -510,7 +523,7 @@ def run_layer(args):
         "step_ms_percentiles": dict(pct, steps=PCT_STEPS),
         "algorithmic_bytes": {"K": kb, "V": vb, "q_out_idx": small, "step": step_bytes},
         "stages_us": {n: round(float(stage_ms[:, i].mean()) * 1e3, 2) for i, n in enumerate(names)},
-        "roofline": {"kernel": "scan_kernel (score scan + candidate staging)",
+        "roofline": {"kernel": "scan_kernel (score scan with the candidate bounds + candidate staging)",
                      "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -584,9 +597,9 @@ def run_model(args):
                 ra.append_decode_step(kn, vn, pos_all[s], *a)
             else:
                 ra.kv_append(kvs[l], kn, vn, pos_all[s])
-                ra.decode_stages(*a, 0, S - 1)
+                ra.decode_stages(*a, ra.STAGE_SAMPLE, ra.STAGE_SAMPLE)
                 ev[2 * l].record()
-                ra.decode_stages(*a, S, S)
+                ra.decode_stages(*a, ra.STAGE_THRESHOLD, S)
                 ev[2 * l + 1].record()
                 ra.decode_stages(*a, S + 1, n_stage - 1)
 
@@ -660,7 +673,7 @@ def run_model(args):
         "step_frac_of_copy": round(step_gbps / copy_gbps, 4),
         "step_ms_percentiles": dict(pct, steps=args.steps),
         "algorithmic_bytes": {"K": kb, "V": vb, "q_out_idx_append": small, "step": step_bytes},
-        "roofline": {"kernel": "scan_kernel (score scan + candidate staging)",
+        "roofline": {"kernel": "scan_kernel (score scan with the candidate bounds + candidate staging)",
                      "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

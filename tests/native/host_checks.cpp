@@ -33,10 +33,12 @@
 static std::vector<std::string> g_calls;
 static ra::Params g_p;
 static ra::PfParams g_pf;
+static bool g_fused = true;  // what the scan_computes_bounds stub answers
 
 namespace ra {
 hipError_t launch_sample(const Params& p, hipStream_t) { g_calls.push_back("sample"); g_p = p; return hipSuccess; }
 hipError_t launch_threshold(const Params& p, hipStream_t) { g_calls.push_back("threshold"); g_p = p; return hipSuccess; }
+bool scan_computes_bounds(const Params&) { return g_fused; }
 hipError_t launch_scan(const Params& p, hipStream_t) { g_calls.push_back("scan"); g_p = p; return hipSuccess; }
 hipError_t launch_select(const Params& p, hipStream_t) { g_calls.push_back("select"); g_p = p; return hipSuccess; }
 hipError_t launch_gather(const Params& p, hipStream_t) { g_calls.push_back("gather"); g_p = p; return hipSuccess; }
@@ -175,27 +177,50 @@ static void decode_calls() {
   const int32_t* i32 = static_cast<const int32_t*>(at(2048));
   float* f32 = static_cast<float*>(at(4096));
   int32_t* oi = static_cast<int32_t*>(at(8192));
+  // the threshold launch is left out when the scan computes the bounds
+  g_fused = false;
   g_calls.clear();
   CHECK(ra_decode_step(q, H_q, &kv, i32, B, N, i32, K, 128, 512, f32, oi, ws, need, nullptr) == RA_OK);
   CHECK((g_calls == std::vector<std::string>{"sample", "threshold", "scan", "select", "gather", "merge"}));
+  CHECK(g_p.scan_bounds == 0);  // the scan finds the bounds published
+  g_calls.clear();
+  CHECK(ra_append_decode_step(q, q, i32, q, H_q, &kv, i32, B, N, i32, K, 128, 512, f32, nullptr,
+                              oi, ws, need, 0, nullptr) == RA_OK);
+  CHECK((g_calls == std::vector<std::string>{"sample", "threshold", "scan", "select", "gather", "merge"}));
+  g_fused = true;
+  g_calls.clear();
+  CHECK(ra_decode_step(q, H_q, &kv, i32, B, N, i32, K, 128, 512, f32, oi, ws, need, nullptr) == RA_OK);
+  CHECK((g_calls == std::vector<std::string>{"sample", "scan", "select", "gather", "merge"}));
+  CHECK(g_p.scan_bounds == 1);
+  // a scan in a call of its own computes whatever bounds are missing
+  g_calls.clear();
+  CHECK(ra_decode_stages(q, H_q, &kv, i32, B, N, i32, K, 128, 512, f32, nullptr, oi, ws, need, 0,
+                         RA_STAGE_SCAN, RA_STAGE_MERGE, nullptr) == RA_OK);
+  CHECK(g_calls.size() == 4 && g_p.scan_bounds == 1);
   check_params_in(g_p, ws, need);
   CHECK(g_p.lse == nullptr && g_p.keep_scores == 0 && g_p.app_pos == nullptr);
   CHECK(g_p.num_cus == 256 && g_p.G == 4);
   g_calls.clear();
   CHECK(ra_decode_step_ex(q, H_q, &kv, i32, B, N, i32, K, 0, 0, f32, f32, oi, ws, need,
                           RA_DECODE_KEEP_SCORES, nullptr) == RA_OK);
-  CHECK(g_calls.size() == 6 && g_p.keep_scores == 1 && g_p.lse == f32);
+  CHECK(g_calls.size() == 5 && g_p.keep_scores == 1 && g_p.lse == f32);
   g_calls.clear();
   CHECK(ra_append_decode_step(q, q, i32, q, H_q, &kv, i32, B, N, i32, K, 128, 512, f32, nullptr,
                               oi, ws, need, 0, nullptr) == RA_OK);
-  CHECK(g_calls.size() == 6 && g_p.app_pos == i32);
-  for (int a = 0; a < 6; ++a)
-    for (int b = a; b < 6; ++b) {
-      g_calls.clear();
-      CHECK(ra_decode_stages(q, H_q, &kv, i32, B, N, i32, K, 128, 512, f32, nullptr, oi, ws, need,
-                             0, a, b, nullptr) == RA_OK);
-      CHECK(int(g_calls.size()) == b - a + 1);
-    }
+  CHECK((g_calls == std::vector<std::string>{"sample", "scan", "select", "gather", "merge"}));
+  CHECK(g_p.app_pos == i32);
+  for (int fused = 0; fused < 2; ++fused)
+    for (int a = 0; a < 6; ++a)
+      for (int b = a; b < 6; ++b) {
+        g_fused = fused != 0;
+        g_calls.clear();
+        CHECK(ra_decode_stages(q, H_q, &kv, i32, B, N, i32, K, 128, 512, f32, nullptr, oi, ws, need,
+                               0, a, b, nullptr) == RA_OK);
+        // the threshold stage launches nothing when the scan follows in the call
+        const bool skipped = fused && a <= RA_STAGE_THRESHOLD && b >= RA_STAGE_SCAN;
+        CHECK(int(g_calls.size()) == b - a + 1 - (skipped ? 1 : 0));
+      }
+  g_fused = true;
   // invalid host arguments: nothing is launched
   g_calls.clear();
   CHECK(ra_decode_step(nullptr, H_q, &kv, i32, B, N, i32, K, 1, 1, f32, oi, ws, need, nullptr) == RA_ERR_INVALID_ARGUMENT);
@@ -219,7 +244,7 @@ static void decode_calls() {
   // the call without a workspace: its array, or RA_ERR_WORKSPACE past it
   g_calls.clear();
   CHECK(ra_decode_step_noalloc(q, H_q, &kv, i32, 1, 4096, i32, 64, 16, 64, f32, nullptr, oi, 0, nullptr) == RA_OK);
-  CHECK(g_calls.size() == 6);
+  CHECK(g_calls.size() == 5);
   check_params_in(g_p, reinterpret_cast<const char*>(g_p.scores), RA_NOALLOC_WS_BYTES);
   const size_t big = ra_decode_workspace_bytes(1, 32, 8, 1 << 20, 10485);
   CHECK(big > RA_NOALLOC_WS_BYTES);

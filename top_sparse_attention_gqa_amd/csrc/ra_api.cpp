@@ -306,7 +306,13 @@ ra_status ra_decode_stages(const uint16_t* q, int32_t H_q,
   static const Launcher stages[RA_STAGE_COUNT] = {
       launch_sample, launch_threshold, launch_scan,
       launch_select, launch_gather,    launch_merge};
+  // with the scan in the same call, the scan may compute the bounds; a scan
+  // that follows the threshold launch in the same call finds them published
+  const bool thr_here = first_stage <= RA_STAGE_THRESHOLD && last_stage >= RA_STAGE_THRESHOLD;
+  const bool fuse = thr_here && last_stage >= RA_STAGE_SCAN && scan_computes_bounds(p);
+  p.scan_bounds = (thr_here && !fuse) ? 0 : 1;
   for (int s = first_stage; s <= last_stage; ++s) {
+    if (s == RA_STAGE_THRESHOLD && fuse) continue;
     if (stages[s](p, stream) != hipSuccess) return RA_ERR_HIP;
   }
   return RA_OK;
@@ -335,7 +341,9 @@ ra_status ra_append_decode_step(const uint16_t* k_new, const uint16_t* v_new,
   p.app_k = k_new;
   p.app_v = v_new;
   p.app_pos = pos;
-  if (launch_sample(p, stream) != hipSuccess || launch_threshold(p, stream) != hipSuccess ||
+  p.scan_bounds = scan_computes_bounds(p) ? 1 : 0;
+  if (launch_sample(p, stream) != hipSuccess ||
+      (!p.scan_bounds && launch_threshold(p, stream) != hipSuccess) ||
       launch_scan(p, stream) != hipSuccess || launch_select(p, stream) != hipSuccess ||
       launch_gather(p, stream) != hipSuccess || launch_merge(p, stream) != hipSuccess)
     return RA_ERR_HIP;

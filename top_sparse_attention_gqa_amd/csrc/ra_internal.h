@@ -45,8 +45,11 @@ __host__ __device__ inline int sampled_pages(int P) {
 // The list of (head, unit u) starts at entry u * kUnit of the head's row and
 // has capacity kUnit, so it can hold every position of the unit.
 
-struct HeadState {
+struct alignas(8) HeadState {
+  // lo_key and lo_set form one 64-bit word, written once per call with a
+  // single atomic store once the bound is known (sample_bound.h)
   uint32_t lo_key;      // candidates are the members of M with key >= lo_key
+  uint32_t lo_set;      // 1: lo_key is this call's bound
   uint32_t max_w;       // order-preserving key of the largest score over W
   uint32_t max_m;       // ... over M (0 = no position seen)
   uint32_t dense;       // 1: too few candidates; rescanned with lo_key = 0
@@ -54,8 +57,9 @@ struct HeadState {
   // retrieved iff thr_shift < 64 and (c >> thr_shift) >= thr
   uint32_t thr_shift;
   uint32_t thr_lo, thr_hi;
-  uint32_t pad;
 };
+static_assert(sizeof(HeadState) == 32 && offsetof(HeadState, lo_set) == 4,
+              "the bound and its flag share the first 64-bit word");
 
 struct WsLayout {
   int64_t n_cap;    // row stride (positions), a multiple of kTile
@@ -112,6 +116,8 @@ struct Params {
   int32_t samp_cap;
   int32_t num_cus;
   int32_t keep_scores;  // also store the retrieved set's scores in the rows
+  int32_t scan_bounds;  // 1: the scan's blocks compute the heads' candidate
+                        // bounds up front (no threshold launch in this call)
 };
 
 // Prefill top-k (prefill_topk.hip).
@@ -201,6 +207,9 @@ hipError_t launch_select(const Params& p, hipStream_t s);  // + rescan of short 
 // Grid of the persistent unit loops (scan, rescan): one block per CU, at
 // most one per unit.
 unsigned scan_blocks(const Params& p);
+// True when the scan, run right after the sample, should compute the
+// heads' candidate bounds itself instead of a threshold launch.
+bool scan_computes_bounds(const Params& p);
 hipError_t launch_gather(const Params& p, hipStream_t s);
 hipError_t launch_merge(const Params& p, hipStream_t s);
 hipError_t launch_kv_append(const ra_kv_layer& kv, const uint16_t* k_new,

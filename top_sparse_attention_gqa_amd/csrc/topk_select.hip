@@ -9,11 +9,9 @@
 // score, then a lower position, and all composites are distinct, so "the
 // k_eff largest composites" is the unique tie-broken top-k.
 //
-// threshold (one block per head, before the scan): from the keys of the
-// sampled positions, a key at or just below the R-th largest sampled member
-// (its top 22 bits), with R a conservative stand-in for the rank of the k-th
-// largest member of M in the sample. Members at or above it are the head's
-// candidates.
+// threshold (one block per head, before the scan, when the scan does not
+// run in the same call): the head's candidate bound from its sampled keys
+// (sample_bound.h).
 //
 // select (one block per head, after the scan): if the per-unit candidate
 // lists hold at least k_eff entries, the top-k of M is the top-k of the
@@ -23,15 +21,14 @@
 // the dense stage rescans its group with every member of M as a candidate
 // and selects again.
 #include "page_scores.h"
+#include "sample_bound.h"
 
 namespace ra {
 
 constexpr int kSelThreads = 512;
 constexpr int kSubCap = 2048;     // LDS list for one radix sub-bucket
 constexpr uint32_t kRankMax = 256; // sub-buckets up to this size are finished by ranking
-constexpr int kBatch = 8;         // global entries per lane in flight per pass
 constexpr int kRegEntries = 64;   // candidate entries per lane kept in registers (wide select)
-constexpr int kRegKeys = 32;      // sampled keys per lane kept in registers
 constexpr int kStartRows = 4096;  // rows of 64 list entries whose first unit is tabled (wide)
 static_assert(kRegEntries * kSelThreads / 64 <= kStartRows, "register rows must be tabled");
 // The narrow select (select_kernel_narrow) holds 24 entries per lane and
@@ -192,49 +189,6 @@ struct RegLists {
   }
 };
 
-// Keys of a head's sampled positions in global memory; 0 marks a position
-// outside M (and is skipped).
-struct SampleKeys {
-  const uint32_t* keys;
-  uint32_t count;
-  template <typename Fn>
-  __device__ __forceinline__ void for_each(Fn&& fn) const {
-    for (uint32_t base = 0; base < count; base += blockDim.x * kBatch) {
-      uint32_t v[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const uint32_t i = base + u * blockDim.x + threadIdx.x;
-        v[u] = i < count ? keys[i] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) fn(uint64_t(v[u]), 0, v[u] != 0u);
-    }
-  }
-};
-
-// The same keys read once into registers.
-template <int NR>
-struct RegKeys {
-  uint32_t k[NR];
-  uint32_t count;
-  __device__ __forceinline__ void load(const uint32_t* keys, uint32_t n) {
-    count = n;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const uint32_t i = r * blockDim.x + threadIdx.x;
-      k[r] = i < count ? keys[i] : 0u;
-    }
-  }
-  template <typename Fn>
-  __device__ __forceinline__ void for_each(Fn&& fn) const {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      if (uint32_t(r) * blockDim.x >= count) break;  // uniform
-      fn(uint64_t(k[r]), 0, k[r] != 0u);
-    }
-  }
-};
-
 // Composites already reduced to one sub-bucket, in LDS.
 struct LdsSource {
   const uint64_t* c;
@@ -248,65 +202,6 @@ struct LdsSource {
     }
   }
 };
-
-struct Radix {
-  uint32_t* hist;  // LDS [2048]
-  uint32_t* s_d;   // LDS scalars: chosen digit, count above it, its count
-  uint32_t* s_above;
-  uint32_t* s_cnt;
-};
-
-// One radix pass: histogram the next w bits of the composites whose top
-// plen bits equal prefix, then pick the digit where the running count from
-// the top reaches need. Updates need/prefix/plen; returns the chosen digit's
-// population (all block threads get the same values).
-template <typename Src>
-__device__ __forceinline__ uint32_t radix_pass(const Src& src, const Radix& rx, int TB, uint32_t& need,
-                               uint64_t& prefix, int& plen) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int w = min(11, TB - plen);
-  const int shift = TB - plen - w;
-  for (int i = tid; i < 2048; i += blockDim.x) rx.hist[i] = 0;
-  __syncthreads();
-  const int pl = plen;
-  const uint64_t pf = prefix;
-  const uint32_t dmask = (1u << w) - 1u;
-  src.for_each([&](uint64_t c, int, bool valid) {
-    if (valid && (pl == 0 || (c >> (TB - pl)) == pf))
-      atomicAdd(&rx.hist[uint32_t(c >> shift) & dmask], 1u);
-  });
-  __syncthreads();
-  if (wave == 0) {
-    // lane l sums bins 32 l .. 32 l + 31 (starting at a lane-dependent bin,
-    // so that the lanes read different LDS banks); the lane where the count
-    // from the top reaches need owns the digit, found among its 32 bins in
-    // parallel
-    uint32_t s = 0;
-    for (int i = 0; i < 32; ++i) s += rx.hist[lane * 32 + ((i + lane) & 31)];
-    const uint32_t suf = wave_suffix_sum(s);
-    const uint64_t m = __ballot(suf >= need);
-    const int L = m ? 63 - __clzll(m) : 0;
-    const uint32_t above_l = __shfl(suf - s, L);
-    const uint32_t v = lane < 32 ? rx.hist[L * 32 + lane] : 0u;
-    const uint32_t fsuf = wave_suffix_sum(v) + above_l;
-    const uint64_t mf = __ballot(lane < 32 && fsuf >= need);
-    const int F = mf ? 63 - __clzll(mf) : 0;
-    if (lane == F) {
-      *rx.s_d = uint32_t(L * 32 + F);
-      *rx.s_above = fsuf - v;
-      *rx.s_cnt = v;
-    }
-  }
-  __syncthreads();
-  need -= *rx.s_above;
-  prefix = (prefix << w) | *rx.s_d;
-  plen += w;
-  const uint32_t cnt = *rx.s_cnt;
-  __syncthreads();
-  return cnt;
-}
 
 // Passes until the chosen digit's whole population is needed (or every bit
 // is fixed, where the population is one).
@@ -380,132 +275,16 @@ __device__ __forceinline__ void find_threshold(const Src& src, const Radix& rx, 
 // ---------------------------------------------------------------- threshold
 __device__ __forceinline__ int bit_length(uint32_t x) { return 32 - __clz(x); }
 
-// One block per head. Also resets the per-call state the later stages
-// accumulate into (head state, group flags, the rescan counter) and writes
-// the unit prefix the scan distributes its work by.
+// One block per head: the head's candidate bound, published in its state.
+// Left out when the scan runs in the same call: then the scan's blocks
+// compute the bounds themselves (score_scan.hip).
 __global__ __launch_bounds__(kSelThreads) void threshold_kernel(Params p) {
-  const int bh = blockIdx.x;
-  const int b = bh / p.H_q;
-  const int hq = bh - b * p.H_q;
-  const int tid = threadIdx.x;
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t s_d, s_above, s_cnt;
   __shared__ int64_t tmp[16];
-
-  if (p.app_pos != nullptr && hq % p.G == 0 && tid < 32) {
-    // the step's new token: the group's first head writes its K and V rows
-    // (lanes 0..15 K, 16..31 V, 16 bytes each). The sample kernel ran
-    // before and the scan runs after this launch: the sample only bounds
-    // the candidates (a stale row there costs at most the rescan), and
-    // everything that reads keys or values for the result comes later.
-    const int g = hq / p.G;
-    const int ps = p.app_pos[b];
-    if (ps >= 0 && ps < p.max_pages * kPage) {
-      const int pg = p.block_table[size_t(b) * p.max_pages + ps / kPage];
-      if ((unsigned)pg < (unsigned)p.num_pages) {
-        const int part = tid >> 4, c = tid & 15;
-        const uint16_t* src = (part ? p.app_v : p.app_k) + (size_t(b) * p.H_kv + g) * kHeadDim + c * 8;
-        uint16_t* dst = const_cast<uint16_t*>(part ? p.v_pool : p.k_pool) +
-                        ((size_t(pg) * p.H_kv + g) * kPage + (ps & (kPage - 1))) * kHeadDim + c * 8;
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-      }
-    }
-  }
-
-  if (bh == 0) {
-    // unit prefix over the batch
-    const int per = (p.B + kSelThreads - 1) / kSelThreads;
-    int64_t sum = 0;
-    for (int i = 0; i < per; ++i) {
-      const int bb = tid * per + i;
-      if (bb < p.B) {
-        const int P = (seq_geom(p, bb).N + kPage - 1) / kPage;
-        sum += int64_t(p.H_kv) * ((P + kUnitPages - 1) / kUnitPages);
-      }
-    }
-    int64_t total;
-    int64_t run = block_excl_scan(sum, tmp, &total);
-    for (int i = 0; i < per; ++i) {
-      const int bb = tid * per + i;
-      if (bb < p.B) {
-        const int P = (seq_geom(p, bb).N + kPage - 1) / kPage;
-        p.unit_off[bb] = run;
-        run += int64_t(p.H_kv) * ((P + kUnitPages - 1) / kUnitPages);
-      }
-    }
-    if (tid == 0) {
-      p.unit_off[p.B] = total;
-      *p.any_dense = 0u;
-    }
-  }
-  if (tid == 0 && hq % p.G == 0) p.gdone[size_t(b) * p.H_kv + hq / p.G] = 0u;
-  {
-    // the scan may reserve list slots with atomics: its counts start at zero
-    const int Pz = (seq_geom(p, b).N + kPage - 1) / kPage;
-    const int nuz = (Pz + kUnitPages - 1) / kUnitPages;
-    for (int u = tid; u < nuz; u += kSelThreads) p.ucnt[size_t(bh) * p.n_units + u] = 0u;
-  }
-
-  const SeqGeom sg = seq_geom(p, b);
-  uint32_t lo = 0xFFFFFFFFu;  // k_eff == 0: no candidates
-  if (sg.k_eff > 0) {
-    const int P = (sg.N + kPage - 1) / kPage;
-    const int ns = sampled_pages(P);
-    const int S = 1 << sample_log2(P);
-    const uint32_t* keys = p.samp + size_t(bh) * p.samp_cap;
-    const uint32_t count = uint32_t(ns * kPage);
-    RegKeys<kRegKeys> rk;
-    const bool in_regs = count <= uint32_t(kRegKeys * kSelThreads);
-    if (in_regs) rk.load(keys, count);  // in flight while the count below runs
-    // sampled members of M: overlap of every sampled page with [lo, hi)
-    int64_t c = 0;
-    for (int t = tid; t < ns; t += kSelThreads) {
-      const int j = (S >> 1) + t * S;
-      const int a = max(j * kPage, sg.lo), e = min(j * kPage + kPage, sg.hi);
-      c += e > a ? e - a : 0;
-    }
-    int64_t m_s;
-    block_excl_scan(c, tmp, &m_s);
-    const int64_t m_all = sg.hi - sg.lo;
-    uint32_t R;
-    if (m_s >= m_all) {
-      R = uint32_t(sg.k_eff);  // the sample is all of M: exact
-    } else {
-      const float kr = float(sg.k_eff) * float(m_s) / float(m_all);
-      R = uint32_t(ceilf(1.05f * kr + 5.0f * sqrtf(kr) + 8.0f));
-    }
-    if (m_s == 0 || int64_t(R) >= m_s) {
-      lo = 0u;  // keep every member of M
-    } else {
-      // the bound need not be exact, only at or below the R-th largest
-      // sampled key: two radix passes fix its top 22 bits
-      const Radix rx{hist, &s_d, &s_above, &s_cnt};
-      uint64_t prefix = 0;
-      int plen = 0;
-      uint32_t need = R;
-      if (in_regs) {
-        radix_pass(rk, rx, 32, need, prefix, plen);
-        radix_pass(rk, rx, 32, need, prefix, plen);
-      } else {
-        const SampleKeys sk{keys, count};
-        radix_pass(sk, rx, 32, need, prefix, plen);
-        radix_pass(sk, rx, 32, need, prefix, plen);
-      }
-      lo = uint32_t(prefix << (32 - plen));
-    }
-  }
-  if (tid == 0) {
-    HeadState st;
-    st.lo_key = lo;
-    st.max_w = 0u;
-    st.max_m = 0u;
-    st.dense = 0u;
-    st.thr_shift = 64u;  // nothing passes until select decides
-    st.thr_lo = 0xFFFFFFFFu;
-    st.thr_hi = 0xFFFFFFFFu;
-    st.pad = 0u;
-    p.state[bh] = st;
-  }
+  const Radix rx{hist, &s_d, &s_above, &s_cnt};
+  const uint32_t lo = head_bound(p, blockIdx.x, rx, tmp);
+  if (threadIdx.x == 0) publish_bound(p, blockIdx.x, lo);
 }
 
 hipError_t launch_threshold(const Params& p, hipStream_t s) {
