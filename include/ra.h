@@ -211,11 +211,17 @@ ra_status ra_append_decode_step(const uint16_t* k_new, const uint16_t* v_new,
  * sub-range of them with the same arguments, so each kernel can be timed or
  * inspected on its own. State passes between stages through `ws`, so a range
  * must start where the previous range on the same workspace ended.
+ * When a range holds both RA_STAGE_THRESHOLD and RA_STAGE_SCAN and the batch
+ * has at most one query head per scan block (one block per compute unit, at
+ * most one per 4096 positions of capacity per KV head), the scan computes
+ * the thresholds itself and RA_STAGE_THRESHOLD launches nothing; a scan run
+ * without the threshold stage before it computes any that are missing. The
+ * results are the same bit for bit either way.
  */
 typedef enum ra_stage {
-  RA_STAGE_SAMPLE = 0, /* score one page in S (S <= 64) of every sequence */
-  RA_STAGE_THRESHOLD = 1, /* per head: candidate threshold from the sample,
-                             reset of the per-call state */
+  RA_STAGE_SAMPLE = 0, /* score one page in S (S <= 64) of every sequence;
+                          reset of the per-call state */
+  RA_STAGE_THRESHOLD = 1, /* per head: candidate threshold from the sample */
   RA_STAGE_SCAN = 2,   /* all scores; keep W and the candidates above it */
   RA_STAGE_SELECT = 3, /* exact top-k threshold over the candidates, ties to
                           the lower position; heads with fewer candidates
