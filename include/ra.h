@@ -210,7 +210,10 @@ ra_status ra_append_decode_step(const uint16_t* k_new, const uint16_t* v_new,
  * stages RA_STAGE_SAMPLE .. RA_STAGE_MERGE; ra_decode_stages runs a contiguous
  * sub-range of them with the same arguments, so each kernel can be timed or
  * inspected on its own. State passes between stages through `ws`, so a range
- * must start where the previous range on the same workspace ended.
+ * must start where the previous range on the same workspace ended, and the
+ * inputs (q, the pools, lengths and budgets) must not change between the
+ * calls of one step: the scan takes the sampled pages' scores from the
+ * sample stage.
  * When a range holds both RA_STAGE_THRESHOLD and RA_STAGE_SCAN and the batch
  * has at most one query head per scan block (one block per compute unit, at
  * most one per 4096 positions of capacity per KV head), the scan computes

@@ -96,7 +96,7 @@ struct Params {
                        // when kept, or when the tile's lists overflow
                        // the gather's LDS staging
   uint32_t* samp;      // [B*H_q][samp_cap] keys of the sampled positions
-                       // (0: not a member of M)
+                       // (0: past the sequence's end)
   HeadState* state;    // [B*H_q]
   uint32_t* gdone;     // [B*H_kv] units of the group rescanned so far
   uint32_t* any_dense; // heads rescanned in this call

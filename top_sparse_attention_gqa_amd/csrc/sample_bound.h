@@ -20,11 +20,22 @@ namespace ra {
 constexpr int kBatch = 8;     // global entries per lane in flight per pass
 constexpr int kRegKeys = 32;  // sampled keys per lane kept in registers
 
-// Keys of a head's sampled positions in global memory; 0 marks a position
-// outside M (and is skipped).
+// Which sampled positions are members of M: slot i of a head's sample row
+// holds position (S / 2 + (i / 64) * S) * 64 + i % 64 (the row also keeps
+// the keys of W, which the scan uses).
+struct SampledM {
+  int sh, lo, hi;  // S = 1 << sh; M = [lo, hi)
+  __device__ __forceinline__ bool has(uint32_t i) const {
+    const int pos = (((1 << sh) >> 1) + int(i >> 6) * (1 << sh)) * kPage + int(i & 63u);
+    return pos >= lo && pos < hi;
+  }
+};
+
+// Keys of a head's sampled positions in global memory.
 struct SampleKeys {
   const uint32_t* keys;
   uint32_t count;
+  SampledM m;
   template <typename Fn>
   __device__ __forceinline__ void for_each(Fn&& fn) const {
     for (uint32_t base = 0; base < count; base += blockDim.x * kBatch) {
@@ -35,7 +46,10 @@ struct SampleKeys {
         v[u] = i < count ? keys[i] : 0u;
       }
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) fn(uint64_t(v[u]), 0, v[u] != 0u);
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t i = base + u * blockDim.x + threadIdx.x;
+        fn(uint64_t(v[u]), 0, i < count && m.has(i));
+      }
     }
   }
 };
@@ -45,8 +59,10 @@ template <int NR>
 struct RegKeys {
   uint32_t k[NR];
   uint32_t count;
-  __device__ __forceinline__ void load(const uint32_t* keys, uint32_t n) {
+  SampledM m;
+  __device__ __forceinline__ void load(const uint32_t* keys, uint32_t n, SampledM mm) {
     count = n;
+    m = mm;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const uint32_t i = r * blockDim.x + threadIdx.x;
@@ -58,7 +74,8 @@ struct RegKeys {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       if (uint32_t(r) * blockDim.x >= count) break;  // uniform
-      fn(uint64_t(k[r]), 0, k[r] != 0u);
+      const uint32_t i = r * blockDim.x + threadIdx.x;
+      fn(uint64_t(k[r]), 0, i < count && m.has(i));
     }
   }
 };
@@ -135,9 +152,10 @@ __device__ __forceinline__ uint32_t head_bound(const Params& p, int bh, const Ra
   const int S = 1 << sample_log2(P);
   const uint32_t* keys = p.samp + size_t(bh) * p.samp_cap;
   const uint32_t count = uint32_t(ns * kPage);
+  const SampledM sm{sample_log2(P), sg.lo, sg.hi};
   RegKeys<kRegKeys> rk;
   const bool in_regs = count <= uint32_t(kRegKeys) * blockDim.x;
-  if (in_regs) rk.load(keys, count);  // in flight while the count below runs
+  if (in_regs) rk.load(keys, count, sm);  // in flight while the count below runs
   // sampled members of M: overlap of every sampled page with [lo, hi)
   int64_t c = 0;
   for (int t = tid; t < ns; t += blockDim.x) {
@@ -165,7 +183,7 @@ __device__ __forceinline__ uint32_t head_bound(const Params& p, int bh, const Ra
     radix_pass(rk, rx, 32, need, prefix, plen);
     radix_pass(rk, rx, 32, need, prefix, plen);
   } else {
-    const SampleKeys sk{keys, count};
+    const SampleKeys sk{keys, count, sm};
     radix_pass(sk, rx, 32, need, prefix, plen);
     radix_pass(sk, rx, 32, need, prefix, plen);
   }

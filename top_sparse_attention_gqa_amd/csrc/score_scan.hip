@@ -105,7 +105,9 @@ __device__ __forceinline__ void batch_reset(const Params& p, int64_t* tmp) {
 
 // Grid (B * H_kv, chunks + 1): block (bg, c < chunks) scores the sampled
 // pages c * kSampleWaves .. of group bg, one page per wave, and stores the
-// keys of the sampled positions per head (0 for positions outside M); block
+// keys of the sampled positions per head (0 past the sequence's end; the
+// scan takes these pages' scores from here instead of reading them again);
+// block
 // (bg, chunks) resets the group's per-call state, and (0, chunks) also the
 // batch's, so that the sampling blocks do nothing else.
 template <int G>
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(Params p) {
   for (int s = 0; s < G; ++s) {
     const int pos = j * kPage + L.tok(s);
     if (RA_IN(size_t(t) * kPage + L.tok(s) < size_t(p.samp_cap), p, 3))
-      row[L.tok(s)] = (pos >= sg.lo && pos < sg.hi) ? f2key(z[s]) : 0u;
+      row[L.tok(s)] = pos < sg.N ? f2key(z[s]) : 0u;
   }
 }
 
@@ -312,6 +314,24 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
                           ? page_of(p, b, ur.u * kUnitPages + pa + wave + kScanWaves * L.lane)
                           : 0;
 
+    // Scores of page jj of the unit: a sampled page's come from its keys in
+    // the sample rows (the same function of the same K and q, so the same
+    // values), except the page of a token appended in this call, whose row
+    // the sample launch may have read before it was written
+    const int ssh = sample_log2((sg.N + kPage - 1) / kPage);
+    const int app_ps = p.app_pos != nullptr ? p.app_pos[b] : -1;
+    const int app_page = app_ps >= 0 ? app_ps / kPage : -1;
+    const uint32_t* krow = p.samp + (bh0 + L.F) * size_t(p.samp_cap);
+    auto scores = [&](int jj, int j, float (&z)[G]) {
+      if ((j & ((1 << ssh) - 1)) == ((1 << ssh) >> 1) && j != app_page) {  // wave-uniform
+        const size_t t = size_t(j >> ssh) * kPage;
+#pragma unroll
+        for (int s = 0; s < G; ++s)
+          z[s] = RA_IN(t + L.tok(s) < size_t(p.samp_cap), p, 3) ? key2f(krow[t + L.tok(s)]) : 0.0f;
+      } else {
+        page_scores<G>(p, __shfl(my_pg, (jj - pa - wave) / kScanWaves), g, L, qreg, z);
+      }
+    };
     // W score and running maxima of one scored position; true if it is a
     // member of M
     // (the maxima as value selects: conditional updates of the two were
@@ -359,7 +379,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
           bw = __hip_atomic_load(bound_slot(p, bh0 + L.lane), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
         float z[G];
-        page_scores<G>(p, __shfl(my_pg, (jj - pa - wave) / kScanWaves), g, L, qreg, z);
+        scores(jj, j, z);
 #pragma unroll
         for (int s = 0; s < G; ++s) {
           const int n = j * kPage + L.tok(s);
@@ -451,7 +471,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
     for (int jj = pr + wave; jj < pe; jj += kScanWaves) {
       const int j = ur.u * kUnitPages + jj;
       float z[G];
-      page_scores<G>(p, __shfl(my_pg, (jj - pa - wave) / kScanWaves), g, L, qreg, z);
+      scores(jj, j, z);
 #pragma unroll
       for (int s = 0; s < G; ++s) {
         const int n = j * kPage + L.tok(s);
