@@ -130,6 +130,32 @@ def algorithmic_bytes(c, lens, ks, idx_np, n_sink, window):
     return kb, vrows * 256, small
 
 
+def sample_stride(P):
+    """One page in S is sampled before the scan (page j with j % S == S / 2):
+    S is the largest power of two up to 64 that leaves at least 32 sampled
+    pages."""
+    s = 0
+    while s < 6 and (P >> (s + 1)) >= 32:
+        s += 1
+    return 1 << s
+
+
+def scan_read_bytes(lens, H_q, H_kv):
+    """What the scan itself reads: K of every page but the sampled ones, whose
+    scores it takes from the sample rows (4 B per slot and query head), plus
+    q. The sample kernel reads the sampled pages' K."""
+    total = 0
+    for n in lens:
+        P = (n + 63) // 64
+        S = sample_stride(P)
+        sampled = len(range(S // 2, P, S))
+        last = n - 64 * (P - 1)  # tokens on the last page
+        last_sampled = (P - 1) % S == S // 2
+        kpos = n - 64 * sampled - (last - 64 if last_sampled else 0)
+        total += kpos * H_kv * 256 + sampled * 64 * H_q * 4
+    return total + len(lens) * H_q * 256
+
+
 def traffic_from_profile(workload, name="score_scan", srcs=None):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter
     summary profiles/{name}_{workload}_pmc.json, scaled by the copy-kernel
@@ -477,7 +503,7 @@ def run_layer(args):
             idx.cpu().numpy())
     kb, vb, small = algorithmic_bytes(c, lens, ks, gpu0[2], c.n_sink, c.window)
     step_bytes = kb + vb + small
-    scan_bytes = kb + B * H_q * 256
+    scan_bytes = scan_read_bytes(lens, H_q, H_kv)
     scan_s = float(scan_ms.mean()) * 1e-3
     achieved = scan_bytes / scan_s / 1e9
     traffic = traffic_from_profile(args.workload)
@@ -635,8 +661,10 @@ def run_model(args):
                                       c.n_sink, c.window)
         kb, vb, small = kb + a, vb + b_, small + sm + 2 * H_kv * 256 * 2
     step_bytes = kb + vb + small
-    n_mean = N0 + args.warmup + (args.steps + 1) / 2.0
-    scan_bytes = int(n_mean * H_kv * 256 + H_q * 256)
+    # the event-timed scans run at lengths spread over the timed steps
+    timed_lens = [lens[args.warmup + i] for i in ev]
+    n_mean = N0 + args.warmup + (args.steps + 1) / 2.0  # mean length over the timed steps
+    scan_bytes = int(np.mean([scan_read_bytes([n], H_q, H_kv) for n in timed_lens]))
     scan_s = float(scan_ms.mean()) * 1e-3
     achieved = scan_bytes / scan_s / 1e9
     copy_gbps = copy_bandwidth(dev)
