@@ -15,7 +15,8 @@ and requires the outputs to be equal bit for bit, and the one-call step to
 match the fp64 oracle. The cases cover G = 1, 2, 4, 8 (with G = 8 a block
 holds 32 of a unit's 64 pages, so the unit's other half is scored after the
 bounds are known), ragged batches, the scan's page split, one head per
-block, and batches with four and eight heads per block."""
+block, batches with four and eight heads per block, and a sample too large
+for one block's registers."""
 
 import numpy as np
 import pytest
@@ -74,6 +75,9 @@ CASES = [
     ("one_bound_per_block", 4, 1, [4096] * 40, [50] * 40, 16, 64, 16384, False),
     ("four_bounds_per_block", 4, 1, [4096] * 40, [50] * 40, 16, 64, None, False),
     ("eight_bounds_per_block", 8, 1, [4096] * 41, [50] * 41, 16, 64, None, False),
+    # a sample past the registers (18,752 keys per head): one call launches
+    # the threshold stage, the scan alone streams the keys for its bound
+    ("streamed_sample", 4, 1, [1_200_000], [12000], 128, 512, None, False),
 ]
 
 

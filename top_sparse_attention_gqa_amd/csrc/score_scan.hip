@@ -546,9 +546,13 @@ unsigned scan_blocks(const Params& p) {
 // a launch of their own (measured: 3.4 us less per step for one 1M-token
 // Llama-3-8B layer, 2.4 us at 128K); with two per block (16 sequences of
 // 32 heads) every block starts streaming late and the threshold launch is
-// the faster one.
+// the faster one. The sample must also fit the registers of one block
+// (16,384 keys per head, lengths up to about 2^20 + 4,000): a bound over a
+// larger sample is streamed and takes longer than the blocks hold their
+// first pages.
 bool scan_computes_bounds(const Params& p) {
-  return int64_t(p.B) * p.H_q <= int64_t(scan_blocks(p));
+  return int64_t(p.B) * p.H_q <= int64_t(scan_blocks(p)) &&
+         int64_t(p.samp_cap) <= int64_t(kRegKeys) * kScanThreads;
 }
 
 hipError_t launch_scan(const Params& p, hipStream_t s) {
