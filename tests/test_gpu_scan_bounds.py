@@ -16,7 +16,8 @@ match the fp64 oracle. The cases cover G = 1, 2, 4, 8 (with G = 8 a block
 holds 32 of a unit's 64 pages, so the unit's other half is scored after the
 bounds are known), ragged batches, the scan's page split, one head per
 block, batches with four and eight heads per block, and a sample too large
-for one block's registers."""
+for one block's registers; a last case puts one sampled key far above the
+rest of the sample (about 200 times the bulk's scores)."""
 
 import numpy as np
 import pytest
@@ -100,3 +101,28 @@ def test_bounds_in_the_scan_equal_the_threshold_launch(name, H_q, H_kv, lens, ks
     assert one.rescanned == 0
     for b in sorted({0, len(lens) // 2, len(lens) - 1}):
         compare_sequence(L, one, b)
+
+
+def test_one_sampled_key_far_above_the_rest():
+    # one key on a sampled page scores about 200 times the bulk: the bound
+    # (the R-th largest sampled key's top bits) must not depend on how far
+    # the largest sampled key is from it
+    say("case scan_bounds far_top: N=32768 k=3000, one huge key on a sampled page")
+    L = synth.make_layer(4, 1, [32768], [3000], 16, 64, 2, 78, DEV)
+    P = 32768 // 64
+    s = 0
+    while s < 6 and (P >> (s + 1)) >= 32:
+        s += 1
+    j = (1 << s) // 2  # the first sampled page
+    qdir = L.q[0, 0:4].float().sum(0)
+    qdir = qdir / qdir.norm()
+    pg = int(L.block_table[0, j])
+    L.k_pool[pg, 0, 5] = (200.0 * qdir).to(torch.bfloat16)
+    one = gpu_decode(L)
+    for first_end in (ra.STAGE_THRESHOLD, ra.STAGE_SAMPLE):
+        out2, lse2, idx2 = two_call_step(L, 32768, first_end)
+        assert np.array_equal(one.out, out2, equal_nan=True), first_end
+        assert np.array_equal(one.idx, idx2), first_end
+    assert one.rescanned == 0
+    compare_sequence(L, one, 0)
+    assert (j * 64 + 5) in one.idx[0, 0]
