@@ -16,9 +16,9 @@ only, so the scan kernel's own duration is measured live on the stream it
 runs on; the other steps are single calls. An event between two
 kernels costs about 3 us of GPU time, so 20 more event-timed scans follow
 right after the timed region instead of perturbing it. Separate untimed
-passes give the per-step latency percentiles (an event at every step
-boundary), the per-stage breakdown (events between all stages) and a plain
-device copy's bandwidth. The cpu_baseline leg times the fp64 oracle on
+passes before the timed region give the per-step latency percentiles (an
+event at every step boundary) and the per-stage breakdown (events between
+the stage calls); a plain device copy's bandwidth is measured after it. The cpu_baseline leg times the fp64 oracle on
 a bounded sample and compares the benchmark's own outputs with it (the
 parity fields). Prints ONE JSON line.
 
@@ -449,6 +449,27 @@ def run_layer(args):
         step(i)
     torch.cuda.synchronize()
 
+    # The untimed passes run before the timed region, so that it starts on a
+    # GPU in its steady state (right after a few warmup steps the same steps
+    # measured about 2 % slower).
+    # per-step latency percentiles: an event at every step boundary
+    pev = [torch.cuda.Event(enable_timing=True) for _ in range(PCT_STEPS + 1)]
+    pev[0].record()
+    for i in range(PCT_STEPS):
+        step(i)
+        pev[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([pev[i].elapsed_time(pev[i + 1]) for i in range(PCT_STEPS)])
+
+    # per-stage breakdown (untimed for the headline figure)
+    n_break = min(args.steps, 50)
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(groups) + 1)]
+           for _ in range(n_break)]
+    for i in range(n_break):
+        step_staged(i, bev[i])
+    torch.cuda.synchronize()
+    stage_ms = np.array([[e[s].elapsed_time(e[s + 1]) for s in range(len(groups))] for e in bev])
+
     # The scan's launches are timed by events in the timed region on a few
     # steps (every IN_REGION_EVERY-th, those split in three calls around the
     # scan; the others are one call each): an event between two kernels
@@ -474,24 +495,6 @@ def run_layer(args):
     torch.cuda.synchronize()
     scan_in = [e[0].elapsed_time(e[1]) for e in events.values()]
     scan_ms = np.array(scan_in + [e[0].elapsed_time(e[1]) for e in after])
-
-    # per-step latency percentiles: an event at every step boundary
-    pev = [torch.cuda.Event(enable_timing=True) for _ in range(PCT_STEPS + 1)]
-    pev[0].record()
-    for i in range(PCT_STEPS):
-        step(i)
-        pev[i + 1].record()
-    torch.cuda.synchronize()
-    per_step = np.array([pev[i].elapsed_time(pev[i + 1]) for i in range(PCT_STEPS)])
-
-    # per-stage breakdown (untimed for the headline figure)
-    n_break = min(args.steps, 50)
-    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(groups) + 1)]
-           for _ in range(n_break)]
-    for i in range(n_break):
-        step_staged(i, bev[i])
-    torch.cuda.synchronize()
-    stage_ms = np.array([[e[s].elapsed_time(e[s + 1]) for s in range(len(groups))] for e in bev])
 
     names = [name for _, _, name in groups]
 
