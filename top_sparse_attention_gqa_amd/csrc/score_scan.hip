@@ -26,6 +26,7 @@
 namespace ra {
 
 constexpr int kStage = 6144;       // LDS candidate staging entries per block
+constexpr int kDeferUnits = 16;    // units whose candidates one burst may write
 constexpr int kSampleWaves = 8;    // sampled pages per sample block (one per wave)
 constexpr int kSampleThreads = kSampleWaves * 64;
 
@@ -204,6 +205,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
   __shared__ uint32_t s_lo[G];
   __shared__ uint32_t s_set[G];   // 1: s_lo holds the head's bound
   __shared__ uint32_t s_cnt[G];
+  __shared__ uint32_t s_ucnt[G][kDeferUnits];  // list slots taken per (head, staged unit)
   __shared__ uint32_t s_base[G];  // first slot the burst reserved in each head's list (page split)
   __shared__ uint32_t lmax[G][2];     // max key over W, over M
   __shared__ uint32_t r_d, r_above, r_cnt, s_flag;
@@ -237,6 +239,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
   __syncthreads();
   if (tid == 0) s_fill = 0;
   if (tid < G) s_cnt[tid] = 0;
+  for (int i = tid; i < G * kDeferUnits; i += kScanThreads) (&s_ucnt[0][0])[i] = 0u;
   if (tid < 2 * G) lmax[tid >> 1][tid & 1] = 0u;
 
   // Units split evenly over the blocks. For one sequence whose units do
@@ -253,6 +256,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
   const int64_t X1p = split ? TP * (blockIdx.x + 1) / NB : (T * (blockIdx.x + 1) / NB) * kUnitPages;
   const int64_t X0 = X0p / kUnitPages, X1 = (X1p + kUnitPages - 1) / kUnitPages;
   uint32_t mw = 0u, mm = 0u;  // running max keys of head F over W and M
+  int u_first = 0, nu_st = 0;  // staged units: u_first .. u_first + nu_st - 1 of one group
   int cur_b = -1, cur_g = -1;
   uint4 qreg[G];
   for (int64_t x = X0; x < X1; ++x) {
@@ -260,6 +264,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
     const int b = ur.b, g = ur.g;
     const SeqGeom sg = seq_geom(p, b);
     const size_t bh0 = size_t(b) * p.H_q + size_t(g) * G;
+    if (nu_st == 0) u_first = ur.u;
+    const int lu = nu_st;  // this unit among the staged ones (0 in a split scan)
     if (b != cur_b || g != cur_g) {
       if (cur_b >= 0) {
         // fold the maxima of the previous group
@@ -362,7 +368,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
         } else {
           // staging full: take a slot of the list at once
           const uint32_t slot = split ? atomicAdd(&p.ucnt[(bh0 + L.F) * p.n_units + ur.u], 1u)
-                                      : atomicAdd(&s_cnt[L.F], 1u);
+                                      : atomicAdd(&s_ucnt[L.F][lu], 1u);
           if (RA_IN(slot < uint32_t(kUnit), p, 1))
             crow[slot] = (uint64_t(key) << 32) | uint32_t(n);
         }
@@ -458,7 +464,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
               } else {
                 // staging full: take a slot of the list at once
                 const uint32_t slot = split ? atomicAdd(&p.ucnt[(bh0 + L.F) * p.n_units + ur.u], 1u)
-                                            : atomicAdd(&s_cnt[L.F], 1u);
+                                            : atomicAdd(&s_ucnt[L.F][lu], 1u);
                 if (RA_IN(slot < uint32_t(kUnit), p, 1))
                   crow[slot] = (uint64_t(key) << 32) | uint32_t(n);
               }
@@ -484,27 +490,56 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
     // burst the staged candidates into the (head, unit) lists; streaming
     // stores, since cached writes interleaved with the K stream cost it
     // about twice as much time
-    const uint32_t nst = min(s_fill, uint32_t(kStage));
     if (split) {
+      // a unit two blocks share: its slots are reserved with global atomics,
+      // one burst per unit
+      const uint32_t nst = min(s_fill, uint32_t(kStage));
       if (tid < G) {
         s_base[tid] = s_cnt[tid] ? atomicAdd(&p.ucnt[(bh0 + tid) * p.n_units + ur.u], s_cnt[tid]) : 0u;
         s_cnt[tid] = 0;
       }
       __syncthreads();
+      for (uint32_t i = tid; i < nst; i += kScanThreads) {
+        const uint32_t nh = st_nh[i];
+        const uint32_t hh = nh >> 27;
+        const uint32_t slot = s_base[hh] + atomicAdd(&s_cnt[hh], 1u);
+        if (RA_IN(slot < uint32_t(kUnit), p, 0))
+          __builtin_nontemporal_store((uint64_t(st_key[i]) << 32) | (nh & ((1u << 27) - 1u)),
+                                      &p.cand[(bh0 + hh) * p.n_cap + ubase + slot]);
+      }
+      __syncthreads();
+      if (tid < G) s_cnt[tid] = 0;
+      if (tid == 0) s_fill = 0;
+      continue;
     }
+    // The block owns its units: the staging is kept over several units of
+    // the group and written in one burst when the group ends, the block's
+    // last unit is done, kDeferUnits units are staged or it is half full
+    // (each burst stalls the block's K stream on its barriers).
+    ++nu_st;
+    const bool next_here = x + 1 < X1 && (ur.u + 1) * kUnitPages < (sg.N + kPage - 1) / kPage;
+    if (next_here && nu_st < kDeferUnits && s_fill <= uint32_t(kStage / 2)) continue;  // block-uniform
+    const uint32_t nst = min(s_fill, uint32_t(kStage));
     for (uint32_t i = tid; i < nst; i += kScanThreads) {
       const uint32_t nh = st_nh[i];
       const uint32_t hh = nh >> 27;
-      const uint32_t slot = (split ? s_base[hh] : 0u) + atomicAdd(&s_cnt[hh], 1u);
-      if (RA_IN(slot < uint32_t(kUnit), p, 0))
-        __builtin_nontemporal_store((uint64_t(st_key[i]) << 32) | (nh & ((1u << 27) - 1u)),
-                                    &p.cand[(bh0 + hh) * p.n_cap + ubase + slot]);
+      const uint32_t n = nh & ((1u << 27) - 1u);
+      const int su = int(n / uint32_t(kUnit)) - u_first;  // staged unit of the entry
+      if (RA_IN(su >= 0 && su < nu_st, p, 0)) {
+        const uint32_t slot = atomicAdd(&s_ucnt[hh][su], 1u);
+        if (RA_IN(slot < uint32_t(kUnit), p, 0))
+          __builtin_nontemporal_store((uint64_t(st_key[i]) << 32) | n,
+                                      &p.cand[(bh0 + hh) * p.n_cap +
+                                              size_t(u_first + su) * kUnit + slot]);
+      }
     }
     __syncthreads();
-    if (tid < G) {
-      if (!split) p.ucnt[(bh0 + tid) * p.n_units + ur.u] = s_cnt[tid];
-      s_cnt[tid] = 0;
+    for (int i = tid; i < G * nu_st; i += kScanThreads) {
+      const int hh = i / nu_st, su = i - hh * nu_st;
+      p.ucnt[(bh0 + hh) * p.n_units + u_first + su] = s_ucnt[hh][su];
+      s_ucnt[hh][su] = 0u;
     }
+    nu_st = 0;
     if (tid == 0) s_fill = 0;
   }
   if (cur_b >= 0) {
