@@ -25,7 +25,7 @@
 
 namespace ra {
 
-constexpr int kStage = 6144;       // LDS candidate staging entries per block
+constexpr int kStage = 8192;       // LDS candidate staging entries per block
 constexpr int kDeferUnits = 16;    // units whose candidates one burst may write
 constexpr int kSampleWaves = 8;    // sampled pages per sample block (one per wave)
 constexpr int kSampleThreads = kSampleWaves * 64;
@@ -257,6 +257,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
   const int64_t X0 = X0p / kUnitPages, X1 = (X1p + kUnitPages - 1) / kUnitPages;
   uint32_t mw = 0u, mm = 0u;  // running max keys of head F over W and M
   int u_first = 0, nu_st = 0;  // staged units: u_first .. u_first + nu_st - 1 of one group
+  bool sync_top = true;        // LDS state changed since the last barrier
   int cur_b = -1, cur_g = -1;
   uint4 qreg[G];
   for (int64_t x = X0; x < X1; ++x) {
@@ -300,8 +301,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
         s_lo[tid] = lo;
       }
       load_q<G>(p, b, g, L, qreg);
+      sync_top = true;
     }
-    __syncthreads();
+    // between two units of a group whose candidates stay staged, the
+    // waves run on without meeting
+    if (sync_top) __syncthreads();
+    sync_top = false;
     bool ready = true;  // block-uniform: every bound of the group is known
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) ready = ready && s_set[hh] != 0u;
@@ -486,13 +491,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
         stage(in_m && key >= lo_f, key, n);
       }
     }
-    __syncthreads();
     // burst the staged candidates into the (head, unit) lists; streaming
     // stores, since cached writes interleaved with the K stream cost it
     // about twice as much time
     if (split) {
-      // a unit two blocks share: its slots are reserved with global atomics,
-      // one burst per unit
+      // a split scan reserves the list slots of each unit with global
+      // atomics (two blocks may share it) and writes one burst per unit
+      // (kept over several units, its bursts measured slower: 335 against
+      // 325 us per scan for the 32-layer workload at 2^20 + 1000 tokens)
+      __syncthreads();
       const uint32_t nst = min(s_fill, uint32_t(kStage));
       if (tid < G) {
         s_base[tid] = s_cnt[tid] ? atomicAdd(&p.ucnt[(bh0 + tid) * p.n_units + ur.u], s_cnt[tid]) : 0u;
@@ -510,15 +517,24 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
       __syncthreads();
       if (tid < G) s_cnt[tid] = 0;
       if (tid == 0) s_fill = 0;
+      sync_top = true;
       continue;
     }
-    // The block owns its units: the staging is kept over several units of
-    // the group and written in one burst when the group ends, the block's
-    // last unit is done, kDeferUnits units are staged or it is half full
-    // (each burst stalls the block's K stream on its barriers).
+    // Otherwise the block owns its units: their candidates stay staged over
+    // several units of the group and are written in one burst when the
+    // group ends, the block is done, or as many units are staged as the
+    // staging holds at twice the expected candidate rate (the sampled bound
+    // passes about 1.5 k_eff per head). Each burst stops the block's waves
+    // at two barriers; between bursts they do not meet.
     ++nu_st;
-    const bool next_here = x + 1 < X1 && (ur.u + 1) * kUnitPages < (sg.N + kPage - 1) / kPage;
-    if (next_here && nu_st < kDeferUnits && s_fill <= uint32_t(kStage / 2)) continue;  // block-uniform
+    const int np_seq = (sg.N + kPage - 1) / kPage;
+    const int np_next = min(kUnitPages, np_seq - (ur.u + 1) * kUnitPages);
+    const bool next_here = x + 1 < X1 && np_next > 0;
+    const int64_t per_unit =
+        int64_t(G) * 2 * sg.k_eff / ((np_seq + kUnitPages - 1) / kUnitPages) + 64;
+    const int n_defer = int(max<int64_t>(1, min<int64_t>(kDeferUnits, (kStage * 5 / 8) / per_unit)));
+    if (next_here && nu_st < n_defer) continue;  // block-uniform
+    __syncthreads();
     const uint32_t nst = min(s_fill, uint32_t(kStage));
     for (uint32_t i = tid; i < nst; i += kScanThreads) {
       const uint32_t nh = st_nh[i];
@@ -541,6 +557,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
     }
     nu_st = 0;
     if (tid == 0) s_fill = 0;
+    sync_top = true;
   }
   if (cur_b >= 0) {
     const size_t pbh0 = size_t(cur_b) * p.H_q + size_t(cur_g) * G;
