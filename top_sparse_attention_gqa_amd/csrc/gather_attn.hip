@@ -30,8 +30,8 @@
 // merge: per query head, one block combines the partials,
 // out = sum_t e^{m_t - m} N_t / sum_t e^{m_t - m} Z_t, lse = m + ln(...),
 // and pads out_idx with -1 after k_eff; further blocks each copy the
-// retrieved positions of kMergeTiles tiles into out_idx at the offset the
-// counts of the tiles before them give.
+// retrieved positions of up to kMergeTiles tiles into out_idx at the
+// offset the counts of the tiles before them give.
 #include "ra_internal.h"
 
 namespace ra {
@@ -452,20 +452,34 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeGroups = kMergeThreads / 32;
 constexpr int kMergeDepth = 16;
 constexpr int kMergeUnroll = 4;  // positions per thread in flight in the copy
-constexpr int kMergeTiles = 8;   // tiles per out_idx copy block
+constexpr int kMergeTiles = 8;   // most tiles per out_idx copy block
+constexpr int kCopySlots = kMergeThreads * kMergeUnroll;
 
-// out_idx for tiles [c * kMergeTiles, (c + 1) * kMergeTiles) of head bh.
-// Every count the block needs is loaded in one round: thread t holds tile
-// t's count, the tiles before ta are summed, the block's own go to LDS.
-__device__ void copy_positions(const Params& p, int bh, int c, int nt, int tile) {
+// out_idx for tiles [c * tpb, (c + 1) * tpb) of head bh. One round of loads
+// brings every count the block needs (thread t holds tile t's count; the
+// tiles before ta are summed, the block's own go to LDS) together with the
+// first kCopySlots / tpb positions of each of its tiles, read before their
+// counts are known; positions past a count are dropped, and only a tile
+// with more than that many takes a second round for the rest.
+__device__ void copy_positions(const Params& p, int bh, int c, int nt, int tile, int tpb) {
   const int tid = threadIdx.x;
-  const int ta = c * kMergeTiles;
+  const int ta = c * tpb;
   if (ta >= nt) return;
-  const int tb = min(nt, ta + kMergeTiles);
+  const int tb = min(nt, ta + tpb);
+  const uint32_t spt = uint32_t(kCopySlots / tpb);  // positions per tile read up front
   __shared__ uint32_t s_pre[kMergeTiles + 1];
   __shared__ uint32_t s_own[kMergeTiles];
   __shared__ uint32_t s_part[kMergeThreads / 64];
   const uint32_t* sc = p.scnt + size_t(bh) * p.n_tiles;
+  const int32_t* src = reinterpret_cast<const int32_t*>(p.cand + size_t(bh) * p.n_cap);
+  int32_t spec[kMergeUnroll];
+#pragma unroll
+  for (int u = 0; u < kMergeUnroll; ++u) {
+    const uint32_t e = uint32_t(u * kMergeThreads + tid);
+    const int j = int(e / spt);
+    const uint32_t i = e - uint32_t(j) * spt;  // < spt <= 2 * tile
+    spec[u] = ta + j < tb ? src[size_t(ta + j) * (2 * tile) + i] : 0;
+  }
   // offset: retrieved positions of the tiles before ta
   uint32_t before = 0;
   for (int t = tid; t < tb; t += kMergeThreads) {
@@ -487,40 +501,36 @@ __device__ void copy_positions(const Params& p, int bh, int c, int nt, int tile)
   __syncthreads();
   uint32_t off = 0;
   for (int w = 0; w < kMergeThreads / 64; ++w) off += s_part[w];
-  const uint32_t total = s_pre[tb - ta];
-  int32_t* dst = p.out_idx + size_t(bh) * p.k_max;
-  const int32_t* src = reinterpret_cast<const int32_t*>(p.cand + size_t(bh) * p.n_cap);
-  for (uint32_t base = 0; base < total; base += kMergeThreads * kMergeUnroll) {
-    int32_t v[kMergeUnroll];
-    uint32_t at[kMergeUnroll];
+  int32_t* dst = p.out_idx + size_t(bh) * p.k_max + off;
 #pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) {
-      const uint32_t i = base + u * kMergeThreads + tid;
-      int j = 0;
-      while (j + 1 < tb - ta && s_pre[j + 1] <= i) ++j;
-      at[u] = off + i;
-      v[u] = i < total && RA_IN(i - s_pre[j] < uint32_t(2 * tile), p, 8)
-                 ? src[size_t(ta + j) * (2 * tile) + (i - s_pre[j])]
-                 : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) {
-      const uint32_t i = base + u * kMergeThreads + tid;
-      if (i < total && RA_GUARD(at[u] < uint32_t(p.k_max), p, 9)) dst[at[u]] = v[u];
+  for (int u = 0; u < kMergeUnroll; ++u) {
+    const uint32_t e = uint32_t(u * kMergeThreads + tid);
+    const int j = int(e / spt);
+    const uint32_t i = e - uint32_t(j) * spt;
+    if (ta + j < tb && i < s_own[j] && RA_GUARD(off + s_pre[j] + i < uint32_t(p.k_max), p, 9))
+      dst[s_pre[j] + i] = spec[u];
+  }
+  // the rest of the tiles holding more than spt positions
+  for (int j = 0; j < tb - ta; ++j) {
+    const uint32_t cnt = s_own[j];
+    for (uint32_t i = spt + uint32_t(tid); i < cnt; i += kMergeThreads) {
+      const int32_t v = RA_IN(i < uint32_t(2 * tile), p, 8) ? src[size_t(ta + j) * (2 * tile) + i] : 0;
+      if (RA_GUARD(off + s_pre[j] + i < uint32_t(p.k_max), p, 9)) dst[s_pre[j] + i] = v;
     }
   }
 }
 
 // Grid (1 + copy blocks, B * H_q): x == 0 merges the partials of head y,
-// x > 0 copies positions. tile_units: the gather's tile size, in units.
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p, int tile_units) {
+// x > 0 copies positions. tile_units: the gather's tile size, in units;
+// tpb: tiles per copy block.
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p, int tile_units, int tpb) {
   const int bh = blockIdx.y;
   const int b = bh / p.H_q;
   const SeqGeom sg = seq_geom(p, b);
   const int tile = tile_units * kUnit;
   const int nt = (sg.N + tile - 1) / tile;
   if (blockIdx.x > 0) {
-    if (p.k_max > 0 && sg.k_eff > 0) copy_positions(p, bh, int(blockIdx.x) - 1, nt, tile);
+    if (p.k_max > 0 && sg.k_eff > 0) copy_positions(p, bh, int(blockIdx.x) - 1, nt, tile, tpb);
     return;
   }
   const int tid = threadIdx.x;
@@ -601,12 +611,24 @@ static int64_t gather_tiles(const Params& p, int upt) {
   return std::max<int64_t>(1, std::min<int64_t>((cap + tile - 1) / tile, p.n_tiles));
 }
 
+// Tiles per copy block: as many as leave about 1.5 times a tile's mean
+// share of k_max in the positions read up front (at most kMergeTiles, a
+// power of two so the up-front slots divide evenly).
+static int merge_tiles_per_block(const Params& p, int upt) {
+  const int64_t nt = gather_tiles(p, upt);
+  const int64_t per_tile = (3 * int64_t(p.k_max)) / (2 * nt) + 1;
+  int tpb = kMergeTiles;
+  while (tpb > 1 && int64_t(kCopySlots / tpb) < per_tile) tpb >>= 1;
+  return tpb;
+}
+
 hipError_t launch_merge(const Params& p, hipStream_t s) {
   const int upt = gather_tile_units(p);
+  const int tpb = merge_tiles_per_block(p, upt);
   const unsigned copies =
-      p.k_max > 0 ? unsigned((gather_tiles(p, upt) + kMergeTiles - 1) / kMergeTiles) : 0u;
+      p.k_max > 0 ? unsigned((gather_tiles(p, upt) + tpb - 1) / tpb) : 0u;
   hipLaunchKernelGGL(merge_kernel, dim3(1 + copies, unsigned(p.B * p.H_q)), dim3(kMergeThreads), 0,
-                     s, p, upt);
+                     s, p, upt, tpb);
   return hipGetLastError();
 }
 
