@@ -444,29 +444,29 @@ void gather_kernel(Params p) {
 
 // ---------------------------------------------------------------- merge
 // One block per (sequence, query head): 8 groups of 32 threads each take
-// every 8th partial, 4 dims per thread (float4 loads issued kMergeDepth
-// deep, so up to 128 tiles take one round trip, together with the head
-// state that gives the partials' common reference), then the groups are
-// summed in LDS in a fixed order.
+// every 8th partial, 4 dims per thread (float4 loads issued DEPTH deep, so
+// up to 8 * DEPTH tiles take one round trip, together with the head state
+// that gives the partials' common reference), then the groups are summed
+// in LDS in a fixed order.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeGroups = kMergeThreads / 32;
-constexpr int kMergeDepth = 16;
-constexpr int kMergeUnroll = 4;  // positions per thread in flight in the copy
+constexpr int kMergeUnroll = 8;  // positions per thread in flight in the copy
 constexpr int kMergeTiles = 8;   // most tiles per out_idx copy block
 constexpr int kCopySlots = kMergeThreads * kMergeUnroll;
 
 // out_idx for tiles [c * tpb, (c + 1) * tpb) of head bh. One round of loads
 // brings every count the block needs (thread t holds tile t's count; the
 // tiles before ta are summed, the block's own go to LDS) together with the
-// first kCopySlots / tpb positions of each of its tiles, read before their
-// counts are known; positions past a count are dropped, and only a tile
-// with more than that many takes a second round for the rest.
-__device__ void copy_positions(const Params& p, int bh, int c, int nt, int tile, int tpb) {
+// first spt = 2^spt_log2 positions of each of its tiles (tpb * spt <=
+// kCopySlots), read before their counts are known; positions past a count
+// are dropped, and only a tile with more than spt takes a second round.
+__device__ void copy_positions(const Params& p, int bh, int c, int nt, int tile, int tpb,
+                               int spt_log2) {
   const int tid = threadIdx.x;
   const int ta = c * tpb;
   if (ta >= nt) return;
   const int tb = min(nt, ta + tpb);
-  const uint32_t spt = uint32_t(kCopySlots / tpb);  // positions per tile read up front
+  const uint32_t spt = 1u << spt_log2;  // positions per tile read up front
   __shared__ uint32_t s_pre[kMergeTiles + 1];
   __shared__ uint32_t s_own[kMergeTiles];
   __shared__ uint32_t s_part[kMergeThreads / 64];
@@ -476,8 +476,8 @@ __device__ void copy_positions(const Params& p, int bh, int c, int nt, int tile,
 #pragma unroll
   for (int u = 0; u < kMergeUnroll; ++u) {
     const uint32_t e = uint32_t(u * kMergeThreads + tid);
-    const int j = int(e / spt);
-    const uint32_t i = e - uint32_t(j) * spt;  // < spt <= 2 * tile
+    const int j = int(e >> spt_log2);
+    const uint32_t i = e & (spt - 1u);  // < spt <= 2 * tile
     spec[u] = ta + j < tb ? src[size_t(ta + j) * (2 * tile) + i] : 0;
   }
   // offset: retrieved positions of the tiles before ta
@@ -505,8 +505,8 @@ __device__ void copy_positions(const Params& p, int bh, int c, int nt, int tile,
 #pragma unroll
   for (int u = 0; u < kMergeUnroll; ++u) {
     const uint32_t e = uint32_t(u * kMergeThreads + tid);
-    const int j = int(e / spt);
-    const uint32_t i = e - uint32_t(j) * spt;
+    const int j = int(e >> spt_log2);
+    const uint32_t i = e & (spt - 1u);
     if (ta + j < tb && i < s_own[j] && RA_GUARD(off + s_pre[j] + i < uint32_t(p.k_max), p, 9))
       dst[s_pre[j] + i] = spec[u];
   }
@@ -523,14 +523,18 @@ __device__ void copy_positions(const Params& p, int bh, int c, int nt, int tile,
 // Grid (1 + copy blocks, B * H_q): x == 0 merges the partials of head y,
 // x > 0 copies positions. tile_units: the gather's tile size, in units;
 // tpb: tiles per copy block.
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p, int tile_units, int tpb) {
+// DEPTH: partials per thread group in flight; 8 groups take 8 * DEPTH tiles
+// per round trip, and a smaller DEPTH leaves room for more resident blocks.
+template <int DEPTH>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p, int tile_units, int tpb,
+                                                              int spt_log2) {
   const int bh = blockIdx.y;
   const int b = bh / p.H_q;
   const SeqGeom sg = seq_geom(p, b);
   const int tile = tile_units * kUnit;
   const int nt = (sg.N + tile - 1) / tile;
   if (blockIdx.x > 0) {
-    if (p.k_max > 0 && sg.k_eff > 0) copy_positions(p, bh, int(blockIdx.x) - 1, nt, tile, tpb);
+    if (p.k_max > 0 && sg.k_eff > 0) copy_positions(p, bh, int(blockIdx.x) - 1, nt, tile, tpb, spt_log2);
     return;
   }
   const int tid = threadIdx.x;
@@ -550,11 +554,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p, int tile
   float Z = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   {
-    for (int j0 = grp; j0 < np; j0 += kMergeGroups * kMergeDepth) {
-      float2 w2[kMergeDepth];
-      float4 v[kMergeDepth];
+    for (int j0 = grp; j0 < np; j0 += kMergeGroups * DEPTH) {
+      float2 w2[DEPTH];
+      float4 v[DEPTH];
 #pragma unroll
-      for (int u = 0; u < kMergeDepth; ++u) {
+      for (int u = 0; u < DEPTH; ++u) {
         const int j = j0 + u * kMergeGroups;
         const int t = slot(j);
         w2[u] = j < np ? *reinterpret_cast<const float2*>(mz + 2 * t) : make_float2(0.f, 0.f);
@@ -562,7 +566,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p, int tile
                       : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
-      for (int u = 0; u < kMergeDepth; ++u) {
+      for (int u = 0; u < DEPTH; ++u) {
         // e^{m_t - m}: 1 for every non-empty partial here, kept general
         const float sc = w2[u].y > 0.0f ? expf(w2[u].x - m) : 0.0f;
         Z += sc * w2[u].y;
@@ -611,24 +615,30 @@ static int64_t gather_tiles(const Params& p, int upt) {
   return std::max<int64_t>(1, std::min<int64_t>((cap + tile - 1) / tile, p.n_tiles));
 }
 
-// Tiles per copy block: as many as leave about 1.5 times a tile's mean
-// share of k_max in the positions read up front (at most kMergeTiles, a
-// power of two so the up-front slots divide evenly).
-static int merge_tiles_per_block(const Params& p, int upt) {
+// Positions per tile read up front: the power of two at or above 1.5 times
+// a tile's mean share of k_max (at most kCopySlots); tiles per copy block:
+// as many as those slots allow, up to kMergeTiles.
+static void merge_copy_shape(const Params& p, int upt, int* tpb, int* spt_log2) {
   const int64_t nt = gather_tiles(p, upt);
   const int64_t per_tile = (3 * int64_t(p.k_max)) / (2 * nt) + 1;
-  int tpb = kMergeTiles;
-  while (tpb > 1 && int64_t(kCopySlots / tpb) < per_tile) tpb >>= 1;
-  return tpb;
+  int sl = 0;
+  while ((int64_t(1) << sl) < per_tile && (1 << sl) < kCopySlots) ++sl;
+  *spt_log2 = sl;
+  *tpb = std::max(1, std::min(kMergeTiles, kCopySlots >> sl));
 }
 
 hipError_t launch_merge(const Params& p, hipStream_t s) {
   const int upt = gather_tile_units(p);
-  const int tpb = merge_tiles_per_block(p, upt);
+  int tpb, spt_log2;
+  merge_copy_shape(p, upt, &tpb, &spt_log2);
   const unsigned copies =
       p.k_max > 0 ? unsigned((gather_tiles(p, upt) + tpb - 1) / tpb) : 0u;
-  hipLaunchKernelGGL(merge_kernel, dim3(1 + copies, unsigned(p.B * p.H_q)), dim3(kMergeThreads), 0,
-                     s, p, upt, tpb);
+  // 17 x 8 groups: the 129 tiles of a length just past 2^20 in one round
+  const dim3 grid{1 + copies, unsigned(p.B * p.H_q)};
+  if (gather_tiles(p, upt) <= 8 * 4)
+    hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(kMergeThreads), 0, s, p, upt, tpb, spt_log2);
+  else
+    hipLaunchKernelGGL(merge_kernel<17>, grid, dim3(kMergeThreads), 0, s, p, upt, tpb, spt_log2);
   return hipGetLastError();
 }
 
