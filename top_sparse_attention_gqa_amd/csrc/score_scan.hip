@@ -27,7 +27,8 @@ namespace ra {
 
 constexpr int kStage = 8192;       // LDS candidate staging entries per block
 constexpr int kDeferUnits = 16;    // units whose candidates one burst may write
-constexpr int kSampleWaves = 8;    // sampled pages per sample block (one per wave)
+constexpr int kSampleWaves = 4;    // sampled pages per sample block (one per wave): at 95
+                                   // VGPRs five such blocks fit a CU, two of eight waves
 constexpr int kSampleThreads = kSampleWaves * 64;
 
 // ---------------------------------------------------------------- sample
