@@ -52,14 +52,14 @@ def test_split_scan_many_blocks_per_unit():
 
 
 def test_split_scan_staging_overflow_every_member_a_candidate():
-    H_q, H_kv, N, cap = 4, 1, 4096 * 100 + 100, 4096 * 300
+    H_q, H_kv, N, cap = 4, 1, 4096 * 200 + 100, 4096 * 300
     split, T, NB = split_geometry(H_kv, N, cap)
     ns, win = 16, 64
     M = N - ns - win
     say(f"case split_overflow: N={N} max_seq_len={cap} units={T} blocks={NB} k=|M|={M}")
-    # about 25 pages per block: 6400 candidates of 4 heads overflow the
-    # 6144-entry staging
-    assert split and T * 64 / NB * 64 * H_q > 6144
+    # about 50 pages per block: 12800 candidates of 4 heads overflow the
+    # 8192-entry staging
+    assert split and T * 64 / NB * 64 * H_q > 8192
     L = synth.make_layer(H_q, H_kv, [N], [M], ns, win, 2, 22, DEV)
     run = gpu_decode(L, max_seq_len=cap)
     assert run.rescanned == 0
