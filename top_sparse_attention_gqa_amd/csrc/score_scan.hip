@@ -169,10 +169,13 @@ hipError_t launch_sample(const Params& p, hipStream_t s) {
 
 // ---------------------------------------------------------------- scan
 // Pages of a unit whose keys a block can hold in LDS while it waits for the
-// group's candidate bounds (64 KiB at most; a multiple of kScanWaves).
+// group's candidate bounds (a multiple of kScanWaves). 32 pages are four per
+// wave, past the time a bound takes, and fewer held keys to decide once the
+// bounds are out measured faster than a whole unit (64 pages: C3_1 scan
+// 1-1.5 us, C2 1.4 us more).
 template <int G>
 struct RawCfg {
-  static constexpr int pages = 256 / G < kUnitPages ? 256 / G : kUnitPages;
+  static constexpr int pages = G >= 4 ? 32 : kUnitPages;
   static constexpr int words = pages * kPage * G;
   static_assert(pages % kScanWaves == 0, "whole rounds of the block's waves");
 };
