@@ -132,10 +132,10 @@ def algorithmic_bytes(c, lens, ks, idx_np, n_sink, window):
 
 def sample_stride(P):
     """One page in S is sampled before the scan (page j with j % S == S / 2):
-    S is the largest power of two up to 64 that leaves at least 32 sampled
+    S is the largest power of two up to 64 that leaves at least 16 sampled
     pages."""
     s = 0
-    while s < 6 and (P >> (s + 1)) >= 32:
+    while s < 6 and (P >> (s + 1)) >= 16:
         s += 1
     return 1 << s
 

@@ -173,9 +173,9 @@ def test_constant_keys_rescan_path():
 
 def sample_stride(P):
     """One page in S is sampled (page j with j % S == S / 2): S is the
-    largest power of two up to 64 that leaves at least 32 sampled pages."""
+    largest power of two up to 64 that leaves at least 16 sampled pages."""
     s = 0
-    while s < 6 and (P >> (s + 1)) >= 32:
+    while s < 6 and (P >> (s + 1)) >= 16:
         s += 1
     return 1 << s
 

@@ -111,7 +111,7 @@ def test_one_sampled_key_far_above_the_rest():
     L = synth.make_layer(4, 1, [32768], [3000], 16, 64, 2, 78, DEV)
     P = 32768 // 64
     s = 0
-    while s < 6 and (P >> (s + 1)) >= 32:
+    while s < 6 and (P >> (s + 1)) >= 16:
         s += 1
     j = (1 << s) // 2  # the first sampled page
     qdir = L.q[0, 0:4].float().sum(0)

@@ -26,7 +26,7 @@ constexpr int kMaxUnits = RA_MAX_SEQ_LEN / kUnit;
 // chosen so that at least kSampleMinPages pages of a (sequence, KV head)
 // are sampled, and S <= 2^kSampleMaxLog2. Page j is sampled iff
 // j % S == S / 2.
-constexpr int kSampleMinPages = 32;
+constexpr int kSampleMinPages = 16;
 constexpr int kSampleMaxLog2 = 6;
 
 __host__ __device__ inline int sample_log2(int P) {
