@@ -527,16 +527,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p) {
     // Otherwise the block owns its units: their candidates stay staged over
     // several units of the group and are written in one burst when the
     // group ends, the block is done, or as many units are staged as the
-    // staging holds at twice the expected candidate rate (the sampled bound
-    // passes about 1.5 k_eff per head). Each burst stops the block's waves
-    // at two barriers; between bursts they do not meet.
+    // staging holds at 1.6 k_eff candidates per head (the sampled bound
+    // passes about 1.5 k_eff; a unit that passes more sends the excess
+    // straight to its list). Each burst stops the block's waves at two
+    // barriers; between bursts they do not meet.
     ++nu_st;
     const int np_seq = (sg.N + kPage - 1) / kPage;
     const int np_next = min(kUnitPages, np_seq - (ur.u + 1) * kUnitPages);
     const bool next_here = x + 1 < X1 && np_next > 0;
     const int64_t per_unit =
-        int64_t(G) * 2 * sg.k_eff / ((np_seq + kUnitPages - 1) / kUnitPages) + 64;
-    const int n_defer = int(max<int64_t>(1, min<int64_t>(kDeferUnits, (kStage * 5 / 8) / per_unit)));
+        int64_t(G) * 8 * sg.k_eff / (5 * ((np_seq + kUnitPages - 1) / kUnitPages)) + 64;
+    const int n_defer = int(max<int64_t>(1, min<int64_t>(kDeferUnits, kStage / per_unit)));
     if (next_here && nu_st < n_defer) continue;  // block-uniform
     __syncthreads();
     const uint32_t nst = min(s_fill, uint32_t(kStage));
