@@ -514,7 +514,8 @@ __device__ void copy_positions(const Params& p, int bh, int c, int nt, int tile,
   for (int j = 0; j < tb - ta; ++j) {
     const uint32_t cnt = s_own[j];
     for (uint32_t i = spt + uint32_t(tid); i < cnt; i += kMergeThreads) {
-      const int32_t v = RA_IN(i < uint32_t(2 * tile), p, 8) ? src[size_t(ta + j) * (2 * tile) + i] : 0;
+      const int32_t v =
+          RA_IN(i < uint32_t(2 * tile), p, 8) ? src[size_t(ta + j) * (2 * tile) + i] : 0;
       if (RA_GUARD(off + s_pre[j] + i < uint32_t(p.k_max), p, 9)) dst[s_pre[j] + i] = v;
     }
   }
@@ -534,7 +535,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(Params p, int tile
   const int tile = tile_units * kUnit;
   const int nt = (sg.N + tile - 1) / tile;
   if (blockIdx.x > 0) {
-    if (p.k_max > 0 && sg.k_eff > 0) copy_positions(p, bh, int(blockIdx.x) - 1, nt, tile, tpb, spt_log2);
+    if (p.k_max > 0 && sg.k_eff > 0)
+      copy_positions(p, bh, int(blockIdx.x) - 1, nt, tile, tpb, spt_log2);
     return;
   }
   const int tid = threadIdx.x;

@@ -8,8 +8,9 @@
 // scores one page in S; from the sample every head gets a conservative
 // threshold such that, with a wide statistical margin, at least k_eff
 // members of M score at or above it. The scan then keeps only those
-// candidates, staged in LDS and written in one burst per unit of 64 pages
-// to per-(head, unit) lists, plus the scores of the static set W. The
+// candidates, staged in LDS over one or several units of 64 pages and
+// written in one burst to per-(head, unit) lists, plus the scores of the
+// static set W. The
 // selection checks the margin exactly (it needs at least k_eff candidates);
 // heads that fail it are rescanned with every member of M as a candidate.
 //
@@ -27,8 +28,9 @@ namespace ra {
 
 constexpr int kStage = 8192;       // LDS candidate staging entries per block
 constexpr int kDeferUnits = 16;    // units whose candidates one burst may write
-constexpr int kSampleWaves = 4;    // sampled pages per sample block (one per wave): at 95
-                                   // VGPRs five such blocks fit a CU, two of eight waves
+// sampled pages per sample block, one per wave: at 95 VGPRs five such
+// blocks fit a CU, against two of eight waves
+constexpr int kSampleWaves = 4;
 constexpr int kSampleThreads = kSampleWaves * 64;
 
 // ---------------------------------------------------------------- sample
@@ -193,10 +195,12 @@ constexpr bool kHelpOddHeads = true;
 #endif
 
 // Persistent over the linear unit index (sequence, KV head, unit of 64
-// pages): each block takes a contiguous range of units. Per unit, the
-// candidates (members of M scoring at or above the head's threshold) are
-// staged in LDS and written after the unit to the (head, unit) lists with
-// their counts; the block owns the unit, so no global atomics are needed.
+// pages): each block takes a contiguous range of units. The candidates
+// (members of M scoring at or above the head's threshold) are staged in LDS
+// over one or several units of a group and written in one burst to the
+// (head, unit) lists with their counts; the block owns those units, so no
+// global atomics are needed (in a split scan, where two blocks may share a
+// unit, each unit's slots are reserved with them).
 // W scores go straight to the score rows. Running maxima over W and M per
 // head are folded into the head state whenever the block moves to another
 // (sequence, KV head) and at its end.
