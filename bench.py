@@ -475,9 +475,12 @@ def run_layer(args):
     # scan; the others are one call each): an event between two kernels
     # costs about 3 us of GPU time, so events on every step would move the
     # headline. SCAN_SAMPLES more event-timed scans follow right after it.
+    # The split steps are the last of each stretch of `every`, never the
+    # first step: there the GPU has no queued work yet and would wait for
+    # the host to issue the split step's second call (about 30 us).
     every = max(IN_REGION_EVERY, args.steps // 4)
     events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-              for i in range(0, args.steps, every)}
+              for i in range(min(every, args.steps) - 1, args.steps, every)}
     loop_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -638,8 +641,10 @@ def run_model(args):
             keep(0)
     torch.cuda.synchronize()
     every = max(1, args.steps // SCAN_SAMPLES)         # scan events on 20 of the steps
+    # (the last of each stretch of `every`, so that the GPU has queued work
+    # while the host issues a split layer's calls)
     ev = {s: [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_layers)]
-          for s in range(0, args.steps, every)}
+          for s in range(min(every, args.steps) - 1, args.steps, every)}
     bnd = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
     bnd[0].record()
@@ -864,7 +869,7 @@ def run_prefill(args):
     # two contraction kernels of the sampled pass (maxima of the sampled
     # pages, filter) on the launching stream
     events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-              for i in range(0, args.steps, PF_EVERY)}
+              for i in range(min(PF_EVERY, args.steps) - 1, args.steps, PF_EVERY)}
     loop_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
